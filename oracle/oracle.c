@@ -1,0 +1,248 @@
+/*
+ * oracle.c -- plain, slow CPU definition of the dense GEMM with a fused
+ * bias/ReLU epilogue.  TEST INFRASTRUCTURE ONLY: the tests, the smoke check
+ * and the CPU-baseline leg of the benchmark may call it; the product path
+ * (the HIP library) never does, and this file shares no code, header, table
+ * or helper with it.
+ *
+ * What it computes (one definition, written out):
+ *
+ *     C[i][j] = epi( bias[j] + sum_{k=0}^{K-1} a(i,k) * b(k,j) )
+ *
+ *   - The problem statement is the matrix product with an added bias,
+ *     Output = Input * Weight + Bias, from the FuseReductionEpilogue series
+ *     (page "kimm240.github.io/tvm", post "1. Problem Analysis and Limitations
+ *     of Existing Solutions").
+ *   - The bias is the initial value of the reduction rather than a separate
+ *     addition afterwards (same page, post "2. TIR Structure Transformation
+ *     Design": reduction init = Bias instead of 0).  The oracle therefore
+ *     starts every accumulator at bias[j] (or 0 without bias) and adds the
+ *     products in ascending k.
+ *   - ReLU after the bias is the Conv2d + Bias + ReLU pattern (same page, post
+ *     "Implement and enable Conv2d-Reshape-Add-ReLU fusion"); epi(x) is x, or
+ *     x > 0 ? x : 0 with ReLU.
+ *   - Low-precision inputs with a wide accumulator is the mixed-precision
+ *     multiply-accumulate of the Tensor Core notes (page
+ *     "je-d.tistory.com/entry/tvm", first section).  The oracle goes further
+ *     than any GPU: f16, bf16 and f32 inputs are decoded to their exact values
+ *     and accumulated in IEEE binary64; int8 inputs are accumulated as exact
+ *     integers that must stay inside int32 (the GPU's accumulator), checked
+ *     at every step.
+ *
+ * Operand storage (element offsets):
+ *   a(i,k) = A[i*lda + k]     (a_col == 0, row-major)   or  A[k*lda + i]  (a_col == 1)
+ *   b(k,j) = B[k*ldb + j]     (b_col == 0, row-major)   or  B[j*ldb + k]  (b_col == 1)
+ *   C[i*ldc + j]  -- double for the float types, int32 for int8.
+ *
+ * Decoders are written from the IEEE 754 binary16 field layout (1 sign bit,
+ * 5 exponent bits, bias 15, 10 fraction bits) and the bfloat16 layout (1 sign
+ * bit, 8 exponent bits, bias 127, 7 fraction bits).  binary32 is read as the
+ * host's float.
+ *
+ * The full entry point nests its loops i, k, j so that a row of C is built
+ * while streaming rows of b; every C[i][j] still receives bias[j] first and
+ * then the products in ascending k, one binary64 add each -- the same
+ * operations in the same order as the per-entry entry point, which the tests
+ * check bit-for-bit.
+ *
+ * Return codes: 0 = ok, 1 = invalid argument, 2 = an int8 sum left the int32
+ * range (the result is then not what an int32 accumulator holds).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_F16 = 0, OR_BF16 = 1, OR_F32 = 2, OR_I8 = 3 };
+
+/* ---- exact decoders -------------------------------------------------- */
+
+double oracle_decode_f16(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 10) & 0x1f;
+    int frac = h & 0x3ff;
+    double v;
+    if (expo == 0)          /* zero / subnormal: frac * 2^(1-15-10) */
+        v = ldexp((double)frac, -24);
+    else if (expo == 0x1f)  /* infinity / NaN */
+        v = frac ? NAN : INFINITY;
+    else                    /* (1 + frac/2^10) * 2^(expo-15) */
+        v = ldexp((double)(1024 + frac), expo - 25);
+    return sign ? -v : v;
+}
+
+double oracle_decode_bf16(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 7) & 0xff;
+    int frac = h & 0x7f;
+    double v;
+    if (expo == 0)          /* zero / subnormal: frac * 2^(1-127-7) */
+        v = ldexp((double)frac, -133);
+    else if (expo == 0xff)
+        v = frac ? NAN : INFINITY;
+    else                    /* (1 + frac/2^7) * 2^(expo-127) */
+        v = ldexp((double)(128 + frac), expo - 134);
+    return sign ? -v : v;
+}
+
+static double decode_f32(const float* p) { return (double)*p; }
+
+/* value of element `idx` of a float-typed operand, exactly */
+static double elem_f(const void* X, int dtype, int64_t idx) {
+    switch (dtype) {
+    case OR_F16:  return oracle_decode_f16(((const uint16_t*)X)[idx]);
+    case OR_BF16: return oracle_decode_bf16(((const uint16_t*)X)[idx]);
+    default:      return decode_f32((const float*)X + idx);
+    }
+}
+
+static int64_t a_off(int64_t i, int64_t k, int64_t lda, int a_col) { return a_col ? k * lda + i : i * lda + k; }
+static int64_t b_off(int64_t k, int64_t j, int64_t ldb, int b_col) { return b_col ? j * ldb + k : k * ldb + j; }
+
+static double relu_f(double x) { return x > 0.0 ? x : 0.0; }
+
+static int check_args(int64_t M, int64_t N, int64_t K, int64_t lda, int a_col, int64_t ldb, int b_col, int dtype) {
+    if (M < 0 || N < 0 || K < 0) return 1;
+    if (dtype < OR_F16 || dtype > OR_I8) return 1;
+    if (lda < (a_col ? M : K) || lda < 1) return 1;
+    if (ldb < (b_col ? K : N) || ldb < 1) return 1;
+    return 0;
+}
+
+/* ---- decode a whole operand (used by tests to pin the decoders) -------- */
+
+int oracle_decode(int dtype, const void* X, int64_t n, double* out) {
+    if (dtype < OR_F16 || dtype > OR_I8) return 1;
+    for (int64_t t = 0; t < n; ++t)
+        out[t] = dtype == OR_I8 ? (double)((const int8_t*)X)[t] : elem_f(X, dtype, t);
+    return 0;
+}
+
+/* ---- full product ------------------------------------------------------- */
+
+int oracle_gemm(int64_t M, int64_t N, int64_t K,
+                const void* A, int64_t lda, int a_col,
+                const void* B, int64_t ldb, int b_col,
+                int dtype, const void* bias, int relu,
+                void* C, int64_t ldc) {
+    if (check_args(M, N, K, lda, a_col, ldb, b_col, dtype) || ldc < N) return 1;
+    if (M == 0 || N == 0) return 0;
+    int overflow = 0;
+
+    if (dtype == OR_I8) {
+        const int8_t* a8 = (const int8_t*)A;
+        const int8_t* b8 = (const int8_t*)B;
+        const int32_t* bi = (const int32_t*)bias;
+        int32_t* c = (int32_t*)C;
+        /* b(k,j) as a dense K x N int32 array */
+        int32_t* bd = (int32_t*)malloc(sizeof(int32_t) * (size_t)(K > 0 ? K : 1) * (size_t)N);
+        if (!bd) return 1;
+        for (int64_t k = 0; k < K; ++k)
+            for (int64_t j = 0; j < N; ++j) bd[k * N + j] = b8[b_off(k, j, ldb, b_col)];
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : overflow)
+        for (int64_t i = 0; i < M; ++i) {
+            int64_t* acc = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
+            for (int64_t j = 0; j < N; ++j) acc[j] = bi ? bi[j] : 0;
+            for (int64_t k = 0; k < K; ++k) {
+                int64_t aik = a8[a_off(i, k, lda, a_col)];
+                const int32_t* brow = bd + k * N;
+                for (int64_t j = 0; j < N; ++j) {
+                    acc[j] += aik * brow[j];
+                    if (acc[j] > INT32_MAX || acc[j] < INT32_MIN) overflow = 1;
+                }
+            }
+            for (int64_t j = 0; j < N; ++j) {
+                int64_t v = acc[j];
+                if (relu && !(v > 0)) v = 0;
+                c[i * ldc + j] = (int32_t)v;
+            }
+            free(acc);
+        }
+        free(bd);
+        return overflow ? 2 : 0;
+    }
+
+    const float* bf = (const float*)bias;
+    double* c = (double*)C;
+    double* bd = (double*)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1) * (size_t)N);
+    if (!bd) return 1;
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t j = 0; j < N; ++j) bd[k * N + j] = elem_f(B, dtype, b_off(k, j, ldb, b_col));
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < M; ++i) {
+        double* acc = c + i * ldc;
+        for (int64_t j = 0; j < N; ++j) acc[j] = bf ? (double)bf[j] : 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double aik = elem_f(A, dtype, a_off(i, k, lda, a_col));
+            const double* brow = bd + k * N;
+            for (int64_t j = 0; j < N; ++j) acc[j] += aik * brow[j];
+        }
+        if (relu)
+            for (int64_t j = 0; j < N; ++j) acc[j] = relu_f(acc[j]);
+    }
+    free(bd);
+    return 0;
+}
+
+/* ---- selected entries ---------------------------------------------------- */
+
+int oracle_gemm_entries(int64_t M, int64_t N, int64_t K,
+                        const void* A, int64_t lda, int a_col,
+                        const void* B, int64_t ldb, int b_col,
+                        int dtype, const void* bias, int relu,
+                        const int64_t* ii, const int64_t* jj, int64_t n, void* out) {
+    if (check_args(M, N, K, lda, a_col, ldb, b_col, dtype) || n < 0) return 1;
+    for (int64_t t = 0; t < n; ++t)
+        if (ii[t] < 0 || ii[t] >= M || jj[t] < 0 || jj[t] >= N) return 1;
+    int overflow = 0;
+    if (dtype == OR_I8) {
+        const int8_t* a8 = (const int8_t*)A;
+        const int8_t* b8 = (const int8_t*)B;
+        const int32_t* bi = (const int32_t*)bias;
+        int32_t* o = (int32_t*)out;
+#pragma omp parallel for schedule(dynamic, 16) reduction(| : overflow)
+        for (int64_t t = 0; t < n; ++t) {
+            int64_t i = ii[t], j = jj[t];
+            int64_t acc = bi ? bi[j] : 0;
+            for (int64_t k = 0; k < K; ++k) {
+                acc += (int64_t)a8[a_off(i, k, lda, a_col)] * (int64_t)b8[b_off(k, j, ldb, b_col)];
+                if (acc > INT32_MAX || acc < INT32_MIN) overflow = 1;
+            }
+            if (relu && !(acc > 0)) acc = 0;
+            o[t] = (int32_t)acc;
+        }
+        return overflow ? 2 : 0;
+    }
+    const float* bf = (const float*)bias;
+    double* o = (double*)out;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t t = 0; t < n; ++t) {
+        int64_t i = ii[t], j = jj[t];
+        double acc = bf ? (double)bf[j] : 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            acc += elem_f(A, dtype, a_off(i, k, lda, a_col)) * elem_f(B, dtype, b_off(k, j, ldb, b_col));
+        o[t] = relu ? relu_f(acc) : acc;
+    }
+    return 0;
+}
+
+/* ---- threads used by the parallel loops ---------------------------------- */
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}

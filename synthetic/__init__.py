@@ -1,0 +1,166 @@
+"""Seeded synthetic inputs for the GEMM workloads.
+
+This module only draws numbers: it holds none of the product's arithmetic,
+and both the CPU oracle side (tests) and the HIP side (tests, benchmark) take
+their inputs from it.
+
+Recipe (one numpy PCG64 generator per problem, ``np.random.default_rng(seed)``):
+  * draw A, then B, then the bias, each in its *storage* order: a row-major
+    M x K operand is drawn as an (M, K) array, a column-major one as the
+    (K, M) array it is stored as (likewise B: (K, N) row-major, (N, K)
+    column-major);
+  * "uniform": ``rng.uniform(-1, 1)``; "normal": ``rng.standard_normal()``;
+    both are drawn in float64, rounded to float32 (round-to-nearest-even),
+    then to the operand type: float16 with numpy's RNE cast, bfloat16 with
+    torch's RNE cast on the CPU, float32 as is;
+  * int8 operands: ``rng.integers(-128, 127, endpoint=True)``; int32 bias:
+    ``rng.integers(-2**20, 2**20, endpoint=True)``;
+  * f16/bf16 operands are returned as uint16 bit patterns, f32 as float32,
+    int8 as int8, bias as float32 or int32.
+The sampled-entry list of a large problem comes from a second generator,
+``default_rng(1000 + seed)``: 4096 rows then 4096 columns (duplicates kept),
+followed by every entry of rows 0 and M - 1.
+"""
+from dataclasses import dataclass, replace
+
+import numpy as np
+
+# element-type codes (the same numbering as the library's dtype argument)
+F16, BF16, F32, I8 = 0, 1, 2, 3
+DTYPE_NAMES = {F16: "f16", BF16: "bf16", F32: "f32", I8: "i8"}
+
+
+@dataclass(frozen=True)
+class Problem:
+    name: str
+    dtype: int
+    M: int
+    N: int
+    K: int
+    a_col: bool = False
+    b_col: bool = False
+    dist: str = "uniform"      # "uniform" | "normal" | "int"
+    seed: int = 0
+    bias: bool = False
+    relu: bool = False
+    lda: int = 0               # 0 = tight
+    ldb: int = 0
+    ldc: int = 0
+
+    @property
+    def LDA(self):
+        return self.lda or (self.M if self.a_col else self.K)
+
+    @property
+    def LDB(self):
+        return self.ldb or (self.K if self.b_col else self.N)
+
+    @property
+    def LDC(self):
+        return self.ldc or self.N
+
+    @property
+    def flops(self):
+        return 2.0 * self.M * self.N * self.K
+
+    @property
+    def in_bytes(self):
+        return 1 if self.dtype == I8 else (4 if self.dtype == F32 else 2)
+
+    @property
+    def alg_bytes(self):
+        """Bytes the product must move at least: A and B read once, C written once, bias read once."""
+        b = (self.M * self.K + self.K * self.N) * self.in_bytes + self.M * self.N * 4
+        if self.bias:
+            b += self.N * 4
+        return b
+
+
+def _workloads():
+    w = {}
+    w["f16_512"] = Problem("f16_512", F16, 512, 512, 512, dist="uniform", seed=0)
+    w["f32_2048"] = Problem("f32_2048", F32, 2048, 2048, 2048, dist="uniform", seed=1)
+    w["f16_8192"] = Problem("f16_8192", F16, 8192, 8192, 8192, b_col=True, dist="normal", seed=2)
+    w["bf16_8192"] = Problem("bf16_8192", BF16, 8192, 8192, 8192, b_col=True, dist="normal", seed=2)
+    for m in (1, 16, 64, 256):
+        w[f"skinny_m{m}"] = Problem(f"skinny_m{m}", F16, m, 4096, 4096, dist="uniform", seed=3)
+    w["sk_1536x1536x16384"] = Problem("sk_1536x1536x16384", F16, 1536, 1536, 16384, dist="uniform", seed=3)
+    w["sk_3840x3840x4096"] = Problem("sk_3840x3840x4096", F16, 3840, 3840, 4096, dist="uniform", seed=3)
+    w["i8_4096"] = Problem("i8_4096", I8, 4096, 4096, 4096, dist="int", seed=4, bias=True, relu=True)
+    return w
+
+
+WORKLOADS = _workloads()
+
+
+def workload(name, **overrides):
+    p = WORKLOADS[name]
+    return replace(p, **overrides) if overrides else p
+
+
+def _to_storage(x64, dtype):
+    x32 = x64.astype(np.float32)
+    if dtype == F32:
+        return x32
+    if dtype == F16:
+        return x32.astype(np.float16).view(np.uint16)
+    if dtype == BF16:
+        import torch
+        t = torch.from_numpy(x32).to(torch.bfloat16)
+        return t.view(torch.int16).numpy().view(np.uint16)
+    raise ValueError(dtype)
+
+
+def _draw(rng, shape, dist, dtype):
+    if dtype == I8:
+        return rng.integers(-128, 127, size=shape, endpoint=True, dtype=np.int8)
+    if dist == "uniform":
+        x = rng.uniform(-1.0, 1.0, size=shape)
+    elif dist == "normal":
+        x = rng.standard_normal(size=shape)
+    else:
+        raise ValueError(f"distribution {dist!r} needs an int8 problem")
+    return _to_storage(x, dtype)
+
+
+def _operand_shape(rows, cols, col_major, ld):
+    """Storage array shape of a rows x cols logical operand (padded to ld)."""
+    return (cols, ld) if col_major else (rows, ld)
+
+
+def generate(p: Problem):
+    """Storage arrays {'A', 'B', 'bias'} of problem p (bias None when unused).
+
+    With ld larger than the extent, the padding columns are drawn too (from
+    the same stream, as part of the storage array)."""
+    rng = np.random.default_rng(p.seed)
+    A = _draw(rng, _operand_shape(p.M, p.K, p.a_col, p.LDA), p.dist, p.dtype)
+    B = _draw(rng, _operand_shape(p.K, p.N, p.b_col, p.LDB), p.dist, p.dtype)
+    bias = None
+    if p.bias:
+        if p.dtype == I8:
+            bias = rng.integers(-2 ** 20, 2 ** 20, size=p.N, endpoint=True, dtype=np.int64).astype(np.int32)
+        else:
+            bias = rng.uniform(-1.0, 1.0, size=p.N).astype(np.float32)
+    return {"A": A, "B": B, "bias": bias}
+
+
+def sample_entries(p: Problem, n=4096):
+    """(ii, jj) int64 arrays: n seeded random entries plus all of rows 0 and M-1."""
+    rng = np.random.default_rng(1000 + p.seed)
+    ii = rng.integers(0, p.M, size=n, dtype=np.int64)
+    jj = rng.integers(0, p.N, size=n, dtype=np.int64)
+    cols = np.arange(p.N, dtype=np.int64)
+    rows = [0] if p.M == 1 else [0, p.M - 1]
+    ii = np.concatenate([ii] + [np.full(p.N, r, dtype=np.int64) for r in rows])
+    jj = np.concatenate([jj] + [cols for _ in rows])
+    return ii, jj
+
+
+def small_problem(dtype, M, N, K, seed=0, a_col=False, b_col=False, bias=False, relu=False,
+                  lda=0, ldb=0, ldc=0, dist=None):
+    """An ad-hoc problem for parity cases (ragged shapes, padding, layouts)."""
+    if dist is None:
+        dist = "int" if dtype == I8 else "uniform"
+    return Problem(f"{DTYPE_NAMES[dtype]}_{M}x{N}x{K}", dtype, M, N, K, a_col=a_col, b_col=b_col, dist=dist,
+                   seed=seed, bias=bias, relu=relu, lda=lda, ldb=ldb, ldc=ldc)

@@ -1,0 +1,75 @@
+"""The pins are strong enough: plant one plausible mistake at a time in a copy
+of oracle.c (on the CPU), build it, and check that some pin rejects it."""
+import os
+import subprocess
+
+import pytest
+
+import oracle_pins as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+
+# (name, text in oracle.c, replacement): each a mistake someone could make
+MUTANTS = [
+    ("drop_last_k", "k < K; ++k)", "k + 1 < K; ++k)"),
+    ("drop_first_k", "for (int64_t k = 0; k < K; ++k)", "for (int64_t k = 1; k < K; ++k)"),
+    ("sign_full_float", "acc[j] += aik * brow[j];", "acc[j] -= aik * brow[j];"),
+    ("sign_full_int", "acc[j] += aik * brow[j];\n                    if", "acc[j] -= aik * brow[j];\n                    if"),
+    ("transposed_b", "return b_col ? j * ldb + k : k * ldb + j;", "return b_col ? k * ldb + j : j * ldb + k;"),
+    ("transposed_a", "return a_col ? k * lda + i : i * lda + k;", "return a_col ? i * lda + k : k * lda + i;"),
+    ("b_ignores_col_flag", "return b_col ? j * ldb + k : k * ldb + j;", "return k * ldb + j;"),
+    ("bias_by_row_int", "bi ? bi[j] : 0", "bi ? bi[i] : 0"),
+    ("bias_by_row_float", "bf ? (double)bf[j] : 0.0", "bf ? (double)bf[i] : 0.0"),
+    ("bias_dropped_float", "bf ? (double)bf[j] : 0.0", "0.0"),
+    ("bias_twice_int", "acc[j] = bi ? bi[j] : 0;", "acc[j] = bi ? 2 * bi[j] : 0;"),
+    ("relu_abs", "return x > 0.0 ? x : 0.0;", "return x > 0.0 ? x : -x;"),
+    ("relu_int_missing", "if (relu && !(v > 0)) v = 0;", ""),
+    ("f16_exponent_off_by_one", "expo - 25", "expo - 24"),
+    ("f16_subnormal_scale", "ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
+    ("f16_no_implicit_bit", "(double)(1024 + frac)", "(double)(frac)"),
+    ("bf16_frac_mask", "int frac = h & 0x7f;", "int frac = h & 0x3f;"),
+    ("bf16_exponent_bias", "expo - 134", "expo - 133"),
+    ("f16_sign_dropped", "return sign ? -v : v;\n}\n\ndouble oracle_decode_bf16", "return v;\n}\n\ndouble oracle_decode_bf16"),
+    ("int8_as_uint8", "const int8_t* a8 = (const int8_t*)A;", "const uint8_t* a8 = (const uint8_t*)A;"),
+    ("overflow_check_missing", "if (acc[j] > INT32_MAX || acc[j] < INT32_MIN) overflow = 1;", ""),
+    ("entries_wrong_k_order_term", "elem_f(B, dtype, b_off(k, j, ldb, b_col));", "elem_f(B, dtype, b_off(k, j, ldb, !b_col));"),
+]
+
+
+def _build_mutant(tmp_path, name, old, new):
+    text = open(SRC).read()
+    assert old in text, f"mutant {name}: pattern not found in oracle.c"
+    src = tmp_path / f"{name}.c"
+    src.write_text(text.replace(old, new))
+    lib = tmp_path / f"lib{name}.so"
+    subprocess.run(["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-std=c11",
+                    str(src), "-o", str(lib), "-lm"], check=True)
+    return str(lib)
+
+
+_RUNNER = """
+import sys
+sys.path.insert(0, {tests!r}); sys.path.insert(0, {root!r})
+import oracle, oracle_pins as P
+o = oracle.Oracle({lib!r})
+failed = []
+for pin in P.ALL_PINS:
+    try:
+        pin(o)
+    except (AssertionError, OverflowError, oracle.OracleError):
+        failed.append(pin.__name__)
+print("FAILED_PINS", ",".join(failed))
+"""
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    import sys
+    lib = _build_mutant(tmp_path, name, old, new)
+    code = _RUNNER.format(tests=os.path.join(ROOT, "tests"), root=ROOT, lib=lib)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    if r.returncode != 0:
+        return  # the planted mistake crashed the oracle (e.g. an out-of-bounds read): caught
+    line = [l for l in r.stdout.splitlines() if l.startswith("FAILED_PINS")][-1]
+    assert line.split(" ", 1)[1:] and line.split(" ", 1)[1].strip(), f"no pin rejects the planted mistake {name}"
