@@ -1,0 +1,167 @@
+/*
+ * tcm.h -- C ABI of the MI355X (gfx950) dense GEMM engine.
+ *
+ * One operation: the matrix product with a fused bias / ReLU epilogue,
+ *
+ *     C[i][j] = epi( bias[j] + sum_k a(i,k) * b(k,j) ),
+ *
+ * the product-plus-bias whose bias is the initial value of the reduction
+ * (kimm240.github.io/tvm, FuseReductionEpilogue posts 1 and 2), followed by
+ * the ReLU of the Conv2d + Bias + ReLU pattern (same page, Conv2d-Reshape-
+ * Add-ReLU fusion post), computed on the matrix cores with low-precision
+ * inputs and a wide accumulator (je-d.tistory.com/entry/tvm, Tensor Core
+ * notes: mixed-precision multiply-accumulate).  Large problems are tiled and
+ * staged through LDS (kimm240.github.io/tvm, GEMM optimisation Steps 2-6);
+ * shapes whose tile count fills the GPU badly are split along k across
+ * workgroups (leiblog.wang, the Stream-K reproduction post).
+ *
+ * All pointers are DEVICE pointers (any allocation the HIP runtime can read
+ * on the current device).  The caller owns A, B, C and bias; the library
+ * never frees them.  Calls are asynchronous on `stream` (a hipStream_t passed
+ * as void*, NULL = the null stream) and never synchronise; results are
+ * ready when the stream reaches the call.  Calls on one stream run in order;
+ * the library's only state is a cached split-k workspace per (device,
+ * stream), so concurrent calls on different streams are independent.
+ *
+ * Errors are returned, never raised; argument checks run before any HIP call.
+ */
+#ifndef TCM_H
+#define TCM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes --------------------------------------------------------- */
+typedef enum {
+    TCM_OK = 0,
+    TCM_ERR_INVALID_VALUE = 1, /* a bad size, leading dimension, pointer, flag or option */
+    TCM_ERR_NOT_SUPPORTED = 2, /* a valid request this build cannot serve (none today) */
+    TCM_ERR_HIP = 3,           /* a HIP runtime error (no device, launch failure, ...) */
+    TCM_ERR_ALLOC = 4          /* the split-k workspace could not be allocated */
+} tcm_status;
+
+/* ---- element types (low byte of `dtype`) ---------------------------------- */
+/*   TCM_F16_F32  : A, B IEEE binary16; accumulate and C in binary32; bias f32
+ *   TCM_BF16_F32 : A, B bfloat16;      accumulate and C in binary32; bias f32
+ *   TCM_F32_F32  : A, B binary32;      accumulate and C in binary32; bias f32
+ *   TCM_I8_I32   : A, B int8;          accumulate and C in int32 (wrapping
+ *                  two's complement on overflow); bias int32                */
+enum { TCM_F16_F32 = 0, TCM_BF16_F32 = 1, TCM_F32_F32 = 2, TCM_I8_I32 = 3 };
+
+/* ---- operand layout flags (or-ed into `dtype`) ---------------------------- */
+/* Row-major unless flagged:
+ *   a(i,k) = A[i*lda + k]   or, with TCM_A_COLMAJOR,  A[k*lda + i]
+ *   b(k,j) = B[k*ldb + j]   or, with TCM_B_COLMAJOR,  B[j*ldb + k]
+ *   C is always row-major: C[i*ldc + j].                                      */
+#define TCM_A_COLMAJOR (1 << 8)
+#define TCM_B_COLMAJOR (1 << 9)
+
+/* ---- epilogue flags -------------------------------------------------------- */
+/* TCM_EPI_BIAS: bias[j] (length N, f32 or int32 per dtype) seeds the
+ *               accumulator of column j before any product is added.
+ * TCM_EPI_RELU: C = x > 0 ? x : 0 after the sum (NaN and -0 become +0).     */
+enum { TCM_EPI_NONE = 0, TCM_EPI_BIAS = 1, TCM_EPI_RELU = 2, TCM_EPI_BIAS_RELU = 3 };
+
+/*
+ * tcm_gemm -- C = epi(bias + A.B) with M x K A, K x N B, M x N C.
+ *
+ *   M, N, K      sizes, >= 0.  M == 0 or N == 0: nothing to do, TCM_OK.
+ *                K == 0: C = epi(bias or 0).
+ *   A, lda       A and its leading dimension in elements:
+ *                lda >= K (row-major) or lda >= M (TCM_A_COLMAJOR), lda >= 1.
+ *   B, ldb       likewise: ldb >= N (row-major) or ldb >= K (TCM_B_COLMAJOR).
+ *   C, ldc       output, ldc >= N; f32 for float types, int32 for int8.
+ *                C must not overlap A, B or bias.
+ *   dtype        one element type above, optionally or-ed with layout flags.
+ *   bias         device vector of N elements, read only with TCM_EPI_BIAS.
+ *   epilogue     TCM_EPI_* flags.
+ *   stream       hipStream_t as void* (NULL: null stream).
+ *
+ * Any alignment and any leading dimension is served; aligned, 16-byte
+ * multiple layouts take the fast path.
+ * Returns TCM_OK once the work is enqueued; TCM_ERR_INVALID_VALUE for
+ * negative sizes, too-small leading dimensions, a NULL operand with a
+ * non-empty extent, unknown dtype/flags/epilogue, TCM_EPI_BIAS with a NULL
+ * bias, or C overlapping an input; TCM_ERR_ALLOC if the split-k workspace
+ * cannot be allocated; TCM_ERR_HIP on a launch error.
+ */
+int tcm_gemm(int64_t M, int64_t N, int64_t K,
+             const void* A, int64_t lda,
+             const void* B, int64_t ldb,
+             void* C, int64_t ldc,
+             int dtype, const void* bias, int epilogue,
+             void* stream);
+
+/* Text of a status code (static storage; never NULL). */
+const char* tcm_status_string(int status);
+
+/*
+ * tcm_set_option / tcm_get_option -- process-wide tuning switches, for
+ * experiments and tests.  Keys:
+ *   "force_mode"   0 = planner decides, 1 = data-parallel tiles only,
+ *                  2 = split-k (Stream-K) over a persistent grid.
+ *   "force_config" -1 = planner decides, else an index into the tile table
+ *                  (tcm_config_count()); a config that cannot serve the call
+ *                  is ignored.
+ *   "sk_grid"      0 = planner decides, else the persistent grid size for
+ *                  split-k (clamped to the number of co-resident workgroups).
+ *   "generic"      1 = route every call to the generic (any-alignment) kernel.
+ * Unknown keys or out-of-range values: TCM_ERR_INVALID_VALUE.
+ * tcm_get_option returns the value, or -2 for an unknown key.
+ */
+int tcm_set_option(const char* key, int64_t value);
+int64_t tcm_get_option(const char* key);
+
+/* ---- planning (host only, no HIP call) ----------------------------------- */
+typedef struct {
+    int32_t kernel;        /* 0 = generic kernel, 1 = tiled MFMA kernel */
+    int32_t config;        /* tile-table index (tiled kernel) or -1 */
+    int32_t bm, bn, bk;    /* macro tile; bk in elements */
+    int32_t mode;          /* 1 = data-parallel, 2 = Stream-K (+ data-parallel tiles) */
+    int32_t grid;          /* workgroups launched */
+    int64_t tiles;         /* ceil(M/bm) * ceil(N/bn) */
+    int64_t iters_per_tile;/* ceil(K/bk) */
+    int64_t dp_tiles;      /* tiles done whole by one workgroup */
+    int64_t sk_tiles;      /* tiles whose k range is split over workgroups */
+    int64_t workspace_bytes; /* split-k workspace the call needs */
+} tcm_plan_info;
+
+/*
+ * tcm_plan -- the plan tcm_gemm would use for this problem (same arguments
+ * minus the pointers; `aligned` says whether A, B, C, bias would be 16-byte
+ * aligned).  Pure host computation.  Returns TCM_OK or TCM_ERR_INVALID_VALUE.
+ */
+int tcm_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+             int dtype, int epilogue, int aligned, tcm_plan_info* out);
+
+/* Number of rows of the tile table, and row i as (bm, bn, bk, waves). */
+int tcm_config_count(void);
+int tcm_config_info(int index, int dtype, int32_t* bm, int32_t* bn, int32_t* bk, int32_t* waves);
+
+/*
+ * tcm_streamk_range -- the k-iteration range [begin, end) that workgroup
+ * `wg` of a Stream-K grid of `grid` workgroups owns over `sk_tiles` tiles of
+ * `iters_per_tile` iterations (even split of the total).  Host mirror of the
+ * device partition, for tests.
+ */
+int tcm_streamk_range(int64_t sk_tiles, int64_t iters_per_tile, int32_t grid, int32_t wg,
+                      int64_t* begin, int64_t* end);
+
+/* Describe the last plan tcm_gemm launched on this thread into buf (NUL-
+ * terminated, truncated to len).  Returns the full length. */
+int tcm_last_plan(char* buf, int64_t len);
+
+/* Free every cached split-k workspace (waits for their streams first). */
+void tcm_release_workspace(void);
+
+/* Library version string. */
+const char* tcm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TCM_H */

@@ -1,0 +1,197 @@
+"""tensor_core_mixed_amd -- MI355X (gfx950) dense GEMM engine, Python binding.
+
+The engine is the C-ABI library ``_build/libtcm.so`` (declared in
+``include/tcm.h``); every step of the product runs in its HIP kernels.  This
+module only marshals arguments: the ``tcm_*`` functions take and return
+exactly what the C functions do (device pointers as Python ints), and
+``gemm`` turns torch tensors into those arguments.  There is no fallback:
+if the library is missing, importing the binding's functions raises.
+
+Build the library with ``python -m tensor_core_mixed_amd.build``.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "_build", "libtcm.so")
+
+# element types and flags (include/tcm.h)
+TCM_F16_F32, TCM_BF16_F32, TCM_F32_F32, TCM_I8_I32 = 0, 1, 2, 3
+TCM_A_COLMAJOR, TCM_B_COLMAJOR = 1 << 8, 1 << 9
+TCM_EPI_NONE, TCM_EPI_BIAS, TCM_EPI_RELU, TCM_EPI_BIAS_RELU = 0, 1, 2, 3
+TCM_OK, TCM_ERR_INVALID_VALUE, TCM_ERR_NOT_SUPPORTED, TCM_ERR_HIP, TCM_ERR_ALLOC = 0, 1, 2, 3, 4
+
+
+class TcmError(RuntimeError):
+    def __init__(self, status, what=""):
+        self.status = status
+        super().__init__(f"{what}: {tcm_status_string(status)}" if what else tcm_status_string(status))
+
+
+class _PlanInfo(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("config", ctypes.c_int32), ("bm", ctypes.c_int32),
+                ("bn", ctypes.c_int32), ("bk", ctypes.c_int32), ("mode", ctypes.c_int32), ("grid", ctypes.c_int32),
+                ("tiles", ctypes.c_int64), ("iters_per_tile", ctypes.c_int64), ("dp_tiles", ctypes.c_int64),
+                ("sk_tiles", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libtcm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libtcm.so not found at {LIB_PATH}; build it with "
+                               "`python -m tensor_core_mixed_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+        L.tcm_gemm.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, vp, ci, vp]
+        L.tcm_gemm.restype = ci
+        L.tcm_status_string.argtypes = [ci]
+        L.tcm_status_string.restype = ctypes.c_char_p
+        L.tcm_set_option.argtypes = [ctypes.c_char_p, i64]
+        L.tcm_set_option.restype = ci
+        L.tcm_get_option.argtypes = [ctypes.c_char_p]
+        L.tcm_get_option.restype = i64
+        L.tcm_plan.argtypes = [i64, i64, i64, i64, i64, i64, ci, ci, ci, ctypes.POINTER(_PlanInfo)]
+        L.tcm_plan.restype = ci
+        L.tcm_config_count.restype = ci
+        L.tcm_config_info.argtypes = [ci, ci] + [ctypes.POINTER(ctypes.c_int32)] * 4
+        L.tcm_config_info.restype = ci
+        L.tcm_streamk_range.argtypes = [i64, i64, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.POINTER(i64), ctypes.POINTER(i64)]
+        L.tcm_streamk_range.restype = ci
+        L.tcm_last_plan.argtypes = [ctypes.c_char_p, i64]
+        L.tcm_last_plan.restype = ci
+        L.tcm_release_workspace.restype = None
+        L.tcm_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+# ---------------------------------------------------------------- C ABI mirror
+
+def tcm_gemm(M, N, K, A, lda, B, ldb, C, ldc, dtype, bias, epilogue, stream):
+    """C = epi(bias + A.B); pointers are device addresses (ints), stream a
+    hipStream_t handle (int) or None.  Returns the tcm status code."""
+    return lib().tcm_gemm(M, N, K, A, lda, B, ldb, C, ldc, dtype, bias, epilogue, stream)
+
+
+def tcm_status_string(status):
+    return lib().tcm_status_string(status).decode()
+
+
+def tcm_set_option(key, value):
+    return lib().tcm_set_option(key.encode(), int(value))
+
+
+def tcm_get_option(key):
+    return lib().tcm_get_option(key.encode())
+
+
+def tcm_plan(M, N, K, lda, ldb, ldc, dtype, epilogue=0, aligned=True):
+    """The plan tcm_gemm would use (host-only query) as a dict."""
+    info = _PlanInfo()
+    st = lib().tcm_plan(M, N, K, lda, ldb, ldc, dtype, epilogue, int(aligned), ctypes.byref(info))
+    if st != TCM_OK:
+        raise TcmError(st, "tcm_plan")
+    return {f: getattr(info, f) for f, _ in _PlanInfo._fields_}
+
+
+def tcm_config_count():
+    return lib().tcm_config_count()
+
+
+def tcm_config_info(index, dtype):
+    v = [ctypes.c_int32() for _ in range(4)]
+    st = lib().tcm_config_info(index, dtype, *[ctypes.byref(x) for x in v])
+    if st != TCM_OK:
+        raise TcmError(st, "tcm_config_info")
+    return tuple(x.value for x in v)
+
+
+def tcm_streamk_range(sk_tiles, iters_per_tile, grid, wg):
+    b, e = ctypes.c_int64(), ctypes.c_int64()
+    st = lib().tcm_streamk_range(sk_tiles, iters_per_tile, grid, wg, ctypes.byref(b), ctypes.byref(e))
+    if st != TCM_OK:
+        raise TcmError(st, "tcm_streamk_range")
+    return b.value, e.value
+
+
+def tcm_last_plan():
+    n = lib().tcm_last_plan(None, 0)
+    buf = ctypes.create_string_buffer(n + 1)
+    lib().tcm_last_plan(buf, n + 1)
+    return buf.value.decode()
+
+
+def tcm_release_workspace():
+    lib().tcm_release_workspace()
+
+
+def tcm_version():
+    return lib().tcm_version().decode()
+
+
+# ---------------------------------------------------------------- torch convenience
+
+def _torch_dtype_code(t):
+    import torch
+    codes = {torch.float16: TCM_F16_F32, torch.bfloat16: TCM_BF16_F32, torch.float32: TCM_F32_F32,
+             torch.int8: TCM_I8_I32}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported operand dtype {t.dtype}")
+    return codes[t.dtype]
+
+
+def _layout(t, name):
+    """(leading dimension, column-major?) of a 2-D view with one unit stride."""
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    r, c = t.shape
+    s0, s1 = t.stride()
+    if s1 == 1 and (r <= 1 or s0 >= max(c, 1)):
+        return max(s0, c, 1), False
+    if s0 == 1 and (c <= 1 or s1 >= max(r, 1)):
+        return max(s1, r, 1), True
+    raise ValueError(f"{name} needs one unit stride (row- or column-major view)")
+
+
+def gemm(A, B, C=None, bias=None, relu=False, stream=None):
+    """C = relu?(A @ B + bias) on the GPU via tcm_gemm.
+
+    A: (M, K) and B: (K, N) CUDA tensors of one type (float16, bfloat16,
+    float32 or int8), each a row- or column-major view (transposed views
+    select the layout flags).  C: optional (M, N) row-major output, float32
+    (int32 for int8).  bias: optional length-N float32 (int32) vector.
+    Runs on `stream` (default: torch's current stream) and returns C."""
+    import torch
+    if A.dtype != B.dtype:
+        raise TypeError("A and B must have the same dtype")
+    code = _torch_dtype_code(A)
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner sizes differ: {K} vs {K2}")
+    lda, a_col = _layout(A, "A")
+    ldb, b_col = _layout(B, "B")
+    out_dtype = torch.int32 if code == TCM_I8_I32 else torch.float32
+    if C is None:
+        C = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    if C.dtype != out_dtype or C.dim() != 2 or tuple(C.shape) != (M, N) or (N > 1 and C.stride(1) != 1):
+        raise ValueError("C must be a row-major (M, N) tensor of the accumulator type")
+    ldc = max(C.stride(0), N, 1)
+    epi = (TCM_EPI_BIAS if bias is not None else 0) | (TCM_EPI_RELU if relu else 0)
+    if bias is not None:
+        if bias.dtype != out_dtype or bias.numel() < N or not bias.is_contiguous():
+            raise ValueError("bias must be a contiguous length-N vector of the accumulator type")
+    dtype = code | (TCM_A_COLMAJOR if a_col else 0) | (TCM_B_COLMAJOR if b_col else 0)
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+    st = tcm_gemm(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc, dtype,
+                  bias.data_ptr() if bias is not None else None, epi, stream)
+    if st != TCM_OK:
+        raise TcmError(st, "tcm_gemm")
+    return C

@@ -1,0 +1,158 @@
+// Generic GEMM kernel: any element alignment, any leading dimension, either
+// layout of A and B.  It keeps the promise that a problem the fast path
+// cannot take still gets the same result, only slower (je-d.tistory.com,
+// the auto-tensorcore note: without the matrix-core rewrite the code is
+// slower but functionally equal).  Structure: 64x64 output tile per
+// workgroup, four waves of 2x2 16x16 MFMA tiles, a 64-byte k-slab per step
+// staged through LDS element by element with bounds checks, bias as the
+// accumulator's initial value, ReLU before the bounds-checked store.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "tcm_internal.h"
+
+namespace tcm {
+namespace {
+
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef int i4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 64;
+constexpr int kSlab = 64;             // bytes of k per step
+constexpr int kRow = kSlab + 16;      // LDS row pitch (bytes), keeps 16-byte alignment
+
+template <int DT> struct G;
+template <> struct G<F16> { using T = uint16_t; using Acc = f4_t; using AccS = float; };
+template <> struct G<BF16> { using T = uint16_t; using Acc = f4_t; using AccS = float; };
+template <> struct G<F32> { using T = float; using Acc = f4_t; using AccS = float; };
+template <> struct G<I8> { using T = int8_t; using Acc = i4_t; using AccS = int; };
+
+template <int DT>
+__device__ __forceinline__ void mma16(typename G<DT>::Acc& acc, i4_t a, i4_t b) {
+    if constexpr (DT == F16)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, a), __builtin_bit_cast(h8_t, b), acc, 0, 0, 0);
+    else if constexpr (DT == BF16)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf8_t, a), __builtin_bit_cast(bf8_t, b), acc, 0, 0, 0);
+    else if constexpr (DT == I8)
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc, 0, 0, 0);
+    else {
+        // reinterpret the whole vectors, then index (see the tiled kernel:
+        // bit-casting one vector element is mis-folded to element 0)
+        const f4_t af = __builtin_bit_cast(f4_t, a), bf = __builtin_bit_cast(f4_t, b);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(af[e], bf[e], acc, 0, 0, 0);
+    }
+}
+
+// Copy the 64 x slab piece of one operand into LDS as [row][k] (k contiguous).
+// rows index M (for A) or N (for B); `kmajor` says whether the operand is
+// stored with k contiguous (then consecutive threads walk k).
+template <int DT>
+__device__ __forceinline__ void stage(char* lds, const typename G<DT>::T* X, int64_t ld, bool kmajor, int64_t r0,
+                                      int64_t rows, int64_t k0, int64_t K) {
+    using T = typename G<DT>::T;
+    constexpr int ES = sizeof(T);
+    constexpr int BKE = kSlab / ES;
+    for (int idx = threadIdx.x; idx < kTile * BKE; idx += 256) {
+        int r, kk;
+        if (kmajor) { r = idx / BKE; kk = idx % BKE; }
+        else { kk = idx / kTile; r = idx % kTile; }
+        const int64_t gr = r0 + r, gk = k0 + kk;
+        T v = T(0);
+        if (gr < rows && gk < K) v = kmajor ? X[gr * ld + gk] : X[gk * ld + gr];
+        *(T*)(lds + r * kRow + kk * ES) = v;
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void generic_gemm_kernel(GenericArgs a) {
+    using T = typename G<DT>::T;
+    using Acc = typename G<DT>::Acc;
+    using AccS = typename G<DT>::AccS;
+    constexpr int ES = sizeof(T);
+    constexpr int BKE = kSlab / ES;
+    __shared__ __attribute__((aligned(16))) char As[kTile * kRow];
+    __shared__ __attribute__((aligned(16))) char Bs[kTile * kRow];
+
+    const int tm = blockIdx.x / a.tiles_n, tn = blockIdx.x % a.tiles_n;
+    const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int r16 = lane & 15, grp = lane >> 4;
+
+    Acc acc[2][2];
+#pragma unroll
+    for (int fn = 0; fn < 2; ++fn) {
+        AccS v = 0;
+        const int64_t col = n0 + wn * 32 + fn * 16 + r16;
+        if (a.has_bias && col < a.N) v = ((const AccS*)a.bias)[col];
+#pragma unroll
+        for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[fm][fn][r] = v;
+    }
+
+    for (int64_t k0 = 0; k0 < a.K; k0 += BKE) {
+        stage<DT>(As, (const T*)a.A, a.lda, !a.a_col, m0, a.M, k0, a.K);
+        stage<DT>(Bs, (const T*)a.B, a.ldb, (bool)a.b_col, n0, a.N, k0, a.K);
+        __syncthreads();
+        i4_t af[2], bf[2];
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            af[f] = *(const i4_t*)(As + (wm * 32 + f * 16 + r16) * kRow + grp * 16);
+            bf[f] = *(const i4_t*)(Bs + (wn * 32 + f * 16 + r16) * kRow + grp * 16);
+        }
+#pragma unroll
+        for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < 2; ++fn) mma16<DT>(acc[fm][fn], af[fm], bf[fn]);
+        __syncthreads();
+    }
+
+    AccS* C = (AccS*)a.C;
+#pragma unroll
+    for (int fm = 0; fm < 2; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < 2; ++fn) {
+            const int64_t col = n0 + wn * 32 + fn * 16 + r16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t row = m0 + wm * 32 + fm * 16 + 4 * grp + r;
+                AccS v = acc[fm][fn][r];
+                if (a.relu) v = v > (AccS)0 ? v : (AccS)0;
+                if (row < a.M && col < a.N) C[row * a.ldc + col] = v;
+            }
+        }
+}
+
+__global__ void fill_zero_kernel(int* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0;
+}
+
+}  // namespace
+
+int launch_generic(int dtype, const GenericArgs& a, void* stream) {
+    const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
+    hipStream_t s = (hipStream_t)stream;
+    switch (dtype) {
+    case F16: hipLaunchKernelGGL(generic_gemm_kernel<F16>, dim3((unsigned)blocks), dim3(256), 0, s, a); break;
+    case BF16: hipLaunchKernelGGL(generic_gemm_kernel<BF16>, dim3((unsigned)blocks), dim3(256), 0, s, a); break;
+    case F32: hipLaunchKernelGGL(generic_gemm_kernel<F32>, dim3((unsigned)blocks), dim3(256), 0, s, a); break;
+    case I8: hipLaunchKernelGGL(generic_gemm_kernel<I8>, dim3((unsigned)blocks), dim3(256), 0, s, a); break;
+    default: return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
+}
+
+int launch_fill_zero(int* p, int64_t n, void* stream) {
+    if (n <= 0) return 0;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, p, n);
+    return (int)hipGetLastError();
+}
+
+}  // namespace tcm

@@ -1,0 +1,214 @@
+// Planner: tile config + data-parallel / Stream-K choice from a small cost
+// model of one MI355X CU.
+//
+// Work unit: one K-step (128 bytes of every operand row) of one macro tile.
+// A CU spends max(matrix-core time, LDS time, L2 time) on it.  Data-parallel
+// time is the number of full "waves" of tiles times a tile's K-steps; the
+// last, partial wave costs as much as a full one, which is the waste that
+// Stream-K removes by splitting the total K-steps evenly over a persistent
+// grid (leiblog.wang, Stream-K reproduction post: even k split across SMs
+// against wave waste at small shapes), at the price of writing and summing
+// partial tiles.  Problems with tiny M are bound by reading B from HBM; the
+// model floors every estimate at the HBM time of the unique bytes.
+#include "planner.h"
+
+#include <algorithm>
+#include <cmath>
+
+namespace tcm {
+namespace {
+
+constexpr int64_t kOffsetLimit = 0x40000000LL;  // buffer-descriptor range used by the kernels
+constexpr double kLdsBytesPerClk = 200.0;       // measured ds_read_b128 rate per CU
+constexpr double kL2BytesPerClk = 64.0;         // per-CU share of L2 bandwidth
+constexpr double kHbmBytesPerClk = 8.0e12 / 2.4e9;  // whole chip
+constexpr double kStepOverhead = 96.0;          // barrier + wait per K-step
+
+double flops_per_clk(int dt) {
+    switch (dt) {
+    case F16:
+    case BF16: return 4096.0 * 0.92;
+    case I8: return 8192.0 * 0.92;
+    default: return 256.0 * 0.97;
+    }
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+int tile_wg_per_cu(const TileConfig& c) {
+    int by_lds = (160 * 1024) / lds_bytes(c);
+    // four waves per workgroup; 128x128-per-wave accumulators (256 registers)
+    // leave room for one wave per SIMD
+    int by_regs = (c.bm / c.wm) * (c.bn / c.wn) >= 128 * 128 ? 1 : 2;
+    return std::max(1, std::min(by_lds, by_regs));
+}
+
+bool tile_eligible(const Problem& p, const TileConfig& c) {
+    const int es = elem_bytes(p.dtype);
+    const int ce = kChunkBytes / es;
+    if (p.a_col || !p.aligned) return false;
+    if (p.K <= 0 || p.M <= 0 || p.N <= 0) return false;
+    if (p.M >= (1LL << 31) || p.N >= (1LL << 31) || p.K >= (1LL << 31)) return false;
+    if (p.lda >= (1LL << 31) || p.ldb >= (1LL << 31) || p.ldc >= (1LL << 31)) return false;
+    if (p.K % ce || p.lda % ce) return false;
+    if (p.b_col) {
+        if (p.ldb % ce) return false;
+    } else {
+        if (p.N % ce || p.ldb % ce) return false;
+    }
+    // every per-tile byte offset must stay inside the descriptor range
+    if ((int64_t)c.bm * p.lda * es + kStepBytes >= kOffsetLimit) return false;
+    if (p.b_col) {
+        if ((int64_t)c.bn * p.ldb * es + kStepBytes >= kOffsetLimit) return false;
+    } else {
+        if ((int64_t)bk_elems(p.dtype) * p.ldb * es + (int64_t)c.bn * es >= kOffsetLimit) return false;
+    }
+    if ((int64_t)c.bm * p.ldc * 4 + (int64_t)c.bn * 4 >= kOffsetLimit) return false;
+    const int64_t tiles = cdiv(p.M, c.bm) * cdiv(p.N, c.bn);
+    if (tiles >= (1LL << 31)) return false;
+    return true;
+}
+
+void streamk_range(int64_t sk_tiles, int64_t iters, int grid, int wg, int64_t* begin, int64_t* end) {
+    const int64_t W = sk_tiles * iters;
+    *begin = (int64_t)wg * W / grid;
+    *end = (int64_t)(wg + 1) * W / grid;
+}
+
+namespace {
+
+struct Estimate {
+    double cycles;
+    int mode;
+    int grid;
+    int64_t dp_tiles, sk_tiles;
+};
+
+Estimate estimate(const Problem& p, const TileConfig& c, int cus, int force_mode, int sk_grid) {
+    const int dt = p.dtype;
+    const int bke = bk_elems(dt);
+    const int64_t T = cdiv(p.M, c.bm) * cdiv(p.N, c.bn);
+    const int64_t I = cdiv(p.K, bke);
+    const int occ = tile_wg_per_cu(c);
+    const int64_t slots = (int64_t)cus * occ;
+
+    const double mfma = 2.0 * c.bm * c.bn * bke / flops_per_clk(dt);
+    const double lds = ((c.bm + c.bn) * (double)kStepBytes + (double)(c.bm * c.wn + c.bn * c.wm) * kStepBytes) / kLdsBytesPerClk;
+    const double l2 = (c.bm + c.bn) * (double)kStepBytes / kL2BytesPerClk;
+    const double step = std::max(mfma, std::max(lds, l2)) + kStepOverhead;  // per K-step, CU to itself
+    const double tile_store = (double)c.bm * c.bn * 4 / kL2BytesPerClk;
+    const double hbm_floor = ((double)p.M * p.K + (double)p.K * p.N) * elem_bytes(dt) / kHbmBytesPerClk +
+                             (double)p.M * p.N * 4 / kHbmBytesPerClk;
+
+    // data-parallel: waves of `slots` tiles, each wave takes I steps on a CU shared by `occ` workgroups
+    Estimate dp{0, 1, (int)std::min<int64_t>(T, 1LL << 30), T, 0};
+    {
+        const int64_t waves = cdiv(T, slots);
+        const int64_t busy = std::min<int64_t>(T, slots);
+        const double share = (double)std::min<int64_t>(occ, cdiv(busy, cus));  // workgroups per busy CU
+        dp.cycles = std::max(waves * (I * step + tile_store) * share, hbm_floor);
+    }
+    // Stream-K: hybrid of (full waves - 1) data-parallel waves, then an even
+    // split of the remaining tiles' K-steps over the grid
+    Estimate sk{0, 2, 0, 0, 0};
+    {
+        // every workgroup of the grid must own at least one K-step: the
+        // kernel counts a split tile's arrivals as the number of workgroups
+        // between its first and last owner
+        int64_t grid = sk_grid > 0 ? sk_grid : slots;
+        grid = std::max<int64_t>(1, std::min(grid, T * I));
+        const int64_t full = T / grid, rem = T % grid;
+        int64_t dp_tiles = 0;
+        if (full >= 1 && rem != 0) dp_tiles = (full - 1) * grid;
+        else if (rem == 0) dp_tiles = (full - 1) * grid;  // even split: the last wave is Stream-K anyway
+        if (dp_tiles < 0) dp_tiles = 0;
+        const int64_t sk_tiles = T - dp_tiles;
+        const int64_t W = sk_tiles * I;
+        const double per_wg = (double)cdiv(W, grid);
+        const double share = (double)std::min<int64_t>(occ, cdiv(std::min<int64_t>(grid, W), cus));
+        const int64_t dp_waves = dp_tiles / grid;
+        // a split tile costs its writers a partial store and the last arrival
+        // the reads of every segment (about two per tile)
+        const double fixup = (W % grid != 0 || I % std::max<int64_t>(1, W / grid) != 0 || sk_tiles < grid) ? 3.0 * tile_store : 0.0;
+        sk.cycles = std::max(dp_waves * (I * step + tile_store) * share + (per_wg * step + tile_store + fixup) * share, hbm_floor);
+        sk.grid = (int)grid;
+        sk.dp_tiles = dp_tiles;
+        sk.sk_tiles = sk_tiles;
+    }
+    if (force_mode == 1) return dp;
+    if (force_mode == 2) return sk;
+    return sk.cycles < 0.97 * dp.cycles ? sk : dp;
+}
+
+}  // namespace
+
+bool make_plan(const Problem& p, const Options& o, int cus, Plan* out) {
+    Plan pl;
+    if (p.M < 0 || p.N < 0 || p.K < 0) return false;
+    if (p.M == 0 || p.N == 0) {
+        pl.kernel = 0;
+        *out = pl;
+        return true;
+    }
+    if (cus <= 0) cus = kDefaultCUs;
+    int best = -1;
+    Estimate best_e{1e300, 1, 0, 0, 0};
+    if (!o.generic) {
+        for (int c = 0; c < kNumConfigs; ++c) {
+            if (o.force_config >= 0 && c != o.force_config) continue;
+            if (!tile_eligible(p, kConfigs[c])) continue;
+            Estimate e = estimate(p, kConfigs[c], cus, o.force_mode, o.sk_grid);
+            if (e.cycles < best_e.cycles * 0.999) {
+                best = c;
+                best_e = e;
+            }
+        }
+        // a forced config that cannot serve the call falls back to the planner's choice
+        if (best < 0 && o.force_config >= 0) {
+            Options o2 = o;
+            o2.force_config = -1;
+            return make_plan(p, o2, cus, out);
+        }
+    }
+    if (best < 0) {
+        pl.kernel = 1;
+        pl.bm = pl.bn = 64;
+        pl.bk = 64 / elem_bytes(p.dtype);
+        pl.tiles = cdiv(p.M, 64) * cdiv(p.N, 64);
+        pl.iters = cdiv(p.K, pl.bk);
+        pl.mode = 1;
+        pl.grid = (int)std::min<int64_t>(pl.tiles, (1LL << 31) - 1);
+        pl.dp_tiles = pl.tiles;
+        if (pl.tiles >= (1LL << 31)) return false;
+        *out = pl;
+        return true;
+    }
+    const TileConfig& c = kConfigs[best];
+    pl.kernel = 2;
+    pl.config = best;
+    pl.bm = c.bm;
+    pl.bn = c.bn;
+    pl.bk = bk_elems(p.dtype);
+    pl.tiles = cdiv(p.M, c.bm) * cdiv(p.N, c.bn);
+    pl.iters = cdiv(p.K, pl.bk);
+    pl.mode = best_e.mode;
+    pl.est_cycles = best_e.cycles;
+    if (pl.mode == 1) {
+        pl.grid = (int)pl.tiles;
+        pl.dp_tiles = pl.tiles;
+        pl.sk_tiles = 0;
+    } else {
+        pl.grid = best_e.grid;
+        pl.dp_tiles = best_e.dp_tiles;
+        pl.sk_tiles = best_e.sk_tiles;
+        pl.ws_partial_bytes = 2LL * pl.grid * c.bm * c.bn * 4;
+        pl.ws_counters = pl.sk_tiles;
+    }
+    pl.group_m = 4;
+    *out = pl;
+    return true;
+}
+
+}  // namespace tcm

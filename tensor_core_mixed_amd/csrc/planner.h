@@ -1,0 +1,50 @@
+// Planner: which kernel, which tile config, data-parallel or Stream-K, and
+// the launch geometry for one GEMM call.  Pure host code (no HIP calls), so
+// the C ABI can expose it for CPU-side tests.
+#pragma once
+#include <cstdint>
+
+#include "tcm_internal.h"
+
+namespace tcm {
+
+struct Options {
+    int force_mode = 0;     // 0 auto, 1 data-parallel, 2 Stream-K
+    int force_config = -1;  // -1 auto, else tile-table index
+    int sk_grid = 0;        // 0 auto, else persistent grid size
+    int generic = 0;        // 1: always the generic kernel
+};
+
+struct Problem {
+    int64_t M, N, K, lda, ldb, ldc;
+    int dtype;     // element type (low byte of the ABI dtype)
+    bool a_col, b_col;
+    int epilogue;
+    bool aligned;  // every pointer 16-byte aligned
+};
+
+struct Plan {
+    int kernel = 0;   // 0 none (empty problem), 1 generic, 2 tiled
+    int config = -1;
+    int bm = 0, bn = 0, bk = 0;
+    int mode = 1;     // 1 data-parallel, 2 Stream-K (+ data-parallel tiles)
+    int grid = 0;     // Stream-K persistent grid (mode 2) or data-parallel workgroups
+    int64_t tiles = 0, iters = 0, dp_tiles = 0, sk_tiles = 0;
+    int64_t ws_partial_bytes = 0, ws_counters = 0;
+    int group_m = 4;
+    double est_cycles = 0;  // the cost model's estimate (for logs)
+};
+
+// Number of CUs the cost model assumes when no device is queried.
+constexpr int kDefaultCUs = 256;
+
+// Tile kernel eligibility for a config (alignment, strides, 32-bit offsets).
+bool tile_eligible(const Problem& p, const TileConfig& c);
+// Workgroups of a config that fit on one CU (LDS- and register-limited estimate).
+int tile_wg_per_cu(const TileConfig& c);
+// Fill `out` for problem p.  Returns false if p is invalid.
+bool make_plan(const Problem& p, const Options& o, int cus, Plan* out);
+// Stream-K share [begin, end) of workgroup wg (same split the kernel uses).
+void streamk_range(int64_t sk_tiles, int64_t iters, int grid, int wg, int64_t* begin, int64_t* end);
+
+}  // namespace tcm

@@ -1,0 +1,369 @@
+// C ABI of the engine (declared in include/tcm.h): argument checks, the
+// per-(device, stream) Stream-K workspace, and dispatch to the kernels.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+
+#include "../../include/tcm.h"
+#include "planner.h"
+#include "tcm_internal.h"
+
+namespace tcm {
+TileLauncher tile_launcher_f16(int config, bool b_kmajor);
+TileLauncher tile_launcher_bf16(int config, bool b_kmajor);
+TileLauncher tile_launcher_f32(int config, bool b_kmajor);
+TileLauncher tile_launcher_i8(int config, bool b_kmajor);
+
+TileLauncher tile_launcher(int config, int dtype, bool b_kmajor) {
+    switch (dtype) {
+    case F16: return tile_launcher_f16(config, b_kmajor);
+    case BF16: return tile_launcher_bf16(config, b_kmajor);
+    case F32: return tile_launcher_f32(config, b_kmajor);
+    case I8: return tile_launcher_i8(config, b_kmajor);
+    default: return nullptr;
+    }
+}
+
+namespace {
+
+std::mutex g_mu;
+Options g_opts;
+
+struct Workspace {
+    void* partial = nullptr;
+    int64_t partial_bytes = 0;
+    int* counters = nullptr;
+    int64_t n_counters = 0;
+};
+std::map<std::pair<int, void*>, Workspace> g_ws;  // (device, stream) -> workspace
+
+thread_local std::string t_last_plan;
+
+int device_cus(int dev) {
+    static std::map<int, int> cache;
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = cache.find(dev);
+    if (it != cache.end()) return it->second;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = kDefaultCUs;
+    cache[dev] = n;
+    return n;
+}
+
+// Grow (never shrink) the workspace of (dev, stream); counters start at zero
+// and every split tile's last arrival resets its counter, so they stay zero
+// between calls.
+int get_workspace(int dev, void* stream, int64_t partial_bytes, int64_t n_counters, Workspace* out) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    Workspace& w = g_ws[{dev, stream}];
+    if (w.partial_bytes < partial_bytes) {
+        if (w.partial) {
+            if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return TCM_ERR_HIP;
+            (void)hipFree(w.partial);
+            w.partial = nullptr;
+            w.partial_bytes = 0;
+        }
+        if (hipMalloc(&w.partial, (size_t)partial_bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            w.partial = nullptr;
+            return TCM_ERR_ALLOC;
+        }
+        w.partial_bytes = partial_bytes;
+    }
+    if (w.n_counters < n_counters) {
+        if (w.counters) {
+            if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return TCM_ERR_HIP;
+            (void)hipFree(w.counters);
+            w.counters = nullptr;
+            w.n_counters = 0;
+        }
+        if (hipMalloc((void**)&w.counters, (size_t)n_counters * sizeof(int)) != hipSuccess) {
+            (void)hipGetLastError();
+            w.counters = nullptr;
+            return TCM_ERR_ALLOC;
+        }
+        if (launch_fill_zero(w.counters, n_counters, stream) != 0) return TCM_ERR_HIP;
+        w.n_counters = n_counters;
+    }
+    *out = w;
+    return TCM_OK;
+}
+
+bool overlaps(const void* a, int64_t abytes, const void* b, int64_t bbytes) {
+    if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
+    const char* x = (const char*)a;
+    const char* y = (const char*)b;
+    return x < y + bbytes && y < x + abytes;
+}
+
+// extent in elements of a rows x cols matrix with leading dimension ld
+int64_t extent(int64_t rows, int64_t cols, int64_t ld) { return rows == 0 || cols == 0 ? 0 : (rows - 1) * ld + cols; }
+
+std::string describe(const Plan& pl, const Problem& p) {
+    char buf[320];
+    if (pl.kernel == 0) {
+        snprintf(buf, sizeof buf, "empty problem M=%lld N=%lld", (long long)p.M, (long long)p.N);
+    } else if (pl.kernel == 1) {
+        snprintf(buf, sizeof buf, "kernel=generic tile=64x64 tiles=%lld iters=%lld M=%lld N=%lld K=%lld dtype=%d",
+                 (long long)pl.tiles, (long long)pl.iters, (long long)p.M, (long long)p.N, (long long)p.K, p.dtype);
+    } else {
+        snprintf(buf, sizeof buf,
+                 "kernel=tile config=%d tile=%dx%dx%d mode=%s grid=%d tiles=%lld iters=%lld dp_tiles=%lld sk_tiles=%lld "
+                 "M=%lld N=%lld K=%lld dtype=%d b_col=%d est_cycles=%.0f",
+                 pl.config, pl.bm, pl.bn, pl.bk, pl.mode == 1 ? "dp" : "streamk", pl.grid, (long long)pl.tiles,
+                 (long long)pl.iters, (long long)pl.dp_tiles, (long long)pl.sk_tiles, (long long)p.M, (long long)p.N,
+                 (long long)p.K, p.dtype, (int)p.b_col, pl.est_cycles);
+    }
+    return buf;
+}
+
+int check_problem(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype, int epilogue,
+                  Problem* p) {
+    const int dt = dtype & 0xff;
+    const int flags = dtype & ~0xff;
+    if (dt < F16 || dt > I8) return TCM_ERR_INVALID_VALUE;
+    if (flags & ~(TCM_A_COLMAJOR | TCM_B_COLMAJOR)) return TCM_ERR_INVALID_VALUE;
+    if (epilogue < 0 || epilogue > TCM_EPI_BIAS_RELU) return TCM_ERR_INVALID_VALUE;
+    if (M < 0 || N < 0 || K < 0) return TCM_ERR_INVALID_VALUE;
+    const bool a_col = flags & TCM_A_COLMAJOR, b_col = flags & TCM_B_COLMAJOR;
+    if (lda < 1 || lda < (a_col ? M : K)) return TCM_ERR_INVALID_VALUE;
+    if (ldb < 1 || ldb < (b_col ? K : N)) return TCM_ERR_INVALID_VALUE;
+    if (ldc < 1 || ldc < N) return TCM_ERR_INVALID_VALUE;
+    p->M = M;
+    p->N = N;
+    p->K = K;
+    p->lda = lda;
+    p->ldb = ldb;
+    p->ldc = ldc;
+    p->dtype = dt;
+    p->a_col = a_col;
+    p->b_col = b_col;
+    p->epilogue = epilogue;
+    p->aligned = true;
+    return TCM_OK;
+}
+
+}  // namespace
+}  // namespace tcm
+
+using namespace tcm;
+
+extern "C" {
+
+const char* tcm_version(void) { return "tcm 0.1 (gfx950)"; }
+
+const char* tcm_status_string(int status) {
+    switch (status) {
+    case TCM_OK: return "TCM_OK";
+    case TCM_ERR_INVALID_VALUE: return "TCM_ERR_INVALID_VALUE: invalid argument";
+    case TCM_ERR_NOT_SUPPORTED: return "TCM_ERR_NOT_SUPPORTED: request not supported";
+    case TCM_ERR_HIP: return "TCM_ERR_HIP: HIP runtime error";
+    case TCM_ERR_ALLOC: return "TCM_ERR_ALLOC: workspace allocation failed";
+    default: return "unknown tcm status";
+    }
+}
+
+int tcm_set_option(const char* key, int64_t value) {
+    if (!key) return TCM_ERR_INVALID_VALUE;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!strcmp(key, "force_mode")) {
+        if (value < 0 || value > 2) return TCM_ERR_INVALID_VALUE;
+        g_opts.force_mode = (int)value;
+    } else if (!strcmp(key, "force_config")) {
+        if (value < -1 || value >= kNumConfigs) return TCM_ERR_INVALID_VALUE;
+        g_opts.force_config = (int)value;
+    } else if (!strcmp(key, "sk_grid")) {
+        if (value < 0 || value > (1 << 20)) return TCM_ERR_INVALID_VALUE;
+        g_opts.sk_grid = (int)value;
+    } else if (!strcmp(key, "generic")) {
+        if (value < 0 || value > 1) return TCM_ERR_INVALID_VALUE;
+        g_opts.generic = (int)value;
+    } else {
+        return TCM_ERR_INVALID_VALUE;
+    }
+    return TCM_OK;
+}
+
+int64_t tcm_get_option(const char* key) {
+    if (!key) return -2;
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (!strcmp(key, "force_mode")) return g_opts.force_mode;
+    if (!strcmp(key, "force_config")) return g_opts.force_config;
+    if (!strcmp(key, "sk_grid")) return g_opts.sk_grid;
+    if (!strcmp(key, "generic")) return g_opts.generic;
+    return -2;
+}
+
+int tcm_config_count(void) { return kNumConfigs; }
+
+int tcm_config_info(int index, int dtype, int32_t* bm, int32_t* bn, int32_t* bk, int32_t* waves) {
+    const int dt = dtype & 0xff;
+    if (index < 0 || index >= kNumConfigs || dt < F16 || dt > I8) return TCM_ERR_INVALID_VALUE;
+    if (bm) *bm = kConfigs[index].bm;
+    if (bn) *bn = kConfigs[index].bn;
+    if (bk) *bk = bk_elems(dt);
+    if (waves) *waves = kConfigs[index].wm * kConfigs[index].wn;
+    return TCM_OK;
+}
+
+int tcm_streamk_range(int64_t sk_tiles, int64_t iters_per_tile, int32_t grid, int32_t wg, int64_t* begin, int64_t* end) {
+    if (sk_tiles < 0 || iters_per_tile < 1 || grid < 1 || wg < 0 || wg >= grid || !begin || !end) return TCM_ERR_INVALID_VALUE;
+    streamk_range(sk_tiles, iters_per_tile, grid, wg, begin, end);
+    return TCM_OK;
+}
+
+int tcm_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype, int epilogue, int aligned,
+             tcm_plan_info* out) {
+    if (!out) return TCM_ERR_INVALID_VALUE;
+    Problem p;
+    int st = check_problem(M, N, K, lda, ldb, ldc, dtype, epilogue, &p);
+    if (st != TCM_OK) return st;
+    p.aligned = aligned != 0;
+    Options o;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        o = g_opts;
+    }
+    Plan pl;
+    if (!make_plan(p, o, kDefaultCUs, &pl)) return TCM_ERR_INVALID_VALUE;
+    out->kernel = pl.kernel == 2 ? 1 : 0;
+    out->config = pl.config;
+    out->bm = pl.bm;
+    out->bn = pl.bn;
+    out->bk = pl.bk;
+    out->mode = pl.mode;
+    out->grid = pl.grid;
+    out->tiles = pl.tiles;
+    out->iters_per_tile = pl.iters;
+    out->dp_tiles = pl.dp_tiles;
+    out->sk_tiles = pl.sk_tiles;
+    out->workspace_bytes = pl.ws_partial_bytes + pl.ws_counters * (int64_t)sizeof(int);
+    return TCM_OK;
+}
+
+int tcm_last_plan(char* buf, int64_t len) {
+    const std::string& s = t_last_plan;
+    if (buf && len > 0) {
+        int64_t n = std::min<int64_t>(len - 1, (int64_t)s.size());
+        memcpy(buf, s.data(), (size_t)n);
+        buf[n] = 0;
+    }
+    return (int)s.size();
+}
+
+void tcm_release_workspace(void) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (auto& kv : g_ws) {
+        int cur = 0;
+        (void)hipGetDevice(&cur);
+        (void)hipSetDevice(kv.first.first);
+        (void)hipStreamSynchronize((hipStream_t)kv.first.second);
+        if (kv.second.partial) (void)hipFree(kv.second.partial);
+        if (kv.second.counters) (void)hipFree(kv.second.counters);
+        (void)hipSetDevice(cur);
+    }
+    g_ws.clear();
+}
+
+int tcm_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+             int dtype, const void* bias, int epilogue, void* stream) {
+    Problem p;
+    int st = check_problem(M, N, K, lda, ldb, ldc, dtype, epilogue, &p);
+    if (st != TCM_OK) return st;
+    if (M == 0 || N == 0) {
+        t_last_plan = "empty problem";
+        return TCM_OK;
+    }
+    const int es = elem_bytes(p.dtype);
+    const int64_t a_ext = extent(p.a_col ? K : M, p.a_col ? M : K, lda) * es;
+    const int64_t b_ext = extent(p.b_col ? N : K, p.b_col ? K : N, ldb) * es;
+    const int64_t c_ext = extent(M, N, ldc) * 4;
+    const bool use_bias = epilogue & TCM_EPI_BIAS;
+    if (!C) return TCM_ERR_INVALID_VALUE;
+    if (a_ext > 0 && !A) return TCM_ERR_INVALID_VALUE;
+    if (b_ext > 0 && !B) return TCM_ERR_INVALID_VALUE;
+    if (use_bias && !bias) return TCM_ERR_INVALID_VALUE;
+    // pointers must be aligned to their element
+    if (((uintptr_t)A % es) || ((uintptr_t)B % es) || ((uintptr_t)C % 4) || (use_bias && ((uintptr_t)bias % 4)))
+        return TCM_ERR_INVALID_VALUE;
+    if (overlaps(C, c_ext, A, a_ext) || overlaps(C, c_ext, B, b_ext) || (use_bias && overlaps(C, c_ext, bias, N * 4)))
+        return TCM_ERR_INVALID_VALUE;
+    p.aligned = ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) && ((uintptr_t)C % 16 == 0) &&
+                (!use_bias || (uintptr_t)bias % 16 == 0);
+
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return TCM_ERR_HIP;
+    }
+    Options o;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        o = g_opts;
+    }
+    Plan pl;
+    if (!make_plan(p, o, device_cus(dev), &pl)) return TCM_ERR_INVALID_VALUE;
+    t_last_plan = describe(pl, p);
+
+    if (pl.kernel == 1) {
+        GenericArgs g;
+        g.A = A;
+        g.B = B;
+        g.C = C;
+        g.bias = use_bias ? bias : nullptr;
+        g.M = M;
+        g.N = N;
+        g.K = K;
+        g.lda = lda;
+        g.ldb = ldb;
+        g.ldc = ldc;
+        g.a_col = p.a_col;
+        g.b_col = p.b_col;
+        g.relu = (epilogue & TCM_EPI_RELU) != 0;
+        g.has_bias = use_bias;
+        g.tiles_m = (int)((M + 63) / 64);
+        g.tiles_n = (int)((N + 63) / 64);
+        return launch_generic(p.dtype, g, stream) == 0 ? TCM_OK : TCM_ERR_HIP;
+    }
+
+    TileArgs a;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.bias = use_bias ? bias : nullptr;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.lda = (int)lda;
+    a.ldb = (int)ldb;
+    a.ldc = (int)ldc;
+    a.relu = (epilogue & TCM_EPI_RELU) != 0;
+    a.has_bias = use_bias;
+    a.tiles_m = (int)((M + pl.bm - 1) / pl.bm);
+    a.tiles_n = (int)((N + pl.bn - 1) / pl.bn);
+    a.iters = (int)pl.iters;
+    a.dp_tiles = (int)pl.dp_tiles;
+    a.sk_tiles = (int)pl.sk_tiles;
+    a.grid = pl.grid;
+    a.group_m = pl.group_m;
+    a.ws_partial = nullptr;
+    a.ws_counter = nullptr;
+    if (pl.mode == 2 && pl.sk_tiles > 0) {
+        Workspace w;
+        int ws = get_workspace(dev, stream, pl.ws_partial_bytes, pl.ws_counters, &w);
+        if (ws != TCM_OK) return ws;
+        a.ws_partial = (float*)w.partial;
+        a.ws_counter = w.counters;
+    }
+    TileLauncher launch = tile_launcher(pl.config, p.dtype, p.b_col);
+    if (!launch) return TCM_ERR_NOT_SUPPORTED;
+    return launch(a, stream) == 0 ? TCM_OK : TCM_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,3 @@
+// Tiled-kernel instances for i8 inputs.
+#include "tile_instances.h"
+TCM_TILE_TU(tcm::I8, i8)

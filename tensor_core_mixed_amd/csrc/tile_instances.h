@@ -1,0 +1,24 @@
+// Instantiates the tiled kernel for every (tile config, B layout) of one
+// element type; each element type is compiled in its own translation unit.
+#pragma once
+#include "tile_kernel.h"
+
+namespace tcm {
+
+template <int DT>
+TileLauncher pick_tile(int config, bool b_kmajor) {
+    switch (config) {
+    case 0: return b_kmajor ? &launch_tile<DT, 0, true> : &launch_tile<DT, 0, false>;
+    case 1: return b_kmajor ? &launch_tile<DT, 1, true> : &launch_tile<DT, 1, false>;
+    case 2: return b_kmajor ? &launch_tile<DT, 2, true> : &launch_tile<DT, 2, false>;
+    case 3: return b_kmajor ? &launch_tile<DT, 3, true> : &launch_tile<DT, 3, false>;
+    default: return nullptr;
+    }
+}
+
+}  // namespace tcm
+
+#define TCM_TILE_TU(DT, NAME)                                                                          \
+    namespace tcm {                                                                                    \
+    TileLauncher tile_launcher_##NAME(int config, bool b_kmajor) { return pick_tile<DT>(config, b_kmajor); } \
+    }

@@ -1,0 +1,548 @@
+// Tiled MFMA GEMM kernel for gfx950 (CDNA4), one template for all element
+// types.  What each part implements, with the passage that describes it:
+//
+//  * Tiling + loop order (kimm240.github.io/tvm, GEMM optimisation Step 2):
+//    C is cut into BM x BN macro tiles, one per workgroup; each of the
+//    WM x WN waves owns a (BM/WM) x (BN/WN) block of 32x32 MFMA tiles whose
+//    accumulators stay in registers for the whole k loop.
+//  * Cooperative staging through LDS (same page, Step 3): all lanes of the
+//    workgroup copy the A and B k-slabs of one K-step into LDS with 16-byte
+//    direct-to-LDS buffer loads (one lane = one 16-byte chunk; a wave
+//    instruction fills 1 KiB of LDS), coalesced along the contiguous
+//    dimension of each operand.
+//  * Bank-conflict-free LDS layout (leiblog.wang, the padding/bank-conflict
+//    post and the storage_align answer): instead of padding rows, the
+//    16-byte chunk index of every row is XOR-ed with a function of the row,
+//    chosen so that the 64 lanes of each fragment read hit distinct banks
+//    on gfx950's LDS; no LDS is spent on padding.
+//  * Vectorised fragment loads (Step 4): one ds_read_b128 per lane per
+//    fragment for k-contiguous operands; for operands stored n-contiguous
+//    (row-major B) the gfx950 transpose reads ds_read_b64_tr_b16/_b8 build
+//    the k-contiguous fragment directly from the [k][n] LDS tile.
+//  * Software pipelining (Step 5): two LDS stages; the loads of K-step k+1
+//    are in flight while the MFMAs of step k run.
+//  * Unrolled inner loop of matrix-core ops (Step 6; Tensor Core notes on
+//    je-d.tistory.com: mixed-precision multiply-accumulate per warp-level
+//    operation): v_mfma_f32_32x32x16_{f16,bf16}, v_mfma_i32_32x32x32_i8,
+//    v_mfma_f32_32x32x2_f32, fully unrolled over the K-step.
+//  * Bias as the reduction's initial value, ReLU before the store
+//    (FuseReductionEpilogue posts; Conv2d + Bias + ReLU fusion post).
+//  * Stream-K (leiblog.wang, Stream-K reproduction post): the k-iterations
+//    of the split tiles are divided evenly over a persistent grid; a tile
+//    cut between workgroups is finished by whichever of them arrives last,
+//    summing the partial tiles in workgroup order (deterministic result).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "tcm_internal.h"
+
+namespace tcm {
+
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
+typedef float f16v_t __attribute__((ext_vector_type(16)));
+typedef int i16v_t __attribute__((ext_vector_type(16)));
+typedef int i4_t __attribute__((ext_vector_type(4)));
+typedef int i2_t __attribute__((ext_vector_type(2)));
+typedef short s4_t __attribute__((ext_vector_type(4)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+// Offset that lies beyond every buffer descriptor's range: loads through it
+// return zeros (used for rows/columns/k beyond the matrix).
+constexpr unsigned kOOB = 0x40000000u;
+// gfx9 buffer descriptor word 3 for raw (untyped, unswizzled) dword access.
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)kOOB, kRsrcWord3);
+}
+
+// XOR swizzles of the 16-byte chunk index (see the header comment).
+// k-contiguous rows of 128 bytes (8 chunks), read as 32x32 fragments: rows
+// r..r+31 at one chunk column; measured conflict-free on gfx950.
+__device__ __forceinline__ int swz_k(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+template <int DT>
+struct Elem;
+template <>
+struct Elem<F16> {
+    static constexpr int bytes = 2;
+};
+template <>
+struct Elem<BF16> {
+    static constexpr int bytes = 2;
+};
+template <>
+struct Elem<F32> {
+    static constexpr int bytes = 4;
+};
+template <>
+struct Elem<I8> {
+    static constexpr int bytes = 1;
+};
+
+// n-contiguous [k][n] tiles (row-major B): swizzle as a function of the k row,
+// so the rows that one transpose read touches land on distinct banks.  CPR
+// (chunks per k row) bounds the result so the chunk stays inside its row.
+template <int DT, int CPR>
+__device__ __forceinline__ int swz_mn(int k) {
+    int s;
+    if constexpr (DT == I8) s = 2 * (k & 7);               // 8 rows x 16 B per 16-lane group
+    else if constexpr (DT == F32) s = 8 * ((k >> 2) & 1);  // two k rows per wave read
+    else s = 4 * (k & 3);                                  // 4 rows x 32 B per 16-lane group
+    return s & (CPR - 1);
+}
+
+template <int DT, int CFG, bool B_KMAJ>
+struct TileKernel {
+    static constexpr TileConfig cfg = kConfigs[CFG];
+    static constexpr int BM = cfg.bm, BN = cfg.bn, WM = cfg.wm, WN = cfg.wn;
+    static constexpr int NW = WM * WN, NT = NW * 64;
+    static constexpr int ES = Elem<DT>::bytes;
+    static constexpr int CE = kChunkBytes / ES;      // elements per 16-byte chunk
+    static constexpr int BKE = kStepBytes / ES;      // elements per K-step
+    static constexpr int TM = BM / WM, TN = BN / WN; // wave tile
+    static constexpr int FM = TM / 32, FN = TN / 32; // 32x32 MFMA tiles per wave
+    static constexpr int A_BYTES = BM * kStepBytes, B_BYTES = BN * kStepBytes;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static constexpr int LDS = 2 * STAGE;
+    static constexpr int IA = BM / (8 * NW);         // DMA instructions per wave per stage (A)
+    static constexpr int IB = BN / (8 * NW);         // (B)
+    static constexpr int B_CPR = BN * ES / kChunkBytes;  // chunks per [k] row of an n-contiguous B tile
+    static_assert((B_CPR & (B_CPR - 1)) == 0, "chunk count per row must be a power of two");
+    static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile rows must fill whole wave DMA instructions");
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32x32");
+    static_assert(LDS <= 160 * 1024, "LDS budget of one CU");
+
+    using Acc = typename std::conditional<DT == I8, i16v_t, f16v_t>::type;
+    using AccS = typename std::conditional<DT == I8, int, float>::type;
+
+    // ---------------------------------------------------------------- DMA
+    // Lane `lane` of wave `wave` fills LDS chunk slot p = (j*NW + wave)*64 + lane
+    // with its j-th copy instruction of a stage (a wave instruction fills 1 KiB
+    // of consecutive LDS).  The per-lane byte offsets of all IA + IB chunks are
+    // computed once per tile, with rows/columns outside the matrix already
+    // replaced by the out-of-range offset; only the k tail is masked per step.
+    struct Dma {
+        unsigned a_off[IA];
+        unsigned b_off[IB];
+        int a_k[2];   // k (within the K-step) of the lane's A chunk for even / odd j
+        int b_k[2];   // B: k within the step (k-contiguous), or the k row of j = 0, 1 (n-contiguous)
+    };
+    static constexpr int B_RPI = B_KMAJ ? 8 : 64 / B_CPR;  // k rows per instruction (n-contiguous B)
+
+    __device__ __forceinline__ static void dma_setup(Dma& d, const TileArgs& a, int m0, int n0, int wave, int lane) {
+        const int mrem = a.M - m0, nrem = a.N - n0;
+#pragma unroll
+        for (int j = 0; j < IA; ++j) {
+            const int p = (j * NW + wave) * 64 + lane;
+            const int r = p >> 3, c = (p & 7) ^ swz_k(r);
+            d.a_off[j] = r < mrem ? (unsigned)(r * a.lda + c * CE) * ES : kOOB;
+            if (j < 2) d.a_k[j] = c * CE;
+        }
+#pragma unroll
+        for (int j = 0; j < IB; ++j) {
+            const int p = (j * NW + wave) * 64 + lane;
+            if constexpr (B_KMAJ) {
+                const int r = p >> 3, c = (p & 7) ^ swz_k(r);
+                d.b_off[j] = r < nrem ? (unsigned)(r * a.ldb + c * CE) * ES : kOOB;
+                if (j < 2) d.b_k[j] = c * CE;
+            } else {
+                const int kr = p / B_CPR, c = (p % B_CPR) ^ swz_mn<DT, B_CPR>(kr);
+                d.b_off[j] = c * CE < nrem ? (unsigned)(kr * a.ldb + c * CE) * ES : kOOB;
+                if (j < 2) d.b_k[j] = kr;
+            }
+        }
+    }
+
+    // Issue the copies of K-step kt of tile (m0, n0) into LDS stage `st`.
+    // `tail`: the step reaches past K, so chunks at k >= K read as zeros.
+    __device__ __forceinline__ static void dma_issue(const Dma& d, const TileArgs& a, lds_char* smem, int st, int kt,
+                                                     int m0, int n0, int wave, bool tail) {
+        const int k0 = kt * BKE;
+        const int krem = a.K - k0;
+        const __amdgpu_buffer_rsrc_t ra = make_rsrc((const char*)a.A + ((int64_t)m0 * a.lda + k0) * ES);
+        lds_char* la = smem + st * STAGE;
+#pragma unroll
+        for (int j = 0; j < IA; ++j) {
+            unsigned off = d.a_off[j];
+            if (tail && d.a_k[j & 1] >= krem) off = kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(la + (j * NW + wave) * 1024), 16,
+                                                     off, 0, 0, 0);
+        }
+        const char* bbase;
+        if constexpr (B_KMAJ) bbase = (const char*)a.B + ((int64_t)n0 * a.ldb + k0) * ES;
+        else bbase = (const char*)a.B + ((int64_t)k0 * a.ldb + n0) * ES;
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(bbase);
+        lds_char* lb = smem + st * STAGE + A_BYTES;
+#pragma unroll
+        for (int j = 0; j < IB; ++j) {
+            unsigned off = d.b_off[j];
+            if constexpr (B_KMAJ) {
+                if (tail && d.b_k[j & 1] >= krem) off = kOOB;
+            } else {
+                if (tail && d.b_k[j & 1] + (j >> 1) * (2 * NW * B_RPI) >= krem) off = kOOB;
+            }
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)(lb + (j * NW + wave) * 1024), 16,
+                                                     off, 0, 0, 0);
+        }
+    }
+
+    // ------------------------------------------------------ fragment loads
+    template <typename V>
+    __device__ __forceinline__ static V lds_read16(const lds_char* p) {
+        return *(const __attribute__((address_space(3))) V*)p;
+    }
+
+    // A fragment (k-contiguous): rows r..r+31 of the wave's block, chunk c.
+    __device__ __forceinline__ static i4_t load_a(const lds_char* la, int row, int sub, int h) {
+        int c = 2 * sub + h;
+        return lds_read16<i4_t>(la + row * kStepBytes + ((c ^ swz_k(row)) << 4));
+    }
+    __device__ __forceinline__ static i4_t load_b_kmaj(const lds_char* lb, int row, int sub, int h) {
+        int c = 2 * sub + h;
+        return lds_read16<i4_t>(lb + row * kStepBytes + ((c ^ swz_k(row)) << 4));
+    }
+    // B fragment from an n-contiguous [k][n] tile: the lane's column n and
+    // the 8 (f16/bf16) or 16 (int8) k-values of chunk c = 2*sub + h.
+    __device__ __forceinline__ static i4_t load_b_mn(const lds_char* lb, int ncol0, int sub, int lane) {
+        constexpr int RB = BN * ES;  // bytes per k row
+        const int g = lane >> 4, t = lane & 15, h = g >> 1;
+        const int c = 2 * sub + h;
+        i4_t out;
+        if constexpr (DT == I8) {
+            const int n = ncol0 + 16 * (g & 1) + 8 * (t & 1);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int k = 16 * c + 8 * q + (t >> 1);
+                const lds_char* p = lb + k * RB + (((n >> 4) ^ swz_mn<DT, B_CPR>(k)) << 4) + (n & 15);
+                i2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i2_t*)p);
+                out[2 * q] = v[0];
+                out[2 * q + 1] = v[1];
+            }
+        } else {
+            const int n = ncol0 + 16 * (g & 1) + 4 * (t & 3);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int k = 8 * c + 4 * q + (t >> 2);
+                const lds_char* p = lb + k * RB + (((n >> 3) ^ swz_mn<DT, B_CPR>(k)) << 4) + ((n & 7) << 1);
+                s4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4_t*)p);
+                i2_t w = __builtin_bit_cast(i2_t, v);
+                out[2 * q] = w[0];
+                out[2 * q + 1] = w[1];
+            }
+        }
+        return out;
+    }
+    // f32, n-contiguous B: single k-value e of chunk-substep sub.
+    __device__ __forceinline__ static float load_b_mn_f32(const lds_char* lb, int n, int sub, int h, int e) {
+        constexpr int RB = BN * ES;
+        const int k = 8 * sub + 4 * h + e;
+        return *(const __attribute__((address_space(3))) float*)(lb + k * RB + (((n >> 2) ^ swz_mn<DT, B_CPR>(k)) << 4) + ((n & 3) << 2));
+    }
+
+    // ------------------------------------------------------------- MFMA
+    __device__ __forceinline__ static void mma(Acc& acc, i4_t a, i4_t b) {
+        if constexpr (DT == F16)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8_t, a), __builtin_bit_cast(h8_t, b), acc, 0, 0, 0);
+        else if constexpr (DT == BF16)
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf8_t, a), __builtin_bit_cast(bf8_t, b), acc, 0, 0, 0);
+        else if constexpr (DT == I8)
+            acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, acc, 0, 0, 0);
+    }
+    __device__ __forceinline__ static void mma_f32(Acc& acc, float a, float b) {
+        if constexpr (DT == F32) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+    }
+
+    // Operand fragments of one sub-step (a quarter K-step): for every 32-row
+    // block of the wave's A rows and 32-column block of its B columns, the
+    // 16 bytes this lane feeds to the MFMA.
+    struct Frag {
+        i4_t a[FM];
+        i4_t b[FN];
+    };
+
+    __device__ __forceinline__ static void load_frag(Frag& f, const lds_char* smem, int st, int sub, int wm, int wn, int lane) {
+        const lds_char* la = smem + st * STAGE;
+        const lds_char* lb = la + A_BYTES;
+        const int h = lane >> 5, l32 = lane & 31;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) f.a[fm] = load_a(la, wm * TM + fm * 32 + l32, sub, h);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            if constexpr (B_KMAJ) {
+                f.b[fn] = load_b_kmaj(lb, wn * TN + fn * 32 + l32, sub, h);
+            } else if constexpr (DT == F32) {
+                f4_t v;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = load_b_mn_f32(lb, wn * TN + fn * 32 + l32, sub, h, e);
+                f.b[fn] = __builtin_bit_cast(i4_t, v);
+            } else {
+                f.b[fn] = load_b_mn(lb, wn * TN + fn * 32, sub, lane);
+            }
+        }
+    }
+
+    __device__ __forceinline__ static void mma_frag(Acc (&acc)[FM][FN], const Frag& f) {
+        if constexpr (DT == F32) {
+            // Reinterpret whole vectors, then index: this compiler mis-folds
+            // __builtin_bit_cast applied to a single vector element (it always
+            // yields element 0).
+            f4_t fa[FM], fb[FN];
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) fa[fm] = __builtin_bit_cast(f4_t, f.a[fm]);
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) fb[fn] = __builtin_bit_cast(f4_t, f.b[fn]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn) mma_f32(acc[fm][fn], fa[fm][e], fb[fn][e]);
+        } else {
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) mma(acc[fm][fn], f.a[fm], f.b[fn]);
+        }
+    }
+
+    // ------------------------------------------------------- tile order
+    // Tile t -> (tm, tn).  Workgroups are dealt to the 8 XCDs round-robin by
+    // id, so ids t, t+8, t+16, ... share one XCD's L2: renumber so that each
+    // XCD gets a contiguous run of tiles, then walk runs in groups of
+    // group_m tile rows so that concurrently running tiles of one XCD share
+    // A rows and B columns.
+    __device__ __forceinline__ static void tile_coords(int t, const TileArgs& a, int& tm, int& tn) {
+        const int T = a.tiles_m * a.tiles_n;
+        const int q = T >> 3, r = T & 7, x = t & 7, local = t >> 3;
+        const int nt = x * q + min(x, r) + local;
+        const int gsz = a.group_m * a.tiles_n;
+        const int g = nt / gsz;
+        const int first_m = g * a.group_m;
+        const int gm = min(a.tiles_m - first_m, a.group_m);
+        const int inner = nt - g * gsz;
+        tm = first_m + inner % gm;
+        tn = inner / gm;
+    }
+
+    // ------------------------------------------------------- epilogue
+    __device__ __forceinline__ static void init_acc(Acc (&acc)[FM][FN], const TileArgs& a, bool seed_bias, int n0, int wn, int lane) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            AccS v = 0;
+            if (seed_bias) {
+                const int col = n0 + wn * TN + fn * 32 + (lane & 31);
+                if (col < a.N) v = ((const AccS*)a.bias)[col];
+            }
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[fm][fn][r] = v;
+        }
+    }
+
+    // 32x32 accumulator layout: lane l, register r holds row
+    // 8*(r/4) + 4*(l/32) + r%4 and column l%32 of its MFMA tile.  Stores go
+    // through a buffer descriptor whose range ends at row M, with columns
+    // >= N given the out-of-range offset: the hardware drops those writes.
+    __device__ __forceinline__ static void store_tile(const Acc (&acc)[FM][FN], const TileArgs& a, int m0, int n0, int wm, int wn, int lane) {
+        const int row0 = wm * TM + 4 * (lane >> 5);
+        const int mrem = a.M - m0;
+        const int64_t bytes = (int64_t)mrem * a.ldc * 4 - (int64_t)n0 * 4;  // from (m0, n0) to the end of row M-1's stride
+        const int nrec = bytes < (int64_t)kOOB ? (int)bytes : (int)kOOB;
+        const __amdgpu_buffer_rsrc_t rc =
+            __builtin_amdgcn_make_buffer_rsrc((char*)a.C + ((int64_t)m0 * a.ldc + n0) * 4, (short)0, nrec, kRsrcWord3);
+        const bool relu = a.relu;
+        unsigned coff[FN];
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            const int col = wn * TN + fn * 32 + (lane & 31);
+            coff[fn] = n0 + col < a.N ? (unsigned)(row0 * a.ldc + col) * 4 : kOOB;
+        }
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const unsigned roff = (unsigned)((fm * 32 + 8 * (r >> 2) + (r & 3)) * a.ldc) * 4;
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                    AccS v = acc[fm][fn][r];
+                    if (relu) v = v > (AccS)0 ? v : (AccS)0;
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), rc, coff[fn] + roff, 0, 0);
+                }
+            }
+    }
+
+    // Partial tiles live in the workspace in register order: element
+    // (wave, fm, fn, r, lane), so every store/load is 256 contiguous bytes.
+    __device__ __forceinline__ static AccS* partial_slot(const TileArgs& a, int slot) {
+        return (AccS*)a.ws_partial + (int64_t)slot * BM * BN;
+    }
+    __device__ __forceinline__ static void store_partial(const Acc (&acc)[FM][FN], AccS* p, int wave, int lane) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) p[(((wave * FM + fm) * FN + fn) * 16 + r) * 64 + lane] = acc[fm][fn][r];
+    }
+    __device__ __forceinline__ static void add_partial(Acc (&acc)[FM][FN], const AccS* p, int wave, int lane, bool first) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    AccS v = p[(((wave * FM + fm) * FN + fn) * 16 + r) * 64 + lane];
+                    acc[fm][fn][r] = first ? v : acc[fm][fn][r] + v;
+                }
+    }
+
+    // ------------------------------------------------------- main loop
+    // Accumulate K-steps [k_lo, k_hi) of tile (m0, n0) into acc.  Schedule of
+    // one K-step kt (stage kt&1): MFMAs of sub-steps 0..2, each overlapping the
+    // fragment loads of the next sub-step; then wait for this wave's copies
+    // of step kt+1 and barrier; issue the copies of step kt+2 into the stage
+    // just drained and load sub-step 0 of step kt+1; then the MFMAs of sub-step
+    // 3 cover that latency.
+    __device__ __forceinline__ static void mainloop(Acc (&acc)[FM][FN], const TileArgs& a, lds_char* smem, int m0, int n0,
+                                                    int k_lo, int k_hi, int wave, int lane) {
+        const int wm = wave / WN, wn = wave % WN;
+        const int last = a.iters - 1;
+        const bool ktail = (a.K % BKE) != 0;
+        Dma d;
+        dma_setup(d, a, m0, n0, wave, lane);
+        __syncthreads();  // the previous tile's readers are done with both stages
+        if (k_lo >= k_hi) return;
+        dma_issue(d, a, smem, 0, k_lo, m0, n0, wave, ktail && k_lo == last);
+        if (k_lo + 1 < k_hi) dma_issue(d, a, smem, 1, k_lo + 1, m0, n0, wave, ktail && k_lo + 1 == last);
+        if (k_lo + 1 < k_hi) {
+            if constexpr (IA + IB == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+            else if constexpr (IA + IB == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+            else if constexpr (IA + IB == 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+            else if constexpr (IA + IB == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        __syncthreads();
+        Frag f[2];
+        load_frag(f[0], smem, 0, 0, wm, wn, lane);
+        for (int kt = k_lo; kt < k_hi; ++kt) {
+            const int st = (kt - k_lo) & 1;
+            load_frag(f[1], smem, st, 1, wm, wn, lane);
+            mma_frag(acc, f[0]);
+            load_frag(f[0], smem, st, 2, wm, wn, lane);
+            mma_frag(acc, f[1]);
+            load_frag(f[1], smem, st, 3, wm, wn, lane);
+            mma_frag(acc, f[0]);
+            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+            __syncthreads();  // step kt+1 is in LDS everywhere; stage st is drained
+            if (kt + 2 < k_hi) dma_issue(d, a, smem, st, kt + 2, m0, n0, wave, ktail && kt + 2 == last);
+            if (kt + 1 < k_hi) load_frag(f[0], smem, st ^ 1, 0, wm, wn, lane);
+            mma_frag(acc, f[1]);
+        }
+    }
+
+    // Data-parallel kernel: workgroup b computes tile b (in L2-aware order).
+    __device__ __forceinline__ static void run_dp(const TileArgs& a) {
+        __shared__ __attribute__((aligned(1024))) char smem_raw[LDS];
+        lds_char* smem = (lds_char*)smem_raw;
+        const int tid = threadIdx.x, lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: DMA bases go to M0
+        const int wm = wave / WN, wn = wave % WN;
+        Acc acc[FM][FN];
+        int tm, tn;
+        tile_coords(blockIdx.x, a, tm, tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+        init_acc(acc, a, a.has_bias, n0, wn, lane);
+        mainloop(acc, a, smem, m0, n0, 0, a.iters, wave, lane);
+        store_tile(acc, a, m0, n0, wm, wn, lane);
+    }
+
+    // Stream-K kernel: the k-iterations of tiles [dp_tiles, dp_tiles + sk_tiles)
+    // are split evenly over the persistent grid; workgroup wg walks its share
+    // [it0, it1) tile segment by tile segment.  The grid is never larger than
+    // the number of iterations, so every workgroup owns at least one and the
+    // workgroups holding a split tile are exactly its first owner .. last owner.
+    __device__ __forceinline__ static void run_sk(const TileArgs& a) {
+        __shared__ __attribute__((aligned(1024))) char smem_raw[LDS];
+        __shared__ int s_flag;
+        lds_char* smem = (lds_char*)smem_raw;
+        const int tid = threadIdx.x, lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int wm = wave / WN, wn = wave % WN;
+        const int wg = blockIdx.x;
+        Acc acc[FM][FN];
+        const int64_t I = a.iters;
+        const int64_t W = (int64_t)a.sk_tiles * I;
+        const int64_t it0 = (int64_t)wg * W / a.grid, it1 = (int64_t)(wg + 1) * W / a.grid;
+        const int64_t first_tile = it0 / I;
+        for (int64_t it = it0; it < it1;) {
+            const int64_t tsk = it / I;
+            const int k_lo = (int)(it - tsk * I);
+            const int k_hi = (int)min<int64_t>(I, k_lo + (it1 - it));
+            int tm, tn;
+            tile_coords(a.dp_tiles + (int)tsk, a, tm, tn);
+            const int m0 = tm * BM, n0 = tn * BN;
+            init_acc(acc, a, a.has_bias && k_lo == 0, n0, wn, lane);
+            mainloop(acc, a, smem, m0, n0, k_lo, k_hi, wave, lane);
+            it += k_hi - k_lo;
+            if (k_lo == 0 && k_hi == I) {
+                store_tile(acc, a, m0, n0, wm, wn, lane);
+                continue;
+            }
+            // Split tile: publish this segment, count arrivals.
+            const int slot = 2 * wg + (tsk == first_tile ? 0 : 1);
+            store_partial(acc, partial_slot(a, slot), wave, lane);
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            __syncthreads();
+            // workgroups holding a segment of tile tsk: owners of its first and last iteration
+            const int64_t x0 = tsk * I, x1 = tsk * I + I - 1;
+            const int w_first = (int)(((x0 + 1) * a.grid + W - 1) / W - 1);
+            const int w_last = (int)(((x1 + 1) * a.grid + W - 1) / W - 1);
+            if (tid == 0) {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                s_flag = __hip_atomic_fetch_add(a.ws_counter + tsk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __syncthreads();
+            const int arrived = s_flag;
+            __syncthreads();  // s_flag is rewritten by the next split tile
+            if (arrived != w_last - w_first) continue;  // not the last arrival
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            // Last arrival: sum every segment's partial in workgroup order.
+            for (int w = w_first; w <= w_last; ++w) {
+                const int64_t ft = ((int64_t)w * W / a.grid) / I;
+                const int sl = 2 * w + (tsk == ft ? 0 : 1);
+                add_partial(acc, partial_slot(a, sl), wave, lane, w == w_first);
+            }
+            store_tile(acc, a, m0, n0, wm, wn, lane);
+            if (tid == 0) __hip_atomic_store(a.ws_counter + tsk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+};
+
+template <int DT, int CFG, bool B_KMAJ, bool SK>
+__global__ __launch_bounds__(256) void tile_gemm_kernel(TileArgs a) {
+    static_assert(TileKernel<DT, CFG, B_KMAJ>::NT == 256, "every tile config runs four waves");
+    if constexpr (SK) TileKernel<DT, CFG, B_KMAJ>::run_sk(a);
+    else TileKernel<DT, CFG, B_KMAJ>::run_dp(a);
+}
+
+// One call = up to two launches on the stream: the data-parallel tiles
+// [0, dp_tiles) with one workgroup each, then the Stream-K tiles on the
+// persistent grid.
+template <int DT, int CFG, bool B_KMAJ>
+int launch_tile(const TileArgs& a, void* stream) {
+    hipStream_t s = (hipStream_t)stream;
+    if (a.dp_tiles > 0)
+        hipLaunchKernelGGL((tile_gemm_kernel<DT, CFG, B_KMAJ, false>), dim3(a.dp_tiles), dim3(256), 0, s, a);
+    if (a.sk_tiles > 0)
+        hipLaunchKernelGGL((tile_gemm_kernel<DT, CFG, B_KMAJ, true>), dim3(a.grid), dim3(256), 0, s, a);
+    return (int)hipGetLastError();
+}
+
+}  // namespace tcm

@@ -1,0 +1,120 @@
+"""Helpers for the GPU parity tests: upload seeded inputs, call tcm_gemm
+through the C ABI, compare with the CPU oracle.
+
+Bars:
+  * int8 -> int32: bit-exact on every checked entry;
+  * f16/bf16 -> f32: max|C - C_ref| / (K * max|A| * max|B| + max|bias|) <= 1e-3;
+  * f32: the same normalised error <= 1e-5;
+where the maxima run over the whole stored operands and C_ref is the oracle's
+binary64 value of the exact inputs.  K == 0 is checked exactly.
+"""
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import synthetic as S
+import tensor_core_mixed_amd as T
+
+TOL = {S.F16: 1e-3, S.BF16: 1e-3, S.F32: 1e-5}
+_TORCH = {S.F16: torch.float16, S.BF16: torch.bfloat16, S.F32: torch.float32, S.I8: torch.int8}
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def to_device(store, dtype, offset_elems=0):
+    """Upload a storage array; optionally start it `offset_elems` into a larger
+    allocation (to make the pointer unaligned).  Returns (keepalive, pointer)."""
+    flat = np.ascontiguousarray(store).reshape(-1)
+    if dtype in (S.F16, S.BF16):
+        t = torch.from_numpy(flat.view(np.int16).copy())
+    else:
+        t = torch.from_numpy(flat.copy())
+    if offset_elems:
+        big = torch.zeros(t.numel() + offset_elems, dtype=t.dtype)
+        big[offset_elems:] = t
+        t = big
+    t = t.cuda()
+    return t, t.data_ptr() + offset_elems * t.element_size()
+
+
+def value_range(store, dtype):
+    if dtype == S.F16:
+        v = store.view(np.float16).astype(np.float64)
+    elif dtype == S.BF16:
+        v = torch.from_numpy(store.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    else:
+        v = store.astype(np.float64)
+    return float(np.max(np.abs(v))) if v.size else 0.0
+
+
+def run_tcm(p, g, stream=None, a_offset=0, b_offset=0, c_offset=0, c_fill=None):
+    """Run problem p with inputs g on the GPU; return C (M x ldc int32/float32
+    host array, including the padding columns) and the plan text."""
+    dt = p.dtype
+    acc_t = torch.int32 if dt == S.I8 else torch.float32
+    ka, pa = to_device(g["A"], dt, a_offset)
+    kb, pb = to_device(g["B"], dt, b_offset)
+    pbias, kbias = None, None
+    if g["bias"] is not None:
+        kbias = torch.from_numpy(g["bias"].copy()).cuda()
+        pbias = kbias.data_ptr()
+    fill = c_fill if c_fill is not None else (-7 if dt == S.I8 else float("nan"))
+    C = torch.full((max(p.M, 1) * p.LDC + c_offset,), fill, dtype=acc_t, device="cuda")
+    pc = C.data_ptr() + c_offset * 4
+    epi = (T.TCM_EPI_BIAS if p.bias else 0) | (T.TCM_EPI_RELU if p.relu else 0)
+    code = dt | (T.TCM_A_COLMAJOR if p.a_col else 0) | (T.TCM_B_COLMAJOR if p.b_col else 0)
+    st = T.tcm_gemm(p.M, p.N, p.K, pa, p.LDA, pb, p.LDB, pc, p.LDC, code, pbias, epi,
+                    stream if stream is not None else torch.cuda.current_stream().cuda_stream)
+    assert st == T.TCM_OK, T.tcm_status_string(st)
+    plan = T.tcm_last_plan()
+    torch.cuda.synchronize()
+    out = C[c_offset:c_offset + p.M * p.LDC].cpu().numpy().reshape(p.M, p.LDC) if p.M else np.zeros((0, p.LDC))
+    del ka, kb, kbias
+    return out, plan
+
+
+def oracle_ref(p, g, ii=None, jj=None):
+    o = oracle.get()
+    if ii is None:
+        return o.gemm(p.M, p.N, p.K, g["A"], p.LDA, p.a_col, g["B"], p.LDB, p.b_col, p.dtype, bias=g["bias"],
+                      relu=p.relu)
+    return o.gemm_entries(p.M, p.N, p.K, g["A"], p.LDA, p.a_col, g["B"], p.LDB, p.b_col, p.dtype, ii, jj,
+                          bias=g["bias"], relu=p.relu)
+
+
+def check(p, g, C, ii=None, jj=None):
+    """Compare C (M x ldc) with the oracle on all entries or on (ii, jj).
+    Returns the normalised error (0 for int8)."""
+    got = C[:, :p.N] if ii is None else C[ii, jj]
+    ref = oracle_ref(p, g, ii, jj)
+    if ii is None:
+        assert np.all(np.isfinite(got)) if p.dtype != S.I8 else True, "unwritten or non-finite outputs"
+    if p.dtype == S.I8:
+        bad = np.flatnonzero(got.reshape(-1) != ref.reshape(-1))
+        assert bad.size == 0, f"{p.name}: {bad.size} int8 mismatches, first at flat index {bad[0]}: {got.reshape(-1)[bad[0]]} vs {ref.reshape(-1)[bad[0]]}"
+        return 0.0
+    diff = np.abs(got.astype(np.float64) - ref)
+    if p.K == 0:
+        assert np.array_equal(got.astype(np.float64), ref), f"{p.name}: K == 0 must give epi(bias) exactly"
+        return 0.0
+    denom = p.K * value_range(g["A"], p.dtype) * value_range(g["B"], p.dtype)
+    if g["bias"] is not None:
+        denom += float(np.max(np.abs(g["bias"])))
+    err = float(np.max(diff)) / denom if diff.size else 0.0
+    assert err <= TOL[p.dtype], f"{p.name}: normalised error {err:.3e} > {TOL[p.dtype]:.0e}"
+    return err
+
+
+def check_padding_untouched(p, C, fill):
+    """Columns N..ldc-1 of every row must keep the fill value."""
+    if p.LDC > p.N and p.M:
+        pad = C[:, p.N:]
+        if isinstance(fill, float) and np.isnan(fill):
+            assert np.all(np.isnan(pad)), "wrote into C's padding columns"
+        else:
+            assert np.all(pad == fill), "wrote into C's padding columns"

@@ -1,0 +1,206 @@
+"""The C-ABI library on the CPU: exports, argument checks, the planner and the
+Stream-K partition.  No kernel runs here (no GPU in this process)."""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import tensor_core_mixed_amd as T
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tcm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tcm_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert "tcm_gemm" in names and len(names) >= 10
+    out = subprocess.run(["nm", "-D", "--defined-only", T.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (tcm_[a-z_]+)\b", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    lib = T.lib()
+    for n in names:
+        getattr(lib, n)
+
+
+def test_status_strings_and_version():
+    for s in range(5):
+        assert T.tcm_status_string(s).startswith("TCM_")
+    assert "unknown" in T.tcm_status_string(99)
+    assert "gfx950" in T.tcm_version()
+
+
+BAD = [  # (M, N, K, lda, ldb, ldc, dtype, epilogue, A, B, C, bias)
+    (-1, 4, 4, 4, 4, 4, 0, 0, 16, 16, 16, 0),           # negative size
+    (4, 4, 4, 3, 4, 4, 0, 0, 16, 16, 16, 0),            # lda < K
+    (4, 4, 4, 4, 3, 4, 0, 0, 16, 16, 16, 0),            # ldb < N
+    (4, 4, 8, 8, 4, 4, T.TCM_B_COLMAJOR, 0, 16, 16, 16, 0),  # col-major B needs ldb >= K
+    (4, 4, 4, 4, 4, 3, 0, 0, 16, 16, 16, 0),            # ldc < N
+    (4, 4, 4, 4, 4, 4, 7, 0, 16, 16, 16, 0),            # unknown element type
+    (4, 4, 4, 4, 4, 4, 1 << 12, 0, 16, 16, 16, 0),      # unknown flag
+    (4, 4, 4, 4, 4, 4, 0, 4, 16, 16, 16, 0),            # unknown epilogue
+    (4, 4, 4, 4, 4, 4, 0, 1, 16, 16, 16, 0),            # bias flag without bias
+    (4, 4, 4, 4, 4, 4, 0, 0, 0, 16, 16, 0),             # NULL A
+    (4, 4, 4, 4, 4, 4, 0, 0, 16, 0, 16, 0),             # NULL B
+    (4, 4, 4, 4, 4, 4, 0, 0, 16, 16, 0, 0),             # NULL C
+    (4, 4, 4, 4, 4, 4, 0, 0, 17, 16, 4096, 0),          # A not aligned to its element
+    (4, 4, 4, 4, 4, 4, 0, 0, 4096, 16, 4100, 0),        # C overlaps A
+    (4, 4, 4, 4, 4, 4, 0, 0, 16, 4096, 4100, 0),        # C overlaps B
+    (4, 4, 4, 4, 4, 4, 0, 1, 16, 256, 4096, 4100),      # C overlaps bias
+]
+
+
+@pytest.mark.parametrize("args", BAD)
+def test_invalid_arguments_rejected_before_any_hip_call(args):
+    M, N, K, lda, ldb, ldc, dt, epi, A, B, C, bias = args
+    st = T.tcm_gemm(M, N, K, A or None, lda, B or None, ldb, C or None, ldc, dt, bias or None, epi, None)
+    assert st == T.TCM_ERR_INVALID_VALUE
+
+
+def test_empty_problem_is_ok_without_device():
+    # nothing is read or written for M == 0 or N == 0, so NULL pointers are fine
+    assert T.tcm_gemm(0, 5, 3, None, 3, None, 5, None, 5, 0, None, 0, None) == T.TCM_OK
+    assert T.tcm_gemm(0, 5, 3, 16, 3, 16, 5, 4096, 5, 0, None, 0, None) == T.TCM_OK
+    assert T.tcm_gemm(5, 0, 3, 16, 3, 16, 5, 4096, 5, 0, None, 0, None) == T.TCM_OK
+
+
+def test_valid_call_without_device_reports_hip_error():
+    # real-looking (fake) pointers: checks pass, the first HIP call fails
+    st = T.tcm_gemm(64, 64, 64, 1 << 20, 64, 2 << 20, 64, 3 << 20, 64, 0, None, 0, None)
+    assert st == T.TCM_ERR_HIP
+
+
+def test_options():
+    assert T.tcm_get_option("force_mode") == 0
+    assert T.tcm_set_option("force_mode", 2) == T.TCM_OK and T.tcm_get_option("force_mode") == 2
+    assert T.tcm_set_option("force_mode", 3) == T.TCM_ERR_INVALID_VALUE
+    assert T.tcm_set_option("no_such_key", 1) == T.TCM_ERR_INVALID_VALUE
+    assert T.tcm_get_option("no_such_key") == -2
+    assert T.tcm_set_option("force_config", T.tcm_config_count()) == T.TCM_ERR_INVALID_VALUE
+    assert T.tcm_set_option("force_mode", 0) == T.TCM_OK
+
+
+def test_config_table():
+    n = T.tcm_config_count()
+    assert n >= 3
+    for i in range(n):
+        for dt, bk in ((0, 64), (1, 64), (2, 32), (3, 128)):
+            bm, bn, k, waves = T.tcm_config_info(i, dt)
+            assert k == bk and waves == 4 and bm % 32 == 0 and bn % 32 == 0
+            assert 2 * (bm + bn) * 128 <= 160 * 1024  # two LDS stages fit one CU
+
+
+def test_planner_headline_shape_is_data_parallel_big_tiles():
+    p = T.tcm_plan(8192, 8192, 8192, 8192, 8192, 8192, T.TCM_F16_F32 | T.TCM_B_COLMAJOR)
+    assert p["kernel"] == 1 and (p["bm"], p["bn"]) == (256, 256) and p["mode"] == 1
+    assert p["tiles"] == 1024 and p["iters_per_tile"] == 128 and p["grid"] == 1024
+
+
+@pytest.mark.parametrize("M", [1, 16, 64])
+def test_planner_skinny_uses_streamk(M):
+    p = T.tcm_plan(M, 4096, 4096, 4096, 4096, 4096, T.TCM_F16_F32)
+    assert p["kernel"] == 1 and p["mode"] == 2 and p["bm"] <= 64
+    assert p["sk_tiles"] > 0 and p["workspace_bytes"] > 0
+
+
+def test_planner_generic_fallbacks():
+    # K not a multiple of the 16-byte chunk, unaligned pointers, column-major A
+    assert T.tcm_plan(100, 100, 17, 17, 100, 100, 0)["kernel"] == 0
+    assert T.tcm_plan(100, 100, 64, 64, 100, 100, 0, aligned=False)["kernel"] == 0
+    assert T.tcm_plan(100, 100, 64, 100, 100, 100, T.TCM_A_COLMAJOR)["kernel"] == 0
+    assert T.tcm_plan(100, 100, 64, 64, 100, 100, 0)["kernel"] == 0  # row-major B, N % 8 != 0
+    assert T.tcm_plan(100, 104, 64, 64, 104, 104, 0)["kernel"] == 1
+    assert T.tcm_plan(100, 100, 64, 64, 64, 100, T.TCM_B_COLMAJOR)["kernel"] == 1
+    assert T.tcm_plan(100, 100, 0, 1, 100, 100, 0)["kernel"] == 0  # K == 0
+
+
+def test_planner_forced_modes():
+    try:
+        assert T.tcm_set_option("force_mode", 2) == 0
+        p = T.tcm_plan(1024, 1024, 1024, 1024, 1024, 1024, 0)
+        assert p["mode"] == 2 and p["sk_tiles"] + p["dp_tiles"] == p["tiles"]
+        assert T.tcm_set_option("force_mode", 1) == 0
+        p = T.tcm_plan(1, 4096, 4096, 4096, 4096, 4096, 0)
+        assert p["mode"] == 1 and p["dp_tiles"] == p["tiles"]
+        assert T.tcm_set_option("force_config", 1) == 0
+        p = T.tcm_plan(1000, 1000, 512, 512, 1000, 1000, 0)
+        assert (p["bm"], p["bn"]) == (128, 128)
+    finally:
+        T.tcm_set_option("force_mode", 0)
+        T.tcm_set_option("force_config", -1)
+
+
+SK_SHAPES = [(9, 16, 256), (36, 256, 256), (225, 64, 256), (144, 256, 512), (1, 7, 300), (5, 3, 2), (300, 1, 1000),
+             (17, 13, 64)]
+
+
+@pytest.mark.parametrize("sk_tiles,iters,grid", SK_SHAPES)
+def test_streamk_partition_covers_each_iteration_once(sk_tiles, iters, grid):
+    W = sk_tiles * iters
+    ranges = [T.tcm_streamk_range(sk_tiles, iters, grid, w) for w in range(grid)]
+    assert ranges[0][0] == 0 and ranges[-1][1] == W
+    for (b0, e0), (b1, e1) in zip(ranges, ranges[1:]):
+        assert e0 == b1  # contiguous, in workgroup order
+    sizes = [e - b for b, e in ranges]
+    assert max(sizes) - min(sizes) <= 1  # even split
+    # each workgroup stores at most two partial tiles (its first and last segment)
+    for b, e in ranges:
+        if e > b:
+            assert (e - 1) // iters - b // iters + 1 >= 1
+
+
+def _segments(sk_tiles, iters, grid):
+    """(wg, tile, k_lo, k_hi) segments in workgroup order, as the kernel walks them."""
+    segs = []
+    for w in range(grid):
+        b, e = T.tcm_streamk_range(sk_tiles, iters, grid, w)
+        it = b
+        while it < e:
+            t = it // iters
+            k_lo = it - t * iters
+            k_hi = min(iters, k_lo + (e - it))
+            segs.append((w, t, k_lo, k_hi))
+            it += k_hi - k_lo
+    return segs
+
+
+@pytest.mark.parametrize("sk_tiles,iters,grid", [(4, 8, 3), (2, 5, 7), (3, 16, 16), (6, 4, 5)])
+def test_streamk_cpu_simulation_matches_oracle_int8(oracle_lib, sk_tiles, iters, grid):
+    """Run the Stream-K decomposition on the CPU: each segment's partial is the
+    oracle's exact int8 sum over its k range (bias only in the k = 0 segment),
+    partials are summed in workgroup order; the result equals the oracle's
+    full product bit-for-bit."""
+    import oracle
+    rng = np.random.default_rng(7)
+    bm, bn, bk = 8, 8, 16
+    tiles_n = 2 if sk_tiles % 2 == 0 else 1
+    tiles_m = sk_tiles // tiles_n
+    M, N, K = tiles_m * bm, tiles_n * bn, iters * bk
+    A = rng.integers(-128, 128, size=(M, K)).astype(np.int8)
+    B = rng.integers(-128, 128, size=(K, N)).astype(np.int8)
+    bias = rng.integers(-2 ** 20, 2 ** 20, size=N).astype(np.int32)
+    full = oracle_lib.gemm(M, N, K, A, K, False, B, N, False, oracle.I8, bias=bias)
+    out = np.zeros((M, N), dtype=np.int64)
+    seen = {}
+    for w, t, k_lo, k_hi in _segments(sk_tiles, iters, grid):
+        tm, tn = divmod(t, tiles_n)
+        rows, cols = slice(tm * bm, tm * bm + bm), slice(tn * bm, tn * bn + bn)
+        a = np.ascontiguousarray(A[rows, k_lo * bk:k_hi * bk])
+        b = np.ascontiguousarray(B[k_lo * bk:k_hi * bk, cols])
+        part = oracle_lib.gemm(bm, bn, (k_hi - k_lo) * bk, a, a.shape[1], False, b, bn, False, oracle.I8,
+                               bias=bias[cols] if k_lo == 0 else None)
+        out[rows, cols] += part
+        seen.setdefault(t, []).append((w, k_lo, k_hi))
+    assert np.array_equal(out.astype(np.int32), full)
+    for t, parts in seen.items():  # every tile's segments tile its k range exactly once, in order
+        ks = sorted(parts)
+        assert ks[0][1] == 0 and ks[-1][2] == iters
+        assert all(a[2] == b[1] for a, b in zip(ks, ks[1:]))

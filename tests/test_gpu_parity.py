@@ -1,0 +1,208 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the
+same seeded inputs (bars in gpu_util.py).  Each case prints its name, shape
+and seed before touching the GPU."""
+import numpy as np
+import pytest
+import torch
+
+import synthetic as S
+import tensor_core_mixed_amd as T
+from gpu_util import check, check_padding_untouched, run_tcm, say
+
+pytestmark = pytest.mark.gpu
+
+DTYPES = [S.F16, S.BF16, S.F32, S.I8]
+
+
+@pytest.fixture(autouse=True)
+def _reset_options():
+    yield
+    T.tcm_set_option("force_mode", 0)
+    T.tcm_set_option("force_config", -1)
+    T.tcm_set_option("sk_grid", 0)
+    T.tcm_set_option("generic", 0)
+
+
+def _run(p, **kw):
+    say(f"[case] {p.name} M={p.M} N={p.N} K={p.K} dtype={p.dtype} a_col={p.a_col} b_col={p.b_col} "
+        f"bias={p.bias} relu={p.relu} lda={p.LDA} ldb={p.LDB} ldc={p.LDC} seed={p.seed} "
+        f"force_mode={T.tcm_get_option('force_mode')} force_config={T.tcm_get_option('force_config')} "
+        f"sk_grid={T.tcm_get_option('sk_grid')} generic={T.tcm_get_option('generic')}")
+    g = S.generate(p)
+    C, plan = run_tcm(p, g, **kw)
+    say(f"       plan: {plan}")
+    return g, C, plan
+
+
+# ------------------------------------------------------------ small cases, all entries
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("b_col", [False, True])
+def test_first_slice_512(dtype, b_col):
+    """512^3 (several tiles, all entries) for every type and both B layouts."""
+    p = S.small_problem(dtype, 512, 512, 512, seed=0, b_col=b_col)
+    g, C, plan = _run(p)
+    assert "kernel=tile" in plan
+    check(p, g, C)
+
+
+RAGGED = [(300, 264, 200), (257, 136, 72), (33, 520, 136), (1, 8, 64), (17, 40, 8), (600, 96, 392)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("b_col", [False, True])
+def test_ragged_tiles_and_k_tail(dtype, shape, b_col):
+    """Ragged M and N edges and a K tail, on the tiled kernel, with bias + ReLU."""
+    M, N, K = shape
+    ce = {S.F16: 8, S.BF16: 8, S.F32: 4, S.I8: 16}[dtype]
+    K = max(ce, K // ce * ce)
+    if not b_col:
+        N = max(ce, N // ce * ce)
+    p = S.small_problem(dtype, M, N, K, seed=11, b_col=b_col, bias=True, relu=True)
+    g, C, plan = _run(p)
+    assert "kernel=tile" in plan
+    check(p, g, C)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("config", [0, 1, 2, 3])
+@pytest.mark.parametrize("mode", [1, 2])
+def test_every_config_and_mode(dtype, config, mode):
+    """Each tile config, data-parallel and Stream-K, on a shape with edges in M, N and K."""
+    ce = {S.F16: 8, S.BF16: 8, S.F32: 4, S.I8: 16}[dtype]
+    p = S.small_problem(dtype, 190, 304, 53 * ce, seed=config * 10 + mode, bias=True, relu=(mode == 2))
+    T.tcm_set_option("force_config", config)
+    T.tcm_set_option("force_mode", mode)
+    g, C, plan = _run(p)
+    assert f"config={config}" in plan and ("mode=dp" if mode == 1 else "mode=streamk") in plan
+    check(p, g, C)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("sk_grid", [3, 7, 64, 301])
+def test_streamk_many_segments_per_tile(dtype, sk_grid):
+    """Small persistent grids split each tile over several workgroups (and
+    large ones give workgroups a few iterations each)."""
+    ce = {S.F16: 8, S.BF16: 8, S.F32: 4, S.I8: 16}[dtype]
+    p = S.small_problem(dtype, 260, 208, 40 * ce, seed=sk_grid, b_col=(sk_grid % 2 == 1), bias=True)
+    T.tcm_set_option("force_mode", 2)
+    T.tcm_set_option("force_config", 1)
+    T.tcm_set_option("sk_grid", sk_grid)
+    g, C, plan = _run(p)
+    grid = int(plan.split("grid=")[1].split()[0])
+    assert "mode=streamk" in plan and 1 <= grid <= sk_grid
+    check(p, g, C)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_int8_and_float_dp_vs_streamk_agree(dtype):
+    """Data-parallel and Stream-K give the same int8 result bit-for-bit, and
+    Stream-K's float result is the same bits on every run (fixed sum order)."""
+    ce = {S.F16: 8, S.BF16: 8, S.F32: 4, S.I8: 16}[dtype]
+    p = S.small_problem(dtype, 384, 384, 48 * ce, seed=5, bias=True, relu=True)
+    T.tcm_set_option("force_config", 1)
+    T.tcm_set_option("force_mode", 1)
+    g, C_dp, _ = _run(p)
+    T.tcm_set_option("force_mode", 2)
+    T.tcm_set_option("sk_grid", 29)
+    _, C_sk1, _ = _run(p)
+    _, C_sk2, _ = _run(p)
+    check(p, g, C_sk1)
+    assert np.array_equal(C_sk1, C_sk2), "Stream-K result differs between runs"
+    if dtype == S.I8:
+        assert np.array_equal(C_dp, C_sk1), "int8 data-parallel and Stream-K differ"
+
+
+# ------------------------------------------------------------ generic kernel
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("layout", ["odd_k", "a_col", "both_col", "padded_ld", "unaligned"])
+def test_generic_path(dtype, layout):
+    """Shapes and layouts the tiled kernel does not take: same results, slower."""
+    kw = {}
+    if layout == "odd_k":
+        p = S.small_problem(dtype, 70, 90, 37, seed=3, bias=True, relu=True)
+    elif layout == "a_col":
+        p = S.small_problem(dtype, 130, 72, 96, seed=4, a_col=True, bias=True)
+    elif layout == "both_col":
+        p = S.small_problem(dtype, 65, 129, 100, seed=5, a_col=True, b_col=True, relu=True)
+    elif layout == "padded_ld":
+        p = S.small_problem(dtype, 100, 60, 75, seed=6, lda=81, ldb=67, ldc=70, bias=True)
+    else:
+        p = S.small_problem(dtype, 128, 128, 128, seed=7, bias=True)
+        kw = dict(a_offset=1, b_offset=3, c_offset=1)
+    g, C, plan = _run(p, **kw)
+    assert "kernel=generic" in plan
+    check(p, g, C)
+    if layout == "padded_ld":
+        check_padding_untouched(p, C, -7 if dtype == S.I8 else float("nan"))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_forced_generic_matches_tiled(dtype):
+    ce = {S.F16: 8, S.BF16: 8, S.F32: 4, S.I8: 16}[dtype]
+    p = S.small_problem(dtype, 200, 144, 20 * ce, seed=9, bias=True, relu=True)
+    g, C_tile, plan = _run(p)
+    assert "kernel=tile" in plan
+    T.tcm_set_option("generic", 1)
+    _, C_gen, plan = _run(p)
+    assert "kernel=generic" in plan
+    check(p, g, C_gen)
+    if dtype == S.I8:
+        assert np.array_equal(C_tile, C_gen)
+
+
+# ------------------------------------------------------------ degenerate cases
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_k_zero_gives_epilogue_of_bias(dtype):
+    p = S.small_problem(dtype, 5, 7, 0, seed=1, bias=True, relu=True, lda=1)
+    g, C, _ = _run(p)
+    check(p, g, C)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_one_by_one(dtype):
+    ce = {S.F16: 8, S.BF16: 8, S.F32: 4, S.I8: 16}[dtype]
+    for K in (1, ce):
+        p = S.small_problem(dtype, 1, 1, K, seed=2, bias=True)
+        g, C, _ = _run(p)
+        check(p, g, C)
+
+
+def test_empty_problem_leaves_c_untouched():
+    C = torch.full((16,), 3.0, device="cuda")
+    A = torch.zeros(16, dtype=torch.float16, device="cuda")
+    st = T.tcm_gemm(0, 4, 4, A.data_ptr(), 4, A.data_ptr(), 4, C.data_ptr(), 4, 0, None, 0, None)
+    assert st == T.TCM_OK
+    torch.cuda.synchronize()
+    assert torch.all(C == 3.0)
+
+
+def test_block_sum_printed_value_on_gpu():
+    """The pages' worked example, through the engine: sum(arange(256)) = 32640."""
+    for dtype, tdt in ((S.F16, torch.float16), (S.BF16, torch.bfloat16), (S.F32, torch.float32)):
+        a = torch.arange(256, dtype=tdt, device="cuda").reshape(1, 256)
+        b = torch.ones((256, 8), dtype=tdt, device="cuda")
+        say(f"[case] block sum dtype={dtype}")
+        C = T.gemm(a, b)
+        torch.cuda.synchronize()
+        assert torch.all(C == 32640.0), C
+    a = (torch.arange(256, device="cuda") - 128).to(torch.int8).reshape(1, 256)
+    C = T.gemm(a, torch.ones((256, 16), dtype=torch.int8, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.all(C == -128)
+
+
+def test_torch_convenience_layouts():
+    """gemm() reads row/column-major views from strides."""
+    torch.manual_seed(0)
+    A = torch.randn(96, 64, device="cuda").half()
+    Bt = torch.randn(80, 64, device="cuda").half()
+    say("[case] torch convenience: B as transposed view")
+    C = T.gemm(A, Bt.t())
+    ref = A.float().cpu() @ Bt.float().cpu().t()
+    assert torch.allclose(C.cpu(), ref, atol=1e-2, rtol=1e-3)
+    C2 = T.gemm(A.t().contiguous().t(), Bt.t())  # column-major A view -> generic kernel
+    assert torch.allclose(C2.cpu(), ref, atol=1e-2, rtol=1e-3)
