@@ -1,0 +1,301 @@
+#!/usr/bin/env python3
+"""Benchmark of the GEMM engine on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one tcm_gemm call of the whole hot path on the workload (default:
+f16 8192^3, A row-major, B column-major, f32 accumulate and output -- the
+shape the headline TFLOP/s figure is quoted on), inputs resident in HBM.
+Prints one JSON line with the throughput, the roofline of the dominant
+kernel (achieved algorithmic FLOP/s from HIP events on the launch stream vs
+the dtype's dense MFMA peak) and the CPU oracle's rate on a bounded sample.
+
+Extra modes (for profiling runs):
+  --calibrate-copy            one 512 MiB device-to-device copy (counter calibration)
+  --summarize-counters DIR    turn rocprofv3 --pmc output into profiles/ JSON
+  --all                       also time every workload and write a table (stderr)
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "GEMM TFLOPS/TOPS on 1 MI355X and % of dtype MFMA peak (fp16 8192³)"
+# dense MFMA peaks of MI355X (256 CUs at 2.4 GHz), TFLOP/s (TOP/s for int8)
+PEAK = {0: 2516.6, 1: 2516.6, 2: 157.3, 3: 5033.2}
+HBM_PEAK_GBS = 8000.0
+DTYPE_NAME = {0: "f16", 1: "bf16", 2: "f32", 3: "i8"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{name}.json")
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources: counters taken on other code are stale."""
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "tensor_core_mixed_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def describe(p):
+    return (f"{DTYPE_NAME[p.dtype]} GEMM {p.M}x{p.N}x{p.K}, A {'col' if p.a_col else 'row'}-major, "
+            f"B {'col' if p.b_col else 'row'}-major, {'int32' if p.dtype == 3 else 'f32'} accumulate and output"
+            + (", bias + ReLU epilogue" if p.bias else ""))
+
+
+def upload(g, p):
+    import torch
+    def dev(x):
+        if x is None:
+            return None
+        if x.dtype == np.uint16:
+            x = x.view(np.int16)
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    return dev(g["A"]), dev(g["B"]), dev(g["bias"])
+
+
+def make_call(p, A, B, bias, C, stream):
+    import tensor_core_mixed_amd as T
+    code = p.dtype | (T.TCM_A_COLMAJOR if p.a_col else 0) | (T.TCM_B_COLMAJOR if p.b_col else 0)
+    epi = (T.TCM_EPI_BIAS if p.bias else 0) | (T.TCM_EPI_RELU if p.relu else 0)
+    args = (p.M, p.N, p.K, A.data_ptr(), p.LDA, B.data_ptr(), p.LDB, C.data_ptr(), p.LDC, code,
+            bias.data_ptr() if bias is not None else None, epi, stream)
+
+    def call():
+        st = T.tcm_gemm(*args)
+        if st != 0:
+            raise RuntimeError(T.tcm_status_string(st))
+    return call
+
+
+def time_steps(call, steps, warmup, stream_obj):
+    import torch
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream_obj)
+    for _ in range(steps):
+        call()
+    e1.record(stream_obj)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
+
+
+def sampled_parity(p, g, C):
+    """Check the sampled entries (4096 seeded + rows 0 and M-1) against the oracle."""
+    import oracle
+    import synthetic as S
+    ii, jj = S.sample_entries(p)
+    got = C.cpu().numpy()[ii, jj] if C.shape[1] == p.N else C.cpu().numpy().reshape(p.M, p.LDC)[ii, jj]
+    ref = oracle.get().gemm_entries(p.M, p.N, p.K, g["A"], p.LDA, p.a_col, g["B"], p.LDB, p.b_col, p.dtype, ii, jj,
+                                    bias=g["bias"], relu=p.relu)
+    if p.dtype == 3:
+        return {"entries": int(ii.size), "mismatches": int(np.sum(got != ref)), "ok": bool(np.all(got == ref))}
+    amax = lambda x: float(np.max(np.abs(_decode(x, p.dtype))))
+    denom = p.K * amax(g["A"]) * amax(g["B"]) + (float(np.max(np.abs(g["bias"]))) if g["bias"] is not None else 0.0)
+    err = float(np.max(np.abs(got.astype(np.float64) - ref))) / denom
+    tol = 1e-5 if p.dtype == 2 else 1e-3
+    return {"entries": int(ii.size), "normalised_error": err, "tolerance": tol, "ok": err <= tol}
+
+
+def _decode(x, dt):
+    if dt == 0:
+        return x.view(np.float16).astype(np.float64)
+    if dt == 1:
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def cpu_baseline(p, g, unit_scale, rows=1536):
+    """The oracle (full-product entry point) on the first `rows` rows of C."""
+    import oracle
+    o = oracle.get()
+    rows = min(rows, p.M)
+    A = g["A"]
+    a_rows = A[:rows] if not p.a_col else A
+    t = time.perf_counter()
+    o.gemm(rows, p.N, p.K, a_rows, p.LDA, p.a_col, g["B"], p.LDB, p.b_col, p.dtype, bias=g["bias"], relu=p.relu)
+    dt = time.perf_counter() - t
+    flops = 2.0 * rows * p.N * p.K
+    return {"value": flops / dt / unit_scale, "unit": "TFLOP/s" if p.dtype != 3 else "TOP/s", "cores": o.max_threads(),
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"rows 0..{rows - 1} of C ({rows}x{p.N} entries, K={p.K}; {rows / p.M:.4f} of the product), "
+                      f"binary64 accumulation"}
+
+
+def load_traffic(name, launches_per_step):
+    path = TRAFFIC_FILE.format(name=name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def run_bench(args):
+    import torch
+
+    import synthetic as S
+    import tensor_core_mixed_amd as T
+    p = S.workload(args.workload)
+    torch.cuda.set_device(0)
+    print(f"[bench] workload {p.name}: {describe(p)}", file=sys.stderr, flush=True)
+    g = S.generate(p)
+    A, B, bias = upload(g, p)
+    out_dt = torch.int32 if p.dtype == 3 else torch.float32
+    C = torch.empty((p.M, p.LDC), dtype=out_dt, device="cuda")
+    stream_obj = torch.cuda.current_stream()
+    call = make_call(p, A, B, bias, C, stream_obj.cuda_stream)
+    call()
+    torch.cuda.synchronize()
+    plan = T.tcm_last_plan()
+    print(f"[bench] plan: {plan}", file=sys.stderr, flush=True)
+    ms, wall_ms = time_steps(call, args.steps, args.warmup, stream_obj)
+    flops = p.flops
+    unit_scale = 1e12
+    value = flops / (ms * 1e-3) / unit_scale
+    parity = sampled_parity(p, g, C)
+    print(f"[bench] {ms:.4f} ms/step, {value:.1f} T(FL)OP/s, parity {parity}", file=sys.stderr, flush=True)
+    launches = 1 if "mode=dp" in plan else 2
+    roof = {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK[p.dtype],
+            "unit": "TFLOP/s" if p.dtype != 3 else "TOP/s", "frac": round(value / PEAK[p.dtype], 4),
+            "traffic": load_traffic(p.name, launches)}
+    cpu = cpu_baseline(p, g, unit_scale) if not args.no_cpu else None
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s" if p.dtype != 3 else "TOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE_NAME[p.dtype],
+        "data": "synthetic",
+        "config": {"workload": describe(p), "M": p.M, "N": p.N, "K": p.K, "seed": p.seed, "dist": p.dist,
+                   "plan": plan, "wall_ms_per_step": round(wall_ms, 5), "parity": parity},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    if args.all:
+        run_all(args)
+
+
+def run_all(args):
+    """Time every workload (DP, Stream-K and auto for the split-k shapes) -> stderr table."""
+    import torch
+
+    import synthetic as S
+    import tensor_core_mixed_amd as T
+    rows = []
+    for name, p in S.WORKLOADS.items():
+        g = S.generate(p)
+        A, B, bias = upload(g, p)
+        C = torch.empty((p.M, p.LDC), dtype=torch.int32 if p.dtype == 3 else torch.float32, device="cuda")
+        s = torch.cuda.current_stream()
+        modes = [0, 1, 2] if name.startswith(("skinny", "sk_")) else [0]
+        for mode in modes:
+            T.tcm_set_option("force_mode", mode)
+            call = make_call(p, A, B, bias, C, s.cuda_stream)
+            call()
+            torch.cuda.synchronize()
+            plan = T.tcm_last_plan()
+            ms, _ = time_steps(call, max(5, args.steps // 2), 3, s)
+            par = sampled_parity(p, g, C)
+            v = p.flops / (ms * 1e-3) / 1e12
+            rows.append({"workload": name, "mode": ["auto", "dp", "streamk"][mode], "ms": round(ms, 5),
+                         "tflops": round(v, 2), "frac_peak": round(v / PEAK[p.dtype], 4),
+                         "hbm_frac": round(p.alg_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                         "parity_ok": par["ok"], "plan": plan})
+            print("[all] " + json.dumps(rows[-1]), file=sys.stderr, flush=True)
+        T.tcm_set_option("force_mode", 0)
+        del A, B, bias, C
+        torch.cuda.empty_cache()
+    if args.report:
+        with open(args.report, "w") as f:
+            json.dump(rows, f, indent=1)
+
+
+def calibrate_copy():
+    """One device-to-device copy of exactly 512 MiB (read 512 MiB, write 512 MiB)."""
+    import torch
+    n = 512 * 2 ** 20 // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty(n, device="cuda")
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n * 4}), flush=True)
+
+
+def summarize_counters(d, name):
+    """profiles/traffic_<name>.json from rocprofv3 --pmc runs under d/{fetch,write,copy_fetch,copy_write}."""
+    import csv
+    import glob
+
+    def per_dispatch(sub, counter, kernel_pat):
+        files = glob.glob(os.path.join(d, sub, "**", "*counter_collection.csv"), recursive=True)
+        vals = []
+        for f in files:
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter and kernel_pat in r["Kernel_Name"]:
+                    vals.append(float(r["Counter_Value"]))
+        return vals
+
+    fetch = per_dispatch("fetch", "FETCH_SIZE", "tile_gemm_kernel")
+    write = per_dispatch("write", "WRITE_SIZE", "tile_gemm_kernel")
+    cf = per_dispatch("copy_fetch", "FETCH_SIZE", "copy")
+    cw = per_dispatch("copy_write", "WRITE_SIZE", "copy")
+    copy_kib = 512 * 1024
+    f_fac = copy_kib / max(cf) if cf else 1.0
+    w_fac = copy_kib / max(cw) if cw else 1.0
+    fk = float(np.median(fetch)) if fetch else None
+    wk = float(np.median(write)) if write else None
+    out = {"kernel": "tile_gemm_kernel", "workload": name, "source_hash": kernel_source_hash(),
+           "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
+           "copy_fetch_kib": max(cf) if cf else None, "copy_write_kib": max(cw) if cw else None,
+           "fetch_scale": f_fac, "write_scale": w_fac,
+           "hbm_bytes_per_launch": (fk * f_fac + wk * w_fac) * 1024 if fk and wk else None,
+           "dispatches": {"fetch": len(fetch), "write": len(write)}}
+    path = TRAFFIC_FILE.format(name=name)
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="f16_8192")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
+    ap.add_argument("--all", action="store_true")
+    ap.add_argument("--report", default=None)
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--summarize-counters", default=None)
+    args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.workload)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this engine runs on one GPU: every GPU box here has one, and the GEMM path "
+                                   "has no collectives; run with --gpus 1"}), flush=True)
+        sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
+    run_bench(args)
+
+
+if __name__ == "__main__":
+    main()
