@@ -39,9 +39,9 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int tile_wg_per_cu(const TileConfig& c) {
     int by_lds = (160 * 1024) / lds_bytes(c);
-    // four waves per workgroup; 128x128-per-wave accumulators (256 registers)
-    // leave room for one wave per SIMD
-    int by_regs = (c.bm / c.wm) * (c.bn / c.wn) >= 128 * 128 ? 1 : 2;
+    // accumulators of a 128x128 wave tile (256 registers) leave room for one
+    // wave per SIMD; eight-wave workgroups already put two waves on each SIMD
+    int by_regs = ((c.bm / c.wm) * (c.bn / c.wn) >= 128 * 128 || c.wm * c.wn > 4) ? 1 : 2;
     return std::max(1, std::min(by_lds, by_regs));
 }
 
@@ -139,6 +139,9 @@ Estimate estimate(const Problem& p, const TileConfig& c, int cus, int force_mode
     }
     if (force_mode == 1) return dp;
     if (force_mode == 2) return sk;
+    // the 8-wave 256x256 config runs out of registers in its Stream-K variant
+    // (partial-tile fix-up on top of 128 accumulators per wave): data-parallel only
+    if (c.wm * c.wn > 4) return dp;
     return sk.cycles < 0.97 * dp.cycles ? sk : dp;
 }
 

@@ -24,7 +24,7 @@ struct TileConfig {
 };
 constexpr int kNumConfigs = 4;
 constexpr TileConfig kConfigs[kNumConfigs] = {
-    {256, 256, 2, 2, "256x256 w2x2"},  // big square problems: 128x128 per wave
+    {256, 256, 4, 2, "256x256 w4x2"},  // big square problems: 64x128 per wave, two waves per SIMD
     {128, 128, 2, 2, "128x128 w2x2"},  // mid sizes, 2 workgroups per CU
     {32, 256, 1, 4, "32x256 w1x4"},    // skinny M (M <= 32)
     {64, 256, 1, 4, "64x256 w1x4"},    // skinny M (M <= 64)

@@ -121,72 +121,90 @@ struct TileKernel {
 
     // ---------------------------------------------------------------- DMA
     // Lane `lane` of wave `wave` fills LDS chunk slot p = (j*NW + wave)*64 + lane
-    // with its j-th copy instruction of a stage (a wave instruction fills 1 KiB
-    // of consecutive LDS).  The per-lane byte offsets of all IA + IB chunks are
-    // computed once per tile, with rows/columns outside the matrix already
-    // replaced by the out-of-range offset; only the k tail is masked per step.
+    // with its j-th copy instruction of a stage (one wave instruction fills
+    // 1 KiB of consecutive LDS).  The chunk column of a slot depends on j only
+    // through j's parity and its row advances by ADV rows every two
+    // instructions, so a lane keeps two offsets per operand and adds a
+    // uniform stride.  Rows outside the matrix (m >= M, n >= N for
+    // k-contiguous operands; k >= K for n-contiguous B) lie past the end of
+    // the step's buffer range and read as zeros; columns n >= N of an
+    // n-contiguous B are folded into the offsets; the k tail of k-contiguous
+    // operands is one select per parity.
+    static constexpr int B_RPI = B_KMAJ ? 8 : 64 / B_CPR;  // rows per instruction of the B tile
+    static constexpr int A_ADV = 2 * NW * 8;
+    static constexpr int B_ADV = 2 * NW * B_RPI;
+
     struct Dma {
-        unsigned a_off[IA];
-        unsigned b_off[IB];
-        int a_k[2];   // k (within the K-step) of the lane's A chunk for even / odd j
-        int b_k[2];   // B: k within the step (k-contiguous), or the k row of j = 0, 1 (n-contiguous)
+        unsigned a_off[2];
+        int a_k[2];
+        unsigned b_off[2];
+        int b_k[2];
     };
-    static constexpr int B_RPI = B_KMAJ ? 8 : 64 / B_CPR;  // k rows per instruction (n-contiguous B)
 
     __device__ __forceinline__ static void dma_setup(Dma& d, const TileArgs& a, int m0, int n0, int wave, int lane) {
-        const int mrem = a.M - m0, nrem = a.N - n0;
 #pragma unroll
-        for (int j = 0; j < IA; ++j) {
-            const int p = (j * NW + wave) * 64 + lane;
-            const int r = p >> 3, c = (p & 7) ^ swz_k(r);
-            d.a_off[j] = r < mrem ? (unsigned)(r * a.lda + c * CE) * ES : kOOB;
-            if (j < 2) d.a_k[j] = c * CE;
-        }
-#pragma unroll
-        for (int j = 0; j < IB; ++j) {
-            const int p = (j * NW + wave) * 64 + lane;
+        for (int q = 0; q < 2; ++q) {
+            const int p = (q * NW + wave) * 64 + lane;
+            {
+                const int r = p >> 3, c = (p & 7) ^ swz_k(r);
+                d.a_off[q] = (unsigned)(r * a.lda + c * CE) * ES;
+                d.a_k[q] = c * CE;
+            }
             if constexpr (B_KMAJ) {
                 const int r = p >> 3, c = (p & 7) ^ swz_k(r);
-                d.b_off[j] = r < nrem ? (unsigned)(r * a.ldb + c * CE) * ES : kOOB;
-                if (j < 2) d.b_k[j] = c * CE;
+                d.b_off[q] = (unsigned)(r * a.ldb + c * CE) * ES;
+                d.b_k[q] = c * CE;
             } else {
                 const int kr = p / B_CPR, c = (p % B_CPR) ^ swz_mn<DT, B_CPR>(kr);
-                d.b_off[j] = c * CE < nrem ? (unsigned)(kr * a.ldb + c * CE) * ES : kOOB;
-                if (j < 2) d.b_k[j] = kr;
+                d.b_off[q] = n0 + c * CE < a.N ? (unsigned)(kr * a.ldb + c * CE) * ES : kOOB;
+                d.b_k[q] = 0;
             }
         }
     }
 
+    __device__ __forceinline__ static int clamp_range(int64_t bytes) {
+        return bytes <= 0 ? 0 : (bytes < (int64_t)kOOB ? (int)bytes : (int)kOOB);
+    }
+
     // Issue the copies of K-step kt of tile (m0, n0) into LDS stage `st`.
-    // `tail`: the step reaches past K, so chunks at k >= K read as zeros.
     __device__ __forceinline__ static void dma_issue(const Dma& d, const TileArgs& a, lds_char* smem, int st, int kt,
-                                                     int m0, int n0, int wave, bool tail) {
+                                                     int m0, int n0, int wave) {
         const int k0 = kt * BKE;
         const int krem = a.K - k0;
-        const __amdgpu_buffer_rsrc_t ra = make_rsrc((const char*)a.A + ((int64_t)m0 * a.lda + k0) * ES);
-        lds_char* la = smem + st * STAGE;
+        {
+            const char* base = (const char*)a.A + ((int64_t)m0 * a.lda + k0) * ES;
+            const int nrec = clamp_range(((int64_t)(a.M - m0) * a.lda - k0) * ES);
+            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, nrec, kRsrcWord3);
+            const unsigned o0 = d.a_k[0] < krem ? d.a_off[0] : kOOB, o1 = d.a_k[1] < krem ? d.a_off[1] : kOOB;
+            const unsigned hop = (unsigned)(A_ADV * a.lda * ES);
+            lds_char* la = smem + st * STAGE;
 #pragma unroll
-        for (int j = 0; j < IA; ++j) {
-            unsigned off = d.a_off[j];
-            if (tail && d.a_k[j & 1] >= krem) off = kOOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)(la + (j * NW + wave) * 1024), 16,
-                                                     off, 0, 0, 0);
+            for (int j = 0; j < IA; ++j)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(la + (j * NW + wave) * 1024),
+                                                         16, ((j & 1) ? o1 : o0) + (j >> 1) * hop, 0, 0, 0);
         }
-        const char* bbase;
-        if constexpr (B_KMAJ) bbase = (const char*)a.B + ((int64_t)n0 * a.ldb + k0) * ES;
-        else bbase = (const char*)a.B + ((int64_t)k0 * a.ldb + n0) * ES;
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(bbase);
-        lds_char* lb = smem + st * STAGE + A_BYTES;
-#pragma unroll
-        for (int j = 0; j < IB; ++j) {
-            unsigned off = d.b_off[j];
+        {
+            const char* base;
+            int nrec;
+            unsigned o0, o1;
             if constexpr (B_KMAJ) {
-                if (tail && d.b_k[j & 1] >= krem) off = kOOB;
+                base = (const char*)a.B + ((int64_t)n0 * a.ldb + k0) * ES;
+                nrec = clamp_range(((int64_t)(a.N - n0) * a.ldb - k0) * ES);
+                o0 = d.b_k[0] < krem ? d.b_off[0] : kOOB;
+                o1 = d.b_k[1] < krem ? d.b_off[1] : kOOB;
             } else {
-                if (tail && d.b_k[j & 1] + (j >> 1) * (2 * NW * B_RPI) >= krem) off = kOOB;
+                base = (const char*)a.B + ((int64_t)k0 * a.ldb + n0) * ES;
+                nrec = clamp_range(((int64_t)krem * a.ldb - n0) * ES);
+                o0 = d.b_off[0];
+                o1 = d.b_off[1];
             }
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (__attribute__((address_space(3))) void*)(lb + (j * NW + wave) * 1024), 16,
-                                                     off, 0, 0, 0);
+            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, nrec, kRsrcWord3);
+            const unsigned hop = (unsigned)(B_ADV * a.ldb * ES);
+            lds_char* lb = smem + st * STAGE + A_BYTES;
+#pragma unroll
+            for (int j = 0; j < IB; ++j)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lb + (j * NW + wave) * 1024),
+                                                         16, ((j & 1) ? o1 : o0) + (j >> 1) * hop, 0, 0, 0);
         }
     }
 
@@ -268,8 +286,8 @@ struct TileKernel {
         const lds_char* la = smem + st * STAGE;
         const lds_char* lb = la + A_BYTES;
         const int h = lane >> 5, l32 = lane & 31;
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) f.a[fm] = load_a(la, wm * TM + fm * 32 + l32, sub, h);
+        // issue order = first use by the MFMA sequence: a0, b0..b(FN-1), a1..a(FM-1)
+        f.a[0] = load_a(la, wm * TM + l32, sub, h);
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             if constexpr (B_KMAJ) {
@@ -283,6 +301,8 @@ struct TileKernel {
                 f.b[fn] = load_b_mn(lb, wn * TN + fn * 32, sub, lane);
             }
         }
+#pragma unroll
+        for (int fm = 1; fm < FM; ++fm) f.a[fm] = load_a(la, wm * TM + fm * 32 + l32, sub, h);
     }
 
     __device__ __forceinline__ static void mma_frag(Acc (&acc)[FM][FN], const Frag& f) {
@@ -402,23 +422,60 @@ struct TileKernel {
     }
 
     // ------------------------------------------------------- main loop
-    // Accumulate K-steps [k_lo, k_hi) of tile (m0, n0) into acc.  Schedule of
-    // one K-step kt (stage kt&1): MFMAs of sub-steps 0..2, each overlapping the
-    // fragment loads of the next sub-step; then wait for this wave's copies
-    // of step kt+1 and barrier; issue the copies of step kt+2 into the stage
-    // just drained and load sub-step 0 of step kt+1; then the MFMAs of sub-step
-    // 3 cover that latency.
+    // Interleave the next sub-step's 8 fragment reads with this sub-step's
+    // 16 MFMAs (one read between each pair).
+    static constexpr int NMF = FM * FN * (DT == F32 ? 4 : 1);              // MFMAs per sub-step
+    static constexpr int NRD = FM + FN * ((DT == F32 && !B_KMAJ) ? 4 : (B_KMAJ ? 1 : 2));  // LDS reads per sub-step
+    __device__ __forceinline__ static void sched_reads() {
+#pragma unroll
+        for (int i = 0; i < NMF; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (i < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    }
+    // Last sub-step of a K-step: 16 MFMAs, the 16 copies of step kt+2 and
+    // the 8 reads of the next step's first sub-step.
+    __device__ __forceinline__ static void sched_reads_dma() {
+#pragma unroll
+        for (int i = 0; i < NMF; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            if (i < IA + IB) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+            if (i < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    }
+
+    // One K-step kt from stage st.  DMA: issue the copies of step kt+2 into
+    // stage st once it is drained; NEXT: load sub-step 0 of step kt+1.
+    template <bool DMA, bool NEXT>
+    __device__ __forceinline__ static void kstep(Acc (&acc)[FM][FN], Frag (&f)[2], const Dma& d, const TileArgs& a,
+                                                 lds_char* smem, int st, int kt, int m0, int n0, int wave, int wm,
+                                                 int wn, int lane) {
+#pragma unroll
+        for (int sub = 0; sub < 3; ++sub) {
+            load_frag(f[(sub + 1) & 1], smem, st, sub + 1, wm, wn, lane);
+            mma_frag(acc, f[sub & 1]);
+            sched_reads();
+        }
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __syncthreads();  // step kt+1 is in LDS everywhere; stage st is drained
+        if constexpr (DMA) dma_issue(d, a, smem, st, kt + 2, m0, n0, wave);
+        if constexpr (NEXT) load_frag(f[0], smem, st ^ 1, 0, wm, wn, lane);
+        mma_frag(acc, f[1]);
+        if constexpr (DMA) sched_reads_dma();
+        else if constexpr (NEXT) sched_reads();
+    }
+
+    // Accumulate K-steps [k_lo, k_hi) of tile (m0, n0) into acc, two LDS
+    // stages, the copies running two K-steps ahead of the MFMAs.
     __device__ __forceinline__ static void mainloop(Acc (&acc)[FM][FN], const TileArgs& a, lds_char* smem, int m0, int n0,
                                                     int k_lo, int k_hi, int wave, int lane) {
         const int wm = wave / WN, wn = wave % WN;
-        const int last = a.iters - 1;
-        const bool ktail = (a.K % BKE) != 0;
         Dma d;
         dma_setup(d, a, m0, n0, wave, lane);
         __syncthreads();  // the previous tile's readers are done with both stages
         if (k_lo >= k_hi) return;
-        dma_issue(d, a, smem, 0, k_lo, m0, n0, wave, ktail && k_lo == last);
-        if (k_lo + 1 < k_hi) dma_issue(d, a, smem, 1, k_lo + 1, m0, n0, wave, ktail && k_lo + 1 == last);
+        dma_issue(d, a, smem, 0, k_lo, m0, n0, wave);
+        if (k_lo + 1 < k_hi) dma_issue(d, a, smem, 1, k_lo + 1, m0, n0, wave);
         if (k_lo + 1 < k_hi) {
             if constexpr (IA + IB == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
             else if constexpr (IA + IB == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
@@ -431,21 +488,16 @@ struct TileKernel {
         __syncthreads();
         Frag f[2];
         load_frag(f[0], smem, 0, 0, wm, wn, lane);
-        for (int kt = k_lo; kt < k_hi; ++kt) {
-            const int st = (kt - k_lo) & 1;
-            load_frag(f[1], smem, st, 1, wm, wn, lane);
-            mma_frag(acc, f[0]);
-            load_frag(f[0], smem, st, 2, wm, wn, lane);
-            mma_frag(acc, f[1]);
-            load_frag(f[1], smem, st, 3, wm, wn, lane);
-            mma_frag(acc, f[0]);
-            asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-            __syncthreads();  // step kt+1 is in LDS everywhere; stage st is drained
-            if (kt + 2 < k_hi) dma_issue(d, a, smem, st, kt + 2, m0, n0, wave, ktail && kt + 2 == last);
-            if (kt + 1 < k_hi) load_frag(f[0], smem, st ^ 1, 0, wm, wn, lane);
-            mma_frag(acc, f[1]);
+        int kt = k_lo;
+        for (; kt + 2 < k_hi; ++kt)
+            kstep<true, true>(acc, f, d, a, smem, (kt - k_lo) & 1, kt, m0, n0, wave, wm, wn, lane);
+        if (kt + 1 < k_hi) {
+            kstep<false, true>(acc, f, d, a, smem, (kt - k_lo) & 1, kt, m0, n0, wave, wm, wn, lane);
+            ++kt;
         }
+        kstep<false, false>(acc, f, d, a, smem, (kt - k_lo) & 1, kt, m0, n0, wave, wm, wn, lane);
     }
+
 
     // Data-parallel kernel: workgroup b computes tile b (in L2-aware order).
     __device__ __forceinline__ static void run_dp(const TileArgs& a) {
@@ -525,9 +577,13 @@ struct TileKernel {
     }
 };
 
+template <int CFG>
+struct TileThreads {
+    static constexpr int value = kConfigs[CFG].wm * kConfigs[CFG].wn * 64;
+};
+
 template <int DT, int CFG, bool B_KMAJ, bool SK>
-__global__ __launch_bounds__(256) void tile_gemm_kernel(TileArgs a) {
-    static_assert(TileKernel<DT, CFG, B_KMAJ>::NT == 256, "every tile config runs four waves");
+__global__ __launch_bounds__(TileThreads<CFG>::value) void tile_gemm_kernel(TileArgs a) {
     if constexpr (SK) TileKernel<DT, CFG, B_KMAJ>::run_sk(a);
     else TileKernel<DT, CFG, B_KMAJ>::run_dp(a);
 }
@@ -539,9 +595,9 @@ template <int DT, int CFG, bool B_KMAJ>
 int launch_tile(const TileArgs& a, void* stream) {
     hipStream_t s = (hipStream_t)stream;
     if (a.dp_tiles > 0)
-        hipLaunchKernelGGL((tile_gemm_kernel<DT, CFG, B_KMAJ, false>), dim3(a.dp_tiles), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((tile_gemm_kernel<DT, CFG, B_KMAJ, false>), dim3(a.dp_tiles), dim3(TileThreads<CFG>::value), 0, s, a);
     if (a.sk_tiles > 0)
-        hipLaunchKernelGGL((tile_gemm_kernel<DT, CFG, B_KMAJ, true>), dim3(a.grid), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((tile_gemm_kernel<DT, CFG, B_KMAJ, true>), dim3(a.grid), dim3(TileThreads<CFG>::value), 0, s, a);
     return (int)hipGetLastError();
 }
 
