@@ -1,0 +1,62 @@
+"""Parity at the full workload sizes, in the launch configuration the benchmark
+uses (the planner's choice), plus forced data-parallel / Stream-K for the
+split-k sweep.  Small products are compared on every entry; the large ones
+on 4096 seeded entries plus all of rows 0 and M-1, computed one by one by
+the oracle."""
+import numpy as np
+import pytest
+
+import synthetic as S
+import tensor_core_mixed_amd as T
+from gpu_util import check, run_tcm, say
+
+pytestmark = pytest.mark.gpu
+
+FULL = {"f16_512", "f32_2048", "skinny_m1", "skinny_m16", "skinny_m64", "skinny_m256"}
+SPLITK = ["skinny_m1", "skinny_m16", "skinny_m64", "skinny_m256", "sk_1536x1536x16384", "sk_3840x3840x4096"]
+
+
+@pytest.fixture(autouse=True)
+def _reset_options():
+    yield
+    T.tcm_set_option("force_mode", 0)
+
+
+def _check_workload(name, mode):
+    p = S.workload(name)
+    T.tcm_set_option("force_mode", mode)
+    say(f"[case] workload {name} M={p.M} N={p.N} K={p.K} dtype={p.dtype} b_col={p.b_col} seed={p.seed} force_mode={mode}")
+    g = S.generate(p)
+    C, plan = run_tcm(p, g)
+    say(f"       plan: {plan}")
+    if name in FULL:
+        err = check(p, g, C)
+    else:
+        ii, jj = S.sample_entries(p)
+        err = check(p, g, C, ii, jj)
+    say(f"       normalised error {err:.3e}")
+    return C, plan
+
+
+@pytest.mark.parametrize("name", list(S.WORKLOADS))
+def test_workload_as_benchmarked(name):
+    _check_workload(name, 0)
+
+
+@pytest.mark.parametrize("name", SPLITK)
+@pytest.mark.parametrize("mode", [1, 2])
+def test_splitk_sweep_both_modes(name, mode):
+    C, plan = _check_workload(name, mode)
+    assert ("mode=dp" if mode == 1 else "mode=streamk") in plan
+
+
+def test_int8_full_rows_bit_exact():
+    """int8 4096^3 with bias + ReLU: 64 complete rows bit-exact (plus the sampled entries above)."""
+    p = S.workload("i8_4096")
+    say(f"[case] i8_4096 64 full rows")
+    g = S.generate(p)
+    C, plan = run_tcm(p, g)
+    rows = np.arange(0, p.M, p.M // 64)
+    ii = np.repeat(rows, p.N)
+    jj = np.tile(np.arange(p.N), rows.size)
+    check(p, g, C, ii, jj)
