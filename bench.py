@@ -118,7 +118,7 @@ def _decode(x, dt):
     return x.astype(np.float64)
 
 
-def cpu_baseline(p, g, unit_scale, rows=1536):
+def cpu_baseline(p, g, unit_scale, rows=4096):
     """The oracle (full-product entry point) on the first `rows` rows of C."""
     import oracle
     o = oracle.get()
@@ -224,6 +224,42 @@ def run_all(args):
             json.dump(rows, f, indent=1)
 
 
+def run_sweep(args):
+    """Every (tile config, mode) on the split-k workloads -> JSON rows (tuning data)."""
+    import torch
+
+    import synthetic as S
+    import tensor_core_mixed_amd as T
+    rows = []
+    names = [n for n in S.WORKLOADS if n.startswith(("skinny", "sk_", "f16_512", "f32_2048", "i8_"))]
+    for name in names:
+        p = S.workload(name)
+        g = S.generate(p)
+        A, B, bias = upload(g, p)
+        C = torch.empty((p.M, p.LDC), dtype=torch.int32 if p.dtype == 3 else torch.float32, device="cuda")
+        s = torch.cuda.current_stream()
+        for cfg in range(T.tcm_config_count()):
+            for mode in (1, 2):
+                T.tcm_set_option("force_config", cfg)
+                T.tcm_set_option("force_mode", mode)
+                call = make_call(p, A, B, bias, C, s.cuda_stream)
+                call()
+                torch.cuda.synchronize()
+                plan = T.tcm_last_plan()
+                if f"config={cfg}" not in plan:
+                    continue
+                ms, _ = time_steps(call, 10, 3, s)
+                rows.append({"workload": name, "config": cfg, "mode": mode, "us": round(ms * 1e3, 2), "plan": plan})
+                print("[sweep] " + json.dumps(rows[-1]), file=sys.stderr, flush=True)
+        T.tcm_set_option("force_config", -1)
+        T.tcm_set_option("force_mode", 0)
+        del A, B, bias, C
+        torch.cuda.empty_cache()
+    if args.report:
+        with open(args.report, "w") as f:
+            json.dump(rows, f, indent=1)
+
+
 def calibrate_copy():
     """One device-to-device copy of exactly 512 MiB (read 512 MiB, write 512 MiB)."""
     import torch
@@ -280,6 +316,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--all", action="store_true")
     ap.add_argument("--report", default=None)
+    ap.add_argument("--sweep", action="store_true", help="time every tile config and mode on the split-k workloads")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize-counters", default=None)
     args = ap.parse_args()
@@ -293,6 +330,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.sweep:
+        run_sweep(args)
         return
     run_bench(args)
 

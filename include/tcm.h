@@ -150,6 +150,17 @@ int tcm_config_info(int index, int dtype, int32_t* bm, int32_t* bn, int32_t* bk,
 int tcm_streamk_range(int64_t sk_tiles, int64_t iters_per_tile, int32_t grid, int32_t wg,
                       int64_t* begin, int64_t* end);
 
+/*
+ * tcm_tile_order -- the output tile (tm, tn) that workgroup t of a
+ * data-parallel launch computes on a tiles_m x tiles_n grid: each XCD's
+ * workgroups get one near-square block of tiles so they share A rows and B
+ * columns in that XCD's L2 (the cache-blocking idea of the tiling step,
+ * kimm240.github.io/tvm, GEMM optimisation Step 2, applied to whole tiles).
+ * Host mirror of the device order, for tests.  TCM_ERR_INVALID_VALUE for
+ * t outside [0, tiles_m * tiles_n) or a grid of 2^31 tiles or more.
+ */
+int tcm_tile_order(int32_t t, int32_t tiles_m, int32_t tiles_n, int32_t* tm, int32_t* tn);
+
 /* Describe the last plan tcm_gemm launched on this thread into buf (NUL-
  * terminated, truncated to len).  Returns the full length. */
 int tcm_last_plan(char* buf, int64_t len);

@@ -63,6 +63,9 @@ def lib():
         L.tcm_streamk_range.argtypes = [i64, i64, ctypes.c_int32, ctypes.c_int32,
                                         ctypes.POINTER(i64), ctypes.POINTER(i64)]
         L.tcm_streamk_range.restype = ci
+        L.tcm_tile_order.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+        L.tcm_tile_order.restype = ci
         L.tcm_last_plan.argtypes = [ctypes.c_char_p, i64]
         L.tcm_last_plan.restype = ci
         L.tcm_release_workspace.restype = None
@@ -118,6 +121,14 @@ def tcm_streamk_range(sk_tiles, iters_per_tile, grid, wg):
     if st != TCM_OK:
         raise TcmError(st, "tcm_streamk_range")
     return b.value, e.value
+
+
+def tcm_tile_order(t, tiles_m, tiles_n):
+    tm, tn = ctypes.c_int32(), ctypes.c_int32()
+    st = lib().tcm_tile_order(t, tiles_m, tiles_n, ctypes.byref(tm), ctypes.byref(tn))
+    if st != TCM_OK:
+        raise TcmError(st, "tcm_tile_order")
+    return tm.value, tn.value
 
 
 def tcm_last_plan():

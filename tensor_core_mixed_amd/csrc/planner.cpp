@@ -19,17 +19,24 @@ namespace tcm {
 namespace {
 
 constexpr int64_t kOffsetLimit = 0x40000000LL;  // buffer-descriptor range used by the kernels
+// Cost-model constants, fitted to measured MI355X runs of every tile config
+// in both modes on the workload set (lone-workgroup step time, fix-up
+// round trips) and to the MFMA rate the kernels reach on N(0,1) inputs
+// (the matrix cores are power-limited: their rate falls with operand entropy).
 constexpr double kLdsBytesPerClk = 200.0;       // measured ds_read_b128 rate per CU
 constexpr double kL2BytesPerClk = 64.0;         // per-CU share of L2 bandwidth
 constexpr double kHbmBytesPerClk = 8.0e12 / 2.4e9;  // whole chip
 constexpr double kStepOverhead = 96.0;          // barrier + wait per K-step
+constexpr double kStepLatency = 500.0;          // lone workgroup: fixed part of a K-step ...
+constexpr double kStepBytesPerClk = 16.0;       // ... plus its copies at this rate
+constexpr double kFixupLatency = 1500.0;        // one device-coherent round trip per partial tile read back
 
 double flops_per_clk(int dt) {
     switch (dt) {
     case F16:
-    case BF16: return 4096.0 * 0.92;
-    case I8: return 8192.0 * 0.92;
-    default: return 256.0 * 0.97;
+    case BF16: return 4096.0 * 0.47;
+    case I8: return 8192.0 * 0.40;
+    default: return 256.0 * 0.82;
     }
 }
 
@@ -39,10 +46,18 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int tile_wg_per_cu(const TileConfig& c) {
     int by_lds = (160 * 1024) / lds_bytes(c);
-    // accumulators of a 128x128 wave tile (256 registers) leave room for one
-    // wave per SIMD; eight-wave workgroups already put two waves on each SIMD
-    int by_regs = ((c.bm / c.wm) * (c.bn / c.wn) >= 128 * 128 || c.wm * c.wn > 4) ? 1 : 2;
+    // registers: a 128x128 wave tile (256 accumulators) or eight-wave
+    // workgroups leave one workgroup per CU; 64x64 wave tiles two; 32x32 four
+    const int wave_tile = (c.bm / c.wm) * (c.bn / c.wn);
+    int by_regs = (wave_tile >= 128 * 128 || c.wm * c.wn > 4) ? 1 : (wave_tile >= 64 * 64 ? 2 : 4);
     return std::max(1, std::min(by_lds, by_regs));
+}
+
+int tile_sk_wg_per_cu(const TileConfig& c) {
+    // the Stream-K kernels carry the partial-tile fix-up on top: only the
+    // 32x32-per-wave config stays small enough for several workgroups per CU
+    const int wave_tile = (c.bm / c.wm) * (c.bn / c.wn);
+    return wave_tile <= 32 * 32 ? std::min(2, (160 * 1024) / lds_bytes(c)) : 1;
 }
 
 bool tile_eligible(const Problem& p, const TileConfig& c) {
@@ -86,7 +101,7 @@ struct Estimate {
     int64_t dp_tiles, sk_tiles;
 };
 
-Estimate estimate(const Problem& p, const TileConfig& c, int cus, int force_mode, int sk_grid) {
+Estimate estimate(const Problem& p, const TileConfig& c, int cus, int force_mode, int sk_grid, int sk_occ_known) {
     const int dt = p.dtype;
     const int bke = bk_elems(dt);
     const int64_t T = cdiv(p.M, c.bm) * cdiv(p.N, c.bn);
@@ -98,6 +113,7 @@ Estimate estimate(const Problem& p, const TileConfig& c, int cus, int force_mode
     const double lds = ((c.bm + c.bn) * (double)kStepBytes + (double)(c.bm * c.wn + c.bn * c.wm) * kStepBytes) / kLdsBytesPerClk;
     const double l2 = (c.bm + c.bn) * (double)kStepBytes / kL2BytesPerClk;
     const double step = std::max(mfma, std::max(lds, l2)) + kStepOverhead;  // per K-step, CU to itself
+    const double lone_step = kStepLatency + (c.bm + c.bn) * (double)kStepBytes / kStepBytesPerClk;
     const double tile_store = (double)c.bm * c.bn * 4 / kL2BytesPerClk;
     const double hbm_floor = ((double)p.M * p.K + (double)p.K * p.N) * elem_bytes(dt) / kHbmBytesPerClk +
                              (double)p.M * p.N * 4 / kHbmBytesPerClk;
@@ -108,7 +124,7 @@ Estimate estimate(const Problem& p, const TileConfig& c, int cus, int force_mode
         const int64_t waves = cdiv(T, slots);
         const int64_t busy = std::min<int64_t>(T, slots);
         const double share = (double)std::min<int64_t>(occ, cdiv(busy, cus));  // workgroups per busy CU
-        dp.cycles = std::max(waves * (I * step + tile_store) * share, hbm_floor);
+        dp.cycles = std::max(waves * (I * std::max(step * share, lone_step) + tile_store * share), hbm_floor);
     }
     // Stream-K: hybrid of (full waves - 1) data-parallel waves, then an even
     // split of the remaining tiles' K-steps over the grid
@@ -117,22 +133,29 @@ Estimate estimate(const Problem& p, const TileConfig& c, int cus, int force_mode
         // every workgroup of the grid must own at least one K-step: the
         // kernel counts a split tile's arrivals as the number of workgroups
         // between its first and last owner
-        int64_t grid = sk_grid > 0 ? sk_grid : slots;
+        const int sk_occ = sk_occ_known > 0 ? sk_occ_known : tile_sk_wg_per_cu(c);
+        int64_t grid = sk_grid > 0 ? sk_grid : (int64_t)cus * sk_occ;
         grid = std::max<int64_t>(1, std::min(grid, T * I));
         const int64_t full = T / grid, rem = T % grid;
-        int64_t dp_tiles = 0;
-        if (full >= 1 && rem != 0) dp_tiles = (full - 1) * grid;
-        else if (rem == 0) dp_tiles = (full - 1) * grid;  // even split: the last wave is Stream-K anyway
-        if (dp_tiles < 0) dp_tiles = 0;
+        int64_t dp_tiles = full >= 1 ? (full - 1) * grid : 0;
+        (void)rem;
         const int64_t sk_tiles = T - dp_tiles;
         const int64_t W = sk_tiles * I;
-        const double per_wg = (double)cdiv(W, grid);
-        const double share = (double)std::min<int64_t>(occ, cdiv(std::min<int64_t>(grid, W), cus));
+        const int64_t per_wg = cdiv(W, grid);
+        const double share = (double)std::min<int64_t>(sk_occ, cdiv(std::min<int64_t>(grid, W), cus));
         const int64_t dp_waves = dp_tiles / grid;
-        // a split tile costs its writers a partial store and the last arrival
-        // the reads of every segment (about two per tile)
-        const double fixup = (W % grid != 0 || I % std::max<int64_t>(1, W / grid) != 0 || sk_tiles < grid) ? 3.0 * tile_store : 0.0;
-        sk.cycles = std::max(dp_waves * (I * step + tile_store) * share + (per_wg * step + tile_store + fixup) * share, hbm_floor);
+        // a split tile: every segment stores its partial (agent-coherent
+        // stores), the last arrival reads all of them back
+        const double partial = (double)c.bm * c.bn * 4;
+        const int64_t nseg = per_wg >= I ? 2 : cdiv(I, per_wg) + 1;
+        const bool splits = (W % grid != 0) || (I % per_wg != 0) || per_wg < I;
+        // only rows below M travel (skinny problems move a sliver of each partial)
+        const double rows_frac = std::min(1.0, (double)std::max<int64_t>(p.M, 1) / c.bm);
+        // the last arrival's reads are latency-bound: about one memory round
+        // trip per segment (the next partial's loads overlap the current add)
+        const double fixup = splits ? rows_frac * partial / kL2BytesPerClk + nseg * (kFixupLatency + rows_frac * partial / kL2BytesPerClk) : 0.0;
+        const double wg_step = std::max(step * share, lone_step);
+        sk.cycles = std::max(dp_waves * (I * wg_step + tile_store * share) + per_wg * wg_step + tile_store * share + fixup, hbm_floor);
         sk.grid = (int)grid;
         sk.dp_tiles = dp_tiles;
         sk.sk_tiles = sk_tiles;
@@ -162,7 +185,7 @@ bool make_plan(const Problem& p, const Options& o, int cus, Plan* out) {
         for (int c = 0; c < kNumConfigs; ++c) {
             if (o.force_config >= 0 && c != o.force_config) continue;
             if (!tile_eligible(p, kConfigs[c])) continue;
-            Estimate e = estimate(p, kConfigs[c], cus, o.force_mode, o.sk_grid);
+            Estimate e = estimate(p, kConfigs[c], cus, o.force_mode, o.sk_grid, o.sk_occ[c]);
             if (e.cycles < best_e.cycles * 0.999) {
                 best = c;
                 best_e = e;

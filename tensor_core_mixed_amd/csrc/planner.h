@@ -13,6 +13,7 @@ struct Options {
     int force_config = -1;  // -1 auto, else tile-table index
     int sk_grid = 0;        // 0 auto, else persistent grid size
     int generic = 0;        // 1: always the generic kernel
+    int sk_occ[kNumConfigs] = {0};  // Stream-K workgroups per CU by config (0: static estimate)
 };
 
 struct Problem {
@@ -40,8 +41,10 @@ constexpr int kDefaultCUs = 256;
 
 // Tile kernel eligibility for a config (alignment, strides, 32-bit offsets).
 bool tile_eligible(const Problem& p, const TileConfig& c);
-// Workgroups of a config that fit on one CU (LDS- and register-limited estimate).
+// Workgroups of a config that fit on one CU (LDS- and register-limited
+// estimate), for the data-parallel and the Stream-K kernel.
 int tile_wg_per_cu(const TileConfig& c);
+int tile_sk_wg_per_cu(const TileConfig& c);
 // Fill `out` for problem p.  Returns false if p is invalid.
 bool make_plan(const Problem& p, const Options& o, int cus, Plan* out);
 // Stream-K share [begin, end) of workgroup wg (same split the kernel uses).

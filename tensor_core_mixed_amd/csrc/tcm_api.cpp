@@ -9,6 +9,7 @@
 #include <mutex>
 #include <string>
 #include <utility>
+#include <vector>
 
 #include "../../include/tcm.h"
 #include "planner.h"
@@ -19,6 +20,20 @@ TileLauncher tile_launcher_f16(int config, bool b_kmajor);
 TileLauncher tile_launcher_bf16(int config, bool b_kmajor);
 TileLauncher tile_launcher_f32(int config, bool b_kmajor);
 TileLauncher tile_launcher_i8(int config, bool b_kmajor);
+int tile_sk_occupancy_f16(int config, bool b_kmajor);
+int tile_sk_occupancy_bf16(int config, bool b_kmajor);
+int tile_sk_occupancy_f32(int config, bool b_kmajor);
+int tile_sk_occupancy_i8(int config, bool b_kmajor);
+
+int tile_sk_occupancy(int config, int dtype, bool b_kmajor) {
+    switch (dtype) {
+    case F16: return tile_sk_occupancy_f16(config, b_kmajor);
+    case BF16: return tile_sk_occupancy_bf16(config, b_kmajor);
+    case F32: return tile_sk_occupancy_f32(config, b_kmajor);
+    case I8: return tile_sk_occupancy_i8(config, b_kmajor);
+    default: return 0;
+    }
+}
 
 TileLauncher tile_launcher(int config, int dtype, bool b_kmajor) {
     switch (dtype) {
@@ -247,6 +262,17 @@ int tcm_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t 
     return TCM_OK;
 }
 
+int tcm_tile_order(int32_t t, int32_t tiles_m, int32_t tiles_n, int32_t* tm, int32_t* tn) {
+    if (tiles_m < 1 || tiles_n < 1 || (int64_t)tiles_m * tiles_n >= (1LL << 31) || t < 0 ||
+        (int64_t)t >= (int64_t)tiles_m * tiles_n || !tm || !tn)
+        return TCM_ERR_INVALID_VALUE;
+    int sm, sn;
+    const int gm = 4;
+    tile_order_shape(tiles_m, tiles_n, gm, &sm, &sn);
+    tile_coords(t, tiles_m, tiles_n, gm, sm, sn, tm, tn);
+    return TCM_OK;
+}
+
 int tcm_last_plan(char* buf, int64_t len) {
     const std::string& s = t_last_plan;
     if (buf && len > 0) {
@@ -307,6 +333,19 @@ int tcm_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
         std::lock_guard<std::mutex> lk(g_mu);
         o = g_opts;
     }
+    // occupancy of the Stream-K kernels of this (dtype, B layout), queried once
+    {
+        static std::map<int, std::vector<int>> occ_cache;
+        std::lock_guard<std::mutex> lk(g_mu);
+        const int key = p.dtype * 2 + (p.b_col ? 1 : 0);
+        auto it = occ_cache.find(key);
+        if (it == occ_cache.end()) {
+            std::vector<int> v(kNumConfigs);
+            for (int c = 0; c < kNumConfigs; ++c) v[c] = tile_sk_occupancy(c, p.dtype, p.b_col);
+            it = occ_cache.emplace(key, v).first;
+        }
+        for (int c = 0; c < kNumConfigs; ++c) o.sk_occ[c] = it->second[c];
+    }
     Plan pl;
     if (!make_plan(p, o, device_cus(dev), &pl)) return TCM_ERR_INVALID_VALUE;
     t_last_plan = describe(pl, p);
@@ -352,6 +391,7 @@ int tcm_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
     a.sk_tiles = (int)pl.sk_tiles;
     a.grid = pl.grid;
     a.group_m = pl.group_m;
+    tile_order_shape(a.tiles_m, a.tiles_n, a.group_m, &a.super_m, &a.super_n);
     a.ws_partial = nullptr;
     a.ws_counter = nullptr;
     if (pl.mode == 2 && pl.sk_tiles > 0) {

@@ -22,12 +22,13 @@ struct TileConfig {
     int bm, bn, wm, wn;
     const char* name;
 };
-constexpr int kNumConfigs = 4;
+constexpr int kNumConfigs = 5;
 constexpr TileConfig kConfigs[kNumConfigs] = {
     {256, 256, 4, 2, "256x256 w4x2"},  // big square problems: 64x128 per wave, two waves per SIMD
     {128, 128, 2, 2, "128x128 w2x2"},  // mid sizes, 2 workgroups per CU
     {32, 256, 1, 4, "32x256 w1x4"},    // skinny M (M <= 32)
     {64, 256, 1, 4, "64x256 w1x4"},    // skinny M (M <= 64)
+    {64, 64, 2, 2, "64x64 w2x2"},      // Stream-K units for skinny / small problems (16 KiB partials)
 };
 inline int lds_bytes(const TileConfig& c) { return 2 * (c.bm + c.bn) * kStepBytes; }
 
@@ -49,10 +50,56 @@ struct TileArgs {
     int dp_tiles;
     int sk_tiles;
     int grid;
-    int group_m;          // tile-order group height (L2 reuse)
+    int group_m;          // tile order: rows per group inside a super-tile
+    int super_m, super_n; // tile order: super-tile (one XCD's share) in tiles
     float* ws_partial;    // Stream-K partial tiles: 2 slots per workgroup, bm*bn 4-byte values each
     int* ws_counter;      // one arrival counter per split tile (zero between launches)
 };
+
+// Tile t -> (tm, tn) for a grid of tiles_m x tiles_n tiles.  Workgroups are
+// dealt to the 8 XCDs round-robin by id, and each XCD has its own L2, so:
+//  1. renumber ids so that XCD x (ids x, x+8, x+16, ...) owns one contiguous
+//     run of the tile order;
+//  2. walk the grid in super-tiles of super_m x super_n tiles (bands of
+//     super_m rows, super-tiles left to right), sized so one run covers about
+//     one near-square super-tile -- an XCD then reads the A rows and B
+//     columns of that block only;
+//  3. inside a super-tile, walk groups of group_m rows column by column, so
+//     the 32 tiles an XCD runs at once form a group_m x (32/group_m) block.
+// Every step is a bijection on [0, tiles_m * tiles_n).
+#if defined(__HIPCC__)
+__host__ __device__
+#endif
+inline void tile_coords(int t, int tiles_m, int tiles_n, int group_m, int super_m, int super_n, int* tm, int* tn) {
+    const int T = tiles_m * tiles_n;
+    const int q = T >> 3, r = T & 7, x = t & 7, local = t >> 3;
+    const int nt = x * q + (x < r ? x : r) + local;
+    const int band = nt / (super_m * tiles_n);
+    const int o = nt - band * super_m * tiles_n;
+    const int h = tiles_m - band * super_m < super_m ? tiles_m - band * super_m : super_m;
+    const int J = o / (h * super_n);
+    const int o2 = o - J * h * super_n;
+    const int w = tiles_n - J * super_n < super_n ? tiles_n - J * super_n : super_n;
+    const int g = o2 / (group_m * w);
+    const int gh = h - g * group_m < group_m ? h - g * group_m : group_m;
+    const int inner = o2 - g * group_m * w;
+    *tm = band * super_m + g * group_m + inner % gh;
+    *tn = J * super_n + inner / gh;
+}
+
+// Super-tile shape for a tiles_m x tiles_n grid: about T/8 tiles, near square.
+inline void tile_order_shape(int tiles_m, int tiles_n, int group_m, int* super_m, int* super_n) {
+    const long long T = (long long)tiles_m * tiles_n;
+    const long long share = (T + 7) / 8;
+    int sm = group_m;
+    while ((long long)(2 * sm) * (2 * sm) <= share && 2 * sm <= tiles_m) sm *= 2;
+    if (sm > tiles_m) sm = tiles_m;
+    long long sn = (share + sm - 1) / sm;
+    if (sn > tiles_n) sn = tiles_n;
+    if (sn < 1) sn = 1;
+    *super_m = sm;
+    *super_n = (int)sn;
+}
 
 // Arguments of the generic (any alignment / layout) kernel.
 struct GenericArgs {
@@ -72,6 +119,9 @@ struct GenericArgs {
 using TileLauncher = int (*)(const TileArgs&, void* stream);
 // config index, dtype, B column-major (K-contiguous) -> launcher, or nullptr
 TileLauncher tile_launcher(int config, int dtype, bool b_kmajor);
+// Stream-K workgroups of a config that fit on one CU, from the compiled
+// kernel's resources (0 if the runtime cannot tell).
+int tile_sk_occupancy(int config, int dtype, bool b_kmajor);
 int launch_generic(int dtype, const GenericArgs& a, void* stream);
 int launch_fill_zero(int* p, int64_t n, void* stream);
 

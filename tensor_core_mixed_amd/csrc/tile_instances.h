@@ -12,7 +12,20 @@ TileLauncher pick_tile(int config, bool b_kmajor) {
     case 1: return b_kmajor ? &launch_tile<DT, 1, true> : &launch_tile<DT, 1, false>;
     case 2: return b_kmajor ? &launch_tile<DT, 2, true> : &launch_tile<DT, 2, false>;
     case 3: return b_kmajor ? &launch_tile<DT, 3, true> : &launch_tile<DT, 3, false>;
+    case 4: return b_kmajor ? &launch_tile<DT, 4, true> : &launch_tile<DT, 4, false>;
     default: return nullptr;
+    }
+}
+
+template <int DT>
+int pick_sk_occupancy(int config, bool b_kmajor) {
+    switch (config) {
+    case 0: return b_kmajor ? sk_occupancy<DT, 0, true>() : sk_occupancy<DT, 0, false>();
+    case 1: return b_kmajor ? sk_occupancy<DT, 1, true>() : sk_occupancy<DT, 1, false>();
+    case 2: return b_kmajor ? sk_occupancy<DT, 2, true>() : sk_occupancy<DT, 2, false>();
+    case 3: return b_kmajor ? sk_occupancy<DT, 3, true>() : sk_occupancy<DT, 3, false>();
+    case 4: return b_kmajor ? sk_occupancy<DT, 4, true>() : sk_occupancy<DT, 4, false>();
+    default: return 0;
     }
 }
 
@@ -21,4 +34,5 @@ TileLauncher pick_tile(int config, bool b_kmajor) {
 #define TCM_TILE_TU(DT, NAME)                                                                          \
     namespace tcm {                                                                                    \
     TileLauncher tile_launcher_##NAME(int config, bool b_kmajor) { return pick_tile<DT>(config, b_kmajor); } \
+    int tile_sk_occupancy_##NAME(int config, bool b_kmajor) { return pick_sk_occupancy<DT>(config, b_kmajor); } \
     }

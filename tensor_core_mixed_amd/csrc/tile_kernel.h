@@ -330,22 +330,8 @@ struct TileKernel {
     }
 
     // ------------------------------------------------------- tile order
-    // Tile t -> (tm, tn).  Workgroups are dealt to the 8 XCDs round-robin by
-    // id, so ids t, t+8, t+16, ... share one XCD's L2: renumber so that each
-    // XCD gets a contiguous run of tiles, then walk runs in groups of
-    // group_m tile rows so that concurrently running tiles of one XCD share
-    // A rows and B columns.
     __device__ __forceinline__ static void tile_coords(int t, const TileArgs& a, int& tm, int& tn) {
-        const int T = a.tiles_m * a.tiles_n;
-        const int q = T >> 3, r = T & 7, x = t & 7, local = t >> 3;
-        const int nt = x * q + min(x, r) + local;
-        const int gsz = a.group_m * a.tiles_n;
-        const int g = nt / gsz;
-        const int first_m = g * a.group_m;
-        const int gm = min(a.tiles_m - first_m, a.group_m);
-        const int inner = nt - g * gsz;
-        tm = first_m + inner % gm;
-        tn = inner / gm;
+        tcm::tile_coords(t, a.tiles_m, a.tiles_n, a.group_m, a.super_m, a.super_n, &tm, &tn);
     }
 
     // ------------------------------------------------------- epilogue
@@ -396,28 +382,64 @@ struct TileKernel {
             }
     }
 
-    // Partial tiles live in the workspace in register order: element
-    // (wave, fm, fn, r, lane), so every store/load is 256 contiguous bytes.
-    __device__ __forceinline__ static AccS* partial_slot(const TileArgs& a, int slot) {
-        return (AccS*)a.ws_partial + (int64_t)slot * BM * BN;
+    // Partial tiles live in the workspace in register order, four
+    // accumulator registers (rows 8q..8q+3 of a 32x32 MFMA tile, one column)
+    // per 16-byte lane vector: element (wave, fm, fn, q, lane) -> 16 bytes.
+    // They cross XCDs (each has its own L2), so they are written and read
+    // with the device-coherent cache policy (sc1) instead of whole-cache
+    // write-back / invalidate fences.  Quads whose rows all lie at or past M
+    // are neither written nor read (out-of-range offset).
+    static constexpr int kCoherent = 16;  // buffer-op cache policy: sc1
+    __device__ __forceinline__ static __amdgpu_buffer_rsrc_t partial_rsrc(const TileArgs& a, int slot) {
+        char* base = (char*)a.ws_partial + (int64_t)slot * BM * BN * 4;
+        return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, BM * BN * 4, kRsrcWord3);
     }
-    __device__ __forceinline__ static void store_partial(const Acc (&acc)[FM][FN], AccS* p, int wave, int lane) {
+    __device__ __forceinline__ static unsigned partial_off(int wave, int fm, int fn, int q, int lane, int wm, int mrem) {
+        const int row = wm * TM + fm * 32 + 8 * q + 4 * (lane >> 5);
+        return row < mrem ? (unsigned)(((((wave * FM + fm) * FN + fn) * 4 + q) * 64 + lane) * 16) : kOOB;
+    }
+    __device__ __forceinline__ static void store_partial(const Acc (&acc)[FM][FN], __amdgpu_buffer_rsrc_t r, int wave, int wm,
+                                                         int lane, int mrem) {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) p[(((wave * FM + fm) * FN + fn) * 16 + r) * 64 + lane] = acc[fm][fn][r];
+                for (int q = 0; q < 4; ++q) {
+                    i4_t v;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = __builtin_bit_cast(int, (AccS)acc[fm][fn][4 * q + e]);
+                    __builtin_amdgcn_raw_buffer_store_b128(v, r, partial_off(wave, fm, fn, q, lane, wm, mrem), 0, kCoherent);
+                }
     }
-    __device__ __forceinline__ static void add_partial(Acc (&acc)[FM][FN], const AccS* p, int wave, int lane, bool first) {
+    struct Partial {
+        i4_t v[FM][FN][4];
+    };
+    __device__ __forceinline__ static void load_partial(Partial& pt, __amdgpu_buffer_rsrc_t r, int wave, int wm, int lane, int mrem) {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    AccS v = p[(((wave * FM + fm) * FN + fn) * 16 + r) * 64 + lane];
-                    acc[fm][fn][r] = first ? v : acc[fm][fn][r] + v;
+                for (int q = 0; q < 4; ++q)
+                    pt.v[fm][fn][q] = __builtin_amdgcn_raw_buffer_load_b128(r, partial_off(wave, fm, fn, q, lane, wm, mrem), 0, kCoherent);
+    }
+    __device__ __forceinline__ static void add_partial(Acc (&acc)[FM][FN], const Partial& pt, bool first) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if constexpr (DT == I8) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            acc[fm][fn][4 * q + e] = first ? pt.v[fm][fn][q][e] : acc[fm][fn][4 * q + e] + pt.v[fm][fn][q][e];
+                    } else {
+                        const f4_t fv = __builtin_bit_cast(f4_t, pt.v[fm][fn][q]);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc[fm][fn][4 * q + e] = first ? fv[e] : acc[fm][fn][4 * q + e] + fv[e];
+                    }
                 }
     }
 
@@ -547,29 +569,47 @@ struct TileKernel {
                 store_tile(acc, a, m0, n0, wm, wn, lane);
                 continue;
             }
-            // Split tile: publish this segment, count arrivals.
+            // Split tile: publish this segment (every wave waits until its
+            // partial stores are acknowledged), then count the arrival.
             const int slot = 2 * wg + (tsk == first_tile ? 0 : 1);
-            store_partial(acc, partial_slot(a, slot), wave, lane);
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+            store_partial(acc, partial_rsrc(a, slot), wave, wm, lane, a.M - m0);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             // workgroups holding a segment of tile tsk: owners of its first and last iteration
             const int64_t x0 = tsk * I, x1 = tsk * I + I - 1;
             const int w_first = (int)(((x0 + 1) * a.grid + W - 1) / W - 1);
             const int w_last = (int)(((x1 + 1) * a.grid + W - 1) / W - 1);
-            if (tid == 0) {
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-                s_flag = __hip_atomic_fetch_add(a.ws_counter + tsk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
+            if (tid == 0) s_flag = __hip_atomic_fetch_add(a.ws_counter + tsk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __syncthreads();
             const int arrived = s_flag;
             __syncthreads();  // s_flag is rewritten by the next split tile
             if (arrived != w_last - w_first) continue;  // not the last arrival
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            // Last arrival: sum every segment's partial in workgroup order.
-            for (int w = w_first; w <= w_last; ++w) {
+            // Last arrival: sum every segment's partial in workgroup order,
+            // the loads of partial w+1 in flight while partial w is added.
+            auto slot_of = [&](int w) {
                 const int64_t ft = ((int64_t)w * W / a.grid) / I;
-                const int sl = 2 * w + (tsk == ft ? 0 : 1);
-                add_partial(acc, partial_slot(a, sl), wave, lane, w == w_first);
+                return 2 * w + (tsk == ft ? 0 : 1);
+            };
+            if constexpr (NW > 4) {
+                // eight waves have 256 registers each: no room for a second buffer
+                for (int w = w_first; w <= w_last; ++w) {
+                    Partial pw;
+                    load_partial(pw, partial_rsrc(a, slot_of(w)), wave, wm, lane, a.M - m0);
+                    add_partial(acc, pw, w == w_first);
+                }
+                store_tile(acc, a, m0, n0, wm, wn, lane);
+                if (tid == 0) __hip_atomic_store(a.ws_counter + tsk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                continue;
+            }
+            // (unrolled by two so both buffers stay in registers)
+            Partial p0, p1;
+            load_partial(p0, partial_rsrc(a, slot_of(w_first)), wave, wm, lane, a.M - m0);
+            for (int w = w_first; w <= w_last; w += 2) {
+                if (w + 1 <= w_last) load_partial(p1, partial_rsrc(a, slot_of(w + 1)), wave, wm, lane, a.M - m0);
+                add_partial(acc, p0, w == w_first);
+                if (w + 1 > w_last) break;
+                if (w + 2 <= w_last) load_partial(p0, partial_rsrc(a, slot_of(w + 2)), wave, wm, lane, a.M - m0);
+                add_partial(acc, p1, false);
             }
             store_tile(acc, a, m0, n0, wm, wn, lane);
             if (tid == 0) __hip_atomic_store(a.ws_counter + tsk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -591,6 +631,15 @@ __global__ __launch_bounds__(TileThreads<CFG>::value) void tile_gemm_kernel(Tile
 // One call = up to two launches on the stream: the data-parallel tiles
 // [0, dp_tiles) with one workgroup each, then the Stream-K tiles on the
 // persistent grid.
+template <int DT, int CFG, bool B_KMAJ>
+int sk_occupancy() {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tile_gemm_kernel<DT, CFG, B_KMAJ, true>, TileThreads<CFG>::value, 0) !=
+        hipSuccess)
+        return 0;
+    return n;
+}
+
 template <int DT, int CFG, bool B_KMAJ>
 int launch_tile(const TileArgs& a, void* stream) {
     hipStream_t s = (hipStream_t)stream;

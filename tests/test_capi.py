@@ -107,7 +107,7 @@ def test_planner_headline_shape_is_data_parallel_big_tiles():
 @pytest.mark.parametrize("M", [1, 16, 64])
 def test_planner_skinny_uses_streamk(M):
     p = T.tcm_plan(M, 4096, 4096, 4096, 4096, 4096, T.TCM_F16_F32)
-    assert p["kernel"] == 1 and p["mode"] == 2 and p["bm"] <= 64
+    assert p["kernel"] == 1 and p["mode"] == 2
     assert p["sk_tiles"] > 0 and p["workspace_bytes"] > 0
 
 
@@ -204,3 +204,28 @@ def test_streamk_cpu_simulation_matches_oracle_int8(oracle_lib, sk_tiles, iters,
         ks = sorted(parts)
         assert ks[0][1] == 0 and ks[-1][2] == iters
         assert all(a[2] == b[1] for a, b in zip(ks, ks[1:]))
+
+
+@pytest.mark.parametrize("tiles_m,tiles_n", [(32, 32), (15, 15), (1, 16), (16, 1), (6, 6), (2, 32), (33, 7),
+                                             (8, 8), (1, 1), (3, 5), (100, 3), (17, 64)])
+def test_tile_order_is_a_bijection(tiles_m, tiles_n):
+    seen = set()
+    for t in range(tiles_m * tiles_n):
+        tm, tn = T.tcm_tile_order(t, tiles_m, tiles_n)
+        assert 0 <= tm < tiles_m and 0 <= tn < tiles_n
+        seen.add((tm, tn))
+    assert len(seen) == tiles_m * tiles_n
+    with pytest.raises(T.TcmError):
+        T.tcm_tile_order(tiles_m * tiles_n, tiles_m, tiles_n)
+
+
+def test_tile_order_gives_each_xcd_one_block():
+    """32 x 32 tiles (8192^2 at 256x256): XCD x = workgroup id mod 8 gets an 8 x 16
+    block, and the 32 workgroups it runs first form a 4 x 8 block."""
+    for x in range(8):
+        tiles = [T.tcm_tile_order(t, 32, 32) for t in range(x, 1024, 8)]
+        rows = {tm for tm, _ in tiles}
+        cols = {tn for _, tn in tiles}
+        assert len(rows) == 8 and len(cols) == 16
+        first = tiles[:32]
+        assert len({tm for tm, _ in first}) == 4 and len({tn for _, tn in first}) == 8

@@ -66,7 +66,7 @@ def test_ragged_tiles_and_k_tail(dtype, shape, b_col):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("config", [0, 1, 2, 3])
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4])
 @pytest.mark.parametrize("mode", [1, 2])
 def test_every_config_and_mode(dtype, config, mode):
     """Each tile config, data-parallel and Stream-K, on a shape with edges in M, N and K."""
