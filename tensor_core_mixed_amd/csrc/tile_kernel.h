@@ -84,14 +84,24 @@ struct Elem<I8> {
 };
 
 // n-contiguous [k][n] tiles (row-major B): swizzle as a function of the k row,
-// so the rows that one transpose read touches land on distinct banks.  CPR
-// (chunks per k row) bounds the result so the chunk stays inside its row.
+// so the rows that one transpose read touches land on distinct banks.  The
+// choice depends on CPR (chunks per k row): with few chunks per row the rows
+// of one read wrap onto the same banks sooner, so narrow tiles use a coarser
+// pattern.  Each case was checked lane by lane against the 64-bank model
+// (half a wave per pass, 8 bytes per lane) for every read the tile issues.
 template <int DT, int CPR>
 __device__ __forceinline__ int swz_mn(int k) {
     int s;
-    if constexpr (DT == I8) s = 2 * (k & 7);               // 8 rows x 16 B per 16-lane group
-    else if constexpr (DT == F32) s = 8 * ((k >> 2) & 1);  // two k rows per wave read
-    else s = 4 * (k & 3);                                  // 4 rows x 32 B per 16-lane group
+    if constexpr (DT == I8) {  // 8 rows x 16 B per 16-lane group
+        if constexpr (CPR == 4) s = 2 * ((k >> 2) & 1);
+        else if constexpr (CPR == 8) s = 2 * ((k >> 1) & 3);
+        else s = 2 * (k & 7);
+    } else if constexpr (DT == F32) {  // two k rows per wave read
+        s = 8 * ((k >> 2) & 1);
+    } else {  // 4 rows x 32 B per 16-lane group
+        if constexpr (CPR == 8) s = 4 * ((k >> 1) & 1);
+        else s = 4 * (k & 3);
+    }
     return s & (CPR - 1);
 }
 
