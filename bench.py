@@ -35,14 +35,32 @@ DTYPE_NAME = {0: "f16", 1: "bf16", 2: "f32", 3: "i8"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{name}.json")
 
 
+KERNEL_SOURCES = ("tcm_internal.h", "tile_kernel.h", "tile_instances.h", "tile_f16.hip", "tile_bf16.hip",
+                  "tile_f32.hip", "tile_i8.hip", "generic_kernel.hip")
+
+
 def kernel_source_hash():
-    """Hash of the HIP sources: counters taken on other code are stale."""
+    """Hash of the device-code sources: counters taken on other kernels are stale."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "tensor_core_mixed_amd", "csrc")
-    for f in sorted(os.listdir(d)):
+    for f in KERNEL_SOURCES:
         with open(os.path.join(d, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
+
+
+def plan_kernels(plan):
+    """Kernel names a tcm_last_plan() string launches (tiled kernel only)."""
+    f = dict(kv.split("=", 1) for kv in plan.split() if "=" in kv)
+    if f.get("kernel") != "tile":
+        return set()
+    b = "true" if f.get("b_col") == "1" else "false"
+    names = set()
+    if int(f.get("dp_tiles", 0)) > 0:
+        names.add(f"void tcm::tile_gemm_kernel<{f['dtype']}, {f['config']}, {b}, false>(tcm::TileArgs)")
+    if int(f.get("sk_tiles", 0)) > 0:
+        names.add(f"void tcm::tile_gemm_kernel<{f['dtype']}, {f['config']}, {b}, true>(tcm::TileArgs)")
+    return names
 
 
 def describe(p):
@@ -105,7 +123,7 @@ def sampled_parity(p, g, C):
         return {"entries": int(ii.size), "mismatches": int(np.sum(got != ref)), "ok": bool(np.all(got == ref))}
     amax = lambda x: float(np.max(np.abs(_decode(x, p.dtype))))
     denom = p.K * amax(g["A"]) * amax(g["B"]) + (float(np.max(np.abs(g["bias"]))) if g["bias"] is not None else 0.0)
-    err = float(np.max(np.abs(got.astype(np.float64) - ref))) / denom
+    err = float(np.max(np.abs(got.astype(np.float64) - ref))) / (denom if denom > 0 else 1.0)
     tol = 1e-5 if p.dtype == 2 else 1e-3
     return {"entries": int(ii.size), "normalised_error": err, "tolerance": tol, "ok": err <= tol}
 
@@ -135,13 +153,16 @@ def cpu_baseline(p, g, unit_scale, rows=4096):
                       f"binary64 accumulation"}
 
 
-def load_traffic(name, launches_per_step):
-    path = TRAFFIC_FILE.format(name=name)
+def load_traffic(p, plan):
+    """Calibrated HBM bytes per launch of the dominant kernel from profiles/, or
+    None when the kernel sources changed since the counters were taken or the
+    plan no longer launches that kernel."""
+    path = TRAFFIC_FILE.format(name=p.name)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("source_hash") != kernel_source_hash():
+    if t.get("source_hash") != kernel_source_hash() or t.get("dominant_kernel") not in plan_kernels(plan):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -151,7 +172,7 @@ def run_bench(args):
 
     import synthetic as S
     import tensor_core_mixed_amd as T
-    p = S.workload(args.workload)
+    p = S.workload(args.workload, **({"dist": args.dist} if args.dist else {}))
     torch.cuda.set_device(0)
     print(f"[bench] workload {p.name}: {describe(p)}", file=sys.stderr, flush=True)
     g = S.generate(p)
@@ -170,10 +191,9 @@ def run_bench(args):
     value = flops / (ms * 1e-3) / unit_scale
     parity = sampled_parity(p, g, C)
     print(f"[bench] {ms:.4f} ms/step, {value:.1f} T(FL)OP/s, parity {parity}", file=sys.stderr, flush=True)
-    launches = 1 if "mode=dp" in plan else 2
     roof = {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK[p.dtype],
             "unit": "TFLOP/s" if p.dtype != 3 else "TOP/s", "frac": round(value / PEAK[p.dtype], 4),
-            "traffic": load_traffic(p.name, launches)}
+            "traffic": load_traffic(p, plan)}
     cpu = cpu_baseline(p, g, unit_scale) if not args.no_cpu else None
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s" if p.dtype != 3 else "TOP/s",
@@ -272,13 +292,24 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes": n * 4}), flush=True)
 
 
-def summarize_counters(d, name):
-    """profiles/traffic_<name>.json from rocprofv3 --pmc runs under d/{fetch,write,copy_fetch,copy_write}."""
+def summarize_counters(d, name, calib=None):
+    """profiles/traffic_<name>.json from rocprofv3 --pmc runs under d/{fetch,write} and the
+    copy calibration under calib/{copy_fetch,copy_write} (calib defaults to d)."""
     import csv
     import glob
 
-    def per_dispatch(sub, counter, kernel_pat):
-        files = glob.glob(os.path.join(d, sub, "**", "*counter_collection.csv"), recursive=True)
+    calib = calib or d
+
+    def per_kernel(root, sub, counter, kernel_pat):
+        out = {}
+        for f in glob.glob(os.path.join(root, sub, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                if r["Counter_Name"] == counter and kernel_pat in r["Kernel_Name"]:
+                    out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return out
+
+    def per_dispatch_in(root, sub, counter, kernel_pat):
+        files = glob.glob(os.path.join(root, sub, "**", "*counter_collection.csv"), recursive=True)
         vals = []
         for f in files:
             for r in csv.DictReader(open(f)):
@@ -286,21 +317,25 @@ def summarize_counters(d, name):
                     vals.append(float(r["Counter_Value"]))
         return vals
 
-    fetch = per_dispatch("fetch", "FETCH_SIZE", "tile_gemm_kernel")
-    write = per_dispatch("write", "WRITE_SIZE", "tile_gemm_kernel")
-    cf = per_dispatch("copy_fetch", "FETCH_SIZE", "copy")
-    cw = per_dispatch("copy_write", "WRITE_SIZE", "copy")
+    # per kernel (a Stream-K plan launches a data-parallel and a Stream-K kernel): medians per dispatch
+    fetch = per_kernel(d, "fetch", "FETCH_SIZE", "tile_gemm_kernel")
+    write = per_kernel(d, "write", "WRITE_SIZE", "tile_gemm_kernel")
+    cf = per_dispatch_in(calib, "copy_fetch", "FETCH_SIZE", "copy")
+    cw = per_dispatch_in(calib, "copy_write", "WRITE_SIZE", "copy")
     copy_kib = 512 * 1024
     f_fac = copy_kib / max(cf) if cf else 1.0
     w_fac = copy_kib / max(cw) if cw else 1.0
-    fk = float(np.median(fetch)) if fetch else None
-    wk = float(np.median(write)) if write else None
-    out = {"kernel": "tile_gemm_kernel", "workload": name, "source_hash": kernel_source_hash(),
-           "fetch_kib_per_dispatch": fk, "write_kib_per_dispatch": wk,
+    kernels = {k: {"fetch_kib_per_dispatch": float(np.median(fetch[k])),
+                   "write_kib_per_dispatch": float(np.median(write.get(k, [0.0]))),
+                   "dispatches": len(fetch[k])} for k in fetch}
+    dom = max(kernels, key=lambda k: kernels[k]["fetch_kib_per_dispatch"]) if kernels else None
+    hbm = None
+    if dom:
+        kd = kernels[dom]
+        hbm = (kd["fetch_kib_per_dispatch"] * f_fac + kd["write_kib_per_dispatch"] * w_fac) * 1024
+    out = {"workload": name, "source_hash": kernel_source_hash(), "dominant_kernel": dom, "kernels": kernels,
            "copy_fetch_kib": max(cf) if cf else None, "copy_write_kib": max(cw) if cw else None,
-           "fetch_scale": f_fac, "write_scale": w_fac,
-           "hbm_bytes_per_launch": (fk * f_fac + wk * w_fac) * 1024 if fk and wk else None,
-           "dispatches": {"fetch": len(fetch), "write": len(write)}}
+           "fetch_scale": f_fac, "write_scale": w_fac, "hbm_bytes_per_launch": hbm}
     path = TRAFFIC_FILE.format(name=name)
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
@@ -314,14 +349,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="f16_8192")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
+    ap.add_argument("--dist", default=None, choices=["uniform", "normal", "uniform12", "ones", "zeros"],
+                    help="override the workload's value distribution (the matrix cores' clock depends on the data)")
     ap.add_argument("--all", action="store_true")
     ap.add_argument("--report", default=None)
     ap.add_argument("--sweep", action="store_true", help="time every tile config and mode on the split-k workloads")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize-counters", default=None)
+    ap.add_argument("--calibration", default=None, help="directory holding the copy-calibration counter runs")
     args = ap.parse_args()
     if args.summarize_counters:
-        summarize_counters(args.summarize_counters, args.workload)
+        summarize_counters(args.summarize_counters, args.workload, args.calibration)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -115,7 +115,7 @@ const char* tcm_status_string(int status);
 int tcm_set_option(const char* key, int64_t value);
 int64_t tcm_get_option(const char* key);
 
-/* ---- planning (host only, no HIP call) ----------------------------------- */
+/* ---- planning and introspection ------------------------------------------ */
 typedef struct {
     int32_t kernel;        /* 0 = generic kernel, 1 = tiled MFMA kernel */
     int32_t config;        /* tile-table index (tiled kernel) or -1 */
@@ -132,7 +132,11 @@ typedef struct {
 /*
  * tcm_plan -- the plan tcm_gemm would use for this problem (same arguments
  * minus the pointers; `aligned` says whether A, B, C, bias would be 16-byte
- * aligned).  Pure host computation.  Returns TCM_OK or TCM_ERR_INVALID_VALUE.
+ * aligned).  Launches nothing and allocates nothing.  With a device present
+ * it plans for the current device exactly as tcm_gemm does (its CU count and
+ * the workgroups per CU the runtime reports for the split-k kernels); with
+ * none it plans for 256 CUs with a static occupancy estimate.
+ * Returns TCM_OK or TCM_ERR_INVALID_VALUE.
  */
 int tcm_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
              int dtype, int epilogue, int aligned, tcm_plan_info* out);

@@ -39,7 +39,7 @@ class Problem:
     K: int
     a_col: bool = False
     b_col: bool = False
-    dist: str = "uniform"      # "uniform" | "normal" | "int"
+    dist: str = "uniform"      # "uniform" | "normal" | "int"; "uniform12" | "ones" | "zeros" for power studies
     seed: int = 0
     bias: bool = False
     relu: bool = False
@@ -118,6 +118,12 @@ def _draw(rng, shape, dist, dtype):
         x = rng.uniform(-1.0, 1.0, size=shape)
     elif dist == "normal":
         x = rng.standard_normal(size=shape)
+    elif dist == "uniform12":  # [1, 2): the exponent never changes, only the mantissa toggles
+        x = rng.uniform(1.0, 2.0, size=shape)
+    elif dist == "ones":
+        x = np.ones(shape)
+    elif dist == "zeros":
+        x = np.zeros(shape)
     else:
         raise ValueError(f"distribution {dist!r} needs an int8 problem")
     return _to_storage(x, dtype)

@@ -71,6 +71,38 @@ int device_cus(int dev) {
     return n;
 }
 
+Options current_options() {
+    std::lock_guard<std::mutex> lk(g_mu);
+    return g_opts;
+}
+
+// Workgroups per CU of the Stream-K kernels of p's (dtype, B layout), as the
+// runtime reports them for the compiled kernels (queried once per pair); a
+// runtime that cannot answer (no device) leaves the planner's static estimate.
+void fill_sk_occupancy(const Problem& p, Options* o) {
+    static std::map<int, std::vector<int>> occ_cache;
+    std::lock_guard<std::mutex> lk(g_mu);
+    const int key = p.dtype * 2 + (p.b_col ? 1 : 0);
+    auto it = occ_cache.find(key);
+    if (it == occ_cache.end()) {
+        std::vector<int> v(kNumConfigs);
+        for (int c = 0; c < kNumConfigs; ++c) v[c] = tile_sk_occupancy(c, p.dtype, p.b_col);
+        (void)hipGetLastError();
+        it = occ_cache.emplace(key, v).first;
+    }
+    for (int c = 0; c < kNumConfigs; ++c) o->sk_occ[c] = it->second[c];
+}
+
+// CUs of the current device, or the default without one.
+int current_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return kDefaultCUs;
+    }
+    return device_cus(dev);
+}
+
 // Grow (never shrink) the workspace of (dev, stream); counters start at zero
 // and every split tile's last arrival resets its counter, so they stay zero
 // between calls.
@@ -240,13 +272,10 @@ int tcm_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t 
     int st = check_problem(M, N, K, lda, ldb, ldc, dtype, epilogue, &p);
     if (st != TCM_OK) return st;
     p.aligned = aligned != 0;
-    Options o;
-    {
-        std::lock_guard<std::mutex> lk(g_mu);
-        o = g_opts;
-    }
+    Options o = current_options();
+    fill_sk_occupancy(p, &o);
     Plan pl;
-    if (!make_plan(p, o, kDefaultCUs, &pl)) return TCM_ERR_INVALID_VALUE;
+    if (!make_plan(p, o, current_cus(), &pl)) return TCM_ERR_INVALID_VALUE;
     out->kernel = pl.kernel == 2 ? 1 : 0;
     out->config = pl.config;
     out->bm = pl.bm;
@@ -328,24 +357,8 @@ int tcm_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
         (void)hipGetLastError();
         return TCM_ERR_HIP;
     }
-    Options o;
-    {
-        std::lock_guard<std::mutex> lk(g_mu);
-        o = g_opts;
-    }
-    // occupancy of the Stream-K kernels of this (dtype, B layout), queried once
-    {
-        static std::map<int, std::vector<int>> occ_cache;
-        std::lock_guard<std::mutex> lk(g_mu);
-        const int key = p.dtype * 2 + (p.b_col ? 1 : 0);
-        auto it = occ_cache.find(key);
-        if (it == occ_cache.end()) {
-            std::vector<int> v(kNumConfigs);
-            for (int c = 0; c < kNumConfigs; ++c) v[c] = tile_sk_occupancy(c, p.dtype, p.b_col);
-            it = occ_cache.emplace(key, v).first;
-        }
-        for (int c = 0; c < kNumConfigs; ++c) o.sk_occ[c] = it->second[c];
-    }
+    Options o = current_options();
+    fill_sk_occupancy(p, &o);
     Plan pl;
     if (!make_plan(p, o, device_cus(dev), &pl)) return TCM_ERR_INVALID_VALUE;
     t_last_plan = describe(pl, p);

@@ -52,3 +52,19 @@ def test_sample_entries():
     assert np.all(ii[4096:4096 + 8192] == 0) and np.all(ii[4096 + 8192:] == p.M - 1)
     ii2, jj2 = S.sample_entries(p)
     assert np.array_equal(ii, ii2) and np.array_equal(jj, jj2)
+
+
+@pytest.mark.parametrize("dist,lo,hi", [("uniform12", 1.0, 2.0), ("ones", 1.0, 1.0), ("zeros", 0.0, 0.0)])
+def test_power_study_distributions(dist, lo, hi):
+    """The extra value distributions (used to show the clock's dependence on the data) stay in range."""
+    for dt in (S.F16, S.BF16, S.F32):
+        p = S.small_problem(dt, 8, 16, 32, dist=dist)
+        g = S.generate(p)
+        for x in (g["A"], g["B"]):
+            if dt == S.F16:
+                v = x.view(np.float16).astype(np.float64)
+            elif dt == S.BF16:
+                v = (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+            else:
+                v = x.astype(np.float64)
+            assert v.min() >= lo and v.max() <= hi
