@@ -228,7 +228,7 @@ def run_all(args):
             call()
             torch.cuda.synchronize()
             plan = T.tcm_last_plan()
-            ms, _ = time_steps(call, max(5, args.steps // 2), 3, s)
+            ms, _ = time_steps(call, max(5, args.steps // 2), 10, s)
             par = sampled_parity(p, g, C)
             v = p.flops / (ms * 1e-3) / 1e12
             rows.append({"workload": name, "mode": ["auto", "dp", "streamk"][mode], "ms": round(ms, 5),
@@ -268,7 +268,7 @@ def run_sweep(args):
                 plan = T.tcm_last_plan()
                 if f"config={cfg}" not in plan:
                     continue
-                ms, _ = time_steps(call, 10, 3, s)
+                ms, _ = time_steps(call, 10, 10, s)
                 rows.append({"workload": name, "config": cfg, "mode": mode, "us": round(ms * 1e3, 2), "plan": plan})
                 print("[sweep] " + json.dumps(rows[-1]), file=sys.stderr, flush=True)
         T.tcm_set_option("force_config", -1)
