@@ -111,6 +111,49 @@ def time_steps(call, steps, warmup, stream_obj):
     return e0.elapsed_time(e1) / steps, wall * 1e3 / steps
 
 
+def per_call_us(call, calls, stream_obj):
+    """Each call bracketed by its own event pair (after the timed block): median and min in us."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for e0, e1 in ev:
+        e0.record(stream_obj)
+        call()
+        e1.record(stream_obj)
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
+    return {"median": round(t[len(t) // 2], 2), "min": round(t[0], 2), "calls": calls}
+
+
+def cold_us(call, calls, stream_obj):
+    """Median time of calls each preceded by a 512 MiB write (outside the event pair) that
+    evicts the 256 MB MALL and the L2s: the HBM-bound shapes with nothing cached."""
+    import torch
+    scratch = torch.empty(512 * 2 ** 20 // 4, dtype=torch.float32, device="cuda")
+    t = []
+    for i in range(calls):
+        scratch.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream_obj)
+        call()
+        e1.record(stream_obj)
+        torch.cuda.synchronize()
+        t.append(e0.elapsed_time(e1) * 1e3)
+    del scratch
+    return round(sorted(t)[len(t) // 2], 2)
+
+
+def gpu_clock():
+    """Current shader clock as rocm-smi reports it (best effort, None if unavailable)."""
+    import re
+    import subprocess
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20).stdout
+    except Exception:
+        return None
+    m = re.search(r"sclk.*?\((\d+)\s*Mhz\)", out, re.IGNORECASE)
+    return m.group(1) + " MHz" if m else None
+
+
 def sampled_parity(p, g, C):
     """Check the sampled entries (4096 seeded + rows 0 and M-1) against the oracle."""
     import oracle
@@ -136,21 +179,36 @@ def _decode(x, dt):
     return x.astype(np.float64)
 
 
-def cpu_baseline(p, g, unit_scale, rows=4096):
-    """The oracle (full-product entry point) on the first `rows` rows of C."""
-    import oracle
-    o = oracle.get()
-    rows = min(rows, p.M)
+def _oracle_rows(o, p, g, rows):
     A = g["A"]
     a_rows = A[:rows] if not p.a_col else A
     t = time.perf_counter()
     o.gemm(rows, p.N, p.K, a_rows, p.LDA, p.a_col, g["B"], p.LDB, p.b_col, p.dtype, bias=g["bias"], relu=p.relu)
-    dt = time.perf_counter() - t
+    return time.perf_counter() - t
+
+
+def cpu_baseline(p, g, unit_scale, rows=4096, per_core_rows=64):
+    """The oracle (full-product entry point) on the first `rows` rows of C with
+    every OpenMP thread, then on `per_core_rows` rows with one thread."""
+    import oracle
+    o = oracle.get()
+    rows = min(rows, p.M)
+    threads = o.max_threads()
+    dt = _oracle_rows(o, p, g, rows)
     flops = 2.0 * rows * p.N * p.K
-    return {"value": flops / dt / unit_scale, "unit": "TFLOP/s" if p.dtype != 3 else "TOP/s", "cores": o.max_threads(),
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"rows 0..{rows - 1} of C ({rows}x{p.N} entries, K={p.K}; {rows / p.M:.4f} of the product), "
-                      f"binary64 accumulation"}
+    out = {"value": flops / dt / unit_scale, "unit": "TFLOP/s" if p.dtype != 3 else "TOP/s", "cores": threads,
+           "kind": "oracle", "seconds": round(dt, 2),
+           "sample": f"rows 0..{rows - 1} of C ({rows}x{p.N} entries, K={p.K}; {rows / p.M:.4f} of the product), "
+                     f"binary64 accumulation"}
+    if per_core_rows:
+        r1 = min(per_core_rows, p.M)
+        o.set_threads(1)
+        try:
+            d1 = _oracle_rows(o, p, g, r1)
+        finally:
+            o.set_threads(threads)
+        out["per_core"] = {"value": 2.0 * r1 * p.N * p.K / d1 / unit_scale, "rows": r1, "seconds": round(d1, 2)}
+    return out
 
 
 def load_traffic(p, plan):
@@ -185,7 +243,10 @@ def run_bench(args):
     torch.cuda.synchronize()
     plan = T.tcm_last_plan()
     print(f"[bench] plan: {plan}", file=sys.stderr, flush=True)
+    clock_before = gpu_clock()
     ms, wall_ms = time_steps(call, args.steps, args.warmup, stream_obj)
+    calls = per_call_us(call, args.steps, stream_obj)
+    clock_after = gpu_clock()
     flops = p.flops
     unit_scale = 1e12
     value = flops / (ms * 1e-3) / unit_scale
@@ -201,7 +262,8 @@ def run_bench(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE_NAME[p.dtype],
         "data": "synthetic",
         "config": {"workload": describe(p), "M": p.M, "N": p.N, "K": p.K, "seed": p.seed, "dist": p.dist,
-                   "plan": plan, "wall_ms_per_step": round(wall_ms, 5), "parity": parity},
+                   "plan": plan, "wall_ms_per_step": round(wall_ms, 5), "per_call_us": calls,
+                   "sclk_before_after": [clock_before, clock_after], "parity": parity},
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -229,14 +291,31 @@ def run_all(args):
             torch.cuda.synchronize()
             plan = T.tcm_last_plan()
             ms, _ = time_steps(call, max(5, args.steps // 2), 10, s)
+            pc = per_call_us(call, max(5, args.steps // 2), s)
             par = sampled_parity(p, g, C)
             v = p.flops / (ms * 1e-3) / 1e12
-            rows.append({"workload": name, "mode": ["auto", "dp", "streamk"][mode], "ms": round(ms, 5),
-                         "tflops": round(v, 2), "frac_peak": round(v / PEAK[p.dtype], 4),
-                         "hbm_frac": round(p.alg_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
-                         "parity_ok": par["ok"], "plan": plan})
-            print("[all] " + json.dumps(rows[-1]), file=sys.stderr, flush=True)
+            row = {"workload": name, "mode": ["auto", "dp", "streamk"][mode], "ms": round(ms, 5),
+                   "per_call_us": pc, "tflops": round(v, 2), "frac_peak": round(v / PEAK[p.dtype], 4),
+                   "hbm_frac": round(p.alg_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                   "parity_ok": par["ok"], "plan": plan}
+            if name.startswith("skinny"):
+                row["cold_median_us"] = cold_us(call, 20, s)
+            rows.append(row)
         T.tcm_set_option("force_mode", 0)
+        mine = [r for r in rows if r["workload"] == name]
+        if len(mine) == 3:
+            lift = mine[1]["ms"] / mine[2]["ms"]
+            for r in mine:
+                r["streamk_lift_dp_over_sk"] = round(lift, 3)
+        if not args.no_cpu:
+            import oracle
+            r_cpu = min(p.M, max(1, int(2e10 // (2 * p.N * p.K))))
+            dt = _oracle_rows(oracle.get(), p, g, r_cpu)
+            for r in mine:
+                r["cpu_oracle"] = {"tflops": round(2.0 * r_cpu * p.N * p.K / dt / 1e12, 5), "rows": r_cpu,
+                                   "seconds": round(dt, 2), "threads": oracle.get().max_threads()}
+        for r in mine:
+            print("[all] " + json.dumps(r), file=sys.stderr, flush=True)
         del A, B, bias, C
         torch.cuda.empty_cache()
     if args.report:

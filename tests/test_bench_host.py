@@ -1,0 +1,69 @@
+"""Host-side logic of bench.py: the one-GPU guard, plan parsing, and the
+checks that keep stale HBM-traffic counters out of the roofline."""
+import json
+import os
+import subprocess
+import sys
+
+import bench
+import synthetic as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+DP_PLAN = ("kernel=tile config=0 tile=256x256x64 mode=dp grid=1024 tiles=1024 iters=128 dp_tiles=1024 sk_tiles=0 "
+           "M=8192 N=8192 K=8192 dtype=0 b_col=1 est_cycles=1")
+SK_PLAN = ("kernel=tile config=4 tile=64x64x64 mode=streamk grid=768 tiles=576 iters=256 dp_tiles=0 sk_tiles=576 "
+           "M=1536 N=1536 K=16384 dtype=0 b_col=0 est_cycles=1")
+HYBRID_PLAN = ("kernel=tile config=1 tile=128x128x64 mode=streamk grid=256 tiles=900 iters=64 dp_tiles=512 "
+               "sk_tiles=388 M=3840 N=3840 K=4096 dtype=0 b_col=0 est_cycles=1")
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert "one GPU" in msg["error"]
+
+
+def test_plan_kernels_names_the_launched_kernels():
+    assert bench.plan_kernels(DP_PLAN) == {"void tcm::tile_gemm_kernel<0, 0, true, false>(tcm::TileArgs)"}
+    assert bench.plan_kernels(SK_PLAN) == {"void tcm::tile_gemm_kernel<0, 4, false, true>(tcm::TileArgs)"}
+    assert bench.plan_kernels(HYBRID_PLAN) == {"void tcm::tile_gemm_kernel<0, 1, false, false>(tcm::TileArgs)",
+                                               "void tcm::tile_gemm_kernel<0, 1, false, true>(tcm::TileArgs)"}
+    assert bench.plan_kernels("kernel=generic tile=64x64 tiles=4 iters=2 M=1 N=1 K=1 dtype=0") == set()
+
+
+def _with_traffic(tmp_path, monkeypatch, record):
+    d = tmp_path / "profiles"
+    d.mkdir()
+    (d / "traffic_f16_8192.json").write_text(json.dumps(record))
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(d / "traffic_{name}.json"))
+
+
+def test_traffic_used_only_for_the_profiled_kernel_and_sources(tmp_path, monkeypatch):
+    p = S.workload("f16_8192")
+    good = {"source_hash": bench.kernel_source_hash(),
+            "dominant_kernel": "void tcm::tile_gemm_kernel<0, 0, true, false>(tcm::TileArgs)",
+            "hbm_bytes_per_launch": 1.5e9}
+    _with_traffic(tmp_path, monkeypatch, good)
+    assert bench.load_traffic(p, DP_PLAN) == 1.5e9
+    # the plan now launches another kernel: the counters do not describe it
+    assert bench.load_traffic(p, SK_PLAN) is None
+
+
+def test_traffic_dropped_when_kernel_sources_change(tmp_path, monkeypatch):
+    p = S.workload("f16_8192")
+    stale = {"source_hash": "0000000000000000",
+             "dominant_kernel": "void tcm::tile_gemm_kernel<0, 0, true, false>(tcm::TileArgs)",
+             "hbm_bytes_per_launch": 1.5e9}
+    _with_traffic(tmp_path, monkeypatch, stale)
+    assert bench.load_traffic(p, DP_PLAN) is None
+
+
+def test_kernel_hash_covers_every_device_source():
+    """Every file with device code is in the hash; host-only files are not."""
+    csrc = os.path.join(ROOT, "tensor_core_mixed_amd", "csrc")
+    device = {f for f in os.listdir(csrc) if f.endswith(".hip") or f in ("tile_kernel.h", "tile_instances.h",
+                                                                          "tcm_internal.h")}
+    assert device == set(bench.KERNEL_SOURCES)

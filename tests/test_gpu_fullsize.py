@@ -60,3 +60,21 @@ def test_int8_full_rows_bit_exact():
     ii = np.repeat(rows, p.N)
     jj = np.tile(np.arange(p.N), rows.size)
     check(p, g, C, ii, jj)
+
+
+@pytest.mark.parametrize("name", list(S.WORKLOADS))
+def test_host_plan_query_matches_launch(name):
+    """tcm_plan (no launch) reports the kernel, config, mode and grid tcm_gemm then launches."""
+    p = S.workload(name)
+    code = p.dtype | (T.TCM_A_COLMAJOR if p.a_col else 0) | (T.TCM_B_COLMAJOR if p.b_col else 0)
+    epi = (T.TCM_EPI_BIAS if p.bias else 0) | (T.TCM_EPI_RELU if p.relu else 0)
+    q = T.tcm_plan(p.M, p.N, p.K, p.LDA, p.LDB, p.LDC, code, epi, True)
+    say(f"[case] plan query {name}: {q}")
+    g = S.generate(p)
+    _, plan = run_tcm(p, g)
+    f = dict(kv.split("=", 1) for kv in plan.split() if "=" in kv)
+    assert f["kernel"] == ("tile" if q["kernel"] == 1 else "generic")
+    assert int(f["config"]) == q["config"]
+    assert f["mode"] == ("dp" if q["mode"] == 1 else "streamk")
+    assert int(f["grid"]) == q["grid"]
+    assert int(f["dp_tiles"]) == q["dp_tiles"] and int(f["sk_tiles"]) == q["sk_tiles"]
