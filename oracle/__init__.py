@@ -8,6 +8,9 @@ library and never imports it.
 Operands are passed in their storage form as numpy arrays:
   dtype 0 (f16) and 1 (bf16): uint16 bit patterns;  2 (f32): float32;
   3 (int8): int8.  Bias: float32 (float types) or int32 (int8).
+  Optional c_in (the reduction's per-element initial value, row-major with
+  leading dimension ldcin): for float problems stored as f16/bf16 (uint16,
+  c_in_type 0/1) or float32 (c_in_type 2); for int8 problems int32.
 Results: float64 for the float types (the exact-input, binary64-accumulated
 value), int32 for int8.
 """
@@ -39,9 +42,10 @@ class Oracle:
         self.path = path
         lib = ctypes.CDLL(path)
         i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
-        lib.oracle_gemm.argtypes = [i64, i64, i64, vp, i64, ci, vp, i64, ci, ci, vp, ci, vp, i64]
+        lib.oracle_gemm.argtypes = [i64, i64, i64, vp, i64, ci, vp, i64, ci, ci, vp, ci, vp, i64, ci, vp, i64]
         lib.oracle_gemm.restype = ci
-        lib.oracle_gemm_entries.argtypes = [i64, i64, i64, vp, i64, ci, vp, i64, ci, ci, vp, ci, vp, vp, i64, vp]
+        lib.oracle_gemm_entries.argtypes = [i64, i64, i64, vp, i64, ci, vp, i64, ci, ci, vp, ci, vp, i64, ci, vp, vp, i64,
+                                            vp]
         lib.oracle_gemm_entries.restype = ci
         lib.oracle_decode.argtypes = [ci, vp, i64, vp]
         lib.oracle_decode.restype = ci
@@ -82,20 +86,39 @@ class Oracle:
             raise OracleError("bias shorter than N")
         return A, B, bias
 
+    def _cin(self, c_in, c_in_type, ldcin, M, N, dtype):
+        """(pointer, ld, type code, array) of the optional initial-value tensor."""
+        if c_in is None:
+            return None, max(N, 1), 0, None
+        if dtype == I8:
+            c_in_type = I8
+            c_in = np.ascontiguousarray(c_in, dtype=np.int32)
+        else:
+            if c_in_type not in (F16, BF16, F32):
+                raise OracleError("c_in_type must be 0 (f16), 1 (bf16) or 2 (f32)")
+            c_in = self._buf(c_in, c_in_type)
+        ldcin = ldcin if ldcin is not None else max(N, 1)
+        self._check_extent(c_in, M, N, ldcin, "c_in")
+        return c_in.ctypes.data, ldcin, c_in_type, c_in
+
     # -- entry points ----------------------------------------------------
-    def gemm(self, M, N, K, A, lda, a_col, B, ldb, b_col, dtype, bias=None, relu=False):
+    def gemm(self, M, N, K, A, lda, a_col, B, ldb, b_col, dtype, bias=None, relu=False, c_in=None, c_in_type=None,
+             ldcin=None):
         """Full C (M x N): float64 for float types, int32 for int8."""
         A, B, bias = self._prep(M, N, K, A, lda, a_col, B, ldb, b_col, dtype, bias)
+        cp, cld, ct, _keep = self._cin(c_in, c_in_type, ldcin, M, N, dtype)
         C = np.zeros((M, N), dtype=np.int32 if dtype == I8 else np.float64)
         rc = self.lib.oracle_gemm(M, N, K, A.ctypes.data, lda, int(a_col), B.ctypes.data, ldb, int(b_col),
                                   dtype, None if bias is None else bias.ctypes.data, int(relu),
-                                  C.ctypes.data, max(N, 1))
+                                  cp, cld, ct, C.ctypes.data, max(N, 1))
         self._rc(rc)
         return C
 
-    def gemm_entries(self, M, N, K, A, lda, a_col, B, ldb, b_col, dtype, ii, jj, bias=None, relu=False):
+    def gemm_entries(self, M, N, K, A, lda, a_col, B, ldb, b_col, dtype, ii, jj, bias=None, relu=False, c_in=None,
+                     c_in_type=None, ldcin=None):
         """C at the listed (ii[t], jj[t]) entries, same arithmetic as gemm()."""
         A, B, bias = self._prep(M, N, K, A, lda, a_col, B, ldb, b_col, dtype, bias)
+        cp, cld, ct, _keep = self._cin(c_in, c_in_type, ldcin, M, N, dtype)
         ii = np.ascontiguousarray(ii, dtype=np.int64)
         jj = np.ascontiguousarray(jj, dtype=np.int64)
         if ii.shape != jj.shape:
@@ -103,7 +126,7 @@ class Oracle:
         out = np.zeros(ii.size, dtype=np.int32 if dtype == I8 else np.float64)
         rc = self.lib.oracle_gemm_entries(M, N, K, A.ctypes.data, lda, int(a_col), B.ctypes.data, ldb, int(b_col),
                                           dtype, None if bias is None else bias.ctypes.data, int(relu),
-                                          ii.ctypes.data, jj.ctypes.data, ii.size, out.ctypes.data)
+                                          cp, cld, ct, ii.ctypes.data, jj.ctypes.data, ii.size, out.ctypes.data)
         self._rc(rc)
         return out
 

@@ -7,7 +7,7 @@
  *
  * What it computes (one definition, written out):
  *
- *     C[i][j] = epi( bias[j] + sum_{k=0}^{K-1} a(i,k) * b(k,j) )
+ *     C[i][j] = epi( c_in[i][j] + bias[j] + sum_{k=0}^{K-1} a(i,k) * b(k,j) )
  *
  *   - The problem statement is the matrix product with an added bias,
  *     Output = Input * Weight + Bias, from the FuseReductionEpilogue series
@@ -18,6 +18,11 @@
  *     Design": reduction init = Bias instead of 0).  The oracle therefore
  *     starts every accumulator at bias[j] (or 0 without bias) and adds the
  *     products in ascending k.
+ *   - The same post's generalisation, an arbitrary per-element tensor as the
+ *     reduction's initial value, is the optional c_in: when given, the
+ *     accumulator starts at c_in[i][j] + bias[j].  c_in is stored row-major
+ *     with its own leading dimension, as f16, bf16 or f32 for the float
+ *     types (cin_type 0, 1, 2) and as int32 for int8.
  *   - ReLU after the bias is the Conv2d + Bias + ReLU pattern (same page, post
  *     "Implement and enable Conv2d-Reshape-Add-ReLU fusion"); epi(x) is x, or
  *     x > 0 ? x : 0 with ReLU.
@@ -33,6 +38,7 @@
  *   a(i,k) = A[i*lda + k]     (a_col == 0, row-major)   or  A[k*lda + i]  (a_col == 1)
  *   b(k,j) = B[k*ldb + j]     (b_col == 0, row-major)   or  B[j*ldb + k]  (b_col == 1)
  *   C[i*ldc + j]  -- double for the float types, int32 for int8.
+ *   c_in[i*ldcin + j]  -- optional; see above.
  *
  * Decoders are written from the IEEE 754 binary16 field layout (1 sign bit,
  * 5 exponent bits, bias 15, 10 fraction bits) and the bfloat16 layout (1 sign
@@ -112,6 +118,23 @@ static int check_args(int64_t M, int64_t N, int64_t K, int64_t lda, int a_col, i
     return 0;
 }
 
+static int check_cin(const void* cin, int64_t ldcin, int cin_type, int64_t N, int dtype) {
+    if (!cin) return 0;
+    if (ldcin < N || ldcin < 1) return 1;
+    if (dtype == OR_I8) return cin_type != OR_I8;  /* int32 storage */
+    return cin_type < OR_F16 || cin_type > OR_F32;
+}
+
+/* initial value of C[i][j]: c_in (if any) plus bias (if any) */
+static double init_f(const void* cin, int64_t ldcin, int cin_type, const float* bias, int64_t i, int64_t j) {
+    double v = cin ? elem_f(cin, cin_type, i * ldcin + j) : 0.0;
+    return bias ? v + (double)bias[j] : v;
+}
+static int64_t init_i(const int32_t* cin, int64_t ldcin, const int32_t* bias, int64_t i, int64_t j) {
+    int64_t v = cin ? (int64_t)cin[i * ldcin + j] : 0;
+    return bias ? v + bias[j] : v;
+}
+
 /* ---- decode a whole operand (used by tests to pin the decoders) -------- */
 
 int oracle_decode(int dtype, const void* X, int64_t n, double* out) {
@@ -127,8 +150,10 @@ int oracle_gemm(int64_t M, int64_t N, int64_t K,
                 const void* A, int64_t lda, int a_col,
                 const void* B, int64_t ldb, int b_col,
                 int dtype, const void* bias, int relu,
+                const void* cin, int64_t ldcin, int cin_type,
                 void* C, int64_t ldc) {
     if (check_args(M, N, K, lda, a_col, ldb, b_col, dtype) || ldc < N) return 1;
+    if (check_cin(cin, ldcin, cin_type, N, dtype)) return 1;
     if (M == 0 || N == 0) return 0;
     int overflow = 0;
 
@@ -145,7 +170,10 @@ int oracle_gemm(int64_t M, int64_t N, int64_t K,
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : overflow)
         for (int64_t i = 0; i < M; ++i) {
             int64_t* acc = (int64_t*)malloc(sizeof(int64_t) * (size_t)N);
-            for (int64_t j = 0; j < N; ++j) acc[j] = bi ? bi[j] : 0;
+            for (int64_t j = 0; j < N; ++j) {
+                acc[j] = init_i((const int32_t*)cin, ldcin, bi, i, j);
+                if (acc[j] > INT32_MAX || acc[j] < INT32_MIN) overflow = 1;
+            }
             for (int64_t k = 0; k < K; ++k) {
                 int64_t aik = a8[a_off(i, k, lda, a_col)];
                 const int32_t* brow = bd + k * N;
@@ -174,7 +202,7 @@ int oracle_gemm(int64_t M, int64_t N, int64_t K,
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t i = 0; i < M; ++i) {
         double* acc = c + i * ldc;
-        for (int64_t j = 0; j < N; ++j) acc[j] = bf ? (double)bf[j] : 0.0;
+        for (int64_t j = 0; j < N; ++j) acc[j] = init_f(cin, ldcin, cin_type, bf, i, j);
         for (int64_t k = 0; k < K; ++k) {
             double aik = elem_f(A, dtype, a_off(i, k, lda, a_col));
             const double* brow = bd + k * N;
@@ -193,8 +221,10 @@ int oracle_gemm_entries(int64_t M, int64_t N, int64_t K,
                         const void* A, int64_t lda, int a_col,
                         const void* B, int64_t ldb, int b_col,
                         int dtype, const void* bias, int relu,
+                        const void* cin, int64_t ldcin, int cin_type,
                         const int64_t* ii, const int64_t* jj, int64_t n, void* out) {
     if (check_args(M, N, K, lda, a_col, ldb, b_col, dtype) || n < 0) return 1;
+    if (check_cin(cin, ldcin, cin_type, N, dtype)) return 1;
     for (int64_t t = 0; t < n; ++t)
         if (ii[t] < 0 || ii[t] >= M || jj[t] < 0 || jj[t] >= N) return 1;
     int overflow = 0;
@@ -206,7 +236,8 @@ int oracle_gemm_entries(int64_t M, int64_t N, int64_t K,
 #pragma omp parallel for schedule(dynamic, 16) reduction(| : overflow)
         for (int64_t t = 0; t < n; ++t) {
             int64_t i = ii[t], j = jj[t];
-            int64_t acc = bi ? bi[j] : 0;
+            int64_t acc = init_i((const int32_t*)cin, ldcin, bi, i, j);
+            if (acc > INT32_MAX || acc < INT32_MIN) overflow = 1;
             for (int64_t k = 0; k < K; ++k) {
                 acc += (int64_t)a8[a_off(i, k, lda, a_col)] * (int64_t)b8[b_off(k, j, ldb, b_col)];
                 if (acc > INT32_MAX || acc < INT32_MIN) overflow = 1;
@@ -221,7 +252,7 @@ int oracle_gemm_entries(int64_t M, int64_t N, int64_t K,
 #pragma omp parallel for schedule(dynamic, 16)
     for (int64_t t = 0; t < n; ++t) {
         int64_t i = ii[t], j = jj[t];
-        double acc = bf ? (double)bf[j] : 0.0;
+        double acc = init_f(cin, ldcin, cin_type, bf, i, j);
         for (int64_t k = 0; k < K; ++k)
             acc += elem_f(A, dtype, a_off(i, k, lda, a_col)) * elem_f(B, dtype, b_off(k, j, ldb, b_col));
         o[t] = relu ? relu_f(acc) : acc;

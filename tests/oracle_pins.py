@@ -299,6 +299,109 @@ def pin_degenerate(o):
         assert o.gemm(0, 4, 3, A, 3, False, to_storage(np.zeros(12), dtype), 4, False, dtype).shape == (0, 4)
 
 
+def _cin_store(logical, ctype, ld):
+    """Row-major initial-value tensor in storage (padding: NaN / int32 sentinel)."""
+    logical = np.asarray(logical, dtype=np.float64)
+    R, C = logical.shape
+    if ctype == I8:
+        out = np.full((R, ld), -77777, dtype=np.int32)
+        out[:, :C] = logical.astype(np.int32)
+        return out.reshape(-1)
+    s = to_storage(logical, ctype)
+    out = np.full((R, ld), pad_value(ctype), dtype=s.dtype)
+    out[:, :C] = s
+    return out.reshape(-1)
+
+
+def _cin_types(dtype):
+    return (I8,) if dtype == I8 else (F16, BF16, F32)
+
+
+def pin_init_tensor_closed_forms(o):
+    """With an initial-value tensor c_in (stored f16 / bf16 / f32, or int32 for
+    int8; row-major with padding past its leading dimension):
+      K = 0            -> C = epi(c_in + bias), c_in decoded by numpy / torch;
+      all-ones, K = 37 -> C = c_in + 37 exactly;
+    with an asymmetric c_in, so a transposed or mis-strided read fails."""
+    rng = np.random.default_rng(21)
+    M, N = 4, 6
+    for dtype in ALL:
+        for ct in _cin_types(dtype):
+            ld = N + 3
+            logical = (rng.integers(-40, 40, size=(M, N)) if ct == I8
+                       else random_logical(rng, (M, N), ct, -8.0, 8.0))
+            cin = _cin_store(logical, ct, ld)
+            want_cin = logical if ct == I8 else lib_decode(to_storage(logical, ct), ct).reshape(M, N)
+            bias = (rng.integers(-9, 9, size=N).astype(np.int32) if dtype == I8
+                    else rng.integers(-9, 9, size=N).astype(np.float32))
+            Z = to_storage(np.zeros(1), dtype)
+            C = o.gemm(M, N, 0, Z, 1, False, Z, N, False, dtype, bias=bias, relu=True, c_in=cin, c_in_type=ct,
+                       ldcin=ld)
+            assert np.array_equal(C.astype(np.float64), np.maximum(want_cin + bias, 0)), \
+                f"K=0 with c_in != relu(c_in + bias) (dtype {dtype}, c_in type {ct})"
+            K = 37
+            ones = np.ones((M, K))
+            C = run_cin(o, ones, np.ones((K, N)), dtype, cin, ct, ld)
+            assert np.array_equal(C.astype(np.float64), want_cin + K), f"ones with c_in (dtype {dtype}, {ct})"
+
+
+def run_cin(o, A_log, B_log, dtype, cin, ct, ld, bias=None, relu=False):
+    M, K = A_log.shape
+    N = B_log.shape[1]
+    A = store_matrix(A_log, dtype, False, K)
+    B = store_matrix(B_log, dtype, False, N)
+    return o.gemm(M, N, K, A, K, False, B, N, False, dtype, bias=bias, relu=relu, c_in=cin, c_in_type=ct, ldcin=ld)
+
+
+def pin_init_tensor_linearity(o):
+    """int8: C(A, B, c_in) - C(A, B, no c_in) == c_in exactly, entry by entry
+    (a dropped, doubled or shifted c_in changes the difference); the int32
+    range check covers the initial value too."""
+    rng = np.random.default_rng(22)
+    M, N, K = 7, 9, 33
+    A = rng.integers(-128, 128, size=(M, K)).astype(np.float64)
+    B = rng.integers(-128, 128, size=(K, N)).astype(np.float64)
+    X = rng.integers(-10 ** 6, 10 ** 6, size=(M, N))
+    cin = _cin_store(X, I8, N + 2)
+    C1 = run_cin(o, A, B, I8, cin, I8, N + 2)
+    A8, B8 = store_matrix(A, I8, False, K), store_matrix(B, I8, False, N)
+    C0 = o.gemm(M, N, K, A8, K, False, B8, N, False, I8)
+    assert np.array_equal(C1.astype(np.int64) - C0.astype(np.int64), X)
+    # c_in + bias leaves int32 although the final sum (after a product of -1) is back inside
+    big = _cin_store(np.full((1, 1), 2 ** 31 - 1), I8, 1)
+    one, neg = to_storage(np.ones(1), I8), to_storage(-np.ones(1), I8)
+    b1 = np.ones(1, dtype=np.int32)
+    for call in (lambda: o.gemm(1, 1, 1, neg, 1, False, one, 1, False, I8, bias=b1, c_in=big, ldcin=1),
+                 lambda: o.gemm_entries(1, 1, 1, neg, 1, False, one, 1, False, I8, [0], [0], bias=b1, c_in=big,
+                                        ldcin=1)):
+        try:
+            call()
+        except OverflowError:
+            pass
+        else:
+            raise AssertionError("int32 overflow through c_in not reported")
+
+
+def pin_init_tensor_entries(o):
+    """Per-entry and full entry points agree bit-for-bit with a c_in (every type)."""
+    rng = np.random.default_rng(23)
+    M, N, K = 9, 11, 40
+    for dtype in ALL:
+        for ct in _cin_types(dtype):
+            A_log = random_logical(rng, (M, K), dtype)
+            B_log = random_logical(rng, (K, N), dtype)
+            X = rng.integers(-500, 500, size=(M, N)) if ct == I8 else random_logical(rng, (M, N), ct)
+            cin = _cin_store(X, ct, N + 1)
+            A = store_matrix(A_log, dtype, False, K)
+            B = store_matrix(B_log, dtype, True, K)
+            C = o.gemm(M, N, K, A, K, False, B, K, True, dtype, c_in=cin, c_in_type=ct, ldcin=N + 1)
+            ii, jj = np.meshgrid(np.arange(M), np.arange(N), indexing="ij")
+            E = o.gemm_entries(M, N, K, A, K, False, B, K, True, dtype, ii.ravel(), jj.ravel(), c_in=cin,
+                               c_in_type=ct, ldcin=N + 1)
+            assert np.array_equal(E.reshape(M, N), C), f"entries != full with c_in (dtype {dtype}, {ct})"
+
+
 ALL_PINS = [pin_decoders, pin_identity, pin_closed_forms, pin_printed_value, pin_bruteforce_exact,
             pin_library_matmul, pin_transpose, pin_linearity_int, pin_entries_match_full,
-            pin_int32_range, pin_degenerate]
+            pin_int32_range, pin_degenerate, pin_init_tensor_closed_forms, pin_init_tensor_linearity,
+            pin_init_tensor_entries]

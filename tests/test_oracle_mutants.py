@@ -19,10 +19,19 @@ MUTANTS = [
     ("transposed_b", "return b_col ? j * ldb + k : k * ldb + j;", "return b_col ? k * ldb + j : j * ldb + k;"),
     ("transposed_a", "return a_col ? k * lda + i : i * lda + k;", "return a_col ? i * lda + k : k * lda + i;"),
     ("b_ignores_col_flag", "return b_col ? j * ldb + k : k * ldb + j;", "return k * ldb + j;"),
-    ("bias_by_row_int", "bi ? bi[j] : 0", "bi ? bi[i] : 0"),
-    ("bias_by_row_float", "bf ? (double)bf[j] : 0.0", "bf ? (double)bf[i] : 0.0"),
-    ("bias_dropped_float", "bf ? (double)bf[j] : 0.0", "0.0"),
-    ("bias_twice_int", "acc[j] = bi ? bi[j] : 0;", "acc[j] = bi ? 2 * bi[j] : 0;"),
+    ("bias_by_row_int", "return bias ? v + bias[j] : v;", "return bias ? v + bias[i] : v;"),
+    ("bias_by_row_float", "return bias ? v + (double)bias[j] : v;", "return bias ? v + (double)bias[i] : v;"),
+    ("bias_dropped_float", "return bias ? v + (double)bias[j] : v;", "return v;"),
+    ("bias_twice_int", "return bias ? v + bias[j] : v;", "return bias ? v + 2 * bias[j] : v;"),
+    ("cin_ignored_float", "double v = cin ? elem_f(cin, cin_type, i * ldcin + j) : 0.0;", "double v = 0.0;"),
+    ("cin_ignored_int", "int64_t v = cin ? (int64_t)cin[i * ldcin + j] : 0;", "int64_t v = 0;"),
+    ("cin_transposed_float", "elem_f(cin, cin_type, i * ldcin + j)", "elem_f(cin, cin_type, j * ldcin + i)"),
+    ("cin_transposed_int", "(int64_t)cin[i * ldcin + j]", "(int64_t)cin[j * ldcin + i]"),
+    ("cin_ignores_ld", "acc[j] = init_f(cin, ldcin, cin_type, bf, i, j);", "acc[j] = init_f(cin, N, cin_type, bf, i, j);"),
+    ("cin_wrong_type", "elem_f(cin, cin_type,", "elem_f(cin, OR_F16,"),
+    ("cin_negated_int", "int64_t v = cin ? (int64_t)cin[i * ldcin + j] : 0;", "int64_t v = cin ? -(int64_t)cin[i * ldcin + j] : 0;"),
+    ("cin_overflow_unchecked", "            if (acc > INT32_MAX || acc < INT32_MIN) overflow = 1;\n            for (int64_t k = 0; k < K; ++k) {",
+     "            for (int64_t k = 0; k < K; ++k) {"),
     ("relu_abs", "return x > 0.0 ? x : 0.0;", "return x > 0.0 ? x : -x;"),
     ("relu_int_missing", "if (relu && !(v > 0)) v = 0;", ""),
     ("f16_exponent_off_by_one", "expo - 25", "expo - 24"),
