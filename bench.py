@@ -64,9 +64,29 @@ def plan_kernels(plan):
 
 
 def describe(p):
+    acc = "int32" if p.dtype == 3 else "f32"
+    out = acc if p.c_type == "acc" else p.c_type
     return (f"{DTYPE_NAME[p.dtype]} GEMM {p.M}x{p.N}x{p.K}, A {'col' if p.a_col else 'row'}-major, "
-            f"B {'col' if p.b_col else 'row'}-major, {'int32' if p.dtype == 3 else 'f32'} accumulate and output"
+            f"B {'col' if p.b_col else 'row'}-major, {acc} accumulate, {out} output"
+            + (", C's contents as the initial value" if p.accum else "")
             + (", bias + ReLU epilogue" if p.bias else ""))
+
+
+def make_c(p):
+    """C on the device in its storage type (M x ldc)."""
+    import torch
+    dt = {"f16": torch.float16, "bf16": torch.bfloat16}.get(p.c_type, torch.int32 if p.dtype == 3 else torch.float32)
+    return torch.empty((max(p.M, 1), p.LDC), dtype=dt, device="cuda")
+
+
+def reset_c(p, g, C):
+    """With accumulation, put the initial-value tensor back into C (no-op otherwise)."""
+    import torch
+    if p.accum:
+        cin = g["C_in"]
+        src = (torch.from_numpy(cin.view(np.int16).copy()).view(C.dtype) if cin.dtype == np.uint16
+               else torch.from_numpy(cin.copy()))
+        C.copy_(src.reshape(C.shape))
 
 
 def upload(g, p):
@@ -83,7 +103,8 @@ def upload(g, p):
 def make_call(p, A, B, bias, C, stream):
     import tensor_core_mixed_amd as T
     code = p.dtype | (T.TCM_A_COLMAJOR if p.a_col else 0) | (T.TCM_B_COLMAJOR if p.b_col else 0)
-    epi = (T.TCM_EPI_BIAS if p.bias else 0) | (T.TCM_EPI_RELU if p.relu else 0)
+    code |= {"acc": 0, "f16": T.TCM_C_F16, "bf16": T.TCM_C_BF16}[p.c_type]
+    epi = (T.TCM_EPI_BIAS if p.bias else 0) | (T.TCM_EPI_RELU if p.relu else 0) | (T.TCM_EPI_ACCUM if p.accum else 0)
     args = (p.M, p.N, p.K, A.data_ptr(), p.LDA, B.data_ptr(), p.LDB, C.data_ptr(), p.LDC, code,
             bias.data_ptr() if bias is not None else None, epi, stream)
 
@@ -154,19 +175,32 @@ def gpu_clock():
     return m.group(1) + " MHz" if m else None
 
 
-def sampled_parity(p, g, C):
-    """Check the sampled entries (4096 seeded + rows 0 and M-1) against the oracle."""
+def _oracle_sampled_check(p, g, C):
+    """(CPU leg) The sampled entries (4096 seeded + rows 0 and M-1) of C after one
+    call from the initial state, against the oracle's values."""
+    import torch
+
     import oracle
     import synthetic as S
     ii, jj = S.sample_entries(p)
-    got = C.cpu().numpy()[ii, jj] if C.shape[1] == p.N else C.cpu().numpy().reshape(p.M, p.LDC)[ii, jj]
+    Cc = C.float() if C.dtype in (torch.float16, torch.bfloat16) else C
+    got = Cc.cpu().numpy().reshape(-1, p.LDC)[ii, jj]
+    cin = {}
+    if p.accum:
+        cin = {"c_in": g["C_in"].reshape(-1), "c_in_type": S.C_TYPE_CODE.get(p.c_type, S.F32), "ldcin": p.LDC}
     ref = oracle.get().gemm_entries(p.M, p.N, p.K, g["A"], p.LDA, p.a_col, g["B"], p.LDB, p.b_col, p.dtype, ii, jj,
-                                    bias=g["bias"], relu=p.relu)
+                                    bias=g["bias"], relu=p.relu, **cin)
     if p.dtype == 3:
         return {"entries": int(ii.size), "mismatches": int(np.sum(got != ref)), "ok": bool(np.all(got == ref))}
-    amax = lambda x: float(np.max(np.abs(_decode(x, p.dtype))))
-    denom = p.K * amax(g["A"]) * amax(g["B"]) + (float(np.max(np.abs(g["bias"]))) if g["bias"] is not None else 0.0)
-    err = float(np.max(np.abs(got.astype(np.float64) - ref))) / (denom if denom > 0 else 1.0)
+
+    def amax(x, dt):
+        return float(np.max(np.abs(_decode(x, dt))))
+    denom = p.K * amax(g["A"], p.dtype) * amax(g["B"], p.dtype)
+    denom += float(np.max(np.abs(g["bias"]))) if g["bias"] is not None else 0.0
+    denom += amax(g["C_in"], S.C_TYPE_CODE.get(p.c_type, S.F32)) if p.accum else 0.0
+    u = {"acc": 0.0, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}[p.c_type]  # half an ulp of a 16-bit C
+    excess = np.abs(got.astype(np.float64) - ref) - u * np.abs(ref)
+    err = max(float(np.max(excess)), 0.0) / (denom if denom > 0 else 1.0)
     tol = 1e-5 if p.dtype == 2 else 1e-3
     return {"entries": int(ii.size), "normalised_error": err, "tolerance": tol, "ok": err <= tol}
 
@@ -235,10 +269,10 @@ def run_bench(args):
     print(f"[bench] workload {p.name}: {describe(p)}", file=sys.stderr, flush=True)
     g = S.generate(p)
     A, B, bias = upload(g, p)
-    out_dt = torch.int32 if p.dtype == 3 else torch.float32
-    C = torch.empty((p.M, p.LDC), dtype=out_dt, device="cuda")
+    C = make_c(p)
     stream_obj = torch.cuda.current_stream()
     call = make_call(p, A, B, bias, C, stream_obj.cuda_stream)
+    reset_c(p, g, C)
     call()
     torch.cuda.synchronize()
     plan = T.tcm_last_plan()
@@ -250,12 +284,19 @@ def run_bench(args):
     flops = p.flops
     unit_scale = 1e12
     value = flops / (ms * 1e-3) / unit_scale
-    parity = sampled_parity(p, g, C)
-    print(f"[bench] {ms:.4f} ms/step, {value:.1f} T(FL)OP/s, parity {parity}", file=sys.stderr, flush=True)
+    print(f"[bench] {ms:.4f} ms/step, {value:.1f} T(FL)OP/s", file=sys.stderr, flush=True)
     roof = {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK[p.dtype],
             "unit": "TFLOP/s" if p.dtype != 3 else "TOP/s", "frac": round(value / PEAK[p.dtype], 4),
             "traffic": load_traffic(p, plan)}
-    cpu = cpu_baseline(p, g, unit_scale) if not args.no_cpu else None
+    cpu, parity = None, None
+    if not args.no_cpu:
+        # CPU leg: one more call from the initial state, checked on sampled entries, then the oracle's rate
+        reset_c(p, g, C)
+        call()
+        torch.cuda.synchronize()
+        parity = _oracle_sampled_check(p, g, C)
+        print(f"[bench] sampled check {parity}", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(p, g, unit_scale)
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s" if p.dtype != 3 else "TOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
@@ -281,23 +322,29 @@ def run_all(args):
     for name, p in S.WORKLOADS.items():
         g = S.generate(p)
         A, B, bias = upload(g, p)
-        C = torch.empty((p.M, p.LDC), dtype=torch.int32 if p.dtype == 3 else torch.float32, device="cuda")
+        C = make_c(p)
         s = torch.cuda.current_stream()
         modes = [0, 1, 2] if name.startswith(("skinny", "sk_")) else [0]
         for mode in modes:
             T.tcm_set_option("force_mode", mode)
             call = make_call(p, A, B, bias, C, s.cuda_stream)
+            reset_c(p, g, C)
             call()
             torch.cuda.synchronize()
             plan = T.tcm_last_plan()
             ms, _ = time_steps(call, max(5, args.steps // 2), 10, s)
             pc = per_call_us(call, max(5, args.steps // 2), s)
-            par = sampled_parity(p, g, C)
+            par = None
+            if not args.no_cpu:  # CPU leg: sampled check of one call from the initial state
+                reset_c(p, g, C)
+                call()
+                torch.cuda.synchronize()
+                par = _oracle_sampled_check(p, g, C)
             v = p.flops / (ms * 1e-3) / 1e12
             row = {"workload": name, "mode": ["auto", "dp", "streamk"][mode], "ms": round(ms, 5),
                    "per_call_us": pc, "tflops": round(v, 2), "frac_peak": round(v / PEAK[p.dtype], 4),
                    "hbm_frac": round(p.alg_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
-                   "parity_ok": par["ok"], "plan": plan}
+                   "parity_ok": par["ok"] if par else None, "plan": plan}
             if name.startswith("skinny"):
                 row["cold_median_us"] = cold_us(call, 20, s)
             rows.append(row)
@@ -335,7 +382,7 @@ def run_sweep(args):
         p = S.workload(name)
         g = S.generate(p)
         A, B, bias = upload(g, p)
-        C = torch.empty((p.M, p.LDC), dtype=torch.int32 if p.dtype == 3 else torch.float32, device="cuda")
+        C = make_c(p)
         s = torch.cuda.current_stream()
         for cfg in range(T.tcm_config_count()):
             for mode in (1, 2):

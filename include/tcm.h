@@ -3,10 +3,12 @@
  *
  * One operation: the matrix product with a fused bias / ReLU epilogue,
  *
- *     C[i][j] = epi( bias[j] + sum_k a(i,k) * b(k,j) ),
+ *     C[i][j] = epi( [C_in[i][j] +] bias[j] + sum_k a(i,k) * b(k,j) ),
  *
  * the product-plus-bias whose bias is the initial value of the reduction
- * (kimm240.github.io/tvm, FuseReductionEpilogue posts 1 and 2), followed by
+ * (kimm240.github.io/tvm, FuseReductionEpilogue posts 1 and 2; post 2 also
+ * generalises the initial value to a per-element tensor, the optional C_in,
+ * which is C's own contents before the call), followed by
  * the ReLU of the Conv2d + Bias + ReLU pattern (same page, Conv2d-Reshape-
  * Add-ReLU fusion post), computed on the matrix cores with low-precision
  * inputs and a wide accumulator (je-d.tistory.com/entry/tvm, Tensor Core
@@ -59,11 +61,23 @@ enum { TCM_F16_F32 = 0, TCM_BF16_F32 = 1, TCM_F32_F32 = 2, TCM_I8_I32 = 3 };
 #define TCM_A_COLMAJOR (1 << 8)
 #define TCM_B_COLMAJOR (1 << 9)
 
+/* ---- output type flags (or-ed into `dtype`; float element types only) ---- */
+/* C (and C_in with TCM_EPI_ACCUM) stored as IEEE binary16 or as bfloat16
+ * instead of binary32: the f32 accumulator is rounded to nearest-even at the
+ * store (the mixed-precision output of the Tensor Core notes,
+ * je-d.tistory.com/entry/tvm: narrow inputs and outputs, wide accumulation).
+ * At most one of the two; TCM_ERR_INVALID_VALUE with int8.                   */
+#define TCM_C_F16 (1 << 10)
+#define TCM_C_BF16 (1 << 11)
+
 /* ---- epilogue flags -------------------------------------------------------- */
-/* TCM_EPI_BIAS: bias[j] (length N, f32 or int32 per dtype) seeds the
- *               accumulator of column j before any product is added.
- * TCM_EPI_RELU: C = x > 0 ? x : 0 after the sum (NaN and -0 become +0).     */
-enum { TCM_EPI_NONE = 0, TCM_EPI_BIAS = 1, TCM_EPI_RELU = 2, TCM_EPI_BIAS_RELU = 3 };
+/* TCM_EPI_BIAS:  bias[j] (length N, f32 or int32 per dtype) seeds the
+ *                accumulator of column j before any product is added.
+ * TCM_EPI_RELU:  C = x > 0 ? x : 0 after the sum (NaN and -0 become +0).
+ * TCM_EPI_ACCUM: C's contents before the call (C_in, in C's own type) also
+ *                seed the accumulator: C = epi(C_in + bias + A.B) in place.
+ *                Every element of C is read once before it is written.     */
+enum { TCM_EPI_NONE = 0, TCM_EPI_BIAS = 1, TCM_EPI_RELU = 2, TCM_EPI_BIAS_RELU = 3, TCM_EPI_ACCUM = 4 };
 
 /*
  * tcm_gemm -- C = epi(bias + A.B) with M x K A, K x N B, M x N C.
@@ -73,20 +87,23 @@ enum { TCM_EPI_NONE = 0, TCM_EPI_BIAS = 1, TCM_EPI_RELU = 2, TCM_EPI_BIAS_RELU =
  *   A, lda       A and its leading dimension in elements:
  *                lda >= K (row-major) or lda >= M (TCM_A_COLMAJOR), lda >= 1.
  *   B, ldb       likewise: ldb >= N (row-major) or ldb >= K (TCM_B_COLMAJOR).
- *   C, ldc       output, ldc >= N; f32 for float types, int32 for int8.
+ *   C, ldc       output (input too with TCM_EPI_ACCUM), ldc >= N; f32 for
+ *                float types unless TCM_C_F16 / TCM_C_BF16, int32 for int8.
  *                C must not overlap A, B or bias.
- *   dtype        one element type above, optionally or-ed with layout flags.
+ *   dtype        one element type above, optionally or-ed with layout and
+ *                output type flags.
  *   bias         device vector of N elements, read only with TCM_EPI_BIAS.
- *   epilogue     TCM_EPI_* flags.
+ *   epilogue     TCM_EPI_* flags (any combination).
  *   stream       hipStream_t as void* (NULL: null stream).
  *
  * Any alignment and any leading dimension is served; aligned, 16-byte
  * multiple layouts take the fast path.
  * Returns TCM_OK once the work is enqueued; TCM_ERR_INVALID_VALUE for
  * negative sizes, too-small leading dimensions, a NULL operand with a
- * non-empty extent, unknown dtype/flags/epilogue, TCM_EPI_BIAS with a NULL
- * bias, or C overlapping an input; TCM_ERR_ALLOC if the split-k workspace
- * cannot be allocated; TCM_ERR_HIP on a launch error.
+ * non-empty extent, unknown dtype/flags/epilogue, both output type flags or
+ * an output type flag with int8, TCM_EPI_BIAS with a NULL bias, a pointer
+ * not aligned to its element, or C overlapping an input; TCM_ERR_ALLOC if
+ * the split-k workspace cannot be allocated; TCM_ERR_HIP on a launch error.
  */
 int tcm_gemm(int64_t M, int64_t N, int64_t K,
              const void* A, int64_t lda,

@@ -15,6 +15,10 @@ Recipe (one numpy PCG64 generator per problem, ``np.random.default_rng(seed)``):
     torch's RNE cast on the CPU, float32 as is;
   * int8 operands: ``rng.integers(-128, 127, endpoint=True)``; int32 bias:
     ``rng.integers(-2**20, 2**20, endpoint=True)``;
+  * with ``accum``, the initial-value tensor C_in (the M x ldc storage of C
+    before the call, padding included) is drawn last: float problems
+    ``rng.uniform(-1, 1)`` rounded like the operands to C's type (f32, f16
+    or bf16), int8 problems int32 ``rng.integers(-2**20, 2**20, endpoint=True)``;
   * f16/bf16 operands are returned as uint16 bit patterns, f32 as float32,
     int8 as int8, bias as float32 or int32.
 The sampled-entry list of a large problem comes from a second generator,
@@ -46,6 +50,8 @@ class Problem:
     lda: int = 0               # 0 = tight
     ldb: int = 0
     ldc: int = 0
+    c_type: str = "acc"        # C storage: "acc" (f32 / int32), "f16", "bf16"
+    accum: bool = False        # C's contents before the call seed the accumulator
 
     @property
     def LDA(self):
@@ -68,9 +74,14 @@ class Problem:
         return 1 if self.dtype == I8 else (4 if self.dtype == F32 else 2)
 
     @property
+    def c_bytes(self):
+        return 4 if self.c_type == "acc" else 2
+
+    @property
     def alg_bytes(self):
-        """Bytes the product must move at least: A and B read once, C written once, bias read once."""
-        b = (self.M * self.K + self.K * self.N) * self.in_bytes + self.M * self.N * 4
+        """Bytes the product must move at least: A and B read once, C written once (and read
+        once with accum), bias read once."""
+        b = (self.M * self.K + self.K * self.N) * self.in_bytes + self.M * self.N * self.c_bytes * (2 if self.accum else 1)
         if self.bias:
             b += self.N * 4
         return b
@@ -87,6 +98,14 @@ def _workloads():
     w["sk_1536x1536x16384"] = Problem("sk_1536x1536x16384", F16, 1536, 1536, 16384, dist="uniform", seed=3)
     w["sk_3840x3840x4096"] = Problem("sk_3840x3840x4096", F16, 3840, 3840, 4096, dist="uniform", seed=3)
     w["i8_4096"] = Problem("i8_4096", I8, 4096, 4096, 4096, dist="int", seed=4, bias=True, relu=True)
+    # wider epilogues: low-precision C, C's own contents as the initial value
+    w["f16_8192_c16"] = Problem("f16_8192_c16", F16, 8192, 8192, 8192, b_col=True, dist="normal", seed=2, c_type="f16")
+    w["bf16_4096_accum"] = Problem("bf16_4096_accum", BF16, 4096, 4096, 4096, b_col=True, dist="normal", seed=5,
+                                   bias=True, relu=True, c_type="bf16", accum=True)
+    w["i8_4096_accum"] = Problem("i8_4096_accum", I8, 4096, 4096, 4096, dist="int", seed=6, bias=True, relu=True,
+                                 accum=True)
+    w["skinny_m16_accum_c16"] = Problem("skinny_m16_accum_c16", F16, 16, 4096, 4096, dist="uniform", seed=7,
+                                        c_type="f16", accum=True)
     return w
 
 
@@ -134,8 +153,18 @@ def _operand_shape(rows, cols, col_major, ld):
     return (cols, ld) if col_major else (rows, ld)
 
 
+C_TYPE_CODE = {"f16": F16, "bf16": BF16}   # storage codes of a low-precision C
+
+
+def c_storage_dtype(p: Problem):
+    """numpy storage type of C (uint16 bit patterns for f16 / bf16)."""
+    if p.c_type != "acc":
+        return np.uint16
+    return np.int32 if p.dtype == I8 else np.float32
+
+
 def generate(p: Problem):
-    """Storage arrays {'A', 'B', 'bias'} of problem p (bias None when unused).
+    """Storage arrays {'A', 'B', 'bias', 'C_in'} of problem p (bias / C_in None when unused).
 
     With ld larger than the extent, the padding columns are drawn too (from
     the same stream, as part of the storage array)."""
@@ -148,7 +177,14 @@ def generate(p: Problem):
             bias = rng.integers(-2 ** 20, 2 ** 20, size=p.N, endpoint=True, dtype=np.int64).astype(np.int32)
         else:
             bias = rng.uniform(-1.0, 1.0, size=p.N).astype(np.float32)
-    return {"A": A, "B": B, "bias": bias}
+    c_in = None
+    if p.accum:
+        shape = (max(p.M, 1), p.LDC)
+        if p.dtype == I8:
+            c_in = rng.integers(-2 ** 20, 2 ** 20, size=shape, endpoint=True, dtype=np.int64).astype(np.int32)
+        else:
+            c_in = _to_storage(rng.uniform(-1.0, 1.0, size=shape), C_TYPE_CODE.get(p.c_type, F32))
+    return {"A": A, "B": B, "bias": bias, "C_in": c_in}
 
 
 def sample_entries(p: Problem, n=4096):
@@ -164,9 +200,9 @@ def sample_entries(p: Problem, n=4096):
 
 
 def small_problem(dtype, M, N, K, seed=0, a_col=False, b_col=False, bias=False, relu=False,
-                  lda=0, ldb=0, ldc=0, dist=None):
+                  lda=0, ldb=0, ldc=0, dist=None, c_type="acc", accum=False):
     """An ad-hoc problem for parity cases (ragged shapes, padding, layouts)."""
     if dist is None:
         dist = "int" if dtype == I8 else "uniform"
     return Problem(f"{DTYPE_NAMES[dtype]}_{M}x{N}x{K}", dtype, M, N, K, a_col=a_col, b_col=b_col, dist=dist,
-                   seed=seed, bias=bias, relu=relu, lda=lda, ldb=ldb, ldc=ldc)
+                   seed=seed, bias=bias, relu=relu, lda=lda, ldb=ldb, ldc=ldc, c_type=c_type, accum=accum)

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(HERE, "_build", "libtcm.so")
 # element types and flags (include/tcm.h)
 TCM_F16_F32, TCM_BF16_F32, TCM_F32_F32, TCM_I8_I32 = 0, 1, 2, 3
 TCM_A_COLMAJOR, TCM_B_COLMAJOR = 1 << 8, 1 << 9
-TCM_EPI_NONE, TCM_EPI_BIAS, TCM_EPI_RELU, TCM_EPI_BIAS_RELU = 0, 1, 2, 3
+TCM_C_F16, TCM_C_BF16 = 1 << 10, 1 << 11
+TCM_EPI_NONE, TCM_EPI_BIAS, TCM_EPI_RELU, TCM_EPI_BIAS_RELU, TCM_EPI_ACCUM = 0, 1, 2, 3, 4
 TCM_OK, TCM_ERR_INVALID_VALUE, TCM_ERR_NOT_SUPPORTED, TCM_ERR_HIP, TCM_ERR_ALLOC = 0, 1, 2, 3, 4
 
 
@@ -170,14 +171,18 @@ def _layout(t, name):
     raise ValueError(f"{name} needs one unit stride (row- or column-major view)")
 
 
-def gemm(A, B, C=None, bias=None, relu=False, stream=None):
-    """C = relu?(A @ B + bias) on the GPU via tcm_gemm.
+def gemm(A, B, C=None, bias=None, relu=False, accumulate=False, out_dtype=None, stream=None):
+    """C = relu?(A @ B + bias [+ C]) on the GPU via tcm_gemm.
 
     A: (M, K) and B: (K, N) CUDA tensors of one type (float16, bfloat16,
     float32 or int8), each a row- or column-major view (transposed views
-    select the layout flags).  C: optional (M, N) row-major output, float32
-    (int32 for int8).  bias: optional length-N float32 (int32) vector.
-    Runs on `stream` (default: torch's current stream) and returns C."""
+    select the layout flags).  C: optional (M, N) row-major output; its type
+    is the accumulator's (float32, int32 for int8) or, for float inputs,
+    float16 / bfloat16 (rounded to nearest even); `out_dtype` picks the type
+    of a new C.  With `accumulate`, C's current contents are the initial
+    value of the sum (C must be given).  bias: optional length-N float32
+    (int32) vector.  Runs on `stream` (default: torch's current stream) and
+    returns C."""
     import torch
     if A.dtype != B.dtype:
         raise TypeError("A and B must have the same dtype")
@@ -188,17 +193,22 @@ def gemm(A, B, C=None, bias=None, relu=False, stream=None):
         raise ValueError(f"inner sizes differ: {K} vs {K2}")
     lda, a_col = _layout(A, "A")
     ldb, b_col = _layout(B, "B")
-    out_dtype = torch.int32 if code == TCM_I8_I32 else torch.float32
+    acc_dtype = torch.int32 if code == TCM_I8_I32 else torch.float32
+    if accumulate and C is None:
+        raise ValueError("accumulate needs C")
     if C is None:
-        C = torch.empty((M, N), dtype=out_dtype, device=A.device)
-    if C.dtype != out_dtype or C.dim() != 2 or tuple(C.shape) != (M, N) or (N > 1 and C.stride(1) != 1):
-        raise ValueError("C must be a row-major (M, N) tensor of the accumulator type")
+        C = torch.empty((M, N), dtype=out_dtype or acc_dtype, device=A.device)
+    c_flags = {torch.float16: TCM_C_F16, torch.bfloat16: TCM_C_BF16}.get(C.dtype, 0)
+    if c_flags and code == TCM_I8_I32:
+        raise TypeError("int8 products have an int32 C")
+    if (C.dtype != acc_dtype and not c_flags) or C.dim() != 2 or tuple(C.shape) != (M, N) or (N > 1 and C.stride(1) != 1):
+        raise ValueError("C must be a row-major (M, N) tensor of the accumulator type, float16 or bfloat16")
     ldc = max(C.stride(0), N, 1)
-    epi = (TCM_EPI_BIAS if bias is not None else 0) | (TCM_EPI_RELU if relu else 0)
+    epi = (TCM_EPI_BIAS if bias is not None else 0) | (TCM_EPI_RELU if relu else 0) | (TCM_EPI_ACCUM if accumulate else 0)
     if bias is not None:
-        if bias.dtype != out_dtype or bias.numel() < N or not bias.is_contiguous():
+        if bias.dtype != acc_dtype or bias.numel() < N or not bias.is_contiguous():
             raise ValueError("bias must be a contiguous length-N vector of the accumulator type")
-    dtype = code | (TCM_A_COLMAJOR if a_col else 0) | (TCM_B_COLMAJOR if b_col else 0)
+    dtype = code | (TCM_A_COLMAJOR if a_col else 0) | (TCM_B_COLMAJOR if b_col else 0) | c_flags
     if stream is None:
         stream = torch.cuda.current_stream(A.device).cuda_stream
     st = tcm_gemm(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), ldc, dtype,

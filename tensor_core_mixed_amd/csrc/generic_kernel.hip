@@ -4,8 +4,10 @@
 // the auto-tensorcore note: without the matrix-core rewrite the code is
 // slower but functionally equal).  Structure: 64x64 output tile per
 // workgroup, four waves of 2x2 16x16 MFMA tiles, a 64-byte k-slab per step
-// staged through LDS element by element with bounds checks, bias as the
-// accumulator's initial value, ReLU before the bounds-checked store.
+// staged through LDS element by element with bounds checks, bias (plus C's
+// current value with accum) as the accumulator's initial value, ReLU before
+// the bounds-checked store in C's type (f32 / int32, or f16 / bf16 rounded
+// to nearest even).
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -67,6 +69,28 @@ __device__ __forceinline__ void stage(char* lds, const typename G<DT>::T* X, int
     }
 }
 
+// C element (row, col) as the accumulator type, and its store.
+template <int DT>
+__device__ __forceinline__ typename G<DT>::AccS load_c(const GenericArgs& a, int64_t idx) {
+    if constexpr (DT == I8) {
+        return ((const int*)a.C)[idx];
+    } else {
+        if (a.c_type == C_F16) return (float)((const _Float16*)a.C)[idx];
+        if (a.c_type == C_BF16) return __builtin_bit_cast(float, (unsigned)((const uint16_t*)a.C)[idx] << 16);
+        return ((const float*)a.C)[idx];
+    }
+}
+template <int DT>
+__device__ __forceinline__ void store_c(const GenericArgs& a, int64_t idx, typename G<DT>::AccS v) {
+    if constexpr (DT == I8) {
+        ((int*)a.C)[idx] = v;
+    } else {
+        if (a.c_type == C_F16) ((_Float16*)a.C)[idx] = (_Float16)v;
+        else if (a.c_type == C_BF16) ((__bf16*)a.C)[idx] = (__bf16)v;
+        else ((float*)a.C)[idx] = v;
+    }
+}
+
 template <int DT>
 __global__ __launch_bounds__(256) void generic_gemm_kernel(GenericArgs a) {
     using T = typename G<DT>::T;
@@ -92,7 +116,11 @@ __global__ __launch_bounds__(256) void generic_gemm_kernel(GenericArgs a) {
 #pragma unroll
         for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[fm][fn][r] = v;
+            for (int r = 0; r < 4; ++r) {
+                acc[fm][fn][r] = v;
+                const int64_t row = m0 + wm * 32 + fm * 16 + 4 * grp + r;
+                if (a.accum && row < a.M && col < a.N) acc[fm][fn][r] += load_c<DT>(a, row * a.ldc + col);
+            }
     }
 
     for (int64_t k0 = 0; k0 < a.K; k0 += BKE) {
@@ -112,7 +140,6 @@ __global__ __launch_bounds__(256) void generic_gemm_kernel(GenericArgs a) {
         __syncthreads();
     }
 
-    AccS* C = (AccS*)a.C;
 #pragma unroll
     for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
@@ -123,7 +150,7 @@ __global__ __launch_bounds__(256) void generic_gemm_kernel(GenericArgs a) {
                 const int64_t row = m0 + wm * 32 + fm * 16 + 4 * grp + r;
                 AccS v = acc[fm][fn][r];
                 if (a.relu) v = v > (AccS)0 ? v : (AccS)0;
-                if (row < a.M && col < a.N) C[row * a.ldc + col] = v;
+                if (row < a.M && col < a.N) store_c<DT>(a, row * a.ldc + col, v);
             }
         }
 }

@@ -80,7 +80,8 @@ bool tile_eligible(const Problem& p, const TileConfig& c) {
     } else {
         if ((int64_t)bk_elems(p.dtype) * p.ldb * es + (int64_t)c.bn * es >= kOffsetLimit) return false;
     }
-    if ((int64_t)c.bm * p.ldc * 4 + (int64_t)c.bn * 4 >= kOffsetLimit) return false;
+    const int cs = c_elem_bytes(p.c_type);
+    if ((int64_t)c.bm * p.ldc * cs + (int64_t)c.bn * cs >= kOffsetLimit) return false;
     const int64_t tiles = cdiv(p.M, c.bm) * cdiv(p.N, c.bn);
     if (tiles >= (1LL << 31)) return false;
     return true;

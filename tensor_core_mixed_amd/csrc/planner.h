@@ -21,6 +21,7 @@ struct Problem {
     int dtype;     // element type (low byte of the ABI dtype)
     bool a_col, b_col;
     int epilogue;
+    int c_type;    // CType
     bool aligned;  // every pointer 16-byte aligned
 };
 

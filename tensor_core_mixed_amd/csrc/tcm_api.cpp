@@ -175,8 +175,11 @@ int check_problem(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int
     const int dt = dtype & 0xff;
     const int flags = dtype & ~0xff;
     if (dt < F16 || dt > I8) return TCM_ERR_INVALID_VALUE;
-    if (flags & ~(TCM_A_COLMAJOR | TCM_B_COLMAJOR)) return TCM_ERR_INVALID_VALUE;
-    if (epilogue < 0 || epilogue > TCM_EPI_BIAS_RELU) return TCM_ERR_INVALID_VALUE;
+    if (flags & ~(TCM_A_COLMAJOR | TCM_B_COLMAJOR | TCM_C_F16 | TCM_C_BF16)) return TCM_ERR_INVALID_VALUE;
+    const int c_type = (flags & TCM_C_F16) ? C_F16 : ((flags & TCM_C_BF16) ? C_BF16 : C_ACC);
+    if ((flags & TCM_C_F16) && (flags & TCM_C_BF16)) return TCM_ERR_INVALID_VALUE;
+    if (c_type != C_ACC && dt == I8) return TCM_ERR_INVALID_VALUE;
+    if (epilogue < 0 || epilogue > (TCM_EPI_BIAS | TCM_EPI_RELU | TCM_EPI_ACCUM)) return TCM_ERR_INVALID_VALUE;
     if (M < 0 || N < 0 || K < 0) return TCM_ERR_INVALID_VALUE;
     const bool a_col = flags & TCM_A_COLMAJOR, b_col = flags & TCM_B_COLMAJOR;
     if (lda < 1 || lda < (a_col ? M : K)) return TCM_ERR_INVALID_VALUE;
@@ -192,6 +195,7 @@ int check_problem(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int
     p->a_col = a_col;
     p->b_col = b_col;
     p->epilogue = epilogue;
+    p->c_type = c_type;
     p->aligned = true;
     return TCM_OK;
 }
@@ -338,14 +342,15 @@ int tcm_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
     const int es = elem_bytes(p.dtype);
     const int64_t a_ext = extent(p.a_col ? K : M, p.a_col ? M : K, lda) * es;
     const int64_t b_ext = extent(p.b_col ? N : K, p.b_col ? K : N, ldb) * es;
-    const int64_t c_ext = extent(M, N, ldc) * 4;
+    const int cs = c_elem_bytes(p.c_type);
+    const int64_t c_ext = extent(M, N, ldc) * cs;
     const bool use_bias = epilogue & TCM_EPI_BIAS;
     if (!C) return TCM_ERR_INVALID_VALUE;
     if (a_ext > 0 && !A) return TCM_ERR_INVALID_VALUE;
     if (b_ext > 0 && !B) return TCM_ERR_INVALID_VALUE;
     if (use_bias && !bias) return TCM_ERR_INVALID_VALUE;
     // pointers must be aligned to their element
-    if (((uintptr_t)A % es) || ((uintptr_t)B % es) || ((uintptr_t)C % 4) || (use_bias && ((uintptr_t)bias % 4)))
+    if (((uintptr_t)A % es) || ((uintptr_t)B % es) || ((uintptr_t)C % cs) || (use_bias && ((uintptr_t)bias % 4)))
         return TCM_ERR_INVALID_VALUE;
     if (overlaps(C, c_ext, A, a_ext) || overlaps(C, c_ext, B, b_ext) || (use_bias && overlaps(C, c_ext, bias, N * 4)))
         return TCM_ERR_INVALID_VALUE;
@@ -379,6 +384,8 @@ int tcm_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
         g.b_col = p.b_col;
         g.relu = (epilogue & TCM_EPI_RELU) != 0;
         g.has_bias = use_bias;
+        g.accum = (epilogue & TCM_EPI_ACCUM) != 0;
+        g.c_type = p.c_type;
         g.tiles_m = (int)((M + 63) / 64);
         g.tiles_n = (int)((N + 63) / 64);
         return launch_generic(p.dtype, g, stream) == 0 ? TCM_OK : TCM_ERR_HIP;
@@ -397,6 +404,8 @@ int tcm_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
     a.ldc = (int)ldc;
     a.relu = (epilogue & TCM_EPI_RELU) != 0;
     a.has_bias = use_bias;
+    a.accum = (epilogue & TCM_EPI_ACCUM) != 0;
+    a.c_type = p.c_type;
     a.tiles_m = (int)((M + pl.bm - 1) / pl.bm);
     a.tiles_n = (int)((N + pl.bn - 1) / pl.bn);
     a.iters = (int)pl.iters;

@@ -9,6 +9,11 @@ enum DType : int { F16 = 0, BF16 = 1, F32 = 2, I8 = 3 };
 
 inline int elem_bytes(int dt) { return dt == F32 ? 4 : (dt == I8 ? 1 : 2); }
 
+// Storage of C: the accumulator type (f32, or int32 for int8), or a
+// rounded-to-nearest-even 16-bit float.
+enum CType : int { C_ACC = 0, C_F16 = 1, C_BF16 = 2 };
+constexpr int c_elem_bytes(int c_type) { return c_type == C_ACC ? 4 : 2; }
+
 // One K-step stages 128 bytes of every operand row/column: 64 f16/bf16,
 // 32 f32 or 128 int8 elements.  Each 16-byte chunk is one MFMA operand
 // fragment of one lane (8 f16, 16 int8) or four f32 k-values.
@@ -45,6 +50,8 @@ struct TileArgs {
     int lda, ldb, ldc;
     int relu;
     int has_bias;
+    int accum;            // C's contents seed the accumulator (read before written)
+    int c_type;           // C storage: 0 the accumulator type (f32 / int32), 1 f16, 2 bf16
     int tiles_m, tiles_n;
     int iters;            // k-iterations per tile = ceil(K / bk)
     int dp_tiles;
@@ -112,6 +119,8 @@ struct GenericArgs {
     int a_col, b_col;
     int relu;
     int has_bias;
+    int accum;
+    int c_type;
     int tiles_m, tiles_n;
 };
 

@@ -345,11 +345,71 @@ struct TileKernel {
     }
 
     // ------------------------------------------------------- epilogue
-    __device__ __forceinline__ static void init_acc(Acc (&acc)[FM][FN], const TileArgs& a, bool seed_bias, int n0, int wn, int lane) {
+    // 32x32 accumulator layout: lane l, register r holds row
+    // 8*(r/4) + 4*(l/32) + r%4 and column l%32 of its MFMA tile.  C is read
+    // (initial values) and written through a buffer descriptor whose range
+    // ends at row M, with columns >= N given the out-of-range offset: such
+    // loads return 0 and such stores are dropped, so there are no per-element
+    // branches.  C holds the accumulator type, or f16 / bf16 (c_type).
+    struct CView {
+        __amdgpu_buffer_rsrc_t rc;
+        unsigned coff[FN];  // per fn: byte offset of this lane's column in row 0 of the wave block (or kOOB)
+        int row0;           // first row of the lane within the tile
+        int cs;             // bytes per C element
+    };
+    __device__ __forceinline__ static CView c_view(const TileArgs& a, int m0, int n0, int wm, int wn, int lane) {
+        CView v;
+        v.cs = c_elem_bytes(a.c_type);
+        v.row0 = wm * TM + 4 * (lane >> 5);
+        const int mrem = a.M - m0;
+        const int64_t bytes = ((int64_t)mrem * a.ldc - n0) * v.cs;  // from (m0, n0) to the end of row M-1's stride
+        const int nrec = bytes < (int64_t)kOOB ? (int)bytes : (int)kOOB;
+        v.rc = __builtin_amdgcn_make_buffer_rsrc((char*)a.C + ((int64_t)m0 * a.ldc + n0) * v.cs, (short)0, nrec, kRsrcWord3);
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) {
+            const int col = wn * TN + fn * 32 + (lane & 31);
+            v.coff[fn] = n0 + col < a.N ? (unsigned)((v.row0 * a.ldc + col) * v.cs) : kOOB;
+        }
+        return v;
+    }
+    __device__ __forceinline__ static unsigned c_roff(const TileArgs& a, const CView& v, int fm, int r) {
+        return (unsigned)((fm * 32 + 8 * (r >> 2) + (r & 3)) * a.ldc * v.cs);
+    }
+    __device__ __forceinline__ static AccS load_c(const TileArgs& a, const CView& v, unsigned off) {
+        if constexpr (DT == I8) {
+            return __builtin_amdgcn_raw_buffer_load_b32(v.rc, off, 0, 0);
+        } else {
+            if (a.c_type == C_F16) {
+                const unsigned short h = __builtin_amdgcn_raw_buffer_load_b16(v.rc, off, 0, 0);
+                return (float)__builtin_bit_cast(_Float16, h);
+            }
+            if (a.c_type == C_BF16) {
+                const unsigned short h = __builtin_amdgcn_raw_buffer_load_b16(v.rc, off, 0, 0);
+                return __builtin_bit_cast(float, (unsigned)h << 16);
+            }
+            return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(v.rc, off, 0, 0));
+        }
+    }
+    template <int CT>
+    __device__ __forceinline__ static void store_c(const CView& v, unsigned off, AccS x) {
+        if constexpr (DT == I8)
+            __builtin_amdgcn_raw_buffer_store_b32(x, v.rc, off, 0, 0);
+        else if constexpr (CT == C_F16)  // round to nearest even (the conversion's default mode)
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (_Float16)x), v.rc, off, 0, 0);
+        else if constexpr (CT == C_BF16)
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (__bf16)x), v.rc, off, 0, 0);
+        else
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, x), v.rc, off, 0, 0);
+    }
+
+    // Initial accumulator of a tile segment: with `seed` (the segment that
+    // starts at k = 0), bias[col] plus, with accum, C's current value; else 0.
+    __device__ __forceinline__ static void init_acc(Acc (&acc)[FM][FN], const TileArgs& a, bool seed, int m0, int n0, int wm,
+                                                    int wn, int lane) {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             AccS v = 0;
-            if (seed_bias) {
+            if (seed && a.has_bias) {
                 const int col = n0 + wn * TN + fn * 32 + (lane & 31);
                 if (col < a.N) v = ((const AccS*)a.bias)[col];
             }
@@ -358,38 +418,50 @@ struct TileKernel {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[fm][fn][r] = v;
         }
+        if (seed && a.accum) {
+            const CView cv = c_view(a, m0, n0, wm, wn, lane);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const unsigned roff = c_roff(a, cv, fm, r);
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn) acc[fm][fn][r] += load_c(a, cv, cv.coff[fn] + roff);
+                }
+        }
     }
 
-    // 32x32 accumulator layout: lane l, register r holds row
-    // 8*(r/4) + 4*(l/32) + r%4 and column l%32 of its MFMA tile.  Stores go
-    // through a buffer descriptor whose range ends at row M, with columns
-    // >= N given the out-of-range offset: the hardware drops those writes.
-    __device__ __forceinline__ static void store_tile(const Acc (&acc)[FM][FN], const TileArgs& a, int m0, int n0, int wm, int wn, int lane) {
-        const int row0 = wm * TM + 4 * (lane >> 5);
-        const int mrem = a.M - m0;
-        const int64_t bytes = (int64_t)mrem * a.ldc * 4 - (int64_t)n0 * 4;  // from (m0, n0) to the end of row M-1's stride
-        const int nrec = bytes < (int64_t)kOOB ? (int)bytes : (int)kOOB;
-        const __amdgpu_buffer_rsrc_t rc =
-            __builtin_amdgcn_make_buffer_rsrc((char*)a.C + ((int64_t)m0 * a.ldc + n0) * 4, (short)0, nrec, kRsrcWord3);
+    template <int CT>
+    __device__ __forceinline__ static void store_tile_as(const Acc (&acc)[FM][FN], const TileArgs& a, int m0, int n0, int wm,
+                                                         int wn, int lane) {
+        const CView cv = c_view(a, m0, n0, wm, wn, lane);
         const bool relu = a.relu;
-        unsigned coff[FN];
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) {
-            const int col = wn * TN + fn * 32 + (lane & 31);
-            coff[fn] = n0 + col < a.N ? (unsigned)(row0 * a.ldc + col) * 4 : kOOB;
-        }
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const unsigned roff = (unsigned)((fm * 32 + 8 * (r >> 2) + (r & 3)) * a.ldc) * 4;
+                const unsigned roff = c_roff(a, cv, fm, r);
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn) {
                     AccS v = acc[fm][fn][r];
                     if (relu) v = v > (AccS)0 ? v : (AccS)0;
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), rc, coff[fn] + roff, 0, 0);
+                    store_c<CT>(cv, cv.coff[fn] + roff, v);
                 }
             }
+    }
+    // one branch per tile picks the store of C's type
+    __device__ __forceinline__ static void store_tile(const Acc (&acc)[FM][FN], const TileArgs& a, int m0, int n0, int wm, int wn, int lane) {
+        if constexpr (DT != I8) {
+            if (a.c_type == C_F16) {
+                store_tile_as<C_F16>(acc, a, m0, n0, wm, wn, lane);
+                return;
+            }
+            if (a.c_type == C_BF16) {
+                store_tile_as<C_BF16>(acc, a, m0, n0, wm, wn, lane);
+                return;
+            }
+        }
+        store_tile_as<C_ACC>(acc, a, m0, n0, wm, wn, lane);
     }
 
     // Partial tiles live in the workspace in register order, four
@@ -542,7 +614,7 @@ struct TileKernel {
         int tm, tn;
         tile_coords(blockIdx.x, a, tm, tn);
         const int m0 = tm * BM, n0 = tn * BN;
-        init_acc(acc, a, a.has_bias, n0, wn, lane);
+        init_acc(acc, a, true, m0, n0, wm, wn, lane);
         mainloop(acc, a, smem, m0, n0, 0, a.iters, wave, lane);
         store_tile(acc, a, m0, n0, wm, wn, lane);
     }
@@ -572,7 +644,7 @@ struct TileKernel {
             int tm, tn;
             tile_coords(a.dp_tiles + (int)tsk, a, tm, tn);
             const int m0 = tm * BM, n0 = tn * BN;
-            init_acc(acc, a, a.has_bias && k_lo == 0, n0, wn, lane);
+            init_acc(acc, a, k_lo == 0, m0, n0, wm, wn, lane);
             mainloop(acc, a, smem, m0, n0, k_lo, k_hi, wave, lane);
             it += k_hi - k_lo;
             if (k_lo == 0 && k_hi == I) {

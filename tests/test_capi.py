@@ -46,7 +46,11 @@ BAD = [  # (M, N, K, lda, ldb, ldc, dtype, epilogue, A, B, C, bias)
     (4, 4, 4, 4, 4, 3, 0, 0, 16, 16, 16, 0),            # ldc < N
     (4, 4, 4, 4, 4, 4, 7, 0, 16, 16, 16, 0),            # unknown element type
     (4, 4, 4, 4, 4, 4, 1 << 12, 0, 16, 16, 16, 0),      # unknown flag
-    (4, 4, 4, 4, 4, 4, 0, 4, 16, 16, 16, 0),            # unknown epilogue
+    (4, 4, 4, 4, 4, 4, 0, 8, 16, 16, 16, 0),            # unknown epilogue
+    (4, 4, 4, 4, 4, 4, T.TCM_C_F16 | T.TCM_C_BF16, 0, 16, 16, 16, 0),  # two output types
+    (4, 4, 4, 4, 4, 4, T.TCM_I8_I32 | T.TCM_C_F16, 0, 16, 16, 16, 0),  # 16-bit C for int8
+    (4, 4, 4, 4, 4, 4, T.TCM_C_F16, 0, 16, 16, 4097, 0),  # f16 C not aligned to its element
+    (4, 4, 4, 4, 4, 4, 0, 0, 16, 16, 4098, 0),          # f32 C not aligned to its element
     (4, 4, 4, 4, 4, 4, 0, 1, 16, 16, 16, 0),            # bias flag without bias
     (4, 4, 4, 4, 4, 4, 0, 0, 0, 16, 16, 0),             # NULL A
     (4, 4, 4, 4, 4, 4, 0, 0, 16, 0, 16, 0),             # NULL B
@@ -76,6 +80,12 @@ def test_valid_call_without_device_reports_hip_error():
     # real-looking (fake) pointers: checks pass, the first HIP call fails
     st = T.tcm_gemm(64, 64, 64, 1 << 20, 64, 2 << 20, 64, 3 << 20, 64, 0, None, 0, None)
     assert st == T.TCM_ERR_HIP
+    # every epilogue combination and a 16-bit C at a 2-byte-aligned address are valid requests
+    for epi in range(8):
+        for flags in (0, T.TCM_C_F16, T.TCM_C_BF16):
+            st = T.tcm_gemm(64, 64, 64, 1 << 20, 64, 2 << 20, 64, (3 << 20) + 2, 64, T.TCM_BF16_F32 | flags,
+                            4 << 20, epi, None)
+            assert st == (T.TCM_ERR_HIP if flags else T.TCM_ERR_INVALID_VALUE), (epi, flags)
 
 
 def test_options():

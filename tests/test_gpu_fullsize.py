@@ -67,7 +67,8 @@ def test_host_plan_query_matches_launch(name):
     """tcm_plan (no launch) reports the kernel, config, mode and grid tcm_gemm then launches."""
     p = S.workload(name)
     code = p.dtype | (T.TCM_A_COLMAJOR if p.a_col else 0) | (T.TCM_B_COLMAJOR if p.b_col else 0)
-    epi = (T.TCM_EPI_BIAS if p.bias else 0) | (T.TCM_EPI_RELU if p.relu else 0)
+    code |= {"acc": 0, "f16": T.TCM_C_F16, "bf16": T.TCM_C_BF16}[p.c_type]
+    epi = (T.TCM_EPI_BIAS if p.bias else 0) | (T.TCM_EPI_RELU if p.relu else 0) | (T.TCM_EPI_ACCUM if p.accum else 0)
     q = T.tcm_plan(p.M, p.N, p.K, p.LDA, p.LDB, p.LDC, code, epi, True)
     say(f"[case] plan query {name}: {q}")
     g = S.generate(p)

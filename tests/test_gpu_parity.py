@@ -206,3 +206,111 @@ def test_torch_convenience_layouts():
     assert torch.allclose(C.cpu(), ref, atol=1e-2, rtol=1e-3)
     C2 = T.gemm(A.t().contiguous().t(), Bt.t())  # column-major A view -> generic kernel
     assert torch.allclose(C2.cpu(), ref, atol=1e-2, rtol=1e-3)
+
+
+# ------------------------------------------------------- wider epilogues: C_in and a 16-bit C
+
+# (element type, C type, accumulate) combinations; int8 keeps an int32 C
+EPI_VARIANTS = [(S.F16, "f16", True), (S.F16, "bf16", False), (S.BF16, "bf16", True), (S.BF16, "acc", True),
+                (S.F32, "f16", True), (S.F32, "acc", True), (S.I8, "acc", True)]
+
+
+def _epi_id(v):
+    return f"{S.DTYPE_NAMES[v[0]]}-C{v[1]}-{'accum' if v[2] else 'store'}"
+
+
+@pytest.mark.parametrize("variant", EPI_VARIANTS, ids=_epi_id)
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("mode", [1, 2])
+def test_init_tensor_and_16bit_c_every_config_and_mode(variant, config, mode):
+    """C_in as the initial value and/or C stored in f16 / bf16, on every tile
+    config in both modes, ragged edges, bias + ReLU, padded ldc (whose padding
+    must keep C_in's values)."""
+    dtype, c_type, accum = variant
+    T.tcm_set_option("force_config", config)
+    T.tcm_set_option("force_mode", mode)
+    # N and K multiples of the 16-byte chunk so every config can take the row-major B
+    p = S.small_problem(dtype, 300, 272, 208, seed=40 + config, bias=True, relu=True, ldc=280, c_type=c_type,
+                        accum=accum)
+    g, C, plan = _run(p)
+    assert f"config={config}" in plan and ("mode=dp" if mode == 1 else "mode=streamk") in plan
+    err = check(p, g, C)
+    say(f"       normalised error {err:.3e}")
+    if accum:
+        cin = g["C_in"].reshape(p.M, p.LDC)[:, p.N:]
+        pad = C[:, p.N:]
+        if c_type != "acc":
+            code = S.C_TYPE_CODE[c_type]
+            want = (cin.view(np.float16).astype(np.float32) if code == S.F16 else
+                    torch.from_numpy(cin.view(np.int16).copy()).view(torch.bfloat16).float().numpy())
+        else:
+            want = cin
+        assert np.array_equal(pad, want), "C's padding columns changed"
+
+
+@pytest.mark.parametrize("variant", EPI_VARIANTS, ids=_epi_id)
+def test_init_tensor_streamk_many_segments(variant):
+    """Only the k = 0 segment of a split tile may add C_in (and the bias)."""
+    dtype, c_type, accum = variant
+    T.tcm_set_option("force_config", 4)
+    T.tcm_set_option("force_mode", 2)
+    T.tcm_set_option("sk_grid", 37)
+    K = 1024 if dtype != S.I8 else 2048
+    p = S.small_problem(dtype, 96, 128, K, seed=50, bias=True, c_type=c_type, accum=accum)
+    g, C, plan = _run(p)
+    assert "mode=streamk" in plan
+    check(p, g, C)
+
+
+@pytest.mark.parametrize("variant", EPI_VARIANTS, ids=_epi_id)
+@pytest.mark.parametrize("layout", ["a_col", "odd_ld", "unaligned_c"])
+def test_init_tensor_generic_path(variant, layout):
+    """The generic kernel's C_in read and 16-bit store (any layout, ld, alignment)."""
+    dtype, c_type, accum = variant
+    kw = {}
+    if layout == "a_col":
+        p = S.small_problem(dtype, 70, 50, 37, seed=60, a_col=True, bias=True, relu=True, c_type=c_type, accum=accum)
+    elif layout == "odd_ld":
+        p = S.small_problem(dtype, 65, 33, 41, seed=61, lda=43, ldb=35, ldc=37, c_type=c_type, accum=accum)
+    else:
+        p = S.small_problem(dtype, 64, 64, 64, seed=62, bias=True, c_type=c_type, accum=accum)
+        kw = {"c_offset": 1}
+    g, C, plan = _run(p, **kw)
+    assert "kernel=generic" in plan
+    check(p, g, C)
+
+
+@pytest.mark.parametrize("variant", EPI_VARIANTS, ids=_epi_id)
+def test_init_tensor_k_zero(variant):
+    """K = 0: C = epi(C_in + bias), exactly (up to the 16-bit output rounding)."""
+    dtype, c_type, accum = variant
+    p = S.small_problem(dtype, 40, 24, 0, seed=70, bias=True, relu=True, lda=1, ldc=27, c_type=c_type, accum=accum)
+    g, C, plan = _run(p)
+    check(p, g, C)
+
+
+def test_init_tensor_dp_and_streamk_bit_exact_int8():
+    """int8 with C_in: data-parallel and Stream-K give identical C."""
+    p = S.small_problem(S.I8, 256, 256, 4096, seed=80, bias=True, relu=True, accum=True)
+    out = []
+    for mode in (1, 2):
+        T.tcm_set_option("force_mode", mode)
+        g, C, plan = _run(p)
+        check(p, g, C)
+        out.append(C)
+    assert np.array_equal(out[0], out[1])
+
+
+def test_torch_convenience_accumulate_and_16bit_out():
+    """gemm(..., accumulate=True) adds into C; out_dtype picks a 16-bit C."""
+    torch.manual_seed(0)
+    A = torch.randn(130, 96, device="cuda").half()
+    B = torch.randn(96, 72, device="cuda").half()
+    C0 = torch.randn(130, 72, device="cuda")
+    C = C0.clone()
+    T.gemm(A, B, C, accumulate=True)
+    ref = C0 + A.float() @ B.float()
+    assert torch.allclose(C, ref, atol=1e-2, rtol=1e-3)
+    Ch = T.gemm(A, B, out_dtype=torch.bfloat16)
+    assert Ch.dtype == torch.bfloat16
+    assert torch.allclose(Ch.float(), (A.float() @ B.float()), atol=0.05, rtol=2 ** -7)
