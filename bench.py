@@ -164,15 +164,22 @@ def cold_us(call, calls, stream_obj):
 
 
 def gpu_clock():
-    """Current shader clock as rocm-smi reports it (best effort, None if unavailable)."""
+    """Current shader clock level from the driver's sysfs table (the line marked
+    with '*' in pp_dpm_sclk), or None.  A plain file read: no other program is
+    started from this process."""
+    import glob
     import re
-    import subprocess
-    try:
-        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20).stdout
-    except Exception:
-        return None
-    m = re.search(r"sclk.*?\((\d+)\s*Mhz\)", out, re.IGNORECASE)
-    return m.group(1) + " MHz" if m else None
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if "*" in line:
+                        m = re.search(r"(\d+)\s*Mhz", line, re.IGNORECASE)
+                        if m:
+                            return m.group(1) + " MHz"
+        except OSError:
+            continue
+    return None
 
 
 def _oracle_sampled_check(p, g, C):
