@@ -76,7 +76,8 @@ def make_c(p):
     """C on the device in its storage type (M x ldc)."""
     import torch
     dt = {"f16": torch.float16, "bf16": torch.bfloat16}.get(p.c_type, torch.int32 if p.dtype == 3 else torch.float32)
-    return torch.empty((max(p.M, 1), p.LDC), dtype=dt, device="cuda")
+    lead = (p.batch,) if p.batch > 1 else ()
+    return torch.empty(lead + (max(p.M, 1), p.LDC), dtype=dt, device="cuda")
 
 
 def reset_c(p, g, C):
@@ -105,11 +106,18 @@ def make_call(p, A, B, bias, C, stream):
     code = p.dtype | (T.TCM_A_COLMAJOR if p.a_col else 0) | (T.TCM_B_COLMAJOR if p.b_col else 0)
     code |= {"acc": 0, "f16": T.TCM_C_F16, "bf16": T.TCM_C_BF16}[p.c_type]
     epi = (T.TCM_EPI_BIAS if p.bias else 0) | (T.TCM_EPI_RELU if p.relu else 0) | (T.TCM_EPI_ACCUM if p.accum else 0)
-    args = (p.M, p.N, p.K, A.data_ptr(), p.LDA, B.data_ptr(), p.LDB, C.data_ptr(), p.LDC, code,
-            bias.data_ptr() if bias is not None else None, epi, stream)
+    bptr = bias.data_ptr() if bias is not None else None
+    if p.batch > 1:  # entries packed back to back (B shared with stride 0 if so drawn)
+        sa, sb, sc = A[0].numel(), 0 if p.b_shared else B[0].numel(), C[0].numel()
+        args = (p.batch, p.M, p.N, p.K, A.data_ptr(), p.LDA, sa, B.data_ptr(), p.LDB, sb, C.data_ptr(), p.LDC, sc, code,
+                bptr, p.N if bias is not None else 0, epi, stream)
+        fn = T.tcm_gemm_batched
+    else:
+        args = (p.M, p.N, p.K, A.data_ptr(), p.LDA, B.data_ptr(), p.LDB, C.data_ptr(), p.LDC, code, bptr, epi, stream)
+        fn = T.tcm_gemm
 
     def call():
-        st = T.tcm_gemm(*args)
+        st = fn(*args)
         if st != 0:
             raise RuntimeError(T.tcm_status_string(st))
     return call
@@ -189,16 +197,24 @@ def _oracle_sampled_check(p, g, C):
 
     import oracle
     import synthetic as S
-    ii, jj = S.sample_entries(p)
     Cc = C.float() if C.dtype in (torch.float16, torch.bfloat16) else C
-    got = Cc.cpu().numpy().reshape(-1, p.LDC)[ii, jj]
-    cin = {}
-    if p.accum:
-        cin = {"c_in": g["C_in"].reshape(-1), "c_in_type": S.C_TYPE_CODE.get(p.c_type, S.F32), "ldcin": p.LDC}
-    ref = oracle.get().gemm_entries(p.M, p.N, p.K, g["A"], p.LDA, p.a_col, g["B"], p.LDB, p.b_col, p.dtype, ii, jj,
-                                    bias=g["bias"], relu=p.relu, **cin)
+    Cc = Cc.cpu().numpy().reshape(max(p.batch, 1), -1, p.LDC)
+    # a batch: the first and the last entry, each checked like a single product
+    entries = [0] if p.batch == 1 else [0, p.batch - 1]
+    got, ref = [], []
+    for e in entries:
+        pe, ge = (p, g) if p.batch == 1 else (p.entry(e), S.entry_inputs(p, g, e))
+        ii, jj = S.sample_entries(pe)
+        got.append(Cc[e][ii, jj])
+        cin = {}
+        if p.accum:
+            cin = {"c_in": ge["C_in"].reshape(-1), "c_in_type": S.C_TYPE_CODE.get(p.c_type, S.F32), "ldcin": p.LDC}
+        ref.append(oracle.get().gemm_entries(p.M, p.N, p.K, ge["A"], p.LDA, p.a_col, ge["B"], p.LDB, p.b_col, p.dtype,
+                                             ii, jj, bias=ge["bias"], relu=p.relu, **cin))
+    got, ref = np.concatenate(got), np.concatenate(ref)
+    n_checked = int(got.size)
     if p.dtype == 3:
-        return {"entries": int(ii.size), "mismatches": int(np.sum(got != ref)), "ok": bool(np.all(got == ref))}
+        return {"entries": n_checked, "mismatches": int(np.sum(got != ref)), "ok": bool(np.all(got == ref))}
 
     def amax(x, dt):
         return float(np.max(np.abs(_decode(x, dt))))
@@ -209,7 +225,7 @@ def _oracle_sampled_check(p, g, C):
     excess = np.abs(got.astype(np.float64) - ref) - u * np.abs(ref)
     err = max(float(np.max(excess)), 0.0) / (denom if denom > 0 else 1.0)
     tol = 1e-5 if p.dtype == 2 else 1e-3
-    return {"entries": int(ii.size), "normalised_error": err, "tolerance": tol, "ok": err <= tol}
+    return {"entries": n_checked, "normalised_error": err, "tolerance": tol, "ok": err <= tol}
 
 
 def _decode(x, dt):
@@ -221,6 +237,9 @@ def _decode(x, dt):
 
 
 def _oracle_rows(o, p, g, rows):
+    if p.batch > 1:  # one entry of a batch stands for all of them
+        import synthetic as S
+        p, g = p.entry(0), S.entry_inputs(p, g, 0)
     A = g["A"]
     a_rows = A[:rows] if not p.a_col else A
     t = time.perf_counter()

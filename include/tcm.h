@@ -112,6 +112,39 @@ int tcm_gemm(int64_t M, int64_t N, int64_t K,
              int dtype, const void* bias, int epilogue,
              void* stream);
 
+/*
+ * tcm_gemm_batched -- `batch` independent products of one shape,
+ *
+ *     C_e = epi( [C_e,in +] bias_e + A_e . B_e ),   e = 0 .. batch-1,
+ *
+ * with entry e of each operand at a fixed element stride from the first:
+ * A_e = A + e*stride_a, B_e = B + e*stride_b, C_e = C + e*stride_c,
+ * bias_e = bias + e*stride_bias (pointer arithmetic in elements of each
+ * operand's own type).  All entries share M, N, K, the leading dimensions,
+ * dtype and epilogue.  The tiles of all entries form one work list, so
+ * split-k (Stream-K) spreads the k-iterations of every entry's tiles over
+ * one persistent grid: many skinny products fill the GPU together, the
+ * contiguous-batching case that motivates Stream-K (leiblog.wang, the
+ * Stream-K reproduction post).
+ *
+ *   batch        >= 0 (0: nothing to do).  batch < 2^31.
+ *   stride_*     >= 0 and < 2^40 elements.  0 shares one operand (or bias)
+ *                across the batch.  The entries of C are written, so with
+ *                batch > 1 stride_c must be at least the extent of one C
+ *                ((M-1)*ldc + N elements): C entries never overlap.
+ *   the rest     as tcm_gemm, per entry; the overlap check covers the
+ *                whole span of each operand over the batch.
+ * Returns as tcm_gemm; TCM_ERR_INVALID_VALUE also for a negative batch or
+ * stride, or overlapping C entries.  tcm_gemm(...) is tcm_gemm_batched with
+ * batch 1.
+ */
+int tcm_gemm_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
+                     const void* A, int64_t lda, int64_t stride_a,
+                     const void* B, int64_t ldb, int64_t stride_b,
+                     void* C, int64_t ldc, int64_t stride_c,
+                     int dtype, const void* bias, int64_t stride_bias, int epilogue,
+                     void* stream);
+
 /* Text of a status code (static storage; never NULL). */
 const char* tcm_status_string(int status);
 

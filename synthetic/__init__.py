@@ -15,6 +15,9 @@ Recipe (one numpy PCG64 generator per problem, ``np.random.default_rng(seed)``):
     torch's RNE cast on the CPU, float32 as is;
   * int8 operands: ``rng.integers(-128, 127, endpoint=True)``; int32 bias:
     ``rng.integers(-2**20, 2**20, endpoint=True)``;
+  * a batch of ``batch`` entries draws each operand for all entries at once,
+    entry after entry (A: (batch, storage shape), then B -- one shared entry
+    with ``b_shared`` --, then the bias (batch, N), then C_in);
   * with ``accum``, the initial-value tensor C_in (the M x ldc storage of C
     before the call, padding included) is drawn last: float problems
     ``rng.uniform(-1, 1)`` rounded like the operands to C's type (f32, f16
@@ -52,6 +55,8 @@ class Problem:
     ldc: int = 0
     c_type: str = "acc"        # C storage: "acc" (f32 / int32), "f16", "bf16"
     accum: bool = False        # C's contents before the call seed the accumulator
+    batch: int = 1             # entries of a strided batch (arrays gain a leading batch axis when > 1)
+    b_shared: bool = False     # one B for every entry (batch stride 0)
 
     @property
     def LDA(self):
@@ -77,13 +82,19 @@ class Problem:
     def c_bytes(self):
         return 4 if self.c_type == "acc" else 2
 
+    def entry(self, e=0):
+        """One entry of a batch as a single problem (same shapes and storage)."""
+        return replace(self, batch=1, b_shared=False, name=f"{self.name}[{e}]")
+
     @property
     def alg_bytes(self):
         """Bytes the product must move at least: A and B read once, C written once (and read
         once with accum), bias read once."""
-        b = (self.M * self.K + self.K * self.N) * self.in_bytes + self.M * self.N * self.c_bytes * (2 if self.accum else 1)
+        nb = 1 if self.b_shared else self.batch
+        b = self.batch * self.M * self.K * self.in_bytes + nb * self.K * self.N * self.in_bytes
+        b += self.batch * self.M * self.N * self.c_bytes * (2 if self.accum else 1)
         if self.bias:
-            b += self.N * 4
+            b += self.batch * self.N * 4
         return b
 
 
@@ -106,6 +117,8 @@ def _workloads():
                                  accum=True)
     w["skinny_m16_accum_c16"] = Problem("skinny_m16_accum_c16", F16, 16, 4096, 4096, dist="uniform", seed=7,
                                         c_type="f16", accum=True)
+    # a strided batch of skinny products, each with its own B (experts of a mixture, a few rows each)
+    w["batch8_m16_4096"] = Problem("batch8_m16_4096", F16, 16, 4096, 4096, dist="uniform", seed=8, batch=8)
     return w
 
 
@@ -169,17 +182,19 @@ def generate(p: Problem):
     With ld larger than the extent, the padding columns are drawn too (from
     the same stream, as part of the storage array)."""
     rng = np.random.default_rng(p.seed)
-    A = _draw(rng, _operand_shape(p.M, p.K, p.a_col, p.LDA), p.dist, p.dtype)
-    B = _draw(rng, _operand_shape(p.K, p.N, p.b_col, p.LDB), p.dist, p.dtype)
+    lead = (p.batch,) if p.batch > 1 else ()
+    A = _draw(rng, lead + _operand_shape(p.M, p.K, p.a_col, p.LDA), p.dist, p.dtype)
+    B = _draw(rng, (lead if not p.b_shared else (1,) if lead else ()) + _operand_shape(p.K, p.N, p.b_col, p.LDB),
+              p.dist, p.dtype)
     bias = None
     if p.bias:
         if p.dtype == I8:
-            bias = rng.integers(-2 ** 20, 2 ** 20, size=p.N, endpoint=True, dtype=np.int64).astype(np.int32)
+            bias = rng.integers(-2 ** 20, 2 ** 20, size=lead + (p.N,), endpoint=True, dtype=np.int64).astype(np.int32)
         else:
-            bias = rng.uniform(-1.0, 1.0, size=p.N).astype(np.float32)
+            bias = rng.uniform(-1.0, 1.0, size=lead + (p.N,)).astype(np.float32)
     c_in = None
     if p.accum:
-        shape = (max(p.M, 1), p.LDC)
+        shape = lead + (max(p.M, 1), p.LDC)
         if p.dtype == I8:
             c_in = rng.integers(-2 ** 20, 2 ** 20, size=shape, endpoint=True, dtype=np.int64).astype(np.int32)
         else:
@@ -200,9 +215,19 @@ def sample_entries(p: Problem, n=4096):
 
 
 def small_problem(dtype, M, N, K, seed=0, a_col=False, b_col=False, bias=False, relu=False,
-                  lda=0, ldb=0, ldc=0, dist=None, c_type="acc", accum=False):
+                  lda=0, ldb=0, ldc=0, dist=None, c_type="acc", accum=False, batch=1, b_shared=False):
     """An ad-hoc problem for parity cases (ragged shapes, padding, layouts)."""
     if dist is None:
         dist = "int" if dtype == I8 else "uniform"
-    return Problem(f"{DTYPE_NAMES[dtype]}_{M}x{N}x{K}", dtype, M, N, K, a_col=a_col, b_col=b_col, dist=dist,
-                   seed=seed, bias=bias, relu=relu, lda=lda, ldb=ldb, ldc=ldc, c_type=c_type, accum=accum)
+    return Problem(f"{DTYPE_NAMES[dtype]}_{M}x{N}x{K}" + (f"_b{batch}" if batch > 1 else ""), dtype, M, N, K,
+                   a_col=a_col, b_col=b_col, dist=dist, seed=seed, bias=bias, relu=relu, lda=lda, ldb=ldb, ldc=ldc,
+                   c_type=c_type, accum=accum, batch=batch, b_shared=b_shared)
+
+
+def entry_inputs(p: Problem, g, e):
+    """The storage arrays of entry e of a batched problem's inputs g."""
+    if p.batch == 1:
+        return g
+    return {"A": g["A"][e], "B": g["B"][0 if p.b_shared else e],
+            "bias": None if g["bias"] is None else g["bias"][e],
+            "C_in": None if g["C_in"] is None else g["C_in"][e]}

@@ -50,6 +50,8 @@ def lib():
         i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         L.tcm_gemm.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, vp, ci, vp]
         L.tcm_gemm.restype = ci
+        L.tcm_gemm_batched.argtypes = [i64, i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64, ci, vp, i64, ci, vp]
+        L.tcm_gemm_batched.restype = ci
         L.tcm_status_string.argtypes = [ci]
         L.tcm_status_string.restype = ctypes.c_char_p
         L.tcm_set_option.argtypes = [ctypes.c_char_p, i64]
@@ -81,6 +83,14 @@ def tcm_gemm(M, N, K, A, lda, B, ldb, C, ldc, dtype, bias, epilogue, stream):
     """C = epi(bias + A.B); pointers are device addresses (ints), stream a
     hipStream_t handle (int) or None.  Returns the tcm status code."""
     return lib().tcm_gemm(M, N, K, A, lda, B, ldb, C, ldc, dtype, bias, epilogue, stream)
+
+
+def tcm_gemm_batched(batch, M, N, K, A, lda, stride_a, B, ldb, stride_b, C, ldc, stride_c, dtype, bias, stride_bias,
+                     epilogue, stream):
+    """`batch` products C_e = epi(bias_e + A_e.B_e), entry e of each operand
+    `stride_*` elements after entry e-1.  Returns the tcm status code."""
+    return lib().tcm_gemm_batched(batch, M, N, K, A, lda, stride_a, B, ldb, stride_b, C, ldc, stride_c, dtype, bias,
+                                  stride_bias, epilogue, stream)
 
 
 def tcm_status_string(status):
@@ -215,4 +225,52 @@ def gemm(A, B, C=None, bias=None, relu=False, accumulate=False, out_dtype=None, 
                   bias.data_ptr() if bias is not None else None, epi, stream)
     if st != TCM_OK:
         raise TcmError(st, "tcm_gemm")
+    return C
+
+
+def gemm_batched(A, B, C=None, bias=None, relu=False, accumulate=False, out_dtype=None, stream=None):
+    """C[e] = relu?(A[e] @ B[e] + bias [+ C[e]]) for every e, via tcm_gemm_batched.
+
+    A: (batch, M, K), B: (batch, K, N) CUDA tensors whose last two dimensions
+    are row- or column-major views; a batch stride of 0 (an expanded tensor)
+    shares that operand across the batch.  C: optional (batch, M, N) with
+    row-major entries.  bias: optional (N,) shared or (batch, N) per entry.
+    Other arguments as gemm()."""
+    import torch
+    if A.dim() != 3 or B.dim() != 3 or A.shape[0] != B.shape[0]:
+        raise ValueError("A and B must be (batch, M, K) and (batch, K, N)")
+    if A.dtype != B.dtype:
+        raise TypeError("A and B must have the same dtype")
+    code = _torch_dtype_code(A)
+    batch, M, K = A.shape
+    _, K2, N = B.shape
+    if K != K2:
+        raise ValueError(f"inner sizes differ: {K} vs {K2}")
+    lda, a_col = _layout(A[0], "A")
+    ldb, b_col = _layout(B[0], "B")
+    acc_dtype = torch.int32 if code == TCM_I8_I32 else torch.float32
+    if accumulate and C is None:
+        raise ValueError("accumulate needs C")
+    if C is None:
+        C = torch.empty((batch, M, N), dtype=out_dtype or acc_dtype, device=A.device)
+    c_flags = {torch.float16: TCM_C_F16, torch.bfloat16: TCM_C_BF16}.get(C.dtype, 0)
+    if c_flags and code == TCM_I8_I32:
+        raise TypeError("int8 products have an int32 C")
+    if (C.dtype != acc_dtype and not c_flags) or C.dim() != 3 or tuple(C.shape) != (batch, M, N) or \
+            (N > 1 and C.stride(2) != 1):
+        raise ValueError("C must be (batch, M, N) with row-major entries of the accumulator type, float16 or bfloat16")
+    ldc = max(C.stride(1), N, 1)
+    sb_bias = 0
+    if bias is not None:
+        if bias.dtype != acc_dtype or bias.shape[-1] < N or bias.stride(-1) != 1:
+            raise ValueError("bias must be (N,) or (batch, N) of the accumulator type with contiguous rows")
+        sb_bias = bias.stride(0) if bias.dim() == 2 else 0
+    epi = (TCM_EPI_BIAS if bias is not None else 0) | (TCM_EPI_RELU if relu else 0) | (TCM_EPI_ACCUM if accumulate else 0)
+    dtype = code | (TCM_A_COLMAJOR if a_col else 0) | (TCM_B_COLMAJOR if b_col else 0) | c_flags
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+    st = tcm_gemm_batched(batch, M, N, K, A.data_ptr(), lda, A.stride(0), B.data_ptr(), ldb, B.stride(0), C.data_ptr(),
+                          ldc, C.stride(0), dtype, bias.data_ptr() if bias is not None else None, sb_bias, epi, stream)
+    if st != TCM_OK:
+        raise TcmError(st, "tcm_gemm_batched")
     return C

@@ -101,7 +101,14 @@ __global__ __launch_bounds__(256) void generic_gemm_kernel(GenericArgs a) {
     __shared__ __attribute__((aligned(16))) char As[kTile * kRow];
     __shared__ __attribute__((aligned(16))) char Bs[kTile * kRow];
 
-    const int tm = blockIdx.x / a.tiles_n, tn = blockIdx.x % a.tiles_n;
+    // workgroup -> (entry of the batch, tile of that entry)
+    const int per = a.tiles_m * a.tiles_n;
+    const int bi = blockIdx.x / per, t = blockIdx.x - bi * per;
+    a.A = (const T*)a.A + bi * a.stride_a;
+    a.B = (const T*)a.B + bi * a.stride_b;
+    a.C = (char*)a.C + bi * a.stride_c * c_elem_bytes(a.c_type);
+    if (a.bias) a.bias = (const AccS*)a.bias + bi * a.stride_bias;
+    const int tm = t / a.tiles_n, tn = t % a.tiles_n;
     const int64_t m0 = (int64_t)tm * kTile, n0 = (int64_t)tn * kTile;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -162,7 +169,7 @@ __global__ void fill_zero_kernel(int* p, int64_t n) {
 }  // namespace
 
 int launch_generic(int dtype, const GenericArgs& a, void* stream) {
-    const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n;
+    const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n * a.batch;
     hipStream_t s = (hipStream_t)stream;
     switch (dtype) {
     case F16: hipLaunchKernelGGL(generic_gemm_kernel<F16>, dim3((unsigned)blocks), dim3(256), 0, s, a); break;

@@ -82,7 +82,7 @@ bool tile_eligible(const Problem& p, const TileConfig& c) {
     }
     const int cs = c_elem_bytes(p.c_type);
     if ((int64_t)c.bm * p.ldc * cs + (int64_t)c.bn * cs >= kOffsetLimit) return false;
-    const int64_t tiles = cdiv(p.M, c.bm) * cdiv(p.N, c.bn);
+    const int64_t tiles = cdiv(p.M, c.bm) * cdiv(p.N, c.bn) * std::max<int64_t>(p.batch, 1);
     if (tiles >= (1LL << 31)) return false;
     return true;
 }
@@ -105,7 +105,7 @@ struct Estimate {
 Estimate estimate(const Problem& p, const TileConfig& c, int cus, int force_mode, int sk_grid, int sk_occ_known) {
     const int dt = p.dtype;
     const int bke = bk_elems(dt);
-    const int64_t T = cdiv(p.M, c.bm) * cdiv(p.N, c.bn);
+    const int64_t T = cdiv(p.M, c.bm) * cdiv(p.N, c.bn) * std::max<int64_t>(p.batch, 1);
     const int64_t I = cdiv(p.K, bke);
     const int occ = tile_wg_per_cu(c);
     const int64_t slots = (int64_t)cus * occ;
@@ -116,8 +116,9 @@ Estimate estimate(const Problem& p, const TileConfig& c, int cus, int force_mode
     const double step = std::max(mfma, std::max(lds, l2)) + kStepOverhead;  // per K-step, CU to itself
     const double lone_step = kStepLatency + (c.bm + c.bn) * (double)kStepBytes / kStepBytesPerClk;
     const double tile_store = (double)c.bm * c.bn * 4 / kL2BytesPerClk;
-    const double hbm_floor = ((double)p.M * p.K + (double)p.K * p.N) * elem_bytes(dt) / kHbmBytesPerClk +
-                             (double)p.M * p.N * 4 / kHbmBytesPerClk;
+    const double hbm_floor = (double)std::max<int64_t>(p.batch, 1) *
+                             (((double)p.M * p.K + (double)p.K * p.N) * elem_bytes(dt) + (double)p.M * p.N * 4) /
+                             kHbmBytesPerClk;
 
     // data-parallel: waves of `slots` tiles, each wave takes I steps on a CU shared by `occ` workgroups
     Estimate dp{0, 1, (int)std::min<int64_t>(T, 1LL << 30), T, 0};
@@ -203,7 +204,7 @@ bool make_plan(const Problem& p, const Options& o, int cus, Plan* out) {
         pl.kernel = 1;
         pl.bm = pl.bn = 64;
         pl.bk = 64 / elem_bytes(p.dtype);
-        pl.tiles = cdiv(p.M, 64) * cdiv(p.N, 64);
+        pl.tiles = cdiv(p.M, 64) * cdiv(p.N, 64) * std::max<int64_t>(p.batch, 1);
         pl.iters = cdiv(p.K, pl.bk);
         pl.mode = 1;
         pl.grid = (int)std::min<int64_t>(pl.tiles, (1LL << 31) - 1);
@@ -218,7 +219,7 @@ bool make_plan(const Problem& p, const Options& o, int cus, Plan* out) {
     pl.bm = c.bm;
     pl.bn = c.bn;
     pl.bk = bk_elems(p.dtype);
-    pl.tiles = cdiv(p.M, c.bm) * cdiv(p.N, c.bn);
+    pl.tiles = cdiv(p.M, c.bm) * cdiv(p.N, c.bn) * std::max<int64_t>(p.batch, 1);
     pl.iters = cdiv(p.K, pl.bk);
     pl.mode = best_e.mode;
     pl.est_cycles = best_e.cycles;

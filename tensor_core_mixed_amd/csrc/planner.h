@@ -22,6 +22,7 @@ struct Problem {
     bool a_col, b_col;
     int epilogue;
     int c_type;    // CType
+    int64_t batch = 1;  // entries of a strided batch
     bool aligned;  // every pointer 16-byte aligned
 };
 

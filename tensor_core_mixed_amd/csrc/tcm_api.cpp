@@ -157,15 +157,16 @@ std::string describe(const Plan& pl, const Problem& p) {
     if (pl.kernel == 0) {
         snprintf(buf, sizeof buf, "empty problem M=%lld N=%lld", (long long)p.M, (long long)p.N);
     } else if (pl.kernel == 1) {
-        snprintf(buf, sizeof buf, "kernel=generic tile=64x64 tiles=%lld iters=%lld M=%lld N=%lld K=%lld dtype=%d",
-                 (long long)pl.tiles, (long long)pl.iters, (long long)p.M, (long long)p.N, (long long)p.K, p.dtype);
+        snprintf(buf, sizeof buf, "kernel=generic tile=64x64 tiles=%lld iters=%lld M=%lld N=%lld K=%lld dtype=%d batch=%lld",
+                 (long long)pl.tiles, (long long)pl.iters, (long long)p.M, (long long)p.N, (long long)p.K, p.dtype,
+                 (long long)p.batch);
     } else {
         snprintf(buf, sizeof buf,
                  "kernel=tile config=%d tile=%dx%dx%d mode=%s grid=%d tiles=%lld iters=%lld dp_tiles=%lld sk_tiles=%lld "
-                 "M=%lld N=%lld K=%lld dtype=%d b_col=%d est_cycles=%.0f",
+                 "M=%lld N=%lld K=%lld dtype=%d b_col=%d batch=%lld est_cycles=%.0f",
                  pl.config, pl.bm, pl.bn, pl.bk, pl.mode == 1 ? "dp" : "streamk", pl.grid, (long long)pl.tiles,
                  (long long)pl.iters, (long long)pl.dp_tiles, (long long)pl.sk_tiles, (long long)p.M, (long long)p.N,
-                 (long long)p.K, p.dtype, (int)p.b_col, pl.est_cycles);
+                 (long long)p.K, p.dtype, (int)p.b_col, (long long)p.batch, pl.est_cycles);
     }
     return buf;
 }
@@ -330,21 +331,45 @@ void tcm_release_workspace(void) {
     g_ws.clear();
 }
 
-int tcm_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
-             int dtype, const void* bias, int epilogue, void* stream) {
+}  // extern "C"
+
+namespace tcm {
+namespace {
+
+// Bytes spanned by `batch` entries of `ext` bytes placed `stride_bytes` apart.
+int64_t batch_extent(int64_t batch, int64_t stride_bytes, int64_t ext) {
+    return ext > 0 ? (batch - 1) * stride_bytes + ext : 0;
+}
+
+int gemm_impl(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int64_t sa, const void* B,
+              int64_t ldb, int64_t sb, void* C, int64_t ldc, int64_t sc, int dtype, const void* bias, int64_t sbias,
+              int epilogue, void* stream) {
     Problem p;
     int st = check_problem(M, N, K, lda, ldb, ldc, dtype, epilogue, &p);
     if (st != TCM_OK) return st;
-    if (M == 0 || N == 0) {
+    if (batch < 0 || sa < 0 || sb < 0 || sc < 0 || sbias < 0) return TCM_ERR_INVALID_VALUE;
+    // keep every byte offset of the batch inside int64 (and the tile count inside int32 below)
+    const int64_t kStrideLimit = (int64_t)1 << 40;
+    if (batch >= ((int64_t)1 << 31) || sa >= kStrideLimit || sb >= kStrideLimit || sc >= kStrideLimit ||
+        sbias >= kStrideLimit)
+        return TCM_ERR_INVALID_VALUE;
+    p.batch = batch;
+    if (M == 0 || N == 0 || batch == 0) {
         t_last_plan = "empty problem";
         return TCM_OK;
     }
     const int es = elem_bytes(p.dtype);
-    const int64_t a_ext = extent(p.a_col ? K : M, p.a_col ? M : K, lda) * es;
-    const int64_t b_ext = extent(p.b_col ? N : K, p.b_col ? K : N, ldb) * es;
     const int cs = c_elem_bytes(p.c_type);
-    const int64_t c_ext = extent(M, N, ldc) * cs;
+    const int64_t a_one = extent(p.a_col ? K : M, p.a_col ? M : K, lda) * es;
+    const int64_t b_one = extent(p.b_col ? N : K, p.b_col ? K : N, ldb) * es;
+    const int64_t c_one = extent(M, N, ldc) * cs;
+    // entries of C are written: they must not overlap one another
+    if (batch > 1 && sc * cs < c_one) return TCM_ERR_INVALID_VALUE;
+    const int64_t a_ext = batch_extent(batch, sa * es, a_one);
+    const int64_t b_ext = batch_extent(batch, sb * es, b_one);
+    const int64_t c_ext = batch_extent(batch, sc * cs, c_one);
     const bool use_bias = epilogue & TCM_EPI_BIAS;
+    const int64_t bias_ext = use_bias ? batch_extent(batch, sbias * 4, N * 4) : 0;
     if (!C) return TCM_ERR_INVALID_VALUE;
     if (a_ext > 0 && !A) return TCM_ERR_INVALID_VALUE;
     if (b_ext > 0 && !B) return TCM_ERR_INVALID_VALUE;
@@ -352,10 +377,13 @@ int tcm_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
     // pointers must be aligned to their element
     if (((uintptr_t)A % es) || ((uintptr_t)B % es) || ((uintptr_t)C % cs) || (use_bias && ((uintptr_t)bias % 4)))
         return TCM_ERR_INVALID_VALUE;
-    if (overlaps(C, c_ext, A, a_ext) || overlaps(C, c_ext, B, b_ext) || (use_bias && overlaps(C, c_ext, bias, N * 4)))
+    if (overlaps(C, c_ext, A, a_ext) || overlaps(C, c_ext, B, b_ext) || (use_bias && overlaps(C, c_ext, bias, bias_ext)))
         return TCM_ERR_INVALID_VALUE;
+    // the fast path wants every entry 16-byte aligned
     p.aligned = ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) && ((uintptr_t)C % 16 == 0) &&
-                (!use_bias || (uintptr_t)bias % 16 == 0);
+                (!use_bias || (uintptr_t)bias % 16 == 0) &&
+                (batch == 1 || ((sa * es) % 16 == 0 && (sb * es) % 16 == 0 && (sc * cs) % 16 == 0 &&
+                                (!use_bias || (sbias * 4) % 16 == 0)));
 
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) {
@@ -386,6 +414,11 @@ int tcm_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
         g.has_bias = use_bias;
         g.accum = (epilogue & TCM_EPI_ACCUM) != 0;
         g.c_type = p.c_type;
+        g.batch = (int)batch;
+        g.stride_a = sa;
+        g.stride_b = sb;
+        g.stride_c = sc;
+        g.stride_bias = sbias;
         g.tiles_m = (int)((M + 63) / 64);
         g.tiles_n = (int)((N + 63) / 64);
         return launch_generic(p.dtype, g, stream) == 0 ? TCM_OK : TCM_ERR_HIP;
@@ -406,6 +439,11 @@ int tcm_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
     a.has_bias = use_bias;
     a.accum = (epilogue & TCM_EPI_ACCUM) != 0;
     a.c_type = p.c_type;
+    a.batch = (int)batch;
+    a.stride_a = sa;
+    a.stride_b = sb;
+    a.stride_c = sc;
+    a.stride_bias = sbias;
     a.tiles_m = (int)((M + pl.bm - 1) / pl.bm);
     a.tiles_n = (int)((N + pl.bn - 1) / pl.bn);
     a.iters = (int)pl.iters;
@@ -426,6 +464,23 @@ int tcm_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
     TileLauncher launch = tile_launcher(pl.config, p.dtype, p.b_col);
     if (!launch) return TCM_ERR_NOT_SUPPORTED;
     return launch(a, stream) == 0 ? TCM_OK : TCM_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace tcm
+
+extern "C" {
+
+int tcm_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+             int dtype, const void* bias, int epilogue, void* stream) {
+    return gemm_impl(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, dtype, bias, 0, epilogue, stream);
+}
+
+int tcm_gemm_batched(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int64_t stride_a,
+                     const void* B, int64_t ldb, int64_t stride_b, void* C, int64_t ldc, int64_t stride_c, int dtype,
+                     const void* bias, int64_t stride_bias, int epilogue, void* stream) {
+    return gemm_impl(batch, M, N, K, A, lda, stride_a, B, ldb, stride_b, C, ldc, stride_c, dtype, bias, stride_bias, epilogue,
+                     stream);
 }
 
 }  // extern "C"

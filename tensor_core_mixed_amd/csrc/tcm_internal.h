@@ -41,6 +41,7 @@ inline int lds_bytes(const TileConfig& c) { return 2 * (c.bm + c.bn) * kStepByte
 // operands in elements.  The kernel runs `dp_tiles` tiles whole (tile t on
 // workgroup t % grid), then splits the k-iterations of the next `sk_tiles`
 // tiles evenly over the grid (Stream-K), fixing split tiles up through ws.
+// Tiles are counted over all `batch` entries.
 struct TileArgs {
     const void* A;
     const void* B;
@@ -52,7 +53,9 @@ struct TileArgs {
     int has_bias;
     int accum;            // C's contents seed the accumulator (read before written)
     int c_type;           // C storage: 0 the accumulator type (f32 / int32), 1 f16, 2 bf16
-    int tiles_m, tiles_n;
+    int batch;            // entries of a strided batch (1: a single product)
+    int64_t stride_a, stride_b, stride_c, stride_bias;  // element strides between entries
+    int tiles_m, tiles_n; // tiles of one entry
     int iters;            // k-iterations per tile = ceil(K / bk)
     int dp_tiles;
     int sk_tiles;
@@ -73,14 +76,20 @@ struct TileArgs {
 //     columns of that block only;
 //  3. inside a super-tile, walk groups of group_m rows column by column, so
 //     the 32 tiles an XCD runs at once form a group_m x (32/group_m) block.
-// Every step is a bijection on [0, tiles_m * tiles_n).
+// Every step is a bijection on [0, tiles_m * tiles_n).  A batch of
+// matrices shares one tile space: step 1 runs over all of it, then each
+// position splits into (entry, tile within the entry) before steps 2-3.
 #if defined(__HIPCC__)
 __host__ __device__
 #endif
-inline void tile_coords(int t, int tiles_m, int tiles_n, int group_m, int super_m, int super_n, int* tm, int* tn) {
-    const int T = tiles_m * tiles_n;
+inline int xcd_order(int t, int T) {
     const int q = T >> 3, r = T & 7, x = t & 7, local = t >> 3;
-    const int nt = x * q + (x < r ? x : r) + local;
+    return x * q + (x < r ? x : r) + local;
+}
+#if defined(__HIPCC__)
+__host__ __device__
+#endif
+inline void super_order(int nt, int tiles_m, int tiles_n, int group_m, int super_m, int super_n, int* tm, int* tn) {
     const int band = nt / (super_m * tiles_n);
     const int o = nt - band * super_m * tiles_n;
     const int h = tiles_m - band * super_m < super_m ? tiles_m - band * super_m : super_m;
@@ -92,6 +101,23 @@ inline void tile_coords(int t, int tiles_m, int tiles_n, int group_m, int super_
     const int inner = o2 - g * group_m * w;
     *tm = band * super_m + g * group_m + inner % gh;
     *tn = J * super_n + inner / gh;
+}
+#if defined(__HIPCC__)
+__host__ __device__
+#endif
+inline void tile_coords(int t, int tiles_m, int tiles_n, int group_m, int super_m, int super_n, int* tm, int* tn) {
+    super_order(xcd_order(t, tiles_m * tiles_n), tiles_m, tiles_n, group_m, super_m, super_n, tm, tn);
+}
+// Batched: tile t of a batch of `batch` entries of tiles_m x tiles_n tiles.
+#if defined(__HIPCC__)
+__host__ __device__
+#endif
+inline void batch_tile_coords(int t, int batch, int tiles_m, int tiles_n, int group_m, int super_m, int super_n, int* b,
+                              int* tm, int* tn) {
+    const int per = tiles_m * tiles_n;
+    const int nt = xcd_order(t, per * batch);
+    *b = nt / per;
+    super_order(nt - *b * per, tiles_m, tiles_n, group_m, super_m, super_n, tm, tn);
 }
 
 // Super-tile shape for a tiles_m x tiles_n grid: about T/8 tiles, near square.
@@ -121,6 +147,8 @@ struct GenericArgs {
     int has_bias;
     int accum;
     int c_type;
+    int batch;
+    int64_t stride_a, stride_b, stride_c, stride_bias;
     int tiles_m, tiles_n;
 };
 

@@ -340,8 +340,21 @@ struct TileKernel {
     }
 
     // ------------------------------------------------------- tile order
-    __device__ __forceinline__ static void tile_coords(int t, const TileArgs& a, int& tm, int& tn) {
-        tcm::tile_coords(t, a.tiles_m, a.tiles_n, a.group_m, a.super_m, a.super_n, &tm, &tn);
+    // Tile t of the (batched) tile space: its coordinates within its entry and
+    // the arguments with that entry's operand pointers (uniform per workgroup).
+    __device__ __forceinline__ static TileArgs tile_of(const TileArgs& a, int t, int& tm, int& tn) {
+        TileArgs e = a;
+        if (a.batch > 1) {
+            int b;
+            tcm::batch_tile_coords(t, a.batch, a.tiles_m, a.tiles_n, a.group_m, a.super_m, a.super_n, &b, &tm, &tn);
+            e.A = (const char*)a.A + b * a.stride_a * ES;
+            e.B = (const char*)a.B + b * a.stride_b * ES;
+            e.C = (char*)a.C + b * a.stride_c * c_elem_bytes(a.c_type);
+            if (a.bias) e.bias = (const char*)a.bias + b * a.stride_bias * (int64_t)sizeof(AccS);
+        } else {
+            tcm::tile_coords(t, a.tiles_m, a.tiles_n, a.group_m, a.super_m, a.super_n, &tm, &tn);
+        }
+        return e;
     }
 
     // ------------------------------------------------------- epilogue
@@ -612,11 +625,11 @@ struct TileKernel {
         const int wm = wave / WN, wn = wave % WN;
         Acc acc[FM][FN];
         int tm, tn;
-        tile_coords(blockIdx.x, a, tm, tn);
+        const TileArgs e = tile_of(a, blockIdx.x, tm, tn);
         const int m0 = tm * BM, n0 = tn * BN;
-        init_acc(acc, a, true, m0, n0, wm, wn, lane);
-        mainloop(acc, a, smem, m0, n0, 0, a.iters, wave, lane);
-        store_tile(acc, a, m0, n0, wm, wn, lane);
+        init_acc(acc, e, true, m0, n0, wm, wn, lane);
+        mainloop(acc, e, smem, m0, n0, 0, e.iters, wave, lane);
+        store_tile(acc, e, m0, n0, wm, wn, lane);
     }
 
     // Stream-K kernel: the k-iterations of tiles [dp_tiles, dp_tiles + sk_tiles)
@@ -642,13 +655,13 @@ struct TileKernel {
             const int k_lo = (int)(it - tsk * I);
             const int k_hi = (int)min<int64_t>(I, k_lo + (it1 - it));
             int tm, tn;
-            tile_coords(a.dp_tiles + (int)tsk, a, tm, tn);
+            const TileArgs e = tile_of(a, a.dp_tiles + (int)tsk, tm, tn);
             const int m0 = tm * BM, n0 = tn * BN;
-            init_acc(acc, a, k_lo == 0, m0, n0, wm, wn, lane);
-            mainloop(acc, a, smem, m0, n0, k_lo, k_hi, wave, lane);
+            init_acc(acc, e, k_lo == 0, m0, n0, wm, wn, lane);
+            mainloop(acc, e, smem, m0, n0, k_lo, k_hi, wave, lane);
             it += k_hi - k_lo;
             if (k_lo == 0 && k_hi == I) {
-                store_tile(acc, a, m0, n0, wm, wn, lane);
+                store_tile(acc, e, m0, n0, wm, wn, lane);
                 continue;
             }
             // Split tile: publish this segment (every wave waits until its
@@ -679,7 +692,7 @@ struct TileKernel {
                     load_partial(pw, partial_rsrc(a, slot_of(w)), wave, wm, lane, a.M - m0);
                     add_partial(acc, pw, w == w_first);
                 }
-                store_tile(acc, a, m0, n0, wm, wn, lane);
+                store_tile(acc, e, m0, n0, wm, wn, lane);
                 if (tid == 0) __hip_atomic_store(a.ws_counter + tsk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 continue;
             }
@@ -693,7 +706,7 @@ struct TileKernel {
                 if (w + 2 <= w_last) load_partial(p0, partial_rsrc(a, slot_of(w + 2)), wave, wm, lane, a.M - m0);
                 add_partial(acc, p1, false);
             }
-            store_tile(acc, a, m0, n0, wm, wn, lane);
+            store_tile(acc, e, m0, n0, wm, wn, lane);
             if (tid == 0) __hip_atomic_store(a.ws_counter + tsk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }

@@ -239,3 +239,26 @@ def test_tile_order_gives_each_xcd_one_block():
         assert len(rows) == 8 and len(cols) == 16
         first = tiles[:32]
         assert len({tm for tm, _ in first}) == 4 and len({tn for _, tn in first}) == 8
+
+
+BAD_BATCHED = [  # (batch, sa, sb, sc, sbias, C address)
+    (-1, 16, 16, 16, 0, 4096),     # negative batch
+    (2, -1, 16, 16, 0, 4096),      # negative stride
+    (2, 16, 16, 15, 0, 4096),      # C entries overlap (stride_c < (M-1)*ldc + N = 16)
+    (2, 1 << 40, 16, 16, 0, 4096), # stride beyond the limit
+    (3, 2048, 16, 16, 0, 4096 + 2 * 2048 * 2 - 8),  # C overlaps the last entry of A
+]
+
+
+@pytest.mark.parametrize("args", BAD_BATCHED)
+def test_invalid_batched_arguments(args):
+    batch, sa, sb, sc, sbias, cptr = args
+    st = T.tcm_gemm_batched(batch, 4, 4, 4, 4096, 4, sa, 1 << 20, 4, sb, cptr, 4, sc, T.TCM_F16_F32, None, sbias, 0, None)
+    assert st == T.TCM_ERR_INVALID_VALUE
+
+
+def test_batched_empty_and_valid_without_device():
+    # batch 0 is a no-op even with NULL pointers; a valid batch reaches the first HIP call
+    assert T.tcm_gemm_batched(0, 4, 4, 4, None, 4, 0, None, 4, 0, None, 4, 0, 0, None, 0, 0, None) == T.TCM_OK
+    st = T.tcm_gemm_batched(4, 64, 64, 64, 1 << 20, 64, 4096, 2 << 20, 64, 0, 3 << 20, 64, 4096, 0, None, 0, 0, None)
+    assert st == T.TCM_ERR_HIP

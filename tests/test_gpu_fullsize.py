@@ -13,7 +13,8 @@ from gpu_util import check, run_tcm, say
 pytestmark = pytest.mark.gpu
 
 FULL = {"f16_512", "f32_2048", "skinny_m1", "skinny_m16", "skinny_m64", "skinny_m256"}
-SPLITK = ["skinny_m1", "skinny_m16", "skinny_m64", "skinny_m256", "sk_1536x1536x16384", "sk_3840x3840x4096"]
+SPLITK = ["skinny_m1", "skinny_m16", "skinny_m64", "skinny_m256", "sk_1536x1536x16384", "sk_3840x3840x4096",
+          "batch8_m16_4096"]
 
 
 @pytest.fixture(autouse=True)
@@ -25,15 +26,22 @@ def _reset_options():
 def _check_workload(name, mode):
     p = S.workload(name)
     T.tcm_set_option("force_mode", mode)
-    say(f"[case] workload {name} M={p.M} N={p.N} K={p.K} dtype={p.dtype} b_col={p.b_col} seed={p.seed} force_mode={mode}")
+    say(f"[case] workload {name} M={p.M} N={p.N} K={p.K} dtype={p.dtype} b_col={p.b_col} batch={p.batch} "
+        f"seed={p.seed} force_mode={mode}")
     g = S.generate(p)
-    C, plan = run_tcm(p, g)
-    say(f"       plan: {plan}")
-    if name in FULL:
-        err = check(p, g, C)
+    if p.batch > 1:
+        from test_gpu_batched import check_batch, run_batched
+        C, plan = run_batched(p, g)
+        say(f"       plan: {plan}")
+        err = check_batch(p, g, C)  # every entry of every product
     else:
-        ii, jj = S.sample_entries(p)
-        err = check(p, g, C, ii, jj)
+        C, plan = run_tcm(p, g)
+        say(f"       plan: {plan}")
+        if name in FULL:
+            err = check(p, g, C)
+        else:
+            ii, jj = S.sample_entries(p)
+            err = check(p, g, C, ii, jj)
     say(f"       normalised error {err:.3e}")
     return C, plan
 
@@ -66,6 +74,8 @@ def test_int8_full_rows_bit_exact():
 def test_host_plan_query_matches_launch(name):
     """tcm_plan (no launch) reports the kernel, config, mode and grid tcm_gemm then launches."""
     p = S.workload(name)
+    if p.batch > 1:
+        pytest.skip("tcm_plan describes a single product")
     code = p.dtype | (T.TCM_A_COLMAJOR if p.a_col else 0) | (T.TCM_B_COLMAJOR if p.b_col else 0)
     code |= {"acc": 0, "f16": T.TCM_C_F16, "bf16": T.TCM_C_BF16}[p.c_type]
     epi = (T.TCM_EPI_BIAS if p.bias else 0) | (T.TCM_EPI_RELU if p.relu else 0) | (T.TCM_EPI_ACCUM if p.accum else 0)
