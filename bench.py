@@ -35,12 +35,13 @@ DTYPE_NAME = {0: "f16", 1: "bf16", 2: "f32", 3: "i8"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{name}.json")
 
 
+# the sources of the tiled GEMM kernel, whose launches the stored counters describe
 KERNEL_SOURCES = ("tcm_internal.h", "tile_kernel.h", "tile_instances.h", "tile_f16.hip", "tile_bf16.hip",
-                  "tile_f32.hip", "tile_i8.hip", "generic_kernel.hip")
+                  "tile_f32.hip", "tile_i8.hip")
 
 
 def kernel_source_hash():
-    """Hash of the device-code sources: counters taken on other kernels are stale."""
+    """Hash of the tiled kernel's sources: counters taken on other code are stale."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "tensor_core_mixed_amd", "csrc")
     for f in KERNEL_SOURCES:

@@ -72,7 +72,7 @@ class Problem:
 
     @property
     def flops(self):
-        return 2.0 * self.M * self.N * self.K
+        return 2.0 * self.M * self.N * self.K * self.batch
 
     @property
     def in_bytes(self):
