@@ -124,10 +124,17 @@ def make_call(p, A, B, bias, C, stream):
     return call
 
 
-def time_steps(call, steps, warmup, stream_obj):
+def time_steps(call, steps, warmup, stream_obj, min_warm_ms=0.0):
+    """`warmup` untimed calls (continued until `min_warm_ms` of wall time has
+    passed, if given), then `steps` calls between two events on the stream."""
     import torch
-    for _ in range(warmup):
+    t_warm = time.perf_counter()
+    done = 0
+    while done < warmup or (time.perf_counter() - t_warm) * 1e3 < min_warm_ms:
         call()
+        done += 1
+        if done % 32 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -359,7 +366,7 @@ def run_all(args):
             call()
             torch.cuda.synchronize()
             plan = T.tcm_last_plan()
-            ms, _ = time_steps(call, max(5, args.steps // 2), 10, s)
+            ms, _ = time_steps(call, max(5, args.steps // 2), 10, s, min_warm_ms=200.0)
             pc = per_call_us(call, max(5, args.steps // 2), s)
             par = None
             if not args.no_cpu:  # CPU leg: sampled check of one call from the initial state
@@ -374,6 +381,21 @@ def run_all(args):
                    "parity_ok": par["ok"] if par else None, "plan": plan}
             if name.startswith("skinny"):
                 row["cold_median_us"] = cold_us(call, 20, s)
+            if args.tune and mode == 0 and p.batch == 1:
+                # the tuning table's choice for this signature, then the same timing
+                code = p.dtype | (T.TCM_A_COLMAJOR if p.a_col else 0) | (T.TCM_B_COLMAJOR if p.b_col else 0)
+                code |= {"acc": 0, "f16": T.TCM_C_F16, "bf16": T.TCM_C_BF16}[p.c_type]
+                epi = (T.TCM_EPI_BIAS if p.bias else 0) | (T.TCM_EPI_RELU if p.relu else 0) | \
+                      (T.TCM_EPI_ACCUM if p.accum else 0)
+                st, best = T.tcm_tune(p.M, p.N, p.K, A.data_ptr(), p.LDA, B.data_ptr(), p.LDB, C.data_ptr(), p.LDC, code,
+                                      bias.data_ptr() if bias is not None else None, epi, 10, s.cuda_stream)
+                if st != 0:
+                    raise RuntimeError(T.tcm_status_string(st))
+                reset_c(p, g, C)
+                call()
+                torch.cuda.synchronize()
+                tms, _ = time_steps(call, max(5, args.steps // 2), 10, s, min_warm_ms=200.0)
+                row["tuned"] = {"ms": round(tms, 5), "plan": T.tcm_last_plan(), "model_over_tuned": round(ms / tms, 3)}
             rows.append(row)
         T.tcm_set_option("force_mode", 0)
         mine = [r for r in rows if r["workload"] == name]
@@ -421,7 +443,7 @@ def run_sweep(args):
                 plan = T.tcm_last_plan()
                 if f"config={cfg}" not in plan:
                     continue
-                ms, _ = time_steps(call, 10, 10, s)
+                ms, _ = time_steps(call, 10, 10, s, min_warm_ms=200.0)
                 rows.append({"workload": name, "config": cfg, "mode": mode, "us": round(ms * 1e3, 2), "plan": plan})
                 print("[sweep] " + json.dumps(rows[-1]), file=sys.stderr, flush=True)
         T.tcm_set_option("force_config", -1)
@@ -499,7 +521,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed calls before the timed ones (the clock needs tens of ms of load to settle)")
     ap.add_argument("--workload", default="f16_8192")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg")
     ap.add_argument("--dist", default=None, choices=["uniform", "normal", "uniform12", "ones", "zeros"],
@@ -507,6 +530,7 @@ def main():
     ap.add_argument("--all", action="store_true")
     ap.add_argument("--report", default=None)
     ap.add_argument("--sweep", action="store_true", help="time every tile config and mode on the split-k workloads")
+    ap.add_argument("--tune", action="store_true", help="with --all: also time each workload on its auto-tuned plan")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize-counters", default=None)
     ap.add_argument("--calibration", default=None, help="directory holding the copy-calibration counter runs")

@@ -21,9 +21,10 @@
  * on the current device).  The caller owns A, B, C and bias; the library
  * never frees them.  Calls are asynchronous on `stream` (a hipStream_t passed
  * as void*, NULL = the null stream) and never synchronise; results are
- * ready when the stream reaches the call.  Calls on one stream run in order;
- * the library's only state is a cached split-k workspace per (device,
- * stream), so concurrent calls on different streams are independent.
+ * ready when the stream reaches the call.  Calls on one stream run in order.
+ * The library's state is a cached split-k workspace per (device, stream),
+ * so concurrent calls on different streams are independent, plus the
+ * process-wide switches and tuning table below (mutex-protected).
  *
  * Errors are returned, never raised; argument checks run before any HIP call.
  */
@@ -159,6 +160,8 @@ const char* tcm_status_string(int status);
  *   "sk_grid"      0 = planner decides, else the persistent grid size for
  *                  split-k (clamped to the number of co-resident workgroups).
  *   "generic"      1 = route every call to the generic (any-alignment) kernel.
+ *   "tuned"        1 (default) = use the tuning table (tcm_tune) for problems
+ *                  it holds; 0 = ignore it.  force_config / force_mode win.
  * Unknown keys or out-of-range values: TCM_ERR_INVALID_VALUE.
  * tcm_get_option returns the value, or -2 for an unknown key.
  */
@@ -214,6 +217,41 @@ int tcm_streamk_range(int64_t sk_tiles, int64_t iters_per_tile, int32_t grid, in
  * t outside [0, tiles_m * tiles_n) or a grid of 2^31 tiles or more.
  */
 int tcm_tile_order(int32_t t, int32_t tiles_m, int32_t tiles_n, int32_t* tm, int32_t* tn);
+
+/* ---- auto-tuning ----------------------------------------------------------- */
+/*
+ * tcm_tune -- time every tile config in both modes (data-parallel, split-k)
+ * on this problem and remember the fastest for its signature (sizes, leading
+ * dimensions, dtype and flags, epilogue, 16-byte alignment of the pointers).
+ * Later tcm_gemm and tcm_plan calls with the same signature use it (option
+ * "tuned").  This is the schedule search of the pages (Fireiron's
+ * auto-tuning, the GEMM schedule exploration on kimm240.github.io/tvm)
+ * restricted to the tile table.
+ *
+ * Same arguments as tcm_gemm plus `iters` (timed calls per candidate,
+ * 1..10000) and `best` (optional: the chosen plan).  Runs on `stream`
+ * with the caller's buffers and BLOCKS until timing is done; C is written by
+ * every candidate, so its contents afterwards are one correct result, except
+ * with TCM_EPI_ACCUM, where C has been accumulated into repeatedly.
+ * Returns as tcm_gemm.
+ */
+int tcm_tune(int64_t M, int64_t N, int64_t K,
+             const void* A, int64_t lda, const void* B, int64_t ldb,
+             void* C, int64_t ldc, int dtype, const void* bias, int epilogue,
+             int iters, void* stream, tcm_plan_info* best);
+
+/*
+ * tcm_tune_table -- the tuning table as text, one line per signature:
+ *   "tcm-tune-1 batch M N K lda ldb ldc dtype a_col b_col c_type epilogue
+ *    aligned config mode microseconds"
+ * Writes it NUL-terminated into buf (truncated to len) and returns its full
+ * length.  tcm_tune_load parses such text and adds or replaces its entries
+ * (all-or-nothing: TCM_ERR_INVALID_VALUE and no change on a malformed line).
+ * tcm_tune_clear empties the table.  All three are host-only.
+ */
+int tcm_tune_table(char* buf, int64_t len);
+int tcm_tune_load(const char* text);
+void tcm_tune_clear(void);
 
 /* Describe the last plan tcm_gemm launched on this thread into buf (NUL-
  * terminated, truncated to len).  Returns the full length. */

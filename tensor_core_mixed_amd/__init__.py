@@ -69,6 +69,13 @@ def lib():
         L.tcm_tile_order.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                      ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
         L.tcm_tile_order.restype = ci
+        L.tcm_tune.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, vp, ci, ci, vp, ctypes.POINTER(_PlanInfo)]
+        L.tcm_tune.restype = ci
+        L.tcm_tune_table.argtypes = [ctypes.c_char_p, i64]
+        L.tcm_tune_table.restype = ci
+        L.tcm_tune_load.argtypes = [ctypes.c_char_p]
+        L.tcm_tune_load.restype = ci
+        L.tcm_tune_clear.restype = None
         L.tcm_last_plan.argtypes = [ctypes.c_char_p, i64]
         L.tcm_last_plan.restype = ci
         L.tcm_release_workspace.restype = None
@@ -140,6 +147,29 @@ def tcm_tile_order(t, tiles_m, tiles_n):
     if st != TCM_OK:
         raise TcmError(st, "tcm_tile_order")
     return tm.value, tn.value
+
+
+def tcm_tune(M, N, K, A, lda, B, ldb, C, ldc, dtype, bias, epilogue, iters, stream):
+    """Time every (tile config, mode) on this problem, remember the fastest;
+    returns (status, chosen plan as a dict or None)."""
+    info = _PlanInfo()
+    st = lib().tcm_tune(M, N, K, A, lda, B, ldb, C, ldc, dtype, bias, epilogue, iters, stream, ctypes.byref(info))
+    return st, ({f: getattr(info, f) for f, _ in _PlanInfo._fields_} if st == TCM_OK else None)
+
+
+def tcm_tune_table():
+    n = lib().tcm_tune_table(None, 0)
+    buf = ctypes.create_string_buffer(n + 1)
+    lib().tcm_tune_table(buf, n + 1)
+    return buf.value.decode()
+
+
+def tcm_tune_load(text):
+    return lib().tcm_tune_load(text.encode())
+
+
+def tcm_tune_clear():
+    lib().tcm_tune_clear()
 
 
 def tcm_last_plan():

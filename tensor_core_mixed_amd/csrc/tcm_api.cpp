@@ -49,6 +49,31 @@ namespace {
 
 std::mutex g_mu;
 Options g_opts;
+int g_use_tuned = 1;  // option "tuned"
+
+// Auto-tuned choices: the (tile config, mode) that measured fastest for one
+// problem signature.  Consulted by the planner for exactly that signature.
+struct TuneKey {
+    int64_t batch, M, N, K, lda, ldb, ldc;
+    int dtype, a_col, b_col, c_type, epilogue, aligned;
+    bool operator<(const TuneKey& o) const {
+        const int64_t x[13] = {batch, M, N, K, lda, ldb, ldc, dtype, a_col, b_col, c_type, epilogue, aligned};
+        const int64_t y[13] = {o.batch, o.M, o.N, o.K, o.lda, o.ldb, o.ldc, o.dtype, o.a_col, o.b_col, o.c_type,
+                               o.epilogue, o.aligned};
+        return std::lexicographical_compare(x, x + 13, y, y + 13);
+    }
+};
+struct TuneEntry {
+    int config, mode;
+    double us;  // measured time per call
+};
+std::map<TuneKey, TuneEntry> g_tune;
+TuneKey tune_key(const Problem& p) {
+    return TuneKey{p.batch, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, p.dtype, (int)p.a_col, (int)p.b_col, p.c_type,
+                   p.epilogue, (int)p.aligned};
+}
+// Candidates forced by tcm_tune on this thread (-1 / 0: none).
+thread_local int t_tune_config = -1, t_tune_mode = 0;
 
 struct Workspace {
     void* partial = nullptr;
@@ -74,6 +99,29 @@ int device_cus(int dev) {
 Options current_options() {
     std::lock_guard<std::mutex> lk(g_mu);
     return g_opts;
+}
+
+// Options for planning problem p: the global switches, then a tuned choice
+// for p's signature (unless a switch already forces config or mode), then a
+// candidate tcm_tune is timing on this thread.
+Options plan_options(const Problem& p) {
+    Options o;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        o = g_opts;
+        if (g_use_tuned && o.force_config < 0 && o.force_mode == 0) {
+            auto it = g_tune.find(tune_key(p));
+            if (it != g_tune.end()) {
+                o.force_config = it->second.config;
+                o.force_mode = it->second.mode;
+            }
+        }
+    }
+    if (t_tune_config >= 0) {
+        o.force_config = t_tune_config;
+        o.force_mode = t_tune_mode;
+    }
+    return o;
 }
 
 // Workgroups per CU of the Stream-K kernels of p's (dtype, B layout), as the
@@ -236,6 +284,9 @@ int tcm_set_option(const char* key, int64_t value) {
     } else if (!strcmp(key, "generic")) {
         if (value < 0 || value > 1) return TCM_ERR_INVALID_VALUE;
         g_opts.generic = (int)value;
+    } else if (!strcmp(key, "tuned")) {
+        if (value < 0 || value > 1) return TCM_ERR_INVALID_VALUE;
+        g_use_tuned = (int)value;
     } else {
         return TCM_ERR_INVALID_VALUE;
     }
@@ -249,6 +300,7 @@ int64_t tcm_get_option(const char* key) {
     if (!strcmp(key, "force_config")) return g_opts.force_config;
     if (!strcmp(key, "sk_grid")) return g_opts.sk_grid;
     if (!strcmp(key, "generic")) return g_opts.generic;
+    if (!strcmp(key, "tuned")) return g_use_tuned;
     return -2;
 }
 
@@ -277,7 +329,7 @@ int tcm_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t 
     int st = check_problem(M, N, K, lda, ldb, ldc, dtype, epilogue, &p);
     if (st != TCM_OK) return st;
     p.aligned = aligned != 0;
-    Options o = current_options();
+    Options o = plan_options(p);
     fill_sk_occupancy(p, &o);
     Plan pl;
     if (!make_plan(p, o, current_cus(), &pl)) return TCM_ERR_INVALID_VALUE;
@@ -390,7 +442,7 @@ int gemm_impl(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int
         (void)hipGetLastError();
         return TCM_ERR_HIP;
     }
-    Options o = current_options();
+    Options o = plan_options(p);
     fill_sk_occupancy(p, &o);
     Plan pl;
     if (!make_plan(p, o, device_cus(dev), &pl)) return TCM_ERR_INVALID_VALUE;
@@ -481,6 +533,150 @@ int tcm_gemm_batched(int64_t batch, int64_t M, int64_t N, int64_t K, const void*
                      const void* bias, int64_t stride_bias, int epilogue, void* stream) {
     return gemm_impl(batch, M, N, K, A, lda, stride_a, B, ldb, stride_b, C, ldc, stride_c, dtype, bias, stride_bias, epilogue,
                      stream);
+}
+
+int tcm_tune(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+             int dtype, const void* bias, int epilogue, int iters, void* stream, tcm_plan_info* best) {
+    if (iters < 1 || iters > 10000) return TCM_ERR_INVALID_VALUE;
+    // the model's own choice first: it validates the call and names the key
+    int st = gemm_impl(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, dtype, bias, 0, epilogue, stream);
+    if (st != TCM_OK) return st;
+    if (M == 0 || N == 0) return TCM_OK;
+    Problem p;
+    check_problem(M, N, K, lda, ldb, ldc, dtype, epilogue, &p);
+    const bool use_bias = epilogue & TCM_EPI_BIAS;
+    const int cs = c_elem_bytes(p.c_type);
+    p.aligned = ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) && ((uintptr_t)C % 16 == 0) &&
+                (!use_bias || (uintptr_t)bias % 16 == 0) && ((uintptr_t)C % cs == 0);
+    hipStream_t s = (hipStream_t)stream;
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess) return TCM_ERR_HIP;
+    if (hipEventCreate(&e1) != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return TCM_ERR_HIP;
+    }
+    auto run = [&]() { return gemm_impl(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, dtype, bias, 0, epilogue, stream); };
+    // The shader clock needs tens of milliseconds of load to settle: keep the
+    // model's plan running for at least 50 ms (measured on the stream) first.
+    {
+        float warm_ms = 0;
+        while (st == TCM_OK && warm_ms < 50.0f) {
+            if (hipEventRecord(e0, s) != hipSuccess) st = TCM_ERR_HIP;
+            for (int i = 0; i < 8 && st == TCM_OK; ++i) st = run();
+            float ms = 0;
+            if (st == TCM_OK && (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                                 hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
+                st = TCM_ERR_HIP;
+            warm_ms += ms;
+            if (ms <= 0 && st == TCM_OK) break;
+        }
+    }
+    // Two sweeps over the candidates; each keeps its better time.
+    double best_us = 1e300;
+    int best_cfg = -1, best_mode = 1;
+    std::vector<std::pair<int, int>> cands;
+    for (int c = 0; c < kNumConfigs; ++c)
+        for (int mode = 1; mode <= 2; ++mode) cands.emplace_back(c, mode);
+    std::vector<double> t_us(cands.size(), 1e300);
+    std::vector<char> valid(cands.size(), 1);
+    for (int sweep = 0; sweep < 2 && st == TCM_OK; ++sweep) {
+        for (size_t ci = 0; ci < cands.size() && st == TCM_OK; ++ci) {
+            if (!valid[ci]) continue;
+            t_tune_config = cands[ci].first;
+            t_tune_mode = cands[ci].second;
+            st = run();  // warm-up, and the plan this candidate really gets
+            // (an ineligible config falls back to the model's plan: skip it)
+            const char* cp = strstr(t_last_plan.c_str(), "config=");
+            const int pc = cp ? atoi(cp + 7) : -1;
+            const int pm = strstr(t_last_plan.c_str(), "mode=streamk") ? 2 : 1;
+            if (st != TCM_OK || pc != cands[ci].first || pm != cands[ci].second) {
+                valid[ci] = 0;
+                continue;
+            }
+            if (hipEventRecord(e0, s) != hipSuccess) st = TCM_ERR_HIP;
+            for (int i = 0; i < iters && st == TCM_OK; ++i) st = run();
+            float ms = 0;
+            if (st == TCM_OK && (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                                 hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
+                st = TCM_ERR_HIP;
+            if (st == TCM_OK) t_us[ci] = std::min(t_us[ci], (double)ms * 1e3 / iters);
+        }
+    }
+    for (size_t ci = 0; ci < cands.size(); ++ci)
+        if (valid[ci] && t_us[ci] < best_us) {
+            best_us = t_us[ci];
+            best_cfg = cands[ci].first;
+            best_mode = cands[ci].second;
+        }
+    t_tune_config = -1;
+    t_tune_mode = 0;
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (st != TCM_OK) return st;
+    if (best_cfg >= 0) {
+        std::lock_guard<std::mutex> lk(g_mu);
+        g_tune[tune_key(p)] = TuneEntry{best_cfg, best_mode, best_us};
+    }
+    if (best) return tcm_plan(M, N, K, lda, ldb, ldc, dtype, epilogue, p.aligned ? 1 : 0, best);
+    return TCM_OK;
+}
+
+int tcm_tune_table(char* buf, int64_t len) {
+    std::string out;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        char line[320];
+        for (const auto& kv : g_tune) {
+            const TuneKey& k = kv.first;
+            snprintf(line, sizeof line, "tcm-tune-1 %lld %lld %lld %lld %lld %lld %lld %d %d %d %d %d %d %d %d %.3f\n",
+                     (long long)k.batch, (long long)k.M, (long long)k.N, (long long)k.K, (long long)k.lda,
+                     (long long)k.ldb, (long long)k.ldc, k.dtype, k.a_col, k.b_col, k.c_type, k.epilogue, k.aligned,
+                     kv.second.config, kv.second.mode, kv.second.us);
+            out += line;
+        }
+    }
+    if (buf && len > 0) {
+        const int64_t n = std::min<int64_t>(len - 1, (int64_t)out.size());
+        memcpy(buf, out.data(), (size_t)n);
+        buf[n] = 0;
+    }
+    return (int)out.size();
+}
+
+int tcm_tune_load(const char* text) {
+    if (!text) return TCM_ERR_INVALID_VALUE;
+    std::vector<std::pair<TuneKey, TuneEntry>> rows;
+    const char* q = text;
+    while (*q) {
+        const char* eol = strchr(q, '\n');
+        std::string line(q, eol ? (size_t)(eol - q) : strlen(q));
+        q = eol ? eol + 1 : q + strlen(q);
+        if (line.find_first_not_of(" \t\r") == std::string::npos) continue;
+        long long v[7];
+        int d[8];
+        double us = 0;
+        char tag[16];
+        int used = 0;
+        const int n = sscanf(line.c_str(), "%15s %lld %lld %lld %lld %lld %lld %lld %d %d %d %d %d %d %d %d %lf %n", tag,
+                             &v[0], &v[1], &v[2], &v[3], &v[4], &v[5], &v[6], &d[0], &d[1], &d[2], &d[3], &d[4], &d[5],
+                             &d[6], &d[7], &us, &used);
+        if (n != 17 || strcmp(tag, "tcm-tune-1") || line.find_first_not_of(" \t\r", (size_t)used) != std::string::npos)
+            return TCM_ERR_INVALID_VALUE;
+        const TuneKey k{v[0], v[1], v[2], v[3], v[4], v[5], v[6], d[0], d[1], d[2], d[3], d[4], d[5]};
+        const int cfg = d[6], mode = d[7];
+        if (k.batch < 1 || k.M < 0 || k.N < 0 || k.K < 0 || k.dtype < F16 || k.dtype > I8 || cfg < 0 ||
+            cfg >= kNumConfigs || mode < 1 || mode > 2 || !(us >= 0))
+            return TCM_ERR_INVALID_VALUE;
+        rows.emplace_back(k, TuneEntry{cfg, mode, us});
+    }
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (const auto& r : rows) g_tune[r.first] = r.second;
+    return TCM_OK;
+}
+
+void tcm_tune_clear(void) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_tune.clear();
 }
 
 }  // extern "C"

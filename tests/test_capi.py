@@ -262,3 +262,60 @@ def test_batched_empty_and_valid_without_device():
     assert T.tcm_gemm_batched(0, 4, 4, 4, None, 4, 0, None, 4, 0, None, 4, 0, 0, None, 0, 0, None) == T.TCM_OK
     st = T.tcm_gemm_batched(4, 64, 64, 64, 1 << 20, 64, 4096, 2 << 20, 64, 0, 3 << 20, 64, 4096, 0, None, 0, 0, None)
     assert st == T.TCM_ERR_HIP
+
+
+HEADLINE_SIG = (1, 8192, 8192, 8192, 8192, 8192, 8192, 0, 0, 1, 0, 0, 1)  # batch M N K lda ldb ldc dtype a_col b_col c_type epi aligned
+
+
+def _line(sig, config, mode, us=12.5):
+    return "tcm-tune-1 " + " ".join(str(v) for v in sig) + f" {config} {mode} {us:.3f}"
+
+
+def test_tune_table_round_trip_and_use_by_the_planner():
+    T.tcm_tune_clear()
+    model = T.tcm_plan(8192, 8192, 8192, 8192, 8192, 8192, T.TCM_F16_F32 | T.TCM_B_COLMAJOR)
+    assert model["config"] == 0
+    text = _line(HEADLINE_SIG, 1, 2) + "\n" + _line((1, 64, 64, 64, 64, 64, 64, 3, 0, 0, 0, 3, 1), 4, 1) + "\n"
+    assert T.tcm_tune_load(text) == T.TCM_OK
+    out = T.tcm_tune_table()
+    assert sorted(out.strip().splitlines()) == sorted(text.strip().splitlines())
+    tuned = T.tcm_plan(8192, 8192, 8192, 8192, 8192, 8192, T.TCM_F16_F32 | T.TCM_B_COLMAJOR)
+    assert (tuned["config"], tuned["mode"]) == (1, 2)
+    # another signature (unaligned) is untouched
+    assert T.tcm_plan(8192, 8192, 8192, 8192, 8192, 8192, T.TCM_F16_F32 | T.TCM_B_COLMAJOR, aligned=False)["kernel"] == 0
+    T.tcm_set_option("tuned", 0)
+    try:
+        assert T.tcm_plan(8192, 8192, 8192, 8192, 8192, 8192, T.TCM_F16_F32 | T.TCM_B_COLMAJOR)["config"] == 0
+    finally:
+        T.tcm_set_option("tuned", 1)
+    # an explicit switch wins over the table
+    T.tcm_set_option("force_config", 2)
+    try:
+        assert T.tcm_plan(8192, 8192, 8192, 8192, 8192, 8192, T.TCM_F16_F32 | T.TCM_B_COLMAJOR)["config"] == 2
+    finally:
+        T.tcm_set_option("force_config", -1)
+    T.tcm_tune_clear()
+    assert T.tcm_tune_table() == ""
+    assert T.tcm_plan(8192, 8192, 8192, 8192, 8192, 8192, T.TCM_F16_F32 | T.TCM_B_COLMAJOR)["config"] == 0
+
+
+@pytest.mark.parametrize("bad", [
+    "tcm-tune-2 1 8 8 8 8 8 8 0 0 0 0 0 1 0 1 1.0",          # unknown version tag
+    "tcm-tune-1 1 8 8 8 8 8 8 0 0 0 0 0 1 9 1 1.0",          # no such config
+    "tcm-tune-1 1 8 8 8 8 8 8 0 0 0 0 0 1 0 3 1.0",          # no such mode
+    "tcm-tune-1 1 8 8 8 8 8 8 0 0 0 0 0 1 0 1",              # missing field
+    "tcm-tune-1 1 8 8 8 8 8 8 0 0 0 0 0 1 0 1 1.0 extra",    # trailing text
+    "tcm-tune-1 0 8 8 8 8 8 8 0 0 0 0 0 1 0 1 1.0",          # batch 0
+])
+def test_tune_load_rejects_malformed_text_all_or_nothing(bad):
+    T.tcm_tune_clear()
+    good = _line(HEADLINE_SIG, 1, 1)
+    assert T.tcm_tune_load(good + "\n" + bad + "\n") == T.TCM_ERR_INVALID_VALUE
+    assert T.tcm_tune_table() == ""  # the good line was not applied either
+    assert T.tcm_tune_load("") == T.TCM_OK  # empty text: nothing to do
+
+
+def test_tune_invalid_arguments_without_device():
+    assert T.tcm_tune(64, 64, 64, 1 << 20, 64, 2 << 20, 64, 3 << 20, 64, 0, None, 0, 0, None)[0] == T.TCM_ERR_INVALID_VALUE
+    assert T.tcm_tune(64, 64, 64, 1 << 20, 3, 2 << 20, 64, 3 << 20, 64, 0, None, 0, 5, None)[0] == T.TCM_ERR_INVALID_VALUE
+    assert T.tcm_tune(64, 64, 64, 1 << 20, 64, 2 << 20, 64, 3 << 20, 64, 0, None, 0, 5, None)[0] == T.TCM_ERR_HIP

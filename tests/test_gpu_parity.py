@@ -314,3 +314,34 @@ def test_torch_convenience_accumulate_and_16bit_out():
     Ch = T.gemm(A, B, out_dtype=torch.bfloat16)
     assert Ch.dtype == torch.bfloat16
     assert torch.allclose(Ch.float(), (A.float() @ B.float()), atol=0.05, rtol=2 ** -7)
+
+
+# ------------------------------------------------------------ auto-tuning
+
+@pytest.mark.parametrize("dtype", [S.F16, S.I8])
+def test_autotune_choice_is_used_and_correct(dtype):
+    """tcm_tune times the candidates, records the fastest; the next tcm_gemm on
+    the same signature launches exactly that plan and stays correct."""
+    from gpu_util import to_device
+    T.tcm_tune_clear()
+    try:
+        p = S.small_problem(dtype, 768, 512, 1024, seed=110, bias=True, relu=True)
+        g = S.generate(p)
+        say(f"[case] autotune {p.name}")
+        ka, pa = to_device(g["A"], dtype)
+        kb, pb = to_device(g["B"], dtype)
+        kbias = torch.from_numpy(g["bias"].copy()).cuda()
+        C = torch.empty((p.M, p.LDC), dtype=torch.int32 if dtype == S.I8 else torch.float32, device="cuda")
+        epi = T.TCM_EPI_BIAS | T.TCM_EPI_RELU
+        st, best = T.tcm_tune(p.M, p.N, p.K, pa, p.LDA, pb, p.LDB, C.data_ptr(), p.LDC, dtype, kbias.data_ptr(), epi, 3,
+                              torch.cuda.current_stream().cuda_stream)
+        assert st == T.TCM_OK and best["kernel"] == 1
+        table = T.tcm_tune_table().strip().splitlines()
+        assert len(table) == 1 and table[0].startswith(f"tcm-tune-1 1 {p.M} {p.N} {p.K} ")
+        say(f"       tuned: {table[0]}")
+        C2, plan = run_tcm(p, g)
+        assert f"config={best['config']} " in plan
+        assert ("mode=dp" if best["mode"] == 1 else "mode=streamk") in plan
+        check(p, g, C2)
+    finally:
+        T.tcm_tune_clear()
