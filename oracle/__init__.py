@@ -47,6 +47,8 @@ class Oracle:
         lib.oracle_gemm_entries.argtypes = [i64, i64, i64, vp, i64, ci, vp, i64, ci, ci, vp, ci, vp, i64, ci, vp, vp, i64,
                                             vp]
         lib.oracle_gemm_entries.restype = ci
+        lib.oracle_conv2d.argtypes = [i64] * 13 + [vp, vp, ci, vp, ci, vp]
+        lib.oracle_conv2d.restype = ci
         lib.oracle_decode.argtypes = [ci, vp, i64, vp]
         lib.oracle_decode.restype = ci
         lib.oracle_max_threads.restype = ci
@@ -129,6 +131,27 @@ class Oracle:
                                           cp, cld, ct, ii.ctypes.data, jj.ctypes.data, ii.size, out.ctypes.data)
         self._rc(rc)
         return out
+
+    def conv2d(self, x, f, dtype, pad=(0, 0), stride=(1, 1), dil=(1, 1), bias=None, relu=False):
+        """y (N, P, Q, K) of the NHWC input x (N, H, W, C) and KRSC filter f
+        (K, R, S, C), both storage arrays; float64 for float types, int32 for int8."""
+        x = self._buf(x, dtype)
+        f = self._buf(f, dtype)
+        if x.ndim != 4 or f.ndim != 4 or x.shape[3] != f.shape[3]:
+            raise OracleError("x must be (N, H, W, C) and f (K, R, S, C) with the same C")
+        N, H, W, C = x.shape
+        K, R, S, _ = f.shape
+        P = (H + 2 * pad[0] - dil[0] * (R - 1) - 1) // stride[0] + 1
+        Q = (W + 2 * pad[1] - dil[1] * (S - 1) - 1) // stride[1] + 1
+        bias = self._bias(bias, dtype)
+        if bias is not None and bias.size < K:
+            raise OracleError("bias shorter than K")
+        y = np.zeros((N, max(P, 0), max(Q, 0), K), dtype=np.int32 if dtype == I8 else np.float64)
+        rc = self.lib.oracle_conv2d(N, H, W, C, K, R, S, pad[0], pad[1], stride[0], stride[1], dil[0], dil[1],
+                                    x.ctypes.data, f.ctypes.data, dtype, None if bias is None else bias.ctypes.data,
+                                    int(relu), y.ctypes.data)
+        self._rc(rc)
+        return y
 
     def decode(self, dtype, X):
         X = self._buf(X, dtype)

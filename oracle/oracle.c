@@ -277,3 +277,65 @@ void oracle_set_threads(int n) {
     (void)n;
 #endif
 }
+
+/* ---- 2-D convolution -------------------------------------------------------
+ *
+ * The Conv2d + Bias + ReLU pattern (kimm240.github.io/tvm, post "Implement
+ * and enable Conv2d-Reshape-Add-ReLU fusion") written out directly, with the
+ * same exact decoders and wide accumulation as the product above:
+ *
+ *   y[n][p][q][k] = epi( bias[k] + sum_{r,s,c} x[n][h][w][c] * f[k][r][s][c] ),
+ *   h = p*stride_h - pad_h + r*dil_h,   w = q*stride_w - pad_w + s*dil_w,
+ *
+ * where taps with h or w outside the input contribute nothing (zero padding),
+ * and the sum runs over r (outer), s, c (inner) in ascending order after the
+ * bias.  x is NHWC, f is KRSC, y is NPQK (all dense, channels fastest), with
+ * P = (H + 2*pad_h - dil_h*(R-1) - 1) / stride_h + 1 and Q likewise.
+ * y is double for float types, int32 for int8 (range checked as above).
+ */
+int oracle_conv2d(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R, int64_t S,
+                  int64_t pad_h, int64_t pad_w, int64_t stride_h, int64_t stride_w, int64_t dil_h, int64_t dil_w,
+                  const void* x, const void* f, int dtype, const void* bias, int relu, void* y) {
+    if (N < 0 || H < 0 || W < 0 || C < 0 || K < 0 || R < 1 || S < 1) return 1;
+    if (pad_h < 0 || pad_w < 0 || stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1) return 1;
+    if (dtype < OR_F16 || dtype > OR_I8) return 1;
+    const int64_t eh = H + 2 * pad_h - dil_h * (R - 1) - 1, ew = W + 2 * pad_w - dil_w * (S - 1) - 1;
+    if (eh < 0 || ew < 0) return 1;
+    const int64_t P = eh / stride_h + 1, Q = ew / stride_w + 1;
+    int overflow = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1) reduction(| : overflow)
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t p = 0; p < P; ++p)
+            for (int64_t q = 0; q < Q; ++q)
+                for (int64_t k = 0; k < K; ++k) {
+                    const int64_t out = ((n * P + p) * Q + q) * K + k;
+                    if (dtype == OR_I8) {
+                        const int8_t* x8 = (const int8_t*)x;
+                        const int8_t* f8 = (const int8_t*)f;
+                        int64_t acc = bias ? ((const int32_t*)bias)[k] : 0;
+                        for (int64_t r = 0; r < R; ++r)
+                            for (int64_t s = 0; s < S; ++s) {
+                                const int64_t h = p * stride_h - pad_h + r * dil_h, w = q * stride_w - pad_w + s * dil_w;
+                                if (h < 0 || h >= H || w < 0 || w >= W) continue;
+                                for (int64_t c = 0; c < C; ++c) {
+                                    acc += (int64_t)x8[((n * H + h) * W + w) * C + c] * (int64_t)f8[((k * R + r) * S + s) * C + c];
+                                    if (acc > INT32_MAX || acc < INT32_MIN) overflow = 1;
+                                }
+                            }
+                        if (relu && !(acc > 0)) acc = 0;
+                        ((int32_t*)y)[out] = (int32_t)acc;
+                    } else {
+                        double acc = bias ? (double)((const float*)bias)[k] : 0.0;
+                        for (int64_t r = 0; r < R; ++r)
+                            for (int64_t s = 0; s < S; ++s) {
+                                const int64_t h = p * stride_h - pad_h + r * dil_h, w = q * stride_w - pad_w + s * dil_w;
+                                if (h < 0 || h >= H || w < 0 || w >= W) continue;
+                                for (int64_t c = 0; c < C; ++c)
+                                    acc += elem_f(x, dtype, ((n * H + h) * W + w) * C + c) *
+                                           elem_f(f, dtype, ((k * R + r) * S + s) * C + c);
+                            }
+                        ((double*)y)[out] = relu ? relu_f(acc) : acc;
+                    }
+                }
+    return overflow ? 2 : 0;
+}

@@ -401,7 +401,75 @@ def pin_init_tensor_entries(o):
             assert np.array_equal(E.reshape(M, N), C), f"entries != full with c_in (dtype {dtype}, {ct})"
 
 
+# ---------------------------------------------------------------- convolution
+
+CONV_CASES = [  # (N, H, W, C, K, R, S, pad, stride, dil)
+    (2, 7, 6, 3, 4, 3, 3, (1, 1), (1, 1), (1, 1)),
+    (1, 9, 8, 2, 3, 3, 2, (0, 1), (2, 1), (1, 1)),
+    (1, 10, 9, 2, 2, 3, 3, (2, 2), (1, 2), (2, 1)),
+    (3, 5, 5, 4, 5, 1, 1, (0, 0), (1, 1), (1, 1)),
+    (1, 11, 11, 1, 2, 5, 5, (2, 2), (3, 3), (1, 2)),
+]
+
+
+def _conv_torch(x_log, f_log, pad, stride, dil, bias, relu):
+    """torch's CPU conv2d in float64 on logical NHWC / KRSC values (exact for small integers)."""
+    import torch.nn.functional as Fn
+    xt = torch.from_numpy(np.ascontiguousarray(x_log.transpose(0, 3, 1, 2)))
+    ft = torch.from_numpy(np.ascontiguousarray(f_log.transpose(0, 3, 1, 2)))
+    bt = None if bias is None else torch.from_numpy(np.asarray(bias, dtype=np.float64))
+    y = Fn.conv2d(xt, ft, bias=bt, stride=stride, padding=pad, dilation=dil).numpy().transpose(0, 2, 3, 1)
+    return np.maximum(y, 0) if relu else y
+
+
+def pin_conv_vs_torch(o):
+    """The convolution equals torch's CPU conv2d (float64) on small-integer inputs,
+    every type, with padding, stride, dilation, bias and ReLU."""
+    rng = np.random.default_rng(31)
+    for case in CONV_CASES:
+        N, H, W, C, K, R, S, pad, stride, dil = case
+        for dtype in ALL:
+            lo, hi = (-128, 128) if dtype == I8 else (-8, 9)
+            x_log = rng.integers(lo, hi, size=(N, H, W, C)).astype(np.float64)
+            f_log = rng.integers(lo, hi, size=(K, R, S, C)).astype(np.float64)
+            bias = rng.integers(-50, 50, size=K)
+            b_st = bias.astype(np.int32 if dtype == I8 else np.float32)
+            y = o.conv2d(to_storage(x_log, dtype).reshape(x_log.shape), to_storage(f_log, dtype).reshape(f_log.shape),
+                         dtype, pad=pad, stride=stride, dil=dil, bias=b_st, relu=True)
+            want = _conv_torch(x_log, f_log, pad, stride, dil, bias, True)
+            assert y.shape == want.shape, f"conv output shape {y.shape} vs {want.shape} for {case}"
+            assert np.array_equal(y.astype(np.float64), want), f"conv != torch conv2d (dtype {dtype}, {case})"
+
+
+def pin_conv_closed_form_padding(o):
+    """All-ones input and filter: each output is C times the number of taps that
+    land inside the input, counted here independently per row and column."""
+    N, H, W, C, K, R, S = 1, 6, 5, 3, 2, 3, 3
+    pad, stride, dil = (1, 2), (2, 1), (1, 2)
+    for dtype in ALL:
+        x = to_storage(np.ones(N * H * W * C), dtype).reshape(N, H, W, C)
+        f = to_storage(np.ones(K * R * S * C), dtype).reshape(K, R, S, C)
+        y = o.conv2d(x, f, dtype, pad=pad, stride=stride, dil=dil)
+        P, Q = y.shape[1], y.shape[2]
+        for p in range(P):
+            rows = sum(0 <= p * stride[0] - pad[0] + r * dil[0] < H for r in range(R))
+            for q in range(Q):
+                cols = sum(0 <= q * stride[1] - pad[1] + s * dil[1] < W for s in range(S))
+                assert np.all(y[0, p, q, :] == rows * cols * C), (dtype, p, q)
+
+
+def pin_conv_1x1_is_the_product(o):
+    """A 1x1, stride-1, unpadded convolution is the (N*H*W x C) . (C x K) product."""
+    rng = np.random.default_rng(33)
+    for dtype in ALL:
+        x_log = random_logical(rng, (2, 3, 4, 5), dtype)
+        f_log = random_logical(rng, (6, 1, 1, 5), dtype)
+        y = o.conv2d(to_storage(x_log, dtype).reshape(x_log.shape), to_storage(f_log, dtype).reshape(f_log.shape), dtype)
+        C = run(o, x_log.reshape(24, 5), f_log.reshape(6, 5).T, dtype)
+        assert np.array_equal(y.reshape(24, 6), C)
+
+
 ALL_PINS = [pin_decoders, pin_identity, pin_closed_forms, pin_printed_value, pin_bruteforce_exact,
             pin_library_matmul, pin_transpose, pin_linearity_int, pin_entries_match_full,
             pin_int32_range, pin_degenerate, pin_init_tensor_closed_forms, pin_init_tensor_linearity,
-            pin_init_tensor_entries]
+            pin_init_tensor_entries, pin_conv_vs_torch, pin_conv_closed_form_padding, pin_conv_1x1_is_the_product]
