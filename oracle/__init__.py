@@ -48,6 +48,8 @@ class Oracle:
                                             vp]
         lib.oracle_gemm_entries.restype = ci
         lib.oracle_conv2d.argtypes = [i64] * 13 + [vp, vp, ci, vp, ci, vp]
+        lib.oracle_conv2d_entries.argtypes = [i64] * 13 + [vp, vp, ci, vp, ci, vp, vp, i64, vp]
+        lib.oracle_conv2d_entries.restype = ci
         lib.oracle_conv2d.restype = ci
         lib.oracle_decode.argtypes = [ci, vp, i64, vp]
         lib.oracle_decode.restype = ci
@@ -152,6 +154,30 @@ class Oracle:
                                     int(relu), y.ctypes.data)
         self._rc(rc)
         return y
+
+    def conv2d_entries(self, x, f, dtype, mm, kk, pad=(0, 0), stride=(1, 1), dil=(1, 1), bias=None, relu=False):
+        """Outputs of conv2d() at output pixel mm[t] (row of y seen as an
+        (N*P*Q, K) matrix) and channel kk[t], same arithmetic as conv2d()."""
+        x = self._buf(x, dtype)
+        f = self._buf(f, dtype)
+        if x.ndim != 4 or f.ndim != 4 or x.shape[3] != f.shape[3]:
+            raise OracleError("x must be (N, H, W, C) and f (K, R, S, C) with the same C")
+        N, H, W, C = x.shape
+        K, R, S, _ = f.shape
+        bias = self._bias(bias, dtype)
+        if bias is not None and bias.size < K:
+            raise OracleError("bias shorter than K")
+        mm = np.ascontiguousarray(mm, dtype=np.int64)
+        kk = np.ascontiguousarray(kk, dtype=np.int64)
+        if mm.shape != kk.shape:
+            raise OracleError("index arrays differ in length")
+        out = np.zeros(mm.size, dtype=np.int32 if dtype == I8 else np.float64)
+        rc = self.lib.oracle_conv2d_entries(N, H, W, C, K, R, S, pad[0], pad[1], stride[0], stride[1], dil[0], dil[1],
+                                            x.ctypes.data, f.ctypes.data, dtype,
+                                            None if bias is None else bias.ctypes.data, int(relu), mm.ctypes.data,
+                                            kk.ctypes.data, mm.size, out.ctypes.data)
+        self._rc(rc)
+        return out
 
     def decode(self, dtype, X):
         X = self._buf(X, dtype)

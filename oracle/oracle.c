@@ -293,49 +293,89 @@ void oracle_set_threads(int n) {
  * P = (H + 2*pad_h - dil_h*(R-1) - 1) / stride_h + 1 and Q likewise.
  * y is double for float types, int32 for int8 (range checked as above).
  */
-int oracle_conv2d(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R, int64_t S,
-                  int64_t pad_h, int64_t pad_w, int64_t stride_h, int64_t stride_w, int64_t dil_h, int64_t dil_w,
-                  const void* x, const void* f, int dtype, const void* bias, int relu, void* y) {
+typedef struct {
+    int64_t N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w, P, Q;
+} conv_geom;
+
+/* The geometry of a call, or 1 for invalid arguments. */
+static int conv_setup(conv_geom* g, int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R, int64_t S,
+                      int64_t pad_h, int64_t pad_w, int64_t stride_h, int64_t stride_w, int64_t dil_h, int64_t dil_w,
+                      int dtype) {
     if (N < 0 || H < 0 || W < 0 || C < 0 || K < 0 || R < 1 || S < 1) return 1;
     if (pad_h < 0 || pad_w < 0 || stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1) return 1;
     if (dtype < OR_F16 || dtype > OR_I8) return 1;
     const int64_t eh = H + 2 * pad_h - dil_h * (R - 1) - 1, ew = W + 2 * pad_w - dil_w * (S - 1) - 1;
     if (eh < 0 || ew < 0) return 1;
-    const int64_t P = eh / stride_h + 1, Q = ew / stride_w + 1;
+    conv_geom c = {N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w, eh / stride_h + 1, ew / stride_w + 1};
+    *g = c;
+    return 0;
+}
+
+/* One output y[n][p][q][k]: int8 into *yi (setting *overflow when a partial
+ * sum leaves the int32 range), float types into *yf. */
+static void conv_point(const conv_geom* g, const void* x, const void* f, int dtype, const void* bias, int relu,
+                       int64_t n, int64_t p, int64_t q, int64_t k, double* yf, int32_t* yi, int* overflow) {
+    const int64_t H = g->H, W = g->W, C = g->C, R = g->R, S = g->S;
+    if (dtype == OR_I8) {
+        const int8_t* x8 = (const int8_t*)x;
+        const int8_t* f8 = (const int8_t*)f;
+        int64_t acc = bias ? ((const int32_t*)bias)[k] : 0;
+        for (int64_t r = 0; r < R; ++r)
+            for (int64_t s = 0; s < S; ++s) {
+                const int64_t h = p * g->stride_h - g->pad_h + r * g->dil_h, w = q * g->stride_w - g->pad_w + s * g->dil_w;
+                if (h < 0 || h >= H || w < 0 || w >= W) continue;
+                for (int64_t c = 0; c < C; ++c) {
+                    acc += (int64_t)x8[((n * H + h) * W + w) * C + c] * (int64_t)f8[((k * R + r) * S + s) * C + c];
+                    if (acc > INT32_MAX || acc < INT32_MIN) *overflow = 1;
+                }
+            }
+        if (relu && !(acc > 0)) acc = 0;
+        *yi = (int32_t)acc;
+        return;
+    }
+    double acc = bias ? (double)((const float*)bias)[k] : 0.0;
+    for (int64_t r = 0; r < R; ++r)
+        for (int64_t s = 0; s < S; ++s) {
+            const int64_t h = p * g->stride_h - g->pad_h + r * g->dil_h, w = q * g->stride_w - g->pad_w + s * g->dil_w;
+            if (h < 0 || h >= H || w < 0 || w >= W) continue;
+            for (int64_t c = 0; c < C; ++c)
+                acc += elem_f(x, dtype, ((n * H + h) * W + w) * C + c) * elem_f(f, dtype, ((k * R + r) * S + s) * C + c);
+        }
+    *yf = relu ? relu_f(acc) : acc;
+}
+
+int oracle_conv2d(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R, int64_t S,
+                  int64_t pad_h, int64_t pad_w, int64_t stride_h, int64_t stride_w, int64_t dil_h, int64_t dil_w,
+                  const void* x, const void* f, int dtype, const void* bias, int relu, void* y) {
+    conv_geom g;
+    if (conv_setup(&g, N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w, dtype)) return 1;
     int overflow = 0;
 #pragma omp parallel for collapse(2) schedule(dynamic, 1) reduction(| : overflow)
     for (int64_t n = 0; n < N; ++n)
-        for (int64_t p = 0; p < P; ++p)
-            for (int64_t q = 0; q < Q; ++q)
+        for (int64_t p = 0; p < g.P; ++p)
+            for (int64_t q = 0; q < g.Q; ++q)
                 for (int64_t k = 0; k < K; ++k) {
-                    const int64_t out = ((n * P + p) * Q + q) * K + k;
-                    if (dtype == OR_I8) {
-                        const int8_t* x8 = (const int8_t*)x;
-                        const int8_t* f8 = (const int8_t*)f;
-                        int64_t acc = bias ? ((const int32_t*)bias)[k] : 0;
-                        for (int64_t r = 0; r < R; ++r)
-                            for (int64_t s = 0; s < S; ++s) {
-                                const int64_t h = p * stride_h - pad_h + r * dil_h, w = q * stride_w - pad_w + s * dil_w;
-                                if (h < 0 || h >= H || w < 0 || w >= W) continue;
-                                for (int64_t c = 0; c < C; ++c) {
-                                    acc += (int64_t)x8[((n * H + h) * W + w) * C + c] * (int64_t)f8[((k * R + r) * S + s) * C + c];
-                                    if (acc > INT32_MAX || acc < INT32_MIN) overflow = 1;
-                                }
-                            }
-                        if (relu && !(acc > 0)) acc = 0;
-                        ((int32_t*)y)[out] = (int32_t)acc;
-                    } else {
-                        double acc = bias ? (double)((const float*)bias)[k] : 0.0;
-                        for (int64_t r = 0; r < R; ++r)
-                            for (int64_t s = 0; s < S; ++s) {
-                                const int64_t h = p * stride_h - pad_h + r * dil_h, w = q * stride_w - pad_w + s * dil_w;
-                                if (h < 0 || h >= H || w < 0 || w >= W) continue;
-                                for (int64_t c = 0; c < C; ++c)
-                                    acc += elem_f(x, dtype, ((n * H + h) * W + w) * C + c) *
-                                           elem_f(f, dtype, ((k * R + r) * S + s) * C + c);
-                            }
-                        ((double*)y)[out] = relu ? relu_f(acc) : acc;
-                    }
+                    const int64_t out = ((n * g.P + p) * g.Q + q) * K + k;
+                    conv_point(&g, x, f, dtype, bias, relu, n, p, q, k, (double*)y + out, (int32_t*)y + out, &overflow);
                 }
+    return overflow ? 2 : 0;
+}
+
+/* The same outputs at listed positions only: output t is pixel mm[t] (the
+ * row (n*P + p)*Q + q of y seen as an N*P*Q x K matrix) and channel kk[t]. */
+int oracle_conv2d_entries(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R, int64_t S,
+                          int64_t pad_h, int64_t pad_w, int64_t stride_h, int64_t stride_w, int64_t dil_h, int64_t dil_w,
+                          const void* x, const void* f, int dtype, const void* bias, int relu,
+                          const int64_t* mm, const int64_t* kk, int64_t n_out, void* out) {
+    conv_geom g;
+    if (conv_setup(&g, N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w, dtype) || n_out < 0) return 1;
+    for (int64_t t = 0; t < n_out; ++t)
+        if (mm[t] < 0 || mm[t] >= N * g.P * g.Q || kk[t] < 0 || kk[t] >= K) return 1;
+    int overflow = 0;
+#pragma omp parallel for schedule(dynamic, 16) reduction(| : overflow)
+    for (int64_t t = 0; t < n_out; ++t) {
+        const int64_t n = mm[t] / (g.P * g.Q), p = mm[t] / g.Q % g.P, q = mm[t] % g.Q;
+        conv_point(&g, x, f, dtype, bias, relu, n, p, q, kk[t], (double*)out + t, (int32_t*)out + t, &overflow);
+    }
     return overflow ? 2 : 0;
 }

@@ -469,7 +469,30 @@ def pin_conv_1x1_is_the_product(o):
         assert np.array_equal(y.reshape(24, 6), C)
 
 
+def pin_conv_entries_vs_torch(o):
+    """Sampled convolution outputs equal torch's conv2d at the same (pixel, channel)
+    positions, every type, with padding, stride and dilation; positions repeat."""
+    rng = np.random.default_rng(35)
+    for case in CONV_CASES:
+        N, H, W, C, K, R, S, pad, stride, dil = case
+        for dtype in ALL:
+            lo, hi = (-128, 128) if dtype == I8 else (-8, 9)
+            x_log = rng.integers(lo, hi, size=(N, H, W, C)).astype(np.float64)
+            f_log = rng.integers(lo, hi, size=(K, R, S, C)).astype(np.float64)
+            bias = rng.integers(-50, 50, size=K)
+            want = _conv_torch(x_log, f_log, pad, stride, dil, bias, True)
+            Mp = want.shape[0] * want.shape[1] * want.shape[2]
+            mm = rng.integers(0, Mp, size=40)
+            kk = rng.integers(0, K, size=40)
+            got = o.conv2d_entries(to_storage(x_log, dtype).reshape(x_log.shape),
+                                   to_storage(f_log, dtype).reshape(f_log.shape), dtype, mm, kk, pad=pad,
+                                   stride=stride, dil=dil, bias=bias.astype(np.int32 if dtype == I8 else np.float32),
+                                   relu=True)
+            assert np.array_equal(got.astype(np.float64), want.reshape(Mp, K)[mm, kk]), (dtype, case)
+
+
 ALL_PINS = [pin_decoders, pin_identity, pin_closed_forms, pin_printed_value, pin_bruteforce_exact,
             pin_library_matmul, pin_transpose, pin_linearity_int, pin_entries_match_full,
             pin_int32_range, pin_degenerate, pin_init_tensor_closed_forms, pin_init_tensor_linearity,
-            pin_init_tensor_entries, pin_conv_vs_torch, pin_conv_closed_form_padding, pin_conv_1x1_is_the_product]
+            pin_init_tensor_entries, pin_conv_vs_torch, pin_conv_closed_form_padding, pin_conv_1x1_is_the_product,
+            pin_conv_entries_vs_torch]

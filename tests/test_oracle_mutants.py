@@ -30,18 +30,19 @@ MUTANTS = [
     ("cin_ignores_ld", "acc[j] = init_f(cin, ldcin, cin_type, bf, i, j);", "acc[j] = init_f(cin, N, cin_type, bf, i, j);"),
     ("cin_wrong_type", "elem_f(cin, cin_type,", "elem_f(cin, OR_F16,"),
     ("cin_negated_int", "int64_t v = cin ? (int64_t)cin[i * ldcin + j] : 0;", "int64_t v = cin ? -(int64_t)cin[i * ldcin + j] : 0;"),
-    ("conv_pad_sign", "const int64_t h = p * stride_h - pad_h + r * dil_h, w = q * stride_w - pad_w + s * dil_w;\n                                if (h < 0 || h >= H || w < 0 || w >= W) continue;\n                                for (int64_t c = 0; c < C; ++c)\n",
-     "const int64_t h = p * stride_h + pad_h + r * dil_h, w = q * stride_w - pad_w + s * dil_w;\n                                if (h < 0 || h >= H || w < 0 || w >= W) continue;\n                                for (int64_t c = 0; c < C; ++c)\n"),
-    ("conv_stride_ignored", "const int64_t h = p * stride_h - pad_h + r * dil_h, w = q * stride_w - pad_w + s * dil_w;\n                                if (h < 0 || h >= H || w < 0 || w >= W) continue;\n                                for (int64_t c = 0; c < C; ++c)\n",
-     "const int64_t h = p - pad_h + r * dil_h, w = q * stride_w - pad_w + s * dil_w;\n                                if (h < 0 || h >= H || w < 0 || w >= W) continue;\n                                for (int64_t c = 0; c < C; ++c)\n"),
-    ("conv_dilation_ignored", "w = q * stride_w - pad_w + s * dil_w;\n                                if (h < 0 || h >= H || w < 0 || w >= W) continue;\n                                for (int64_t c = 0; c < C; ++c)\n",
-     "w = q * stride_w - pad_w + s;\n                                if (h < 0 || h >= H || w < 0 || w >= W) continue;\n                                for (int64_t c = 0; c < C; ++c)\n"),
+    ("conv_pad_sign", "const int64_t h = p * g->stride_h - g->pad_h + r * g->dil_h, w = q * g->stride_w - g->pad_w + s * g->dil_w;\n            if (h < 0",
+     "const int64_t h = p * g->stride_h + g->pad_h + r * g->dil_h, w = q * g->stride_w - g->pad_w + s * g->dil_w;\n            if (h < 0"),
+    ("conv_stride_ignored", "const int64_t h = p * g->stride_h - g->pad_h + r * g->dil_h, w = q * g->stride_w - g->pad_w + s * g->dil_w;\n            if (h < 0",
+     "const int64_t h = p - g->pad_h + r * g->dil_h, w = q * g->stride_w - g->pad_w + s * g->dil_w;\n            if (h < 0"),
+    ("conv_dilation_ignored", "const int64_t h = p * g->stride_h - g->pad_h + r * g->dil_h, w = q * g->stride_w - g->pad_w + s * g->dil_w;\n            if (h < 0",
+     "const int64_t h = p * g->stride_h - g->pad_h + r * g->dil_h, w = q * g->stride_w - g->pad_w + s;\n            if (h < 0"),
     ("conv_filter_rs_swapped", "elem_f(f, dtype, ((k * R + r) * S + s) * C + c)", "elem_f(f, dtype, ((k * S + s) * R + r) * C + c)"),
-    ("conv_edge_off_by_one", "if (h < 0 || h >= H || w < 0 || w >= W) continue;\n                                for (int64_t c = 0; c < C; ++c)\n                                    acc += elem_f",
-     "if (h < 0 || h > H || w < 0 || w >= W) continue;\n                                for (int64_t c = 0; c < C; ++c)\n                                    acc += elem_f"),
+    ("conv_edge_off_by_one", "if (h < 0 || h >= H || w < 0 || w >= W) continue;\n            for (int64_t c = 0; c < C; ++c)\n                acc += elem_f",
+     "if (h < 0 || h > H || w < 0 || w >= W) continue;\n            for (int64_t c = 0; c < C; ++c)\n                acc += elem_f"),
     ("conv_bias_dropped_int", "int64_t acc = bias ? ((const int32_t*)bias)[k] : 0;", "int64_t acc = 0;"),
-    ("conv_relu_missing_float", "((double*)y)[out] = relu ? relu_f(acc) : acc;", "((double*)y)[out] = acc;"),
+    ("conv_relu_missing_float", "*yf = relu ? relu_f(acc) : acc;", "*yf = acc;"),
     ("conv_int8_channel_offset", "(int64_t)x8[((n * H + h) * W + w) * C + c]", "(int64_t)x8[((n * H + h) * W + w) * C + c / 2]"),
+    ("conv_entries_pixel_order", "p = mm[t] / g.Q % g.P, q = mm[t] % g.Q;", "p = mm[t] % g.P, q = mm[t] / g.P % g.Q;"),
     ("cin_overflow_unchecked", "            if (acc > INT32_MAX || acc < INT32_MIN) overflow = 1;\n            for (int64_t k = 0; k < K; ++k) {",
      "            for (int64_t k = 0; k < K; ++k) {"),
     ("relu_abs", "return x > 0.0 ? x : 0.0;", "return x > 0.0 ? x : -x;"),
