@@ -146,6 +146,47 @@ int tcm_gemm_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
                      int dtype, const void* bias, int64_t stride_bias, int epilogue,
                      void* stream);
 
+/*
+ * tcm_conv2d -- 2-D convolution with the fused bias + ReLU epilogue (the
+ * Conv2d + bias + ReLU pattern of kimm240.github.io/tvm, post "Implement and
+ * enable Conv2d-Reshape-Add-ReLU fusion"), computed as an implicit GEMM on
+ * the same matrix-core main loop and epilogue as tcm_gemm:
+ *
+ *     y[n,p,q,k] = epi( bias[k] + sum_{r,s,c} x[n,h,w,c] * f[k,r,s,c] ),
+ *     h = p*stride_h - pad_h + r*dil_h,   w = q*stride_w - pad_w + s*dil_w,
+ *
+ * taps with h or w outside the input add nothing (zero padding).  As a GEMM:
+ * M = N*P*Q output pixels, N = K output channels, K = R*S*C; A is the im2col
+ * view of x (never built in memory: the kernel gathers it tap by tap), B is
+ * the filter with k contiguous, C is y row-major with ldc = K.
+ *
+ *   N, H, W, C   batch, input height, width, channels; >= 0, < 2^31.
+ *   K, R, S      output channels, filter height, width; K >= 0, R, S >= 1.
+ *   pad_*        zero padding on both sides, >= 0.  stride_*, dil_* >= 1.
+ *                P = (H + 2*pad_h - dil_h*(R-1) - 1) / stride_h + 1, Q likewise;
+ *                a dilated filter larger than the padded input is an error.
+ *   x            device, NHWC dense (channels fastest), N*H*W*C elements.
+ *   f            device, KRSC dense, K*R*S*C elements.
+ *   y            device, NPQK dense, N*P*Q*K elements of C's type; written
+ *                only; must not overlap x, f or bias.
+ *   dtype        TCM_F16 / TCM_BF16 / TCM_F32 / TCM_I8, optionally with
+ *                TCM_C_F16 or TCM_C_BF16 (float inputs) for a 16-bit y.  The
+ *                layout flags are errors: the layouts above are fixed.
+ *   bias, epilogue  as tcm_gemm, except that TCM_EPI_ACCUM is an error.
+ *   stream       hipStream_t or NULL.
+ * The tiled kernel takes C a multiple of the K-step (64 for f16/bf16, 32
+ * for f32, 128 for int8), 16-byte aligned pointers and inputs below 1 GiB;
+ * any other valid call runs on the generic kernel with the same result.
+ * Accumulation is f32 (int32 for int8, exact).  Returns as tcm_gemm;
+ * TCM_OK with nothing launched when N*P*Q or K is 0.  Allocates only the
+ * shared Stream-K workspace, as tcm_gemm.
+ */
+int tcm_conv2d(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R, int64_t S,
+               int64_t pad_h, int64_t pad_w, int64_t stride_h, int64_t stride_w,
+               int64_t dil_h, int64_t dil_w,
+               const void* x, const void* f, void* y,
+               int dtype, const void* bias, int epilogue, void* stream);
+
 /* Text of a status code (static storage; never NULL). */
 const char* tcm_status_string(int status);
 

@@ -27,6 +27,13 @@ Recipe (one numpy PCG64 generator per problem, ``np.random.default_rng(seed)``):
 The sampled-entry list of a large problem comes from a second generator,
 ``default_rng(1000 + seed)``: 4096 rows then 4096 columns (duplicates kept),
 followed by every entry of rows 0 and M - 1.
+
+Convolutions (ConvProblem): one ``default_rng(seed)`` draws x as its
+(N, H, W, C) storage array, then f as (K, R, S, C), then the bias (K,), with
+the same distributions and roundings as the GEMM operands; their sampled
+outputs come from ``default_rng(1000 + seed)`` as above, over the
+N*P*Q x K output matrix (4096 pixels then 4096 channels, then every channel
+of the first and last pixel).
 """
 from dataclasses import dataclass, replace
 
@@ -231,3 +238,105 @@ def entry_inputs(p: Problem, g, e):
     return {"A": g["A"][e], "B": g["B"][0 if p.b_shared else e],
             "bias": None if g["bias"] is None else g["bias"][e],
             "C_in": None if g["C_in"] is None else g["C_in"][e]}
+
+
+@dataclass(frozen=True)
+class ConvProblem:
+    """A 2-D convolution: NHWC input x, KRSC filter f, NPQK output y."""
+    name: str
+    dtype: int
+    N: int
+    H: int
+    W: int
+    C: int
+    K: int
+    R: int
+    S: int
+    pad: tuple = (0, 0)
+    stride: tuple = (1, 1)
+    dil: tuple = (1, 1)
+    dist: str = "uniform"
+    seed: int = 0
+    bias: bool = False
+    relu: bool = False
+    c_type: str = "acc"
+
+    @property
+    def P(self):
+        return (self.H + 2 * self.pad[0] - self.dil[0] * (self.R - 1) - 1) // self.stride[0] + 1
+
+    @property
+    def Q(self):
+        return (self.W + 2 * self.pad[1] - self.dil[1] * (self.S - 1) - 1) // self.stride[1] + 1
+
+    def gemm(self):
+        """The implicit GEMM it is: M = N*P*Q pixels, N = K channels, K = R*S*C taps."""
+        return Problem(self.name, self.dtype, self.N * self.P * self.Q, self.K, self.R * self.S * self.C, b_col=True,
+                       dist=self.dist, seed=self.seed, bias=self.bias, relu=self.relu, c_type=self.c_type)
+
+    @property
+    def flops(self):
+        return 2 * self.N * self.P * self.Q * self.K * self.R * self.S * self.C
+
+    def alg_bytes(self):
+        """Unique bytes: x and f read once, y written once (+ the bias)."""
+        es = {F16: 2, BF16: 2, F32: 4, I8: 1}[self.dtype]
+        b = (self.N * self.H * self.W * self.C + self.K * self.R * self.S * self.C) * es
+        b += self.N * self.P * self.Q * self.K * self.gemm().c_bytes
+        if self.bias:
+            b += self.K * 4
+        return b
+
+
+def generate_conv(p: ConvProblem):
+    """Storage arrays {'x', 'f', 'bias'} of convolution p (bias None when unused)."""
+    rng = np.random.default_rng(p.seed)
+    x = _draw(rng, (p.N, p.H, p.W, p.C), p.dist, p.dtype)
+    f = _draw(rng, (p.K, p.R, p.S, p.C), p.dist, p.dtype)
+    bias = None
+    if p.bias:
+        if p.dtype == I8:
+            bias = rng.integers(-2 ** 20, 2 ** 20, size=(p.K,), endpoint=True, dtype=np.int64).astype(np.int32)
+        else:
+            bias = rng.uniform(-1.0, 1.0, size=(p.K,)).astype(np.float32)
+    return {"x": x, "f": f, "bias": bias}
+
+
+def sample_conv_entries(p: ConvProblem, n=4096):
+    """(mm, kk) int64 arrays over the N*P*Q x K output: n seeded random
+    positions plus every channel of the first and last pixel."""
+    rng = np.random.default_rng(1000 + p.seed)
+    M = p.N * p.P * p.Q
+    mm = rng.integers(0, M, size=n, dtype=np.int64)
+    kk = rng.integers(0, p.K, size=n, dtype=np.int64)
+    ch = np.arange(p.K, dtype=np.int64)
+    mm = np.concatenate([mm, np.zeros(p.K, dtype=np.int64), np.full(p.K, M - 1, dtype=np.int64)])
+    return mm, np.concatenate([kk, ch, ch])
+
+
+def small_conv(dtype, N, H, W, C, K, R, S, pad=(0, 0), stride=(1, 1), dil=(1, 1), seed=0, bias=False, relu=False,
+               c_type="acc", dist=None):
+    """An ad-hoc convolution for parity cases."""
+    if dist is None:
+        dist = "int" if dtype == I8 else "uniform"
+    return ConvProblem(f"conv_{DTYPE_NAMES[dtype]}_{N}x{H}x{W}x{C}_k{K}r{R}s{S}", dtype, N, H, W, C, K, R, S,
+                       pad=tuple(pad), stride=tuple(stride), dil=tuple(dil), dist=dist, seed=seed, bias=bias,
+                       relu=relu, c_type=c_type)
+
+
+def _conv_workloads():
+    """3x3 convolutions with the shapes of a residual network's middle stages
+    (channels-last, batch 128), bias + ReLU fused."""
+    w = {}
+    w["conv_f16_28x28_c128"] = ConvProblem("conv_f16_28x28_c128", F16, 128, 28, 28, 128, 128, 3, 3, pad=(1, 1),
+                                           dist="normal", seed=11, bias=True, relu=True)
+    w["conv_f16_14x14_c256"] = ConvProblem("conv_f16_14x14_c256", F16, 128, 14, 14, 256, 256, 3, 3, pad=(1, 1),
+                                           dist="normal", seed=12, bias=True, relu=True)
+    w["conv_f16_56x56_s2_c128"] = ConvProblem("conv_f16_56x56_s2_c128", F16, 128, 56, 56, 128, 128, 3, 3, pad=(1, 1),
+                                              stride=(2, 2), dist="normal", seed=13, bias=True, relu=True)
+    w["conv_i8_14x14_c256"] = ConvProblem("conv_i8_14x14_c256", I8, 128, 14, 14, 256, 256, 3, 3, pad=(1, 1),
+                                          dist="int", seed=14, bias=True, relu=True)
+    return w
+
+
+CONV_WORKLOADS = _conv_workloads()

@@ -52,6 +52,8 @@ def lib():
         L.tcm_gemm.restype = ci
         L.tcm_gemm_batched.argtypes = [i64, i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64, ci, vp, i64, ci, vp]
         L.tcm_gemm_batched.restype = ci
+        L.tcm_conv2d.argtypes = [i64] * 13 + [vp, vp, vp, ci, vp, ci, vp]
+        L.tcm_conv2d.restype = ci
         L.tcm_status_string.argtypes = [ci]
         L.tcm_status_string.restype = ctypes.c_char_p
         L.tcm_set_option.argtypes = [ctypes.c_char_p, i64]
@@ -183,6 +185,14 @@ def tcm_release_workspace():
     lib().tcm_release_workspace()
 
 
+def tcm_conv2d(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w, x, f, y, dtype, bias, epilogue,
+               stream):
+    """y = epi(bias + conv2d(x, f)) for NHWC x, KRSC f, NPQK y (device
+    addresses as ints).  Returns the tcm status code."""
+    return lib().tcm_conv2d(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w, x, f, y, dtype, bias,
+                            epilogue, stream)
+
+
 def tcm_version():
     return lib().tcm_version().decode()
 
@@ -304,3 +314,42 @@ def gemm_batched(A, B, C=None, bias=None, relu=False, accumulate=False, out_dtyp
     if st != TCM_OK:
         raise TcmError(st, "tcm_gemm_batched")
     return C
+
+
+def conv2d(x, f, bias=None, relu=False, padding=0, stride=1, dilation=1, out_dtype=None, stream=None):
+    """y = relu?(conv2d(x, f) + bias) on the GPU via tcm_conv2d.
+
+    x: (N, H, W, C) and f: (K, R, S, C) contiguous CUDA tensors of one type
+    (float16, bfloat16, float32 or int8), channels last.  padding, stride,
+    dilation: an int or an (h, w) pair.  bias: optional length-K vector of
+    the accumulator type.  Returns y (N, P, Q, K) of the accumulator type
+    (float32, int32 for int8) or `out_dtype` float16 / bfloat16."""
+    import torch
+    if x.dim() != 4 or f.dim() != 4 or x.shape[3] != f.shape[3]:
+        raise ValueError("x must be (N, H, W, C) and f (K, R, S, C) with the same C")
+    if x.dtype != f.dtype:
+        raise TypeError("x and f must have the same dtype")
+    if not (x.is_contiguous() and f.is_contiguous()):
+        raise ValueError("x and f must be contiguous (channels last)")
+    pair = lambda v: (v, v) if isinstance(v, int) else tuple(v)
+    (ph, pw), (sh, sw), (dh, dw) = pair(padding), pair(stride), pair(dilation)
+    code = _torch_dtype_code(x)
+    N, H, W, C = x.shape
+    K, R, S, _ = f.shape
+    P = (H + 2 * ph - dh * (R - 1) - 1) // sh + 1
+    Q = (W + 2 * pw - dw * (S - 1) - 1) // sw + 1
+    acc_dtype = torch.int32 if code == TCM_I8_I32 else torch.float32
+    y = torch.empty((N, max(P, 0), max(Q, 0), K), dtype=out_dtype or acc_dtype, device=x.device)
+    c_flags = {torch.float16: TCM_C_F16, torch.bfloat16: TCM_C_BF16}.get(y.dtype, 0)
+    if c_flags and code == TCM_I8_I32:
+        raise TypeError("int8 convolutions have an int32 output")
+    if bias is not None and (bias.dtype != acc_dtype or bias.numel() < K or not bias.is_contiguous()):
+        raise ValueError("bias must be a contiguous length-K vector of the accumulator type")
+    epi = (TCM_EPI_BIAS if bias is not None else 0) | (TCM_EPI_RELU if relu else 0)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    st = tcm_conv2d(N, H, W, C, K, R, S, ph, pw, sh, sw, dh, dw, x.data_ptr(), f.data_ptr(), y.data_ptr(),
+                    code | c_flags, bias.data_ptr() if bias is not None else None, epi, stream)
+    if st != TCM_OK:
+        raise TcmError(st, "tcm_conv2d")
+    return y

@@ -1,5 +1,6 @@
 // Generic GEMM kernel: any element alignment, any leading dimension, either
-// layout of A and B.  It keeps the promise that a problem the fast path
+// layout of A and B; also the implicit-GEMM convolution for shapes the tiled
+// gather does not take (channels not a multiple of the K-step, huge inputs).  It keeps the promise that a problem the fast path
 // cannot take still gets the same result, only slower (je-d.tistory.com,
 // the auto-tensorcore note: without the matrix-core rewrite the code is
 // slower but functionally equal).  Structure: 64x64 output tile per
@@ -69,6 +70,31 @@ __device__ __forceinline__ void stage(char* lds, const typename G<DT>::T* X, int
     }
 }
 
+// The same piece of A for a convolution: A is the im2col view of the NHWC
+// input, row = output pixel (n, p, q), column = (r*S + s)*C + c; taps that
+// fall in the zero padding read as zero.
+template <int DT>
+__device__ __forceinline__ void stage_conv(char* lds, const typename G<DT>::T* X, const GenericArgs& a, int64_t r0,
+                                           int64_t k0) {
+    using T = typename G<DT>::T;
+    constexpr int ES = sizeof(T);
+    constexpr int BKE = kSlab / ES;
+    for (int idx = threadIdx.x; idx < kTile * BKE; idx += 256) {
+        const int r = idx / BKE, kk = idx % BKE;
+        const int64_t gr = r0 + r, gk = k0 + kk;
+        T v = T(0);
+        if (gr < a.M && gk < a.K) {
+            const int64_t pq = a.cv_P * a.cv_Q;
+            const int64_t n = gr / pq, p = (gr % pq) / a.cv_Q, q = gr % a.cv_Q;
+            const int64_t c = gk % a.cv_C, rs = gk / a.cv_C, fr = rs / a.cv_S, fs = rs % a.cv_S;
+            const int64_t h = p * a.cv_stride_h - a.cv_pad_h + fr * a.cv_dil_h;
+            const int64_t w = q * a.cv_stride_w - a.cv_pad_w + fs * a.cv_dil_w;
+            if (h >= 0 && h < a.cv_H && w >= 0 && w < a.cv_W) v = X[((n * a.cv_H + h) * a.cv_W + w) * a.cv_C + c];
+        }
+        *(T*)(lds + r * kRow + kk * ES) = v;
+    }
+}
+
 // C element (row, col) as the accumulator type, and its store.
 template <int DT>
 __device__ __forceinline__ typename G<DT>::AccS load_c(const GenericArgs& a, int64_t idx) {
@@ -131,7 +157,8 @@ __global__ __launch_bounds__(256) void generic_gemm_kernel(GenericArgs a) {
     }
 
     for (int64_t k0 = 0; k0 < a.K; k0 += BKE) {
-        stage<DT>(As, (const T*)a.A, a.lda, !a.a_col, m0, a.M, k0, a.K);
+        if (a.conv) stage_conv<DT>(As, (const T*)a.A, a, m0, k0);
+        else stage<DT>(As, (const T*)a.A, a.lda, !a.a_col, m0, a.M, k0, a.K);
         stage<DT>(Bs, (const T*)a.B, a.ldb, (bool)a.b_col, n0, a.N, k0, a.K);
         __syncthreads();
         i4_t af[2], bf[2];

@@ -74,7 +74,15 @@ bool tile_eligible(const Problem& p, const TileConfig& c) {
         if (p.N % ce || p.ldb % ce) return false;
     }
     // every per-tile byte offset must stay inside the descriptor range
-    if ((int64_t)c.bm * p.lda * es + kStepBytes >= kOffsetLimit) return false;
+    if (p.conv) {
+        // one K-step is one filter tap; the gather addresses x from its base
+        // with 32-bit element offsets, and row indices past M stay in int
+        if (p.conv_c % bk_elems(p.dtype)) return false;
+        if (p.conv_x_bytes >= kOffsetLimit) return false;
+        if (p.M + c.bm >= (1LL << 31)) return false;
+    } else if ((int64_t)c.bm * p.lda * es + kStepBytes >= kOffsetLimit) {
+        return false;
+    }
     if (p.b_col) {
         if ((int64_t)c.bn * p.ldb * es + kStepBytes >= kOffsetLimit) return false;
     } else {
@@ -116,9 +124,10 @@ Estimate estimate(const Problem& p, const TileConfig& c, int cus, int force_mode
     const double step = std::max(mfma, std::max(lds, l2)) + kStepOverhead;  // per K-step, CU to itself
     const double lone_step = kStepLatency + (c.bm + c.bn) * (double)kStepBytes / kStepBytesPerClk;
     const double tile_store = (double)c.bm * c.bn * 4 / kL2BytesPerClk;
+    // unique bytes: a convolution's A is its input x, read once however many taps reuse it
+    const double a_bytes = p.conv ? (double)p.conv_x_bytes : (double)p.M * p.K * elem_bytes(dt);
     const double hbm_floor = (double)std::max<int64_t>(p.batch, 1) *
-                             (((double)p.M * p.K + (double)p.K * p.N) * elem_bytes(dt) + (double)p.M * p.N * 4) /
-                             kHbmBytesPerClk;
+                             (a_bytes + (double)p.K * p.N * elem_bytes(dt) + (double)p.M * p.N * 4) / kHbmBytesPerClk;
 
     // data-parallel: waves of `slots` tiles, each wave takes I steps on a CU shared by `occ` workgroups
     Estimate dp{0, 1, (int)std::min<int64_t>(T, 1LL << 30), T, 0};

@@ -24,6 +24,10 @@ struct Problem {
     int c_type;    // CType
     int64_t batch = 1;  // entries of a strided batch
     bool aligned;  // every pointer 16-byte aligned
+    // implicit-GEMM convolution: A is the im2col view of an NHWC input of
+    // conv_x_bytes bytes and conv_c channels (lda is nominal)
+    bool conv = false;
+    int64_t conv_c = 0, conv_x_bytes = 0;
 };
 
 struct Plan {

@@ -24,6 +24,34 @@ int tile_sk_occupancy_f16(int config, bool b_kmajor);
 int tile_sk_occupancy_bf16(int config, bool b_kmajor);
 int tile_sk_occupancy_f32(int config, bool b_kmajor);
 int tile_sk_occupancy_i8(int config, bool b_kmajor);
+TileLauncher conv_launcher_f16(int config);
+TileLauncher conv_launcher_bf16(int config);
+TileLauncher conv_launcher_f32(int config);
+TileLauncher conv_launcher_i8(int config);
+int conv_sk_occupancy_f16(int config);
+int conv_sk_occupancy_bf16(int config);
+int conv_sk_occupancy_f32(int config);
+int conv_sk_occupancy_i8(int config);
+
+TileLauncher conv_launcher(int config, int dtype) {
+    switch (dtype) {
+    case F16: return conv_launcher_f16(config);
+    case BF16: return conv_launcher_bf16(config);
+    case F32: return conv_launcher_f32(config);
+    case I8: return conv_launcher_i8(config);
+    default: return nullptr;
+    }
+}
+
+int conv_sk_occupancy(int config, int dtype) {
+    switch (dtype) {
+    case F16: return conv_sk_occupancy_f16(config);
+    case BF16: return conv_sk_occupancy_bf16(config);
+    case F32: return conv_sk_occupancy_f32(config);
+    case I8: return conv_sk_occupancy_i8(config);
+    default: return 0;
+    }
+}
 
 int tile_sk_occupancy(int config, int dtype, bool b_kmajor) {
     switch (dtype) {
@@ -109,7 +137,8 @@ Options plan_options(const Problem& p) {
     {
         std::lock_guard<std::mutex> lk(g_mu);
         o = g_opts;
-        if (g_use_tuned && o.force_config < 0 && o.force_mode == 0) {
+        // tuned entries describe GEMM calls; a convolution is planned afresh
+        if (g_use_tuned && !p.conv && o.force_config < 0 && o.force_mode == 0) {
             auto it = g_tune.find(tune_key(p));
             if (it != g_tune.end()) {
                 o.force_config = it->second.config;
@@ -124,17 +153,19 @@ Options plan_options(const Problem& p) {
     return o;
 }
 
-// Workgroups per CU of the Stream-K kernels of p's (dtype, B layout), as the
-// runtime reports them for the compiled kernels (queried once per pair); a
-// runtime that cannot answer (no device) leaves the planner's static estimate.
+// Workgroups per CU of the Stream-K kernels of p's (dtype, B layout, GEMM or
+// convolution), as the runtime reports them for the compiled kernels (queried
+// once per kind); a runtime that cannot answer (no device) leaves the
+// planner's static estimate.
 void fill_sk_occupancy(const Problem& p, Options* o) {
     static std::map<int, std::vector<int>> occ_cache;
     std::lock_guard<std::mutex> lk(g_mu);
-    const int key = p.dtype * 2 + (p.b_col ? 1 : 0);
+    const int key = p.dtype * 4 + (p.b_col ? 1 : 0) + (p.conv ? 2 : 0);
     auto it = occ_cache.find(key);
     if (it == occ_cache.end()) {
         std::vector<int> v(kNumConfigs);
-        for (int c = 0; c < kNumConfigs; ++c) v[c] = tile_sk_occupancy(c, p.dtype, p.b_col);
+        for (int c = 0; c < kNumConfigs; ++c)
+            v[c] = p.conv ? conv_sk_occupancy(c, p.dtype) : tile_sk_occupancy(c, p.dtype, p.b_col);
         (void)hipGetLastError();
         it = occ_cache.emplace(key, v).first;
     }
@@ -205,14 +236,14 @@ std::string describe(const Plan& pl, const Problem& p) {
     if (pl.kernel == 0) {
         snprintf(buf, sizeof buf, "empty problem M=%lld N=%lld", (long long)p.M, (long long)p.N);
     } else if (pl.kernel == 1) {
-        snprintf(buf, sizeof buf, "kernel=generic tile=64x64 tiles=%lld iters=%lld M=%lld N=%lld K=%lld dtype=%d batch=%lld",
+        snprintf(buf, sizeof buf, "kernel=generic tile=64x64 tiles=%lld iters=%lld M=%lld N=%lld K=%lld dtype=%d batch=%lld%s",
                  (long long)pl.tiles, (long long)pl.iters, (long long)p.M, (long long)p.N, (long long)p.K, p.dtype,
-                 (long long)p.batch);
+                 (long long)p.batch, p.conv ? " conv=1" : "");
     } else {
         snprintf(buf, sizeof buf,
-                 "kernel=tile config=%d tile=%dx%dx%d mode=%s grid=%d tiles=%lld iters=%lld dp_tiles=%lld sk_tiles=%lld "
+                 "kernel=%s config=%d tile=%dx%dx%d mode=%s grid=%d tiles=%lld iters=%lld dp_tiles=%lld sk_tiles=%lld "
                  "M=%lld N=%lld K=%lld dtype=%d b_col=%d batch=%lld est_cycles=%.0f",
-                 pl.config, pl.bm, pl.bn, pl.bk, pl.mode == 1 ? "dp" : "streamk", pl.grid, (long long)pl.tiles,
+                 p.conv ? "conv" : "tile", pl.config, pl.bm, pl.bn, pl.bk, pl.mode == 1 ? "dp" : "streamk", pl.grid, (long long)pl.tiles,
                  (long long)pl.iters, (long long)pl.dp_tiles, (long long)pl.sk_tiles, (long long)p.M, (long long)p.N,
                  (long long)p.K, p.dtype, (int)p.b_col, (long long)p.batch, pl.est_cycles);
     }
@@ -393,6 +424,8 @@ int64_t batch_extent(int64_t batch, int64_t stride_bytes, int64_t ext) {
     return ext > 0 ? (batch - 1) * stride_bytes + ext : 0;
 }
 
+int launch_tiled(const Problem& p, const Plan& pl, TileArgs& a, int dev, void* stream);
+
 int gemm_impl(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int64_t sa, const void* B,
               int64_t ldb, int64_t sb, void* C, int64_t ldc, int64_t sc, int dtype, const void* bias, int64_t sbias,
               int epilogue, void* stream) {
@@ -449,7 +482,7 @@ int gemm_impl(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int
     t_last_plan = describe(pl, p);
 
     if (pl.kernel == 1) {
-        GenericArgs g;
+        GenericArgs g{};
         g.A = A;
         g.B = B;
         g.C = C;
@@ -476,28 +509,34 @@ int gemm_impl(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int
         return launch_generic(p.dtype, g, stream) == 0 ? TCM_OK : TCM_ERR_HIP;
     }
 
-    TileArgs a;
+    TileArgs a{};
     a.A = A;
     a.B = B;
     a.C = C;
     a.bias = use_bias ? bias : nullptr;
-    a.M = (int)M;
-    a.N = (int)N;
-    a.K = (int)K;
     a.lda = (int)lda;
     a.ldb = (int)ldb;
     a.ldc = (int)ldc;
-    a.relu = (epilogue & TCM_EPI_RELU) != 0;
-    a.has_bias = use_bias;
-    a.accum = (epilogue & TCM_EPI_ACCUM) != 0;
-    a.c_type = p.c_type;
     a.batch = (int)batch;
     a.stride_a = sa;
     a.stride_b = sb;
     a.stride_c = sc;
     a.stride_bias = sbias;
-    a.tiles_m = (int)((M + pl.bm - 1) / pl.bm);
-    a.tiles_n = (int)((N + pl.bn - 1) / pl.bn);
+    return launch_tiled(p, pl, a, dev, stream);
+}
+
+// Fills the plan-dependent fields of `a` (sizes, epilogue, tile schedule,
+// Stream-K workspace) and launches the tiled kernel the plan names.
+int launch_tiled(const Problem& p, const Plan& pl, TileArgs& a, int dev, void* stream) {
+    a.M = (int)p.M;
+    a.N = (int)p.N;
+    a.K = (int)p.K;
+    a.relu = (p.epilogue & TCM_EPI_RELU) != 0;
+    a.has_bias = (p.epilogue & TCM_EPI_BIAS) != 0;
+    a.accum = (p.epilogue & TCM_EPI_ACCUM) != 0;
+    a.c_type = p.c_type;
+    a.tiles_m = (int)((p.M + pl.bm - 1) / pl.bm);
+    a.tiles_n = (int)((p.N + pl.bn - 1) / pl.bn);
     a.iters = (int)pl.iters;
     a.dp_tiles = (int)pl.dp_tiles;
     a.sk_tiles = (int)pl.sk_tiles;
@@ -513,9 +552,139 @@ int gemm_impl(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int
         a.ws_partial = (float*)w.partial;
         a.ws_counter = w.counters;
     }
-    TileLauncher launch = tile_launcher(pl.config, p.dtype, p.b_col);
+    TileLauncher launch = p.conv ? conv_launcher(pl.config, p.dtype) : tile_launcher(pl.config, p.dtype, p.b_col);
     if (!launch) return TCM_ERR_NOT_SUPPORTED;
     return launch(a, stream) == 0 ? TCM_OK : TCM_ERR_HIP;
+}
+
+// a * b for non-negative a, b; -1 once the product passes 2^62
+int64_t mul_cap(int64_t a, int64_t b) {
+    if (a < 0 || b < 0) return -1;
+    if (a != 0 && b > ((int64_t)1 << 62) / a) return -1;
+    return a * b;
+}
+
+// Convolution of an NHWC input with a KRSC filter as the GEMM
+// y[(n,p,q), k] = sum over (r,s,c) of x[n, p*sh - ph + r*dh, q*sw - pw + s*dw, c] * f[k, r, s, c]
+// with zero padding (the implicit-GEMM reading of a 2-D convolution).
+int conv_impl(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R, int64_t S, int64_t pad_h, int64_t pad_w,
+              int64_t stride_h, int64_t stride_w, int64_t dil_h, int64_t dil_w, const void* x, const void* f, void* y,
+              int dtype, const void* bias, int epilogue, void* stream) {
+    const int64_t kDimLimit = (int64_t)1 << 31;
+    const int64_t dims[13] = {N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w};
+    for (int64_t d : dims)
+        if (d < 0 || d >= kDimLimit) return TCM_ERR_INVALID_VALUE;
+    if (R < 1 || S < 1 || stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1) return TCM_ERR_INVALID_VALUE;
+    if (dtype & (TCM_A_COLMAJOR | TCM_B_COLMAJOR)) return TCM_ERR_INVALID_VALUE;  // layouts are fixed
+    if (epilogue & TCM_EPI_ACCUM) return TCM_ERR_INVALID_VALUE;
+    const int64_t eh = H + 2 * pad_h - dil_h * (R - 1) - 1, ew = W + 2 * pad_w - dil_w * (S - 1) - 1;
+    if (eh < 0 || ew < 0) return TCM_ERR_INVALID_VALUE;  // the dilated filter is larger than the padded image
+    const int64_t P = eh / stride_h + 1, Q = ew / stride_w + 1;
+    const int64_t M = mul_cap(mul_cap(N, P), Q), Kg = mul_cap(mul_cap(R, S), C);
+    const int64_t x_elems = mul_cap(mul_cap(mul_cap(N, H), W), C);
+    if (M < 0 || Kg < 0 || x_elems < 0 || mul_cap(M, K) < 0 || mul_cap(K, Kg) < 0) return TCM_ERR_INVALID_VALUE;
+    Problem p;
+    int st = check_problem(M, K, Kg, std::max<int64_t>(Kg, 1), std::max<int64_t>(Kg, 1), std::max<int64_t>(K, 1),
+                           dtype | TCM_B_COLMAJOR, epilogue, &p);
+    if (st != TCM_OK) return st;
+    p.conv = true;
+    p.conv_c = C;
+    const int es = elem_bytes(p.dtype);
+    const int cs = c_elem_bytes(p.c_type);
+    p.conv_x_bytes = x_elems * es;
+    // the tiled gather keeps its pixel offsets in int: bound them by the
+    // padded image (one image past the last, for rows beyond M)
+    const double span = (double)(N + 1) * (double)(H + 2 * pad_h + 1) * (double)(W + 2 * pad_w + 1) * (double)C * es;
+    if (span >= (double)kDimLimit) p.conv_x_bytes = kDimLimit;  // too large for the tiled gather
+    if (M == 0 || K == 0) {
+        t_last_plan = "empty problem";
+        return TCM_OK;
+    }
+    const bool use_bias = epilogue & TCM_EPI_BIAS;
+    const int64_t x_ext = Kg > 0 ? x_elems * es : 0, f_ext = K * Kg * es, y_ext = M * K * cs;
+    if (!y) return TCM_ERR_INVALID_VALUE;
+    if (x_ext > 0 && !x) return TCM_ERR_INVALID_VALUE;
+    if (f_ext > 0 && !f) return TCM_ERR_INVALID_VALUE;
+    if (use_bias && !bias) return TCM_ERR_INVALID_VALUE;
+    if (((uintptr_t)x % es) || ((uintptr_t)f % es) || ((uintptr_t)y % cs) || (use_bias && ((uintptr_t)bias % 4)))
+        return TCM_ERR_INVALID_VALUE;
+    if (overlaps(y, y_ext, x, x_ext) || overlaps(y, y_ext, f, f_ext) || (use_bias && overlaps(y, y_ext, bias, K * 4)))
+        return TCM_ERR_INVALID_VALUE;
+    p.aligned = ((uintptr_t)x % 16 == 0) && ((uintptr_t)f % 16 == 0) && ((uintptr_t)y % 16 == 0) &&
+                (!use_bias || (uintptr_t)bias % 16 == 0);
+
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return TCM_ERR_HIP;
+    }
+    Options o = plan_options(p);
+    fill_sk_occupancy(p, &o);
+    Plan pl;
+    if (!make_plan(p, o, device_cus(dev), &pl)) return TCM_ERR_INVALID_VALUE;
+    t_last_plan = describe(pl, p);
+
+    if (pl.kernel == 1) {
+        GenericArgs g{};
+        g.A = x;
+        g.B = f;
+        g.C = y;
+        g.bias = use_bias ? bias : nullptr;
+        g.M = M;
+        g.N = K;
+        g.K = Kg;
+        g.lda = Kg;
+        g.ldb = Kg;
+        g.ldc = K;
+        g.a_col = 0;
+        g.b_col = 1;
+        g.relu = (epilogue & TCM_EPI_RELU) != 0;
+        g.has_bias = use_bias;
+        g.accum = 0;
+        g.c_type = p.c_type;
+        g.batch = 1;
+        g.tiles_m = (int)((M + 63) / 64);
+        g.tiles_n = (int)((K + 63) / 64);
+        g.conv = 1;
+        g.cv_H = H;
+        g.cv_W = W;
+        g.cv_C = C;
+        g.cv_P = P;
+        g.cv_Q = Q;
+        g.cv_R = R;
+        g.cv_S = S;
+        g.cv_pad_h = pad_h;
+        g.cv_pad_w = pad_w;
+        g.cv_stride_h = stride_h;
+        g.cv_stride_w = stride_w;
+        g.cv_dil_h = dil_h;
+        g.cv_dil_w = dil_w;
+        return launch_generic(p.dtype, g, stream) == 0 ? TCM_OK : TCM_ERR_HIP;
+    }
+
+    TileArgs a{};
+    a.A = x;
+    a.B = f;
+    a.C = y;
+    a.bias = use_bias ? bias : nullptr;
+    a.lda = (int)Kg;
+    a.ldb = (int)Kg;
+    a.ldc = (int)K;
+    a.batch = 1;
+    a.cv_H = (int)H;
+    a.cv_W = (int)W;
+    a.cv_C = (int)C;
+    a.cv_P = (int)P;
+    a.cv_Q = (int)Q;
+    a.cv_S = (int)S;
+    a.cv_pad_h = (int)pad_h;
+    a.cv_pad_w = (int)pad_w;
+    a.cv_stride_h = (int)stride_h;
+    a.cv_stride_w = (int)stride_w;
+    a.cv_dil_h = (int)dil_h;
+    a.cv_dil_w = (int)dil_w;
+    a.cv_x_bytes = (int)p.conv_x_bytes;
+    return launch_tiled(p, pl, a, dev, stream);
 }
 
 }  // namespace
@@ -526,6 +695,13 @@ extern "C" {
 int tcm_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
              int dtype, const void* bias, int epilogue, void* stream) {
     return gemm_impl(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, dtype, bias, 0, epilogue, stream);
+}
+
+int tcm_conv2d(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R, int64_t S, int64_t pad_h, int64_t pad_w,
+               int64_t stride_h, int64_t stride_w, int64_t dil_h, int64_t dil_w, const void* x, const void* f, void* y,
+               int dtype, const void* bias, int epilogue, void* stream) {
+    return conv_impl(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w, x, f, y, dtype, bias, epilogue,
+                     stream);
 }
 
 int tcm_gemm_batched(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int64_t stride_a,

@@ -64,6 +64,13 @@ struct TileArgs {
     int super_m, super_n; // tile order: super-tile (one XCD's share) in tiles
     float* ws_partial;    // Stream-K partial tiles: 2 slots per workgroup, bm*bn 4-byte values each
     int* ws_counter;      // one arrival counter per split tile (zero between launches)
+    // Implicit-GEMM convolution (kernels built with CONV only): A is the
+    // im2col view of an NHWC input x: row m = output pixel (n, p, q), column
+    // k = (r*S + s)*C + c.  C is a multiple of the K-step, so every K-step
+    // covers one filter tap (r, s).
+    int cv_H, cv_W, cv_C, cv_P, cv_Q, cv_S;
+    int cv_pad_h, cv_pad_w, cv_stride_h, cv_stride_w, cv_dil_h, cv_dil_w;
+    int cv_x_bytes;       // bytes of x (below 2^30)
 };
 
 // Tile t -> (tm, tn) for a grid of tiles_m x tiles_n tiles.  Workgroups are
@@ -150,12 +157,18 @@ struct GenericArgs {
     int batch;
     int64_t stride_a, stride_b, stride_c, stride_bias;
     int tiles_m, tiles_n;
+    // convolution: A is the im2col view of NHWC x (see TileArgs)
+    int conv;
+    int64_t cv_H, cv_W, cv_C, cv_P, cv_Q, cv_R, cv_S;
+    int64_t cv_pad_h, cv_pad_w, cv_stride_h, cv_stride_w, cv_dil_h, cv_dil_w;
 };
 
 // Launchers (defined next to the kernels).  Return hipError_t as int.
 using TileLauncher = int (*)(const TileArgs&, void* stream);
 // config index, dtype, B column-major (K-contiguous) -> launcher, or nullptr
 TileLauncher tile_launcher(int config, int dtype, bool b_kmajor);
+// the implicit-GEMM convolution kernels (B = the KRSC filter, k-contiguous)
+TileLauncher conv_launcher(int config, int dtype);
 // Stream-K workgroups of a config that fit on one CU, from the compiled
 // kernel's resources (0 if the runtime cannot tell).
 int tile_sk_occupancy(int config, int dtype, bool b_kmajor);

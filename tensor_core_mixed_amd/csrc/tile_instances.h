@@ -1,5 +1,6 @@
 // Instantiates the tiled kernel for every (tile config, B layout) of one
-// element type; each element type is compiled in its own translation unit.
+// element type, and the implicit-GEMM convolution kernel for every tile
+// config; each (kernel, element type) is compiled in its own translation unit.
 #pragma once
 #include "tile_kernel.h"
 
@@ -29,10 +30,40 @@ int pick_sk_occupancy(int config, bool b_kmajor) {
     }
 }
 
+template <int DT>
+TileLauncher pick_conv(int config) {
+    switch (config) {
+    case 0: return &launch_conv<DT, 0>;
+    case 1: return &launch_conv<DT, 1>;
+    case 2: return &launch_conv<DT, 2>;
+    case 3: return &launch_conv<DT, 3>;
+    case 4: return &launch_conv<DT, 4>;
+    default: return nullptr;
+    }
+}
+
+template <int DT>
+int pick_conv_occupancy(int config) {
+    switch (config) {
+    case 0: return conv_occupancy<DT, 0>();
+    case 1: return conv_occupancy<DT, 1>();
+    case 2: return conv_occupancy<DT, 2>();
+    case 3: return conv_occupancy<DT, 3>();
+    case 4: return conv_occupancy<DT, 4>();
+    default: return 0;
+    }
+}
+
 }  // namespace tcm
 
 #define TCM_TILE_TU(DT, NAME)                                                                          \
     namespace tcm {                                                                                    \
     TileLauncher tile_launcher_##NAME(int config, bool b_kmajor) { return pick_tile<DT>(config, b_kmajor); } \
     int tile_sk_occupancy_##NAME(int config, bool b_kmajor) { return pick_sk_occupancy<DT>(config, b_kmajor); } \
+    }
+
+#define TCM_CONV_TU(DT, NAME)                                                                     \
+    namespace tcm {                                                                               \
+    TileLauncher conv_launcher_##NAME(int config) { return pick_conv<DT>(config); }               \
+    int conv_sk_occupancy_##NAME(int config) { return pick_conv_occupancy<DT>(config); }          \
     }

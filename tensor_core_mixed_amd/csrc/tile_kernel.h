@@ -105,7 +105,7 @@ __device__ __forceinline__ int swz_mn(int k) {
     return s & (CPR - 1);
 }
 
-template <int DT, int CFG, bool B_KMAJ>
+template <int DT, int CFG, bool B_KMAJ, bool CONV = false>
 struct TileKernel {
     static constexpr TileConfig cfg = kConfigs[CFG];
     static constexpr int BM = cfg.bm, BN = cfg.bn, WM = cfg.wm, WN = cfg.wn;
@@ -149,9 +149,26 @@ struct TileKernel {
         int a_k[2];
         unsigned b_off[2];
         int b_k[2];
+        // convolution: per A copy instruction, this lane's output pixel as the
+        // element offset of its input origin (image n, row h0, column w0) and
+        // h0, w0 themselves (h0 far below zero for rows past M)
+        int cv_pix[CONV ? IA : 1], cv_h0[CONV ? IA : 1], cv_w0[CONV ? IA : 1];
     };
 
     __device__ __forceinline__ static void dma_setup(Dma& d, const TileArgs& a, int m0, int n0, int wave, int lane) {
+        if constexpr (CONV) {
+            const int pq = a.cv_P * a.cv_Q;
+#pragma unroll
+            for (int j = 0; j < IA; ++j) {
+                const int m = m0 + (((j * NW + wave) * 64 + lane) >> 3);
+                const int mm = m < a.M ? m : a.M - 1;  // rows past M: any real pixel, masked below
+                const int n = mm / pq, rem = mm - n * pq, p = rem / a.cv_Q, q = rem - p * a.cv_Q;
+                const int h0 = p * a.cv_stride_h - a.cv_pad_h, w0 = q * a.cv_stride_w - a.cv_pad_w;
+                d.cv_h0[j] = m < a.M ? h0 : -(1 << 28);
+                d.cv_w0[j] = w0;
+                d.cv_pix[j] = ((n * a.cv_H + h0) * a.cv_W + w0) * a.cv_C;
+            }
+        }
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int p = (q * NW + wave) * 64 + lane;
@@ -181,7 +198,24 @@ struct TileKernel {
                                                      int m0, int n0, int wave) {
         const int k0 = kt * BKE;
         const int krem = a.K - k0;
-        {
+        if constexpr (CONV) {
+            // this K-step's filter tap (r, s) and first channel: uniform
+            const int rs = k0 / a.cv_C, c0 = k0 - rs * a.cv_C;
+            const int rr = rs / a.cv_S, ss = rs - rr * a.cv_S;
+            const int dh = rr * a.cv_dil_h, dw = ss * a.cv_dil_w;
+            const int step = (dh * a.cv_W + dw) * a.cv_C + c0;
+            const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.A), (short)0, a.cv_x_bytes, kRsrcWord3);
+            lds_char* la = smem + st * STAGE;
+#pragma unroll
+            for (int j = 0; j < IA; ++j) {
+                const int h = d.cv_h0[j] + dh, w = d.cv_w0[j] + dw;
+                const bool in = (unsigned)h < (unsigned)a.cv_H && (unsigned)w < (unsigned)a.cv_W &&  // zero padding
+                                d.a_k[j & 1] < krem;
+                const unsigned off = in ? (unsigned)((d.cv_pix[j] + step + d.a_k[j & 1]) * ES) : kOOB;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(la + (j * NW + wave) * 1024),
+                                                         16, off, 0, 0, 0);
+            }
+        } else {
             const char* base = (const char*)a.A + ((int64_t)m0 * a.lda + k0) * ES;
             const int nrec = clamp_range(((int64_t)(a.M - m0) * a.lda - k0) * ES);
             const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, nrec, kRsrcWord3);
@@ -743,6 +777,33 @@ int launch_tile(const TileArgs& a, void* stream) {
     if (a.sk_tiles > 0)
         hipLaunchKernelGGL((tile_gemm_kernel<DT, CFG, B_KMAJ, true>), dim3(a.grid), dim3(TileThreads<CFG>::value), 0, s, a);
     return (int)hipGetLastError();
+}
+
+// Implicit-GEMM convolution: the same kernel with the A copies gathering
+// from the NHWC input; B is the KRSC filter (k-contiguous).
+template <int DT, int CFG, bool SK>
+__global__ __launch_bounds__(TileThreads<CFG>::value) void tile_conv_kernel(TileArgs a) {
+    if constexpr (SK) TileKernel<DT, CFG, true, true>::run_sk(a);
+    else TileKernel<DT, CFG, true, true>::run_dp(a);
+}
+
+template <int DT, int CFG>
+int launch_conv(const TileArgs& a, void* stream) {
+    hipStream_t s = (hipStream_t)stream;
+    if (a.dp_tiles > 0)
+        hipLaunchKernelGGL((tile_conv_kernel<DT, CFG, false>), dim3(a.dp_tiles), dim3(TileThreads<CFG>::value), 0, s, a);
+    if (a.sk_tiles > 0)
+        hipLaunchKernelGGL((tile_conv_kernel<DT, CFG, true>), dim3(a.grid), dim3(TileThreads<CFG>::value), 0, s, a);
+    return (int)hipGetLastError();
+}
+
+template <int DT, int CFG>
+int conv_occupancy() {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, tile_conv_kernel<DT, CFG, true>, TileThreads<CFG>::value, 0) !=
+        hipSuccess)
+        return 0;
+    return n;
 }
 
 }  // namespace tcm

@@ -319,3 +319,52 @@ def test_tune_invalid_arguments_without_device():
     assert T.tcm_tune(64, 64, 64, 1 << 20, 64, 2 << 20, 64, 3 << 20, 64, 0, None, 0, 0, None)[0] == T.TCM_ERR_INVALID_VALUE
     assert T.tcm_tune(64, 64, 64, 1 << 20, 3, 2 << 20, 64, 3 << 20, 64, 0, None, 0, 5, None)[0] == T.TCM_ERR_INVALID_VALUE
     assert T.tcm_tune(64, 64, 64, 1 << 20, 64, 2 << 20, 64, 3 << 20, 64, 0, None, 0, 5, None)[0] == T.TCM_ERR_HIP
+
+
+# convolution: (N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w, dtype, epilogue, x, f, y, bias)
+CONV_OK = (2, 8, 8, 64, 32, 3, 3, 1, 1, 1, 1, 1, 1, T.TCM_F16_F32, 0, 1 << 20, 2 << 20, 3 << 20, 0)
+_CONV_FIELDS = "N H W C K R S pad_h pad_w stride_h stride_w dil_h dil_w dtype epilogue x f y bias".split()
+
+
+def _conv(**kw):
+    a = dict(zip(_CONV_FIELDS, CONV_OK), **kw)
+    return T.tcm_conv2d(*(a[k] for k in _CONV_FIELDS[:13]), a["x"] or None, a["f"] or None, a["y"] or None, a["dtype"],
+                        a["bias"] or None, a["epilogue"], None)
+
+
+BAD_CONV = [
+    dict(N=-1), dict(H=-1), dict(C=-1), dict(K=-1), dict(R=0), dict(S=0),  # negative / empty filter
+    dict(pad_h=-1), dict(stride_w=0), dict(dil_h=0),
+    dict(H=2, R=5),                              # dilated filter larger than the padded input
+    dict(W=1, pad_w=0, S=2),
+    dict(H=3, R=2, dil_h=3, pad_h=0),           # dilation pushes the filter past the input
+    dict(H=1 << 31),                             # beyond the dimension limit
+    dict(dtype=T.TCM_F16_F32 | T.TCM_A_COLMAJOR),  # layouts are fixed
+    dict(dtype=T.TCM_F16_F32 | T.TCM_B_COLMAJOR),
+    dict(dtype=T.TCM_I8_I32 | T.TCM_C_F16),      # 16-bit output for int8
+    dict(dtype=7),                               # unknown element type
+    dict(epilogue=T.TCM_EPI_ACCUM),              # accumulate is not offered
+    dict(epilogue=T.TCM_EPI_BIAS),               # bias flag without bias
+    dict(x=0), dict(f=0), dict(y=0),             # NULL operands
+    dict(x=(1 << 20) + 1),                       # x not aligned to its element
+    dict(y=(3 << 20) + 2),                       # f32 y not aligned to its element
+    dict(y=(1 << 20) + 64),                      # y overlaps x
+    dict(y=(2 << 20) - 64),                      # y overlaps f (f starts inside y)
+    dict(epilogue=T.TCM_EPI_BIAS, bias=(3 << 20) + 256),  # bias inside y
+]
+
+
+@pytest.mark.parametrize("kw", BAD_CONV, ids=[",".join(f"{k}={v}" for k, v in d.items()) for d in BAD_CONV])
+def test_invalid_conv_arguments_rejected(kw):
+    assert _conv(**kw) == T.TCM_ERR_INVALID_VALUE
+
+
+def test_conv_empty_and_valid_without_device():
+    # no output pixel or no output channel: nothing to do, NULL pointers allowed
+    assert _conv(N=0, x=0, f=0, y=0) == T.TCM_OK
+    assert _conv(K=0, x=0, f=0, y=0) == T.TCM_OK
+    # valid requests reach the first HIP call: fast-path shapes, a channel count
+    # the tiled gather does not take, strides and dilations, 16-bit outputs
+    for kw in (dict(), dict(C=3), dict(stride_h=2, stride_w=3, dil_h=2, dil_w=2), dict(dtype=T.TCM_BF16_F32 | T.TCM_C_BF16),
+               dict(epilogue=T.TCM_EPI_BIAS | T.TCM_EPI_RELU, bias=4 << 20), dict(dtype=T.TCM_I8_I32), dict(C=0)):
+        assert _conv(**kw) == T.TCM_ERR_HIP, kw
