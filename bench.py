@@ -6,6 +6,7 @@
 A step is one tcm_gemm call of the whole hot path on the workload (default:
 f16 8192^3, A row-major, B column-major, f32 accumulate and output -- the
 shape the headline TFLOP/s figure is quoted on), inputs resident in HBM.
+A convolution workload (conv_*) times one tcm_conv2d call instead.
 Prints one JSON line with the throughput, the roofline of the dominant
 kernel (achieved algorithmic FLOP/s from HIP events on the launch stream vs
 the dtype's dense MFMA peak) and the CPU oracle's rate on a bounded sample.
@@ -35,9 +36,9 @@ DTYPE_NAME = {0: "f16", 1: "bf16", 2: "f32", 3: "i8"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{name}.json")
 
 
-# the sources of the tiled GEMM kernel, whose launches the stored counters describe
+# the sources of the tiled GEMM and convolution kernels, whose launches the stored counters describe
 KERNEL_SOURCES = ("tcm_internal.h", "tile_kernel.h", "tile_instances.h", "tile_f16.hip", "tile_bf16.hip",
-                  "tile_f32.hip", "tile_i8.hip")
+                  "tile_f32.hip", "tile_i8.hip", "conv_f16.hip", "conv_bf16.hip", "conv_f32.hip", "conv_i8.hip")
 
 
 def kernel_source_hash():
@@ -51,16 +52,20 @@ def kernel_source_hash():
 
 
 def plan_kernels(plan):
-    """Kernel names a tcm_last_plan() string launches (tiled kernel only)."""
+    """Kernel names a tcm_last_plan() string launches (tiled GEMM / convolution kernels only)."""
     f = dict(kv.split("=", 1) for kv in plan.split() if "=" in kv)
-    if f.get("kernel") != "tile":
+    if f.get("kernel") not in ("tile", "conv"):
         return set()
     b = "true" if f.get("b_col") == "1" else "false"
+    if f["kernel"] == "conv":
+        head = f"void tcm::tile_conv_kernel<{f['dtype']}, {f['config']}, "
+    else:
+        head = f"void tcm::tile_gemm_kernel<{f['dtype']}, {f['config']}, {b}, "
     names = set()
     if int(f.get("dp_tiles", 0)) > 0:
-        names.add(f"void tcm::tile_gemm_kernel<{f['dtype']}, {f['config']}, {b}, false>(tcm::TileArgs)")
+        names.add(head + "false>(tcm::TileArgs)")
     if int(f.get("sk_tiles", 0)) > 0:
-        names.add(f"void tcm::tile_gemm_kernel<{f['dtype']}, {f['config']}, {b}, true>(tcm::TileArgs)")
+        names.add(head + "true>(tcm::TileArgs)")
     return names
 
 
@@ -71,6 +76,98 @@ def describe(p):
             f"B {'col' if p.b_col else 'row'}-major, {acc} accumulate, {out} output"
             + (", C's contents as the initial value" if p.accum else "")
             + (", bias + ReLU epilogue" if p.bias else ""))
+
+
+def describe_conv(p):
+    acc = "int32" if p.dtype == 3 else "f32"
+    out = acc if p.c_type == "acc" else p.c_type
+    return (f"{DTYPE_NAME[p.dtype]} Conv2d NHWC {p.N}x{p.H}x{p.W}x{p.C} * KRSC {p.K}x{p.R}x{p.S}x{p.C}, "
+            f"pad {p.pad}, stride {p.stride}, dilation {p.dil} -> NPQK {p.N}x{p.P}x{p.Q}x{p.K} "
+            f"(implicit GEMM {p.N * p.P * p.Q}x{p.K}x{p.R * p.S * p.C}), {acc} accumulate, {out} output"
+            + (", bias + ReLU epilogue" if p.bias else ""))
+
+
+class ConvJob:
+    """A convolution workload resident on the device, one tcm_conv2d call per step."""
+
+    def __init__(self, p, stream):
+        import torch
+
+        import synthetic as S
+        import tensor_core_mixed_amd as T
+        self.p, self.g = p, S.generate_conv(p)
+        dev = lambda x: None if x is None else torch.from_numpy(
+            np.ascontiguousarray(x.view(np.int16) if x.dtype == np.uint16 else x)).cuda()
+        self.x, self.f, self.bias = dev(self.g["x"]), dev(self.g["f"]), dev(self.g["bias"])
+        c_t = {"f16": torch.float16, "bf16": torch.bfloat16}.get(p.c_type, torch.int32 if p.dtype == 3 else torch.float32)
+        self.y = torch.empty((p.N * p.P * p.Q, p.K), dtype=c_t, device="cuda")
+        code = p.dtype | {"acc": 0, "f16": T.TCM_C_F16, "bf16": T.TCM_C_BF16}[p.c_type]
+        epi = (T.TCM_EPI_BIAS if p.bias else 0) | (T.TCM_EPI_RELU if p.relu else 0)
+        self.args = (p.N, p.H, p.W, p.C, p.K, p.R, p.S, p.pad[0], p.pad[1], p.stride[0], p.stride[1], p.dil[0],
+                     p.dil[1], self.x.data_ptr(), self.f.data_ptr(), self.y.data_ptr(), code,
+                     self.bias.data_ptr() if self.bias is not None else None, epi, stream)
+
+    def call(self):
+        import tensor_core_mixed_amd as T
+        st = T.tcm_conv2d(*self.args)
+        if st != 0:
+            raise RuntimeError(T.tcm_status_string(st))
+
+    def _oracle(self, mm, kk):
+        import oracle
+        p, g = self.p, self.g
+        return oracle.get().conv2d_entries(g["x"], g["f"], p.dtype, mm, kk, pad=p.pad, stride=p.stride, dil=p.dil,
+                                           bias=g["bias"], relu=p.relu)
+
+    def sampled_check(self):
+        """(CPU leg) The seeded sampled outputs of y against the oracle's values."""
+        import torch
+
+        import synthetic as S
+        p, g = self.p, self.g
+        mm, kk = S.sample_conv_entries(p)
+        yc = self.y.float() if self.y.dtype in (torch.float16, torch.bfloat16) else self.y
+        got = yc.cpu().numpy()[mm, kk]
+        ref = self._oracle(mm, kk)
+        if p.dtype == 3:
+            return {"entries": int(got.size), "mismatches": int(np.sum(got != ref)), "ok": bool(np.all(got == ref))}
+        denom = p.R * p.S * p.C * float(np.max(np.abs(_decode(g["x"], p.dtype)))) * \
+            float(np.max(np.abs(_decode(g["f"], p.dtype))))
+        denom += float(np.max(np.abs(g["bias"]))) if g["bias"] is not None else 0.0
+        u = {"acc": 0.0, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}[p.c_type]
+        err = max(float(np.max(np.abs(got.astype(np.float64) - ref) - u * np.abs(ref))), 0.0) / (denom or 1.0)
+        tol = 1e-5 if p.dtype == 2 else 1e-3
+        return {"entries": int(got.size), "normalised_error": err, "tolerance": tol, "ok": err <= tol}
+
+    def _oracle_seconds(self, n):
+        rng = np.random.default_rng(7)
+        M = self.p.N * self.p.P * self.p.Q
+        mm, kk = rng.integers(0, M, n), rng.integers(0, self.p.K, n)
+        t = time.perf_counter()
+        self._oracle(mm, kk)
+        return time.perf_counter() - t
+
+    def cpu_baseline(self, unit_scale, outputs=1 << 18, per_core_outputs=1 << 12):
+        """The oracle's sampled-output entry point on `outputs` seeded random
+        outputs with every OpenMP thread, then `per_core_outputs` with one."""
+        import oracle
+        o = oracle.get()
+        p = self.p
+        per_out = 2.0 * p.R * p.S * p.C
+        threads = o.max_threads()
+        dt = self._oracle_seconds(outputs)
+        out = {"value": outputs * per_out / dt / unit_scale, "unit": "TFLOP/s" if p.dtype != 3 else "TOP/s",
+               "cores": threads, "kind": "oracle", "seconds": round(dt, 2),
+               "sample": f"{outputs} seeded random outputs of y (each a {p.R * p.S * p.C}-term sum; "
+                         f"{outputs / (p.N * p.P * p.Q * p.K):.4f} of the convolution), binary64 accumulation"}
+        o.set_threads(1)
+        try:
+            d1 = self._oracle_seconds(per_core_outputs)
+        finally:
+            o.set_threads(threads)
+        out["per_core"] = {"value": per_core_outputs * per_out / d1 / unit_scale, "outputs": per_core_outputs,
+                           "seconds": round(d1, 2)}
+        return out
 
 
 def make_c(p):
@@ -293,11 +390,62 @@ def load_traffic(p, plan):
     return t.get("hbm_bytes_per_launch")
 
 
+def run_bench_conv(args):
+    import torch
+
+    import synthetic as S
+    import tensor_core_mixed_amd as T
+    p = S.CONV_WORKLOADS[args.workload]
+    if args.dist:
+        from dataclasses import replace
+        p = replace(p, dist=args.dist)
+    torch.cuda.set_device(0)
+    print(f"[bench] workload {p.name}: {describe_conv(p)}", file=sys.stderr, flush=True)
+    stream_obj = torch.cuda.current_stream()
+    job = ConvJob(p, stream_obj.cuda_stream)
+    job.call()
+    torch.cuda.synchronize()
+    plan = T.tcm_last_plan()
+    print(f"[bench] plan: {plan}", file=sys.stderr, flush=True)
+    clock_before = gpu_clock()
+    ms, wall_ms = time_steps(job.call, args.steps, args.warmup, stream_obj)
+    calls = per_call_us(job.call, args.steps, stream_obj)
+    clock_after = gpu_clock()
+    value = p.flops / (ms * 1e-3) / 1e12
+    print(f"[bench] {ms:.4f} ms/step, {value:.1f} T(FL)OP/s", file=sys.stderr, flush=True)
+    roof = {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK[p.dtype],
+            "unit": "TFLOP/s" if p.dtype != 3 else "TOP/s", "frac": round(value / PEAK[p.dtype], 4),
+            "traffic": load_traffic(p, plan)}
+    cpu, parity = None, None
+    if not args.no_cpu:
+        job.call()
+        torch.cuda.synchronize()
+        parity = job.sampled_check()
+        print(f"[bench] sampled check {parity}", file=sys.stderr, flush=True)
+        cpu = job.cpu_baseline(1e12)
+    g = p.gemm()
+    line = {
+        "metric": "Conv2d + bias + ReLU (implicit GEMM) TFLOPS/TOPS on 1 MI355X and % of dtype MFMA peak",
+        "value": round(value, 2), "unit": "TFLOP/s" if p.dtype != 3 else "TOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE_NAME[p.dtype],
+        "data": "synthetic",
+        "config": {"workload": describe_conv(p), "gemm_M": g.M, "gemm_N": g.N, "gemm_K": g.K, "seed": p.seed,
+                   "dist": p.dist, "plan": plan, "wall_ms_per_step": round(wall_ms, 5), "per_call_us": calls,
+                   "hbm_frac": round(p.alg_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+                   "sclk_before_after": [clock_before, clock_after], "parity": parity},
+        "roofline": roof, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def run_bench(args):
     import torch
 
     import synthetic as S
     import tensor_core_mixed_amd as T
+    if args.workload in S.CONV_WORKLOADS:
+        return run_bench_conv(args)
     p = S.workload(args.workload, **({"dist": args.dist} if args.dist else {}))
     torch.cuda.set_device(0)
     print(f"[bench] workload {p.name}: {describe(p)}", file=sys.stderr, flush=True)
@@ -414,9 +562,41 @@ def run_all(args):
             print("[all] " + json.dumps(r), file=sys.stderr, flush=True)
         del A, B, bias, C
         torch.cuda.empty_cache()
+    for name, p in S.CONV_WORKLOADS.items():
+        s = torch.cuda.current_stream()
+        job = ConvJob(p, s.cuda_stream)
+        job.call()
+        torch.cuda.synchronize()
+        plan = T.tcm_last_plan()
+        ms, _ = time_steps(job.call, max(5, args.steps // 2), 10, s, min_warm_ms=200.0)
+        pc = per_call_us(job.call, max(5, args.steps // 2), s)
+        par = None
+        if not args.no_cpu:
+            job.call()
+            torch.cuda.synchronize()
+            par = job.sampled_check()
+        v = p.flops / (ms * 1e-3) / 1e12
+        row = {"workload": name, "mode": "auto", "ms": round(ms, 5), "per_call_us": pc, "tflops": round(v, 2),
+               "frac_peak": round(v / PEAK[p.dtype], 4),
+               "hbm_frac": round(p.alg_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+               "parity_ok": par["ok"] if par else None, "plan": plan}
+        if not args.no_cpu:
+            n = 1 << 16
+            dt = job._oracle_seconds(n)
+            row["cpu_oracle"] = {"tflops": round(2.0 * p.R * p.S * p.C * n / dt / 1e12, 5), "outputs": n,
+                                 "seconds": round(dt, 2), "threads": oracle_threads()}
+        rows.append(row)
+        print("[all] " + json.dumps(row), file=sys.stderr, flush=True)
+        del job
+        torch.cuda.empty_cache()
     if args.report:
         with open(args.report, "w") as f:
             json.dump(rows, f, indent=1)
+
+
+def oracle_threads():
+    import oracle
+    return oracle.get().max_threads()
 
 
 def run_sweep(args):
@@ -493,8 +673,9 @@ def summarize_counters(d, name, calib=None):
         return vals
 
     # per kernel (a Stream-K plan launches a data-parallel and a Stream-K kernel): medians per dispatch
-    fetch = per_kernel(d, "fetch", "FETCH_SIZE", "tile_gemm_kernel")
-    write = per_kernel(d, "write", "WRITE_SIZE", "tile_gemm_kernel")
+    kpat = "tile_conv_kernel" if name.startswith("conv_") else "tile_gemm_kernel"
+    fetch = per_kernel(d, "fetch", "FETCH_SIZE", kpat)
+    write = per_kernel(d, "write", "WRITE_SIZE", kpat)
     cf = per_dispatch_in(calib, "copy_fetch", "FETCH_SIZE", "copy")
     cw = per_dispatch_in(calib, "copy_write", "WRITE_SIZE", "copy")
     copy_kib = 512 * 1024

@@ -278,6 +278,7 @@ class ConvProblem:
     def flops(self):
         return 2 * self.N * self.P * self.Q * self.K * self.R * self.S * self.C
 
+    @property
     def alg_bytes(self):
         """Unique bytes: x and f read once, y written once (+ the bias)."""
         es = {F16: 2, BF16: 2, F32: 4, I8: 1}[self.dtype]
@@ -326,14 +327,16 @@ def small_conv(dtype, N, H, W, C, K, R, S, pad=(0, 0), stride=(1, 1), dil=(1, 1)
 
 def _conv_workloads():
     """3x3 convolutions with the shapes of a residual network's middle stages
-    (channels-last, batch 128), bias + ReLU fused."""
+    (channels-last, batch 128), bias + ReLU fused; float layers write their
+    activations in f16 for the next layer, int8 layers int32."""
     w = {}
     w["conv_f16_28x28_c128"] = ConvProblem("conv_f16_28x28_c128", F16, 128, 28, 28, 128, 128, 3, 3, pad=(1, 1),
-                                           dist="normal", seed=11, bias=True, relu=True)
+                                           dist="normal", seed=11, bias=True, relu=True, c_type="f16")
     w["conv_f16_14x14_c256"] = ConvProblem("conv_f16_14x14_c256", F16, 128, 14, 14, 256, 256, 3, 3, pad=(1, 1),
-                                           dist="normal", seed=12, bias=True, relu=True)
+                                           dist="normal", seed=12, bias=True, relu=True, c_type="f16")
     w["conv_f16_56x56_s2_c128"] = ConvProblem("conv_f16_56x56_s2_c128", F16, 128, 56, 56, 128, 128, 3, 3, pad=(1, 1),
-                                              stride=(2, 2), dist="normal", seed=13, bias=True, relu=True)
+                                              stride=(2, 2), dist="normal", seed=13, bias=True, relu=True,
+                                              c_type="f16")
     w["conv_i8_14x14_c256"] = ConvProblem("conv_i8_14x14_c256", I8, 128, 14, 14, 256, 256, 3, 3, pad=(1, 1),
                                           dist="int", seed=14, bias=True, relu=True)
     return w

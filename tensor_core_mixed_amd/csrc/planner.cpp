@@ -30,6 +30,14 @@ constexpr double kStepOverhead = 96.0;          // barrier + wait per K-step
 constexpr double kStepLatency = 500.0;          // lone workgroup: fixed part of a K-step ...
 constexpr double kStepBytesPerClk = 16.0;       // ... plus its copies at this rate
 constexpr double kFixupLatency = 1500.0;        // one device-coherent round trip per partial tile read back
+// Stream-K workgroups start their segments at different k, so tiles that
+// share an operand panel no longer read it from L2 at the same time.  For
+// 128x128 tiles (two workgroups per CU) a split K-step then streams its
+// operands at about the CU's share of MALL / HBM bandwidth, ~9 TB/s over
+// 256 CUs (measured on 3840^2 x 4096 and the 3x3 convolutions: split
+// K-steps took twice as long as data-parallel ones).  The 64x64 units keep
+// the fitted per-step cost: their K-steps are a quarter of the bytes.
+constexpr double kStaggerBytesPerClk = 14.6;
 
 double flops_per_clk(int dt) {
     switch (dt) {
@@ -54,10 +62,12 @@ int tile_wg_per_cu(const TileConfig& c) {
 }
 
 int tile_sk_wg_per_cu(const TileConfig& c) {
-    // the Stream-K kernels carry the partial-tile fix-up on top: only the
-    // 32x32-per-wave config stays small enough for several workgroups per CU
+    // the Stream-K kernels carry the partial-tile fix-up on top: the
+    // 32x32-per-wave config, and the 128x128 one compiled for it, hold two
+    // workgroups per CU; the others one
     const int wave_tile = (c.bm / c.wm) * (c.bn / c.wn);
-    return wave_tile <= 32 * 32 ? std::min(2, (160 * 1024) / lds_bytes(c)) : 1;
+    const bool two = wave_tile <= 32 * 32 || (c.wm * c.wn == 4 && c.bm == 128 && c.bn == 128);
+    return two ? std::min(2, (160 * 1024) / (lds_bytes(c) + 16)) : 1;
 }
 
 bool tile_eligible(const Problem& p, const TileConfig& c) {
@@ -166,7 +176,11 @@ Estimate estimate(const Problem& p, const TileConfig& c, int cus, int force_mode
         // trip per segment (the next partial's loads overlap the current add)
         const double fixup = splits ? rows_frac * partial / kL2BytesPerClk + nseg * (kFixupLatency + rows_frac * partial / kL2BytesPerClk) : 0.0;
         const double wg_step = std::max(step * share, lone_step);
-        sk.cycles = std::max(dp_waves * (I * wg_step + tile_store * share) + per_wg * wg_step + tile_store * share + fixup, hbm_floor);
+        const double split_step =
+            c.bm * c.bn >= 128 * 128 ? std::max(wg_step, share * (c.bm + c.bn) * (double)kStepBytes / kStaggerBytesPerClk)
+                                     : wg_step;
+        sk.cycles = std::max(dp_waves * (I * wg_step + tile_store * share) + per_wg * split_step + tile_store * share + fixup,
+                             hbm_floor);
         sk.grid = (int)grid;
         sk.dp_tiles = dp_tiles;
         sk.sk_tiles = sk_tiles;

@@ -115,16 +115,21 @@ __host__ __device__
 inline void tile_coords(int t, int tiles_m, int tiles_n, int group_m, int super_m, int super_n, int* tm, int* tn) {
     super_order(xcd_order(t, tiles_m * tiles_n), tiles_m, tiles_n, group_m, super_m, super_n, tm, tn);
 }
-// Batched: tile t of a batch of `batch` entries of tiles_m x tiles_n tiles.
+// Position n of the locality walk over a batch of tiles_m x tiles_n grids
+// (steps 2-3 above, entry by entry) -> (entry, tm, tn).  Step 1 is the
+// caller's: tile t of the work list (data-parallel tiles first, then the
+// Stream-K tiles in the order of the split) sits at n = xcd_order(t, tiles).
+// (Renumbering the Stream-K workgroups by XCD instead, so that each XCD
+// walks one contiguous run of the split, measured slower on a long-K
+// problem.)
 #if defined(__HIPCC__)
 __host__ __device__
 #endif
-inline void batch_tile_coords(int t, int batch, int tiles_m, int tiles_n, int group_m, int super_m, int super_n, int* b,
-                              int* tm, int* tn) {
+inline void walk_coords(int n, int tiles_m, int tiles_n, int group_m, int super_m, int super_n, int* b, int* tm,
+                        int* tn) {
     const int per = tiles_m * tiles_n;
-    const int nt = xcd_order(t, per * batch);
-    *b = nt / per;
-    super_order(nt - *b * per, tiles_m, tiles_n, group_m, super_m, super_n, tm, tn);
+    *b = n / per;
+    super_order(n - *b * per, tiles_m, tiles_n, group_m, super_m, super_n, tm, tn);
 }
 
 // Super-tile shape for a tiles_m x tiles_n grid: about T/8 tiles, near square.

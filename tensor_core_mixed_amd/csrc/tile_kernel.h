@@ -376,17 +376,17 @@ struct TileKernel {
     // ------------------------------------------------------- tile order
     // Tile t of the (batched) tile space: its coordinates within its entry and
     // the arguments with that entry's operand pointers (uniform per workgroup).
-    __device__ __forceinline__ static TileArgs tile_of(const TileArgs& a, int t, int& tm, int& tn) {
+    // The tile at position n of the locality walk: its coordinates, and a copy
+    // of the arguments whose operand pointers are its batch entry's.
+    __device__ __forceinline__ static TileArgs tile_of(const TileArgs& a, int n, int& tm, int& tn) {
         TileArgs e = a;
+        int b;
+        tcm::walk_coords(n, a.tiles_m, a.tiles_n, a.group_m, a.super_m, a.super_n, &b, &tm, &tn);
         if (a.batch > 1) {
-            int b;
-            tcm::batch_tile_coords(t, a.batch, a.tiles_m, a.tiles_n, a.group_m, a.super_m, a.super_n, &b, &tm, &tn);
             e.A = (const char*)a.A + b * a.stride_a * ES;
             e.B = (const char*)a.B + b * a.stride_b * ES;
             e.C = (char*)a.C + b * a.stride_c * c_elem_bytes(a.c_type);
             if (a.bias) e.bias = (const char*)a.bias + b * a.stride_bias * (int64_t)sizeof(AccS);
-        } else {
-            tcm::tile_coords(t, a.tiles_m, a.tiles_n, a.group_m, a.super_m, a.super_n, &tm, &tn);
         }
         return e;
     }
@@ -659,7 +659,7 @@ struct TileKernel {
         const int wm = wave / WN, wn = wave % WN;
         Acc acc[FM][FN];
         int tm, tn;
-        const TileArgs e = tile_of(a, blockIdx.x, tm, tn);
+        const TileArgs e = tile_of(a, xcd_order(blockIdx.x, a.tiles_m * a.tiles_n * a.batch), tm, tn);
         const int m0 = tm * BM, n0 = tn * BN;
         init_acc(acc, e, true, m0, n0, wm, wn, lane);
         mainloop(acc, e, smem, m0, n0, 0, e.iters, wave, lane);
@@ -689,7 +689,7 @@ struct TileKernel {
             const int k_lo = (int)(it - tsk * I);
             const int k_hi = (int)min<int64_t>(I, k_lo + (it1 - it));
             int tm, tn;
-            const TileArgs e = tile_of(a, a.dp_tiles + (int)tsk, tm, tn);
+            const TileArgs e = tile_of(a, xcd_order(a.dp_tiles + (int)tsk, a.tiles_m * a.tiles_n * a.batch), tm, tn);
             const int m0 = tm * BM, n0 = tn * BN;
             init_acc(acc, e, k_lo == 0, m0, n0, wm, wn, lane);
             mainloop(acc, e, smem, m0, n0, k_lo, k_hi, wave, lane);
@@ -719,8 +719,10 @@ struct TileKernel {
                 const int64_t ft = ((int64_t)w * W / a.grid) / I;
                 return 2 * w + (tsk == ft ? 0 : 1);
             };
-            if constexpr (NW > 4) {
-                // eight waves have 256 registers each: no room for a second buffer
+            if constexpr (NW > 4 || FM * FN >= 4) {
+                // one partial buffer: eight waves have no room for a second,
+                // and for 64x64 wave tiles a second one would halve the
+                // workgroups a CU holds
                 for (int w = w_first; w <= w_last; ++w) {
                     Partial pw;
                     load_partial(pw, partial_rsrc(a, slot_of(w)), wave, wm, lane, a.M - m0);
@@ -751,8 +753,20 @@ struct TileThreads {
     static constexpr int value = kConfigs[CFG].wm * kConfigs[CFG].wn * 64;
 };
 
+// Waves per SIMD the compiler must leave room for: the Stream-K kernel of
+// the four-wave 128x128 config is held to two, so a CU runs two of its
+// workgroups as it does the data-parallel one (left alone, the fix-up path
+// takes it past 256 registers).  The other kernels fit their occupancy by
+// themselves.
+template <int CFG, bool SK>
+struct TileWaves {
+    static constexpr int value =
+        (SK && kConfigs[CFG].wm * kConfigs[CFG].wn == 4 && kConfigs[CFG].bm == 128 && kConfigs[CFG].bn == 128) ? 2 : 1;
+};
+
 template <int DT, int CFG, bool B_KMAJ, bool SK>
-__global__ __launch_bounds__(TileThreads<CFG>::value) void tile_gemm_kernel(TileArgs a) {
+__global__ __launch_bounds__(TileThreads<CFG>::value) __attribute__((amdgpu_waves_per_eu(TileWaves<CFG, SK>::value)))
+void tile_gemm_kernel(TileArgs a) {
     if constexpr (SK) TileKernel<DT, CFG, B_KMAJ>::run_sk(a);
     else TileKernel<DT, CFG, B_KMAJ>::run_dp(a);
 }
@@ -782,7 +796,8 @@ int launch_tile(const TileArgs& a, void* stream) {
 // Implicit-GEMM convolution: the same kernel with the A copies gathering
 // from the NHWC input; B is the KRSC filter (k-contiguous).
 template <int DT, int CFG, bool SK>
-__global__ __launch_bounds__(TileThreads<CFG>::value) void tile_conv_kernel(TileArgs a) {
+__global__ __launch_bounds__(TileThreads<CFG>::value) __attribute__((amdgpu_waves_per_eu(TileWaves<CFG, SK>::value)))
+void tile_conv_kernel(TileArgs a) {
     if constexpr (SK) TileKernel<DT, CFG, true, true>::run_sk(a);
     else TileKernel<DT, CFG, true, true>::run_dp(a);
 }

@@ -32,6 +32,9 @@ def test_plan_kernels_names_the_launched_kernels():
     assert bench.plan_kernels(HYBRID_PLAN) == {"void tcm::tile_gemm_kernel<0, 1, false, false>(tcm::TileArgs)",
                                                "void tcm::tile_gemm_kernel<0, 1, false, true>(tcm::TileArgs)"}
     assert bench.plan_kernels("kernel=generic tile=64x64 tiles=4 iters=2 M=1 N=1 K=1 dtype=0") == set()
+    conv = HYBRID_PLAN.replace("kernel=tile", "kernel=conv").replace("b_col=0", "b_col=1")
+    assert bench.plan_kernels(conv) == {"void tcm::tile_conv_kernel<0, 1, false>(tcm::TileArgs)",
+                                        "void tcm::tile_conv_kernel<0, 1, true>(tcm::TileArgs)"}
 
 
 def _with_traffic(tmp_path, monkeypatch, record):
@@ -62,9 +65,9 @@ def test_traffic_dropped_when_kernel_sources_change(tmp_path, monkeypatch):
 
 
 def test_kernel_hash_covers_the_tiled_kernel_sources():
-    """Every source of the tiled GEMM kernel (the kernel the stored counters
-    describe) is in the hash: its instantiations, its template and the shared
-    argument / tile-table header."""
+    """Every source of the tiled GEMM and convolution kernels (the kernels the
+    stored counters describe) is in the hash: their instantiations, the
+    template and the shared argument / tile-table header."""
     csrc = os.path.join(ROOT, "tensor_core_mixed_amd", "csrc")
-    tiled = {f for f in os.listdir(csrc) if f.startswith("tile_")} | {"tcm_internal.h"}
+    tiled = {f for f in os.listdir(csrc) if f.startswith(("tile_", "conv_"))} | {"tcm_internal.h"}
     assert tiled == set(bench.KERNEL_SOURCES)
