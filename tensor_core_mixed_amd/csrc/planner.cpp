@@ -67,7 +67,7 @@ int tile_sk_wg_per_cu(const TileConfig& c) {
     // workgroups per CU; the others one
     const int wave_tile = (c.bm / c.wm) * (c.bn / c.wn);
     const bool two = wave_tile <= 32 * 32 || (c.wm * c.wn == 4 && c.bm == 128 && c.bn == 128);
-    return two ? std::min(2, (160 * 1024) / (lds_bytes(c) + 16)) : 1;
+    return two ? std::max(1, std::min(2, (160 * 1024) / (lds_bytes(c, true) + 16))) : 1;
 }
 
 bool tile_eligible(const Problem& p, const TileConfig& c) {
@@ -175,10 +175,14 @@ Estimate estimate(const Problem& p, const TileConfig& c, int cus, int force_mode
         // the last arrival's reads are latency-bound: about one memory round
         // trip per segment (the next partial's loads overlap the current add)
         const double fixup = splits ? rows_frac * partial / kL2BytesPerClk + nseg * (kFixupLatency + rows_frac * partial / kL2BytesPerClk) : 0.0;
+        // a lone Stream-K workgroup keeps sk_stages - 1 K-steps of copies in
+        // flight, which divides the latency part of its step
+        const double sk_lone = kStepLatency / (c.sk_stages - 1) + (c.bm + c.bn) * (double)kStepBytes / kStepBytesPerClk;
         const double wg_step = std::max(step * share, lone_step);
+        const double sk_wg_step = std::max(step * share, sk_lone);
         const double split_step =
-            c.bm * c.bn >= 128 * 128 ? std::max(wg_step, share * (c.bm + c.bn) * (double)kStepBytes / kStaggerBytesPerClk)
-                                     : wg_step;
+            c.bm * c.bn >= 128 * 128 ? std::max(sk_wg_step, share * (c.bm + c.bn) * (double)kStepBytes / kStaggerBytesPerClk)
+                                     : sk_wg_step;
         sk.cycles = std::max(dp_waves * (I * wg_step + tile_store * share) + per_wg * split_step + tile_store * share + fixup,
                              hbm_floor);
         sk.grid = (int)grid;

@@ -22,20 +22,26 @@ constexpr int kChunkBytes = 16;
 inline int bk_elems(int dt) { return kStepBytes / elem_bytes(dt); }
 
 // Tile-config table: macro tile BM x BN, waves arranged WM x WN (one wave
-// tile of (BM/WM) x (BN/WN) outputs each), 2 LDS stages.
+// tile of (BM/WM) x (BN/WN) outputs each), and the LDS stages of the
+// Stream-K kernel (the data-parallel kernels use 2).  A short Stream-K
+// segment is latency-bound: each stage is one more K-step of copies in
+// flight per workgroup.
 struct TileConfig {
     int bm, bn, wm, wn;
+    int sk_stages;
     const char* name;
 };
-constexpr int kNumConfigs = 5;
+constexpr int kNumConfigs = 6;
 constexpr TileConfig kConfigs[kNumConfigs] = {
-    {256, 256, 4, 2, "256x256 w4x2"},  // big square problems: 64x128 per wave, two waves per SIMD
-    {128, 128, 2, 2, "128x128 w2x2"},  // mid sizes, 2 workgroups per CU
-    {32, 256, 1, 4, "32x256 w1x4"},    // skinny M (M <= 32)
-    {64, 256, 1, 4, "64x256 w1x4"},    // skinny M (M <= 64)
-    {64, 64, 2, 2, "64x64 w2x2"},      // Stream-K units for skinny / small problems (16 KiB partials)
+    {256, 256, 4, 2, 2, "256x256 w4x2"},     // big square problems: 64x128 per wave, two waves per SIMD
+    {128, 128, 2, 2, 2, "128x128 w2x2"},     // mid sizes, 2 workgroups per CU
+    {32, 256, 1, 4, 2, "32x256 w1x4"},       // skinny M (M <= 32)
+    {64, 256, 1, 4, 2, "64x256 w1x4"},       // skinny M (M <= 64)
+    {64, 64, 2, 2, 2, "64x64 w2x2"},         // Stream-K units for skinny / small problems (16 KiB partials)
+    {64, 64, 2, 2, 4, "64x64 w2x2 deep"},    // the same with four Stream-K stages (two workgroups per CU):
+                                             // short latency-bound segments, e.g. M <= 64 with a few K-steps each
 };
-inline int lds_bytes(const TileConfig& c) { return 2 * (c.bm + c.bn) * kStepBytes; }
+inline int lds_bytes(const TileConfig& c, bool sk = false) { return (sk ? c.sk_stages : 2) * (c.bm + c.bn) * kStepBytes; }
 
 // Arguments of the tiled MFMA kernel.  Sizes are in elements, strides of the
 // operands in elements.  The kernel runs `dp_tiles` tiles whole (tile t on

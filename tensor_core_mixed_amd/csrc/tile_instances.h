@@ -14,6 +14,7 @@ TileLauncher pick_tile(int config, bool b_kmajor) {
     case 2: return b_kmajor ? &launch_tile<DT, 2, true> : &launch_tile<DT, 2, false>;
     case 3: return b_kmajor ? &launch_tile<DT, 3, true> : &launch_tile<DT, 3, false>;
     case 4: return b_kmajor ? &launch_tile<DT, 4, true> : &launch_tile<DT, 4, false>;
+    case 5: return b_kmajor ? &launch_tile<DT, 5, true> : &launch_tile<DT, 5, false>;
     default: return nullptr;
     }
 }
@@ -26,6 +27,7 @@ int pick_sk_occupancy(int config, bool b_kmajor) {
     case 2: return b_kmajor ? sk_occupancy<DT, 2, true>() : sk_occupancy<DT, 2, false>();
     case 3: return b_kmajor ? sk_occupancy<DT, 3, true>() : sk_occupancy<DT, 3, false>();
     case 4: return b_kmajor ? sk_occupancy<DT, 4, true>() : sk_occupancy<DT, 4, false>();
+    case 5: return b_kmajor ? sk_occupancy<DT, 5, true>() : sk_occupancy<DT, 5, false>();
     default: return 0;
     }
 }
@@ -38,6 +40,7 @@ TileLauncher pick_conv(int config) {
     case 2: return &launch_conv<DT, 2>;
     case 3: return &launch_conv<DT, 3>;
     case 4: return &launch_conv<DT, 4>;
+    case 5: return &launch_conv<DT, 5>;
     default: return nullptr;
     }
 }
@@ -50,6 +53,7 @@ int pick_conv_occupancy(int config) {
     case 2: return conv_occupancy<DT, 2>();
     case 3: return conv_occupancy<DT, 3>();
     case 4: return conv_occupancy<DT, 4>();
+    case 5: return conv_occupancy<DT, 5>();
     default: return 0;
     }
 }

@@ -105,7 +105,7 @@ __device__ __forceinline__ int swz_mn(int k) {
     return s & (CPR - 1);
 }
 
-template <int DT, int CFG, bool B_KMAJ, bool CONV = false>
+template <int DT, int CFG, bool B_KMAJ, bool CONV = false, int NST = 2>
 struct TileKernel {
     static constexpr TileConfig cfg = kConfigs[CFG];
     static constexpr int BM = cfg.bm, BN = cfg.bn, WM = cfg.wm, WN = cfg.wn;
@@ -117,7 +117,7 @@ struct TileKernel {
     static constexpr int FM = TM / 32, FN = TN / 32; // 32x32 MFMA tiles per wave
     static constexpr int A_BYTES = BM * kStepBytes, B_BYTES = BN * kStepBytes;
     static constexpr int STAGE = A_BYTES + B_BYTES;
-    static constexpr int LDS = 2 * STAGE;
+    static constexpr int LDS = NST * STAGE;  // NST stages, copies NST - 1 K-steps ahead of the MFMAs
     static constexpr int IA = BM / (8 * NW);         // DMA instructions per wave per stage (A)
     static constexpr int IB = BN / (8 * NW);         // (B)
     static constexpr int B_CPR = BN * ES / kChunkBytes;  // chunks per [k] row of an n-contiguous B tile
@@ -125,6 +125,7 @@ struct TileKernel {
     static_assert(BM % (8 * NW) == 0 && BN % (8 * NW) == 0, "tile rows must fill whole wave DMA instructions");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32x32");
     static_assert(LDS <= 160 * 1024, "LDS budget of one CU");
+    static_assert(NST >= 2 && (NST - 1) * (BM + BN) / (8 * NW) <= 63, "pipeline depth within the vmcnt range");
 
     using Acc = typename std::conditional<DT == I8, i16v_t, f16v_t>::type;
     using AccS = typename std::conditional<DT == I8, int, float>::type;
@@ -595,58 +596,80 @@ struct TileKernel {
         }
     }
 
-    // One K-step kt from stage st.  DMA: issue the copies of step kt+2 into
-    // stage st once it is drained; NEXT: load sub-step 0 of step kt+1.
+    // Wait until at most `steps` K-steps of copies are still in flight (the
+    // copies complete in issue order) and every LDS read has returned.
+    template <int STEPS>
+    __device__ __forceinline__ static void wait_copies() {
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(STEPS * (IA + IB)) : "memory");
+    }
+    // The same for a count known at run time, 0 <= steps <= NST - 1 (the
+    // tail of the loop and the prologue).
+    __device__ __forceinline__ static void wait_copies(int steps) {
+        if constexpr (NST - 1 >= 4) {
+            if (steps >= 4) return wait_copies<4>();
+        }
+        if constexpr (NST - 1 >= 3) {
+            if (steps >= 3) return wait_copies<3>();
+        }
+        if constexpr (NST - 1 >= 2) {
+            if (steps >= 2) return wait_copies<2>();
+        }
+        if (steps >= 1) return wait_copies<1>();
+        wait_copies<0>();
+    }
+    static_assert(NST <= 5, "wait_copies covers up to five stages");
+
+    // One K-step kt from stage st, the copies of steps kt+1 .. kt+NST-1
+    // issued earlier.  DMA: issue the copies of step kt+NST into stage st
+    // once it is drained; NEXT: load sub-step 0 of step kt+1 (next stage).
     template <bool DMA, bool NEXT>
     __device__ __forceinline__ static void kstep(Acc (&acc)[FM][FN], Frag (&f)[2], const Dma& d, const TileArgs& a,
-                                                 lds_char* smem, int st, int kt, int m0, int n0, int wave, int wm,
-                                                 int wn, int lane) {
+                                                 lds_char* smem, int st, int kt, int k_hi, int m0, int n0, int wave,
+                                                 int wm, int wn, int lane) {
 #pragma unroll
         for (int sub = 0; sub < 3; ++sub) {
             load_frag(f[(sub + 1) & 1], smem, st, sub + 1, wm, wn, lane);
             mma_frag(acc, f[sub & 1]);
             sched_reads();
         }
-        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        // step kt+1 must have landed; the copies of later steps may still fly
+        if constexpr (DMA) wait_copies<NST - 2>();
+        else wait_copies(min(k_hi - kt - 2, NST - 2));
         __syncthreads();  // step kt+1 is in LDS everywhere; stage st is drained
-        if constexpr (DMA) dma_issue(d, a, smem, st, kt + 2, m0, n0, wave);
-        if constexpr (NEXT) load_frag(f[0], smem, st ^ 1, 0, wm, wn, lane);
+        if constexpr (DMA) dma_issue(d, a, smem, st, kt + NST, m0, n0, wave);
+        if constexpr (NEXT) load_frag(f[0], smem, st + 1 == NST ? 0 : st + 1, 0, wm, wn, lane);
         mma_frag(acc, f[1]);
         if constexpr (DMA) sched_reads_dma();
         else if constexpr (NEXT) sched_reads();
     }
 
-    // Accumulate K-steps [k_lo, k_hi) of tile (m0, n0) into acc, two LDS
-    // stages, the copies running two K-steps ahead of the MFMAs.
+    // Accumulate K-steps [k_lo, k_hi) of tile (m0, n0) into acc: NST LDS
+    // stages, the copies running NST - 1 K-steps ahead of the MFMAs.
     __device__ __forceinline__ static void mainloop(Acc (&acc)[FM][FN], const TileArgs& a, lds_char* smem, int m0, int n0,
                                                     int k_lo, int k_hi, int wave, int lane) {
         const int wm = wave / WN, wn = wave % WN;
         Dma d;
         dma_setup(d, a, m0, n0, wave, lane);
-        __syncthreads();  // the previous tile's readers are done with both stages
+        __syncthreads();  // the previous tile's readers are done with every stage
         if (k_lo >= k_hi) return;
-        dma_issue(d, a, smem, 0, k_lo, m0, n0, wave);
-        if (k_lo + 1 < k_hi) dma_issue(d, a, smem, 1, k_lo + 1, m0, n0, wave);
-        if (k_lo + 1 < k_hi) {
-            if constexpr (IA + IB == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-            else if constexpr (IA + IB == 9) asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-            else if constexpr (IA + IB == 10) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
-            else if constexpr (IA + IB == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-            else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        } else {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
+        const int first = min(NST, k_hi - k_lo);  // steps copied before the loop
+#pragma unroll
+        for (int i = 0; i < NST; ++i)
+            if (i < first) dma_issue(d, a, smem, i, k_lo + i, m0, n0, wave);
+        wait_copies(first - 1);  // step k_lo has landed
         __syncthreads();
         Frag f[2];
         load_frag(f[0], smem, 0, 0, wm, wn, lane);
-        int kt = k_lo;
-        for (; kt + 2 < k_hi; ++kt)
-            kstep<true, true>(acc, f, d, a, smem, (kt - k_lo) & 1, kt, m0, n0, wave, wm, wn, lane);
-        if (kt + 1 < k_hi) {
-            kstep<false, true>(acc, f, d, a, smem, (kt - k_lo) & 1, kt, m0, n0, wave, wm, wn, lane);
-            ++kt;
+        int kt = k_lo, st = 0;
+        for (; kt + NST < k_hi; ++kt) {
+            kstep<true, true>(acc, f, d, a, smem, st, kt, k_hi, m0, n0, wave, wm, wn, lane);
+            st = st + 1 == NST ? 0 : st + 1;
         }
-        kstep<false, false>(acc, f, d, a, smem, (kt - k_lo) & 1, kt, m0, n0, wave, wm, wn, lane);
+        for (; kt + 1 < k_hi; ++kt) {
+            kstep<false, true>(acc, f, d, a, smem, st, kt, k_hi, m0, n0, wave, wm, wn, lane);
+            st = st + 1 == NST ? 0 : st + 1;
+        }
+        kstep<false, false>(acc, f, d, a, smem, st, kt, k_hi, m0, n0, wave, wm, wn, lane);
     }
 
 
@@ -767,7 +790,7 @@ struct TileWaves {
 template <int DT, int CFG, bool B_KMAJ, bool SK>
 __global__ __launch_bounds__(TileThreads<CFG>::value) __attribute__((amdgpu_waves_per_eu(TileWaves<CFG, SK>::value)))
 void tile_gemm_kernel(TileArgs a) {
-    if constexpr (SK) TileKernel<DT, CFG, B_KMAJ>::run_sk(a);
+    if constexpr (SK) TileKernel<DT, CFG, B_KMAJ, false, kConfigs[CFG].sk_stages>::run_sk(a);
     else TileKernel<DT, CFG, B_KMAJ>::run_dp(a);
 }
 
@@ -798,7 +821,7 @@ int launch_tile(const TileArgs& a, void* stream) {
 template <int DT, int CFG, bool SK>
 __global__ __launch_bounds__(TileThreads<CFG>::value) __attribute__((amdgpu_waves_per_eu(TileWaves<CFG, SK>::value)))
 void tile_conv_kernel(TileArgs a) {
-    if constexpr (SK) TileKernel<DT, CFG, true, true>::run_sk(a);
+    if constexpr (SK) TileKernel<DT, CFG, true, true, kConfigs[CFG].sk_stages>::run_sk(a);
     else TileKernel<DT, CFG, true, true>::run_dp(a);
 }
 

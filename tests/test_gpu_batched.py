@@ -105,7 +105,7 @@ def _case(p, **kw):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("config", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5])
 @pytest.mark.parametrize("mode", [1, 2])
 def test_batched_every_config_and_mode(dtype, config, mode):
     T.tcm_set_option("force_config", config)
@@ -126,9 +126,10 @@ def test_batched_shared_b_and_bias(dtype):
 
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("sk_grid", [5, 37, 200])
-def test_batched_streamk_splits_across_entries(dtype, sk_grid):
+@pytest.mark.parametrize("config", [4, 5])
+def test_batched_streamk_splits_across_entries(dtype, sk_grid, config):
     """One Stream-K grid over the tiles of all entries; segments cross entry boundaries."""
-    T.tcm_set_option("force_config", 4)
+    T.tcm_set_option("force_config", config)
     T.tcm_set_option("force_mode", 2)
     T.tcm_set_option("sk_grid", sk_grid)
     p = S.small_problem(dtype, 16, 192, 1024, seed=96, bias=True, batch=7)

@@ -96,7 +96,7 @@ def _run_check(p, **kw):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("config", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5])
 @pytest.mark.parametrize("mode", [1, 2])
 def test_conv_every_config_and_mode(dtype, config, mode):
     """Every tile config in both modes: 3x3, padding 1, ragged pixel count and channel count."""
@@ -176,9 +176,10 @@ def test_conv_16bit_output(variant, mode):
 
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("sk_grid", [3, 50, 300])
-def test_conv_streamk_split_tiles(dtype, sk_grid):
+@pytest.mark.parametrize("config", [4, 5])
+def test_conv_streamk_split_tiles(dtype, sk_grid, config):
     """Stream-K with grids that split tiles at arbitrary taps."""
-    T.tcm_set_option("force_config", 4)
+    T.tcm_set_option("force_config", config)
     T.tcm_set_option("force_mode", 2)
     T.tcm_set_option("sk_grid", sk_grid)
     p = S.small_conv(dtype, 2, 8, 8, 2 * BKE[dtype], 64, 3, 3, pad=(1, 1), seed=144, bias=True, relu=True)

@@ -66,7 +66,7 @@ def test_ragged_tiles_and_k_tail(dtype, shape, b_col):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("config", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5])
 @pytest.mark.parametrize("mode", [1, 2])
 def test_every_config_and_mode(dtype, config, mode):
     """Each tile config, data-parallel and Stream-K, on a shape with edges in M, N and K."""
@@ -81,13 +81,15 @@ def test_every_config_and_mode(dtype, config, mode):
 
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("sk_grid", [3, 7, 64, 301])
-def test_streamk_many_segments_per_tile(dtype, sk_grid):
+@pytest.mark.parametrize("config", [1, 5])
+def test_streamk_many_segments_per_tile(dtype, sk_grid, config):
     """Small persistent grids split each tile over several workgroups (and
-    large ones give workgroups a few iterations each)."""
+    large ones give workgroups a few iterations each: segments shorter than
+    the pipeline depth)."""
     ce = {S.F16: 8, S.BF16: 8, S.F32: 4, S.I8: 16}[dtype]
     p = S.small_problem(dtype, 260, 208, 40 * ce, seed=sk_grid, b_col=(sk_grid % 2 == 1), bias=True)
     T.tcm_set_option("force_mode", 2)
-    T.tcm_set_option("force_config", 1)
+    T.tcm_set_option("force_config", config)
     T.tcm_set_option("sk_grid", sk_grid)
     g, C, plan = _run(p)
     grid = int(plan.split("grid=")[1].split()[0])
@@ -220,7 +222,7 @@ def _epi_id(v):
 
 
 @pytest.mark.parametrize("variant", EPI_VARIANTS, ids=_epi_id)
-@pytest.mark.parametrize("config", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5])
 @pytest.mark.parametrize("mode", [1, 2])
 def test_init_tensor_and_16bit_c_every_config_and_mode(variant, config, mode):
     """C_in as the initial value and/or C stored in f16 / bf16, on every tile
@@ -249,10 +251,11 @@ def test_init_tensor_and_16bit_c_every_config_and_mode(variant, config, mode):
 
 
 @pytest.mark.parametrize("variant", EPI_VARIANTS, ids=_epi_id)
-def test_init_tensor_streamk_many_segments(variant):
+@pytest.mark.parametrize("config", [4, 5])
+def test_init_tensor_streamk_many_segments(variant, config):
     """Only the k = 0 segment of a split tile may add C_in (and the bias)."""
     dtype, c_type, accum = variant
-    T.tcm_set_option("force_config", 4)
+    T.tcm_set_option("force_config", config)
     T.tcm_set_option("force_mode", 2)
     T.tcm_set_option("sk_grid", 37)
     K = 1024 if dtype != S.I8 else 2048
