@@ -755,6 +755,25 @@ struct TileKernel {
                 if (tid == 0) __hip_atomic_store(a.ws_counter + tsk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 continue;
             }
+            if constexpr (NST > 2) {
+                // deep-pipeline configs hold two workgroups per CU (LDS),
+                // so their registers take four partials at once: a tile
+                // split over many short segments waits for one round trip
+                // per four partials
+                constexpr int NB = 4;
+                for (int w0 = w_first; w0 <= w_last; w0 += NB) {
+                    Partial pb[NB];
+#pragma unroll
+                    for (int j = 0; j < NB; ++j)
+                        if (w0 + j <= w_last) load_partial(pb[j], partial_rsrc(a, slot_of(w0 + j)), wave, wm, lane, a.M - m0);
+#pragma unroll
+                    for (int j = 0; j < NB; ++j)
+                        if (w0 + j <= w_last) add_partial(acc, pb[j], w0 + j == w_first);
+                }
+                store_tile(acc, e, m0, n0, wm, wn, lane);
+                if (tid == 0) __hip_atomic_store(a.ws_counter + tsk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                continue;
+            }
             // (unrolled by two so both buffers stay in registers)
             Partial p0, p1;
             load_partial(p0, partial_rsrc(a, slot_of(w_first)), wave, wm, lane, a.M - m0);
