@@ -119,6 +119,24 @@ def test_planner_skinny_uses_streamk(M):
     p = T.tcm_plan(M, 4096, 4096, 4096, 4096, 4096, T.TCM_F16_F32)
     assert p["kernel"] == 1 and p["mode"] == 2
     assert p["sk_tiles"] > 0 and p["workspace_bytes"] > 0
+    # a few K-steps per workgroup: the 64x64 tile with the deep Stream-K pipeline
+    assert p["config"] == 5 and (p["bm"], p["bn"]) == (64, 64)
+
+
+def test_deep_config_is_the_small_tile_with_more_stages():
+    assert T.tcm_config_count() == 6
+    for dt in range(4):
+        assert T.tcm_config_info(5, dt)[:2] == T.tcm_config_info(4, dt)[:2] == (64, 64)
+
+
+def test_planner_keeps_split_128_tiles_for_phase_aligned_shapes():
+    # 3840^2 x 4096 (900 tiles of 128x128 on 512 slots): a split-k plan would
+    # read shared operand panels out of phase, so the 256x256 data-parallel
+    # plan stays; and 1536^2 x 16384 (too few tiles for one wave) splits k.
+    p = T.tcm_plan(3840, 3840, 4096, 4096, 3840, 3840, T.TCM_F16_F32)
+    assert p["mode"] == 1 and (p["bm"], p["bn"]) == (256, 256)
+    p = T.tcm_plan(1536, 1536, 16384, 16384, 1536, 1536, T.TCM_F16_F32)
+    assert p["mode"] == 2
 
 
 def test_planner_generic_fallbacks():
