@@ -41,13 +41,22 @@ KERNEL_SOURCES = ("tcm_internal.h", "tile_kernel.h", "tile_instances.h", "tile_f
                   "tile_f32.hip", "tile_i8.hip", "conv_f16.hip", "conv_bf16.hip", "conv_f32.hip", "conv_i8.hip")
 
 
+def _code_only(text):
+    """C++ source without comments, trailing spaces and blank lines."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def kernel_source_hash():
-    """Hash of the tiled kernel's sources: counters taken on other code are stale."""
+    """Hash of the tiled kernels' code (comments and layout excluded): counters
+    taken on other code are stale."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "tensor_core_mixed_amd", "csrc")
     for f in KERNEL_SOURCES:
-        with open(os.path.join(d, f), "rb") as fh:
-            h.update(f.encode() + fh.read())
+        with open(os.path.join(d, f)) as fh:
+            h.update(f.encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -5,11 +5,13 @@
 //    C is cut into BM x BN macro tiles, one per workgroup; each of the
 //    WM x WN waves owns a (BM/WM) x (BN/WN) block of 32x32 MFMA tiles whose
 //    accumulators stay in registers for the whole k loop.
-//  * Cooperative staging through LDS (same page, Step 3): all lanes of the
-//    workgroup copy the A and B k-slabs of one K-step into LDS with 16-byte
+//  * Cooperative staging through LDS (same page, Step 3): the lanes of the
+//    workgroup's copier waves (all waves, or half of them in the eight-wave
+//    kernel) copy the A and B k-slabs of one K-step into LDS with 16-byte
 //    direct-to-LDS buffer loads (one lane = one 16-byte chunk; a wave
 //    instruction fills 1 KiB of LDS), coalesced along the contiguous
-//    dimension of each operand.
+//    dimension of each operand.  A convolution gathers A from its NHWC
+//    input instead (implicit GEMM).
 //  * Bank-conflict-free LDS layout (leiblog.wang, the padding/bank-conflict
 //    post and the storage_align answer): instead of padding rows, the
 //    16-byte chunk index of every row is XOR-ed with a function of the row,
@@ -19,8 +21,9 @@
 //    fragment for k-contiguous operands; for operands stored n-contiguous
 //    (row-major B) the gfx950 transpose reads ds_read_b64_tr_b16/_b8 build
 //    the k-contiguous fragment directly from the [k][n] LDS tile.
-//  * Software pipelining (Step 5): two LDS stages; the loads of K-step k+1
-//    are in flight while the MFMAs of step k run.
+//  * Software pipelining (Step 5): NST LDS stages (two for data-parallel
+//    kernels, up to four for Stream-K); the copies of K-steps k+1 ..
+//    k+NST-1 are in flight while the MFMAs of step k run.
 //  * Unrolled inner loop of matrix-core ops (Step 6; Tensor Core notes on
 //    je-d.tistory.com: mixed-precision multiply-accumulate per warp-level
 //    operation): v_mfma_f32_32x32x16_{f16,bf16}, v_mfma_i32_32x32x32_i8,
@@ -594,8 +597,9 @@ struct TileKernel {
             if (i < NRD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
         }
     }
-    // Last sub-step of a K-step: 16 MFMAs, the 16 copies of step kt+2 and
-    // the 8 reads of the next step's first sub-step.
+    // Last sub-step of a K-step: its MFMAs, the copies of step kt+NST and the
+    // reads of the next step's first sub-step.  (Where only some waves copy,
+    // the copies sit in a branch of their own and this interleaves nothing.)
     __device__ __forceinline__ static void sched_reads_dma() {
 #pragma unroll
         for (int i = 0; i < NMF; ++i) {

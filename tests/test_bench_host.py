@@ -71,3 +71,9 @@ def test_kernel_hash_covers_the_tiled_kernel_sources():
     csrc = os.path.join(ROOT, "tensor_core_mixed_amd", "csrc")
     tiled = {f for f in os.listdir(csrc) if f.startswith(("tile_", "conv_"))} | {"tcm_internal.h"}
     assert tiled == set(bench.KERNEL_SOURCES)
+
+
+def test_kernel_hash_ignores_comments_but_not_code():
+    src = "int f(int x) {  // twice\n    /* a\n       block */\n    return 2 * x;\n}\n"
+    assert bench._code_only(src) == bench._code_only(src.replace("twice", "double it").replace("a\n", "b\n"))
+    assert bench._code_only(src) != bench._code_only(src.replace("2 * x", "3 * x"))
