@@ -38,6 +38,11 @@ constexpr double kFixupLatency = 1500.0;        // one device-coherent round tri
 // K-steps took twice as long as data-parallel ones).  The 64x64 units keep
 // the fitted per-step cost: their K-steps are a quarter of the bytes.
 constexpr double kStaggerBytesPerClk = 14.6;
+// Split tiles also lose the L2 reuse of their operand panels across the
+// grid: each tile row re-reads B and each tile column re-reads A, served
+// from MALL (the 256 MiB last-level cache) at ~16 TB/s (fitted to
+// 1536^2 x 16384 with 64x64 and 128x128 units and to M = 256).
+constexpr double kMallBytesPerClk = 16.0e12 / 2.4e9;
 
 double flops_per_clk(int dt) {
     switch (dt) {
@@ -183,8 +188,12 @@ Estimate estimate(const Problem& p, const TileConfig& c, int cus, int force_mode
         const double split_step =
             c.bm * c.bn >= 128 * 128 ? std::max(sk_wg_step, share * (c.bm + c.bn) * (double)kStepBytes / kStaggerBytesPerClk)
                                      : sk_wg_step;
+        const double sk_frac = (double)sk_tiles / (double)T;
+        const double rereads = sk_frac * (double)std::max<int64_t>(p.batch, 1) *
+                               (a_bytes * cdiv(p.N, c.bn) + (double)p.K * p.N * elem_bytes(dt) * cdiv(p.M, c.bm)) /
+                               kMallBytesPerClk;
         sk.cycles = std::max(dp_waves * (I * wg_step + tile_store * share) + per_wg * split_step + tile_store * share + fixup,
-                             hbm_floor);
+                             std::max(hbm_floor, rereads));
         sk.grid = (int)grid;
         sk.dp_tiles = dp_tiles;
         sk.sk_tiles = sk_tiles;
