@@ -235,7 +235,11 @@ typedef struct {
 int tcm_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
              int dtype, int epilogue, int aligned, tcm_plan_info* out);
 
-/* Number of rows of the tile table, and row i as (bm, bn, bk, waves). */
+/* Number of rows of the tile table, and row i as (bm, bn, bk, waves).  Two
+ * rows may share a shape and differ in the depth of their split-k (Stream-K)
+ * pipeline: LDS stages of copies in flight per workgroup, traded against
+ * workgroups per CU.  Returns TCM_OK or TCM_ERR_INVALID_VALUE (bad index or
+ * dtype). */
 int tcm_config_count(void);
 int tcm_config_info(int index, int dtype, int32_t* bm, int32_t* bn, int32_t* bk, int32_t* waves);
 
