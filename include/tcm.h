@@ -15,7 +15,9 @@
  * notes: mixed-precision multiply-accumulate).  Large problems are tiled and
  * staged through LDS (kimm240.github.io/tvm, GEMM optimisation Steps 2-6);
  * shapes whose tile count fills the GPU badly are split along k across
- * workgroups (leiblog.wang, the Stream-K reproduction post).
+ * workgroups (leiblog.wang, the Stream-K reproduction post).  The same
+ * tiled product also serves a strided batch of products (tcm_gemm_batched)
+ * and the Conv2d + bias + ReLU pattern as an implicit GEMM (tcm_conv2d).
  *
  * All pointers are DEVICE pointers (any allocation the HIP runtime can read
  * on the current device).  The caller owns A, B, C and bias; the library
