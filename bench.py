@@ -36,9 +36,10 @@ DTYPE_NAME = {0: "f16", 1: "bf16", 2: "f32", 3: "i8"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{name}.json")
 
 
-# the sources of the tiled GEMM and convolution kernels, whose launches the stored counters describe
+# the sources of the tiled GEMM, grouped and convolution kernels, whose launches the stored counters describe
 KERNEL_SOURCES = ("tcm_internal.h", "tile_kernel.h", "tile_instances.h", "tile_f16.hip", "tile_bf16.hip",
-                  "tile_f32.hip", "tile_i8.hip", "conv_f16.hip", "conv_bf16.hip", "conv_f32.hip", "conv_i8.hip")
+                  "tile_f32.hip", "tile_i8.hip", "conv_f16.hip", "conv_bf16.hip", "conv_f32.hip", "conv_i8.hip",
+                  "group_f16.hip", "group_bf16.hip", "group_f32.hip", "group_i8.hip")
 
 
 def _code_only(text):
@@ -177,6 +178,53 @@ class ConvJob:
         out["per_core"] = {"value": per_core_outputs * per_out / d1 / unit_scale, "outputs": per_core_outputs,
                            "seconds": round(d1, 2)}
         return out
+
+
+class GroupJob:
+    """A group workload resident on the device: one tcm_gemm_grouped call per
+    step, or (call_each) one tcm_gemm call per entry."""
+
+    def __init__(self, ps, stream):
+        import tensor_core_mixed_amd as T
+        import synthetic as S
+        self.ps, self.gs = ps, [S.generate(p) for p in ps]
+        self.dev = [upload(g, p) for p, g in zip(ps, self.gs)]
+        self.Cs = [make_c(p) for p in ps]
+        self.ents = [(p.M, p.N, A.data_ptr(), p.LDA, B.data_ptr(), p.LDB, C.data_ptr(), p.LDC, None)
+                     for p, (A, B, _), C in zip(ps, self.dev, self.Cs)]
+        self.code = ps[0].dtype | (T.TCM_B_COLMAJOR if ps[0].b_col else 0)
+        self.stream = stream
+        self.singles = [make_call(p, A, B, bias, C, stream) for p, (A, B, bias), C in zip(ps, self.dev, self.Cs)]
+
+    def call(self):
+        import tensor_core_mixed_amd as T
+        st = T.tcm_gemm_grouped(self.ents, self.ps[0].K, self.code, 0, self.stream)
+        if st != 0:
+            raise RuntimeError(T.tcm_status_string(st))
+
+    def call_each(self):
+        for c in self.singles:
+            c()
+
+    @property
+    def flops(self):
+        return sum(p.flops for p in self.ps)
+
+    @property
+    def alg_bytes(self):
+        return sum(p.alg_bytes for p in self.ps)
+
+    def sampled_check(self):
+        """(CPU leg) Every non-empty entry's sampled entries against the oracle."""
+        worst, n, ok = 0.0, 0, True
+        for p, g, C in zip(self.ps, self.gs, self.Cs):
+            if p.M == 0:
+                continue
+            r = _oracle_sampled_check(p, g, C)
+            n += r["entries"]
+            ok = ok and r["ok"]
+            worst = max(worst, r.get("normalised_error", 0.0))
+        return {"entries": n, "normalised_error": worst, "ok": ok}
 
 
 def make_c(p):
@@ -570,6 +618,28 @@ def run_all(args):
         for r in mine:
             print("[all] " + json.dumps(r), file=sys.stderr, flush=True)
         del A, B, bias, C
+        torch.cuda.empty_cache()
+    for name, ps in S.GROUP_WORKLOADS.items():
+        s = torch.cuda.current_stream()
+        job = GroupJob(ps, s.cuda_stream)
+        job.call()
+        torch.cuda.synchronize()
+        plan = T.tcm_last_plan()
+        ms, _ = time_steps(job.call, max(5, args.steps // 2), 10, s, min_warm_ms=200.0)
+        ms_each, _ = time_steps(job.call_each, max(5, args.steps // 2), 10, s, min_warm_ms=200.0)
+        par = None
+        if not args.no_cpu:
+            job.call()
+            torch.cuda.synchronize()
+            par = job.sampled_check()
+        v = job.flops / (ms * 1e-3) / 1e12
+        row = {"workload": name, "mode": "auto", "ms": round(ms, 5), "tflops": round(v, 2),
+               "frac_peak": round(v / PEAK[ps[0].dtype], 4),
+               "hbm_frac": round(job.alg_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
+               "entries_one_by_one_ms": round(ms_each, 5), "parity_ok": par["ok"] if par else None, "plan": plan}
+        rows.append(row)
+        print("[all] " + json.dumps(row), file=sys.stderr, flush=True)
+        del job
         torch.cuda.empty_cache()
     for name, p in S.CONV_WORKLOADS.items():
         s = torch.cuda.current_stream()

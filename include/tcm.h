@@ -149,6 +149,45 @@ int tcm_gemm_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
                      void* stream);
 
 /*
+ * tcm_gemm_grouped -- `count` independent products that share K, dtype and
+ * epilogue but not their shapes or operands,
+ *
+ *     C_e = epi( [C_e,in +] bias_e + A_e . B_e ),   A_e: M_e x K, B_e: K x N_e,
+ *
+ * e.g. the experts of a mixture, each with its own rows.  The tiles of all
+ * entries form one work list (entry after entry), so split-k (Stream-K)
+ * spreads the k-iterations of every entry's tiles over one persistent grid,
+ * the contiguous-batching case that motivates Stream-K (leiblog.wang, the
+ * Stream-K reproduction post), here with a different M (and N) per entry.
+ *
+ *   count        0 .. TCM_MAX_GROUP entries (0: nothing to do).
+ *   entries      HOST array of `count` descriptors, read during the call
+ *                only: M, N (>= 0; an entry with M or N == 0 is skipped),
+ *                A, lda, B, ldb, C, ldc, bias as for tcm_gemm (device
+ *                pointers; bias read only with TCM_EPI_BIAS).
+ *   K, dtype, epilogue, stream   as tcm_gemm, shared by every entry.
+ * Every C must not overlap any entry's A, B, bias or another entry's C.
+ * When no tile config can take every entry (odd layouts, unaligned
+ * pointers), the entries run one by one as tcm_gemm calls.
+ * Returns as tcm_gemm; TCM_ERR_INVALID_VALUE also for count outside
+ * [0, TCM_MAX_GROUP], a NULL `entries` with count > 0, or overlapping C.
+ */
+#define TCM_MAX_GROUP 32
+typedef struct {
+    int64_t M, N;
+    const void* A;
+    int64_t lda;
+    const void* B;
+    int64_t ldb;
+    void* C;
+    int64_t ldc;
+    const void* bias;
+} tcm_group_entry;
+
+int tcm_gemm_grouped(int64_t count, const tcm_group_entry* entries, int64_t K,
+                     int dtype, int epilogue, void* stream);
+
+/*
  * tcm_conv2d -- 2-D convolution with the fused bias + ReLU epilogue (the
  * Conv2d + bias + ReLU pattern of kimm240.github.io/tvm, post "Implement and
  * enable Conv2d-Reshape-Add-ReLU fusion"), computed as an implicit GEMM on

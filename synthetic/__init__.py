@@ -343,3 +343,15 @@ def _conv_workloads():
 
 
 CONV_WORKLOADS = _conv_workloads()
+
+
+def _group_workloads():
+    """A mixture-of-experts layer: eight experts of one 4096 x 4096 f16
+    weight each (B row-major), a few to a hundred-odd token rows routed to
+    each (one expert gets none), uniform values; one seed per expert."""
+    rows = (3, 41, 17, 0, 96, 8, 150, 29)
+    return {"moe8_4096": [Problem(f"moe8_4096_e{i}", F16, m, 4096, 4096, dist="uniform", seed=300 + i)
+                          for i, m in enumerate(rows)]}
+
+
+GROUP_WORKLOADS = _group_workloads()

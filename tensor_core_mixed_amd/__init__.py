@@ -21,6 +21,7 @@ TCM_A_COLMAJOR, TCM_B_COLMAJOR = 1 << 8, 1 << 9
 TCM_C_F16, TCM_C_BF16 = 1 << 10, 1 << 11
 TCM_EPI_NONE, TCM_EPI_BIAS, TCM_EPI_RELU, TCM_EPI_BIAS_RELU, TCM_EPI_ACCUM = 0, 1, 2, 3, 4
 TCM_OK, TCM_ERR_INVALID_VALUE, TCM_ERR_NOT_SUPPORTED, TCM_ERR_HIP, TCM_ERR_ALLOC = 0, 1, 2, 3, 4
+TCM_MAX_GROUP = 32
 
 
 class TcmError(RuntimeError):
@@ -34,6 +35,13 @@ class _PlanInfo(ctypes.Structure):
                 ("bn", ctypes.c_int32), ("bk", ctypes.c_int32), ("mode", ctypes.c_int32), ("grid", ctypes.c_int32),
                 ("tiles", ctypes.c_int64), ("iters_per_tile", ctypes.c_int64), ("dp_tiles", ctypes.c_int64),
                 ("sk_tiles", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64)]
+
+
+class GroupEntry(ctypes.Structure):
+    """tcm_group_entry: one product of a group (device addresses as ints)."""
+    _fields_ = [("M", ctypes.c_int64), ("N", ctypes.c_int64), ("A", ctypes.c_void_p), ("lda", ctypes.c_int64),
+                ("B", ctypes.c_void_p), ("ldb", ctypes.c_int64), ("C", ctypes.c_void_p), ("ldc", ctypes.c_int64),
+                ("bias", ctypes.c_void_p)]
 
 
 _lib = None
@@ -52,6 +60,8 @@ def lib():
         L.tcm_gemm.restype = ci
         L.tcm_gemm_batched.argtypes = [i64, i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64, ci, vp, i64, ci, vp]
         L.tcm_gemm_batched.restype = ci
+        L.tcm_gemm_grouped.argtypes = [i64, ctypes.POINTER(GroupEntry), i64, ci, ci, vp]
+        L.tcm_gemm_grouped.restype = ci
         L.tcm_conv2d.argtypes = [i64] * 13 + [vp, vp, vp, ci, vp, ci, vp]
         L.tcm_conv2d.restype = ci
         L.tcm_status_string.argtypes = [ci]
@@ -183,6 +193,15 @@ def tcm_last_plan():
 
 def tcm_release_workspace():
     lib().tcm_release_workspace()
+
+
+def tcm_gemm_grouped(entries, K, dtype, epilogue, stream):
+    """`entries`: a sequence of GroupEntry (or of 9-tuples M, N, A, lda, B,
+    ldb, C, ldc, bias).  Returns the tcm status code."""
+    arr = (GroupEntry * max(len(entries), 1))()
+    for i, e in enumerate(entries):
+        arr[i] = e if isinstance(e, GroupEntry) else GroupEntry(*e)
+    return lib().tcm_gemm_grouped(len(entries), arr, K, dtype, epilogue, stream)
 
 
 def tcm_conv2d(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w, x, f, y, dtype, bias, epilogue,
@@ -353,3 +372,52 @@ def conv2d(x, f, bias=None, relu=False, padding=0, stride=1, dilation=1, out_dty
     if st != TCM_OK:
         raise TcmError(st, "tcm_conv2d")
     return y
+
+
+def gemm_grouped(As, Bs, Cs=None, biases=None, relu=False, accumulate=False, out_dtype=None, stream=None):
+    """Cs[e] = relu?(As[e] @ Bs[e] + biases[e] [+ Cs[e]]) for every e, via tcm_gemm_grouped.
+
+    As[e]: (M_e, K) and Bs[e]: (K, N_e) CUDA tensors of one type, row- or
+    column-major views (one layout for all entries of a kind); Cs: optional
+    row-major outputs; biases: optional list of length-N_e vectors.  Other
+    arguments as gemm().  Returns the list of C tensors."""
+    import torch
+    if not As or len(As) != len(Bs) or len(As) > TCM_MAX_GROUP:
+        raise ValueError(f"As and Bs: 1..{TCM_MAX_GROUP} matching entries")
+    code = _torch_dtype_code(As[0])
+    K = As[0].shape[1]
+    acc_dtype = torch.int32 if code == TCM_I8_I32 else torch.float32
+    if accumulate and Cs is None:
+        raise ValueError("accumulate needs Cs")
+    outs, ents, flags = [], [], set()
+    for i, (A, B) in enumerate(zip(As, Bs)):
+        if A.dtype != As[0].dtype or B.dtype != As[0].dtype:
+            raise TypeError("every A and B must have the same dtype")
+        M, Ka = A.shape
+        Kb, N = B.shape
+        if Ka != K or Kb != K:
+            raise ValueError("every entry must share K")
+        lda, a_col = _layout(A, "A")
+        ldb, b_col = _layout(B, "B")
+        C = Cs[i] if Cs is not None else torch.empty((M, N), dtype=out_dtype or acc_dtype, device=A.device)
+        c_flags = {torch.float16: TCM_C_F16, torch.bfloat16: TCM_C_BF16}.get(C.dtype, 0)
+        if (C.dtype != acc_dtype and not c_flags) or tuple(C.shape) != (M, N) or (N > 1 and C.stride(1) != 1):
+            raise ValueError("each C must be a row-major (M, N) tensor of the accumulator type, float16 or bfloat16")
+        bias = biases[i] if biases is not None else None
+        if bias is not None and (bias.dtype != acc_dtype or bias.numel() < N or not bias.is_contiguous()):
+            raise ValueError("each bias must be a contiguous length-N vector of the accumulator type")
+        flags.add((a_col, b_col, c_flags))
+        ents.append(GroupEntry(M, N, A.data_ptr(), lda, B.data_ptr(), ldb, C.data_ptr(), max(C.stride(0), N, 1),
+                               bias.data_ptr() if bias is not None else None))
+        outs.append(C)
+    if len(flags) != 1:
+        raise ValueError("every entry must have the same layouts and output type")
+    a_col, b_col, c_flags = flags.pop()
+    dtype = code | (TCM_A_COLMAJOR if a_col else 0) | (TCM_B_COLMAJOR if b_col else 0) | c_flags
+    epi = (TCM_EPI_BIAS if biases is not None else 0) | (TCM_EPI_RELU if relu else 0) | (TCM_EPI_ACCUM if accumulate else 0)
+    if stream is None:
+        stream = torch.cuda.current_stream(As[0].device).cuda_stream
+    st = tcm_gemm_grouped(ents, K, dtype, epi, stream)
+    if st != TCM_OK:
+        raise TcmError(st, "tcm_gemm_grouped")
+    return outs

@@ -125,10 +125,17 @@ struct Estimate {
     int64_t dp_tiles, sk_tiles;
 };
 
-Estimate estimate(const Problem& p, const TileConfig& c, int cus, int force_mode, int sk_grid, int sk_occ_known) {
+// Tiles of the work list for config ci.
+int64_t tile_count(const Problem& p, int ci) {
+    const TileConfig& c = kConfigs[ci];
+    return p.group ? p.group_tiles[ci] : cdiv(p.M, c.bm) * cdiv(p.N, c.bn) * std::max<int64_t>(p.batch, 1);
+}
+
+Estimate estimate(const Problem& p, int ci, int cus, int force_mode, int sk_grid, int sk_occ_known) {
+    const TileConfig& c = kConfigs[ci];
     const int dt = p.dtype;
     const int bke = bk_elems(dt);
-    const int64_t T = cdiv(p.M, c.bm) * cdiv(p.N, c.bn) * std::max<int64_t>(p.batch, 1);
+    const int64_t T = tile_count(p, ci);
     const int64_t I = cdiv(p.K, bke);
     const int occ = tile_wg_per_cu(c);
     const int64_t slots = (int64_t)cus * occ;
@@ -222,8 +229,8 @@ bool make_plan(const Problem& p, const Options& o, int cus, Plan* out) {
     if (!o.generic) {
         for (int c = 0; c < kNumConfigs; ++c) {
             if (o.force_config >= 0 && c != o.force_config) continue;
-            if (!tile_eligible(p, kConfigs[c])) continue;
-            Estimate e = estimate(p, kConfigs[c], cus, o.force_mode, o.sk_grid, o.sk_occ[c]);
+            if (p.group ? !p.group_ok[c] : !tile_eligible(p, kConfigs[c])) continue;
+            Estimate e = estimate(p, c, cus, o.force_mode, o.sk_grid, o.sk_occ[c]);
             if (e.cycles < best_e.cycles * 0.999) {
                 best = c;
                 best_e = e;
@@ -255,7 +262,7 @@ bool make_plan(const Problem& p, const Options& o, int cus, Plan* out) {
     pl.bm = c.bm;
     pl.bn = c.bn;
     pl.bk = bk_elems(p.dtype);
-    pl.tiles = cdiv(p.M, c.bm) * cdiv(p.N, c.bn) * std::max<int64_t>(p.batch, 1);
+    pl.tiles = tile_count(p, best);
     pl.iters = cdiv(p.K, pl.bk);
     pl.mode = best_e.mode;
     pl.est_cycles = best_e.cycles;

@@ -28,6 +28,12 @@ struct Problem {
     // conv_x_bytes bytes and conv_c channels (lda is nominal)
     bool conv = false;
     int64_t conv_c = 0, conv_x_bytes = 0;
+    // a group of products sharing K (its M is the entries' total, N their
+    // largest): the work list's exact tile count and the tiled kernel's
+    // eligibility, per config, computed over the entries
+    bool group = false;
+    int64_t group_tiles[kNumConfigs] = {0};
+    bool group_ok[kNumConfigs] = {false};
 };
 
 struct Plan {

@@ -33,6 +33,21 @@ int conv_sk_occupancy_bf16(int config);
 int conv_sk_occupancy_f32(int config);
 int conv_sk_occupancy_i8(int config);
 
+GroupLauncher group_launcher_f16(int config, bool b_kmajor);
+GroupLauncher group_launcher_bf16(int config, bool b_kmajor);
+GroupLauncher group_launcher_f32(int config, bool b_kmajor);
+GroupLauncher group_launcher_i8(int config, bool b_kmajor);
+
+GroupLauncher group_launcher(int config, int dtype, bool b_kmajor) {
+    switch (dtype) {
+    case F16: return group_launcher_f16(config, b_kmajor);
+    case BF16: return group_launcher_bf16(config, b_kmajor);
+    case F32: return group_launcher_f32(config, b_kmajor);
+    case I8: return group_launcher_i8(config, b_kmajor);
+    default: return nullptr;
+    }
+}
+
 TileLauncher conv_launcher(int config, int dtype) {
     switch (dtype) {
     case F16: return conv_launcher_f16(config);
@@ -137,8 +152,8 @@ Options plan_options(const Problem& p) {
     {
         std::lock_guard<std::mutex> lk(g_mu);
         o = g_opts;
-        // tuned entries describe GEMM calls; a convolution is planned afresh
-        if (g_use_tuned && !p.conv && o.force_config < 0 && o.force_mode == 0) {
+        // tuned entries describe single GEMM calls; a convolution or a group is planned afresh
+        if (g_use_tuned && !p.conv && !p.group && o.force_config < 0 && o.force_mode == 0) {
             auto it = g_tune.find(tune_key(p));
             if (it != g_tune.end()) {
                 o.force_config = it->second.config;
@@ -687,6 +702,138 @@ int conv_impl(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R, 
     return launch_tiled(p, pl, a, dev, stream);
 }
 
+// A group of products sharing K, dtype and epilogue (tcm_gemm_grouped).
+static_assert(kMaxGroup == TCM_MAX_GROUP, "the header's group limit is the kernel's");
+int grouped_impl(int64_t count, const tcm_group_entry* ent, int64_t K, int dtype, int epilogue, void* stream) {
+    if (count < 0 || count > kMaxGroup || (count > 0 && !ent)) return TCM_ERR_INVALID_VALUE;
+    Problem pe[kMaxGroup];
+    int64_t a_ext[kMaxGroup], b_ext[kMaxGroup], c_ext[kMaxGroup];
+    const bool use_bias = epilogue & TCM_EPI_BIAS;
+    int64_t M_total = 0, N_max = 0;
+    bool aligned = true, work = false;
+    for (int64_t i = 0; i < count; ++i) {
+        const tcm_group_entry& x = ent[i];
+        int st = check_problem(x.M, x.N, K, x.lda, x.ldb, x.ldc, dtype, epilogue, &pe[i]);
+        if (st != TCM_OK) return st;
+        const Problem& p = pe[i];
+        const int es = elem_bytes(p.dtype), cs = c_elem_bytes(p.c_type);
+        a_ext[i] = extent(p.a_col ? K : x.M, p.a_col ? x.M : K, x.lda) * es;
+        b_ext[i] = extent(p.b_col ? x.N : K, p.b_col ? K : x.N, x.ldb) * es;
+        c_ext[i] = extent(x.M, x.N, x.ldc) * cs;
+        if (x.M == 0 || x.N == 0) continue;  // nothing read or written
+        work = true;
+        if (!x.C || (a_ext[i] > 0 && !x.A) || (b_ext[i] > 0 && !x.B) || (use_bias && !x.bias)) return TCM_ERR_INVALID_VALUE;
+        if (((uintptr_t)x.A % es) || ((uintptr_t)x.B % es) || ((uintptr_t)x.C % cs) || (use_bias && ((uintptr_t)x.bias % 4)))
+            return TCM_ERR_INVALID_VALUE;
+        aligned = aligned && (uintptr_t)x.A % 16 == 0 && (uintptr_t)x.B % 16 == 0 && (uintptr_t)x.C % 16 == 0 &&
+                  (!use_bias || (uintptr_t)x.bias % 16 == 0);
+        M_total += x.M;
+        N_max = std::max(N_max, x.N);
+    }
+    // every C is written: it must not overlap any entry's inputs or another C
+    for (int64_t i = 0; i < count; ++i) {
+        if (ent[i].M == 0 || ent[i].N == 0) continue;
+        for (int64_t j = 0; j < count; ++j) {
+            if (ent[j].M == 0 || ent[j].N == 0) continue;
+            if (overlaps(ent[i].C, c_ext[i], ent[j].A, a_ext[j]) || overlaps(ent[i].C, c_ext[i], ent[j].B, b_ext[j]) ||
+                (use_bias && overlaps(ent[i].C, c_ext[i], ent[j].bias, ent[j].N * 4)) ||
+                (i != j && overlaps(ent[i].C, c_ext[i], ent[j].C, c_ext[j])))
+                return TCM_ERR_INVALID_VALUE;
+        }
+    }
+    if (!work) {
+        t_last_plan = "empty problem";
+        return TCM_OK;
+    }
+    // plan over the whole work list: exact tile counts and eligibility per config
+    Problem p = pe[0];
+    p.M = M_total;
+    p.N = N_max;
+    p.lda = p.ldb = p.ldc = 1;  // per entry; the group fields below decide
+    p.aligned = aligned;
+    p.group = true;
+    for (int c = 0; c < kNumConfigs; ++c) {
+        int64_t tiles = 0;
+        bool ok = aligned;
+        for (int64_t i = 0; i < count && ok; ++i) {
+            if (ent[i].M == 0 || ent[i].N == 0) continue;
+            Problem q = pe[i];
+            q.aligned = aligned;
+            ok = tile_eligible(q, kConfigs[c]);
+            tiles += ((ent[i].M + kConfigs[c].bm - 1) / kConfigs[c].bm) * ((ent[i].N + kConfigs[c].bn - 1) / kConfigs[c].bn);
+        }
+        p.group_ok[c] = ok && tiles < ((int64_t)1 << 31);
+        p.group_tiles[c] = tiles;
+    }
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return TCM_ERR_HIP;
+    }
+    Options o = plan_options(p);
+    fill_sk_occupancy(p, &o);
+    Plan pl;
+    if (!make_plan(p, o, device_cus(dev), &pl)) return TCM_ERR_INVALID_VALUE;
+    if (pl.kernel != 2) {
+        // no tile config serves every entry: each runs on its own (the
+        // generic kernel where the tiled one cannot take it)
+        for (int64_t i = 0; i < count; ++i) {
+            const tcm_group_entry& x = ent[i];
+            int st = gemm_impl(1, x.M, x.N, K, x.A, x.lda, 0, x.B, x.ldb, 0, x.C, x.ldc, 0, dtype, x.bias, 0, epilogue,
+                               stream);
+            if (st != TCM_OK) return st;
+        }
+        t_last_plan = "kernel=generic group=" + std::to_string(count) + " (entries one by one)";
+        return TCM_OK;
+    }
+    t_last_plan = describe(pl, p) + " group=" + std::to_string(count);
+
+    GroupArgs g{};
+    TileArgs& a = g.t;
+    a.K = (int)K;
+    a.relu = (epilogue & TCM_EPI_RELU) != 0;
+    a.has_bias = use_bias;
+    a.accum = (epilogue & TCM_EPI_ACCUM) != 0;
+    a.c_type = p.c_type;
+    a.batch = 1;
+    a.iters = (int)pl.iters;
+    a.dp_tiles = (int)pl.dp_tiles;
+    a.sk_tiles = (int)pl.sk_tiles;
+    a.grid = pl.grid;
+    a.group_m = pl.group_m;
+    int64_t tile0 = 0;
+    for (int64_t i = 0; i < count; ++i) {
+        const tcm_group_entry& x = ent[i];
+        if (x.M == 0 || x.N == 0) continue;
+        GroupEntry& y = g.e[g.count++];
+        y.A = x.A;
+        y.B = x.B;
+        y.C = x.C;
+        y.bias = use_bias ? x.bias : nullptr;
+        y.M = (int)x.M;
+        y.N = (int)x.N;
+        y.lda = (int)x.lda;
+        y.ldb = (int)x.ldb;
+        y.ldc = (int)x.ldc;
+        y.tiles_m = (int)((x.M + pl.bm - 1) / pl.bm);
+        y.tiles_n = (int)((x.N + pl.bn - 1) / pl.bn);
+        tile_order_shape(y.tiles_m, y.tiles_n, pl.group_m, &y.super_m, &y.super_n);
+        y.tile0 = (int)tile0;
+        tile0 += (int64_t)y.tiles_m * y.tiles_n;
+    }
+    if (tile0 != pl.tiles) return TCM_ERR_INVALID_VALUE;  // the plan and the table disagree (cannot happen)
+    if (pl.mode == 2 && pl.sk_tiles > 0) {
+        Workspace w;
+        int ws = get_workspace(dev, stream, pl.ws_partial_bytes, pl.ws_counters, &w);
+        if (ws != TCM_OK) return ws;
+        a.ws_partial = (float*)w.partial;
+        a.ws_counter = w.counters;
+    }
+    GroupLauncher launch = group_launcher(pl.config, p.dtype, p.b_col);
+    if (!launch) return TCM_ERR_NOT_SUPPORTED;
+    return launch(g, stream) == 0 ? TCM_OK : TCM_ERR_HIP;
+}
+
 }  // namespace
 }  // namespace tcm
 
@@ -695,6 +842,10 @@ extern "C" {
 int tcm_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
              int dtype, const void* bias, int epilogue, void* stream) {
     return gemm_impl(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, dtype, bias, 0, epilogue, stream);
+}
+
+int tcm_gemm_grouped(int64_t count, const tcm_group_entry* entries, int64_t K, int dtype, int epilogue, void* stream) {
+    return grouped_impl(count, entries, K, dtype, epilogue, stream);
 }
 
 int tcm_conv2d(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R, int64_t S, int64_t pad_h, int64_t pad_w,

@@ -174,8 +174,33 @@ struct GenericArgs {
     int64_t cv_pad_h, cv_pad_w, cv_stride_h, cv_stride_w, cv_dil_h, cv_dil_w;
 };
 
+// A group of products that share K, the element type and the epilogue but
+// not their shapes or operands (tcm_gemm_grouped).  The tiles of all entries
+// form one work list, entry after entry; the table travels in the kernel
+// arguments, so a group holds at most kMaxGroup entries.
+constexpr int kMaxGroup = 32;
+struct GroupEntry {
+    const void* A;
+    const void* B;
+    void* C;
+    const void* bias;
+    int M, N;
+    int lda, ldb, ldc;
+    int tiles_m, tiles_n;   // of this entry
+    int super_m, super_n;   // its tile walk
+    int tile0;              // its first tile in the work list
+};
+struct GroupArgs {
+    TileArgs t;             // what the entries share: K, epilogue, C type, schedule, workspace
+    int count;              // entries, 1 .. kMaxGroup
+    GroupEntry e[kMaxGroup];
+};
+
 // Launchers (defined next to the kernels).  Return hipError_t as int.
 using TileLauncher = int (*)(const TileArgs&, void* stream);
+using GroupLauncher = int (*)(const GroupArgs&, void* stream);
+// the grouped kernels: config index, dtype, B column-major -> launcher
+GroupLauncher group_launcher(int config, int dtype, bool b_kmajor);
 // config index, dtype, B column-major (K-contiguous) -> launcher, or nullptr
 TileLauncher tile_launcher(int config, int dtype, bool b_kmajor);
 // the implicit-GEMM convolution kernels (B = the KRSC filter, k-contiguous)

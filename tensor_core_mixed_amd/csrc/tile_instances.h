@@ -1,6 +1,7 @@
 // Instantiates the tiled kernel for every (tile config, B layout) of one
-// element type, and the implicit-GEMM convolution kernel for every tile
-// config; each (kernel, element type) is compiled in its own translation unit.
+// element type, its grouped form likewise, and the implicit-GEMM convolution
+// kernel for every tile config; each (kernel, element type) is compiled in
+// its own translation unit.
 #pragma once
 #include "tile_kernel.h"
 
@@ -58,6 +59,19 @@ int pick_conv_occupancy(int config) {
     }
 }
 
+template <int DT>
+GroupLauncher pick_group(int config, bool b_kmajor) {
+    switch (config) {
+    case 0: return b_kmajor ? &launch_group<DT, 0, true> : &launch_group<DT, 0, false>;
+    case 1: return b_kmajor ? &launch_group<DT, 1, true> : &launch_group<DT, 1, false>;
+    case 2: return b_kmajor ? &launch_group<DT, 2, true> : &launch_group<DT, 2, false>;
+    case 3: return b_kmajor ? &launch_group<DT, 3, true> : &launch_group<DT, 3, false>;
+    case 4: return b_kmajor ? &launch_group<DT, 4, true> : &launch_group<DT, 4, false>;
+    case 5: return b_kmajor ? &launch_group<DT, 5, true> : &launch_group<DT, 5, false>;
+    default: return nullptr;
+    }
+}
+
 }  // namespace tcm
 
 #define TCM_TILE_TU(DT, NAME)                                                                          \
@@ -70,4 +84,9 @@ int pick_conv_occupancy(int config) {
     namespace tcm {                                                                               \
     TileLauncher conv_launcher_##NAME(int config) { return pick_conv<DT>(config); }               \
     int conv_sk_occupancy_##NAME(int config) { return pick_conv_occupancy<DT>(config); }          \
+    }
+
+#define TCM_GROUP_TU(DT, NAME)                                                                        \
+    namespace tcm {                                                                                   \
+    GroupLauncher group_launcher_##NAME(int config, bool b_kmajor) { return pick_group<DT>(config, b_kmajor); } \
     }

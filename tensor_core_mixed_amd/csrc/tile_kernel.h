@@ -404,6 +404,42 @@ struct TileKernel {
         return e;
     }
 
+    // The tile at position n of a group's work list: the entry whose first
+    // tile is the last at or before n (entries without tiles are left out
+    // of the table), then that entry's own tile walk.  The table lives in
+    // the kernel arguments: a scalar scan, unrolled so every index is static.
+    __device__ __forceinline__ static TileArgs tile_of(const GroupArgs& g, int n, int& tm, int& tn) {
+        TileArgs e = g.t;
+        int tile0 = 0, sm = 1, sn = 1;
+#pragma unroll
+        for (int i = 0; i < kMaxGroup; ++i) {
+            if (i < g.count && n >= g.e[i].tile0) {
+                const GroupEntry& x = g.e[i];
+                e.A = x.A;
+                e.B = x.B;
+                e.C = x.C;
+                e.bias = x.bias;
+                e.M = x.M;
+                e.N = x.N;
+                e.lda = x.lda;
+                e.ldb = x.ldb;
+                e.ldc = x.ldc;
+                e.tiles_m = x.tiles_m;
+                e.tiles_n = x.tiles_n;
+                tile0 = x.tile0;
+                sm = x.super_m;
+                sn = x.super_n;
+            }
+        }
+        tcm::super_order(n - tile0, e.tiles_m, e.tiles_n, g.t.group_m, sm, sn, &tm, &tn);
+        return e;
+    }
+    __device__ __forceinline__ static const TileArgs& base_args(const TileArgs& a) { return a; }
+    __device__ __forceinline__ static const TileArgs& base_args(const GroupArgs& g) { return g.t; }
+    // tiles in the work list
+    __device__ __forceinline__ static int work_tiles(const TileArgs& a) { return a.tiles_m * a.tiles_n * a.batch; }
+    __device__ __forceinline__ static int work_tiles(const GroupArgs& g) { return g.t.dp_tiles + g.t.sk_tiles; }
+
     // ------------------------------------------------------- epilogue
     // 32x32 accumulator layout: lane l, register r holds row
     // 8*(r/4) + 4*(l/32) + r%4 and column l%32 of its MFMA tile.  C is read
@@ -687,7 +723,8 @@ struct TileKernel {
 
 
     // Data-parallel kernel: workgroup b computes tile b (in L2-aware order).
-    __device__ __forceinline__ static void run_dp(const TileArgs& a) {
+    template <class Args>
+    __device__ __forceinline__ static void run_dp(const Args& g) {
         __shared__ __attribute__((aligned(1024))) char smem_raw[LDS];
         lds_char* smem = (lds_char*)smem_raw;
         const int tid = threadIdx.x, lane = tid & 63;
@@ -695,7 +732,7 @@ struct TileKernel {
         const int wm = wave / WN, wn = wave % WN;
         Acc acc[FM][FN];
         int tm, tn;
-        const TileArgs e = tile_of(a, xcd_order(blockIdx.x, a.tiles_m * a.tiles_n * a.batch), tm, tn);
+        const TileArgs e = tile_of(g, xcd_order(blockIdx.x, work_tiles(g)), tm, tn);
         const int m0 = tm * BM, n0 = tn * BN;
         init_acc(acc, e, true, m0, n0, wm, wn, lane);
         mainloop(acc, e, smem, m0, n0, 0, e.iters, wave, lane);
@@ -707,7 +744,9 @@ struct TileKernel {
     // [it0, it1) tile segment by tile segment.  The grid is never larger than
     // the number of iterations, so every workgroup owns at least one and the
     // workgroups holding a split tile are exactly its first owner .. last owner.
-    __device__ __forceinline__ static void run_sk(const TileArgs& a) {
+    template <class Args>
+    __device__ __forceinline__ static void run_sk(const Args& g) {
+        const TileArgs& a = base_args(g);
         __shared__ __attribute__((aligned(1024))) char smem_raw[LDS];
         __shared__ int s_flag;
         lds_char* smem = (lds_char*)smem_raw;
@@ -725,7 +764,7 @@ struct TileKernel {
             const int k_lo = (int)(it - tsk * I);
             const int k_hi = (int)min<int64_t>(I, k_lo + (it1 - it));
             int tm, tn;
-            const TileArgs e = tile_of(a, xcd_order(a.dp_tiles + (int)tsk, a.tiles_m * a.tiles_n * a.batch), tm, tn);
+            const TileArgs e = tile_of(g, xcd_order(a.dp_tiles + (int)tsk, work_tiles(g)), tm, tn);
             const int m0 = tm * BM, n0 = tn * BN;
             init_acc(acc, e, k_lo == 0, m0, n0, wm, wn, lane);
             mainloop(acc, e, smem, m0, n0, k_lo, k_hi, wave, lane);
@@ -737,7 +776,7 @@ struct TileKernel {
             // Split tile: publish this segment (every wave waits until its
             // partial stores are acknowledged), then count the arrival.
             const int slot = 2 * wg + (tsk == first_tile ? 0 : 1);
-            store_partial(acc, partial_rsrc(a, slot), wave, wm, lane, a.M - m0);
+            store_partial(acc, partial_rsrc(a, slot), wave, wm, lane, e.M - m0);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             // workgroups holding a segment of tile tsk: owners of its first and last iteration
@@ -761,7 +800,7 @@ struct TileKernel {
                 // workgroups a CU holds
                 for (int w = w_first; w <= w_last; ++w) {
                     Partial pw;
-                    load_partial(pw, partial_rsrc(a, slot_of(w)), wave, wm, lane, a.M - m0);
+                    load_partial(pw, partial_rsrc(a, slot_of(w)), wave, wm, lane, e.M - m0);
                     add_partial(acc, pw, w == w_first);
                 }
                 store_tile(acc, e, m0, n0, wm, wn, lane);
@@ -778,7 +817,7 @@ struct TileKernel {
                     Partial pb[NB];
 #pragma unroll
                     for (int j = 0; j < NB; ++j)
-                        if (w0 + j <= w_last) load_partial(pb[j], partial_rsrc(a, slot_of(w0 + j)), wave, wm, lane, a.M - m0);
+                        if (w0 + j <= w_last) load_partial(pb[j], partial_rsrc(a, slot_of(w0 + j)), wave, wm, lane, e.M - m0);
 #pragma unroll
                     for (int j = 0; j < NB; ++j)
                         if (w0 + j <= w_last) add_partial(acc, pb[j], w0 + j == w_first);
@@ -789,12 +828,12 @@ struct TileKernel {
             }
             // (unrolled by two so both buffers stay in registers)
             Partial p0, p1;
-            load_partial(p0, partial_rsrc(a, slot_of(w_first)), wave, wm, lane, a.M - m0);
+            load_partial(p0, partial_rsrc(a, slot_of(w_first)), wave, wm, lane, e.M - m0);
             for (int w = w_first; w <= w_last; w += 2) {
-                if (w + 1 <= w_last) load_partial(p1, partial_rsrc(a, slot_of(w + 1)), wave, wm, lane, a.M - m0);
+                if (w + 1 <= w_last) load_partial(p1, partial_rsrc(a, slot_of(w + 1)), wave, wm, lane, e.M - m0);
                 add_partial(acc, p0, w == w_first);
                 if (w + 1 > w_last) break;
-                if (w + 2 <= w_last) load_partial(p0, partial_rsrc(a, slot_of(w + 2)), wave, wm, lane, a.M - m0);
+                if (w + 2 <= w_last) load_partial(p0, partial_rsrc(a, slot_of(w + 2)), wave, wm, lane, e.M - m0);
                 add_partial(acc, p1, false);
             }
             store_tile(acc, e, m0, n0, wm, wn, lane);
@@ -845,6 +884,24 @@ int launch_tile(const TileArgs& a, void* stream) {
         hipLaunchKernelGGL((tile_gemm_kernel<DT, CFG, B_KMAJ, false>), dim3(a.dp_tiles), dim3(TileThreads<CFG>::value), 0, s, a);
     if (a.sk_tiles > 0)
         hipLaunchKernelGGL((tile_gemm_kernel<DT, CFG, B_KMAJ, true>), dim3(a.grid), dim3(TileThreads<CFG>::value), 0, s, a);
+    return (int)hipGetLastError();
+}
+
+// A group of products on one work list (the tiles of each entry in turn).
+template <int DT, int CFG, bool B_KMAJ, bool SK>
+__global__ __launch_bounds__(TileThreads<CFG>::value) __attribute__((amdgpu_waves_per_eu(TileWaves<CFG, SK>::value)))
+void tile_group_kernel(GroupArgs g) {
+    if constexpr (SK) TileKernel<DT, CFG, B_KMAJ, false, kConfigs[CFG].sk_stages>::run_sk(g);
+    else TileKernel<DT, CFG, B_KMAJ>::run_dp(g);
+}
+
+template <int DT, int CFG, bool B_KMAJ>
+int launch_group(const GroupArgs& g, void* stream) {
+    hipStream_t s = (hipStream_t)stream;
+    if (g.t.dp_tiles > 0)
+        hipLaunchKernelGGL((tile_group_kernel<DT, CFG, B_KMAJ, false>), dim3(g.t.dp_tiles), dim3(TileThreads<CFG>::value), 0, s, g);
+    if (g.t.sk_tiles > 0)
+        hipLaunchKernelGGL((tile_group_kernel<DT, CFG, B_KMAJ, true>), dim3(g.t.grid), dim3(TileThreads<CFG>::value), 0, s, g);
     return (int)hipGetLastError();
 }
 

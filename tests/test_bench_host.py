@@ -69,7 +69,7 @@ def test_kernel_hash_covers_the_tiled_kernel_sources():
     stored counters describe) is in the hash: their instantiations, the
     template and the shared argument / tile-table header."""
     csrc = os.path.join(ROOT, "tensor_core_mixed_amd", "csrc")
-    tiled = {f for f in os.listdir(csrc) if f.startswith(("tile_", "conv_"))} | {"tcm_internal.h"}
+    tiled = {f for f in os.listdir(csrc) if f.startswith(("tile_", "conv_", "group_"))} | {"tcm_internal.h"}
     assert tiled == set(bench.KERNEL_SOURCES)
 
 

@@ -386,3 +386,34 @@ def test_conv_empty_and_valid_without_device():
     for kw in (dict(), dict(C=3), dict(stride_h=2, stride_w=3, dil_h=2, dil_w=2), dict(dtype=T.TCM_BF16_F32 | T.TCM_C_BF16),
                dict(epilogue=T.TCM_EPI_BIAS | T.TCM_EPI_RELU, bias=4 << 20), dict(dtype=T.TCM_I8_I32), dict(C=0)):
         assert _conv(**kw) == T.TCM_ERR_HIP, kw
+
+
+def _gentry(M=64, N=64, A=1 << 20, lda=64, B=2 << 20, ldb=64, C=3 << 20, ldc=64, bias=0):
+    return T.GroupEntry(M, N, A or None, lda, B or None, ldb, C or None, ldc, bias or None)
+
+
+def test_grouped_invalid_arguments():
+    ok = [_gentry(), _gentry(A=4 << 20, B=5 << 20, C=6 << 20)]
+    assert T.tcm_gemm_grouped([_gentry()] * 33, 64, 0, 0, None) == T.TCM_ERR_INVALID_VALUE  # beyond the limit
+    assert T.lib().tcm_gemm_grouped(-1, None, 64, 0, 0, None) == T.TCM_ERR_INVALID_VALUE
+    assert T.lib().tcm_gemm_grouped(2, None, 64, 0, 0, None) == T.TCM_ERR_INVALID_VALUE
+    bad = [
+        [_gentry(lda=32)],                                   # lda < K
+        [_gentry(N=-1)],                                     # negative size
+        [_gentry(C=0)],                                      # NULL C
+        [_gentry(), _gentry(A=4 << 20, B=5 << 20, C=(3 << 20) + 64)],  # two C overlap
+        [_gentry(), _gentry(A=(3 << 20) + 128, B=5 << 20, C=6 << 20)],  # C of entry 0 overlaps A of entry 1
+        [_gentry(C=(3 << 20) + 2)],                          # f32 C not aligned to its element
+    ]
+    for ents in bad:
+        assert T.tcm_gemm_grouped(ents, 64, 0, 0, None) == T.TCM_ERR_INVALID_VALUE, ents
+    assert T.tcm_gemm_grouped(ok, 64, 0, T.TCM_EPI_BIAS, None) == T.TCM_ERR_INVALID_VALUE  # bias flag, no bias
+    assert T.tcm_gemm_grouped(ok, -1, 0, 0, None) == T.TCM_ERR_INVALID_VALUE
+
+
+def test_grouped_empty_and_valid_without_device():
+    assert T.tcm_gemm_grouped([], 64, 0, 0, None) == T.TCM_OK
+    # entries without rows or columns are skipped, NULL pointers and all
+    assert T.tcm_gemm_grouped([_gentry(M=0, A=0, B=0, C=0), _gentry(N=0, A=0, B=0, C=0)], 64, 0, 0, None) == T.TCM_OK
+    ok = [_gentry(), _gentry(M=17, A=4 << 20, B=5 << 20, C=6 << 20), _gentry(M=0, A=0, B=0, C=0)]
+    assert T.tcm_gemm_grouped(ok, 64, 0, 0, None) == T.TCM_ERR_HIP
