@@ -88,6 +88,19 @@ def describe(p):
             + (", bias + ReLU epilogue" if p.bias else ""))
 
 
+def roofline(dtype, flops, alg_bytes, ms, traffic):
+    """The bound of a launch from its algorithmic intensity: below the ridge
+    (MFMA peak / HBM peak) HBM bandwidth, above it the dtype's MFMA peak."""
+    ridge = PEAK[dtype] * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if flops / alg_bytes < ridge:
+        gbs = alg_bytes / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic}
+    value = flops / (ms * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK[dtype],
+            "unit": "TFLOP/s" if dtype != 3 else "TOP/s", "frac": round(value / PEAK[dtype], 4), "traffic": traffic}
+
+
 def describe_conv(p):
     acc = "int32" if p.dtype == 3 else "f32"
     out = acc if p.c_type == "acc" else p.c_type
@@ -470,9 +483,7 @@ def run_bench_conv(args):
     clock_after = gpu_clock()
     value = p.flops / (ms * 1e-3) / 1e12
     print(f"[bench] {ms:.4f} ms/step, {value:.1f} T(FL)OP/s", file=sys.stderr, flush=True)
-    roof = {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK[p.dtype],
-            "unit": "TFLOP/s" if p.dtype != 3 else "TOP/s", "frac": round(value / PEAK[p.dtype], 4),
-            "traffic": load_traffic(p, plan)}
+    roof = roofline(p.dtype, p.flops, p.alg_bytes, ms, load_traffic(p, plan))
     cpu, parity = None, None
     if not args.no_cpu:
         job.call()
@@ -496,6 +507,44 @@ def run_bench_conv(args):
     print(json.dumps(line), flush=True)
 
 
+def run_bench_group(args):
+    import torch
+
+    import synthetic as S
+    import tensor_core_mixed_amd as T
+    ps = S.GROUP_WORKLOADS[args.workload]
+    torch.cuda.set_device(0)
+    desc = (f"group of {len(ps)} f16 GEMMs sharing K={ps[0].K}, N={ps[0].N}, M = {[p.M for p in ps]}, "
+            f"B row-major, f32 accumulate and output")
+    print(f"[bench] workload {args.workload}: {desc}", file=sys.stderr, flush=True)
+    stream_obj = torch.cuda.current_stream()
+    job = GroupJob(ps, stream_obj.cuda_stream)
+    job.call()
+    torch.cuda.synchronize()
+    plan = T.tcm_last_plan()
+    print(f"[bench] plan: {plan}", file=sys.stderr, flush=True)
+    ms, wall_ms = time_steps(job.call, args.steps, args.warmup, stream_obj)
+    ms_each, _ = time_steps(job.call_each, args.steps, args.warmup, stream_obj)
+    value = job.flops / (ms * 1e-3) / 1e12
+    print(f"[bench] {ms:.4f} ms/step ({ms_each:.4f} one entry at a time), {value:.1f} TFLOP/s", file=sys.stderr,
+          flush=True)
+    parity = None
+    if not args.no_cpu:
+        job.call()
+        torch.cuda.synchronize()
+        parity = job.sampled_check()
+    line = {
+        "metric": "Grouped GEMM TFLOPS on 1 MI355X (one call for the whole group)",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": DTYPE_NAME[ps[0].dtype], "data": "synthetic",
+        "config": {"workload": desc, "plan": plan, "wall_ms_per_step": round(wall_ms, 5),
+                   "entries_one_by_one_ms": round(ms_each, 5), "parity": parity},
+        "roofline": roofline(ps[0].dtype, job.flops, job.alg_bytes, ms, None), "cpu_baseline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def run_bench(args):
     import torch
 
@@ -503,6 +552,8 @@ def run_bench(args):
     import tensor_core_mixed_amd as T
     if args.workload in S.CONV_WORKLOADS:
         return run_bench_conv(args)
+    if args.workload in S.GROUP_WORKLOADS:
+        return run_bench_group(args)
     p = S.workload(args.workload, **({"dist": args.dist} if args.dist else {}))
     torch.cuda.set_device(0)
     print(f"[bench] workload {p.name}: {describe(p)}", file=sys.stderr, flush=True)
@@ -524,9 +575,7 @@ def run_bench(args):
     unit_scale = 1e12
     value = flops / (ms * 1e-3) / unit_scale
     print(f"[bench] {ms:.4f} ms/step, {value:.1f} T(FL)OP/s", file=sys.stderr, flush=True)
-    roof = {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK[p.dtype],
-            "unit": "TFLOP/s" if p.dtype != 3 else "TOP/s", "frac": round(value / PEAK[p.dtype], 4),
-            "traffic": load_traffic(p, plan)}
+    roof = roofline(p.dtype, p.flops, p.alg_bytes, ms, load_traffic(p, plan))
     cpu, parity = None, None
     if not args.no_cpu:
         # CPU leg: one more call from the initial state, checked on sampled entries, then the oracle's rate

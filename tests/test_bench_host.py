@@ -77,3 +77,13 @@ def test_kernel_hash_ignores_comments_but_not_code():
     src = "int f(int x) {  // twice\n    /* a\n       block */\n    return 2 * x;\n}\n"
     assert bench._code_only(src) == bench._code_only(src.replace("twice", "double it").replace("a\n", "b\n"))
     assert bench._code_only(src) != bench._code_only(src.replace("2 * x", "3 * x"))
+
+
+def test_roofline_bound_follows_the_intensity():
+    big = S.workload("f16_8192")
+    r = bench.roofline(big.dtype, big.flops, big.alg_bytes, 0.9, None)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and 0 < r["frac"] < 1
+    skinny = S.workload("skinny_m16")
+    r = bench.roofline(skinny.dtype, skinny.flops, skinny.alg_bytes, 0.015, None)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == bench.HBM_PEAK_GBS
+    assert abs(r["achieved"] - skinny.alg_bytes / 15e-6 / 1e9) < 1
