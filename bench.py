@@ -22,6 +22,7 @@ import json
 import os
 import sys
 import time
+import types
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -69,13 +70,16 @@ def plan_kernels(plan):
     b = "true" if f.get("b_col") == "1" else "false"
     if f["kernel"] == "conv":
         head = f"void tcm::tile_conv_kernel<{f['dtype']}, {f['config']}, "
+    elif "group" in f:
+        head = f"void tcm::tile_group_kernel<{f['dtype']}, {f['config']}, {b}, "
     else:
         head = f"void tcm::tile_gemm_kernel<{f['dtype']}, {f['config']}, {b}, "
+    args = "(tcm::GroupArgs)" if "group" in f else "(tcm::TileArgs)"
     names = set()
     if int(f.get("dp_tiles", 0)) > 0:
-        names.add(head + "false>(tcm::TileArgs)")
+        names.add(head + "false>" + args)
     if int(f.get("sk_tiles", 0)) > 0:
-        names.add(head + "true>(tcm::TileArgs)")
+        names.add(head + "true>" + args)
     return names
 
 
@@ -540,7 +544,9 @@ def run_bench_group(args):
         "dtype": DTYPE_NAME[ps[0].dtype], "data": "synthetic",
         "config": {"workload": desc, "plan": plan, "wall_ms_per_step": round(wall_ms, 5),
                    "entries_one_by_one_ms": round(ms_each, 5), "parity": parity},
-        "roofline": roofline(ps[0].dtype, job.flops, job.alg_bytes, ms, None), "cpu_baseline": None,
+        "roofline": roofline(ps[0].dtype, job.flops, job.alg_bytes, ms,
+                             load_traffic(types.SimpleNamespace(name=args.workload), plan)),
+        "cpu_baseline": None,
     }
     print(json.dumps(line), flush=True)
 
@@ -801,7 +807,9 @@ def summarize_counters(d, name, calib=None):
         return vals
 
     # per kernel (a Stream-K plan launches a data-parallel and a Stream-K kernel): medians per dispatch
-    kpat = "tile_conv_kernel" if name.startswith("conv_") else "tile_gemm_kernel"
+    import synthetic as S
+    kpat = ("tile_conv_kernel" if name in S.CONV_WORKLOADS else
+            "tile_group_kernel" if name in S.GROUP_WORKLOADS else "tile_gemm_kernel")
     fetch = per_kernel(d, "fetch", "FETCH_SIZE", kpat)
     write = per_kernel(d, "write", "WRITE_SIZE", kpat)
     cf = per_dispatch_in(calib, "copy_fetch", "FETCH_SIZE", "copy")

@@ -35,6 +35,9 @@ def test_plan_kernels_names_the_launched_kernels():
     conv = HYBRID_PLAN.replace("kernel=tile", "kernel=conv").replace("b_col=0", "b_col=1")
     assert bench.plan_kernels(conv) == {"void tcm::tile_conv_kernel<0, 1, false>(tcm::TileArgs)",
                                         "void tcm::tile_conv_kernel<0, 1, true>(tcm::TileArgs)"}
+    group = HYBRID_PLAN + " group=8"
+    assert bench.plan_kernels(group) == {"void tcm::tile_group_kernel<0, 1, false, false>(tcm::GroupArgs)",
+                                         "void tcm::tile_group_kernel<0, 1, false, true>(tcm::GroupArgs)"}
 
 
 def _with_traffic(tmp_path, monkeypatch, record):
