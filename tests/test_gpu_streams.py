@@ -1,0 +1,91 @@
+"""Streams and graphs: calls on two streams at once (each stream has its own
+split-k workspace), and a captured HIP graph replayed several times with
+eager work in between, each replay checked against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import synthetic as S
+import tensor_core_mixed_amd as T
+from gpu_util import check, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _reset_options():
+    yield
+    T.tcm_set_option("force_mode", 0)
+    T.tcm_set_option("force_config", -1)
+    T.tcm_set_option("sk_grid", 0)
+
+
+def _dev(x):
+    return torch.from_numpy(x.view(np.int16).copy() if x.dtype == np.uint16 else x.copy()).cuda()
+
+
+class Call:
+    """One problem resident on the device, callable on a given stream."""
+
+    def __init__(self, p):
+        self.p, self.g = p, S.generate(p)
+        self.A, self.B = _dev(self.g["A"]), _dev(self.g["B"])
+        self.bias = _dev(self.g["bias"]) if self.g["bias"] is not None else None
+        self.C = torch.full((p.M, p.LDC), float("nan"), device="cuda")
+        self.code = p.dtype | (T.TCM_B_COLMAJOR if p.b_col else 0)
+        self.epi = (T.TCM_EPI_BIAS if p.bias else 0) | (T.TCM_EPI_RELU if p.relu else 0)
+
+    def __call__(self, stream):
+        p = self.p
+        st = T.tcm_gemm(p.M, p.N, p.K, self.A.data_ptr(), p.LDA, self.B.data_ptr(), p.LDB, self.C.data_ptr(), p.LDC,
+                        self.code, self.bias.data_ptr() if self.bias is not None else None, self.epi, stream.cuda_stream)
+        assert st == T.TCM_OK, T.tcm_status_string(st)
+
+    def check(self):
+        return check(self.p, self.g, self.C.cpu().numpy())
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_two_streams_at_once(mode):
+    T.tcm_set_option("force_mode", mode)
+    T.tcm_set_option("force_config", 4)
+    a = Call(S.small_problem(S.F16, 96, 320, 2048, seed=400, bias=True, relu=True))
+    b = Call(S.small_problem(S.F16, 160, 128, 1536, seed=401, bias=True))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    say(f"[case] two streams, mode {mode}")
+    for _ in range(3):  # several rounds, no synchronisation between the streams
+        a(s1)
+        b(s2)
+    torch.cuda.synchronize()
+    say(f"       plan: {T.tcm_last_plan()}")
+    a.check()
+    b.check()
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+def test_graph_capture_replays(mode):
+    """A call captured into a HIP graph (the split-k workspace already exists
+    for the stream, so capture allocates nothing) gives the eager result on
+    every replay; eager work and synchronisations run between the replays."""
+    T.tcm_set_option("force_mode", mode)
+    T.tcm_set_option("force_config", 4)
+    c = Call(S.small_problem(S.F16, 128, 256, 1024, seed=402, bias=True, relu=True))
+    s = torch.cuda.Stream()
+    c(s)  # warm-up: plans, and creates this stream's workspace
+    torch.cuda.synchronize()
+    eager = c.C.clone()
+    c.check()
+    say(f"[case] graph capture, mode {mode}: {T.tcm_last_plan()}")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        c(s)
+    for i in range(3):
+        c.C.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(torch.nan_to_num(c.C, nan=1e9), torch.nan_to_num(eager, nan=1e9)), f"replay {i} differs"
+        x = torch.randn(1024, device="cuda")  # unrelated eager work between the replays
+        (x @ x).item()
+    c.check()
