@@ -26,7 +26,11 @@
  * ready when the stream reaches the call.  Calls on one stream run in order.
  * The library's state is a cached split-k workspace per (device, stream),
  * so concurrent calls on different streams are independent, plus the
- * process-wide switches and tuning table below (mutex-protected).
+ * process-wide switches and tuning table below (mutex-protected).  The
+ * workspace grows on demand (hipMalloc, plus a zero-fill kernel for its
+ * counters); a call whose plan fits the stream's existing workspace
+ * allocates nothing and issues only kernel launches, so it can be captured
+ * into a HIP graph after one warm-up call of the same shape on that stream.
  *
  * Errors are returned, never raised; argument checks run before any HIP call.
  */
