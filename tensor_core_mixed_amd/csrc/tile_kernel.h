@@ -23,7 +23,10 @@
 //    the k-contiguous fragment directly from the [k][n] LDS tile.
 //  * Software pipelining (Step 5): NST LDS stages (two for data-parallel
 //    kernels, up to four for Stream-K); the copies of K-steps k+1 ..
-//    k+NST-1 are in flight while the MFMAs of step k run.
+//    k+NST-1 are in flight while the MFMAs of step k run.  The eight-wave
+//    kernel with an n-contiguous f16/bf16 B runs its two wave groups one
+//    phase apart instead (ping-pong: one wave per SIMD reads fragments while
+//    the other issues MFMAs).
 //  * Unrolled inner loop of matrix-core ops (Step 6; Tensor Core notes on
 //    je-d.tistory.com: mixed-precision multiply-accumulate per warp-level
 //    operation): v_mfma_f32_32x32x16_{f16,bf16}, v_mfma_i32_32x32x32_i8,
@@ -125,7 +128,8 @@ struct TileKernel {
     // copy and waves 4-7 none: waves go to the four SIMDs round-robin, so
     // each SIMD pairs one copier with a wave that only feeds the matrix
     // core while the copier's copies queue (8192^3 f16: 2% faster than all
-    // eight waves interleaving copies with their MFMAs).
+    // eight waves interleaving copies with their MFMAs).  The ping-pong loop
+    // splits the copies by operand between the two groups instead.
     static constexpr int NWC = (NW == 8 && !CONV) ? NW / 2 : NW;
     static constexpr int IA = BM / (8 * NWC);        // DMA instructions per copier wave per stage (A)
     static constexpr int IB = BN / (8 * NWC);        // (B)
@@ -203,15 +207,20 @@ struct TileKernel {
         return bytes <= 0 ? 0 : (bytes < (int64_t)kOOB ? (int)bytes : (int)kOOB);
     }
 
-    // Issue the copies of K-step kt of tile (m0, n0) into LDS stage `st`.
+    // Issue the copies of K-step kt of tile (m0, n0) into LDS stage `st`:
+    // those of operand A if OPS & 1, of operand B if OPS & 2.  With CHECK,
+    // waves past the copier waves return at once; without it the caller
+    // passes the copier slot (0 .. NWC-1) whose copies this wave issues.
+    template <int OPS = 3, bool CHECK = true>
     __device__ __forceinline__ static void dma_issue(const Dma& d, const TileArgs& a, lds_char* smem, int st, int kt,
                                                      int m0, int n0, int wave) {
-        if constexpr (NWC < NW) {
+        if constexpr (NWC < NW && CHECK) {
             if (wave >= NWC) return;
         }
         const int k0 = kt * BKE;
         const int krem = a.K - k0;
-        if constexpr (CONV) {
+        if constexpr (!(OPS & 1)) {
+        } else if constexpr (CONV) {
             // this K-step's filter tap (r, s) and first channel: uniform
             const int rs = k0 / a.cv_C, c0 = k0 - rs * a.cv_C;
             const int rr = rs / a.cv_S, ss = rs - rr * a.cv_S;
@@ -240,7 +249,7 @@ struct TileKernel {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(la + (j * NWC + wave) * 1024),
                                                          16, ((j & 1) ? o1 : o0) + (j >> 1) * hop, 0, 0, 0);
         }
-        {
+        if constexpr ((OPS & 2) != 0) {
             const char* base;
             int nrec;
             unsigned o0, o1;
@@ -692,10 +701,84 @@ struct TileKernel {
         else if constexpr (NEXT) sched_reads();
     }
 
+    // ------------------------------------------------- ping-pong main loop
+    // Eight-wave data-parallel kernel, n-contiguous B (f16 / bf16): waves
+    // 0-3 (group A) and 4-7 (group B) sit one of each per SIMD and run the
+    // same loop one phase apart, phases separated by workgroup barriers.  In
+    // a memory phase a wave reads all fragments of one K-step from LDS; in a
+    // compute phase it issues that step's MFMAs.  While one wave of a SIMD
+    // waits on LDS, its partner keeps the matrix core fed.  This pays where
+    // fragment reads are many: the transpose reads of an n-contiguous B tile
+    // return 8 bytes per lane, twice the LDS instructions of a k-contiguous
+    // one (8192^3 f16: 915 against 1023 us).  With k-contiguous B the
+    // interleaved loop below is faster (880 against 925 us), and on int8
+    // the two are even.
+    //
+    // Copies, two LDS stages.  Group A issues the A-operand copies of step
+    // kt+1 in its memory phase of step kt.  Group B (copier slot wave-4)
+    // issues the B-operand copies of step kt+2 at the start of its compute
+    // phase of step kt, which runs beside group A's memory phase of step
+    // kt+1; the stage they fill held step kt, which group B finished reading
+    // in the phase before.  Each group waits for its own copies before the
+    // barrier that precedes the first read of that step: A at the end of
+    // its compute phase, B at the end of its memory phase.  One loop serves
+    // both groups: two loops in the branches of a group test spill
+    // registers.
+    static constexpr bool PINGPONG = NW == 8 && !CONV && NST == 2 && !B_KMAJ && (DT == F16 || DT == BF16);
+
+    // a workgroup barrier that nothing is scheduled across
+    __device__ __forceinline__ static void phase_barrier() {
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_barrier" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    __device__ __forceinline__ static void mainloop_pp(Acc (&acc)[FM][FN], const TileArgs& a, lds_char* smem, int m0, int n0,
+                                                       int k_lo, int k_hi, int wave, int lane) {
+        static_assert(NWC * 2 == NW, "two groups of copier slots");
+        const int wm = wave / WN, wn = wave % WN;
+        const bool grp_a = wave < NWC;
+        const int slot = grp_a ? wave : wave - NWC;
+        Dma d;
+        dma_setup(d, a, m0, n0, slot, lane);
+        __syncthreads();  // the previous tile's readers are done with every stage
+        if (k_lo >= k_hi) return;
+        if (grp_a) {
+            dma_issue<3, false>(d, a, smem, 0, k_lo, m0, n0, slot);
+            wait_copies<0>();
+        } else if (k_lo + 1 < k_hi) {
+            dma_issue<2, false>(d, a, smem, 1, k_lo + 1, m0, n0, slot);
+        }
+        __syncthreads();  // step k_lo is in LDS
+        if (!grp_a) phase_barrier();  // group B runs one phase behind
+        int st = 0;
+        for (int kt = k_lo; kt < k_hi; ++kt) {
+            // memory phase
+            Frag f[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) load_frag(f[s], smem, st, s, wm, wn, lane);
+            if (grp_a && kt + 1 < k_hi) dma_issue<1, false>(d, a, smem, st ^ 1, kt + 1, m0, n0, slot);
+            if (grp_a) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");  // B's copies of step kt+1
+            phase_barrier();
+            // compute phase
+            if (!grp_a && kt + 2 < k_hi) dma_issue<2, false>(d, a, smem, st, kt + 2, m0, n0, slot);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) mma_frag(acc, f[s]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (grp_a) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // A's copies of step kt+1
+            phase_barrier();
+            st ^= 1;
+        }
+        if (grp_a) phase_barrier();  // pairs with group B's extra barrier: equal counts
+    }
+
     // Accumulate K-steps [k_lo, k_hi) of tile (m0, n0) into acc: NST LDS
     // stages, the copies running NST - 1 K-steps ahead of the MFMAs.
     __device__ __forceinline__ static void mainloop(Acc (&acc)[FM][FN], const TileArgs& a, lds_char* smem, int m0, int n0,
                                                     int k_lo, int k_hi, int wave, int lane) {
+        if constexpr (PINGPONG) return mainloop_pp(acc, a, smem, m0, n0, k_lo, k_hi, wave, lane);
         const int wm = wave / WN, wn = wave % WN;
         Dma d;
         dma_setup(d, a, m0, n0, wave, lane);

@@ -79,6 +79,27 @@ def test_every_config_and_mode(dtype, config, mode):
     check(p, g, C)
 
 
+@pytest.mark.parametrize("dtype", [S.F16, S.BF16])
+@pytest.mark.parametrize("ksteps", [1, 2, 3, 33])
+@pytest.mark.parametrize("mode", [1, 2])
+def test_pingpong_loop_step_counts(dtype, ksteps, mode):
+    """The eight-wave kernel with row-major B runs its wave groups one phase
+    apart, each group copying one operand, group B two K-steps ahead: one,
+    two and three K-steps exercise the prologue and the steps that issue no
+    copies, 33 the steady state (with a ragged k tail), on ragged M and N.
+    Stream-K runs the same loop on segments that start mid-tile."""
+    K = 64 * ksteps - (24 if ksteps == 33 else 0)
+    p = S.small_problem(dtype, 520, 264, K, seed=70 + ksteps, bias=True, relu=(mode == 1))
+    T.tcm_set_option("force_config", 0)
+    T.tcm_set_option("force_mode", mode)
+    if mode == 2:
+        T.tcm_set_option("sk_grid", 5)
+    g, C, plan = _run(p)
+    assert "config=0" in plan and "b_col=0" in plan
+    assert ("mode=dp" if mode == 1 else "mode=streamk") in plan
+    check(p, g, C)
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("sk_grid", [3, 7, 64, 301])
 @pytest.mark.parametrize("config", [1, 5])
