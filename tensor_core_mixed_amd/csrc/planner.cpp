@@ -41,8 +41,13 @@ constexpr double kStaggerBytesPerClk = 14.6;
 // Split tiles also lose the L2 reuse of their operand panels across the
 // grid: each tile row re-reads B and each tile column re-reads A, served
 // from MALL (the 256 MiB last-level cache) at ~16 TB/s (fitted to
-// 1536^2 x 16384 with 64x64 and 128x128 units and to M = 256).
+// 1536^2 x 16384 with 64x64 and 128x128 units and to M = 256).  An operand
+// re-read by split tiles stays in the MALL only while it takes at most half
+// of it (the other operand, C and the partial tiles share the cache); a
+// larger one is re-read from HBM (seven 4096 x 4096 f16 weights of a group,
+// 235 MB: Stream-K 74 us against 49 us data-parallel).
 constexpr double kMallBytesPerClk = 16.0e12 / 2.4e9;
+constexpr double kMallBytes = 128.0 * 1024 * 1024;
 
 double flops_per_clk(int dt) {
     switch (dt) {
@@ -146,10 +151,21 @@ Estimate estimate(const Problem& p, int ci, int cus, int force_mode, int sk_grid
     const double step = std::max(mfma, std::max(lds, l2)) + kStepOverhead;  // per K-step, CU to itself
     const double lone_step = kStepLatency + (c.bm + c.bn) * (double)kStepBytes / kStepBytesPerClk;
     const double tile_store = (double)c.bm * c.bn * 4 / kL2BytesPerClk;
-    // unique bytes: a convolution's A is its input x, read once however many taps reuse it
+    // unique bytes: a convolution's A is its input x, read once however many
+    // taps reuse it; a group's bytes are summed over its entries, each with
+    // its own B
+    const double nb = (double)std::max<int64_t>(p.batch, 1);
     const double a_bytes = p.conv ? (double)p.conv_x_bytes : (double)p.M * p.K * elem_bytes(dt);
-    const double hbm_floor = (double)std::max<int64_t>(p.batch, 1) *
-                             (a_bytes + (double)p.K * p.N * elem_bytes(dt) + (double)p.M * p.N * 4) / kHbmBytesPerClk;
+    double a_uniq = nb * a_bytes, b_uniq = nb * (double)p.K * p.N * elem_bytes(dt), c_uniq = nb * (double)p.M * p.N * 4;
+    double a_reads = a_uniq * cdiv(p.N, c.bn), b_reads = b_uniq * cdiv(p.M, c.bm);
+    if (p.group) {
+        a_uniq = p.group_a_bytes;
+        b_uniq = p.group_b_bytes;
+        c_uniq = p.group_c_bytes;
+        a_reads = p.group_a_reads[ci];
+        b_reads = p.group_b_reads[ci];
+    }
+    const double hbm_floor = (a_uniq + b_uniq + c_uniq) / kHbmBytesPerClk;
 
     // data-parallel: waves of `slots` tiles, each wave takes I steps on a CU shared by `occ` workgroups
     Estimate dp{0, 1, (int)std::min<int64_t>(T, 1LL << 30), T, 0};
@@ -196,9 +212,8 @@ Estimate estimate(const Problem& p, int ci, int cus, int force_mode, int sk_grid
             c.bm * c.bn >= 128 * 128 ? std::max(sk_wg_step, share * (c.bm + c.bn) * (double)kStepBytes / kStaggerBytesPerClk)
                                      : sk_wg_step;
         const double sk_frac = (double)sk_tiles / (double)T;
-        const double rereads = sk_frac * (double)std::max<int64_t>(p.batch, 1) *
-                               (a_bytes * cdiv(p.N, c.bn) + (double)p.K * p.N * elem_bytes(dt) * cdiv(p.M, c.bm)) /
-                               kMallBytesPerClk;
+        const double rereads = sk_frac * (a_reads / (a_uniq <= kMallBytes ? kMallBytesPerClk : kHbmBytesPerClk) +
+                                          b_reads / (b_uniq <= kMallBytes ? kMallBytesPerClk : kHbmBytesPerClk));
         sk.cycles = std::max(dp_waves * (I * wg_step + tile_store * share) + per_wg * split_step + tile_store * share + fixup,
                              std::max(hbm_floor, rereads));
         sk.grid = (int)grid;

@@ -34,6 +34,11 @@ struct Problem {
     bool group = false;
     int64_t group_tiles[kNumConfigs] = {0};
     bool group_ok[kNumConfigs] = {false};
+    // a group's bytes summed over its entries: each operand once, and the
+    // bytes split tiles read (an entry's A once per tile column, its B once
+    // per tile row) per config
+    double group_a_bytes = 0, group_b_bytes = 0, group_c_bytes = 0;
+    double group_a_reads[kNumConfigs] = {0}, group_b_reads[kNumConfigs] = {0};
 };
 
 struct Plan {

@@ -752,6 +752,13 @@ int grouped_impl(int64_t count, const tcm_group_entry* ent, int64_t K, int dtype
     p.lda = p.ldb = p.ldc = 1;  // per entry; the group fields below decide
     p.aligned = aligned;
     p.group = true;
+    const double es = elem_bytes(p.dtype);
+    for (int64_t i = 0; i < count; ++i) {
+        if (ent[i].M == 0 || ent[i].N == 0) continue;
+        p.group_a_bytes += (double)ent[i].M * K * es;
+        p.group_b_bytes += (double)K * ent[i].N * es;
+        p.group_c_bytes += (double)ent[i].M * ent[i].N * 4;
+    }
     for (int c = 0; c < kNumConfigs; ++c) {
         int64_t tiles = 0;
         bool ok = aligned;
@@ -760,7 +767,10 @@ int grouped_impl(int64_t count, const tcm_group_entry* ent, int64_t K, int dtype
             Problem q = pe[i];
             q.aligned = aligned;
             ok = tile_eligible(q, kConfigs[c]);
-            tiles += ((ent[i].M + kConfigs[c].bm - 1) / kConfigs[c].bm) * ((ent[i].N + kConfigs[c].bn - 1) / kConfigs[c].bn);
+            const int64_t tm = (ent[i].M + kConfigs[c].bm - 1) / kConfigs[c].bm, tn = (ent[i].N + kConfigs[c].bn - 1) / kConfigs[c].bn;
+            tiles += tm * tn;
+            p.group_a_reads[c] += (double)ent[i].M * K * es * tn;
+            p.group_b_reads[c] += (double)K * ent[i].N * es * tm;
         }
         p.group_ok[c] = ok && tiles < ((int64_t)1 << 31);
         p.group_tiles[c] = tiles;
