@@ -873,10 +873,11 @@ struct TileKernel {
             if (arrived != w_last - w_first) continue;  // not the last arrival
             // Last arrival: sum every segment's partial in workgroup order,
             // the loads of partial w+1 in flight while partial w is added.
-            auto slot_of = [&](int w) {
-                const int64_t ft = ((int64_t)w * W / a.grid) / I;
-                return 2 * w + (tsk == ft ? 0 : 1);
-            };
+            // every owner after the first starts inside tile tsk (its first
+            // tile, slot 0); the first owner used slot 1 if it started in an
+            // earlier tile
+            const int first_slot1 = ((int64_t)w_first * W / a.grid) < tsk * I ? 1 : 0;
+            auto slot_of = [&](int w) { return 2 * w + (w == w_first ? first_slot1 : 0); };
             if constexpr (NW > 4 || FM * FN >= 4) {
                 // one partial buffer: eight waves have no room for a second,
                 // and for 64x64 wave tiles a second one would halve the
