@@ -246,6 +246,12 @@ const char* tcm_status_string(int status);
  *   "sk_grid"      0 = planner decides, else the persistent grid size for
  *                  split-k (clamped to the number of co-resident workgroups).
  *   "generic"      1 = route every call to the generic (any-alignment) kernel.
+ *   "sk_fixup"     how a split-k tile cut between workgroups is summed:
+ *                  0 = planner decides (a second kernel when the tile has six
+ *                  or more segments), 1 = its last-arriving workgroup sums
+ *                  the partials, 2 = a second kernel launched on the same
+ *                  stream sums them.  Both add the partials in the same
+ *                  order: the results are bit-identical.
  *   "tuned"        1 (default) = use the tuning table (tcm_tune) for problems
  *                  it holds; 0 = ignore it.  force_config / force_mode win.
  * Unknown keys or out-of-range values: TCM_ERR_INVALID_VALUE.

@@ -291,6 +291,15 @@ bool make_plan(const Problem& p, const Options& o, int cus, Plan* out) {
         pl.sk_tiles = best_e.sk_tiles;
         pl.ws_partial_bytes = 2LL * pl.grid * c.bm * c.bn * 4;
         pl.ws_counters = pl.sk_tiles;
+        // Split tiles cut into many short segments are summed by a second
+        // kernel: the segments then store their partials and end, instead
+        // of waiting for the stores, counting their arrival and having the
+        // last arrival read the others back (M = 1 / 16 / 64 with N = K =
+        // 4096 on 64x64 units, eight segments a tile: 13.2 / 13.4 / 15.8 us
+        // in the kernel, 12.2 / 12.5 / 14.0 us with the second kernel; at
+        // three or four segments a tile the launch costs more than it saves).
+        const int64_t per_wg = (pl.sk_tiles * pl.iters + pl.grid - 1) / pl.grid;
+        pl.fixup_kernel = o.sk_fixup == 2 || (o.sk_fixup == 0 && pl.iters >= 6 * per_wg);
     }
     pl.group_m = 4;
     *out = pl;

@@ -13,6 +13,7 @@ struct Options {
     int force_config = -1;  // -1 auto, else tile-table index
     int sk_grid = 0;        // 0 auto, else persistent grid size
     int generic = 0;        // 1: always the generic kernel
+    int sk_fixup = 0;       // 0 planner decides, 1 last arrival sums a split tile, 2 a second kernel does
     int sk_occ[kNumConfigs] = {0};  // Stream-K workgroups per CU by config (0: static estimate)
 };
 
@@ -50,6 +51,7 @@ struct Plan {
     int64_t tiles = 0, iters = 0, dp_tiles = 0, sk_tiles = 0;
     int64_t ws_partial_bytes = 0, ws_counters = 0;
     int group_m = 4;
+    bool fixup_kernel = false;  // Stream-K split tiles summed by a second kernel
     double est_cycles = 0;  // the cost model's estimate (for logs)
 };
 

@@ -257,10 +257,11 @@ std::string describe(const Plan& pl, const Problem& p) {
     } else {
         snprintf(buf, sizeof buf,
                  "kernel=%s config=%d tile=%dx%dx%d mode=%s grid=%d tiles=%lld iters=%lld dp_tiles=%lld sk_tiles=%lld "
-                 "M=%lld N=%lld K=%lld dtype=%d b_col=%d batch=%lld est_cycles=%.0f",
+                 "M=%lld N=%lld K=%lld dtype=%d b_col=%d batch=%lld est_cycles=%.0f%s",
                  p.conv ? "conv" : "tile", pl.config, pl.bm, pl.bn, pl.bk, pl.mode == 1 ? "dp" : "streamk", pl.grid, (long long)pl.tiles,
                  (long long)pl.iters, (long long)pl.dp_tiles, (long long)pl.sk_tiles, (long long)p.M, (long long)p.N,
-                 (long long)p.K, p.dtype, (int)p.b_col, (long long)p.batch, pl.est_cycles);
+                 (long long)p.K, p.dtype, (int)p.b_col, (long long)p.batch, pl.est_cycles,
+                 pl.fixup_kernel ? " fixup=kernel" : "");
     }
     return buf;
 }
@@ -330,6 +331,9 @@ int tcm_set_option(const char* key, int64_t value) {
     } else if (!strcmp(key, "generic")) {
         if (value < 0 || value > 1) return TCM_ERR_INVALID_VALUE;
         g_opts.generic = (int)value;
+    } else if (!strcmp(key, "sk_fixup")) {
+        if (value < 0 || value > 2) return TCM_ERR_INVALID_VALUE;
+        g_opts.sk_fixup = (int)value;
     } else if (!strcmp(key, "tuned")) {
         if (value < 0 || value > 1) return TCM_ERR_INVALID_VALUE;
         g_use_tuned = (int)value;
@@ -346,6 +350,7 @@ int64_t tcm_get_option(const char* key) {
     if (!strcmp(key, "force_config")) return g_opts.force_config;
     if (!strcmp(key, "sk_grid")) return g_opts.sk_grid;
     if (!strcmp(key, "generic")) return g_opts.generic;
+    if (!strcmp(key, "sk_fixup")) return g_opts.sk_fixup;
     if (!strcmp(key, "tuned")) return g_use_tuned;
     return -2;
 }
@@ -560,6 +565,7 @@ int launch_tiled(const Problem& p, const Plan& pl, TileArgs& a, int dev, void* s
     tile_order_shape(a.tiles_m, a.tiles_n, a.group_m, &a.super_m, &a.super_n);
     a.ws_partial = nullptr;
     a.ws_counter = nullptr;
+    a.sk_fixup_kernel = pl.fixup_kernel ? 1 : 0;
     if (pl.mode == 2 && pl.sk_tiles > 0) {
         Workspace w;
         int ws = get_workspace(dev, stream, pl.ws_partial_bytes, pl.ws_counters, &w);
@@ -811,6 +817,7 @@ int grouped_impl(int64_t count, const tcm_group_entry* ent, int64_t K, int dtype
     a.sk_tiles = (int)pl.sk_tiles;
     a.grid = pl.grid;
     a.group_m = pl.group_m;
+    a.sk_fixup_kernel = pl.fixup_kernel ? 1 : 0;
     int64_t tile0 = 0;
     for (int64_t i = 0; i < count; ++i) {
         const tcm_group_entry& x = ent[i];

@@ -70,6 +70,7 @@ struct TileArgs {
     int super_m, super_n; // tile order: super-tile (one XCD's share) in tiles
     float* ws_partial;    // Stream-K partial tiles: 2 slots per workgroup, bm*bn 4-byte values each
     int* ws_counter;      // one arrival counter per split tile (zero between launches)
+    int sk_fixup_kernel;  // 1: split tiles are summed by a second kernel, not by their last arrival
     // Implicit-GEMM convolution (kernels built with CONV only): A is the
     // im2col view of an NHWC input x: row m = output pixel (n, p, q), column
     // k = (r*S + s)*C + c.  C is a multiple of the K-step, so every K-step

@@ -860,6 +860,7 @@ struct TileKernel {
             // partial stores are acknowledged), then count the arrival.
             const int slot = 2 * wg + (tsk == first_tile ? 0 : 1);
             store_partial(acc, partial_rsrc(a, slot), wave, wm, lane, e.M - m0);
+            if (a.sk_fixup_kernel) continue;  // the fix-up kernel sums this tile after the grid ends
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             // workgroups holding a segment of tile tsk: owners of its first and last iteration
@@ -924,6 +925,46 @@ struct TileKernel {
             if (tid == 0) __hip_atomic_store(a.ws_counter + tsk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+
+    // Fix-up kernel of a Stream-K launch whose split tiles are summed after
+    // the grid ends (sk_fixup_kernel): workgroup b finishes Stream-K tile b
+    // if it was split, adding the partials of its segments in workgroup
+    // order as the last arrival would, so both ways give the same bits.
+    // The kernel boundary makes every partial visible: no segment waits for
+    // its stores or counts its arrival.
+    template <class Args>
+    __device__ __forceinline__ static void run_fixup(const Args& g) {
+        const TileArgs& a = base_args(g);
+        const int tid = threadIdx.x, lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int wm = wave / WN, wn = wave % WN;
+        const int64_t I = a.iters;
+        const int64_t W = (int64_t)a.sk_tiles * I;
+        const int64_t tsk = blockIdx.x;
+        const int64_t x0 = tsk * I, x1 = tsk * I + I - 1;
+        const int w_first = (int)(((x0 + 1) * a.grid + W - 1) / W - 1);
+        const int w_last = (int)(((x1 + 1) * a.grid + W - 1) / W - 1);
+        if (w_first == w_last) return;  // one workgroup held the whole tile and stored it
+        int tm, tn;
+        const TileArgs e = tile_of(g, xcd_order(a.dp_tiles + (int)tsk, work_tiles(g)), tm, tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+        const int first_slot1 = ((int64_t)w_first * W / a.grid) < x0 ? 1 : 0;
+        // partials in flight at once: about 128 registers' worth
+        constexpr int NB = FM * FN >= 8 ? 1 : 8 / (FM * FN);
+        Acc acc[FM][FN];
+        for (int w0 = w_first; w0 <= w_last; w0 += NB) {
+            Partial pb[NB];
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                if (w0 + j <= w_last)
+                    load_partial(pb[j], partial_rsrc(a, 2 * (w0 + j) + (w0 + j == w_first ? first_slot1 : 0)), wave, wm, lane,
+                                 e.M - m0);
+#pragma unroll
+            for (int j = 0; j < NB; ++j)
+                if (w0 + j <= w_last) add_partial(acc, pb[j], w0 + j == w_first);
+        }
+        store_tile(acc, e, m0, n0, wm, wn, lane);
+    }
 };
 
 template <int CFG>
@@ -961,6 +1002,12 @@ int sk_occupancy() {
     return n;
 }
 
+// Sums the split tiles of a Stream-K launch (one workgroup per Stream-K tile).
+template <int DT, int CFG, bool B_KMAJ>
+__global__ __launch_bounds__(TileThreads<CFG>::value) void tile_fixup_kernel(TileArgs a) {
+    TileKernel<DT, CFG, B_KMAJ, false, kConfigs[CFG].sk_stages>::run_fixup(a);
+}
+
 template <int DT, int CFG, bool B_KMAJ>
 int launch_tile(const TileArgs& a, void* stream) {
     hipStream_t s = (hipStream_t)stream;
@@ -968,6 +1015,8 @@ int launch_tile(const TileArgs& a, void* stream) {
         hipLaunchKernelGGL((tile_gemm_kernel<DT, CFG, B_KMAJ, false>), dim3(a.dp_tiles), dim3(TileThreads<CFG>::value), 0, s, a);
     if (a.sk_tiles > 0)
         hipLaunchKernelGGL((tile_gemm_kernel<DT, CFG, B_KMAJ, true>), dim3(a.grid), dim3(TileThreads<CFG>::value), 0, s, a);
+    if (a.sk_tiles > 0 && a.sk_fixup_kernel)
+        hipLaunchKernelGGL((tile_fixup_kernel<DT, CFG, B_KMAJ>), dim3(a.sk_tiles), dim3(TileThreads<CFG>::value), 0, s, a);
     return (int)hipGetLastError();
 }
 
@@ -980,12 +1029,19 @@ void tile_group_kernel(GroupArgs g) {
 }
 
 template <int DT, int CFG, bool B_KMAJ>
+__global__ __launch_bounds__(TileThreads<CFG>::value) void group_fixup_kernel(GroupArgs g) {
+    TileKernel<DT, CFG, B_KMAJ, false, kConfigs[CFG].sk_stages>::run_fixup(g);
+}
+
+template <int DT, int CFG, bool B_KMAJ>
 int launch_group(const GroupArgs& g, void* stream) {
     hipStream_t s = (hipStream_t)stream;
     if (g.t.dp_tiles > 0)
         hipLaunchKernelGGL((tile_group_kernel<DT, CFG, B_KMAJ, false>), dim3(g.t.dp_tiles), dim3(TileThreads<CFG>::value), 0, s, g);
     if (g.t.sk_tiles > 0)
         hipLaunchKernelGGL((tile_group_kernel<DT, CFG, B_KMAJ, true>), dim3(g.t.grid), dim3(TileThreads<CFG>::value), 0, s, g);
+    if (g.t.sk_tiles > 0 && g.t.sk_fixup_kernel)
+        hipLaunchKernelGGL((group_fixup_kernel<DT, CFG, B_KMAJ>), dim3(g.t.sk_tiles), dim3(TileThreads<CFG>::value), 0, s, g);
     return (int)hipGetLastError();
 }
 
@@ -999,12 +1055,19 @@ void tile_conv_kernel(TileArgs a) {
 }
 
 template <int DT, int CFG>
+__global__ __launch_bounds__(TileThreads<CFG>::value) void conv_fixup_kernel(TileArgs a) {
+    TileKernel<DT, CFG, true, true, kConfigs[CFG].sk_stages>::run_fixup(a);
+}
+
+template <int DT, int CFG>
 int launch_conv(const TileArgs& a, void* stream) {
     hipStream_t s = (hipStream_t)stream;
     if (a.dp_tiles > 0)
         hipLaunchKernelGGL((tile_conv_kernel<DT, CFG, false>), dim3(a.dp_tiles), dim3(TileThreads<CFG>::value), 0, s, a);
     if (a.sk_tiles > 0)
         hipLaunchKernelGGL((tile_conv_kernel<DT, CFG, true>), dim3(a.grid), dim3(TileThreads<CFG>::value), 0, s, a);
+    if (a.sk_tiles > 0 && a.sk_fixup_kernel)
+        hipLaunchKernelGGL((conv_fixup_kernel<DT, CFG>), dim3(a.sk_tiles), dim3(TileThreads<CFG>::value), 0, s, a);
     return (int)hipGetLastError();
 }
 

@@ -96,6 +96,10 @@ def test_options():
     assert T.tcm_get_option("no_such_key") == -2
     assert T.tcm_set_option("force_config", T.tcm_config_count()) == T.TCM_ERR_INVALID_VALUE
     assert T.tcm_set_option("force_mode", 0) == T.TCM_OK
+    assert T.tcm_get_option("sk_fixup") == 0
+    assert T.tcm_set_option("sk_fixup", 2) == T.TCM_OK and T.tcm_get_option("sk_fixup") == 2
+    assert T.tcm_set_option("sk_fixup", 3) == T.TCM_ERR_INVALID_VALUE
+    assert T.tcm_set_option("sk_fixup", 0) == T.TCM_OK
 
 
 def test_config_table():

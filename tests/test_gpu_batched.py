@@ -24,6 +24,7 @@ def _reset_options():
     T.tcm_set_option("force_config", -1)
     T.tcm_set_option("sk_grid", 0)
     T.tcm_set_option("generic", 0)
+    T.tcm_set_option("sk_fixup", 0)
 
 
 def _pack(arr, n_entries, pad, fill):
@@ -127,11 +128,14 @@ def test_batched_shared_b_and_bias(dtype):
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("sk_grid", [5, 37, 200])
 @pytest.mark.parametrize("config", [4, 5])
-def test_batched_streamk_splits_across_entries(dtype, sk_grid, config):
-    """One Stream-K grid over the tiles of all entries; segments cross entry boundaries."""
+@pytest.mark.parametrize("fixup", [1, 2])
+def test_batched_streamk_splits_across_entries(dtype, sk_grid, config, fixup):
+    """One Stream-K grid over the tiles of all entries; segments cross entry
+    boundaries; split tiles summed by their last arrival or a second kernel."""
     T.tcm_set_option("force_config", config)
     T.tcm_set_option("force_mode", 2)
     T.tcm_set_option("sk_grid", sk_grid)
+    T.tcm_set_option("sk_fixup", fixup)
     p = S.small_problem(dtype, 16, 192, 1024, seed=96, bias=True, batch=7)
     g, C, plan = _case(p)
     assert "mode=streamk" in plan

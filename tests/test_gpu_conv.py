@@ -29,6 +29,7 @@ def _reset_options():
     T.tcm_set_option("force_config", -1)
     T.tcm_set_option("sk_grid", 0)
     T.tcm_set_option("generic", 0)
+    T.tcm_set_option("sk_fixup", 0)
 
 
 def run_conv(p, g, x_offset=0):
@@ -105,6 +106,20 @@ def test_conv_every_config_and_mode(dtype, config, mode):
     p = S.small_conv(dtype, 2, 9, 7, 2 * BKE[dtype], 40, 3, 3, pad=(1, 1), seed=120 + config, bias=True, relu=True)
     _, plan = _run_check(p)
     assert "kernel=conv" in plan and f"config={config}" in plan
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("config", [1, 4, 5])
+def test_conv_streamk_fixup_kernel(dtype, config):
+    """Stream-K convolution with many segments per tile, split tiles summed
+    by the second kernel."""
+    T.tcm_set_option("force_config", config)
+    T.tcm_set_option("force_mode", 2)
+    T.tcm_set_option("sk_grid", 41)
+    T.tcm_set_option("sk_fixup", 2)
+    p = S.small_conv(dtype, 2, 9, 7, 2 * BKE[dtype], 40, 3, 3, pad=(1, 1), seed=140 + config, bias=True, relu=True)
+    _, plan = _run_check(p)
+    assert "kernel=conv" in plan and "mode=streamk" in plan and "fixup=kernel" in plan
 
 
 GEOMETRIES = [  # (N, H, W, K, R, S, pad, stride, dil)

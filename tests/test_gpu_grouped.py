@@ -24,6 +24,7 @@ def _reset_options():
     T.tcm_set_option("force_config", -1)
     T.tcm_set_option("sk_grid", 0)
     T.tcm_set_option("generic", 0)
+    T.tcm_set_option("sk_fixup", 0)
 
 
 def make_group(dtype, shapes, K, seed, b_col=False, bias=False, relu=False, c_type="acc", accum=False, ld_pad=0):
@@ -97,11 +98,14 @@ def test_grouped_every_config_and_mode(dtype, config, mode):
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("config", [4, 5])
 @pytest.mark.parametrize("sk_grid", [3, 37, 200])
-def test_grouped_streamk_splits_across_entries(dtype, config, sk_grid):
-    """One Stream-K grid over the tiles of every entry; segments cross entry boundaries."""
+@pytest.mark.parametrize("fixup", [1, 2])
+def test_grouped_streamk_splits_across_entries(dtype, config, sk_grid, fixup):
+    """One Stream-K grid over the tiles of every entry; segments cross entry
+    boundaries; split tiles summed by their last arrival or a second kernel."""
     T.tcm_set_option("force_config", config)
     T.tcm_set_option("force_mode", 2)
     T.tcm_set_option("sk_grid", sk_grid)
+    T.tcm_set_option("sk_fixup", fixup)
     K = 1024 if dtype != S.I8 else 2048
     ps = make_group(dtype, [(16, 192), (5, 64), (48, 128), (1, 256)], K, seed=210, bias=True)
     gs, outs, plan = run_group(ps)

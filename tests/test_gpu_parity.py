@@ -21,6 +21,7 @@ def _reset_options():
     T.tcm_set_option("force_config", -1)
     T.tcm_set_option("sk_grid", 0)
     T.tcm_set_option("generic", 0)
+    T.tcm_set_option("sk_fixup", 0)
 
 
 def _run(p, **kw):
@@ -103,19 +104,42 @@ def test_pingpong_loop_step_counts(dtype, ksteps, mode):
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("sk_grid", [3, 7, 64, 301])
 @pytest.mark.parametrize("config", [1, 5])
-def test_streamk_many_segments_per_tile(dtype, sk_grid, config):
+@pytest.mark.parametrize("fixup", [1, 2])
+def test_streamk_many_segments_per_tile(dtype, sk_grid, config, fixup):
     """Small persistent grids split each tile over several workgroups (and
     large ones give workgroups a few iterations each: segments shorter than
-    the pipeline depth)."""
+    the pipeline depth).  Split tiles are summed by their last arrival
+    (fixup 1) or by a second kernel (fixup 2)."""
     ce = {S.F16: 8, S.BF16: 8, S.F32: 4, S.I8: 16}[dtype]
     p = S.small_problem(dtype, 260, 208, 40 * ce, seed=sk_grid, b_col=(sk_grid % 2 == 1), bias=True)
     T.tcm_set_option("force_mode", 2)
     T.tcm_set_option("force_config", config)
     T.tcm_set_option("sk_grid", sk_grid)
+    T.tcm_set_option("sk_fixup", fixup)
     g, C, plan = _run(p)
     grid = int(plan.split("grid=")[1].split()[0])
     assert "mode=streamk" in plan and 1 <= grid <= sk_grid
+    assert ("fixup=kernel" in plan) == (fixup == 2)
     check(p, g, C)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("config", [1, 4, 5])
+def test_fixup_kernel_bit_identical_to_last_arrival(dtype, config):
+    """Both ways of finishing a split tile add the same partials in the same
+    order: the outputs agree bit for bit, floats included."""
+    ce = {S.F16: 8, S.BF16: 8, S.F32: 4, S.I8: 16}[dtype]
+    p = S.small_problem(dtype, 150, 272, 96 * ce, seed=60 + config, bias=True, relu=True)
+    T.tcm_set_option("force_mode", 2)
+    T.tcm_set_option("force_config", config)
+    T.tcm_set_option("sk_grid", 37)
+    outs = []
+    for fixup in (1, 2):
+        T.tcm_set_option("sk_fixup", fixup)
+        g, C, plan = _run(p)
+        outs.append(C)
+    check(p, g, outs[1])
+    assert np.array_equal(outs[0], outs[1])
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -273,11 +297,14 @@ def test_init_tensor_and_16bit_c_every_config_and_mode(variant, config, mode):
 
 @pytest.mark.parametrize("variant", EPI_VARIANTS, ids=_epi_id)
 @pytest.mark.parametrize("config", [4, 5])
-def test_init_tensor_streamk_many_segments(variant, config):
-    """Only the k = 0 segment of a split tile may add C_in (and the bias)."""
+@pytest.mark.parametrize("fixup", [1, 2])
+def test_init_tensor_streamk_many_segments(variant, config, fixup):
+    """Only the k = 0 segment of a split tile may add C_in (and the bias),
+    whichever way the split tile is summed."""
     dtype, c_type, accum = variant
     T.tcm_set_option("force_config", config)
     T.tcm_set_option("force_mode", 2)
+    T.tcm_set_option("sk_fixup", fixup)
     T.tcm_set_option("sk_grid", 37)
     K = 1024 if dtype != S.I8 else 2048
     p = S.small_problem(dtype, 96, 128, K, seed=50, bias=True, c_type=c_type, accum=accum)
