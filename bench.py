@@ -80,6 +80,10 @@ def plan_kernels(plan):
         names.add(head + "false>" + args)
     if int(f.get("sk_tiles", 0)) > 0:
         names.add(head + "true>" + args)
+        if f.get("fixup") == "kernel":  # split tiles summed by a second kernel
+            kind = "conv" if f["kernel"] == "conv" else ("group" if "group" in f else "tile")
+            tail = f"{f['dtype']}, {f['config']}>" if kind == "conv" else f"{f['dtype']}, {f['config']}, {b}>"
+            names.add(f"void tcm::{kind}_fixup_kernel<{tail}{args}")
     return names
 
 
