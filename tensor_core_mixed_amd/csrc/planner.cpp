@@ -244,6 +244,10 @@ bool make_plan(const Problem& p, const Options& o, int cus, Plan* out) {
     if (!o.generic) {
         for (int c = 0; c < kNumConfigs; ++c) {
             if (o.force_config >= 0 && c != o.force_config) continue;
+            // the eight-wave config is data-parallel only (its Stream-K kernel
+            // spills registers): a forced Stream-K picks among the others
+            // unless that config is forced too
+            if (o.force_mode == 2 && o.force_config < 0 && kConfigs[c].wm * kConfigs[c].wn > 4) continue;
             if (p.group ? !p.group_ok[c] : !tile_eligible(p, kConfigs[c])) continue;
             Estimate e = estimate(p, c, cus, o.force_mode, o.sk_grid, o.sk_occ[c]);
             if (e.cycles < best_e.cycles * 0.999) {
