@@ -272,6 +272,8 @@ typedef struct {
     int64_t dp_tiles;      /* tiles done whole by one workgroup */
     int64_t sk_tiles;      /* tiles whose k range is split over workgroups */
     int64_t workspace_bytes; /* split-k workspace the call needs */
+    int32_t fixup_kernel;  /* 1 = split tiles are summed by a second kernel on the stream */
+    int32_t reserved;      /* 0 */
 } tcm_plan_info;
 
 /*

@@ -396,6 +396,8 @@ int tcm_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t 
     out->dp_tiles = pl.dp_tiles;
     out->sk_tiles = pl.sk_tiles;
     out->workspace_bytes = pl.ws_partial_bytes + pl.ws_counters * (int64_t)sizeof(int);
+    out->fixup_kernel = pl.fixup_kernel ? 1 : 0;
+    out->reserved = 0;
     return TCM_OK;
 }
 

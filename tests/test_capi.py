@@ -127,6 +127,39 @@ def test_planner_skinny_uses_streamk(M):
     assert p["config"] == 5 and (p["bm"], p["bn"]) == (64, 64)
 
 
+@pytest.mark.parametrize("M,fixup", [(1, 1), (16, 1), (64, 1), (256, 0)])
+def test_planner_fixup_kernel_for_many_segments(M, fixup):
+    """Split tiles with six or more segments are summed by a second kernel;
+    with fewer, by their last arrival.  The option overrides either way."""
+    p = T.tcm_plan(M, 4096, 4096, 4096, 4096, 4096, T.TCM_F16_F32)
+    assert p["mode"] == 2 and p["fixup_kernel"] == fixup
+    per_wg = -(-p["sk_tiles"] * p["iters_per_tile"] // p["grid"])
+    assert (p["iters_per_tile"] >= 6 * per_wg) == bool(fixup)
+    try:
+        for opt, want in ((1, 0), (2, 1)):
+            assert T.tcm_set_option("sk_fixup", opt) == T.TCM_OK
+            assert T.tcm_plan(M, 4096, 4096, 4096, 4096, 4096, T.TCM_F16_F32)["fixup_kernel"] == want
+    finally:
+        T.tcm_set_option("sk_fixup", 0)
+    # data-parallel plans have nothing to sum
+    assert T.tcm_plan(8192, 8192, 8192, 8192, 8192, 8192, T.TCM_F16_F32 | T.TCM_B_COLMAJOR)["fixup_kernel"] == 0
+
+
+def test_forced_streamk_skips_the_eight_wave_config():
+    """The eight-wave config is data-parallel only: a forced Stream-K plan
+    uses another config unless that one is forced too."""
+    try:
+        T.tcm_set_option("force_mode", 2)
+        p = T.tcm_plan(3840, 3840, 4096, 4096, 3840, 3840, T.TCM_F16_F32)
+        assert p["mode"] == 2 and (p["bm"], p["bn"]) != (256, 256)
+        T.tcm_set_option("force_config", 0)
+        p = T.tcm_plan(3840, 3840, 4096, 4096, 3840, 3840, T.TCM_F16_F32)
+        assert p["mode"] == 2 and p["config"] == 0
+    finally:
+        T.tcm_set_option("force_mode", 0)
+        T.tcm_set_option("force_config", -1)
+
+
 def test_deep_config_is_the_small_tile_with_more_stages():
     assert T.tcm_config_count() == 6
     for dt in range(4):
