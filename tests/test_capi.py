@@ -145,6 +145,22 @@ def test_planner_fixup_kernel_for_many_segments(M, fixup):
     assert T.tcm_plan(8192, 8192, 8192, 8192, 8192, 8192, T.TCM_F16_F32 | T.TCM_B_COLMAJOR)["fixup_kernel"] == 0
 
 
+def test_streamk_grid_aligned_to_the_tiles():
+    """When the tiles fit the co-resident grid two or more times over, the
+    Stream-K grid is an exact multiple of the tile count (every tile's shares
+    start at the same k); otherwise it is the co-resident grid."""
+    p = T.tcm_plan(1536, 1536, 16384, 16384, 1536, 1536, T.TCM_F16_F32)
+    assert p["mode"] == 2 and (p["bm"], p["bn"]) == (128, 128)
+    assert p["sk_tiles"] == 144 and p["grid"] == 432  # 144 x 3 of 512 slots
+    p = T.tcm_plan(2048, 2048, 8192, 8192, 2048, 2048, T.TCM_F16_F32)
+    assert p["mode"] == 2 and p["grid"] % p["sk_tiles"] == 0
+    try:
+        T.tcm_set_option("sk_grid", 500)  # an explicit grid is kept
+        assert T.tcm_plan(1536, 1536, 16384, 16384, 1536, 1536, T.TCM_F16_F32)["grid"] == 500
+    finally:
+        T.tcm_set_option("sk_grid", 0)
+
+
 def test_forced_streamk_skips_the_eight_wave_config():
     """The eight-wave config is data-parallel only: a forced Stream-K plan
     uses another config unless that one is forced too."""
