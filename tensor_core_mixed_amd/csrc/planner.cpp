@@ -30,6 +30,7 @@ constexpr double kStepOverhead = 96.0;          // barrier + wait per K-step
 constexpr double kStepLatency = 500.0;          // lone workgroup: fixed part of a K-step ...
 constexpr double kStepBytesPerClk = 16.0;       // ... plus its copies at this rate
 constexpr double kFixupLatency = 1500.0;        // one device-coherent round trip per partial tile read back
+constexpr double kFixupKernel = 9000.0;         // a fix-up kernel: its launch and one read of the partials (~3.8 us)
 // Stream-K workgroups start their segments at different k, so tiles that
 // share an operand panel no longer read it from L2 at the same time.  For
 // 128x128 tiles (two workgroups per CU) a split K-step then streams its
@@ -136,7 +137,7 @@ int64_t tile_count(const Problem& p, int ci) {
     return p.group ? p.group_tiles[ci] : cdiv(p.M, c.bm) * cdiv(p.N, c.bn) * std::max<int64_t>(p.batch, 1);
 }
 
-Estimate estimate(const Problem& p, int ci, int cus, int force_mode, int sk_grid, int sk_occ_known) {
+Estimate estimate(const Problem& p, int ci, int cus, int force_mode, int sk_grid, int sk_occ_known, int sk_fixup) {
     const TileConfig& c = kConfigs[ci];
     const int dt = p.dtype;
     const int bke = bk_elems(dt);
@@ -215,8 +216,14 @@ Estimate estimate(const Problem& p, int ci, int cus, int force_mode, int sk_grid
         // only rows below M travel (skinny problems move a sliver of each partial)
         const double rows_frac = std::min(1.0, (double)std::max<int64_t>(p.M, 1) / c.bm);
         // the last arrival's reads are latency-bound: about one memory round
-        // trip per segment (the next partial's loads overlap the current add)
-        const double fixup = splits ? rows_frac * partial / kL2BytesPerClk + nseg * (kFixupLatency + rows_frac * partial / kL2BytesPerClk) : 0.0;
+        // trip per segment (the next partial's loads overlap the current add);
+        // a fix-up kernel (six or more segments a tile, as make_plan decides)
+        // costs its launch and one read of every partial instead
+        const bool fixup_kernel = sk_fixup == 2 || (sk_fixup == 0 && I >= 6 * per_wg);
+        const double partial_reads = nseg * rows_frac * partial / kL2BytesPerClk;
+        const double fixup = !splits ? 0.0
+                             : fixup_kernel ? rows_frac * partial / kL2BytesPerClk + kFixupKernel + partial_reads
+                                            : rows_frac * partial / kL2BytesPerClk + nseg * kFixupLatency + partial_reads;
         // a lone Stream-K workgroup keeps sk_stages - 1 K-steps of copies in
         // flight, which divides the latency part of its step
         const double sk_lone = kStepLatency / (c.sk_stages - 1) + (c.bm + c.bn) * (double)kStepBytes / kStepBytesPerClk;
@@ -264,7 +271,7 @@ bool make_plan(const Problem& p, const Options& o, int cus, Plan* out) {
             // unless that config is forced too
             if (o.force_mode == 2 && o.force_config < 0 && kConfigs[c].wm * kConfigs[c].wn > 4) continue;
             if (p.group ? !p.group_ok[c] : !tile_eligible(p, kConfigs[c])) continue;
-            Estimate e = estimate(p, c, cus, o.force_mode, o.sk_grid, o.sk_occ[c]);
+            Estimate e = estimate(p, c, cus, o.force_mode, o.sk_grid, o.sk_occ[c], o.sk_fixup);
             if (e.cycles < best_e.cycles * 0.999) {
                 best = c;
                 best_e = e;

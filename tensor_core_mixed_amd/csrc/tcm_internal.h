@@ -31,7 +31,7 @@ struct TileConfig {
     int sk_stages;
     const char* name;
 };
-constexpr int kNumConfigs = 6;
+constexpr int kNumConfigs = 7;
 constexpr TileConfig kConfigs[kNumConfigs] = {
     {256, 256, 4, 2, 2, "256x256 w4x2"},     // big square problems: 64x128 per wave, two waves per SIMD
     {128, 128, 2, 2, 2, "128x128 w2x2"},     // mid sizes, 2 workgroups per CU
@@ -40,6 +40,8 @@ constexpr TileConfig kConfigs[kNumConfigs] = {
     {64, 64, 2, 2, 2, "64x64 w2x2"},         // Stream-K units for skinny / small problems (16 KiB partials)
     {64, 64, 2, 2, 4, "64x64 w2x2 deep"},    // the same with four Stream-K stages (two workgroups per CU):
                                              // short latency-bound segments, e.g. M <= 64 with a few K-steps each
+    {32, 64, 1, 2, 6, "32x64 w1x2 deep"},    // skinny M (M <= 32): six Stream-K stages of 12 KiB, two workgroups
+                                             // per CU, most of a short segment's copies in flight at once
 };
 inline int lds_bytes(const TileConfig& c, bool sk = false) { return (sk ? c.sk_stages : 2) * (c.bm + c.bn) * kStepBytes; }
 

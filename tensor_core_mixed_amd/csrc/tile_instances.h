@@ -16,6 +16,7 @@ TileLauncher pick_tile(int config, bool b_kmajor) {
     case 3: return b_kmajor ? &launch_tile<DT, 3, true> : &launch_tile<DT, 3, false>;
     case 4: return b_kmajor ? &launch_tile<DT, 4, true> : &launch_tile<DT, 4, false>;
     case 5: return b_kmajor ? &launch_tile<DT, 5, true> : &launch_tile<DT, 5, false>;
+    case 6: return b_kmajor ? &launch_tile<DT, 6, true> : &launch_tile<DT, 6, false>;
     default: return nullptr;
     }
 }
@@ -29,6 +30,7 @@ int pick_sk_occupancy(int config, bool b_kmajor) {
     case 3: return b_kmajor ? sk_occupancy<DT, 3, true>() : sk_occupancy<DT, 3, false>();
     case 4: return b_kmajor ? sk_occupancy<DT, 4, true>() : sk_occupancy<DT, 4, false>();
     case 5: return b_kmajor ? sk_occupancy<DT, 5, true>() : sk_occupancy<DT, 5, false>();
+    case 6: return b_kmajor ? sk_occupancy<DT, 6, true>() : sk_occupancy<DT, 6, false>();
     default: return 0;
     }
 }
@@ -42,6 +44,7 @@ TileLauncher pick_conv(int config) {
     case 3: return &launch_conv<DT, 3>;
     case 4: return &launch_conv<DT, 4>;
     case 5: return &launch_conv<DT, 5>;
+    case 6: return &launch_conv<DT, 6>;
     default: return nullptr;
     }
 }
@@ -55,6 +58,7 @@ int pick_conv_occupancy(int config) {
     case 3: return conv_occupancy<DT, 3>();
     case 4: return conv_occupancy<DT, 4>();
     case 5: return conv_occupancy<DT, 5>();
+    case 6: return conv_occupancy<DT, 6>();
     default: return 0;
     }
 }
@@ -68,6 +72,7 @@ GroupLauncher pick_group(int config, bool b_kmajor) {
     case 3: return b_kmajor ? &launch_group<DT, 3, true> : &launch_group<DT, 3, false>;
     case 4: return b_kmajor ? &launch_group<DT, 4, true> : &launch_group<DT, 4, false>;
     case 5: return b_kmajor ? &launch_group<DT, 5, true> : &launch_group<DT, 5, false>;
+    case 6: return b_kmajor ? &launch_group<DT, 6, true> : &launch_group<DT, 6, false>;
     default: return nullptr;
     }
 }

@@ -663,6 +663,9 @@ struct TileKernel {
     // The same for a count known at run time, 0 <= steps <= NST - 1 (the
     // tail of the loop and the prologue).
     __device__ __forceinline__ static void wait_copies(int steps) {
+        if constexpr (NST - 1 >= 5) {
+            if (steps >= 5) return wait_copies<5>();
+        }
         if constexpr (NST - 1 >= 4) {
             if (steps >= 4) return wait_copies<4>();
         }
@@ -675,7 +678,7 @@ struct TileKernel {
         if (steps >= 1) return wait_copies<1>();
         wait_copies<0>();
     }
-    static_assert(NST <= 5, "wait_copies covers up to five stages");
+    static_assert(NST <= 6, "wait_copies covers up to six stages");
 
     // One K-step kt from stage st, the copies of steps kt+1 .. kt+NST-1
     // issued earlier.  DMA: issue the copies of step kt+NST into stage st

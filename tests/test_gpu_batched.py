@@ -106,7 +106,7 @@ def _case(p, **kw):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("mode", [1, 2])
 def test_batched_every_config_and_mode(dtype, config, mode):
     T.tcm_set_option("force_config", config)
@@ -127,7 +127,7 @@ def test_batched_shared_b_and_bias(dtype):
 
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("sk_grid", [5, 37, 200])
-@pytest.mark.parametrize("config", [4, 5])
+@pytest.mark.parametrize("config", [4, 5, 6])
 @pytest.mark.parametrize("fixup", [1, 2])
 def test_batched_streamk_splits_across_entries(dtype, sk_grid, config, fixup):
     """One Stream-K grid over the tiles of all entries; segments cross entry

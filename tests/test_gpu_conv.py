@@ -97,7 +97,7 @@ def _run_check(p, **kw):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("mode", [1, 2])
 def test_conv_every_config_and_mode(dtype, config, mode):
     """Every tile config in both modes: 3x3, padding 1, ragged pixel count and channel count."""
@@ -109,7 +109,7 @@ def test_conv_every_config_and_mode(dtype, config, mode):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("config", [1, 4, 5])
+@pytest.mark.parametrize("config", [1, 4, 5, 6])
 def test_conv_streamk_fixup_kernel(dtype, config):
     """Stream-K convolution with many segments per tile, split tiles summed
     by the second kernel."""
@@ -191,7 +191,7 @@ def test_conv_16bit_output(variant, mode):
 
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("sk_grid", [3, 50, 300])
-@pytest.mark.parametrize("config", [4, 5])
+@pytest.mark.parametrize("config", [4, 5, 6])
 def test_conv_streamk_split_tiles(dtype, sk_grid, config):
     """Stream-K with grids that split tiles at arbitrary taps."""
     T.tcm_set_option("force_config", config)

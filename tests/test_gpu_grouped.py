@@ -83,7 +83,7 @@ SHAPES = [(37, 64), (0, 128), (130, 48), (1, 208), (64, 64), (200, 96)]  # ragge
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("mode", [1, 2])
 def test_grouped_every_config_and_mode(dtype, config, mode):
     T.tcm_set_option("force_config", config)
@@ -96,7 +96,7 @@ def test_grouped_every_config_and_mode(dtype, config, mode):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("config", [4, 5])
+@pytest.mark.parametrize("config", [4, 5, 6])
 @pytest.mark.parametrize("sk_grid", [3, 37, 200])
 @pytest.mark.parametrize("fixup", [1, 2])
 def test_grouped_streamk_splits_across_entries(dtype, config, sk_grid, fixup):

@@ -67,7 +67,7 @@ def test_ragged_tiles_and_k_tail(dtype, shape, b_col):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("mode", [1, 2])
 def test_every_config_and_mode(dtype, config, mode):
     """Each tile config, data-parallel and Stream-K, on a shape with edges in M, N and K."""
@@ -103,7 +103,7 @@ def test_pingpong_loop_step_counts(dtype, ksteps, mode):
 
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("sk_grid", [3, 7, 64, 301])
-@pytest.mark.parametrize("config", [1, 5])
+@pytest.mark.parametrize("config", [1, 5, 6])
 @pytest.mark.parametrize("fixup", [1, 2])
 def test_streamk_many_segments_per_tile(dtype, sk_grid, config, fixup):
     """Small persistent grids split each tile over several workgroups (and
@@ -124,7 +124,7 @@ def test_streamk_many_segments_per_tile(dtype, sk_grid, config, fixup):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
-@pytest.mark.parametrize("config", [1, 4, 5])
+@pytest.mark.parametrize("config", [1, 4, 5, 6])
 def test_fixup_kernel_bit_identical_to_last_arrival(dtype, config):
     """Both ways of finishing a split tile add the same partials in the same
     order: the outputs agree bit for bit, floats included."""
@@ -267,7 +267,7 @@ def _epi_id(v):
 
 
 @pytest.mark.parametrize("variant", EPI_VARIANTS, ids=_epi_id)
-@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("config", [0, 1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("mode", [1, 2])
 def test_init_tensor_and_16bit_c_every_config_and_mode(variant, config, mode):
     """C_in as the initial value and/or C stored in f16 / bf16, on every tile
@@ -296,7 +296,7 @@ def test_init_tensor_and_16bit_c_every_config_and_mode(variant, config, mode):
 
 
 @pytest.mark.parametrize("variant", EPI_VARIANTS, ids=_epi_id)
-@pytest.mark.parametrize("config", [4, 5])
+@pytest.mark.parametrize("config", [4, 5, 6])
 @pytest.mark.parametrize("fixup", [1, 2])
 def test_init_tensor_streamk_many_segments(variant, config, fixup):
     """Only the k = 0 segment of a split tile may add C_in (and the bias),
