@@ -30,7 +30,6 @@ constexpr double kStepOverhead = 96.0;          // barrier + wait per K-step
 constexpr double kStepLatency = 500.0;          // lone workgroup: fixed part of a K-step ...
 constexpr double kStepBytesPerClk = 16.0;       // ... plus its copies at this rate
 constexpr double kFixupLatency = 1500.0;        // one device-coherent round trip per partial tile read back
-constexpr double kFixupKernel = 9000.0;         // a fix-up kernel: its launch and one read of the partials (~3.8 us)
 // Stream-K workgroups start their segments at different k, so tiles that
 // share an operand panel no longer read it from L2 at the same time.  For
 // 128x128 tiles (two workgroups per CU) a split K-step then streams its
@@ -137,7 +136,7 @@ int64_t tile_count(const Problem& p, int ci) {
     return p.group ? p.group_tiles[ci] : cdiv(p.M, c.bm) * cdiv(p.N, c.bn) * std::max<int64_t>(p.batch, 1);
 }
 
-Estimate estimate(const Problem& p, int ci, int cus, int force_mode, int sk_grid, int sk_occ_known, int sk_fixup) {
+Estimate estimate(const Problem& p, int ci, int cus, int force_mode, int sk_grid, int sk_occ_known) {
     const TileConfig& c = kConfigs[ci];
     const int dt = p.dtype;
     const int bke = bk_elems(dt);
@@ -191,8 +190,12 @@ Estimate estimate(const Problem& p, int ci, int cus, int force_mode, int sk_grid
         // Tiles that share an operand panel then stream it through L2
         // together, as data-parallel tiles do (1536^2 x 16384 on 128x128
         // units: 107.5 us at 432 = 144 x 3 workgroups, 116.3 us at 512).
+        // Tiles of different entries of a batch or group share no operand
+        // panel, so only single products are aligned (an aligned 128x128 plan
+        // for eight 16-row products took 54.6 us against 48.7 us on 64x64
+        // Stream-K units).
         bool aligned = false;
-        if (sk_grid <= 0 && T < grid) {
+        if (sk_grid <= 0 && T < grid && !p.group && p.batch <= 1) {
             const int64_t S = grid / T;
             if (S >= 2 && 4 * T * S >= 3 * grid) {
                 grid = T * S;
@@ -216,14 +219,10 @@ Estimate estimate(const Problem& p, int ci, int cus, int force_mode, int sk_grid
         // only rows below M travel (skinny problems move a sliver of each partial)
         const double rows_frac = std::min(1.0, (double)std::max<int64_t>(p.M, 1) / c.bm);
         // the last arrival's reads are latency-bound: about one memory round
-        // trip per segment (the next partial's loads overlap the current add);
-        // a fix-up kernel (six or more segments a tile, as make_plan decides)
-        // costs its launch and one read of every partial instead
-        const bool fixup_kernel = sk_fixup == 2 || (sk_fixup == 0 && I >= 6 * per_wg);
-        const double partial_reads = nseg * rows_frac * partial / kL2BytesPerClk;
-        const double fixup = !splits ? 0.0
-                             : fixup_kernel ? rows_frac * partial / kL2BytesPerClk + kFixupKernel + partial_reads
-                                            : rows_frac * partial / kL2BytesPerClk + nseg * kFixupLatency + partial_reads;
+        // trip per segment (the next partial's loads overlap the current add).
+        // A fix-up kernel (six or more segments) costs about as much: its
+        // launch and one read of the partials; the model keeps one estimate.
+        const double fixup = splits ? rows_frac * partial / kL2BytesPerClk + nseg * (kFixupLatency + rows_frac * partial / kL2BytesPerClk) : 0.0;
         // a lone Stream-K workgroup keeps sk_stages - 1 K-steps of copies in
         // flight, which divides the latency part of its step
         const double sk_lone = kStepLatency / (c.sk_stages - 1) + (c.bm + c.bn) * (double)kStepBytes / kStepBytesPerClk;
@@ -247,6 +246,9 @@ Estimate estimate(const Problem& p, int ci, int cus, int force_mode, int sk_grid
     // the 8-wave 256x256 config runs out of registers in its Stream-K variant
     // (partial-tile fix-up on top of 128 accumulators per wave): data-parallel only
     if (c.wm * c.wn > 4) return dp;
+    // the 32-row deep unit exists for its Stream-K pipeline (as data-parallel
+    // tiles it is no faster than 64x64 ones on the products it may serve)
+    if (c.bm < 64 && c.sk_stages > 2) return sk;
     return sk.cycles < 0.97 * dp.cycles ? sk : dp;
 }
 
@@ -270,8 +272,11 @@ bool make_plan(const Problem& p, const Options& o, int cus, Plan* out) {
             // spills registers): a forced Stream-K picks among the others
             // unless that config is forced too
             if (o.force_mode == 2 && o.force_config < 0 && kConfigs[c].wm * kConfigs[c].wn > 4) continue;
+            // the 32-row deep unit is planned for products of one tile row
+            // (M <= 32; a group counts all its rows) unless it is forced
+            if (o.force_config < 0 && kConfigs[c].bm < 64 && kConfigs[c].sk_stages > 2 && p.M > kConfigs[c].bm) continue;
             if (p.group ? !p.group_ok[c] : !tile_eligible(p, kConfigs[c])) continue;
-            Estimate e = estimate(p, c, cus, o.force_mode, o.sk_grid, o.sk_occ[c], o.sk_fixup);
+            Estimate e = estimate(p, c, cus, o.force_mode, o.sk_grid, o.sk_occ[c]);
             if (e.cycles < best_e.cycles * 0.999) {
                 best = c;
                 best_e = e;

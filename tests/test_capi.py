@@ -127,11 +127,12 @@ def test_planner_skinny_uses_streamk(M):
     assert p["config"] in (5, 6) and p["bm"] <= 64 and p["bn"] == 64
 
 
-@pytest.mark.parametrize("M,fixup", [(1, 1), (16, 1), (64, None), (256, 0)])
-def test_planner_fixup_kernel_for_many_segments(M, fixup):
+@pytest.mark.parametrize("M,N,K,fixup", [(1, 4096, 4096, 1), (16, 4096, 4096, 1), (64, 4096, 4096, None),
+                                         (256, 4096, 4096, None), (1536, 1536, 16384, 0)])
+def test_planner_fixup_kernel_for_many_segments(M, N, K, fixup):
     """Split tiles with six or more segments are summed by a second kernel;
     with fewer, by their last arrival.  The option overrides either way."""
-    p = T.tcm_plan(M, 4096, 4096, 4096, 4096, 4096, T.TCM_F16_F32)
+    p = T.tcm_plan(M, N, K, K, N, N, T.TCM_F16_F32)
     per_wg = -(-p["sk_tiles"] * p["iters_per_tile"] // p["grid"])
     assert p["mode"] == 2 and p["fixup_kernel"] == int(p["iters_per_tile"] >= 6 * per_wg)
     if fixup is not None:
@@ -139,7 +140,7 @@ def test_planner_fixup_kernel_for_many_segments(M, fixup):
     try:
         for opt, want in ((1, 0), (2, 1)):
             assert T.tcm_set_option("sk_fixup", opt) == T.TCM_OK
-            assert T.tcm_plan(M, 4096, 4096, 4096, 4096, 4096, T.TCM_F16_F32)["fixup_kernel"] == want
+            assert T.tcm_plan(M, N, K, K, N, N, T.TCM_F16_F32)["fixup_kernel"] == want
     finally:
         T.tcm_set_option("sk_fixup", 0)
     # data-parallel plans have nothing to sum
@@ -184,6 +185,11 @@ def test_deep_config_is_the_small_tile_with_more_stages():
         # the skinny unit: 32 x 64, two waves
         bm, bn, _, waves = T.tcm_config_info(6, dt)
         assert (bm, bn, waves) == (32, 64, 2)
+    # it serves single-row products only, and as Stream-K
+    p = T.tcm_plan(16, 4096, 4096, 4096, 4096, 4096, T.TCM_F16_F32)
+    assert p["config"] == 6 and p["mode"] == 2
+    assert T.tcm_plan(64, 4096, 4096, 4096, 4096, 4096, T.TCM_F16_F32)["config"] != 6
+    assert T.tcm_plan(512, 512, 512, 512, 512, 512, T.TCM_F16_F32)["config"] != 6
 
 
 def test_planner_keeps_split_128_tiles_for_phase_aligned_shapes():
