@@ -18,6 +18,7 @@ def _reset_options():
     T.tcm_set_option("force_mode", 0)
     T.tcm_set_option("force_config", -1)
     T.tcm_set_option("sk_grid", 0)
+    T.tcm_set_option("sk_fixup", 0)
 
 
 def _dev(x):
@@ -63,20 +64,24 @@ def test_two_streams_at_once(mode):
     b.check()
 
 
-@pytest.mark.parametrize("mode", [1, 2])
-def test_graph_capture_replays(mode):
+@pytest.mark.parametrize("mode,fixup", [(1, 0), (2, 1), (2, 2)])
+def test_graph_capture_replays(mode, fixup):
     """A call captured into a HIP graph (the split-k workspace already exists
     for the stream, so capture allocates nothing) gives the eager result on
-    every replay; eager work and synchronisations run between the replays."""
+    every replay; eager work and synchronisations run between the replays.
+    With fixup 2 the call is two launches: Stream-K and its fix-up kernel."""
     T.tcm_set_option("force_mode", mode)
     T.tcm_set_option("force_config", 4)
+    T.tcm_set_option("sk_fixup", fixup)
     c = Call(S.small_problem(S.F16, 128, 256, 1024, seed=402, bias=True, relu=True))
     s = torch.cuda.Stream()
     c(s)  # warm-up: plans, and creates this stream's workspace
     torch.cuda.synchronize()
     eager = c.C.clone()
     c.check()
-    say(f"[case] graph capture, mode {mode}: {T.tcm_last_plan()}")
+    say(f"[case] graph capture, mode {mode}, fixup {fixup}: {T.tcm_last_plan()}")
+    if mode == 2:
+        assert ("fixup=kernel" in T.tcm_last_plan()) == (fixup == 2)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
         c(s)
