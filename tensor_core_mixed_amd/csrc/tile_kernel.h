@@ -509,8 +509,11 @@ struct TileKernel {
 
     // Initial accumulator of a tile segment: with `seed` (the segment that
     // starts at k = 0), bias[col] plus, with accum, C's current value; else 0.
-    __device__ __forceinline__ static void init_acc(Acc (&acc)[FM][FN], const TileArgs& a, bool seed, int m0, int n0, int wm,
-                                                    int wn, int lane) {
+    // STAGED: a 16-bit C_in goes through LDS (data-parallel kernels; the
+    // Stream-K kernels keep the direct loads, which cost them no registers)
+    template <bool STAGED>
+    __device__ __forceinline__ static void init_acc(Acc (&acc)[FM][FN], const TileArgs& a, lds_char* smem, bool seed, int m0,
+                                                    int n0, int wm, int wn, int lane) {
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             AccS v = 0;
@@ -524,6 +527,12 @@ struct TileKernel {
                 for (int r = 0; r < 16; ++r) acc[fm][fn][r] = v;
         }
         if (seed && a.accum) {
+            if constexpr (DT != I8 && STAGED) {
+                if (a.c_type != C_ACC && (a.ldc & 7) == 0) {
+                    add_c16_staged(acc, a, smem, m0, n0, wm, wn, lane);
+                    return;
+                }
+            }
             const CView cv = c_view(a, m0, n0, wm, wn, lane);
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm)
@@ -534,6 +543,52 @@ struct TileKernel {
                     for (int fn = 0; fn < FN; ++fn) acc[fm][fn][r] += load_c(a, cv, cv.coff[fn] + roff);
                 }
         }
+    }
+
+    // C_in stored in 16 bits: 2-byte loads straight into the accumulator
+    // layout cost 30 us of 133 on a 4096^3 bf16 product (32 MB of C), so the
+    // tile is staged through LDS, which the main loop has not started to
+    // use: 16-byte coalesced direct-to-LDS loads of C's rows (a row-major
+    // BM x BN tile), then each lane reads its elements.  Rows past M read as
+    // zeros (descriptor range); chunks past N are never used.  The main
+    // loop's first barrier orders these reads before its copies.  With
+    // Stream-K a segment that starts at k = 0 would need the same (C_in is
+    // added once per tile), but there the extra code costs the 128x128
+    // kernel register spills, so those kernels load C_in directly.
+    __device__ __forceinline__ static void add_c16_staged(Acc (&acc)[FM][FN], const TileArgs& a, lds_char* smem, int m0,
+                                                          int n0, int wm, int wn, int lane) {
+        constexpr int ROWB = BN * 2;    // bytes of one staged row
+        constexpr int CPRC = ROWB / 16; // 16-byte chunks per row
+        constexpr int NI = BM * CPRC / NT;  // copy instructions per wave
+        static_assert(BM * ROWB <= LDS && (BM * CPRC) % NT == 0, "a 16-bit C tile fills the LDS stages in whole wave copies");
+        const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int64_t bytes = ((int64_t)(a.M - m0) * a.ldc - n0) * 2;
+        const int nrec = bytes < (int64_t)kOOB ? (int)bytes : (int)kOOB;
+        const __amdgpu_buffer_rsrc_t r =
+            __builtin_amdgcn_make_buffer_rsrc((char*)a.C + ((int64_t)m0 * a.ldc + n0) * 2, (short)0, nrec, kRsrcWord3);
+        __syncthreads();  // a previous segment's readers are done with LDS
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int pslot = i * NT + tid, row = pslot / CPRC, c = pslot % CPRC;
+            const unsigned off = n0 + c * 8 < a.N ? (unsigned)(row * a.ldc * 2 + c * 16) : kOOB;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(smem + (i * NT + wave * 64) * 16), 16,
+                                                     off, 0, 0, 0);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        const bool bf = a.c_type == C_BF16;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) {
+                const int row = wm * TM + fm * 32 + 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn) {
+                    const int col = wn * TN + fn * 32 + (lane & 31);
+                    const unsigned short h = *(const __attribute__((address_space(3))) unsigned short*)(smem + row * ROWB + col * 2);
+                    acc[fm][fn][rr] += bf ? __builtin_bit_cast(float, (unsigned)h << 16) : (float)__builtin_bit_cast(_Float16, h);
+                }
+            }
     }
 
     template <int CT>
@@ -820,7 +875,7 @@ struct TileKernel {
         int tm, tn;
         const TileArgs e = tile_of(g, xcd_order(blockIdx.x, work_tiles(g)), tm, tn);
         const int m0 = tm * BM, n0 = tn * BN;
-        init_acc(acc, e, true, m0, n0, wm, wn, lane);
+        init_acc<true>(acc, e, smem, true, m0, n0, wm, wn, lane);
         mainloop(acc, e, smem, m0, n0, 0, e.iters, wave, lane);
         store_tile(acc, e, m0, n0, wm, wn, lane);
     }
@@ -852,7 +907,7 @@ struct TileKernel {
             int tm, tn;
             const TileArgs e = tile_of(g, xcd_order(a.dp_tiles + (int)tsk, work_tiles(g)), tm, tn);
             const int m0 = tm * BM, n0 = tn * BN;
-            init_acc(acc, e, k_lo == 0, m0, n0, wm, wn, lane);
+            init_acc<false>(acc, e, smem, k_lo == 0, m0, n0, wm, wn, lane);
             mainloop(acc, e, smem, m0, n0, k_lo, k_hi, wave, lane);
             it += k_hi - k_lo;
             if (k_lo == 0 && k_hi == I) {
