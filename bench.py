@@ -354,25 +354,6 @@ def cold_us(call, calls, stream_obj):
     return round(sorted(t)[len(t) // 2], 2)
 
 
-def gpu_clock():
-    """Current shader clock level from the driver's sysfs table (the line marked
-    with '*' in pp_dpm_sclk), or None.  A plain file read: no other program is
-    started from this process."""
-    import glob
-    import re
-    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
-        try:
-            with open(path) as f:
-                for line in f:
-                    if "*" in line:
-                        m = re.search(r"(\d+)\s*Mhz", line, re.IGNORECASE)
-                        if m:
-                            return m.group(1) + " MHz"
-        except OSError:
-            continue
-    return None
-
-
 def _oracle_sampled_check(p, g, C):
     """(CPU leg) The sampled entries (4096 seeded + rows 0 and M-1) of C after one
     call from the initial state, against the oracle's values."""
@@ -485,10 +466,8 @@ def run_bench_conv(args):
     torch.cuda.synchronize()
     plan = T.tcm_last_plan()
     print(f"[bench] plan: {plan}", file=sys.stderr, flush=True)
-    clock_before = gpu_clock()
     ms, wall_ms = time_steps(job.call, args.steps, args.warmup, stream_obj)
     calls = per_call_us(job.call, args.steps, stream_obj)
-    clock_after = gpu_clock()
     value = p.flops / (ms * 1e-3) / 1e12
     print(f"[bench] {ms:.4f} ms/step, {value:.1f} T(FL)OP/s", file=sys.stderr, flush=True)
     roof = roofline(p.dtype, p.flops, p.alg_bytes, ms, load_traffic(p, plan))
@@ -508,8 +487,7 @@ def run_bench_conv(args):
         "data": "synthetic",
         "config": {"workload": describe_conv(p), "gemm_M": g.M, "gemm_N": g.N, "gemm_K": g.K, "seed": p.seed,
                    "dist": p.dist, "plan": plan, "wall_ms_per_step": round(wall_ms, 5), "per_call_us": calls,
-                   "hbm_frac": round(p.alg_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
-                   "sclk_before_after": [clock_before, clock_after], "parity": parity},
+                   "hbm_frac": round(p.alg_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4), "parity": parity},
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -577,10 +555,8 @@ def run_bench(args):
     torch.cuda.synchronize()
     plan = T.tcm_last_plan()
     print(f"[bench] plan: {plan}", file=sys.stderr, flush=True)
-    clock_before = gpu_clock()
     ms, wall_ms = time_steps(call, args.steps, args.warmup, stream_obj)
     calls = per_call_us(call, args.steps, stream_obj)
-    clock_after = gpu_clock()
     flops = p.flops
     unit_scale = 1e12
     value = flops / (ms * 1e-3) / unit_scale
@@ -601,8 +577,7 @@ def run_bench(args):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": DTYPE_NAME[p.dtype],
         "data": "synthetic",
         "config": {"workload": describe(p), "M": p.M, "N": p.N, "K": p.K, "seed": p.seed, "dist": p.dist,
-                   "plan": plan, "wall_ms_per_step": round(wall_ms, 5), "per_call_us": calls,
-                   "sclk_before_after": [clock_before, clock_after], "parity": parity},
+                   "plan": plan, "wall_ms_per_step": round(wall_ms, 5), "per_call_us": calls, "parity": parity},
         "roofline": roof, "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -28,9 +28,16 @@
  * so concurrent calls on different streams are independent, plus the
  * process-wide switches and tuning table below (mutex-protected).  The
  * workspace grows on demand (hipMalloc, plus a zero-fill kernel for its
- * counters); a call whose plan fits the stream's existing workspace
+ * counters), never synchronising; an outgrown buffer is kept, not freed,
+ * until tcm_release_workspace, because kernels or graphs enqueued earlier may
+ * still use it.  A call whose plan fits the stream's existing workspace
  * allocates nothing and issues only kernel launches, so it can be captured
- * into a HIP graph after one warm-up call of the same shape on that stream.
+ * into a HIP graph after one warm-up call of the same shape on that stream; a
+ * call that would grow the workspace while its stream is capturing returns
+ * TCM_ERR_NOT_SUPPORTED.  A captured graph uses the workspace of the stream
+ * it was captured on: its replays must not run at the same time as other
+ * calls (eager or replayed) on that stream's workspace, e.g. replay it on the
+ * same stream.
  *
  * Errors are returned, never raised; argument checks run before any HIP call.
  */
@@ -47,7 +54,8 @@ extern "C" {
 typedef enum {
     TCM_OK = 0,
     TCM_ERR_INVALID_VALUE = 1, /* a bad size, leading dimension, pointer, flag or option */
-    TCM_ERR_NOT_SUPPORTED = 2, /* a valid request this build cannot serve (none today) */
+    TCM_ERR_NOT_SUPPORTED = 2, /* a valid request that cannot be served as asked: workspace
+                                  growth while the stream is being captured into a graph */
     TCM_ERR_HIP = 3,           /* a HIP runtime error (no device, launch failure, ...) */
     TCM_ERR_ALLOC = 4          /* the split-k workspace could not be allocated */
 } tcm_status;
@@ -103,14 +111,19 @@ enum { TCM_EPI_NONE = 0, TCM_EPI_BIAS = 1, TCM_EPI_RELU = 2, TCM_EPI_BIAS_RELU =
  *   epilogue     TCM_EPI_* flags (any combination).
  *   stream       hipStream_t as void* (NULL: null stream).
  *
- * Any alignment and any leading dimension is served; aligned, 16-byte
- * multiple layouts take the fast path.
+ * Any alignment and any leading dimension is served (je-d.tistory.com, the
+ * auto-tensorcore note: code off the matrix-core fast path is slower but
+ * functionally equal): 16-byte aligned pointers with 16-byte multiple
+ * layouts take the tiled fast path; anything else runs on the generic
+ * kernel, which reads and writes single bytes when a pointer is not a
+ * multiple of its element size.
  * Returns TCM_OK once the work is enqueued; TCM_ERR_INVALID_VALUE for
  * negative sizes, too-small leading dimensions, a NULL operand with a
  * non-empty extent, unknown dtype/flags/epilogue, both output type flags or
- * an output type flag with int8, TCM_EPI_BIAS with a NULL bias, a pointer
- * not aligned to its element, or C overlapping an input; TCM_ERR_ALLOC if
- * the split-k workspace cannot be allocated; TCM_ERR_HIP on a launch error.
+ * an output type flag with int8, TCM_EPI_BIAS with a NULL bias, or C
+ * overlapping an input; TCM_ERR_ALLOC if the split-k workspace cannot be
+ * allocated; TCM_ERR_NOT_SUPPORTED if it would have to grow while the stream
+ * is capturing; TCM_ERR_HIP on a launch error.
  */
 int tcm_gemm(int64_t M, int64_t N, int64_t K,
              const void* A, int64_t lda,
@@ -288,6 +301,16 @@ typedef struct {
 int tcm_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
              int dtype, int epilogue, int aligned, tcm_plan_info* out);
 
+/*
+ * tcm_plan_batched -- the plan tcm_gemm_batched would use for `batch`
+ * products of this shape (1 <= batch < 2^31; the strides do not enter the
+ * plan, only whether every entry is 16-byte aligned, `aligned`).  `tiles`
+ * counts the tiles of all entries, which share one work list.  tcm_plan is
+ * tcm_plan_batched with batch 1.  Returns TCM_OK or TCM_ERR_INVALID_VALUE.
+ */
+int tcm_plan_batched(int64_t batch, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                     int64_t ldc, int dtype, int epilogue, int aligned, tcm_plan_info* out);
+
 /* Number of rows of the tile table, and row i as (bm, bn, bk, waves).  Two
  * rows may share a shape and differ in the depth of their split-k (Stream-K)
  * pipeline: LDS stages of copies in flight per workgroup, traded against
@@ -355,7 +378,9 @@ void tcm_tune_clear(void);
  * terminated, truncated to len).  Returns the full length. */
 int tcm_last_plan(char* buf, int64_t len);
 
-/* Free every cached split-k workspace (waits for their streams first). */
+/* Free every cached split-k workspace, outgrown ones included (waits for
+ * every device holding one to finish its work first).  No call may run or be
+ * replayed concurrently. */
 void tcm_release_workspace(void);
 
 /* Library version string. */

@@ -73,6 +73,8 @@ def lib():
         L.tcm_get_option.restype = i64
         L.tcm_plan.argtypes = [i64, i64, i64, i64, i64, i64, ci, ci, ci, ctypes.POINTER(_PlanInfo)]
         L.tcm_plan.restype = ci
+        L.tcm_plan_batched.argtypes = [i64, i64, i64, i64, i64, i64, i64, ci, ci, ci, ctypes.POINTER(_PlanInfo)]
+        L.tcm_plan_batched.restype = ci
         L.tcm_config_count.restype = ci
         L.tcm_config_info.argtypes = [ci, ci] + [ctypes.POINTER(ctypes.c_int32)] * 4
         L.tcm_config_info.restype = ci
@@ -131,6 +133,15 @@ def tcm_plan(M, N, K, lda, ldb, ldc, dtype, epilogue=0, aligned=True):
     st = lib().tcm_plan(M, N, K, lda, ldb, ldc, dtype, epilogue, int(aligned), ctypes.byref(info))
     if st != TCM_OK:
         raise TcmError(st, "tcm_plan")
+    return {f: getattr(info, f) for f, _ in _PlanInfo._fields_}
+
+
+def tcm_plan_batched(batch, M, N, K, lda, ldb, ldc, dtype, epilogue=0, aligned=True):
+    """The plan tcm_gemm_batched would use for `batch` entries (host-only query) as a dict."""
+    info = _PlanInfo()
+    st = lib().tcm_plan_batched(batch, M, N, K, lda, ldb, ldc, dtype, epilogue, int(aligned), ctypes.byref(info))
+    if st != TCM_OK:
+        raise TcmError(st, "tcm_plan_batched")
     return {f: getattr(info, f) for f, _ in _PlanInfo._fields_}
 
 

@@ -3,7 +3,10 @@
 // gather does not take (channels not a multiple of the K-step, huge inputs).  It keeps the promise that a problem the fast path
 // cannot take still gets the same result, only slower (je-d.tistory.com,
 // the auto-tensorcore note: without the matrix-core rewrite the code is
-// slower but functionally equal).  Structure: 64x64 output tile per
+// slower but functionally equal).  Pointers need no alignment at all: a
+// call whose operand, C or bias pointer is not a multiple of its element
+// size runs the byte-access instance, which reads and writes every element
+// as single bytes.  Structure: 64x64 output tile per
 // workgroup, four waves of 2x2 16x16 MFMA tiles, a 64-byte k-slab per step
 // staged through LDS element by element with bounds checks, bias (plus C's
 // current value with accum) as the accumulator's initial value, ReLU before
@@ -50,11 +53,37 @@ __device__ __forceinline__ void mma16(typename G<DT>::Acc& acc, i4_t a, i4_t b) 
     }
 }
 
+// Element idx of an array of T at p.  BYTES: p may have any alignment, so
+// the element is assembled from single-byte loads (stores likewise).
+template <typename T, bool BYTES>
+__device__ __forceinline__ T ld_elem(const void* p, int64_t idx) {
+    if constexpr (BYTES && sizeof(T) > 1) {
+        const unsigned char* b = (const unsigned char*)p + idx * (int64_t)sizeof(T);
+        unsigned char v[sizeof(T)];
+#pragma unroll
+        for (int i = 0; i < (int)sizeof(T); ++i) v[i] = b[i];
+        return __builtin_bit_cast(T, v);
+    } else {
+        return ((const T*)p)[idx];
+    }
+}
+template <typename T, bool BYTES>
+__device__ __forceinline__ void st_elem(void* p, int64_t idx, T x) {
+    if constexpr (BYTES && sizeof(T) > 1) {
+        unsigned char* b = (unsigned char*)p + idx * (int64_t)sizeof(T);
+        const auto v = __builtin_bit_cast(unsigned char __attribute__((ext_vector_type(sizeof(T)))), x);
+#pragma unroll
+        for (int i = 0; i < (int)sizeof(T); ++i) b[i] = v[i];
+    } else {
+        ((T*)p)[idx] = x;
+    }
+}
+
 // Copy the 64 x slab piece of one operand into LDS as [row][k] (k contiguous).
 // rows index M (for A) or N (for B); `kmajor` says whether the operand is
 // stored with k contiguous (then consecutive threads walk k).
-template <int DT>
-__device__ __forceinline__ void stage(char* lds, const typename G<DT>::T* X, int64_t ld, bool kmajor, int64_t r0,
+template <int DT, bool BYTES>
+__device__ __forceinline__ void stage(char* lds, const void* X, int64_t ld, bool kmajor, int64_t r0,
                                       int64_t rows, int64_t k0, int64_t K) {
     using T = typename G<DT>::T;
     constexpr int ES = sizeof(T);
@@ -65,7 +94,7 @@ __device__ __forceinline__ void stage(char* lds, const typename G<DT>::T* X, int
         else { kk = idx / kTile; r = idx % kTile; }
         const int64_t gr = r0 + r, gk = k0 + kk;
         T v = T(0);
-        if (gr < rows && gk < K) v = kmajor ? X[gr * ld + gk] : X[gk * ld + gr];
+        if (gr < rows && gk < K) v = ld_elem<T, BYTES>(X, kmajor ? gr * ld + gk : gk * ld + gr);
         *(T*)(lds + r * kRow + kk * ES) = v;
     }
 }
@@ -73,8 +102,8 @@ __device__ __forceinline__ void stage(char* lds, const typename G<DT>::T* X, int
 // The same piece of A for a convolution: A is the im2col view of the NHWC
 // input, row = output pixel (n, p, q), column = (r*S + s)*C + c; taps that
 // fall in the zero padding read as zero.
-template <int DT>
-__device__ __forceinline__ void stage_conv(char* lds, const typename G<DT>::T* X, const GenericArgs& a, int64_t r0,
+template <int DT, bool BYTES>
+__device__ __forceinline__ void stage_conv(char* lds, const void* X, const GenericArgs& a, int64_t r0,
                                            int64_t k0) {
     using T = typename G<DT>::T;
     constexpr int ES = sizeof(T);
@@ -89,35 +118,36 @@ __device__ __forceinline__ void stage_conv(char* lds, const typename G<DT>::T* X
             const int64_t c = gk % a.cv_C, rs = gk / a.cv_C, fr = rs / a.cv_S, fs = rs % a.cv_S;
             const int64_t h = p * a.cv_stride_h - a.cv_pad_h + fr * a.cv_dil_h;
             const int64_t w = q * a.cv_stride_w - a.cv_pad_w + fs * a.cv_dil_w;
-            if (h >= 0 && h < a.cv_H && w >= 0 && w < a.cv_W) v = X[((n * a.cv_H + h) * a.cv_W + w) * a.cv_C + c];
+            if (h >= 0 && h < a.cv_H && w >= 0 && w < a.cv_W)
+                v = ld_elem<T, BYTES>(X, ((n * a.cv_H + h) * a.cv_W + w) * a.cv_C + c);
         }
         *(T*)(lds + r * kRow + kk * ES) = v;
     }
 }
 
 // C element (row, col) as the accumulator type, and its store.
-template <int DT>
+template <int DT, bool BYTES>
 __device__ __forceinline__ typename G<DT>::AccS load_c(const GenericArgs& a, int64_t idx) {
     if constexpr (DT == I8) {
-        return ((const int*)a.C)[idx];
+        return ld_elem<int, BYTES>(a.C, idx);
     } else {
-        if (a.c_type == C_F16) return (float)((const _Float16*)a.C)[idx];
-        if (a.c_type == C_BF16) return __builtin_bit_cast(float, (unsigned)((const uint16_t*)a.C)[idx] << 16);
-        return ((const float*)a.C)[idx];
+        if (a.c_type == C_F16) return (float)ld_elem<_Float16, BYTES>(a.C, idx);
+        if (a.c_type == C_BF16) return __builtin_bit_cast(float, (unsigned)ld_elem<uint16_t, BYTES>(a.C, idx) << 16);
+        return ld_elem<float, BYTES>(a.C, idx);
     }
 }
-template <int DT>
+template <int DT, bool BYTES>
 __device__ __forceinline__ void store_c(const GenericArgs& a, int64_t idx, typename G<DT>::AccS v) {
     if constexpr (DT == I8) {
-        ((int*)a.C)[idx] = v;
+        st_elem<int, BYTES>(a.C, idx, v);
     } else {
-        if (a.c_type == C_F16) ((_Float16*)a.C)[idx] = (_Float16)v;
-        else if (a.c_type == C_BF16) ((__bf16*)a.C)[idx] = (__bf16)v;
-        else ((float*)a.C)[idx] = v;
+        if (a.c_type == C_F16) st_elem<_Float16, BYTES>(a.C, idx, (_Float16)v);
+        else if (a.c_type == C_BF16) st_elem<__bf16, BYTES>(a.C, idx, (__bf16)v);
+        else st_elem<float, BYTES>(a.C, idx, v);
     }
 }
 
-template <int DT>
+template <int DT, bool BYTES>
 __global__ __launch_bounds__(256) void generic_gemm_kernel(GenericArgs a) {
     using T = typename G<DT>::T;
     using Acc = typename G<DT>::Acc;
@@ -145,21 +175,21 @@ __global__ __launch_bounds__(256) void generic_gemm_kernel(GenericArgs a) {
     for (int fn = 0; fn < 2; ++fn) {
         AccS v = 0;
         const int64_t col = n0 + wn * 32 + fn * 16 + r16;
-        if (a.has_bias && col < a.N) v = ((const AccS*)a.bias)[col];
+        if (a.has_bias && col < a.N) v = ld_elem<AccS, BYTES>(a.bias, col);
 #pragma unroll
         for (int fm = 0; fm < 2; ++fm)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 acc[fm][fn][r] = v;
                 const int64_t row = m0 + wm * 32 + fm * 16 + 4 * grp + r;
-                if (a.accum && row < a.M && col < a.N) acc[fm][fn][r] += load_c<DT>(a, row * a.ldc + col);
+                if (a.accum && row < a.M && col < a.N) acc[fm][fn][r] += load_c<DT, BYTES>(a, row * a.ldc + col);
             }
     }
 
     for (int64_t k0 = 0; k0 < a.K; k0 += BKE) {
-        if (a.conv) stage_conv<DT>(As, (const T*)a.A, a, m0, k0);
-        else stage<DT>(As, (const T*)a.A, a.lda, !a.a_col, m0, a.M, k0, a.K);
-        stage<DT>(Bs, (const T*)a.B, a.ldb, (bool)a.b_col, n0, a.N, k0, a.K);
+        if (a.conv) stage_conv<DT, BYTES>(As, a.A, a, m0, k0);
+        else stage<DT, BYTES>(As, a.A, a.lda, !a.a_col, m0, a.M, k0, a.K);
+        stage<DT, BYTES>(Bs, a.B, a.ldb, (bool)a.b_col, n0, a.N, k0, a.K);
         __syncthreads();
         i4_t af[2], bf[2];
 #pragma unroll
@@ -184,7 +214,7 @@ __global__ __launch_bounds__(256) void generic_gemm_kernel(GenericArgs a) {
                 const int64_t row = m0 + wm * 32 + fm * 16 + 4 * grp + r;
                 AccS v = acc[fm][fn][r];
                 if (a.relu) v = v > (AccS)0 ? v : (AccS)0;
-                if (row < a.M && col < a.N) store_c<DT>(a, row * a.ldc + col, v);
+                if (row < a.M && col < a.N) store_c<DT, BYTES>(a, row * a.ldc + col, v);
             }
         }
 }
@@ -198,11 +228,25 @@ __global__ void fill_zero_kernel(int* p, int64_t n) {
 int launch_generic(int dtype, const GenericArgs& a, void* stream) {
     const int64_t blocks = (int64_t)a.tiles_m * a.tiles_n * a.batch;
     hipStream_t s = (hipStream_t)stream;
+    const dim3 grid((unsigned)blocks), block(256);
+    const bool bytes = a.bytewise != 0;
     switch (dtype) {
-    case F16: hipLaunchKernelGGL(generic_gemm_kernel<F16>, dim3((unsigned)blocks), dim3(256), 0, s, a); break;
-    case BF16: hipLaunchKernelGGL(generic_gemm_kernel<BF16>, dim3((unsigned)blocks), dim3(256), 0, s, a); break;
-    case F32: hipLaunchKernelGGL(generic_gemm_kernel<F32>, dim3((unsigned)blocks), dim3(256), 0, s, a); break;
-    case I8: hipLaunchKernelGGL(generic_gemm_kernel<I8>, dim3((unsigned)blocks), dim3(256), 0, s, a); break;
+    case F16:
+        if (bytes) hipLaunchKernelGGL((generic_gemm_kernel<F16, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((generic_gemm_kernel<F16, false>), grid, block, 0, s, a);
+        break;
+    case BF16:
+        if (bytes) hipLaunchKernelGGL((generic_gemm_kernel<BF16, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((generic_gemm_kernel<BF16, false>), grid, block, 0, s, a);
+        break;
+    case F32:
+        if (bytes) hipLaunchKernelGGL((generic_gemm_kernel<F32, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((generic_gemm_kernel<F32, false>), grid, block, 0, s, a);
+        break;
+    case I8:
+        if (bytes) hipLaunchKernelGGL((generic_gemm_kernel<I8, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((generic_gemm_kernel<I8, false>), grid, block, 0, s, a);
+        break;
     default: return (int)hipErrorInvalidValue;
     }
     return (int)hipGetLastError();

@@ -125,6 +125,11 @@ struct Workspace {
     int64_t n_counters = 0;
 };
 std::map<std::pair<int, void*>, Workspace> g_ws;  // (device, stream) -> workspace
+// Buffers a workspace outgrew.  A graph captured before the growth still
+// points at them, and kernels enqueued before it may still run on them, so
+// they live until tcm_release_workspace (no free, and no synchronisation, on
+// the calling path).
+std::vector<std::pair<int, void*>> g_retired;  // (device, pointer)
 
 thread_local std::string t_last_plan;
 
@@ -199,38 +204,53 @@ int current_cus() {
 
 // Grow (never shrink) the workspace of (dev, stream); counters start at zero
 // and every split tile's last arrival resets its counter, so they stay zero
-// between calls.
+// between calls.  A buffer that is outgrown is retired, not freed (see
+// g_retired); growth rounds up to a power of two, so a stream retires at most
+// a few dozen buffers however its calls grow.  Growth while the stream is
+// being captured into a graph is refused (TCM_ERR_NOT_SUPPORTED): the
+// allocation would not be part of the graph.
+int64_t round_pow2(int64_t x) {
+    int64_t r = 1;
+    while (r < x) r <<= 1;
+    return r;
+}
 int get_workspace(int dev, void* stream, int64_t partial_bytes, int64_t n_counters, Workspace* out) {
     std::lock_guard<std::mutex> lk(g_mu);
     Workspace& w = g_ws[{dev, stream}];
-    if (w.partial_bytes < partial_bytes) {
-        if (w.partial) {
-            if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return TCM_ERR_HIP;
-            (void)hipFree(w.partial);
-            w.partial = nullptr;
-            w.partial_bytes = 0;
-        }
-        if (hipMalloc(&w.partial, (size_t)partial_bytes) != hipSuccess) {
+    const bool grow_p = w.partial_bytes < partial_bytes, grow_c = w.n_counters < n_counters;
+    if (grow_p || grow_c) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing((hipStream_t)stream, &cs) != hipSuccess) {
             (void)hipGetLastError();
-            w.partial = nullptr;
-            return TCM_ERR_ALLOC;
+            return TCM_ERR_HIP;
         }
-        w.partial_bytes = partial_bytes;
+        if (cs != hipStreamCaptureStatusNone) return TCM_ERR_NOT_SUPPORTED;
     }
-    if (w.n_counters < n_counters) {
-        if (w.counters) {
-            if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return TCM_ERR_HIP;
-            (void)hipFree(w.counters);
-            w.counters = nullptr;
-            w.n_counters = 0;
-        }
-        if (hipMalloc((void**)&w.counters, (size_t)n_counters * sizeof(int)) != hipSuccess) {
+    if (grow_p) {
+        const int64_t bytes = round_pow2(partial_bytes);
+        void* p = nullptr;
+        if (hipMalloc(&p, (size_t)bytes) != hipSuccess) {
             (void)hipGetLastError();
-            w.counters = nullptr;
             return TCM_ERR_ALLOC;
         }
-        if (launch_fill_zero(w.counters, n_counters, stream) != 0) return TCM_ERR_HIP;
-        w.n_counters = n_counters;
+        if (w.partial) g_retired.emplace_back(dev, w.partial);
+        w.partial = p;
+        w.partial_bytes = bytes;
+    }
+    if (grow_c) {
+        const int64_t n = round_pow2(n_counters);
+        int* c = nullptr;
+        if (hipMalloc((void**)&c, (size_t)n * sizeof(int)) != hipSuccess) {
+            (void)hipGetLastError();
+            return TCM_ERR_ALLOC;
+        }
+        if (launch_fill_zero(c, n, stream) != 0) {
+            (void)hipFree(c);
+            return TCM_ERR_HIP;
+        }
+        if (w.counters) g_retired.emplace_back(dev, (void*)w.counters);
+        w.counters = c;
+        w.n_counters = n;
     }
     *out = w;
     return TCM_OK;
@@ -373,13 +393,14 @@ int tcm_streamk_range(int64_t sk_tiles, int64_t iters_per_tile, int32_t grid, in
     return TCM_OK;
 }
 
-int tcm_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype, int epilogue, int aligned,
-             tcm_plan_info* out) {
-    if (!out) return TCM_ERR_INVALID_VALUE;
+int tcm_plan_batched(int64_t batch, int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
+                     int epilogue, int aligned, tcm_plan_info* out) {
+    if (!out || batch < 1 || batch >= ((int64_t)1 << 31)) return TCM_ERR_INVALID_VALUE;
     Problem p;
     int st = check_problem(M, N, K, lda, ldb, ldc, dtype, epilogue, &p);
     if (st != TCM_OK) return st;
     p.aligned = aligned != 0;
+    p.batch = batch;
     Options o = plan_options(p);
     fill_sk_occupancy(p, &o);
     Plan pl;
@@ -399,6 +420,11 @@ int tcm_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t 
     out->fixup_kernel = pl.fixup_kernel ? 1 : 0;
     out->reserved = 0;
     return TCM_OK;
+}
+
+int tcm_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype, int epilogue, int aligned,
+             tcm_plan_info* out) {
+    return tcm_plan_batched(1, M, N, K, lda, ldb, ldc, dtype, epilogue, aligned, out);
 }
 
 int tcm_tile_order(int32_t t, int32_t tiles_m, int32_t tiles_n, int32_t* tm, int32_t* tn) {
@@ -424,16 +450,29 @@ int tcm_last_plan(char* buf, int64_t len) {
 
 void tcm_release_workspace(void) {
     std::lock_guard<std::mutex> lk(g_mu);
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    std::vector<std::pair<int, void*>> all = g_retired;
     for (auto& kv : g_ws) {
-        int cur = 0;
-        (void)hipGetDevice(&cur);
-        (void)hipSetDevice(kv.first.first);
-        (void)hipStreamSynchronize((hipStream_t)kv.first.second);
-        if (kv.second.partial) (void)hipFree(kv.second.partial);
-        if (kv.second.counters) (void)hipFree(kv.second.counters);
-        (void)hipSetDevice(cur);
+        if (kv.second.partial) all.emplace_back(kv.first.first, kv.second.partial);
+        if (kv.second.counters) all.emplace_back(kv.first.first, (void*)kv.second.counters);
     }
+    // every device that holds a buffer finishes its work first (the streams
+    // themselves may have been destroyed by now)
+    std::vector<int> devs;
+    for (auto& x : all)
+        if (std::find(devs.begin(), devs.end(), x.first) == devs.end()) devs.push_back(x.first);
+    for (int d : devs) {
+        (void)hipSetDevice(d);
+        (void)hipDeviceSynchronize();
+    }
+    for (auto& x : all) {
+        (void)hipSetDevice(x.first);
+        (void)hipFree(x.second);
+    }
+    (void)hipSetDevice(cur);
     g_ws.clear();
+    g_retired.clear();
 }
 
 }  // extern "C"
@@ -481,9 +520,10 @@ int gemm_impl(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int
     if (a_ext > 0 && !A) return TCM_ERR_INVALID_VALUE;
     if (b_ext > 0 && !B) return TCM_ERR_INVALID_VALUE;
     if (use_bias && !bias) return TCM_ERR_INVALID_VALUE;
-    // pointers must be aligned to their element
-    if (((uintptr_t)A % es) || ((uintptr_t)B % es) || ((uintptr_t)C % cs) || (use_bias && ((uintptr_t)bias % 4)))
-        return TCM_ERR_INVALID_VALUE;
+    // pointers (and batch strides in bytes) that are not multiples of their
+    // element size are served by the generic kernel with single-byte accesses
+    const bool bytewise = ((uintptr_t)A % es) || ((uintptr_t)B % es) || ((uintptr_t)C % cs) ||
+                          (use_bias && ((uintptr_t)bias % 4));
     if (overlaps(C, c_ext, A, a_ext) || overlaps(C, c_ext, B, b_ext) || (use_bias && overlaps(C, c_ext, bias, bias_ext)))
         return TCM_ERR_INVALID_VALUE;
     // the fast path wants every entry 16-byte aligned
@@ -521,6 +561,7 @@ int gemm_impl(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int
         g.has_bias = use_bias;
         g.accum = (epilogue & TCM_EPI_ACCUM) != 0;
         g.c_type = p.c_type;
+        g.bytewise = bytewise ? 1 : 0;
         g.batch = (int)batch;
         g.stride_a = sa;
         g.stride_b = sb;
@@ -629,8 +670,8 @@ int conv_impl(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R, 
     if (x_ext > 0 && !x) return TCM_ERR_INVALID_VALUE;
     if (f_ext > 0 && !f) return TCM_ERR_INVALID_VALUE;
     if (use_bias && !bias) return TCM_ERR_INVALID_VALUE;
-    if (((uintptr_t)x % es) || ((uintptr_t)f % es) || ((uintptr_t)y % cs) || (use_bias && ((uintptr_t)bias % 4)))
-        return TCM_ERR_INVALID_VALUE;
+    const bool bytewise = ((uintptr_t)x % es) || ((uintptr_t)f % es) || ((uintptr_t)y % cs) ||
+                          (use_bias && ((uintptr_t)bias % 4));
     if (overlaps(y, y_ext, x, x_ext) || overlaps(y, y_ext, f, f_ext) || (use_bias && overlaps(y, y_ext, bias, K * 4)))
         return TCM_ERR_INVALID_VALUE;
     p.aligned = ((uintptr_t)x % 16 == 0) && ((uintptr_t)f % 16 == 0) && ((uintptr_t)y % 16 == 0) &&
@@ -665,6 +706,7 @@ int conv_impl(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R, 
         g.has_bias = use_bias;
         g.accum = 0;
         g.c_type = p.c_type;
+        g.bytewise = bytewise ? 1 : 0;
         g.batch = 1;
         g.tiles_m = (int)((M + 63) / 64);
         g.tiles_n = (int)((K + 63) / 64);
@@ -731,8 +773,6 @@ int grouped_impl(int64_t count, const tcm_group_entry* ent, int64_t K, int dtype
         if (x.M == 0 || x.N == 0) continue;  // nothing read or written
         work = true;
         if (!x.C || (a_ext[i] > 0 && !x.A) || (b_ext[i] > 0 && !x.B) || (use_bias && !x.bias)) return TCM_ERR_INVALID_VALUE;
-        if (((uintptr_t)x.A % es) || ((uintptr_t)x.B % es) || ((uintptr_t)x.C % cs) || (use_bias && ((uintptr_t)x.bias % 4)))
-            return TCM_ERR_INVALID_VALUE;
         aligned = aligned && (uintptr_t)x.A % 16 == 0 && (uintptr_t)x.B % 16 == 0 && (uintptr_t)x.C % 16 == 0 &&
                   (!use_bias || (uintptr_t)x.bias % 16 == 0);
         M_total += x.M;

@@ -168,6 +168,7 @@ struct GenericArgs {
     int has_bias;
     int accum;
     int c_type;
+    int bytewise;  // some pointer is not aligned to its element: single-byte accesses
     int batch;
     int64_t stride_a, stride_b, stride_c, stride_bias;
     int tiles_m, tiles_n;

@@ -49,13 +49,10 @@ BAD = [  # (M, N, K, lda, ldb, ldc, dtype, epilogue, A, B, C, bias)
     (4, 4, 4, 4, 4, 4, 0, 8, 16, 16, 16, 0),            # unknown epilogue
     (4, 4, 4, 4, 4, 4, T.TCM_C_F16 | T.TCM_C_BF16, 0, 16, 16, 16, 0),  # two output types
     (4, 4, 4, 4, 4, 4, T.TCM_I8_I32 | T.TCM_C_F16, 0, 16, 16, 16, 0),  # 16-bit C for int8
-    (4, 4, 4, 4, 4, 4, T.TCM_C_F16, 0, 16, 16, 4097, 0),  # f16 C not aligned to its element
-    (4, 4, 4, 4, 4, 4, 0, 0, 16, 16, 4098, 0),          # f32 C not aligned to its element
     (4, 4, 4, 4, 4, 4, 0, 1, 16, 16, 16, 0),            # bias flag without bias
     (4, 4, 4, 4, 4, 4, 0, 0, 0, 16, 16, 0),             # NULL A
     (4, 4, 4, 4, 4, 4, 0, 0, 16, 0, 16, 0),             # NULL B
     (4, 4, 4, 4, 4, 4, 0, 0, 16, 16, 0, 0),             # NULL C
-    (4, 4, 4, 4, 4, 4, 0, 0, 17, 16, 4096, 0),          # A not aligned to its element
     (4, 4, 4, 4, 4, 4, 0, 0, 4096, 16, 4100, 0),        # C overlaps A
     (4, 4, 4, 4, 4, 4, 0, 0, 16, 4096, 4100, 0),        # C overlaps B
     (4, 4, 4, 4, 4, 4, 0, 1, 16, 256, 4096, 4100),      # C overlaps bias
@@ -80,12 +77,25 @@ def test_valid_call_without_device_reports_hip_error():
     # real-looking (fake) pointers: checks pass, the first HIP call fails
     st = T.tcm_gemm(64, 64, 64, 1 << 20, 64, 2 << 20, 64, 3 << 20, 64, 0, None, 0, None)
     assert st == T.TCM_ERR_HIP
-    # every epilogue combination and a 16-bit C at a 2-byte-aligned address are valid requests
+    # every epilogue combination, and C at any address: element-misaligned
+    # pointers are served (single-byte accesses on the generic kernel)
     for epi in range(8):
         for flags in (0, T.TCM_C_F16, T.TCM_C_BF16):
             st = T.tcm_gemm(64, 64, 64, 1 << 20, 64, 2 << 20, 64, (3 << 20) + 2, 64, T.TCM_BF16_F32 | flags,
                             4 << 20, epi, None)
-            assert st == (T.TCM_ERR_HIP if flags else T.TCM_ERR_INVALID_VALUE), (epi, flags)
+            assert st == T.TCM_ERR_HIP, (epi, flags)
+
+
+@pytest.mark.parametrize("ptrs", [dict(A=(1 << 20) + 1), dict(B=(2 << 20) + 3), dict(C=(3 << 20) + 1),
+                                  dict(C=(3 << 20) + 2), dict(bias=(4 << 20) + 1)],
+                         ids=lambda d: ",".join(f"{k}+{v & 0xff}" for k, v in d.items()))
+@pytest.mark.parametrize("dtype", [T.TCM_F16_F32, T.TCM_F32_F32, T.TCM_I8_I32, T.TCM_BF16_F32 | T.TCM_C_BF16])
+def test_misaligned_pointers_are_valid_requests(ptrs, dtype):
+    """No pointer needs any alignment: the checks pass and the call reaches its first HIP call."""
+    a = dict(A=1 << 20, B=2 << 20, C=3 << 20, bias=4 << 20)
+    a.update(ptrs)
+    st = T.tcm_gemm(64, 64, 64, a["A"], 64, a["B"], 64, a["C"], 64, dtype, a["bias"], T.TCM_EPI_BIAS, None)
+    assert st == T.TCM_ERR_HIP
 
 
 def test_options():
@@ -427,8 +437,6 @@ BAD_CONV = [
     dict(epilogue=T.TCM_EPI_ACCUM),              # accumulate is not offered
     dict(epilogue=T.TCM_EPI_BIAS),               # bias flag without bias
     dict(x=0), dict(f=0), dict(y=0),             # NULL operands
-    dict(x=(1 << 20) + 1),                       # x not aligned to its element
-    dict(y=(3 << 20) + 2),                       # f32 y not aligned to its element
     dict(y=(1 << 20) + 64),                      # y overlaps x
     dict(y=(2 << 20) - 64),                      # y overlaps f (f starts inside y)
     dict(epilogue=T.TCM_EPI_BIAS, bias=(3 << 20) + 256),  # bias inside y
@@ -447,7 +455,8 @@ def test_conv_empty_and_valid_without_device():
     # valid requests reach the first HIP call: fast-path shapes, a channel count
     # the tiled gather does not take, strides and dilations, 16-bit outputs
     for kw in (dict(), dict(C=3), dict(stride_h=2, stride_w=3, dil_h=2, dil_w=2), dict(dtype=T.TCM_BF16_F32 | T.TCM_C_BF16),
-               dict(epilogue=T.TCM_EPI_BIAS | T.TCM_EPI_RELU, bias=4 << 20), dict(dtype=T.TCM_I8_I32), dict(C=0)):
+               dict(epilogue=T.TCM_EPI_BIAS | T.TCM_EPI_RELU, bias=4 << 20), dict(dtype=T.TCM_I8_I32), dict(C=0),
+               dict(x=(1 << 20) + 1), dict(y=(3 << 20) + 2)):  # element-misaligned pointers are served too
         assert _conv(**kw) == T.TCM_ERR_HIP, kw
 
 
@@ -466,7 +475,6 @@ def test_grouped_invalid_arguments():
         [_gentry(C=0)],                                      # NULL C
         [_gentry(), _gentry(A=4 << 20, B=5 << 20, C=(3 << 20) + 64)],  # two C overlap
         [_gentry(), _gentry(A=(3 << 20) + 128, B=5 << 20, C=6 << 20)],  # C of entry 0 overlaps A of entry 1
-        [_gentry(C=(3 << 20) + 2)],                          # f32 C not aligned to its element
     ]
     for ents in bad:
         assert T.tcm_gemm_grouped(ents, 64, 0, 0, None) == T.TCM_ERR_INVALID_VALUE, ents
@@ -480,3 +488,17 @@ def test_grouped_empty_and_valid_without_device():
     assert T.tcm_gemm_grouped([_gentry(M=0, A=0, B=0, C=0), _gentry(N=0, A=0, B=0, C=0)], 64, 0, 0, None) == T.TCM_OK
     ok = [_gentry(), _gentry(M=17, A=4 << 20, B=5 << 20, C=6 << 20), _gentry(M=0, A=0, B=0, C=0)]
     assert T.tcm_gemm_grouped(ok, 64, 0, 0, None) == T.TCM_ERR_HIP
+    assert T.tcm_gemm_grouped([_gentry(C=(3 << 20) + 2)], 64, 0, 0, None) == T.TCM_ERR_HIP  # any alignment
+
+
+def test_plan_batched_counts_every_entry():
+    """tcm_plan_batched plans one work list over all entries; batch 1 is tcm_plan."""
+    one = T.tcm_plan(16, 4096, 4096, 4096, 4096, 4096, T.TCM_F16_F32)
+    assert T.tcm_plan_batched(1, 16, 4096, 4096, 4096, 4096, 4096, T.TCM_F16_F32) == one
+    b8 = T.tcm_plan_batched(8, 16, 4096, 4096, 4096, 4096, 4096, T.TCM_F16_F32)
+    assert b8["kernel"] == 1
+    assert b8["tiles"] == 8 * ((16 + b8["bm"] - 1) // b8["bm"]) * ((4096 + b8["bn"] - 1) // b8["bn"])
+    assert b8["dp_tiles"] + b8["sk_tiles"] == b8["tiles"]
+    for bad in (0, -1, 1 << 31):
+        with pytest.raises(T.TcmError):
+            T.tcm_plan_batched(bad, 16, 4096, 4096, 4096, 4096, 4096, T.TCM_F16_F32)

@@ -32,10 +32,15 @@ def _reset_options():
     T.tcm_set_option("sk_fixup", 0)
 
 
-def run_conv(p, g, x_offset=0):
-    """tcm_conv2d on p's inputs; returns y as an (N*P*Q, K) float / int array and the plan."""
+def run_conv(p, g, x_offset=0, x_byte_offset=0):
+    """tcm_conv2d on p's inputs; returns y as an (N*P*Q, K) float / int array and the plan.
+    x_offset shifts x by elements, x_byte_offset by bytes (any address)."""
     dt = p.dtype
-    kx, px = to_device(g["x"], dt, x_offset)
+    if x_byte_offset:
+        from gpu_util import _bytes_on_device
+        kx, px = _bytes_on_device(g["x"], x_byte_offset)
+    else:
+        kx, px = to_device(g["x"], dt, x_offset)
     kf, pf = to_device(g["f"], dt)
     kb = torch.from_numpy(g["bias"].copy()).cuda() if g["bias"] is not None else None
     c_t = _C_TORCH.get(p.c_type, torch.int32 if dt == S.I8 else torch.float32)
@@ -44,7 +49,7 @@ def run_conv(p, g, x_offset=0):
     code = dt | {"acc": 0, "f16": T.TCM_C_F16, "bf16": T.TCM_C_BF16}[p.c_type]
     epi = (T.TCM_EPI_BIAS if p.bias else 0) | (T.TCM_EPI_RELU if p.relu else 0)
     say(f"[case] conv {p.name} pad={p.pad} stride={p.stride} dil={p.dil} c_type={p.c_type} bias={p.bias} "
-        f"relu={p.relu} x_offset={x_offset} force_config={T.tcm_get_option('force_config')} "
+        f"relu={p.relu} x_offset={x_offset} x_byte_offset={x_byte_offset} force_config={T.tcm_get_option('force_config')} "
         f"force_mode={T.tcm_get_option('force_mode')} generic={T.tcm_get_option('generic')}")
     st = T.tcm_conv2d(p.N, p.H, p.W, p.C, p.K, p.R, p.S, p.pad[0], p.pad[1], p.stride[0], p.stride[1], p.dil[0],
                       p.dil[1], px, pf, y.data_ptr(), code, kb.data_ptr() if kb is not None else None, epi,
@@ -176,6 +181,17 @@ def test_conv_unaligned_input_goes_generic(dtype):
     p = S.small_conv(dtype, 1, 8, 8, BKE[dtype], 16, 3, 3, pad=(1, 1), seed=142, bias=True)
     g = S.generate_conv(p)
     y, plan = run_conv(p, g, x_offset=1)
+    assert "kernel=generic" in plan
+    check_conv(p, g, y)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_conv_input_not_aligned_to_its_element(dtype):
+    """x one byte past an element boundary (three for f32): served by the
+    generic kernel's byte-access instance, not rejected."""
+    p = S.small_conv(dtype, 1, 7, 9, 5, 12, 3, 3, pad=(1, 0), seed=143, bias=True, relu=True)
+    g = S.generate_conv(p)
+    y, plan = run_conv(p, g, x_byte_offset=3 if dtype == S.F32 else 1)
     assert "kernel=generic" in plan
     check_conv(p, g, y)
 

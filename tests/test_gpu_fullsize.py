@@ -8,7 +8,7 @@ import pytest
 
 import synthetic as S
 import tensor_core_mixed_amd as T
-from gpu_util import check, run_tcm, say
+from gpu_util import FULL_SIZE_GUARD, check, run_tcm, say
 
 pytestmark = pytest.mark.gpu
 
@@ -43,6 +43,8 @@ def _check_workload(name, mode):
             ii, jj = S.sample_entries(p)
             err = check(p, g, C, ii, jj)
     say(f"       normalised error {err:.3e}")
+    if p.dtype in (S.F16, S.BF16):
+        assert err <= FULL_SIZE_GUARD, f"{name}: normalised error {err:.3e} above the regression guard {FULL_SIZE_GUARD:.0e}"
     return C, plan
 
 
@@ -72,17 +74,19 @@ def test_int8_full_rows_bit_exact():
 
 @pytest.mark.parametrize("name", list(S.WORKLOADS))
 def test_host_plan_query_matches_launch(name):
-    """tcm_plan (no launch) reports the kernel, config, mode and grid tcm_gemm then launches."""
+    """tcm_plan / tcm_plan_batched (no launch) report the kernel, config, mode and grid the call then launches."""
     p = S.workload(name)
-    if p.batch > 1:
-        pytest.skip("tcm_plan describes a single product")
     code = p.dtype | (T.TCM_A_COLMAJOR if p.a_col else 0) | (T.TCM_B_COLMAJOR if p.b_col else 0)
     code |= {"acc": 0, "f16": T.TCM_C_F16, "bf16": T.TCM_C_BF16}[p.c_type]
     epi = (T.TCM_EPI_BIAS if p.bias else 0) | (T.TCM_EPI_RELU if p.relu else 0) | (T.TCM_EPI_ACCUM if p.accum else 0)
-    q = T.tcm_plan(p.M, p.N, p.K, p.LDA, p.LDB, p.LDC, code, epi, True)
+    q = T.tcm_plan_batched(p.batch, p.M, p.N, p.K, p.LDA, p.LDB, p.LDC, code, epi, True)
     say(f"[case] plan query {name}: {q}")
     g = S.generate(p)
-    _, plan = run_tcm(p, g)
+    if p.batch > 1:
+        from test_gpu_batched import run_batched
+        _, plan = run_batched(p, g)
+    else:
+        _, plan = run_tcm(p, g)
     f = dict(kv.split("=", 1) for kv in plan.split() if "=" in kv)
     assert f["kernel"] == ("tile" if q["kernel"] == 1 else "generic")
     assert int(f["config"]) == q["config"]

@@ -186,6 +186,39 @@ def test_generic_path(dtype, layout):
         check_padding_untouched(p, C, -7 if dtype == S.I8 else float("nan"))
 
 
+BYTE_OFFSETS = [dict(A=2), dict(B=3), dict(C=1), dict(bias=1), dict(A=1, B=1, C=3, bias=2)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("offs", BYTE_OFFSETS, ids=lambda d: "-".join(f"{k}{v}" for k, v in d.items()))
+def test_generic_path_pointers_not_aligned_to_their_element(dtype, offs):
+    """Pointers at any byte address (e.g. an f32 A two bytes in, a C one
+    byte in) are served, not rejected: the generic kernel's byte-access
+    instance against the oracle, with bias + ReLU and ragged edges."""
+    from gpu_util import run_tcm_bytes
+    p = S.small_problem(dtype, 70, 66, 100, seed=8, bias=True, relu=True)
+    say(f"[case] byte offsets {offs} {p.name} dtype={dtype}")
+    g = S.generate(p)
+    C, plan = run_tcm_bytes(p, g, offs)
+    say(f"       plan: {plan}")
+    assert "kernel=generic" in plan
+    check(p, g, C)
+
+
+@pytest.mark.parametrize("variant", [(S.F16, "f16", True), (S.BF16, "bf16", True), (S.F32, "acc", True)],
+                         ids=["f16-Cf16", "bf16-Cbf16", "f32-Cf32"])
+def test_generic_path_unaligned_16bit_c_with_c_in(variant):
+    """A 16-bit C (read as C_in, then written) one byte past its element boundary."""
+    from gpu_util import run_tcm_bytes
+    dtype, c_type, accum = variant
+    p = S.small_problem(dtype, 40, 34, 48, seed=9, bias=True, c_type=c_type, accum=accum, ldc=37)
+    say(f"[case] unaligned C with C_in {p.name} c_type={c_type}")
+    g = S.generate(p)
+    C, plan = run_tcm_bytes(p, g, dict(C=1))
+    assert "kernel=generic" in plan
+    check(p, g, C)
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_forced_generic_matches_tiled(dtype):
     ce = {S.F16: 8, S.BF16: 8, S.F32: 4, S.I8: 16}[dtype]

@@ -94,3 +94,51 @@ def test_graph_capture_replays(mode, fixup):
         x = torch.randn(1024, device="cuda")  # unrelated eager work between the replays
         (x @ x).item()
     c.check()
+
+
+def test_graph_replay_after_the_workspace_grew():
+    """A graph captured on a stream keeps pointing at that stream's Stream-K
+    workspace.  A later, larger call on the stream grows the workspace: the
+    outgrown buffers are kept (not freed), so replays stay correct.  A call
+    that would grow a workspace while its stream is capturing is refused
+    with TCM_ERR_NOT_SUPPORTED instead of allocating inside the capture."""
+    T.tcm_set_option("force_mode", 2)
+    T.tcm_set_option("force_config", 4)
+    T.tcm_set_option("sk_fixup", 1)
+    small = Call(S.small_problem(S.F16, 128, 256, 1024, seed=403, bias=True, relu=True))
+    big = Call(S.small_problem(S.F16, 1024, 1024, 2048, seed=404, bias=True))
+    s = torch.cuda.Stream()
+    T.tcm_set_option("sk_grid", 16)
+    small(s)  # this stream's workspace: 16 workgroups' partial slots
+    torch.cuda.synchronize()
+    eager = small.C.clone()
+    small.check()
+    say(f"[case] capture before growth: {T.tcm_last_plan()}")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        small(s)
+    T.tcm_set_option("sk_grid", 0)
+    big(s)  # full co-resident grid: the workspace grows
+    torch.cuda.synchronize()
+    say(f"       growth: {T.tcm_last_plan()}")
+    big.check()
+    for i in range(3):
+        small.C.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(torch.nan_to_num(small.C, nan=1e9), torch.nan_to_num(eager, nan=1e9)), f"replay {i} differs"
+        big(s)  # eager calls on the same stream between the replays
+        torch.cuda.synchronize()
+    big.check()
+    # a fresh stream has no workspace yet: capturing a Stream-K call there is refused
+    s2 = torch.cuda.Stream()
+    p = small.p
+    g2 = torch.cuda.CUDAGraph()
+    status = []
+    with torch.cuda.graph(g2, stream=s2):
+        status.append(T.tcm_gemm(p.M, p.N, p.K, small.A.data_ptr(), p.LDA, small.B.data_ptr(), p.LDB,
+                                 small.C.data_ptr(), p.LDC, small.code, small.bias.data_ptr(), small.epi,
+                                 s2.cuda_stream))
+    say(f"       growth under capture: {T.tcm_status_string(status[0])}")
+    assert status == [T.TCM_ERR_NOT_SUPPORTED]
