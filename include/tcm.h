@@ -37,7 +37,7 @@
  * TCM_ERR_NOT_SUPPORTED.  A captured graph uses the workspace of the stream
  * it was captured on: its replays must not run at the same time as other
  * calls (eager or replayed) on that stream's workspace, e.g. replay it on the
- * same stream.
+ * same stream.  tcm_gemm_noalloc needs no workspace at all.
  *
  * Errors are returned, never raised; argument checks run before any HIP call.
  */
@@ -55,7 +55,8 @@ typedef enum {
     TCM_OK = 0,
     TCM_ERR_INVALID_VALUE = 1, /* a bad size, leading dimension, pointer, flag or option */
     TCM_ERR_NOT_SUPPORTED = 2, /* a valid request that cannot be served as asked: workspace
-                                  growth while the stream is being captured into a graph */
+                                  growth while the stream is being captured into a graph, or
+                                  a forced split-k plan beyond tcm_gemm_noalloc's scratch */
     TCM_ERR_HIP = 3,           /* a HIP runtime error (no device, launch failure, ...) */
     TCM_ERR_ALLOC = 4          /* the split-k workspace could not be allocated */
 } tcm_status;
@@ -131,6 +132,33 @@ int tcm_gemm(int64_t M, int64_t N, int64_t K,
              void* C, int64_t ldc,
              int dtype, const void* bias, int epilogue,
              void* stream);
+
+/*
+ * tcm_gemm_noalloc -- tcm_gemm for callers that cannot allocate device
+ * memory: code being captured into a HIP graph, tight serving loops, hosts
+ * that forbid hipMalloc.  Same arguments, results and errors as tcm_gemm; it
+ * never allocates (no hipMalloc, hipFree or allocating library call).  Its
+ * split-k (Stream-K) plans keep their partial tiles and arrival counters in
+ * one fixed array of tcm_noalloc_scratch_bytes() bytes per device (64 MiB of
+ * partial tiles plus 65536 counters), part of the library's device image and
+ * held until the process ends, instead of the per-stream workspace.
+ *   * A planned split-k launch that needs more than that array runs as
+ *     data-parallel tiles instead (no scratch); when split-k is forced
+ *     (tcm_set_option "force_mode" 2) such a call returns
+ *     TCM_ERR_NOT_SUPPORTED and launches nothing.
+ *   * Every call on a device shares that device's array, which keeps the last
+ *     call's contents: the counters a call uses are cleared by a fill kernel
+ *     on its stream first.  Calls that overlap in time on one device (other
+ *     streams, or graph replays) race on the array: order them.
+ */
+int tcm_gemm_noalloc(int64_t M, int64_t N, int64_t K,
+                     const void* A, int64_t lda,
+                     const void* B, int64_t ldb,
+                     void* C, int64_t ldc,
+                     int dtype, const void* bias, int epilogue,
+                     void* stream);
+/* Bytes of tcm_gemm_noalloc's fixed scratch array on each device. */
+int64_t tcm_noalloc_scratch_bytes(void);
 
 /*
  * tcm_gemm_batched -- `batch` independent products of one shape,

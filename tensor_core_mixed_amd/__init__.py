@@ -59,6 +59,10 @@ def lib():
         i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
         L.tcm_gemm.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, vp, ci, vp]
         L.tcm_gemm.restype = ci
+        L.tcm_gemm_noalloc.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, ci, vp, ci, vp]
+        L.tcm_gemm_noalloc.restype = ci
+        L.tcm_noalloc_scratch_bytes.argtypes = []
+        L.tcm_noalloc_scratch_bytes.restype = i64
         L.tcm_gemm_batched.argtypes = [i64, i64, i64, i64, vp, i64, i64, vp, i64, i64, vp, i64, i64, ci, vp, i64, ci, vp]
         L.tcm_gemm_batched.restype = ci
         L.tcm_gemm_grouped.argtypes = [i64, ctypes.POINTER(GroupEntry), i64, ci, ci, vp]
@@ -105,6 +109,16 @@ def tcm_gemm(M, N, K, A, lda, B, ldb, C, ldc, dtype, bias, epilogue, stream):
     """C = epi(bias + A.B); pointers are device addresses (ints), stream a
     hipStream_t handle (int) or None.  Returns the tcm status code."""
     return lib().tcm_gemm(M, N, K, A, lda, B, ldb, C, ldc, dtype, bias, epilogue, stream)
+
+
+def tcm_gemm_noalloc(M, N, K, A, lda, B, ldb, C, ldc, dtype, bias, epilogue, stream):
+    """tcm_gemm without any allocation (split-k scratch in a fixed device
+    array).  Returns the tcm status code."""
+    return lib().tcm_gemm_noalloc(M, N, K, A, lda, B, ldb, C, ldc, dtype, bias, epilogue, stream)
+
+
+def tcm_noalloc_scratch_bytes():
+    return lib().tcm_noalloc_scratch_bytes()
 
 
 def tcm_gemm_batched(batch, M, N, K, A, lda, stride_a, B, ldb, stride_b, C, ldc, stride_c, dtype, bias, stride_bias,

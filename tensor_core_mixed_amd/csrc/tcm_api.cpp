@@ -133,6 +133,38 @@ std::vector<std::pair<int, void*>> g_retired;  // (device, pointer)
 
 thread_local std::string t_last_plan;
 
+// Scratch of tcm_gemm_noalloc: the Stream-K partial tiles (two slots per
+// workgroup of the grid) and the split tiles' arrival counters, in one
+// fixed device array instead of the per-stream workspace.  Each device the
+// library runs on holds its own copy, at its own address, until the process
+// ends.  Host code never uses the array's name as an address (on the host it
+// is only a stand-in): the address of each device's copy comes from
+// hipGetSymbolAddress, called once per device with that device current.
+constexpr int64_t kScratchPartialBytes = (int64_t)64 << 20;
+constexpr int64_t kScratchCounters = (int64_t)1 << 16;
+constexpr int64_t kScratchBytes = kScratchPartialBytes + kScratchCounters * (int64_t)sizeof(int);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::map<int, char*> g_scratch;  // device -> address of its copy of `scratch`
+
+// Address of the current device `dev`'s scratch (looked up on its first use).
+int scratch_of(int dev, char** out) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_scratch.find(dev);
+    if (it == g_scratch.end()) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+            (void)hipGetLastError();
+            return TCM_ERR_HIP;
+        }
+        it = g_scratch.emplace(dev, (char*)p).first;
+    }
+    *out = it->second;
+    return TCM_OK;
+}
+bool scratch_fits(const Plan& pl) {
+    return pl.ws_partial_bytes <= kScratchPartialBytes && pl.ws_counters <= kScratchCounters;
+}
+
 int device_cus(int dev) {
     static std::map<int, int> cache;
     std::lock_guard<std::mutex> lk(g_mu);
@@ -485,11 +517,14 @@ int64_t batch_extent(int64_t batch, int64_t stride_bytes, int64_t ext) {
     return ext > 0 ? (batch - 1) * stride_bytes + ext : 0;
 }
 
-int launch_tiled(const Problem& p, const Plan& pl, TileArgs& a, int dev, void* stream);
+int launch_tiled(const Problem& p, const Plan& pl, TileArgs& a, int dev, void* stream, bool noalloc = false);
 
+// noalloc: the Stream-K partials and counters live in the fixed `scratch`
+// array; a plan that needs more is replaced by the data-parallel one, or
+// refused (TCM_ERR_NOT_SUPPORTED) when Stream-K is forced.
 int gemm_impl(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, int64_t sa, const void* B,
               int64_t ldb, int64_t sb, void* C, int64_t ldc, int64_t sc, int dtype, const void* bias, int64_t sbias,
-              int epilogue, void* stream) {
+              int epilogue, void* stream, bool noalloc = false) {
     Problem p;
     int st = check_problem(M, N, K, lda, ldb, ldc, dtype, epilogue, &p);
     if (st != TCM_OK) return st;
@@ -541,7 +576,15 @@ int gemm_impl(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int
     fill_sk_occupancy(p, &o);
     Plan pl;
     if (!make_plan(p, o, device_cus(dev), &pl)) return TCM_ERR_INVALID_VALUE;
-    t_last_plan = describe(pl, p);
+    if (noalloc && pl.kernel == 2 && pl.mode == 2 && !scratch_fits(pl)) {
+        if (current_options().force_mode == 2) {
+            t_last_plan = describe(pl, p) + " (split-k workspace beyond the fixed scratch)";
+            return TCM_ERR_NOT_SUPPORTED;
+        }
+        o.force_mode = 1;
+        if (!make_plan(p, o, device_cus(dev), &pl)) return TCM_ERR_INVALID_VALUE;
+    }
+    t_last_plan = describe(pl, p) + (noalloc ? " scratch=static" : "");
 
     if (pl.kernel == 1) {
         GenericArgs g{};
@@ -585,12 +628,12 @@ int gemm_impl(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int
     a.stride_b = sb;
     a.stride_c = sc;
     a.stride_bias = sbias;
-    return launch_tiled(p, pl, a, dev, stream);
+    return launch_tiled(p, pl, a, dev, stream, noalloc);
 }
 
 // Fills the plan-dependent fields of `a` (sizes, epilogue, tile schedule,
 // Stream-K workspace) and launches the tiled kernel the plan names.
-int launch_tiled(const Problem& p, const Plan& pl, TileArgs& a, int dev, void* stream) {
+int launch_tiled(const Problem& p, const Plan& pl, TileArgs& a, int dev, void* stream, bool noalloc) {
     a.M = (int)p.M;
     a.N = (int)p.N;
     a.K = (int)p.K;
@@ -609,7 +652,17 @@ int launch_tiled(const Problem& p, const Plan& pl, TileArgs& a, int dev, void* s
     a.ws_partial = nullptr;
     a.ws_counter = nullptr;
     a.sk_fixup_kernel = pl.fixup_kernel ? 1 : 0;
-    if (pl.mode == 2 && pl.sk_tiles > 0) {
+    if (pl.mode == 2 && pl.sk_tiles > 0 && noalloc) {
+        char* base = nullptr;
+        int st = scratch_of(dev, &base);
+        if (st != TCM_OK) return st;
+        a.ws_partial = (float*)base;
+        a.ws_counter = (int*)(base + kScratchPartialBytes);
+        // the arrival counters must start at zero; a previous call on this
+        // device leaves them so, but clear them anyway (a fill kernel, so the
+        // call stays capturable into a graph)
+        if (!pl.fixup_kernel && launch_fill_zero(a.ws_counter, pl.sk_tiles, stream) != 0) return TCM_ERR_HIP;
+    } else if (pl.mode == 2 && pl.sk_tiles > 0) {
         Workspace w;
         int ws = get_workspace(dev, stream, pl.ws_partial_bytes, pl.ws_counters, &w);
         if (ws != TCM_OK) return ws;
@@ -902,6 +955,13 @@ int tcm_gemm(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
              int dtype, const void* bias, int epilogue, void* stream) {
     return gemm_impl(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, dtype, bias, 0, epilogue, stream);
 }
+
+int tcm_gemm_noalloc(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                     int64_t ldc, int dtype, const void* bias, int epilogue, void* stream) {
+    return gemm_impl(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, dtype, bias, 0, epilogue, stream, true);
+}
+
+int64_t tcm_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 int tcm_gemm_grouped(int64_t count, const tcm_group_entry* entries, int64_t K, int dtype, int epilogue, void* stream) {
     return grouped_impl(count, entries, K, dtype, epilogue, stream);
