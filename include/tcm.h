@@ -288,13 +288,21 @@ const char* tcm_status_string(int status);
  *                  split-k (clamped to the number of co-resident workgroups).
  *   "generic"      1 = route every call to the generic (any-alignment) kernel.
  *   "sk_fixup"     how a split-k tile cut between workgroups is summed:
- *                  0 = planner decides (a second kernel when the tile has six
+ *                  0 = planner decides (a second kernel when the tile has five
  *                  or more segments), 1 = its last-arriving workgroup sums
  *                  the partials, 2 = a second kernel launched on the same
  *                  stream sums them.  Both add the partials in the same
  *                  order: the results are bit-identical.
+ *   "group_m"      0 = planner decides (4), else the rows of tiles per group
+ *                  of the tile order (1..16).
+ *   "grid_per_cu8" 0 = planner decides, else a split-k grid of value/8
+ *                  workgroups per CU (1..64).
+ *   "grid_shares"  0 = planner decides, else a split-k grid of value
+ *                  workgroups per tile (1..64): every split tile in equal
+ *                  shares that start at the same k.
  *   "tuned"        1 (default) = use the tuning table (tcm_tune) for problems
- *                  it holds; 0 = ignore it.  force_config / force_mode win.
+ *                  whose class it holds; 0 = ignore it.  force_config /
+ *                  force_mode / sk_grid win.
  * Unknown keys or out-of-range values: TCM_ERR_INVALID_VALUE.
  * tcm_get_option returns the value, or -2 for an unknown key.
  */
@@ -369,20 +377,47 @@ int tcm_tile_order(int32_t t, int32_t tiles_m, int32_t tiles_n, int32_t* tm, int
 
 /* ---- auto-tuning ----------------------------------------------------------- */
 /*
- * tcm_tune -- time every tile config in both modes (data-parallel, split-k)
- * on this problem and remember the fastest for its signature (sizes, leading
- * dimensions, dtype and flags, epilogue, 16-byte alignment of the pointers).
- * Later tcm_gemm and tcm_plan calls with the same signature use it (option
- * "tuned").  This is the schedule search of the pages (Fireiron's
- * auto-tuning, the GEMM schedule exploration on kimm240.github.io/tvm)
- * restricted to the tile table.
+ * The tuning table holds, per shape class, the plan parameters that measured
+ * fastest (the schedule search of the pages: Fireiron is built for
+ * auto-scheduling and auto-tuning, je-d.tistory.com/entry/tvm; the GEMM
+ * schedule exploration of kimm240.github.io/tvm, Steps 2-6).
+ *
+ * A shape class is: element type, A and B layout flags, output type,
+ * epilogue flags, whether every pointer is 16-byte aligned, whether the call
+ * is a batch, and the half octave of each of M, N and K (floor(2*log2(x)):
+ * e.g. every M in [4096, 5792] shares class 24).  An entry gives the tile
+ * config and mode, the split-k grid policy (the planner's; g/8 workgroups
+ * per CU; or s workgroups per tile, every tile split into s equal shares),
+ * the way split tiles are summed (the planner's, last arrival, fix-up
+ * kernel) and the tile-order group rows (the planner's, or 1..16).
+ * tcm_gemm and tcm_plan use the entry of the call's class, or, when the
+ * table holds none, the entry of the nearest class that differs only in
+ * the size classes, by at most one half octave in each (option "tuned");
+ * explicit force_config / force_mode / sk_grid switches win, and switches the
+ * caller set keep their values.  A tile config that cannot serve the call is
+ * ignored as with force_config.
+ *
+ * The library ships a table (tuned/mi355x.txt beside the directory of
+ * libtcm.so, or the file named by the environment variable TCM_TUNE_FILE;
+ * an empty TCM_TUNE_FILE ships none), loaded before the first plan; entries
+ * tuned or loaded before that keep precedence.
+ */
+
+/*
+ * tcm_tune -- search the tuning space on this problem and record the
+ * fastest point for its shape class.  Stage 1 times every tile config in
+ * both modes (data-parallel, split-k) with the planner's other parameters;
+ * stage 2 varies, around the three fastest, the tile-order group rows and,
+ * for split-k, the grid (0.5 to 2 workgroups per CU, 1 to 4 equal shares per
+ * tile) and the fix-up.  Each candidate is timed twice and keeps its better
+ * time.
  *
  * Same arguments as tcm_gemm plus `iters` (timed calls per candidate,
- * 1..10000) and `best` (optional: the chosen plan).  Runs on `stream`
+ * 1..10000) and `best` (optional: the plan now chosen).  Runs on `stream`
  * with the caller's buffers and BLOCKS until timing is done; C is written by
  * every candidate, so its contents afterwards are one correct result, except
- * with TCM_EPI_ACCUM, where C has been accumulated into repeatedly.
- * Returns as tcm_gemm.
+ * with TCM_EPI_ACCUM, where C has been accumulated into repeatedly.  A call
+ * the generic kernel serves records nothing.  Returns as tcm_gemm.
  */
 int tcm_tune(int64_t M, int64_t N, int64_t K,
              const void* A, int64_t lda, const void* B, int64_t ldb,
@@ -390,13 +425,18 @@ int tcm_tune(int64_t M, int64_t N, int64_t K,
              int iters, void* stream, tcm_plan_info* best);
 
 /*
- * tcm_tune_table -- the tuning table as text, one line per signature:
- *   "tcm-tune-1 batch M N K lda ldb ldc dtype a_col b_col c_type epilogue
- *    aligned config mode microseconds"
+ * tcm_tune_table -- the tuning table as text, one class per line:
+ *   "tcm-tune-2 dtype a_col b_col c_type epilogue aligned batched mclass
+ *    nclass kclass config mode grid_kind grid_param fixup group_m
+ *    microseconds M N K"
+ * (c_type 0 = the accumulator type, 1 = f16, 2 = bf16; grid_kind 0 = the
+ * planner's, 1 = grid_param/8 workgroups per CU, 2 = grid_param per tile;
+ * fixup and group_m 0 = the planner's; M N K = the shape it was tuned on).
  * Writes it NUL-terminated into buf (truncated to len) and returns its full
- * length.  tcm_tune_load parses such text and adds or replaces its entries
- * (all-or-nothing: TCM_ERR_INVALID_VALUE and no change on a malformed line).
- * tcm_tune_clear empties the table.  All three are host-only.
+ * length.  tcm_tune_load parses such text (blank lines and lines starting
+ * with '#' are skipped) and adds or replaces its entries (all-or-nothing:
+ * TCM_ERR_INVALID_VALUE and no change on a malformed line).  tcm_tune_clear
+ * empties the table (the shipped entries too).  All three are host-only.
  */
 int tcm_tune_table(char* buf, int64_t len);
 int tcm_tune_load(const char* text);

@@ -136,7 +136,8 @@ int64_t tile_count(const Problem& p, int ci) {
     return p.group ? p.group_tiles[ci] : cdiv(p.M, c.bm) * cdiv(p.N, c.bn) * std::max<int64_t>(p.batch, 1);
 }
 
-Estimate estimate(const Problem& p, int ci, int cus, int force_mode, int sk_grid, int sk_occ_known) {
+Estimate estimate(const Problem& p, int ci, int cus, int force_mode, int sk_grid, int sk_occ_known, int grid_per_cu8 = 0,
+                  int grid_shares = 0) {
     const TileConfig& c = kConfigs[ci];
     const int dt = p.dtype;
     const int bke = bk_elems(dt);
@@ -184,6 +185,9 @@ Estimate estimate(const Problem& p, int ci, int cus, int force_mode, int sk_grid
         // between its first and last owner
         const int sk_occ = sk_occ_known > 0 ? sk_occ_known : tile_sk_wg_per_cu(c);
         int64_t grid = sk_grid > 0 ? sk_grid : (int64_t)cus * sk_occ;
+        if (sk_grid <= 0 && grid_per_cu8 > 0) grid = std::max<int64_t>(1, (int64_t)cus * grid_per_cu8 / 8);
+        if (sk_grid <= 0 && grid_shares > 0) grid = T * grid_shares;
+        const bool chosen = sk_grid > 0 || grid_per_cu8 > 0 || grid_shares > 0;  // the grid is given: no alignment
         // Aligned split: when the tiles fit the co-resident grid S >= 2 times
         // over, a grid of exactly T * S workgroups (if it keeps 3/4 of the
         // slots busy) gives every tile S shares that start at the same k.
@@ -194,8 +198,8 @@ Estimate estimate(const Problem& p, int ci, int cus, int force_mode, int sk_grid
         // panel, so only single products are aligned (an aligned 128x128 plan
         // for eight 16-row products took 54.6 us against 48.7 us on 64x64
         // Stream-K units).
-        bool aligned = false;
-        if (sk_grid <= 0 && T < grid && !p.group && p.batch <= 1) {
+        bool aligned = sk_grid <= 0 && grid_shares > 0;  // equal shares of every tile start at the same k
+        if (!chosen && T < grid && !p.group && p.batch <= 1) {
             const int64_t S = grid / T;
             if (S >= 2 && 4 * T * S >= 3 * grid) {
                 grid = T * S;
@@ -276,7 +280,7 @@ bool make_plan(const Problem& p, const Options& o, int cus, Plan* out) {
             // (M <= 32; a group counts all its rows) unless it is forced
             if (o.force_config < 0 && kConfigs[c].bm < 64 && kConfigs[c].sk_stages > 2 && p.M > kConfigs[c].bm) continue;
             if (p.group ? !p.group_ok[c] : !tile_eligible(p, kConfigs[c])) continue;
-            Estimate e = estimate(p, c, cus, o.force_mode, o.sk_grid, o.sk_occ[c]);
+            Estimate e = estimate(p, c, cus, o.force_mode, o.sk_grid, o.sk_occ[c], o.grid_per_cu8, o.grid_shares);
             // configs run from large tiles to small: a smaller tile must be
             // clearly cheaper, since the model underrates its extra operand
             // traffic (2560 x 4096 x 4096: 64x64 tiles estimated 0.7% below
@@ -331,12 +335,14 @@ bool make_plan(const Problem& p, const Options& o, int cus, Plan* out) {
         // of waiting for the stores, counting their arrival and having the
         // last arrival read the others back (M = 1 / 16 / 64 with N = K =
         // 4096 on 64x64 units, eight segments a tile: 13.2 / 13.4 / 15.8 us
-        // in the kernel, 12.2 / 12.5 / 14.0 us with the second kernel; at
-        // three or four segments a tile the launch costs more than it saves).
+        // in the kernel, 12.2 / 12.5 / 14.0 us with the second kernel;
+        // 1280^2 x 5120 on 128x128 units in five aligned shares: 39.3 us by
+        // the last arrival, 35.2 us with the second kernel; at three or four
+        // segments a tile the launch costs more than it saves).
         const int64_t per_wg = (pl.sk_tiles * pl.iters + pl.grid - 1) / pl.grid;
-        pl.fixup_kernel = o.sk_fixup == 2 || (o.sk_fixup == 0 && pl.iters >= 6 * per_wg);
+        pl.fixup_kernel = o.sk_fixup == 2 || (o.sk_fixup == 0 && pl.iters >= 5 * per_wg);
     }
-    pl.group_m = 4;
+    pl.group_m = o.group_m > 0 ? o.group_m : 4;
     *out = pl;
     return true;
 }

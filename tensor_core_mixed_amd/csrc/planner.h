@@ -14,6 +14,12 @@ struct Options {
     int sk_grid = 0;        // 0 auto, else persistent grid size
     int generic = 0;        // 1: always the generic kernel
     int sk_fixup = 0;       // 0 planner decides, 1 last arrival sums a split tile, 2 a second kernel does
+    // Stream-K grid policy (tunable; sk_grid, an absolute size, wins):
+    // grid_per_cu8 > 0: grid_per_cu8 / 8 workgroups per CU; grid_shares > 0:
+    // exactly tiles x grid_shares workgroups (every split tile in equal shares)
+    int grid_per_cu8 = 0;
+    int grid_shares = 0;
+    int group_m = 0;        // tile-order group rows (0: the planner's 4)
     int sk_occ[kNumConfigs] = {0};  // Stream-K workgroups per CU by config (0: static estimate)
 };
 

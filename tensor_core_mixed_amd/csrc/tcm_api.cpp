@@ -2,11 +2,17 @@
 // per-(device, stream) Stream-K workspace, and dispatch to the kernels.
 #include <hip/hip_runtime.h>
 
+#include <dlfcn.h>
+
 #include <algorithm>
+#include <cmath>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
+#include <fstream>
 #include <map>
 #include <mutex>
+#include <sstream>
 #include <string>
 #include <utility>
 #include <vector>
@@ -94,29 +100,58 @@ std::mutex g_mu;
 Options g_opts;
 int g_use_tuned = 1;  // option "tuned"
 
-// Auto-tuned choices: the (tile config, mode) that measured fastest for one
-// problem signature.  Consulted by the planner for exactly that signature.
+// Auto-tuned choices by shape class.  Problems of one element type, operand
+// layout, output type, epilogue, alignment and batching whose M, N and K
+// each fall in the same half octave (floor(2 log2 x)) form a class; a class
+// entry holds the plan parameters that measured fastest on the shape it was
+// tuned on: tile config and mode, Stream-K grid policy, split-tile fix-up,
+// tile-order group rows.
 struct TuneKey {
-    int64_t batch, M, N, K, lda, ldb, ldc;
-    int dtype, a_col, b_col, c_type, epilogue, aligned;
+    int dtype, a_col, b_col, c_type, epilogue, aligned, batched;
+    int mc, nc, kc;
     bool operator<(const TuneKey& o) const {
-        const int64_t x[13] = {batch, M, N, K, lda, ldb, ldc, dtype, a_col, b_col, c_type, epilogue, aligned};
-        const int64_t y[13] = {o.batch, o.M, o.N, o.K, o.lda, o.ldb, o.ldc, o.dtype, o.a_col, o.b_col, o.c_type,
-                               o.epilogue, o.aligned};
-        return std::lexicographical_compare(x, x + 13, y, y + 13);
+        const int x[10] = {dtype, a_col, b_col, c_type, epilogue, aligned, batched, mc, nc, kc};
+        const int y[10] = {o.dtype, o.a_col, o.b_col, o.c_type, o.epilogue, o.aligned, o.batched, o.mc, o.nc, o.kc};
+        return std::lexicographical_compare(x, x + 10, y, y + 10);
     }
 };
+// One point of the tuning space.
+struct Cand {
+    int config = -1, mode = 0;
+    int grid_kind = 0, grid_param = 0;  // Stream-K grid: 0 the planner's, 1 grid_param/8 per CU, 2 grid_param per tile
+    int fixup = 0;                      // 0 the planner's, 1 last arrival, 2 fix-up kernel
+    int group_m = 0;                    // 0 the planner's (4)
+};
 struct TuneEntry {
-    int config, mode;
-    double us;  // measured time per call
+    Cand c;
+    double us;           // measured time per call
+    int64_t M, N, K;     // the shape it was tuned on
 };
 std::map<TuneKey, TuneEntry> g_tune;
+int half_octave(int64_t x) { return x <= 0 ? -1 : (int)std::floor(2.0 * std::log2((double)x) + 1e-9); }
 TuneKey tune_key(const Problem& p) {
-    return TuneKey{p.batch, p.M, p.N, p.K, p.lda, p.ldb, p.ldc, p.dtype, (int)p.a_col, (int)p.b_col, p.c_type,
-                   p.epilogue, (int)p.aligned};
+    return TuneKey{p.dtype, (int)p.a_col, (int)p.b_col, p.c_type, p.epilogue, (int)p.aligned, p.batch > 1 ? 1 : 0,
+                   half_octave(p.M), half_octave(p.N), half_octave(p.K)};
 }
-// Candidates forced by tcm_tune on this thread (-1 / 0: none).
-thread_local int t_tune_config = -1, t_tune_mode = 0;
+bool valid_cand(const Cand& c) {
+    return c.config >= 0 && c.config < kNumConfigs && (c.mode == 1 || c.mode == 2) && c.grid_kind >= 0 &&
+           c.grid_kind <= 2 && c.grid_param >= 0 && c.grid_param <= 64 && (c.grid_kind == 0 || c.grid_param > 0) &&
+           c.fixup >= 0 && c.fixup <= 2 && c.group_m >= 0 && c.group_m <= 16;
+}
+// Apply candidate c to options o.
+void apply_cand(const Cand& c, Options* o) {
+    o->force_config = c.config;
+    o->force_mode = c.mode;
+    o->sk_grid = 0;
+    o->grid_per_cu8 = c.grid_kind == 1 ? c.grid_param : 0;
+    o->grid_shares = c.grid_kind == 2 ? c.grid_param : 0;
+    if (c.fixup) o->sk_fixup = c.fixup;
+    if (c.group_m) o->group_m = c.group_m;
+}
+// The candidate tcm_tune is timing on this thread (null: none).
+thread_local const Cand* t_cand = nullptr;
+// The class entry the last plan_options call on this thread applied (for tcm_last_plan).
+thread_local std::string t_tuned_note;
 
 struct Workspace {
     void* partial = nullptr;
@@ -181,27 +216,90 @@ Options current_options() {
     return g_opts;
 }
 
-// Options for planning problem p: the global switches, then a tuned choice
-// for p's signature (unless a switch already forces config or mode), then a
-// candidate tcm_tune is timing on this thread.
+int parse_table(const char* text, std::vector<std::pair<TuneKey, TuneEntry>>* rows);
+void load_shipped_table();
+int current_cus();
+
+// Wave regime of T tiles on `slots` co-resident workgroups: the number of
+// full waves when the tiles fill the GPU at least once, else whether the
+// tiles fit it two or more times over (a split-k grid can give every tile
+// equal shares) or not.
+int64_t wave_regime(int64_t T, int64_t slots) {
+    if (T <= 0 || slots <= 0) return -1;
+    if (T >= slots) return 1000 + T / slots;
+    return slots / T >= 2 ? 2 : 1;
+}
+// A class entry applies to problem p only if p's tiles, on the entry's tile
+// config, fall in the same wave regime as the tuned shape's: within one
+// class the plan that wins turns on how the tiles quantise onto the CUs
+// (2048^2 x 8192 on 128x128 units: 256 tiles, exactly two shares per
+// workgroup slot, split-k wins; 2304^2 x 9216, the same class: 324 tiles,
+// split-k at 209 us against 140 us data-parallel).
+bool same_regime(const Problem& p, const TuneEntry& e, int cus) {
+    const TileConfig& c = kConfigs[e.c.config];
+    const int64_t occ = e.c.mode == 2 ? tile_sk_wg_per_cu(c) : tile_wg_per_cu(c);
+    const int64_t nb = std::max<int64_t>(p.batch, 1);
+    const int64_t tq = ((p.M + c.bm - 1) / c.bm) * ((p.N + c.bn - 1) / c.bn) * nb;
+    const int64_t tt = ((e.M + c.bm - 1) / c.bm) * ((e.N + c.bn - 1) / c.bn) * nb;
+    return wave_regime(tq, cus * occ) == wave_regime(tt, cus * occ);
+}
+
+// With no entry for a class, the entry of the nearest class of the same
+// type, layouts, output, epilogue, alignment and batching whose M, N and K
+// classes each lie within one half octave (smallest summed distance; the
+// first in key order on a tie), or g_tune.end().  Caller holds g_mu.
+std::map<TuneKey, TuneEntry>::iterator nearest_class(const TuneKey& k) {
+    auto best = g_tune.end();
+    int best_d = 1 << 30;
+    for (auto it = g_tune.begin(); it != g_tune.end(); ++it) {
+        const TuneKey& e = it->first;
+        if (e.dtype != k.dtype || e.a_col != k.a_col || e.b_col != k.b_col || e.c_type != k.c_type ||
+            e.epilogue != k.epilogue || e.aligned != k.aligned || e.batched != k.batched)
+            continue;
+        const int dm = std::abs(e.mc - k.mc), dn = std::abs(e.nc - k.nc), dk = std::abs(e.kc - k.kc);
+        if (dm > 1 || dn > 1 || dk > 1) continue;
+        if (dm + dn + dk < best_d) {
+            best_d = dm + dn + dk;
+            best = it;
+        }
+    }
+    return best;
+}
+
+// Options for planning problem p: the global switches, then the tuned class
+// entry for p (unless a switch already forces config or mode; switches the
+// caller set keep their values), then a candidate tcm_tune is timing on this
+// thread.
 Options plan_options(const Problem& p) {
+    static std::once_flag shipped;
+    std::call_once(shipped, load_shipped_table);
+    const int cus = current_cus();  // (takes the lock itself)
     Options o;
+    t_tuned_note.clear();
     {
         std::lock_guard<std::mutex> lk(g_mu);
         o = g_opts;
         // tuned entries describe single GEMM calls; a convolution or a group is planned afresh
-        if (g_use_tuned && !p.conv && !p.group && o.force_config < 0 && o.force_mode == 0) {
-            auto it = g_tune.find(tune_key(p));
+        if (g_use_tuned && !p.conv && !p.group && o.force_config < 0 && o.force_mode == 0 && o.sk_grid == 0) {
+            const TuneKey k = tune_key(p);
+            auto it = g_tune.find(k);
+            if (it == g_tune.end()) it = nearest_class(k);
+            if (it != g_tune.end() && !same_regime(p, it->second, cus)) it = g_tune.end();
             if (it != g_tune.end()) {
-                o.force_config = it->second.config;
-                o.force_mode = it->second.mode;
+                const Cand& c = it->second.c;
+                o.force_config = c.config;
+                o.force_mode = c.mode;
+                o.grid_per_cu8 = c.grid_kind == 1 ? c.grid_param : 0;
+                o.grid_shares = c.grid_kind == 2 ? c.grid_param : 0;
+                if (c.fixup && o.sk_fixup == 0) o.sk_fixup = c.fixup;
+                if (c.group_m && o.group_m == 0) o.group_m = c.group_m;
+                char buf[96];
+                snprintf(buf, sizeof buf, " tuned=%d,%d,%d", it->first.mc, it->first.nc, it->first.kc);
+                t_tuned_note = buf;
             }
         }
     }
-    if (t_tune_config >= 0) {
-        o.force_config = t_tune_config;
-        o.force_mode = t_tune_mode;
-    }
+    if (t_cand) apply_cand(*t_cand, &o);
     return o;
 }
 
@@ -386,6 +484,15 @@ int tcm_set_option(const char* key, int64_t value) {
     } else if (!strcmp(key, "sk_fixup")) {
         if (value < 0 || value > 2) return TCM_ERR_INVALID_VALUE;
         g_opts.sk_fixup = (int)value;
+    } else if (!strcmp(key, "group_m")) {
+        if (value < 0 || value > 16) return TCM_ERR_INVALID_VALUE;
+        g_opts.group_m = (int)value;
+    } else if (!strcmp(key, "grid_per_cu8")) {
+        if (value < 0 || value > 64) return TCM_ERR_INVALID_VALUE;
+        g_opts.grid_per_cu8 = (int)value;
+    } else if (!strcmp(key, "grid_shares")) {
+        if (value < 0 || value > 64) return TCM_ERR_INVALID_VALUE;
+        g_opts.grid_shares = (int)value;
     } else if (!strcmp(key, "tuned")) {
         if (value < 0 || value > 1) return TCM_ERR_INVALID_VALUE;
         g_use_tuned = (int)value;
@@ -403,6 +510,9 @@ int64_t tcm_get_option(const char* key) {
     if (!strcmp(key, "sk_grid")) return g_opts.sk_grid;
     if (!strcmp(key, "generic")) return g_opts.generic;
     if (!strcmp(key, "sk_fixup")) return g_opts.sk_fixup;
+    if (!strcmp(key, "group_m")) return g_opts.group_m;
+    if (!strcmp(key, "grid_per_cu8")) return g_opts.grid_per_cu8;
+    if (!strcmp(key, "grid_shares")) return g_opts.grid_shares;
     if (!strcmp(key, "tuned")) return g_use_tuned;
     return -2;
 }
@@ -584,7 +694,7 @@ int gemm_impl(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int
         o.force_mode = 1;
         if (!make_plan(p, o, device_cus(dev), &pl)) return TCM_ERR_INVALID_VALUE;
     }
-    t_last_plan = describe(pl, p) + (noalloc ? " scratch=static" : "");
+    t_last_plan = describe(pl, p) + t_tuned_note + (noalloc ? " scratch=static" : "");
 
     if (pl.kernel == 1) {
         GenericArgs g{};
@@ -946,6 +1056,77 @@ int grouped_impl(int64_t count, const tcm_group_entry* ent, int64_t K, int dtype
     return launch(g, stream) == 0 ? TCM_OK : TCM_ERR_HIP;
 }
 
+// Tuning table text, one class per line (blank lines and lines starting
+// with '#' are skipped): "tcm-tune-2" then dtype a_col b_col c_type epilogue
+// aligned batched, the half-octave classes of M N K, then config mode
+// grid_kind grid_param fixup group_m, the measured microseconds and the
+// tuned shape M N K.  All or nothing: any malformed line rejects the text.
+int parse_table(const char* text, std::vector<std::pair<TuneKey, TuneEntry>>* rows) {
+    const char* q = text;
+    while (*q) {
+        const char* eol = strchr(q, '\n');
+        std::string line(q, eol ? (size_t)(eol - q) : strlen(q));
+        q = eol ? eol + 1 : q + strlen(q);
+        const size_t first = line.find_first_not_of(" \t\r");
+        if (first == std::string::npos || line[first] == '#') continue;
+        int d[16];
+        long long m = 0, n = 0, k = 0;
+        double us = 0;
+        char tag[16];
+        int used = 0;
+        const int got = sscanf(line.c_str(), "%15s %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %lf %lld %lld %lld %n", tag,
+                               &d[0], &d[1], &d[2], &d[3], &d[4], &d[5], &d[6], &d[7], &d[8], &d[9], &d[10], &d[11], &d[12],
+                               &d[13], &d[14], &d[15], &us, &m, &n, &k, &used);
+        if (got != 21 || strcmp(tag, "tcm-tune-2") || line.find_first_not_of(" \t\r", (size_t)used) != std::string::npos)
+            return TCM_ERR_INVALID_VALUE;
+        const TuneKey key{d[0], d[1], d[2], d[3], d[4], d[5], d[6], d[7], d[8], d[9]};
+        Cand c;
+        c.config = d[10];
+        c.mode = d[11];
+        c.grid_kind = d[12];
+        c.grid_param = d[13];
+        c.fixup = d[14];
+        c.group_m = d[15];
+        const bool flags_ok = (key.a_col | key.b_col | key.aligned | key.batched) >= 0 && key.a_col <= 1 && key.b_col <= 1 &&
+                              key.aligned <= 1 && key.batched <= 1 && key.c_type >= 0 && key.c_type <= 2 &&
+                              key.epilogue >= 0 && key.epilogue <= 7;
+        if (key.dtype < F16 || key.dtype > I8 || !flags_ok || key.mc < 0 || key.nc < 0 || key.kc < 0 || !valid_cand(c) ||
+            !(us >= 0) || m < 1 || n < 1 || k < 1)
+            return TCM_ERR_INVALID_VALUE;
+        rows->emplace_back(key, TuneEntry{c, us, m, n, k});
+    }
+    return TCM_OK;
+}
+
+// The tuning table shipped with the library: tuned/mi355x.txt next to the
+// directory that holds libtcm.so (or the file TCM_TUNE_FILE names; an empty
+// TCM_TUNE_FILE ships nothing).  Loaded once, before the first plan; a
+// missing file leaves the table empty, a malformed one is ignored whole.
+void load_shipped_table() {
+    std::string path;
+    const char* env = getenv("TCM_TUNE_FILE");
+    if (env) {
+        path = env;
+    } else {
+        Dl_info info;
+        if (dladdr((void*)&load_shipped_table, &info) && info.dli_fname) {
+            std::string so = info.dli_fname;
+            const size_t slash = so.rfind('/');
+            const std::string dir = slash == std::string::npos ? "." : so.substr(0, slash);
+            path = dir + "/../tuned/mi355x.txt";
+        }
+    }
+    if (path.empty()) return;
+    std::ifstream f(path);
+    if (!f) return;
+    std::stringstream ss;
+    ss << f.rdbuf();
+    std::vector<std::pair<TuneKey, TuneEntry>> rows;
+    if (parse_table(ss.str().c_str(), &rows) != TCM_OK) return;
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (const auto& r : rows) g_tune.emplace(r.first, r.second);  // entries loaded or tuned first stay
+}
+
 }  // namespace
 }  // namespace tcm
 
@@ -994,6 +1175,7 @@ int tcm_tune(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
     const int cs = c_elem_bytes(p.c_type);
     p.aligned = ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) && ((uintptr_t)C % 16 == 0) &&
                 (!use_bias || (uintptr_t)bias % 16 == 0) && ((uintptr_t)C % cs == 0);
+    if (!strstr(t_last_plan.c_str(), "kernel=tile")) return TCM_OK;  // the generic kernel: nothing to choose
     hipStream_t s = (hipStream_t)stream;
     hipEvent_t e0, e1;
     if (hipEventCreate(&e0) != hipSuccess) return TCM_ERR_HIP;
@@ -1002,6 +1184,33 @@ int tcm_tune(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
         return TCM_ERR_HIP;
     }
     auto run = [&]() { return gemm_impl(1, M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, dtype, bias, 0, epilogue, stream); };
+    auto field = [](const std::string& plan, const char* key) {
+        const char* q = strstr(plan.c_str(), key);
+        return q ? atoll(q + strlen(key)) : -1LL;
+    };
+    // Time candidate c (`iters` calls); false if it cannot run as asked (an
+    // ineligible config falls back to another plan).
+    auto time_cand = [&](const Cand& c, double* us, int64_t* tiles) -> bool {
+        t_cand = &c;
+        st = run();  // warm-up, and the plan this candidate really gets
+        const std::string plan = t_last_plan;
+        const int pm = strstr(plan.c_str(), "mode=streamk") ? 2 : 1;
+        if (st != TCM_OK || field(plan, " config=") != c.config || pm != c.mode) {
+            t_cand = nullptr;
+            return false;
+        }
+        if (tiles) *tiles = field(plan, " tiles=");
+        if (hipEventRecord(e0, s) != hipSuccess) st = TCM_ERR_HIP;
+        for (int i = 0; i < iters && st == TCM_OK; ++i) st = run();
+        float ms = 0;
+        if (st == TCM_OK && (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                             hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
+            st = TCM_ERR_HIP;
+        t_cand = nullptr;
+        if (st != TCM_OK) return false;
+        *us = (double)ms * 1e3 / iters;
+        return true;
+    };
     // The shader clock needs tens of milliseconds of load to settle: keep the
     // model's plan running for at least 50 ms (measured on the stream) first.
     {
@@ -1017,51 +1226,90 @@ int tcm_tune(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
             if (ms <= 0 && st == TCM_OK) break;
         }
     }
-    // Two sweeps over the candidates; each keeps its better time.
-    double best_us = 1e300;
-    int best_cfg = -1, best_mode = 1;
-    std::vector<std::pair<int, int>> cands;
+    // Stage 1: every tile config in both modes with the planner's other
+    // parameters, two sweeps, each candidate keeping its better time.
+    struct Timed {
+        Cand c;
+        double us;
+        int64_t tiles;
+    };
+    std::vector<Timed> stage1;
     for (int c = 0; c < kNumConfigs; ++c)
-        for (int mode = 1; mode <= 2; ++mode) cands.emplace_back(c, mode);
-    std::vector<double> t_us(cands.size(), 1e300);
-    std::vector<char> valid(cands.size(), 1);
-    for (int sweep = 0; sweep < 2 && st == TCM_OK; ++sweep) {
-        for (size_t ci = 0; ci < cands.size() && st == TCM_OK; ++ci) {
-            if (!valid[ci]) continue;
-            t_tune_config = cands[ci].first;
-            t_tune_mode = cands[ci].second;
-            st = run();  // warm-up, and the plan this candidate really gets
-            // (an ineligible config falls back to the model's plan: skip it)
-            const char* cp = strstr(t_last_plan.c_str(), "config=");
-            const int pc = cp ? atoi(cp + 7) : -1;
-            const int pm = strstr(t_last_plan.c_str(), "mode=streamk") ? 2 : 1;
-            if (st != TCM_OK || pc != cands[ci].first || pm != cands[ci].second) {
-                valid[ci] = 0;
+        for (int mode = 1; mode <= 2; ++mode) {
+            Cand x;
+            x.config = c;
+            x.mode = mode;
+            stage1.push_back({x, 1e300, 0});
+        }
+    std::vector<char> valid(stage1.size(), 1);
+    for (int sweep = 0; sweep < 2 && st == TCM_OK; ++sweep)
+        for (size_t i = 0; i < stage1.size() && st == TCM_OK; ++i) {
+            if (!valid[i]) continue;
+            double us = 0;
+            if (!time_cand(stage1[i].c, &us, &stage1[i].tiles)) {
+                valid[i] = 0;
                 continue;
             }
-            if (hipEventRecord(e0, s) != hipSuccess) st = TCM_ERR_HIP;
-            for (int i = 0; i < iters && st == TCM_OK; ++i) st = run();
-            float ms = 0;
-            if (st == TCM_OK && (hipEventRecord(e1, s) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
-                                 hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
-                st = TCM_ERR_HIP;
-            if (st == TCM_OK) t_us[ci] = std::min(t_us[ci], (double)ms * 1e3 / iters);
+            stage1[i].us = std::min(stage1[i].us, us);
+        }
+    std::vector<Timed> ranked;
+    for (size_t i = 0; i < stage1.size(); ++i)
+        if (valid[i]) ranked.push_back(stage1[i]);
+    std::sort(ranked.begin(), ranked.end(), [](const Timed& x, const Timed& y) { return x.us < y.us; });
+    // Stage 2: around the three fastest, the parameters the table leaves to
+    // the planner: tile-order group rows; for Stream-K also the grid (per-CU
+    // sizes, equal shares of every tile) and the way split tiles are summed.
+    std::vector<Timed> stage2;
+    const int cus = current_cus();
+    for (size_t r = 0; r < ranked.size() && r < 3; ++r) {
+        const Cand b = ranked[r].c;
+        const int64_t T = ranked[r].tiles;
+        for (int gm : {1, 2, 8}) {
+            Cand x = b;
+            x.group_m = gm;
+            stage2.push_back({x, 1e300, 0});
+        }
+        if (b.mode == 2) {
+            for (int g8 : {4, 8, 12, 16}) {
+                Cand x = b;
+                x.grid_kind = 1;
+                x.grid_param = g8;
+                stage2.push_back({x, 1e300, 0});
+            }
+            for (int sh = 1; sh <= 4; ++sh)
+                if (T > 0 && T * sh <= 4LL * cus) {
+                    Cand x = b;
+                    x.grid_kind = 2;
+                    x.grid_param = sh;
+                    stage2.push_back({x, 1e300, 0});
+                }
+            for (int fx : {1, 2}) {
+                Cand x = b;
+                x.fixup = fx;
+                stage2.push_back({x, 1e300, 0});
+            }
         }
     }
-    for (size_t ci = 0; ci < cands.size(); ++ci)
-        if (valid[ci] && t_us[ci] < best_us) {
-            best_us = t_us[ci];
-            best_cfg = cands[ci].first;
-            best_mode = cands[ci].second;
+    std::vector<char> valid2(stage2.size(), 1);
+    for (int sweep = 0; sweep < 2 && st == TCM_OK; ++sweep)
+        for (size_t i = 0; i < stage2.size() && st == TCM_OK; ++i) {
+            if (!valid2[i]) continue;
+            double us = 0;
+            if (!time_cand(stage2[i].c, &us, nullptr)) {
+                valid2[i] = 0;
+                continue;
+            }
+            stage2[i].us = std::min(stage2[i].us, us);
         }
-    t_tune_config = -1;
-    t_tune_mode = 0;
     (void)hipEventDestroy(e0);
     (void)hipEventDestroy(e1);
     if (st != TCM_OK) return st;
-    if (best_cfg >= 0) {
+    const Timed* win = ranked.empty() ? nullptr : &ranked[0];
+    for (size_t i = 0; i < stage2.size(); ++i)
+        if (valid2[i] && win && stage2[i].us < win->us) win = &stage2[i];
+    if (win) {
         std::lock_guard<std::mutex> lk(g_mu);
-        g_tune[tune_key(p)] = TuneEntry{best_cfg, best_mode, best_us};
+        g_tune[tune_key(p)] = TuneEntry{win->c, win->us, M, N, K};
     }
     if (best) return tcm_plan(M, N, K, lda, ldb, ldc, dtype, epilogue, p.aligned ? 1 : 0, best);
     return TCM_OK;
@@ -1074,10 +1322,11 @@ int tcm_tune_table(char* buf, int64_t len) {
         char line[320];
         for (const auto& kv : g_tune) {
             const TuneKey& k = kv.first;
-            snprintf(line, sizeof line, "tcm-tune-1 %lld %lld %lld %lld %lld %lld %lld %d %d %d %d %d %d %d %d %.3f\n",
-                     (long long)k.batch, (long long)k.M, (long long)k.N, (long long)k.K, (long long)k.lda,
-                     (long long)k.ldb, (long long)k.ldc, k.dtype, k.a_col, k.b_col, k.c_type, k.epilogue, k.aligned,
-                     kv.second.config, kv.second.mode, kv.second.us);
+            const TuneEntry& e = kv.second;
+            snprintf(line, sizeof line, "tcm-tune-2 %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %d %.3f %lld %lld %lld\n",
+                     k.dtype, k.a_col, k.b_col, k.c_type, k.epilogue, k.aligned, k.batched, k.mc, k.nc, k.kc, e.c.config,
+                     e.c.mode, e.c.grid_kind, e.c.grid_param, e.c.fixup, e.c.group_m, e.us, (long long)e.M, (long long)e.N,
+                     (long long)e.K);
             out += line;
         }
     }
@@ -1092,29 +1341,7 @@ int tcm_tune_table(char* buf, int64_t len) {
 int tcm_tune_load(const char* text) {
     if (!text) return TCM_ERR_INVALID_VALUE;
     std::vector<std::pair<TuneKey, TuneEntry>> rows;
-    const char* q = text;
-    while (*q) {
-        const char* eol = strchr(q, '\n');
-        std::string line(q, eol ? (size_t)(eol - q) : strlen(q));
-        q = eol ? eol + 1 : q + strlen(q);
-        if (line.find_first_not_of(" \t\r") == std::string::npos) continue;
-        long long v[7];
-        int d[8];
-        double us = 0;
-        char tag[16];
-        int used = 0;
-        const int n = sscanf(line.c_str(), "%15s %lld %lld %lld %lld %lld %lld %lld %d %d %d %d %d %d %d %d %lf %n", tag,
-                             &v[0], &v[1], &v[2], &v[3], &v[4], &v[5], &v[6], &d[0], &d[1], &d[2], &d[3], &d[4], &d[5],
-                             &d[6], &d[7], &us, &used);
-        if (n != 17 || strcmp(tag, "tcm-tune-1") || line.find_first_not_of(" \t\r", (size_t)used) != std::string::npos)
-            return TCM_ERR_INVALID_VALUE;
-        const TuneKey k{v[0], v[1], v[2], v[3], v[4], v[5], v[6], d[0], d[1], d[2], d[3], d[4], d[5]};
-        const int cfg = d[6], mode = d[7];
-        if (k.batch < 1 || k.M < 0 || k.N < 0 || k.K < 0 || k.dtype < F16 || k.dtype > I8 || cfg < 0 ||
-            cfg >= kNumConfigs || mode < 1 || mode > 2 || !(us >= 0))
-            return TCM_ERR_INVALID_VALUE;
-        rows.emplace_back(k, TuneEntry{cfg, mode, us});
-    }
+    if (parse_table(text, &rows) != TCM_OK) return TCM_ERR_INVALID_VALUE;
     std::lock_guard<std::mutex> lk(g_mu);
     for (const auto& r : rows) g_tune[r.first] = r.second;
     return TCM_OK;

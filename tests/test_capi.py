@@ -19,6 +19,20 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(tcm_[a-z_]+)\s*\(", text)))
 
 
+@pytest.fixture(autouse=True)
+def _planner_model_without_the_table():
+    """The planner tests here check the cost model itself: the tuning table
+    (the shipped one included) is off unless a test turns it on; a test that
+    edits the table gets the process's table back afterwards."""
+    T.tcm_plan(64, 64, 64, 64, 64, 64, 0)  # the first plan loads the shipped table
+    before = T.tcm_tune_table()
+    T.tcm_set_option("tuned", 0)
+    yield
+    T.tcm_set_option("tuned", 1)
+    T.tcm_tune_clear()
+    assert T.tcm_tune_load(before) == T.TCM_OK
+
+
 def test_every_declared_symbol_is_exported():
     names = declared_functions()
     assert "tcm_gemm" in names and len(names) >= 10
@@ -140,11 +154,11 @@ def test_planner_skinny_uses_streamk(M):
 @pytest.mark.parametrize("M,N,K,fixup", [(1, 4096, 4096, 1), (16, 4096, 4096, 1), (64, 4096, 4096, None),
                                          (256, 4096, 4096, None), (1536, 1536, 16384, 0)])
 def test_planner_fixup_kernel_for_many_segments(M, N, K, fixup):
-    """Split tiles with six or more segments are summed by a second kernel;
+    """Split tiles with five or more segments are summed by a second kernel;
     with fewer, by their last arrival.  The option overrides either way."""
     p = T.tcm_plan(M, N, K, K, N, N, T.TCM_F16_F32)
     per_wg = -(-p["sk_tiles"] * p["iters_per_tile"] // p["grid"])
-    assert p["mode"] == 2 and p["fixup_kernel"] == int(p["iters_per_tile"] >= 6 * per_wg)
+    assert p["mode"] == 2 and p["fixup_kernel"] == int(p["iters_per_tile"] >= 5 * per_wg)
     if fixup is not None:
         assert p["fixup_kernel"] == fixup
     try:
@@ -355,24 +369,62 @@ def test_batched_empty_and_valid_without_device():
     assert st == T.TCM_ERR_HIP
 
 
-HEADLINE_SIG = (1, 8192, 8192, 8192, 8192, 8192, 8192, 0, 0, 1, 0, 0, 1)  # batch M N K lda ldb ldc dtype a_col b_col c_type epi aligned
+# class key of the headline: dtype a_col b_col c_type epilogue aligned batched mclass nclass kclass
+HEADLINE_KEY = (0, 0, 1, 0, 0, 1, 0, 26, 26, 26)
 
 
-def _line(sig, config, mode, us=12.5):
-    return "tcm-tune-1 " + " ".join(str(v) for v in sig) + f" {config} {mode} {us:.3f}"
+def _line(key, config, mode, grid_kind=0, grid_param=0, fixup=0, group_m=0, us=12.5, shape=(8192, 8192, 8192)):
+    return ("tcm-tune-2 " + " ".join(str(v) for v in key) +
+            f" {config} {mode} {grid_kind} {grid_param} {fixup} {group_m} {us:.3f} " + " ".join(map(str, shape)))
+
+
+def test_half_octave_classes():
+    """The class of a size is floor(2 log2 x): one class spans [2^(c/2), 2^((c+1)/2))."""
+    T.tcm_tune_clear()
+    T.tcm_set_option("tuned", 1)
+    try:
+        # an entry for the class of 4096 (24) in M, N, K, int8: config 1 Stream-K
+        key = (3, 0, 0, 0, 3, 1, 0, 24, 24, 24)
+        assert T.tcm_tune_load(_line(key, 1, 2, shape=(4096, 4096, 4096))) == T.TCM_OK
+        for n in (4096, 5000, 5792):  # inside the class
+            q = T.tcm_plan(n, 4096, 4096, 4096, 4096, 4096, T.TCM_I8_I32, T.TCM_EPI_BIAS_RELU)
+            assert (q["config"], q["mode"]) == (1, 2), n
+        for n in (2048, 2895, 8192, 12000):  # two or more half octaves away (22, 22, 26, 27)
+            q = T.tcm_plan(n, 4096, 4096, 4096, 4096, 4096, T.TCM_I8_I32, T.TCM_EPI_BIAS_RELU)
+            assert (q["config"], q["mode"]) != (1, 2), n
+        # another epilogue is another class
+        q = T.tcm_plan(4096, 4096, 4096, 4096, 4096, 4096, T.TCM_I8_I32, 0)
+        assert (q["config"], q["mode"]) != (1, 2)
+        # a class without an entry takes the nearest one within a half octave in every size
+        # (K here, so that the tile count stays that of the tuned shape)
+        for m, n, k, near in ((4096, 4096, 3008, True), (4096, 4096, 8000, True), (4096, 4096, 12000, False),
+                              (4096, 4096, 16384, False)):
+            q = T.tcm_plan(m, n, k, k, n, n, T.TCM_I8_I32, T.TCM_EPI_BIAS_RELU)
+            assert ((q["config"], q["mode"]) == (1, 2)) == near, (m, n, k)
+        # an entry applies only in the wave regime it was tuned in: 4096^2 on 128x128
+        # units is 1024 tiles, two full waves of the 512 split-k slots; 3008 x 4096
+        # (the nearest class) is 768 tiles, one and a half waves
+        q = T.tcm_plan(3008, 4096, 4096, 4096, 4096, 4096, T.TCM_I8_I32, T.TCM_EPI_BIAS_RELU)
+        assert (q["config"], q["mode"]) != (1, 2)
+    finally:
+        T.tcm_tune_clear()
 
 
 def test_tune_table_round_trip_and_use_by_the_planner():
     T.tcm_tune_clear()
+    T.tcm_set_option("tuned", 1)
     model = T.tcm_plan(8192, 8192, 8192, 8192, 8192, 8192, T.TCM_F16_F32 | T.TCM_B_COLMAJOR)
     assert model["config"] == 0
-    text = _line(HEADLINE_SIG, 1, 2) + "\n" + _line((1, 64, 64, 64, 64, 64, 64, 3, 0, 0, 0, 3, 1), 4, 1) + "\n"
-    assert T.tcm_tune_load(text) == T.TCM_OK
+    text = (_line(HEADLINE_KEY, 1, 2, grid_kind=2, grid_param=3, fixup=2, group_m=8) + "\n" +
+            _line((3, 0, 0, 0, 3, 1, 0, 12, 12, 12), 4, 1, shape=(64, 64, 64)) + "\n")
+    assert T.tcm_tune_load("# a comment\n\n" + text) == T.TCM_OK
     out = T.tcm_tune_table()
     assert sorted(out.strip().splitlines()) == sorted(text.strip().splitlines())
     tuned = T.tcm_plan(8192, 8192, 8192, 8192, 8192, 8192, T.TCM_F16_F32 | T.TCM_B_COLMAJOR)
+    # config 1 split-k on exactly 3 workgroups per tile, split tiles summed by the fix-up kernel
     assert (tuned["config"], tuned["mode"]) == (1, 2)
-    # another signature (unaligned) is untouched
+    assert tuned["grid"] == 3 * tuned["tiles"] and tuned["fixup_kernel"] == 1
+    # another class (unaligned) is untouched
     assert T.tcm_plan(8192, 8192, 8192, 8192, 8192, 8192, T.TCM_F16_F32 | T.TCM_B_COLMAJOR, aligned=False)["kernel"] == 0
     T.tcm_set_option("tuned", 0)
     try:
@@ -385,22 +437,37 @@ def test_tune_table_round_trip_and_use_by_the_planner():
         assert T.tcm_plan(8192, 8192, 8192, 8192, 8192, 8192, T.TCM_F16_F32 | T.TCM_B_COLMAJOR)["config"] == 2
     finally:
         T.tcm_set_option("force_config", -1)
+    # a switch the caller set keeps its value (here: the fix-up)
+    T.tcm_set_option("sk_fixup", 1)
+    try:
+        assert T.tcm_plan(8192, 8192, 8192, 8192, 8192, 8192, T.TCM_F16_F32 | T.TCM_B_COLMAJOR)["fixup_kernel"] == 0
+    finally:
+        T.tcm_set_option("sk_fixup", 0)
     T.tcm_tune_clear()
     assert T.tcm_tune_table() == ""
     assert T.tcm_plan(8192, 8192, 8192, 8192, 8192, 8192, T.TCM_F16_F32 | T.TCM_B_COLMAJOR)["config"] == 0
 
 
+GOOD_TAIL = " 1 1 0 0 0 0 1.0 8 8 8"
+
+
 @pytest.mark.parametrize("bad", [
-    "tcm-tune-2 1 8 8 8 8 8 8 0 0 0 0 0 1 0 1 1.0",          # unknown version tag
-    "tcm-tune-1 1 8 8 8 8 8 8 0 0 0 0 0 1 9 1 1.0",          # no such config
-    "tcm-tune-1 1 8 8 8 8 8 8 0 0 0 0 0 1 0 3 1.0",          # no such mode
-    "tcm-tune-1 1 8 8 8 8 8 8 0 0 0 0 0 1 0 1",              # missing field
-    "tcm-tune-1 1 8 8 8 8 8 8 0 0 0 0 0 1 0 1 1.0 extra",    # trailing text
-    "tcm-tune-1 0 8 8 8 8 8 8 0 0 0 0 0 1 0 1 1.0",          # batch 0
+    "tcm-tune-1 0 0 1 0 0 1 0 26 26 26" + GOOD_TAIL,           # unknown version tag
+    "tcm-tune-2 0 0 1 0 0 1 0 26 26 26 99 1 0 0 0 0 1.0 8 8 8",  # no such config
+    "tcm-tune-2 0 0 1 0 0 1 0 26 26 26 1 3 0 0 0 0 1.0 8 8 8",   # no such mode
+    "tcm-tune-2 0 0 1 0 0 1 0 26 26 26 1 2 3 1 0 0 1.0 8 8 8",   # no such grid kind
+    "tcm-tune-2 0 0 1 0 0 1 0 26 26 26 1 2 1 0 0 0 1.0 8 8 8",   # a grid kind without its parameter
+    "tcm-tune-2 0 0 1 0 0 1 0 26 26 26 1 2 0 0 3 0 1.0 8 8 8",   # no such fix-up
+    "tcm-tune-2 0 0 1 0 0 1 0 26 26 26 1 2 0 0 0 17 1.0 8 8 8",  # group rows beyond 16
+    "tcm-tune-2 7 0 1 0 0 1 0 26 26 26" + GOOD_TAIL,           # no such element type
+    "tcm-tune-2 0 2 1 0 0 1 0 26 26 26" + GOOD_TAIL,           # a flag that is not 0 / 1
+    "tcm-tune-2 0 0 1 0 0 1 0 26 26 26 1 1 0 0 0 0 1.0 8 8",   # missing field
+    "tcm-tune-2 0 0 1 0 0 1 0 26 26 26" + GOOD_TAIL + " extra",  # trailing text
+    "tcm-tune-2 0 0 1 0 0 1 0 26 26 26 1 1 0 0 0 0 1.0 0 8 8",   # an empty tuned shape
 ])
 def test_tune_load_rejects_malformed_text_all_or_nothing(bad):
     T.tcm_tune_clear()
-    good = _line(HEADLINE_SIG, 1, 1)
+    good = _line(HEADLINE_KEY, 1, 1)
     assert T.tcm_tune_load(good + "\n" + bad + "\n") == T.TCM_ERR_INVALID_VALUE
     assert T.tcm_tune_table() == ""  # the good line was not applied either
     assert T.tcm_tune_load("") == T.TCM_OK  # empty text: nothing to do

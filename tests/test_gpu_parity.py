@@ -407,6 +407,7 @@ def test_autotune_choice_is_used_and_correct(dtype):
     """tcm_tune times the candidates, records the fastest; the next tcm_gemm on
     the same signature launches exactly that plan and stays correct."""
     from gpu_util import to_device
+    saved = T.tcm_tune_table()  # the shipped table, restored afterwards
     T.tcm_tune_clear()
     try:
         p = S.small_problem(dtype, 768, 512, 1024, seed=110, bias=True, relu=True)
@@ -421,11 +422,12 @@ def test_autotune_choice_is_used_and_correct(dtype):
                               torch.cuda.current_stream().cuda_stream)
         assert st == T.TCM_OK and best["kernel"] == 1
         table = T.tcm_tune_table().strip().splitlines()
-        assert len(table) == 1 and table[0].startswith(f"tcm-tune-1 1 {p.M} {p.N} {p.K} ")
+        assert len(table) == 1 and table[0].startswith("tcm-tune-2 ") and table[0].endswith(f" {p.M} {p.N} {p.K}")
         say(f"       tuned: {table[0]}")
         C2, plan = run_tcm(p, g)
-        assert f"config={best['config']} " in plan
+        assert f"config={best['config']} " in plan and " tuned=" in plan
         assert ("mode=dp" if best["mode"] == 1 else "mode=streamk") in plan
         check(p, g, C2)
     finally:
         T.tcm_tune_clear()
+        assert T.tcm_tune_load(saved) == T.TCM_OK
