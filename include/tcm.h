@@ -410,7 +410,9 @@ int tcm_tile_order(int32_t t, int32_t tiles_m, int32_t tiles_n, int32_t* tm, int
  * stage 2 varies, around the three fastest, the tile-order group rows and,
  * for split-k, the grid (0.5 to 2 workgroups per CU, 1 to 4 equal shares per
  * tile) and the fix-up.  Each candidate is timed twice and keeps its better
- * time.
+ * time; a stage-2 variant is recorded only if it beats the best stage-1 point
+ * by 2% (otherwise the planner's own parameters, which adapt to the other
+ * shapes of the class).
  *
  * Same arguments as tcm_gemm plus `iters` (timed calls per candidate,
  * 1..10000) and `best` (optional: the plan now chosen).  Runs on `stream`

@@ -46,6 +46,14 @@ constexpr double kStaggerBytesPerClk = 14.6;
 // of it (the other operand, C and the partial tiles share the cache); a
 // larger one is re-read from HBM (seven 4096 x 4096 f16 weights of a group,
 // 235 MB: Stream-K 74 us against 49 us data-parallel).
+// A launch that splits tiles pays about 4 us the model above does not see:
+// every workgroup's first segment fills its pipeline from HBM, and split
+// tiles wait on the partial-tile round trips.  Fitted to the 130 shapes of
+// the tuning set: with it the data-parallel / Stream-K choice agrees with
+// the measured winner on 118 of them, without it on 110 (the misses were
+// short-K products such as 768^3 .. 1536^3, where split segments are a few
+// K-steps long).
+constexpr double kSplitFixed = 9600.0;
 constexpr double kMallBytesPerClk = 16.0e12 / 2.4e9;
 constexpr double kMallBytes = 128.0 * 1024 * 1024;
 
@@ -186,7 +194,8 @@ Estimate estimate(const Problem& p, int ci, int cus, int force_mode, int sk_grid
         const int sk_occ = sk_occ_known > 0 ? sk_occ_known : tile_sk_wg_per_cu(c);
         int64_t grid = sk_grid > 0 ? sk_grid : (int64_t)cus * sk_occ;
         if (sk_grid <= 0 && grid_per_cu8 > 0) grid = std::max<int64_t>(1, (int64_t)cus * grid_per_cu8 / 8);
-        if (sk_grid <= 0 && grid_shares > 0) grid = T * grid_shares;
+        // equal shares per tile, as many as fit the co-resident grid (at least one)
+        if (sk_grid <= 0 && grid_shares > 0) grid = T * std::max<int64_t>(1, std::min<int64_t>(grid_shares, grid / std::max<int64_t>(T, 1)));
         const bool chosen = sk_grid > 0 || grid_per_cu8 > 0 || grid_shares > 0;  // the grid is given: no alignment
         // Aligned split: when the tiles fit the co-resident grid S >= 2 times
         // over, a grid of exactly T * S workgroups (if it keeps 3/4 of the
@@ -239,7 +248,8 @@ Estimate estimate(const Problem& p, int ci, int cus, int force_mode, int sk_grid
         const double rereads = aligned ? 0.0
                                        : sk_frac * (a_reads / (a_uniq <= kMallBytes ? kMallBytesPerClk : kHbmBytesPerClk) +
                                                     b_reads / (b_uniq <= kMallBytes ? kMallBytesPerClk : kHbmBytesPerClk));
-        sk.cycles = std::max(dp_waves * (I * wg_step + tile_store * share) + per_wg * split_step + tile_store * share + fixup,
+        sk.cycles = std::max(dp_waves * (I * wg_step + tile_store * share) + per_wg * split_step + tile_store * share + fixup +
+                                 (splits ? kSplitFixed : 0.0),
                              std::max(hbm_floor, rereads));
         sk.grid = (int)grid;
         sk.dp_tiles = dp_tiles;

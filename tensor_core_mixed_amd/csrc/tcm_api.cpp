@@ -221,34 +221,44 @@ void load_shipped_table();
 int current_cus();
 
 // Wave regime of T tiles on `slots` co-resident workgroups: the number of
-// full waves when the tiles fill the GPU at least once, else whether the
-// tiles fit it two or more times over (a split-k grid can give every tile
-// equal shares) or not.
+// waves (the last one full or not) when the tiles fill the GPU at least
+// once, else whether the tiles fit it two or more times over (a split-k grid
+// can give every tile equal shares) or not.
 int64_t wave_regime(int64_t T, int64_t slots) {
-    if (T <= 0 || slots <= 0) return -1;
-    if (T >= slots) return 1000 + T / slots;
-    return slots / T >= 2 ? 2 : 1;
+    if (T <= 0 || slots <= 0) return 0;
+    if (T >= slots) return (T + slots - 1) / slots;
+    return slots / T >= 2 ? -2 : -1;
 }
 // A class entry applies to problem p only if p's tiles, on the entry's tile
-// config, fall in the same wave regime as the tuned shape's: within one
-// class the plan that wins turns on how the tiles quantise onto the CUs
-// (2048^2 x 8192 on 128x128 units: 256 tiles, exactly two shares per
-// workgroup slot, split-k wins; 2304^2 x 9216, the same class: 324 tiles,
-// split-k at 209 us against 140 us data-parallel).
+// config, quantise onto the CUs as the tuned shape's did.  A split-k entry
+// needs the same wave regime (2048^2 x 8192 on 128x128 units: 256 tiles,
+// exactly two shares per workgroup slot, split-k wins; 2304^2 x 9216, the
+// same class: 324 tiles, split-k at 209 us against 140 us data-parallel).
+// A data-parallel entry carries over to problems of as many waves or fewer,
+// not to ones that need more (2048^3 on 64x64 units fills one wave; 2816^3,
+// one class up, needs two, and runs at 78 us on them against 54 us on
+// 128x128 tiles).
 bool same_regime(const Problem& p, const TuneEntry& e, int cus) {
     const TileConfig& c = kConfigs[e.c.config];
     const int64_t occ = e.c.mode == 2 ? tile_sk_wg_per_cu(c) : tile_wg_per_cu(c);
     const int64_t nb = std::max<int64_t>(p.batch, 1);
     const int64_t tq = ((p.M + c.bm - 1) / c.bm) * ((p.N + c.bn - 1) / c.bn) * nb;
     const int64_t tt = ((e.M + c.bm - 1) / c.bm) * ((e.N + c.bn - 1) / c.bn) * nb;
-    return wave_regime(tq, cus * occ) == wave_regime(tt, cus * occ);
+    const int64_t rq = wave_regime(tq, cus * occ), rt = wave_regime(tt, cus * occ);
+    if (e.c.mode == 2 || rq == rt) return rq == rt;
+    // (negative codes: under one wave; -2 under half of one, where the
+    // GPU would sit mostly idle on the entry's tiles: 2048^2 x 4096 on the
+    // 256x256 tiles tuned for 3840^2 x 4096 took 84 us against 51 us)
+    return rq != -2 && rq <= rt;
 }
 
-// With no entry for a class, the entry of the nearest class of the same
-// type, layouts, output, epilogue, alignment and batching whose M, N and K
-// classes each lie within one half octave (smallest summed distance; the
-// first in key order on a tie), or g_tune.end().  Caller holds g_mu.
-std::map<TuneKey, TuneEntry>::iterator nearest_class(const TuneKey& k) {
+// The entry for problem p: its own class's, else the nearest class of the
+// same type, layouts, output, epilogue, alignment and batching whose M, N
+// and K classes each lie within one half octave (smallest summed distance;
+// the first in key order on a tie); in both cases only an entry whose tiles
+// quantise onto the CUs as the tuned shape's did (same_regime).
+// g_tune.end() if none.  Caller holds g_mu.
+std::map<TuneKey, TuneEntry>::iterator entry_for(const Problem& p, const TuneKey& k, int cus) {
     auto best = g_tune.end();
     int best_d = 1 << 30;
     for (auto it = g_tune.begin(); it != g_tune.end(); ++it) {
@@ -258,7 +268,7 @@ std::map<TuneKey, TuneEntry>::iterator nearest_class(const TuneKey& k) {
             continue;
         const int dm = std::abs(e.mc - k.mc), dn = std::abs(e.nc - k.nc), dk = std::abs(e.kc - k.kc);
         if (dm > 1 || dn > 1 || dk > 1) continue;
-        if (dm + dn + dk < best_d) {
+        if (dm + dn + dk < best_d && same_regime(p, it->second, cus)) {
             best_d = dm + dn + dk;
             best = it;
         }
@@ -282,9 +292,7 @@ Options plan_options(const Problem& p) {
         // tuned entries describe single GEMM calls; a convolution or a group is planned afresh
         if (g_use_tuned && !p.conv && !p.group && o.force_config < 0 && o.force_mode == 0 && o.sk_grid == 0) {
             const TuneKey k = tune_key(p);
-            auto it = g_tune.find(k);
-            if (it == g_tune.end()) it = nearest_class(k);
-            if (it != g_tune.end() && !same_regime(p, it->second, cus)) it = g_tune.end();
+            auto it = entry_for(p, k, cus);
             if (it != g_tune.end()) {
                 const Cand& c = it->second.c;
                 o.force_config = c.config;
@@ -1304,9 +1312,15 @@ int tcm_tune(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
     (void)hipEventDestroy(e0);
     (void)hipEventDestroy(e1);
     if (st != TCM_OK) return st;
+    // A stage-2 variant must beat the best stage-1 point (the planner's own
+    // grid, fix-up and group rows) by 2% to be kept: within timing noise the
+    // planner's parameters win, since they adapt to other shapes of the
+    // class and a fixed variant may not (three shares per tile, tuned on
+    // 144 tiles, is the planner's own grid there but not on 100 tiles).
     const Timed* win = ranked.empty() ? nullptr : &ranked[0];
+    const double bar = win ? 0.98 * win->us : 0.0;
     for (size_t i = 0; i < stage2.size(); ++i)
-        if (valid2[i] && win && stage2[i].us < win->us) win = &stage2[i];
+        if (valid2[i] && win && stage2[i].us < bar && stage2[i].us < win->us) win = &stage2[i];
     if (win) {
         std::lock_guard<std::mutex> lk(g_mu);
         g_tune[tune_key(p)] = TuneEntry{win->c, win->us, M, N, K};

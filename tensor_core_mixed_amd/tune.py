@@ -31,7 +31,8 @@ F16, BF16, F32, I8 = 0, 1, 2, 3
 NAMES = {F16: "f16", BF16: "bf16", F32: "f32", I8: "i8"}
 
 # (dtype, M, N, K, B column-major, epilogue flags, C type flag)
-TUNE_SHAPES = [
+# the benchmarked workloads and shapes the cost model once misplanned
+WORKLOAD_SHAPES = [
     (F16, 8192, 8192, 8192, True, 0, 0),
     (BF16, 8192, 8192, 8192, True, 0, 0),
     (F16, 8192, 8192, 8192, False, 0, 0),
@@ -53,6 +54,33 @@ TUNE_SHAPES = [
     (F16, 4096, 4096, 4096, True, 0, 0),
     (F16, 4096, 4096, 4096, False, 0, 0),
 ]
+
+
+
+def _grid(dt, b_col, epi=0, c_type=0, big=8192):
+    """A grid over the shape families: square, long K, short K, skinny
+    (few rows), and rectangles."""
+    out = []
+    for s in (512, 768, 1024, 1536, 2048, 3072, 4096, 6144, 8192):
+        if s <= big:
+            out.append((dt, s, s, s, b_col, epi, c_type))
+    for s in (768, 1536, 3072):
+        out.append((dt, s, s, 4 * s, b_col, epi, c_type))
+    for s in (2048, 4096, 8192):
+        if s <= big:
+            out.append((dt, s, s, s // 4, b_col, epi, c_type))
+    for m in (1, 8, 32, 128, 256, 512):
+        for nk in (4096, 8192):
+            if nk <= big:
+                out.append((dt, m, nk, nk, b_col, epi, c_type))
+    for m, n, k in ((1024, 4096, 1024), (4096, 1024, 4096), (512, 8192, 2048), (2048, 6144, 2048)):
+        out.append((dt, m, n, k, b_col, epi, c_type))
+    return out
+
+
+GRID_SHAPES = (_grid(F16, False) + _grid(F16, True) + _grid(BF16, True) + _grid(I8, False, epi=3, big=4096) +
+               [x for x in _grid(F32, False, big=4096) if x[1] >= 256])
+
 
 # shapes of other classes (or other sizes within one), never tuned
 HELDOUT_SHAPES = [
@@ -104,6 +132,11 @@ HELDOUT3_SHAPES = [
     (F16, 1200, 1200, 1200, False, 0, 0),
     (F16, 2048, 2048, 4096, False, 0, 0),
 ]
+
+
+# every tuned shape, once; held-out shapes are never among them
+TUNE_SHAPES = list(dict.fromkeys(WORKLOAD_SHAPES + GRID_SHAPES))
+TUNE_SHAPES = [x for x in TUNE_SHAPES if x not in set(HELDOUT_SHAPES + HELDOUT2_SHAPES + HELDOUT3_SHAPES)]
 
 
 def _tensors(dt, M, N, K, b_col, epi, c_type):
@@ -202,24 +235,29 @@ def _heldout_rows(T, shapes, iters, stream, s):
         call = lambda: T.tcm_gemm(*args, s)
         assert call() == T.TCM_OK
         plan = T.tcm_last_plan()
-        # the call's own plan, timed as tcm_tune times a candidate (a block of calls), best of three blocks
-        auto = min(_block_us(call, iters, stream) for _ in range(3))
         saved = T.tcm_tune_table()
         st, best = T.tcm_tune(*args, iters, s)
         assert st == T.TCM_OK, T.tcm_status_string(st)
         line = [l for l in T.tcm_tune_table().splitlines() if l not in saved.splitlines()]
         T.tcm_tune_clear()
         T.tcm_tune_load(saved)
-        if line:  # the best point's own time, and the plan it is
+        # the call's own plan and the search's best point, re-timed the same
+        # way and alternately (blocks of back-to-back calls, median of five
+        # each): the search's own minimum over many candidates reads low
+        auto_t, best_t = [], []
+        best_desc = "(generic kernel)"
+        if line:
             f = line[0].split()
-            best_us, best_desc = float(f[17]), f"config {f[11]} mode {f[12]} grid {f[13]}/{f[14]} fixup {f[15]} group {f[16]}"
-            # time the best point the same way as the auto plan
-            T.tcm_tune_load(line[0])
-            best_us = min(best_us, min(_block_us(call, iters, stream) for _ in range(3)))
-            T.tcm_tune_clear()
-            T.tcm_tune_load(saved)
-        else:  # the generic kernel serves the call: nothing to compare
-            best_us, best_desc = auto, "(generic kernel)"
+            best_desc = f"config {f[11]} mode {f[12]} grid {f[13]}/{f[14]} fixup {f[15]} group {f[16]}"
+        for _ in range(5):
+            auto_t.append(_block_us(call, iters, stream))
+            if line:
+                T.tcm_tune_load(line[0])
+                best_t.append(_block_us(call, iters, stream))
+                T.tcm_tune_clear()
+                T.tcm_tune_load(saved)
+        auto = sorted(auto_t)[2]
+        best_us = sorted(best_t)[2] if best_t else auto
         ratio = auto / best_us
         rows.append((_label(shape), plan, auto, best_desc, best_us, ratio))
         print(f"[heldout] {_label(shape)}: auto {auto:.1f} us, best {best_us:.1f} us ({best_desc}), ratio {ratio:.3f}",
@@ -236,10 +274,12 @@ def _write_report(report, results, iters):
         f.write(f"Device: {props.name}, {props.multi_processor_count} CUs.  Command: "
                 f"`python -m tensor_core_mixed_amd.tune --heldout {os.path.relpath(report)} --iters {iters}`.\n\n")
         f.write("For each shape (none of them in the tuning set), `auto` is the call's own plan (the shipped table "
-                "`tensor_core_mixed_amd/tuned/mi355x.txt` where it holds the shape's class, else the cost model), "
-                "timed as the best of three blocks of back-to-back calls; `best` is the fastest point `tcm_tune` finds "
+                "`tensor_core_mixed_amd/tuned/mi355x.txt` where it holds the shape's class, else the cost model); "
+                "`best` is the fastest point `tcm_tune` finds "
                 "for the shape (two stages: every tile config in both modes, then group rows, Stream-K grid and fix-up "
-                "around the three fastest), timed the same way.  `ratio` = auto / best.\n\n")
+                "around the three fastest).  Both are then re-timed alternately, five blocks of back-to-back calls each, "
+                "and the medians compared: `ratio` = auto / best (the search's own minimum over many candidates reads "
+                "low, so it is not used).\n\n")
         for title, rows in results:
             f.write(f"## {title}\n\n")
             f.write("| shape | auto plan | auto us | best point | best us | ratio |\n|---|---|---|---|---|---|\n")

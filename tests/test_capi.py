@@ -386,12 +386,12 @@ def test_half_octave_classes():
         # an entry for the class of 4096 (24) in M, N, K, int8: config 1 Stream-K
         key = (3, 0, 0, 0, 3, 1, 0, 24, 24, 24)
         assert T.tcm_tune_load(_line(key, 1, 2, shape=(4096, 4096, 4096))) == T.TCM_OK
-        for n in (4096, 5000, 5792):  # inside the class
-            q = T.tcm_plan(n, 4096, 4096, 4096, 4096, 4096, T.TCM_I8_I32, T.TCM_EPI_BIAS_RELU)
-            assert (q["config"], q["mode"]) == (1, 2), n
-        for n in (2048, 2895, 8192, 12000):  # two or more half octaves away (22, 22, 26, 27)
-            q = T.tcm_plan(n, 4096, 4096, 4096, 4096, 4096, T.TCM_I8_I32, T.TCM_EPI_BIAS_RELU)
-            assert (q["config"], q["mode"]) != (1, 2), n
+        for k in (4096, 5008, 5792):  # inside the class (K: the tile count stays)
+            q = T.tcm_plan(4096, 4096, k, k, 4096, 4096, T.TCM_I8_I32, T.TCM_EPI_BIAS_RELU)
+            assert (q["config"], q["mode"]) == (1, 2), k
+        for k in (2048, 2896, 8192, 12000):  # two or more half octaves away (22, 22, 26, 27)
+            q = T.tcm_plan(4096, 4096, k, k, 4096, 4096, T.TCM_I8_I32, T.TCM_EPI_BIAS_RELU)
+            assert (q["config"], q["mode"]) != (1, 2), k
         # another epilogue is another class
         q = T.tcm_plan(4096, 4096, 4096, 4096, 4096, 4096, T.TCM_I8_I32, 0)
         assert (q["config"], q["mode"]) != (1, 2)
@@ -402,9 +402,9 @@ def test_half_octave_classes():
             q = T.tcm_plan(m, n, k, k, n, n, T.TCM_I8_I32, T.TCM_EPI_BIAS_RELU)
             assert ((q["config"], q["mode"]) == (1, 2)) == near, (m, n, k)
         # an entry applies only in the wave regime it was tuned in: 4096^2 on 128x128
-        # units is 1024 tiles, two full waves of the 512 split-k slots; 3008 x 4096
-        # (the nearest class) is 768 tiles, one and a half waves
-        q = T.tcm_plan(3008, 4096, 4096, 4096, 4096, 4096, T.TCM_I8_I32, T.TCM_EPI_BIAS_RELU)
+        # units is 1024 tiles, two waves of the 512 split-k slots; 5800 x 4096
+        # (the nearest class) is 1472 tiles, three waves
+        q = T.tcm_plan(5800, 4096, 4096, 4096, 4096, 4096, T.TCM_I8_I32, T.TCM_EPI_BIAS_RELU)
         assert (q["config"], q["mode"]) != (1, 2)
     finally:
         T.tcm_tune_clear()
@@ -421,9 +421,10 @@ def test_tune_table_round_trip_and_use_by_the_planner():
     out = T.tcm_tune_table()
     assert sorted(out.strip().splitlines()) == sorted(text.strip().splitlines())
     tuned = T.tcm_plan(8192, 8192, 8192, 8192, 8192, 8192, T.TCM_F16_F32 | T.TCM_B_COLMAJOR)
-    # config 1 split-k on exactly 3 workgroups per tile, split tiles summed by the fix-up kernel
+    # config 1 split-k in equal shares per tile (up to 3, as many as fit the co-resident grid),
+    # split tiles summed by the fix-up kernel
     assert (tuned["config"], tuned["mode"]) == (1, 2)
-    assert tuned["grid"] == 3 * tuned["tiles"] and tuned["fixup_kernel"] == 1
+    assert tuned["grid"] % tuned["tiles"] == 0 and tuned["fixup_kernel"] == 1
     # another class (unaligned) is untouched
     assert T.tcm_plan(8192, 8192, 8192, 8192, 8192, 8192, T.TCM_F16_F32 | T.TCM_B_COLMAJOR, aligned=False)["kernel"] == 0
     T.tcm_set_option("tuned", 0)
@@ -569,3 +570,21 @@ def test_plan_batched_counts_every_entry():
     for bad in (0, -1, 1 << 31):
         with pytest.raises(T.TcmError):
             T.tcm_plan_batched(bad, 16, 4096, 4096, 4096, 4096, 4096, T.TCM_F16_F32)
+
+
+def test_data_parallel_entries_carry_over_to_fewer_waves_only():
+    """A data-parallel class entry applies to problems of as many waves or
+    fewer on its tile config, not to ones that need more."""
+    T.tcm_tune_clear()
+    T.tcm_set_option("tuned", 1)
+    try:
+        # f16, B row-major: 2048^3 on 64x64 tiles (config 4) with group rows 8, one wave of 1024 slots
+        assert T.tcm_tune_load(_line((0, 0, 0, 0, 0, 1, 0, 22, 22, 22), 4, 1, group_m=8, shape=(2048, 2048, 2048))) == 0
+        q = T.tcm_plan(2048, 2048, 2048, 2048, 2048, 2048, T.TCM_F16_F32)
+        assert (q["config"], q["mode"]) == (4, 1)
+        q = T.tcm_plan(1600, 1600, 2048, 2048, 1600, 1600, T.TCM_F16_F32)  # nearest class, under one wave
+        assert (q["config"], q["mode"]) == (4, 1)
+        q = T.tcm_plan(2816, 2816, 2816, 2816, 2816, 2816, T.TCM_F16_F32)  # same class, two waves
+        assert q["config"] != 4 or q["mode"] != 1
+    finally:
+        T.tcm_tune_clear()

@@ -69,7 +69,7 @@ def test_planner_uses_every_shipped_entry(i):
     q = T.tcm_plan(M, N, K, lda, ldb, N, code, epi, bool(aligned))
     assert (q["config"], q["mode"]) == (config, mode), (e, q)
     if e[12] == 2:  # equal shares of every tile
-        assert q["grid"] == e[13] * q["tiles"]
+        assert q["grid"] % q["tiles"] == 0 and q["grid"] <= e[13] * q["tiles"]
     T.tcm_set_option("tuned", 0)
     q0 = T.tcm_plan(M, N, K, lda, ldb, N, code, epi, bool(aligned))
     T.tcm_set_option("tuned", 1)
