@@ -707,6 +707,31 @@ def run_all(args):
             json.dump(rows, f, indent=1)
 
 
+def render_report(src, dst):
+    """A markdown table from the JSON rows `--all --report` writes."""
+    rows = json.load(open(src))
+    L = ["# bench.py --all: every workload, timed on one MI355X", "",
+         "Made by `python bench.py --all --tune --no-cpu --report R.json` on the GPU, then "
+         "`python bench.py --render-report R.json profiles/bench_all.md`.  Each case warms up for at least 200 ms; "
+         "`block` is the average of back-to-back calls between two events, `per call` the median of calls timed one by "
+         "one (it includes the launch gap).  For the split-k workloads every mode is timed: `auto` (the planner, with "
+         "the shipped tuning table), `dp` (data-parallel tiles only) and `streamk`; `lift` = dp / streamk.  `cold` "
+         "(skinny products): the median call after a 512 MiB write that evicts the MALL.  `tuned`: the same call after "
+         "`tcm_tune` searched it (block time).", "",
+         "| workload | mode | block us | per call us | TFLOP/s (TOP/s) | of peak | of HBM | cold us | lift | tuned us | plan |",
+         "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        pc = r.get("per_call_us", {}).get("median", "") if isinstance(r.get("per_call_us"), dict) else ""
+        tuned = r.get("tuned", {}).get("ms")
+        plan = " ".join(kv for kv in r["plan"].split() if kv.split("=")[0] in ("kernel", "config", "tile", "mode", "grid",
+                                                                                  "fixup", "group", "tuned"))
+        L.append(f"| {r['workload']} | {r['mode']} | {r['ms'] * 1e3:.1f} | {pc} | {r['tflops']:.1f} | "
+                 f"{100 * r['frac_peak']:.1f}% | {100 * r['hbm_frac']:.1f}% | {r.get('cold_median_us', '')} | "
+                 f"{r.get('streamk_lift_dp_over_sk', '')} | {'' if tuned is None else f'{tuned * 1e3:.1f}'} | `{plan}` |")
+    with open(dst, "w") as f:
+        f.write("\n".join(L) + "\n")
+
+
 def oracle_threads():
     import oracle
     return oracle.get().max_threads()
@@ -828,11 +853,16 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="time every tile config and mode on the split-k workloads")
     ap.add_argument("--tune", action="store_true", help="with --all: also time each workload on its auto-tuned plan")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--render-report", nargs=2, metavar=("JSON", "MD"), default=None,
+                    help="write the markdown table of a --all --report JSON file (host only)")
     ap.add_argument("--summarize-counters", default=None)
     ap.add_argument("--calibration", default=None, help="directory holding the copy-calibration counter runs")
     args = ap.parse_args()
     if args.summarize_counters:
         summarize_counters(args.summarize_counters, args.workload, args.calibration)
+        return
+    if args.render_report:
+        render_report(*args.render_report)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
