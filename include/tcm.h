@@ -118,6 +118,15 @@ enum { TCM_EPI_NONE = 0, TCM_EPI_BIAS = 1, TCM_EPI_RELU = 2, TCM_EPI_BIAS_RELU =
  * layouts take the tiled fast path; anything else runs on the generic
  * kernel, which reads and writes single bytes when a pointer is not a
  * multiple of its element size.
+ * Products of at most 8 rows (at most 16 with option "gemv" = 2) in f16 or
+ * bf16 with row-major A and B run on a split-k GEMV instead of the tiles
+ * when N is a multiple of 4, lda a multiple of 8, ldb of 4, every pointer
+ * 16-byte aligned and B below 2 GiB: B streams from HBM once, 256 columns
+ * per workgroup over an even split of the k range (the Stream-K
+ * reproduction post on leiblog.wang), each lane multiplying the 4 x 4 blocks
+ * of B it loads on the matrix cores' 4x4x4 blocks; the k ranges' partial
+ * sums (ranges x M x N floats of workspace) are added in range order by a
+ * second kernel on the stream, which runs the epilogue.
  * Returns TCM_OK once the work is enqueued; TCM_ERR_INVALID_VALUE for
  * negative sizes, too-small leading dimensions, a NULL operand with a
  * non-empty extent, unknown dtype/flags/epilogue, both output type flags or
@@ -142,6 +151,8 @@ int tcm_gemm(int64_t M, int64_t N, int64_t K,
  * one fixed array of tcm_noalloc_scratch_bytes() bytes per device (64 MiB of
  * partial tiles plus 65536 counters), part of the library's device image and
  * held until the process ends, instead of the per-stream workspace.
+ *   * The split-k GEMV keeps its partial sums in the same array; one that
+ *     needs more runs on the tiles instead.
  *   * A planned split-k launch that needs more than that array runs as
  *     data-parallel tiles instead (no scratch); when split-k is forced
  *     (tcm_set_option "force_mode" 2) such a call returns
@@ -302,7 +313,15 @@ const char* tcm_status_string(int status);
  *                  shares that start at the same k.
  *   "tuned"        1 (default) = use the tuning table (tcm_tune) for problems
  *                  whose class it holds; 0 = ignore it.  force_config /
- *                  force_mode / sk_grid win.
+ *                  force_mode / sk_grid / gemv win.
+ *   "gemv"         the split-k GEMV (tcm_gemm): 0 = planner decides (calls
+ *                  it can serve with at most 8 rows, or the tuning table's
+ *                  choice), 1 = never, 2 = every call it can serve (at most
+ *                  16 rows) unless a tile config or mode is forced.
+ *   "gemv_splits"  0 = planner decides (about two workgroups per CU, the
+ *                  partial sums kept within an eighth of B's bytes), else
+ *                  the number of k ranges, rounded to ranges of a multiple
+ *                  of 64 rows, at most 1024 each (1..4096).
  * Unknown keys or out-of-range values: TCM_ERR_INVALID_VALUE.
  * tcm_get_option returns the value, or -2 for an unknown key.
  */
@@ -311,9 +330,12 @@ int64_t tcm_get_option(const char* key);
 
 /* ---- planning and introspection ------------------------------------------ */
 typedef struct {
-    int32_t kernel;        /* 0 = generic kernel, 1 = tiled MFMA kernel */
+    int32_t kernel;        /* 0 = generic kernel, 1 = tiled MFMA kernel, 2 = split-k GEMV */
     int32_t config;        /* tile-table index (tiled kernel) or -1 */
-    int32_t bm, bn, bk;    /* macro tile; bk in elements */
+    int32_t bm, bn, bk;    /* macro tile; bk in elements.  GEMV: the rows it is
+                              compiled for (1, 2, 4, 8, 16), 256 columns per
+                              workgroup, k rows per range; iters_per_tile = the
+                              k ranges, tiles = the 256-column blocks */
     int32_t mode;          /* 1 = data-parallel, 2 = Stream-K (+ data-parallel tiles) */
     int32_t grid;          /* workgroups launched */
     int64_t tiles;         /* ceil(M/bm) * ceil(N/bn) */
@@ -386,7 +408,7 @@ int tcm_tile_order(int32_t t, int32_t tiles_m, int32_t tiles_n, int32_t* tm, int
  * epilogue flags, whether every pointer is 16-byte aligned, whether the call
  * is a batch, and the half octave of each of M, N and K (floor(2*log2(x)):
  * e.g. every M in [4096, 5792] shares class 24).  An entry gives the tile
- * config and mode, the split-k grid policy (the planner's; g/8 workgroups
+ * config and mode (or the split-k GEMV, config 7 in the text), the split-k grid policy (the planner's; g/8 workgroups
  * per CU; or s workgroups per tile, every tile split into s equal shares),
  * the way split tiles are summed (the planner's, last arrival, fix-up
  * kernel) and the tile-order group rows (the planner's, or 1..16).
@@ -406,8 +428,9 @@ int tcm_tile_order(int32_t t, int32_t tiles_m, int32_t tiles_n, int32_t* tm, int
 /*
  * tcm_tune -- search the tuning space on this problem and record the
  * fastest point for its shape class.  Stage 1 times every tile config in
- * both modes (data-parallel, split-k) with the planner's other parameters;
- * stage 2 varies, around the three fastest, the tile-order group rows and,
+ * both modes (data-parallel, split-k) with the planner's other parameters,
+ * and the split-k GEMV where it can serve the call;
+ * stage 2 varies, around the three fastest tile plans, the tile-order group rows and,
  * for split-k, the grid (0.5 to 2 workgroups per CU, 1 to 4 equal shares per
  * tile) and the fix-up.  Each candidate is timed twice and keeps its better
  * time; a stage-2 variant is recorded only if it beats the best stage-1 point
@@ -431,7 +454,8 @@ int tcm_tune(int64_t M, int64_t N, int64_t K,
  *   "tcm-tune-2 dtype a_col b_col c_type epilogue aligned batched mclass
  *    nclass kclass config mode grid_kind grid_param fixup group_m
  *    microseconds M N K"
- * (c_type 0 = the accumulator type, 1 = f16, 2 = bf16; grid_kind 0 = the
+ * (c_type 0 = the accumulator type, 1 = f16, 2 = bf16; config 7 = the
+ * split-k GEMV, with mode 1 and zeros after it; grid_kind 0 = the
  * planner's, 1 = grid_param/8 workgroups per CU, 2 = grid_param per tile;
  * fixup and group_m 0 = the planner's; M N K = the shape it was tuned on).
  * Writes it NUL-terminated into buf (truncated to len) and returns its full

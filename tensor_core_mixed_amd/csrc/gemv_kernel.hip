@@ -1,0 +1,300 @@
+// Split-k GEMV kernel for products of at most 16 rows: C = epi(A B + bias)
+// with A (M x K, M <= 16) and B (K x N) both row-major, f16 or bf16.
+//
+// Such a product is bound by streaming B once from HBM: it moves K*N
+// operand elements for 2*M*K*N flops, far below the MFMA ridge.  The tiled
+// kernel serves it with a 32- or 64-row MFMA tile (at M = 1, 31 of 32 rows
+// are padding), stages every K-step of B through LDS to transpose it into
+// k-contiguous fragments, and sums Stream-K partial tiles.  Here B never
+// goes through LDS: every wave-wide load is one 512-byte run of one row of B
+// (64 lanes x 4 columns of 2 bytes), and the lane multiplies the 4 x 4
+// block it holds after four such rows on the matrix cores'
+// v_mfma_f32_4x4x4_16b, whose 16 independent 4x4x4 blocks let each lane
+// bring its own columns (see mul_rows_mfma).  Measured on N = K = 4096:
+// that instruction issues in about 4 ns per SIMD (1024 multiply-adds), the
+// VALU v_dot2_f32_f16 in about 1.9 ns (128), so an earlier dot-product
+// inner loop was 4-30% slower from M = 4 on.
+//
+// Work split (the even k-split of the Stream-K reproduction post on
+// leiblog.wang, applied across workgroups of one column block): workgroup
+// (x, y) owns 256 columns and the k range [kw y, kw y + kw); its four waves
+// take a quarter of that range each, 16 rows per chunk, the loads of chunk
+// c+1 in flight while chunk c is multiplied.  The four waves' sums meet in
+// LDS and are added in wave order; with more than one k range the sum is a
+// partial stored to the workspace, and a second kernel adds the ranges in
+// order and runs the epilogue, so the result does not depend on timing.
+// (Letting the last workgroup of a column block add the ranges instead,
+// after an arrival counter, was slower at every M: 9.0 against 7.3 us at
+// M = 1, 27 against 15 us at M = 16.)
+//
+// Rows of B at or past K read as zeros (buffer range check); the A columns
+// past K are zero in LDS, so no padding value reaches a sum.  Columns at or
+// past N are neither loaded nor stored (N is a multiple of 4).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "tcm_internal.h"
+
+namespace tcm {
+namespace gemv {
+
+typedef unsigned u2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u4_t __attribute__((ext_vector_type(4)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+typedef short s4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;                 // four waves
+constexpr int kChunk = 16;                    // rows of B per wave per pipeline step
+constexpr unsigned kOOB = 0x80000000u;        // beyond every buffer range used here: loads read zeros
+constexpr int kRsrcWord3 = 0x00020000;
+
+template <int DT>
+__device__ __forceinline__ float to_f32(unsigned short h) {
+    if constexpr (DT == F16) return (float)__builtin_bit_cast(_Float16, h);
+    else return __builtin_bit_cast(float, (unsigned)h << 16);
+}
+
+// Partial sums: splits x M x N floats.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t partial_rsrc(const GemvArgs& g) {
+    const int64_t bytes = (int64_t)g.splits * g.M * g.N * 4;
+    return __builtin_amdgcn_make_buffer_rsrc(g.partial, (short)0, bytes < (int64_t)kOOB ? (int)bytes : (int)kOOB, kRsrcWord3);
+}
+// sum over y = 0, 1, .. of the partial at byte offset off + y * mn * 4, in
+// that order: the loads of up to 32 k ranges are issued before any is added
+__device__ __forceinline__ float sum_splits(const GemvArgs& g, __amdgpu_buffer_rsrc_t rp, unsigned off, int64_t mn) {
+    const unsigned step = (unsigned)(mn * 4);
+    float s = 0.f;
+    for (int y0 = 0; y0 < g.splits; y0 += 32) {
+        float v[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j)
+            v[j] = y0 + j < g.splits
+                       ? __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rp, off + (unsigned)(y0 + j) * step, 0, 0))
+                       : 0.f;
+#pragma unroll
+        for (int j = 0; j < 32; ++j)
+            if (y0 + j < g.splits) s += v[j];
+    }
+    return s;
+}
+
+// C[m][n] = epi(init + s): init = C_in (with accum) + bias, in binary32;
+// ReLU; stored in C's type (16-bit types rounded to nearest even).
+__device__ __forceinline__ void finish(const GemvArgs& g, int m, int n, float s) {
+    char* c = (char*)g.C;
+    const int64_t idx = (int64_t)m * g.ldc + n;
+    float init = 0.f;
+    if (g.accum) {
+        if (g.c_type == C_F16) init = to_f32<F16>(((const unsigned short*)c)[idx]);
+        else if (g.c_type == C_BF16) init = to_f32<BF16>(((const unsigned short*)c)[idx]);
+        else init = ((const float*)c)[idx];
+    }
+    if (g.has_bias) init = init + ((const float*)g.bias)[n];
+    float v = init + s;
+    if (g.relu) v = v > 0.f ? v : 0.f;
+    if (g.c_type == C_F16) ((_Float16*)c)[idx] = (_Float16)v;
+    else if (g.c_type == C_BF16) ((__bf16*)c)[idx] = (__bf16)v;
+    else ((float*)c)[idx] = v;
+}
+
+template <int DT, int MB>
+struct Gemv {
+    static constexpr int D = 2;  // register sets of B chunks (four measured no faster)
+    static constexpr int KW_MAX = 1024;  // k per workgroup the LDS copy of A holds (host keeps kw <= this)
+
+    // chunk of 16 rows of B for one lane: 4 columns (8 bytes) per row
+    struct Rows {
+        u2_t v[kChunk];
+    };
+
+    __device__ __forceinline__ static void load_rows(Rows& r, __amdgpu_buffer_rsrc_t rb, unsigned lane_off, int k, int K,
+                                                     int ldb_bytes) {
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) {
+            const unsigned off = (k + i < K && lane_off != kOOB) ? (unsigned)((k + i) * ldb_bytes) + lane_off : kOOB;
+            r.v[i] = __builtin_bit_cast(u2_t, __builtin_amdgcn_raw_buffer_load_b64(rb, off, 0, 0));
+        }
+    }
+
+    // The product on the matrix cores: v_mfma_f32_4x4x4_16b runs 16
+    // independent 4x4x4 blocks, lane 4b+i giving row i of block b's A (4 k
+    // values), lane 4b+j column j of its B, and getting column j of its D
+    // (4 rows).  Every block here takes the same A (4 rows of the product),
+    // and lane l gives one of its own columns as B: one instruction covers 4
+    // rows x 64 columns x 4 k.  The 4 x 4 block of B a lane loads (4 rows of
+    // 4 columns) is transposed in registers, two v_perm per column.
+    static constexpr int MG = MB < 4 ? 1 : MB / 4;  // row groups of 4
+    __device__ __forceinline__ static void mul_rows_mfma(f4_t (&acc)[MG][4], const Rows& r, const unsigned short* sAh, int kw,
+                                                         int kc, int lane) {
+#pragma unroll
+        for (int q = 0; q < kChunk / 4; ++q) {
+            const u2_t r0 = r.v[4 * q], r1 = r.v[4 * q + 1], r2 = r.v[4 * q + 2], r3 = r.v[4 * q + 3];
+            u2_t bc[4];  // column c of the block: (B[k][c], B[k+1][c]) (B[k+2][c], B[k+3][c])
+            bc[0] = u2_t{__builtin_amdgcn_perm(r1[0], r0[0], 0x05040100u), __builtin_amdgcn_perm(r3[0], r2[0], 0x05040100u)};
+            bc[1] = u2_t{__builtin_amdgcn_perm(r1[0], r0[0], 0x07060302u), __builtin_amdgcn_perm(r3[0], r2[0], 0x07060302u)};
+            bc[2] = u2_t{__builtin_amdgcn_perm(r1[1], r0[1], 0x05040100u), __builtin_amdgcn_perm(r3[1], r2[1], 0x05040100u)};
+            bc[3] = u2_t{__builtin_amdgcn_perm(r1[1], r0[1], 0x07060302u), __builtin_amdgcn_perm(r3[1], r2[1], 0x07060302u)};
+#pragma unroll
+            for (int g = 0; g < MG; ++g) {
+                const u2_t a = *(const u2_t*)(sAh + (4 * g + (lane & 3)) * kw + kc + 4 * q);
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    if constexpr (DT == F16)
+                        acc[g][c] = __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(h4_t, a), __builtin_bit_cast(h4_t, bc[c]),
+                                                                       acc[g][c], 0, 0, 0);
+                    else
+                        acc[g][c] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(s4_t, a),
+                                                                           __builtin_bit_cast(s4_t, bc[c]), acc[g][c], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    // LDS: the A block (at least 4 rows) while the waves multiply, then their four sums
+    static constexpr int MBA = MB < 4 ? 4 : MB;
+    static constexpr int A_BYTES = MBA * KW_MAX * 2, RED_BYTES = 4 * MB * kGemvCols * 4;
+    static constexpr int LDS_BYTES = A_BYTES > RED_BYTES ? A_BYTES : RED_BYTES;
+
+    __device__ static void run(const GemvArgs& g) {
+        __shared__ __attribute__((aligned(16))) unsigned lds[LDS_BYTES / 4];
+        unsigned* sA = lds;
+        float(*red)[MB][kGemvCols] = (float(*)[MB][kGemvCols])lds;
+        const int tid = threadIdx.x, lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int n0 = blockIdx.x * kGemvCols;
+        const int kw = g.kw, k0 = blockIdx.y * kw;
+        const int rw = kw / 4;  // rows per wave
+        const int kb = k0 + wave * rw;
+
+        // B: one buffer range over all of it, from column n0 on
+        const int ldb_bytes = g.ldb * 2;
+        const int64_t rb_bytes = g.b_bytes - (int64_t)n0 * 2;
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            (char*)g.B + (int64_t)n0 * 2, (short)0, rb_bytes < (int64_t)kOOB ? (int)rb_bytes : (int)kOOB, kRsrcWord3);
+        const unsigned lane_off = n0 + 4 * lane < g.N ? (unsigned)(8 * lane) : kOOB;
+
+        // A block [MB][kw] into LDS (rows past M and columns past K as zeros):
+        // its loads are issued before the first chunk of B, so waiting for
+        // them leaves B's in flight
+        const unsigned short* A = (const unsigned short*)g.A;
+        const int per_row = kw / 8;  // 16-byte pieces per row
+        for (int i = tid; i < MBA * per_row; i += kThreads) {
+            const int m = i / per_row, k = k0 + 8 * (i - m * per_row);
+            u4_t v = {0u, 0u, 0u, 0u};
+            if (m < g.M && k < g.K) {
+                const unsigned short* src = A + (int64_t)m * g.lda + k;
+                if (k + 8 <= g.K) {
+                    v = *(const u4_t*)src;
+                } else {
+                    unsigned short e[8];
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) e[j] = k + j < g.K ? src[j] : (unsigned short)0;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) v[j] = (unsigned)e[2 * j] | ((unsigned)e[2 * j + 1] << 16);
+                }
+            }
+            *(u4_t*)(sA + (m * kw + 8 * (i - m * per_row)) / 2) = v;
+        }
+
+        // a ring of D register sets: the loads of chunks c+1 .. c+D-1 are in
+        // flight while chunk c is multiplied (the counter of outstanding
+        // loads, 63 at most, holds (D - 1) x 16 of them)
+        static_assert((D - 1) * kChunk <= 63, "loads in flight within the vmcnt range");
+        Rows ring[D];
+        const int chunks = rw / kChunk;
+#pragma unroll
+        for (int j = 0; j < D; ++j)
+            if (j < chunks) load_rows(ring[j], rb, lane_off, kb + j * kChunk, g.K, ldb_bytes);
+        __syncthreads();  // sA written
+        const unsigned short* sAh = (const unsigned short*)sA;
+        f4_t acc[MG][4];
+#pragma unroll
+        for (int q = 0; q < MG; ++q)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[q][c] = f4_t{0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < chunks; c += D) {
+#pragma unroll
+            for (int j = 0; j < D; ++j) {
+                if (c + j < chunks) {
+                    mul_rows_mfma(acc, ring[j], sAh, kw, wave * rw + (c + j) * kChunk, lane);
+                    if (c + j + D < chunks) load_rows(ring[j], rb, lane_off, kb + (c + j + D) * kChunk, g.K, ldb_bytes);
+                }
+            }
+        }
+        __syncthreads();  // the A block is dead
+        // row 4q+i of the product, columns 4 lane .. 4 lane + 3
+#pragma unroll
+        for (int q = 0; q < MG; ++q)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (4 * q + i < MB) *(f4_t*)&red[wave][4 * q + i][4 * lane] = f4_t{acc[q][0][i], acc[q][1][i], acc[q][2][i], acc[q][3][i]};
+        // the four waves' sums, added in wave order
+        __syncthreads();
+        const int n = n0 + tid;
+        const bool col = n < g.N;
+        if (g.splits == 1) {
+            if (!col) return;
+#pragma unroll
+            for (int m = 0; m < MB; ++m)
+                if (m < g.M) finish(g, m, n, ((red[0][m][tid] + red[1][m][tid]) + red[2][m][tid]) + red[3][m][tid]);
+            return;
+        }
+        // the k range's partial sums, added by the second kernel
+        const int64_t mn = (int64_t)g.M * g.N;
+        const __amdgpu_buffer_rsrc_t rp = partial_rsrc(g);
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+            if (m < g.M && col)
+                __builtin_amdgcn_raw_buffer_store_b32(
+                    __builtin_bit_cast(int, ((red[0][m][tid] + red[1][m][tid]) + red[2][m][tid]) + red[3][m][tid]), rp,
+                    (unsigned)((blockIdx.y * mn + (int64_t)m * g.N + n) * 4), 0, 0);
+    }
+};
+
+template <int DT, int MB>
+__global__ __launch_bounds__(kThreads) void gemv_split_kernel(GemvArgs g) {
+    Gemv<DT, MB>::run(g);
+}
+
+// Output (m, n) = epi(init + sum over splits y, in order, of partial[y][m][n]).
+__global__ __launch_bounds__(kThreads) void gemv_reduce_kernel(GemvArgs g) {
+    const int64_t mn = (int64_t)g.M * g.N;
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i >= mn) return;
+    const int m = (int)(i / g.N), n = (int)(i - (int64_t)m * g.N);
+    finish(g, m, n, sum_splits(g, partial_rsrc(g), (unsigned)(i * 4), mn));
+}
+
+template <int DT>
+int launch_dt(const GemvArgs& a, void* stream) {
+    const dim3 grid((unsigned)((a.N + kGemvCols - 1) / kGemvCols), (unsigned)a.splits);
+    hipStream_t s = (hipStream_t)stream;
+    switch (gemv_rows_bucket(a.M)) {
+    case 1: hipLaunchKernelGGL((gemv_split_kernel<DT, 1>), grid, dim3(kThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((gemv_split_kernel<DT, 2>), grid, dim3(kThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((gemv_split_kernel<DT, 4>), grid, dim3(kThreads), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((gemv_split_kernel<DT, 8>), grid, dim3(kThreads), 0, s, a); break;
+    default: hipLaunchKernelGGL((gemv_split_kernel<DT, 16>), grid, dim3(kThreads), 0, s, a); break;
+    }
+    int st = (int)hipGetLastError();
+    if (st != 0 || a.splits <= 1) return st;
+    const int64_t mn = (int64_t)a.M * a.N;
+    hipLaunchKernelGGL(gemv_reduce_kernel, dim3((unsigned)((mn + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, a);
+    return (int)hipGetLastError();
+}
+
+}  // namespace gemv
+
+int launch_gemv(int dtype, const GemvArgs& a, void* stream) {
+    if (a.M < 1 || a.M > kGemvMaxRows || a.N < 1 || a.N % 4 || a.splits < 1 || a.kw < kGemvKAlign ||
+        a.kw % kGemvKAlign || a.kw > gemv::Gemv<F16, 1>::KW_MAX || (int64_t)a.splits * a.kw < a.K ||
+        (a.splits > 1 && !a.partial) || (int64_t)a.splits * a.M * a.N * 4 >= (int64_t)gemv::kOOB)
+        return (int)hipErrorInvalidValue;
+    if (dtype == F16) return gemv::launch_dt<F16>(a, stream);
+    if (dtype == BF16) return gemv::launch_dt<BF16>(a, stream);
+    return (int)hipErrorInvalidValue;
+}
+
+}  // namespace tcm

@@ -268,6 +268,57 @@ Estimate estimate(const Problem& p, int ci, int cus, int force_mode, int sk_grid
 
 }  // namespace
 
+bool gemv_eligible(const Problem& p) {
+    return (p.dtype == F16 || p.dtype == BF16) && !p.a_col && !p.b_col && !p.conv && !p.group && p.batch <= 1 &&
+           p.M >= 1 && p.M <= kGemvMaxRows && p.N >= 4 && p.N % 4 == 0 && p.K >= 1 && p.K <= (1LL << 22) &&
+           p.lda % 8 == 0 &&
+           p.ldb % 4 == 0 && p.aligned && p.ldc < (1LL << 31) && p.lda < (1LL << 31) &&
+           (p.K - 1) * p.ldb * 2 + p.N * 2 < (1LL << 31);
+}
+
+// Up to 8 rows the GEMV beats the tiled kernel's Stream-K plans on N = K =
+// 4096 (f16: 7.3 / 8.1 / 8.7 / 10.5 us at M = 1 / 2 / 4 / 8 against
+// 10.9-11.1 us); at 16 rows it is slower (12.5 against 11.3 us).
+constexpr int64_t kGemvAutoRows = 8;
+bool gemv_preferred(const Problem& p, const Options& o) {
+    if (o.generic || o.gemv == 1 || o.force_config >= 0 || o.force_mode != 0 || o.sk_grid != 0) return false;
+    if (!gemv_eligible(p)) return false;
+    return o.gemv == 2 || p.M <= kGemvAutoRows;
+}
+
+namespace {
+
+// k ranges of the GEMV: about two workgroups per CU (the 16-row kernel's
+// LDS and register budget), but the partial sums (splits x M x N x 4 bytes)
+// kept within an eighth of B's bytes, and at most kGemvKMax rows a range.
+constexpr int64_t kGemvKMax = 1024;
+void gemv_plan(const Problem& p, const Options& o, int cus, Plan* pl) {
+    const int64_t nb = cdiv(p.N, kGemvCols);
+    int64_t splits = o.gemv_splits;
+    if (splits <= 0) {
+        splits = std::max<int64_t>(1, 2 * cus / nb);
+        splits = std::min<int64_t>(splits, std::max<int64_t>(1, p.K / (16 * p.M)));
+    }
+    splits = std::max<int64_t>(1, std::min(splits, cdiv(p.K, kGemvKAlign)));
+    int64_t kw = cdiv(cdiv(p.K, splits), kGemvKAlign) * kGemvKAlign;
+    if (kw > kGemvKMax) kw = kGemvKMax;
+    splits = cdiv(p.K, kw);
+    pl->kernel = 3;
+    pl->config = -1;
+    pl->bm = gemv_rows_bucket(p.M);
+    pl->bn = kGemvCols;
+    pl->bk = (int)kw;
+    pl->mode = 1;
+    pl->iters = splits;
+    pl->tiles = nb;
+    pl->grid = (int)(nb * splits);
+    pl->dp_tiles = nb;
+    pl->ws_partial_bytes = splits > 1 ? splits * p.M * p.N * 4 : 0;
+    pl->fixup_kernel = splits > 1;
+}
+
+}  // namespace
+
 bool make_plan(const Problem& p, const Options& o, int cus, Plan* out) {
     Plan pl;
     if (p.M < 0 || p.N < 0 || p.K < 0) return false;
@@ -277,6 +328,11 @@ bool make_plan(const Problem& p, const Options& o, int cus, Plan* out) {
         return true;
     }
     if (cus <= 0) cus = kDefaultCUs;
+    if (gemv_eligible(p) && (gemv_preferred(p, o) || (o.gemv == 2 && !o.generic && o.force_config < 0))) {
+        gemv_plan(p, o, cus, &pl);
+        *out = pl;
+        return true;
+    }
     int best = -1;
     Estimate best_e{1e300, 1, 0, 0, 0};
     if (!o.generic) {

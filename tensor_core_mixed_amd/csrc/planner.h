@@ -20,6 +20,8 @@ struct Options {
     int grid_per_cu8 = 0;
     int grid_shares = 0;
     int group_m = 0;        // tile-order group rows (0: the planner's 4)
+    int gemv = 0;           // split-k GEMV for products of at most 16 rows: 0 planner decides, 1 never, 2 whenever eligible
+    int gemv_splits = 0;    // its k ranges (0: the planner's)
     int sk_occ[kNumConfigs] = {0};  // Stream-K workgroups per CU by config (0: static estimate)
 };
 
@@ -49,7 +51,8 @@ struct Problem {
 };
 
 struct Plan {
-    int kernel = 0;   // 0 none (empty problem), 1 generic, 2 tiled
+    int kernel = 0;   // 0 none (empty problem), 1 generic, 2 tiled, 3 split-k GEMV (bm = rows bucket,
+                      // bn = columns per workgroup, bk = k per workgroup, iters = k ranges)
     int config = -1;
     int bm = 0, bn = 0, bk = 0;
     int mode = 1;     // 1 data-parallel, 2 Stream-K (+ data-parallel tiles)
@@ -70,6 +73,13 @@ bool tile_eligible(const Problem& p, const TileConfig& c);
 // estimate), for the data-parallel and the Stream-K kernel.
 int tile_wg_per_cu(const TileConfig& c);
 int tile_sk_wg_per_cu(const TileConfig& c);
+// Split-k GEMV eligibility: f16 / bf16, row-major A and B, 1 <= M <= 16,
+// a single product, N a multiple of 4, 16-byte aligned pointers and rows of
+// A, 8-byte aligned rows of B, B below 2 GiB.
+bool gemv_eligible(const Problem& p);
+// Whether the planner (no option forcing a tile config or mode) takes the
+// GEMV for an eligible p.
+bool gemv_preferred(const Problem& p, const Options& o);
 // Fill `out` for problem p.  Returns false if p is invalid.
 bool make_plan(const Problem& p, const Options& o, int cus, Plan* out);
 // Stream-K share [begin, end) of workgroup wg (same split the kernel uses).

@@ -133,16 +133,27 @@ TuneKey tune_key(const Problem& p) {
     return TuneKey{p.dtype, (int)p.a_col, (int)p.b_col, p.c_type, p.epilogue, (int)p.aligned, p.batch > 1 ? 1 : 0,
                    half_octave(p.M), half_octave(p.N), half_octave(p.K)};
 }
+// The split-k GEMV as a candidate: config kGemvCand, mode 1, no other
+// parameter (its k ranges are the planner's).
+constexpr int kGemvCand = kNumConfigs;
 bool valid_cand(const Cand& c) {
+    if (c.config == kGemvCand)
+        return c.mode == 1 && c.grid_kind == 0 && c.grid_param == 0 && c.fixup == 0 && c.group_m == 0;
     return c.config >= 0 && c.config < kNumConfigs && (c.mode == 1 || c.mode == 2) && c.grid_kind >= 0 &&
            c.grid_kind <= 2 && c.grid_param >= 0 && c.grid_param <= 64 && (c.grid_kind == 0 || c.grid_param > 0) &&
            c.fixup >= 0 && c.fixup <= 2 && c.group_m >= 0 && c.group_m <= 16;
 }
 // Apply candidate c to options o.
 void apply_cand(const Cand& c, Options* o) {
+    o->sk_grid = 0;
+    if (c.config == kGemvCand) {
+        o->force_config = -1;
+        o->force_mode = 0;
+        o->gemv = 2;
+        return;
+    }
     o->force_config = c.config;
     o->force_mode = c.mode;
-    o->sk_grid = 0;
     o->grid_per_cu8 = c.grid_kind == 1 ? c.grid_param : 0;
     o->grid_shares = c.grid_kind == 2 ? c.grid_param : 0;
     if (c.fixup) o->sk_fixup = c.fixup;
@@ -290,17 +301,24 @@ Options plan_options(const Problem& p) {
         std::lock_guard<std::mutex> lk(g_mu);
         o = g_opts;
         // tuned entries describe single GEMM calls; a convolution or a group is planned afresh
-        if (g_use_tuned && !p.conv && !p.group && o.force_config < 0 && o.force_mode == 0 && o.sk_grid == 0) {
+        // (option gemv = 2 asks for the GEMV wherever it can serve: the table is not consulted there)
+        if (g_use_tuned && !p.conv && !p.group && o.force_config < 0 && o.force_mode == 0 && o.sk_grid == 0 &&
+            !(o.gemv == 2 && gemv_eligible(p))) {
             const TuneKey k = tune_key(p);
             auto it = entry_for(p, k, cus);
-            if (it != g_tune.end()) {
+            // a GEMV entry does not apply with option gemv = 1 (never)
+            if (it != g_tune.end() && !(it->second.c.config == kGemvCand && o.gemv == 1)) {
                 const Cand& c = it->second.c;
-                o.force_config = c.config;
-                o.force_mode = c.mode;
-                o.grid_per_cu8 = c.grid_kind == 1 ? c.grid_param : 0;
-                o.grid_shares = c.grid_kind == 2 ? c.grid_param : 0;
-                if (c.fixup && o.sk_fixup == 0) o.sk_fixup = c.fixup;
-                if (c.group_m && o.group_m == 0) o.group_m = c.group_m;
+                if (c.config == kGemvCand) {
+                    o.gemv = 2;  // (a problem it cannot serve is planned as if untuned)
+                } else {
+                    o.force_config = c.config;
+                    o.force_mode = c.mode;
+                    o.grid_per_cu8 = c.grid_kind == 1 ? c.grid_param : 0;
+                    o.grid_shares = c.grid_kind == 2 ? c.grid_param : 0;
+                    if (c.fixup && o.sk_fixup == 0) o.sk_fixup = c.fixup;
+                    if (c.group_m && o.group_m == 0) o.group_m = c.group_m;
+                }
                 char buf[96];
                 snprintf(buf, sizeof buf, " tuned=%d,%d,%d", it->first.mc, it->first.nc, it->first.kc);
                 t_tuned_note = buf;
@@ -408,6 +426,11 @@ std::string describe(const Plan& pl, const Problem& p) {
     char buf[320];
     if (pl.kernel == 0) {
         snprintf(buf, sizeof buf, "empty problem M=%lld N=%lld", (long long)p.M, (long long)p.N);
+    } else if (pl.kernel == 3) {
+        snprintf(buf, sizeof buf,
+                 "kernel=gemv rows=%d cols_per_wg=%d k_per_wg=%d splits=%lld grid=%d M=%lld N=%lld K=%lld dtype=%d%s",
+                 pl.bm, pl.bn, pl.bk, (long long)pl.iters, pl.grid, (long long)p.M, (long long)p.N, (long long)p.K, p.dtype,
+                 pl.fixup_kernel ? " fixup=kernel" : "");
     } else if (pl.kernel == 1) {
         snprintf(buf, sizeof buf, "kernel=generic tile=64x64 tiles=%lld iters=%lld M=%lld N=%lld K=%lld dtype=%d batch=%lld%s",
                  (long long)pl.tiles, (long long)pl.iters, (long long)p.M, (long long)p.N, (long long)p.K, p.dtype,
@@ -504,6 +527,12 @@ int tcm_set_option(const char* key, int64_t value) {
     } else if (!strcmp(key, "tuned")) {
         if (value < 0 || value > 1) return TCM_ERR_INVALID_VALUE;
         g_use_tuned = (int)value;
+    } else if (!strcmp(key, "gemv")) {
+        if (value < 0 || value > 2) return TCM_ERR_INVALID_VALUE;
+        g_opts.gemv = (int)value;
+    } else if (!strcmp(key, "gemv_splits")) {
+        if (value < 0 || value > 4096) return TCM_ERR_INVALID_VALUE;
+        g_opts.gemv_splits = (int)value;
     } else {
         return TCM_ERR_INVALID_VALUE;
     }
@@ -522,6 +551,8 @@ int64_t tcm_get_option(const char* key) {
     if (!strcmp(key, "grid_per_cu8")) return g_opts.grid_per_cu8;
     if (!strcmp(key, "grid_shares")) return g_opts.grid_shares;
     if (!strcmp(key, "tuned")) return g_use_tuned;
+    if (!strcmp(key, "gemv")) return g_opts.gemv;
+    if (!strcmp(key, "gemv_splits")) return g_opts.gemv_splits;
     return -2;
 }
 
@@ -555,7 +586,7 @@ int tcm_plan_batched(int64_t batch, int64_t M, int64_t N, int64_t K, int64_t lda
     fill_sk_occupancy(p, &o);
     Plan pl;
     if (!make_plan(p, o, current_cus(), &pl)) return TCM_ERR_INVALID_VALUE;
-    out->kernel = pl.kernel == 2 ? 1 : 0;
+    out->kernel = pl.kernel == 2 ? 1 : (pl.kernel == 3 ? 2 : 0);
     out->config = pl.config;
     out->bm = pl.bm;
     out->bn = pl.bn;
@@ -694,6 +725,10 @@ int gemm_impl(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int
     fill_sk_occupancy(p, &o);
     Plan pl;
     if (!make_plan(p, o, device_cus(dev), &pl)) return TCM_ERR_INVALID_VALUE;
+    if (noalloc && pl.kernel == 3 && !scratch_fits(pl)) {
+        o.gemv = 1;  // its partial sums do not fit the fixed scratch: the tiled kernel serves the call
+        if (!make_plan(p, o, device_cus(dev), &pl)) return TCM_ERR_INVALID_VALUE;
+    }
     if (noalloc && pl.kernel == 2 && pl.mode == 2 && !scratch_fits(pl)) {
         if (current_options().force_mode == 2) {
             t_last_plan = describe(pl, p) + " (split-k workspace beyond the fixed scratch)";
@@ -731,6 +766,41 @@ int gemm_impl(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int
         g.tiles_m = (int)((M + 63) / 64);
         g.tiles_n = (int)((N + 63) / 64);
         return launch_generic(p.dtype, g, stream) == 0 ? TCM_OK : TCM_ERR_HIP;
+    }
+
+    if (pl.kernel == 3) {
+        GemvArgs v{};
+        v.A = A;
+        v.B = B;
+        v.C = C;
+        v.bias = use_bias ? bias : nullptr;
+        v.M = (int)M;
+        v.N = (int)N;
+        v.K = (int)K;
+        v.lda = (int)lda;
+        v.ldb = (int)ldb;
+        v.ldc = (int)ldc;
+        v.relu = (epilogue & TCM_EPI_RELU) != 0;
+        v.has_bias = use_bias;
+        v.accum = (epilogue & TCM_EPI_ACCUM) != 0;
+        v.c_type = p.c_type;
+        v.splits = (int)pl.iters;
+        v.kw = pl.bk;
+        v.b_bytes = b_one;
+        if (pl.ws_partial_bytes > 0) {
+            if (noalloc) {
+                char* base = nullptr;
+                int st2 = scratch_of(dev, &base);
+                if (st2 != TCM_OK) return st2;
+                v.partial = (float*)base;
+            } else {
+                Workspace w;
+                int ws = get_workspace(dev, stream, pl.ws_partial_bytes, 0, &w);
+                if (ws != TCM_OK) return ws;
+                v.partial = (float*)w.partial;
+            }
+        }
+        return launch_gemv(p.dtype, v, stream) == 0 ? TCM_OK : TCM_ERR_HIP;
     }
 
     TileArgs a{};
@@ -1183,7 +1253,7 @@ int tcm_tune(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
     const int cs = c_elem_bytes(p.c_type);
     p.aligned = ((uintptr_t)A % 16 == 0) && ((uintptr_t)B % 16 == 0) && ((uintptr_t)C % 16 == 0) &&
                 (!use_bias || (uintptr_t)bias % 16 == 0) && ((uintptr_t)C % cs == 0);
-    if (!strstr(t_last_plan.c_str(), "kernel=tile")) return TCM_OK;  // the generic kernel: nothing to choose
+    if (strstr(t_last_plan.c_str(), "kernel=generic")) return TCM_OK;  // the generic kernel: nothing to choose
     hipStream_t s = (hipStream_t)stream;
     hipEvent_t e0, e1;
     if (hipEventCreate(&e0) != hipSuccess) return TCM_ERR_HIP;
@@ -1203,7 +1273,9 @@ int tcm_tune(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
         st = run();  // warm-up, and the plan this candidate really gets
         const std::string plan = t_last_plan;
         const int pm = strstr(plan.c_str(), "mode=streamk") ? 2 : 1;
-        if (st != TCM_OK || field(plan, " config=") != c.config || pm != c.mode) {
+        const bool as_asked = c.config == kGemvCand ? strstr(plan.c_str(), "kernel=gemv") != nullptr
+                                                    : strstr(plan.c_str(), "kernel=tile") && field(plan, " config=") == c.config;
+        if (st != TCM_OK || !as_asked || pm != c.mode) {
             t_cand = nullptr;
             return false;
         }
@@ -1235,7 +1307,8 @@ int tcm_tune(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
         }
     }
     // Stage 1: every tile config in both modes with the planner's other
-    // parameters, two sweeps, each candidate keeping its better time.
+    // parameters, and the split-k GEMV where it can serve the call; two
+    // sweeps, each candidate keeping its better time.
     struct Timed {
         Cand c;
         double us;
@@ -1249,6 +1322,12 @@ int tcm_tune(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
             x.mode = mode;
             stage1.push_back({x, 1e300, 0});
         }
+    if (gemv_eligible(p)) {
+        Cand x;
+        x.config = kGemvCand;
+        x.mode = 1;
+        stage1.push_back({x, 1e300, 0});
+    }
     std::vector<char> valid(stage1.size(), 1);
     for (int sweep = 0; sweep < 2 && st == TCM_OK; ++sweep)
         for (size_t i = 0; i < stage1.size() && st == TCM_OK; ++i) {
@@ -1271,6 +1350,7 @@ int tcm_tune(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
     const int cus = current_cus();
     for (size_t r = 0; r < ranked.size() && r < 3; ++r) {
         const Cand b = ranked[r].c;
+        if (b.config == kGemvCand) continue;  // nothing of the tile schedule applies
         const int64_t T = ranked[r].tiles;
         for (int gm : {1, 2, 8}) {
             Cand x = b;

@@ -2,10 +2,11 @@
 
     python -m tensor_core_mixed_amd.tune                 # tune the shape set, write tuned/mi355x.txt
     python -m tensor_core_mixed_amd.tune --heldout R.md  # check held-out shapes against the table
+    python -m tensor_core_mixed_amd.tune --only gemv     # re-tune the shapes the split-k GEMV can serve
 
 Tuning: for every shape of TUNE_SHAPES, tcm_tune searches the tile configs in
-both modes, then the group rows, Stream-K grid and fix-up around the three
-fastest, and records the winner for the shape's class (element type,
+both modes (and the split-k GEMV where it can serve the shape), then the
+group rows, Stream-K grid and fix-up around the three fastest tile plans, and records the winner for the shape's class (element type,
 layouts, output type, epilogue, alignment, and the half octaves of M, N, K;
 see include/tcm.h).  The table text is written to tuned/mi355x.txt beside
 this package's build directory, where libtcm.so finds it.
@@ -173,11 +174,18 @@ def _label(shape):
     return out
 
 
-def tune(shapes, iters, out):
+def gemv_shape(shape):
+    """Shapes the split-k GEMV can serve (f16 / bf16, row-major B, at most 16 rows)."""
+    dt, M, N, K, b_col, epi, c_type = shape
+    return dt in (F16, BF16) and not b_col and M <= 16 and N % 4 == 0 and K % 8 == 0
+
+
+def tune(shapes, iters, out, merge=False):
     import torch
     import tensor_core_mixed_amd as T
     T.tcm_plan(64, 64, 64, 64, 64, 64, F16)  # the first plan loads the shipped table ...
-    T.tcm_tune_clear()                        # ... which is dropped: tune from the cost model
+    if not merge:
+        T.tcm_tune_clear()                    # ... which is dropped: tune from the cost model
     s = torch.cuda.current_stream().cuda_stream
     for shape in shapes:
         A, B, C, bias = _tensors(*shape)
@@ -191,8 +199,9 @@ def tune(shapes, iters, out):
     os.makedirs(os.path.dirname(out), exist_ok=True)
     props = torch.cuda.get_device_properties(0)
     with open(out, "w") as f:
+        what = (f"{len(TUNE_SHAPES)} shapes ({len(shapes)} re-tuned with `--only gemv`)" if merge else f"{len(shapes)} shapes")
         f.write(f"# tuning table of libtcm for {props.name} ({props.multi_processor_count} CUs), "
-                f"written by tensor_core_mixed_amd/tune.py from {len(shapes)} shapes, {iters} timed calls per candidate\n")
+                f"written by tensor_core_mixed_amd/tune.py from {what}, {iters} timed calls per candidate\n")
         f.write("# tcm-tune-2 dtype a_col b_col c_type epilogue aligned batched mclass nclass kclass "
                 "config mode grid_kind grid_param fixup group_m us M N K\n")
         f.write(text)
@@ -297,6 +306,8 @@ def main():
     ap.add_argument("--out", default=TABLE)
     ap.add_argument("--iters", type=int, default=20)
     ap.add_argument("--heldout", default=None, help="write the held-out report here instead of tuning")
+    ap.add_argument("--only", choices=["gemv"], default=None,
+                    help="re-tune only the shapes the split-k GEMV can serve, keeping the shipped entries of the others")
     a = ap.parse_args()
     sys.path.insert(0, os.path.dirname(HERE))
     import torch
@@ -307,6 +318,8 @@ def main():
                   HELDOUT2_SHAPES),
                  ("Held-out set 3 (drawn after set 2 shaped the wave-regime rule)", HELDOUT3_SHAPES)],
                 a.iters, a.heldout)
+    elif a.only == "gemv":
+        tune([x for x in TUNE_SHAPES if gemv_shape(x)], a.iters, a.out, merge=True)
     else:
         tune(TUNE_SHAPES, a.iters, a.out)
 

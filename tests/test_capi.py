@@ -142,8 +142,16 @@ def test_planner_headline_shape_is_data_parallel_big_tiles():
     assert p["tiles"] == 1024 and p["iters_per_tile"] == 128 and p["grid"] == 1024
 
 
+@pytest.fixture
+def tiles_only():
+    """The tiled kernel for every call (no split-k GEMV)."""
+    T.tcm_set_option("gemv", 1)
+    yield
+    T.tcm_set_option("gemv", 0)
+
+
 @pytest.mark.parametrize("M", [1, 16, 64])
-def test_planner_skinny_uses_streamk(M):
+def test_planner_skinny_uses_streamk(M, tiles_only):
     p = T.tcm_plan(M, 4096, 4096, 4096, 4096, 4096, T.TCM_F16_F32)
     assert p["kernel"] == 1 and p["mode"] == 2
     assert p["sk_tiles"] > 0 and p["workspace_bytes"] > 0
@@ -153,7 +161,7 @@ def test_planner_skinny_uses_streamk(M):
 
 @pytest.mark.parametrize("M,N,K,fixup", [(1, 4096, 4096, 1), (16, 4096, 4096, 1), (64, 4096, 4096, None),
                                          (256, 4096, 4096, None), (1536, 1536, 16384, 0)])
-def test_planner_fixup_kernel_for_many_segments(M, N, K, fixup):
+def test_planner_fixup_kernel_for_many_segments(M, N, K, fixup, tiles_only):
     """Split tiles with five or more segments are summed by a second kernel;
     with fewer, by their last arrival.  The option overrides either way."""
     p = T.tcm_plan(M, N, K, K, N, N, T.TCM_F16_F32)
@@ -588,3 +596,77 @@ def test_data_parallel_entries_carry_over_to_fewer_waves_only():
         assert q["config"] != 4 or q["mode"] != 1
     finally:
         T.tcm_tune_clear()
+
+
+# ------------------------------------------------------------ split-k GEMV
+
+@pytest.mark.parametrize("tuned", [0, 1])
+@pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8])
+def test_planner_gemv_for_few_rows(M, tuned):
+    """Row-major f16 products of at most 8 rows run on the split-k GEMV, with
+    or without the shipped table (whose entries for those classes name it):
+    256 columns a workgroup, k ranges of a multiple of 64 rows covering K,
+    their partial sums (ranges x M x N floats) added by a second kernel."""
+    T.tcm_set_option("tuned", tuned)
+    try:
+        p = T.tcm_plan(M, 4096, 4096, 4096, 4096, 4096, T.TCM_F16_F32)
+    finally:
+        T.tcm_set_option("tuned", 1)
+    assert p["kernel"] == 2 and p["config"] == -1
+    assert p["bn"] == 256 and p["bk"] % 64 == 0 and p["bk"] * p["iters_per_tile"] >= 4096
+    assert p["grid"] == 16 * p["iters_per_tile"]
+    assert p["workspace_bytes"] == p["iters_per_tile"] * M * 4096 * 4 and p["fixup_kernel"] == 1
+    assert p["bm"] == {1: 1, 2: 2, 3: 4, 4: 4, 5: 8, 8: 8}[M]
+
+
+def test_planner_gemv_not_taken_when_ineligible():
+    """More than 16 rows, column-major B, N not a multiple of 4, a padded A
+    row off 16 bytes, int8 or f32, a forced tile config or mode: tiles."""
+    code = T.TCM_F16_F32
+    assert T.tcm_plan(8, 4096, 4096, 4096, 4096, 4096, code)["kernel"] == 2
+    assert T.tcm_plan(17, 4096, 4096, 4096, 4096, 4096, code)["kernel"] == 1
+    assert T.tcm_plan(8, 4096, 4096, 4096, 4096, 4096, code | T.TCM_B_COLMAJOR)["kernel"] == 1
+    assert T.tcm_plan(8, 4094, 4096, 4096, 4094, 4094, code)["kernel"] != 2
+    assert T.tcm_plan(8, 4096, 4096, 4100, 4096, 4096, code)["kernel"] != 2
+    assert T.tcm_plan(8, 4096, 4096, 4096, 4096, 4096, T.TCM_F32_F32)["kernel"] != 2
+    assert T.tcm_plan(8, 4096, 4096, 4096, 4096, 4096, T.TCM_I8_I32)["kernel"] != 2
+    assert T.tcm_plan(8, 4096, 4096, 4096, 4096, 4096, code, aligned=False)["kernel"] != 2
+    for key, val in (("force_config", 4), ("force_mode", 2), ("gemv", 1)):
+        T.tcm_set_option(key, val)
+        try:
+            assert T.tcm_plan(8, 4096, 4096, 4096, 4096, 4096, code)["kernel"] == 1
+        finally:
+            T.tcm_set_option(key, -1 if key == "force_config" else 0)
+
+
+def test_planner_gemv_forced_up_to_16_rows():
+    """Option gemv = 2 takes the GEMV for any eligible call (16 rows at most);
+    the planner alone stops at 8 rows."""
+    code = T.TCM_F16_F32
+    T.tcm_set_option("tuned", 0)
+    try:
+        assert T.tcm_plan(16, 4096, 4096, 4096, 4096, 4096, code)["kernel"] == 1
+        T.tcm_set_option("gemv", 2)
+        assert T.tcm_plan(16, 4096, 4096, 4096, 4096, 4096, code)["kernel"] == 2
+        assert T.tcm_plan(17, 4096, 4096, 4096, 4096, 4096, code)["kernel"] == 1
+    finally:
+        T.tcm_set_option("gemv", 0)
+        T.tcm_set_option("tuned", 1)
+
+
+@pytest.mark.parametrize("K,splits", [(64, 1), (100, 1), (4096, 5), (70000, 0)])
+def test_planner_gemv_k_ranges(K, splits):
+    """The k ranges: multiples of 64 rows, at most 1024 each, together
+    covering K; an asked-for count is rounded to that grid."""
+    T.tcm_set_option("gemv_splits", splits)
+    try:
+        p = T.tcm_plan(2, 1024, K, -(-K // 8) * 8, 1024, 1024, T.TCM_BF16_F32)
+    finally:
+        T.tcm_set_option("gemv_splits", 0)
+    kw, ranges = p["bk"], p["iters_per_tile"]
+    assert p["kernel"] == 2 and kw % 64 == 0 and kw <= 1024
+    assert kw * ranges >= K and kw * (ranges - 1) < K
+    if splits:
+        assert kw == min(1024, -(-(-(-K // splits)) // 64) * 64)
+    assert p["fixup_kernel"] == (ranges > 1)
+    assert p["workspace_bytes"] == (ranges * 2 * 1024 * 4 if ranges > 1 else 0)

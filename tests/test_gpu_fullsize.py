@@ -88,6 +88,10 @@ def test_host_plan_query_matches_launch(name):
     else:
         _, plan = run_tcm(p, g)
     f = dict(kv.split("=", 1) for kv in plan.split() if "=" in kv)
+    if q["kernel"] == 2:  # the split-k GEMV
+        assert f["kernel"] == "gemv" and int(f["grid"]) == q["grid"]
+        assert int(f["splits"]) == q["iters_per_tile"] and int(f["k_per_wg"]) == q["bk"] and int(f["rows"]) == q["bm"]
+        return
     assert f["kernel"] == ("tile" if q["kernel"] == 1 else "generic")
     assert int(f["config"]) == q["config"]
     assert f["mode"] == ("dp" if q["mode"] == 1 else "streamk")

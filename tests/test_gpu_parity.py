@@ -16,7 +16,11 @@ DTYPES = [S.F16, S.BF16, S.F32, S.I8]
 
 @pytest.fixture(autouse=True)
 def _reset_options():
+    # these cases are about the tiled and generic kernels: products of a few
+    # rows stay on the tiles (the split-k GEMV has tests of its own)
+    T.tcm_set_option("gemv", 1)
     yield
+    T.tcm_set_option("gemv", 0)
     T.tcm_set_option("force_mode", 0)
     T.tcm_set_option("force_config", -1)
     T.tcm_set_option("sk_grid", 0)

@@ -23,6 +23,7 @@ def _reset_options():
     T.tcm_set_option("force_config", -1)
     T.tcm_set_option("sk_grid", 0)
     T.tcm_set_option("sk_fixup", 0)
+    T.tcm_set_option("gemv", 0)
 
 
 def _call(fn, p, g):
@@ -78,6 +79,24 @@ def test_noalloc_matches_tcm_gemm_two_calls(dtype, case):
             assert np.array_equal(np.nan_to_num(got, nan=1e30), np.nan_to_num(ref, nan=1e30)), "same plan, different bits"
         else:
             check(p, g, ref)
+
+
+@pytest.mark.parametrize("dtype", [S.F16, S.BF16])
+def test_noalloc_gemv_two_calls(dtype):
+    """The split-k GEMV keeps its partial sums in the same array: two calls
+    in a row, the second smaller, bit-identical to tcm_gemm's."""
+    T.tcm_set_option("gemv", 2)
+    for i, (M, N, K) in enumerate(((8, 4096, 4096), (3, 1028, 1000))):
+        p = S.small_problem(dtype, M, N, K, seed=520 + i, bias=True, relu=(i == 1))
+        say(f"[case] noalloc gemv call {i + 1}: {p.name} dtype={dtype}")
+        g = S.generate(p)
+        st0, ref, plan0 = _call(T.tcm_gemm, p, g)
+        st1, got, plan1 = _call(T.tcm_gemm_noalloc, p, g)
+        assert st0 == T.TCM_OK and st1 == T.TCM_OK
+        say(f"       {plan1}")
+        assert "kernel=gemv" in plan0 and plan1 == plan0 + " scratch=static"
+        check(p, g, got)
+        assert np.array_equal(got, ref), "same plan, different bits"
 
 
 def test_noalloc_forced_streamk_beyond_the_scratch_is_refused():
