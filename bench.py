@@ -51,20 +51,29 @@ def _code_only(text):
     return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
 
 
-def kernel_source_hash():
-    """Hash of the tiled kernels' code (comments and layout excluded): counters
+# the sources of the split-k GEMV (products of a few rows)
+GEMV_SOURCES = ("gemv.h", "gemv_kernel.hip")
+
+
+def kernel_source_hash(sources=KERNEL_SOURCES):
+    """Hash of a kernel family's code (comments and layout excluded): counters
     taken on other code are stale."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "tensor_core_mixed_amd", "csrc")
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(d, f)) as fh:
             h.update(f.encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
 def plan_kernels(plan):
-    """Kernel names a tcm_last_plan() string launches (tiled GEMM / convolution kernels only)."""
+    """Kernel names a tcm_last_plan() string launches (tiled GEMM / convolution and GEMV kernels)."""
     f = dict(kv.split("=", 1) for kv in plan.split() if "=" in kv)
+    if f.get("kernel") == "gemv":
+        names = {f"void tcm::gemv::gemv_split_kernel<{f['dtype']}, {f['rows']}>(tcm::GemvArgs)"}
+        if f.get("fixup") == "kernel":
+            names.add("tcm::gemv::gemv_reduce_kernel(tcm::GemvArgs)")
+        return names
     if f.get("kernel") not in ("tile", "conv"):
         return set()
     b = "true" if f.get("b_col") == "1" else "false"
@@ -444,7 +453,8 @@ def load_traffic(p, plan):
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("source_hash") != kernel_source_hash() or t.get("dominant_kernel") not in plan_kernels(plan):
+    family = GEMV_SOURCES if "kernel=gemv" in plan else KERNEL_SOURCES
+    if t.get("source_hash") != kernel_source_hash(family) or t.get("dominant_kernel") not in plan_kernels(plan):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -598,8 +608,11 @@ def run_all(args):
         C = make_c(p)
         s = torch.cuda.current_stream()
         modes = [0, 1, 2] if name.startswith(("skinny", "sk_")) else [0]
+        if name.startswith("skinny") and p.M <= 16:
+            modes += [3, 4]  # the split-k GEMV forced, and the tiled kernel's own plan
         for mode in modes:
-            T.tcm_set_option("force_mode", mode)
+            T.tcm_set_option("force_mode", mode if mode <= 2 else 0)
+            T.tcm_set_option("gemv", {3: 2, 4: 1}.get(mode, 0))
             call = make_call(p, A, B, bias, C, s.cuda_stream)
             reset_c(p, g, C)
             call()
@@ -614,7 +627,7 @@ def run_all(args):
                 torch.cuda.synchronize()
                 par = _oracle_sampled_check(p, g, C)
             v = p.flops / (ms * 1e-3) / 1e12
-            row = {"workload": name, "mode": ["auto", "dp", "streamk"][mode], "ms": round(ms, 5),
+            row = {"workload": name, "mode": ["auto", "dp", "streamk", "gemv", "tiles"][mode], "ms": round(ms, 5),
                    "per_call_us": pc, "tflops": round(v, 2), "frac_peak": round(v / PEAK[p.dtype], 4),
                    "hbm_frac": round(p.alg_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
                    "parity_ok": par["ok"] if par else None, "plan": plan}
@@ -637,11 +650,16 @@ def run_all(args):
                 row["tuned"] = {"ms": round(tms, 5), "plan": T.tcm_last_plan(), "model_over_tuned": round(ms / tms, 3)}
             rows.append(row)
         T.tcm_set_option("force_mode", 0)
+        T.tcm_set_option("gemv", 0)
         mine = [r for r in rows if r["workload"] == name]
-        if len(mine) == 3:
-            lift = mine[1]["ms"] / mine[2]["ms"]
+        by_mode = {r["mode"]: r for r in mine}
+        if "dp" in by_mode and "streamk" in by_mode:
+            lift = by_mode["dp"]["ms"] / by_mode["streamk"]["ms"]
             for r in mine:
                 r["streamk_lift_dp_over_sk"] = round(lift, 3)
+        if "gemv" in by_mode and "tiles" in by_mode:
+            for r in mine:
+                r["gemv_lift_tiles_over_gemv"] = round(by_mode["tiles"]["ms"] / by_mode["gemv"]["ms"], 3)
         if not args.no_cpu:
             import oracle
             r_cpu = min(p.M, max(1, int(2e10 // (2 * p.N * p.K))))
@@ -711,23 +729,26 @@ def render_report(src, dst):
     """A markdown table from the JSON rows `--all --report` writes."""
     rows = json.load(open(src))
     L = ["# bench.py --all: every workload, timed on one MI355X", "",
-         "Made by `python bench.py --all --tune --no-cpu --report R.json` on the GPU, then "
+         "Made by `python -u bench.py --all --tune --no-cpu --report R.json` on the GPU, then "
          "`python bench.py --render-report R.json profiles/bench_all.md`.  Each case warms up for at least 200 ms; "
          "`block` is the average of back-to-back calls between two events, `per call` the median of calls timed one by "
          "one (it includes the launch gap).  For the split-k workloads every mode is timed: `auto` (the planner, with "
-         "the shipped tuning table), `dp` (data-parallel tiles only) and `streamk`; `lift` = dp / streamk.  `cold` "
+         "the shipped tuning table), `dp` (data-parallel tiles only) and `streamk`; `Stream-K lift` = dp / streamk.  "
+         "Products of at most 16 rows also run `gemv` (the split-k GEMV forced) and `tiles` (the tiled kernel's own plan); "
+         "`GEMV lift` = tiles / gemv.  `cold` "
          "(skinny products): the median call after a 512 MiB write that evicts the MALL.  `tuned`: the same call after "
          "`tcm_tune` searched it (block time).", "",
-         "| workload | mode | block us | per call us | TFLOP/s (TOP/s) | of peak | of HBM | cold us | lift | tuned us | plan |",
-         "|---|---|---|---|---|---|---|---|---|---|---|"]
+         "| workload | mode | block us | per call us | TFLOP/s (TOP/s) | of peak | of HBM | cold us | Stream-K lift | GEMV lift | tuned us | plan |",
+         "|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for r in rows:
         pc = r.get("per_call_us", {}).get("median", "") if isinstance(r.get("per_call_us"), dict) else ""
         tuned = r.get("tuned", {}).get("ms")
         plan = " ".join(kv for kv in r["plan"].split() if kv.split("=")[0] in ("kernel", "config", "tile", "mode", "grid",
-                                                                                  "fixup", "group", "tuned"))
+                                                                                  "fixup", "group", "tuned", "splits"))
         L.append(f"| {r['workload']} | {r['mode']} | {r['ms'] * 1e3:.1f} | {pc} | {r['tflops']:.1f} | "
                  f"{100 * r['frac_peak']:.1f}% | {100 * r['hbm_frac']:.1f}% | {r.get('cold_median_us', '')} | "
-                 f"{r.get('streamk_lift_dp_over_sk', '')} | {'' if tuned is None else f'{tuned * 1e3:.1f}'} | `{plan}` |")
+                 f"{r.get('streamk_lift_dp_over_sk', '')} | {r.get('gemv_lift_tiles_over_gemv', '')} | "
+                 f"{'' if tuned is None else f'{tuned * 1e3:.1f}'} | `{plan}` |")
     with open(dst, "w") as f:
         f.write("\n".join(L) + "\n")
 
@@ -816,6 +837,9 @@ def summarize_counters(d, name, calib=None):
             "tile_group_kernel" if name in S.GROUP_WORKLOADS else "tile_gemm_kernel")
     fetch = per_kernel(d, "fetch", "FETCH_SIZE", kpat)
     write = per_kernel(d, "write", "WRITE_SIZE", kpat)
+    if not fetch:  # a product the split-k GEMV serves
+        fetch = per_kernel(d, "fetch", "FETCH_SIZE", "tcm::gemv::")
+        write = per_kernel(d, "write", "WRITE_SIZE", "tcm::gemv::")
     cf = per_dispatch_in(calib, "copy_fetch", "FETCH_SIZE", "copy")
     cw = per_dispatch_in(calib, "copy_write", "WRITE_SIZE", "copy")
     copy_kib = 512 * 1024
@@ -829,7 +853,8 @@ def summarize_counters(d, name, calib=None):
     if dom:
         kd = kernels[dom]
         hbm = (kd["fetch_kib_per_dispatch"] * f_fac + kd["write_kib_per_dispatch"] * w_fac) * 1024
-    out = {"workload": name, "source_hash": kernel_source_hash(), "dominant_kernel": dom, "kernels": kernels,
+    family = GEMV_SOURCES if dom and "tcm::gemv::" in dom else KERNEL_SOURCES
+    out = {"workload": name, "source_hash": kernel_source_hash(family), "dominant_kernel": dom, "kernels": kernels,
            "copy_fetch_kib": max(cf) if cf else None, "copy_write_kib": max(cw) if cw else None,
            "fetch_scale": f_fac, "write_scale": w_fac, "hbm_bytes_per_launch": hbm}
     path = TRAFFIC_FILE.format(name=name)

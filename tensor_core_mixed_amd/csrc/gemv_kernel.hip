@@ -34,6 +34,7 @@
 
 #include <cstdint>
 
+#include "gemv.h"
 #include "tcm_internal.h"
 
 namespace tcm {
@@ -103,6 +104,10 @@ template <int DT, int MB>
 struct Gemv {
     static constexpr int D = 2;  // register sets of B chunks (four measured no faster)
     static constexpr int KW_MAX = 1024;  // k per workgroup the LDS copy of A holds (host keeps kw <= this)
+    // A rows in LDS are kw + 8 elements apart: the four rows one 4x4x4 step
+    // reads (lanes 4b+i read row i) then fall on different banks (kw alone
+    // is a multiple of 128 bytes: a 4-way bank conflict)
+    static constexpr int kRowPad = 8;
 
     // chunk of 16 rows of B for one lane: 4 columns (8 bytes) per row
     struct Rows {
@@ -138,7 +143,7 @@ struct Gemv {
             bc[3] = u2_t{__builtin_amdgcn_perm(r1[1], r0[1], 0x07060302u), __builtin_amdgcn_perm(r3[1], r2[1], 0x07060302u)};
 #pragma unroll
             for (int g = 0; g < MG; ++g) {
-                const u2_t a = *(const u2_t*)(sAh + (4 * g + (lane & 3)) * kw + kc + 4 * q);
+                const u2_t a = *(const u2_t*)(sAh + (4 * g + (lane & 3)) * (kw + kRowPad) + kc + 4 * q);
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     if constexpr (DT == F16)
@@ -154,7 +159,7 @@ struct Gemv {
 
     // LDS: the A block (at least 4 rows) while the waves multiply, then their four sums
     static constexpr int MBA = MB < 4 ? 4 : MB;
-    static constexpr int A_BYTES = MBA * KW_MAX * 2, RED_BYTES = 4 * MB * kGemvCols * 4;
+    static constexpr int A_BYTES = MBA * (KW_MAX + kRowPad) * 2, RED_BYTES = 4 * MB * kGemvCols * 4;
     static constexpr int LDS_BYTES = A_BYTES > RED_BYTES ? A_BYTES : RED_BYTES;
 
     __device__ static void run(const GemvArgs& g) {
@@ -175,7 +180,7 @@ struct Gemv {
             (char*)g.B + (int64_t)n0 * 2, (short)0, rb_bytes < (int64_t)kOOB ? (int)rb_bytes : (int)kOOB, kRsrcWord3);
         const unsigned lane_off = n0 + 4 * lane < g.N ? (unsigned)(8 * lane) : kOOB;
 
-        // A block [MB][kw] into LDS (rows past M and columns past K as zeros):
+        // A block [MB][kw] into LDS, rows kw + kRowPad apart (rows past M and columns past K as zeros):
         // its loads are issued before the first chunk of B, so waiting for
         // them leaves B's in flight
         const unsigned short* A = (const unsigned short*)g.A;
@@ -195,7 +200,7 @@ struct Gemv {
                     for (int j = 0; j < 4; ++j) v[j] = (unsigned)e[2 * j] | ((unsigned)e[2 * j + 1] << 16);
                 }
             }
-            *(u4_t*)(sA + (m * kw + 8 * (i - m * per_row)) / 2) = v;
+            *(u4_t*)(sA + (m * (kw + kRowPad) + 8 * (i - m * per_row)) / 2) = v;
         }
 
         // a ring of D register sets: the loads of chunks c+1 .. c+D-1 are in

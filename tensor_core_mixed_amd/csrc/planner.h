@@ -4,6 +4,7 @@
 #pragma once
 #include <cstdint>
 
+#include "gemv.h"
 #include "tcm_internal.h"
 
 namespace tcm {

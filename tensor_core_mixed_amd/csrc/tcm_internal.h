@@ -200,35 +200,6 @@ struct GroupArgs {
     GroupEntry e[kMaxGroup];
 };
 
-// Arguments of the split-k GEMV kernel (products of at most 16 rows, f16 /
-// bf16, row-major A and B).  Workgroup (x, y) computes the columns
-// [256 x, 256 x + 256) of every row over the k range [kw y, kw y + kw) and,
-// with splits > 1, stores that partial sum to partial[y][m][n]; a second
-// kernel adds the splits in order and runs the epilogue.  With splits == 1
-// the first kernel runs the epilogue itself.
-constexpr int kGemvMaxRows = 16;
-constexpr int kGemvCols = 256;   // columns per workgroup: 64 lanes x 4
-constexpr int kGemvKAlign = 64;  // kw is a multiple of this (4 waves x 16-row chunks)
-struct GemvArgs {
-    const void* A;
-    const void* B;
-    void* C;
-    const void* bias;
-    int M, N, K;
-    int lda, ldb, ldc;
-    int relu;
-    int has_bias;
-    int accum;
-    int c_type;
-    int splits;          // k ranges (gridDim.y)
-    int kw;              // k per range, a multiple of kGemvKAlign
-    float* partial;      // splits x M x N partial sums (splits > 1)
-    int64_t b_bytes;     // extent of B in bytes (its buffer range)
-};
-// rows bucket (1, 2, 4, 8 or 16) of an M <= 16
-inline int gemv_rows_bucket(int64_t M) { return M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : M <= 8 ? 8 : 16; }
-int launch_gemv(int dtype, const GemvArgs& a, void* stream);
-
 // Launchers (defined next to the kernels).  Return hipError_t as int.
 using TileLauncher = int (*)(const TileArgs&, void* stream);
 using GroupLauncher = int (*)(const GroupArgs&, void* stream);

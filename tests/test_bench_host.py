@@ -38,6 +38,20 @@ def test_plan_kernels_names_the_launched_kernels():
     group = HYBRID_PLAN + " group=8"
     assert bench.plan_kernels(group) == {"void tcm::tile_group_kernel<0, 1, false, false>(tcm::GroupArgs)",
                                          "void tcm::tile_group_kernel<0, 1, false, true>(tcm::GroupArgs)"}
+    gemv = "kernel=gemv rows=8 cols_per_wg=256 k_per_wg=128 splits=32 grid=512 M=5 N=4096 K=4096 dtype=1 fixup=kernel"
+    assert bench.plan_kernels(gemv) == {"void tcm::gemv::gemv_split_kernel<1, 8>(tcm::GemvArgs)",
+                                        "tcm::gemv::gemv_reduce_kernel(tcm::GemvArgs)"}
+    assert bench.plan_kernels(gemv.replace(" fixup=kernel", "").replace("splits=32", "splits=1")) == \
+        {"void tcm::gemv::gemv_split_kernel<1, 8>(tcm::GemvArgs)"}
+
+
+def test_gemv_counters_are_keyed_to_the_gemv_sources():
+    """The split-k GEMV's stored counters follow its own sources, the tiled
+    workloads' counters the tiled kernels' sources."""
+    assert bench.kernel_source_hash(bench.GEMV_SOURCES) != bench.kernel_source_hash()
+    t = json.load(open(os.path.join(ROOT, "profiles", "traffic_skinny_m1.json")))
+    if "gemv" in (t.get("dominant_kernel") or ""):
+        assert t["source_hash"] == bench.kernel_source_hash(bench.GEMV_SOURCES)
 
 
 def _with_traffic(tmp_path, monkeypatch, record):
