@@ -408,7 +408,7 @@ int tcm_tile_order(int32_t t, int32_t tiles_m, int32_t tiles_n, int32_t* tm, int
  * epilogue flags, whether every pointer is 16-byte aligned, whether the call
  * is a batch, and the half octave of each of M, N and K (floor(2*log2(x)):
  * e.g. every M in [4096, 5792] shares class 24).  An entry gives the tile
- * config and mode (or the split-k GEMV, config 7 in the text), the split-k grid policy (the planner's; g/8 workgroups
+ * config and mode (or the split-k GEMV, config 100 in the text), the split-k grid policy (the planner's; g/8 workgroups
  * per CU; or s workgroups per tile, every tile split into s equal shares),
  * the way split tiles are summed (the planner's, last arrival, fix-up
  * kernel) and the tile-order group rows (the planner's, or 1..16).
@@ -454,7 +454,7 @@ int tcm_tune(int64_t M, int64_t N, int64_t K,
  *   "tcm-tune-2 dtype a_col b_col c_type epilogue aligned batched mclass
  *    nclass kclass config mode grid_kind grid_param fixup group_m
  *    microseconds M N K"
- * (c_type 0 = the accumulator type, 1 = f16, 2 = bf16; config 7 = the
+ * (c_type 0 = the accumulator type, 1 = f16, 2 = bf16; config 100 = the
  * split-k GEMV, with mode 1 and zeros after it; grid_kind 0 = the
  * planner's, 1 = grid_param/8 workgroups per CU, 2 = grid_param per tile;
  * fixup and group_m 0 = the planner's; M N K = the shape it was tuned on).

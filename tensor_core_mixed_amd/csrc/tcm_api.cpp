@@ -133,9 +133,10 @@ TuneKey tune_key(const Problem& p) {
     return TuneKey{p.dtype, (int)p.a_col, (int)p.b_col, p.c_type, p.epilogue, (int)p.aligned, p.batch > 1 ? 1 : 0,
                    half_octave(p.M), half_octave(p.N), half_octave(p.K)};
 }
-// The split-k GEMV as a candidate: config kGemvCand, mode 1, no other
-// parameter (its k ranges are the planner's).
-constexpr int kGemvCand = kNumConfigs;
+// The split-k GEMV as a candidate: config kGemvCand (outside the tile
+// table's index range), mode 1, no other parameter (its k ranges are the
+// planner's).
+constexpr int kGemvCand = 100;
 bool valid_cand(const Cand& c) {
     if (c.config == kGemvCand)
         return c.mode == 1 && c.grid_kind == 0 && c.grid_param == 0 && c.fixup == 0 && c.group_m == 0;

@@ -96,7 +96,7 @@ def test_gemv_deterministic(dtype):
 
 def test_gemv_is_a_tuning_candidate():
     """tcm_tune times the GEMV beside the tile plans; the class entry it
-    records (config 7: the GEMV, or a tile plan) is what the next call runs,
+    records (config 100: the GEMV, or a tile plan) is what the next call runs,
     and the result stays correct."""
     from gpu_util import to_device
     import torch
@@ -118,7 +118,7 @@ def test_gemv_is_a_tuning_candidate():
         C2, plan = run_tcm(p, g)
         say(f"       plan: {plan}")
         assert " tuned=" in plan
-        assert ("kernel=gemv" in plan) == (line[11] == "7") == (best["kernel"] == 2)
+        assert ("kernel=gemv" in plan) == (line[11] == "100") == (best["kernel"] == 2)
         check(p, g, C2)
     finally:
         T.tcm_tune_clear()
