@@ -285,8 +285,8 @@ def _write_report(report, results, iters):
         f.write("For each shape (none of them in the tuning set), `auto` is the call's own plan (the shipped table "
                 "`tensor_core_mixed_amd/tuned/mi355x.txt` where it holds the shape's class, else the cost model); "
                 "`best` is the fastest point `tcm_tune` finds "
-                "for the shape (two stages: every tile config in both modes, then group rows, Stream-K grid and fix-up "
-                "around the three fastest).  Both are then re-timed alternately, five blocks of back-to-back calls each, "
+                "for the shape (two stages: every tile config in both modes and, where it can serve the shape, the split-k GEMV "
+                "(config 100); then group rows, Stream-K grid and fix-up around the three fastest tile plans).  Both are then re-timed alternately, five blocks of back-to-back calls each, "
                 "and the medians compared: `ratio` = auto / best (the search's own minimum over many candidates reads "
                 "low, so it is not used).\n\n")
         for title, rows in results:
