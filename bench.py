@@ -70,7 +70,10 @@ def plan_kernels(plan):
     """Kernel names a tcm_last_plan() string launches (tiled GEMM / convolution and GEMV kernels)."""
     f = dict(kv.split("=", 1) for kv in plan.split() if "=" in kv)
     if f.get("kernel") == "gemv":
-        names = {f"void tcm::gemv::gemv_split_kernel<{f['dtype']}, {f['rows']}>(tcm::GemvArgs)"}
+        if f.get("b_col") == "1":
+            names = {f"void tcm::gemv::gemv_t_kernel<{f['dtype']}>(tcm::GemvArgs)"}
+        else:
+            names = {f"void tcm::gemv::gemv_split_kernel<{f['dtype']}, {f['rows']}>(tcm::GemvArgs)"}
         if f.get("fixup") == "kernel":
             names.add("tcm::gemv::gemv_reduce_kernel(tcm::GemvArgs)")
         return names

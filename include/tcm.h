@@ -119,14 +119,17 @@ enum { TCM_EPI_NONE = 0, TCM_EPI_BIAS = 1, TCM_EPI_RELU = 2, TCM_EPI_BIAS_RELU =
  * kernel, which reads and writes single bytes when a pointer is not a
  * multiple of its element size.
  * Products of at most 8 rows (at most 16 with option "gemv" = 2) in f16 or
- * bf16 with row-major A and B run on a split-k GEMV instead of the tiles
- * when N is a multiple of 4, lda a multiple of 8, ldb of 4, every pointer
- * 16-byte aligned and B below 2 GiB: B streams from HBM once, 256 columns
- * per workgroup over an even split of the k range (the Stream-K
- * reproduction post on leiblog.wang), each lane multiplying the 4 x 4 blocks
- * of B it loads on the matrix cores' 4x4x4 blocks; the k ranges' partial
- * sums (ranges x M x N floats of workspace) are added in range order by a
- * second kernel on the stream, which runs the epilogue.
+ * bf16 with row-major A run on a split-k GEMV instead of the tiles when lda
+ * is a multiple of 8, every pointer 16-byte aligned, and A and B lie below
+ * 2 GiB; with row-major B also N a multiple of 4 and ldb of 4, with
+ * column-major B (k contiguous) K and ldb multiples of 8.  B streams from
+ * HBM once over an even split of the k range (the Stream-K reproduction
+ * post on leiblog.wang): row-major B 256 columns per workgroup, each lane
+ * multiplying the 4 x 4 blocks of B it loads on the matrix cores' 4x4x4
+ * blocks; column-major B 128 columns per workgroup in 16x16x32 blocks fed
+ * straight from memory.  The k ranges' partial sums (ranges x M x N floats
+ * of workspace) are added in range order by a second kernel on the stream,
+ * which runs the epilogue.
  * Returns TCM_OK once the work is enqueued; TCM_ERR_INVALID_VALUE for
  * negative sizes, too-small leading dimensions, a NULL operand with a
  * non-empty extent, unknown dtype/flags/epilogue, both output type flags or
@@ -318,10 +321,12 @@ const char* tcm_status_string(int status);
  *                  it can serve with at most 8 rows, or the tuning table's
  *                  choice), 1 = never, 2 = every call it can serve (at most
  *                  16 rows) unless a tile config or mode is forced.
- *   "gemv_splits"  0 = planner decides (about two workgroups per CU, the
- *                  partial sums kept within an eighth of B's bytes), else
- *                  the number of k ranges, rounded to ranges of a multiple
- *                  of 64 rows, at most 1024 each (1..4096).
+ *   "gemv_splits"  0 = planner decides (row-major B: about two workgroups
+ *                  per CU, the partial sums kept within an eighth of B's
+ *                  bytes; column-major B: ranges of 256 rows), else the
+ *                  number of k ranges, rounded to ranges of a multiple of
+ *                  64 rows, at most 1024 each (row-major B), or of a
+ *                  multiple of 256 rows (column-major B) (1..4096).
  * Unknown keys or out-of-range values: TCM_ERR_INVALID_VALUE.
  * tcm_get_option returns the value, or -2 for an unknown key.
  */
@@ -332,10 +337,11 @@ int64_t tcm_get_option(const char* key);
 typedef struct {
     int32_t kernel;        /* 0 = generic kernel, 1 = tiled MFMA kernel, 2 = split-k GEMV */
     int32_t config;        /* tile-table index (tiled kernel) or -1 */
-    int32_t bm, bn, bk;    /* macro tile; bk in elements.  GEMV: the rows it is
-                              compiled for (1, 2, 4, 8, 16), 256 columns per
-                              workgroup, k rows per range; iters_per_tile = the
-                              k ranges, tiles = the 256-column blocks */
+    int32_t bm, bn, bk;    /* macro tile; bk in elements.  GEMV: the rows it
+                              computes (1, 2, 4, 8, 16), the columns per
+                              workgroup (256, or 128 with column-major B), k rows
+                              per range; iters_per_tile = the k ranges, tiles =
+                              the column blocks */
     int32_t mode;          /* 1 = data-parallel, 2 = Stream-K (+ data-parallel tiles) */
     int32_t grid;          /* workgroups launched */
     int64_t tiles;         /* ceil(M/bm) * ceil(N/bn) */

@@ -1,5 +1,6 @@
-// Split-k GEMV kernel for products of at most 16 rows: C = epi(A B + bias)
-// with A (M x K, M <= 16) and B (K x N) both row-major, f16 or bf16.
+// Split-k GEMV kernels for products of at most 16 rows: C = epi(A B + bias)
+// with A (M x K, M <= 16) row-major and B (K x N) row-major or, in the
+// second kernel below, column-major; f16 or bf16.
 //
 // Such a product is bound by streaming B once from HBM: it moves K*N
 // operand elements for 2*M*K*N flops, far below the MFMA ridge.  The tiled
@@ -42,8 +43,11 @@ namespace gemv {
 
 typedef unsigned u2_t __attribute__((ext_vector_type(2)));
 typedef unsigned u4_t __attribute__((ext_vector_type(4)));
+typedef int i4_t __attribute__((ext_vector_type(4)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
 typedef short s4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;                 // four waves
@@ -272,10 +276,100 @@ __global__ __launch_bounds__(kThreads) void gemv_reduce_kernel(GemvArgs g) {
     finish(g, m, n, sum_splits(g, partial_rsrc(g), (unsigned)(i * 4), mn));
 }
 
+// ------------------------------------------------------ column-major B
+// B stored column-major (k contiguous: a weight matrix kept as [N][K]).
+// Here the memory layout is the matrix cores' operand layout: for
+// v_mfma_f32_16x16x32, lane l (j = l & 15, g = l >> 4) gives 8 consecutive
+// k (16 bytes) from k = 8g of row j of A and of column j of B.  So each lane
+// loads 16 bytes of column n + j of B and 16 bytes of row j of A (rows past
+// M read as zeros) and one instruction covers 16 rows x 16 columns x 32 k:
+// no LDS, no transpose.  A wave owns 32 columns (two groups of 16) of the
+// workgroup's 128 over the whole k range, with the loads of kGemvTSteps
+// 32-k steps (three 16-byte loads each) in flight at once; waves share
+// nothing.  Each load instruction reads 64 contiguous bytes of 16 columns;
+// the next step reads the rest of those 128-byte lines.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void gemv_t_kernel(GemvArgs g) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 15, grp = lane >> 4;
+    const int n_wave = blockIdx.x * kGemvTCols + wave * 32;
+    const int k0 = blockIdx.y * g.kw;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)g.A, (short)0, g.a_bytes < (int64_t)kOOB ? (int)g.a_bytes : (int)kOOB, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)g.B, (short)0, g.b_bytes < (int64_t)kOOB ? (int)g.b_bytes : (int)kOOB, kRsrcWord3);
+    const unsigned a_row = j < g.M ? (unsigned)(j * g.lda) * 2u : kOOB;  // bytes to row j of A
+    unsigned b_colp[2];                                                   // bytes to this lane's columns of B
+#pragma unroll
+    for (int cg = 0; cg < 2; ++cg) {
+        const int n = n_wave + 16 * cg + j;
+        b_colp[cg] = n < g.N ? (unsigned)((int64_t)n * g.ldb * 2) : kOOB;
+    }
+    f4_t acc[2] = {f4_t{0.f, 0.f, 0.f, 0.f}, f4_t{0.f, 0.f, 0.f, 0.f}};
+    const int steps = g.kw / 32;
+    for (int s0 = 0; s0 < steps; s0 += kGemvTSteps) {
+        u4_t av[kGemvTSteps], bv[kGemvTSteps][2];
+#pragma unroll
+        for (int i = 0; i < kGemvTSteps; ++i) {
+            const int k = k0 + 32 * (s0 + i) + 8 * grp;  // K is a multiple of 8: a piece lies wholly below K or not
+            const bool in = k < g.K;
+            av[i] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 ra, in && a_row != kOOB ? a_row + 2u * (unsigned)k : kOOB, 0, 0));
+#pragma unroll
+            for (int cg = 0; cg < 2; ++cg)
+                bv[i][cg] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                         rb, in && b_colp[cg] != kOOB ? b_colp[cg] + 2u * (unsigned)k : kOOB, 0, 0));
+        }
+        __builtin_amdgcn_sched_barrier(0);  // every load of the group issued before the first multiply waits
+#pragma unroll
+        for (int i = 0; i < kGemvTSteps; ++i)
+#pragma unroll
+            for (int cg = 0; cg < 2; ++cg) {
+                if constexpr (DT == F16)
+                    acc[cg] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, av[i]),
+                                                                     __builtin_bit_cast(h8_t, bv[i][cg]), acc[cg], 0, 0, 0);
+                else
+                    acc[cg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8_t, av[i]),
+                                                                      __builtin_bit_cast(b8_t, bv[i][cg]), acc[cg], 0, 0, 0);
+            }
+    }
+    // lane l holds rows 4g .. 4g+3 of columns n_wave + 16 cg + j
+    const int64_t mn = (int64_t)g.M * g.N;
+    const __amdgpu_buffer_rsrc_t rp = partial_rsrc(g);
+#pragma unroll
+    for (int cg = 0; cg < 2; ++cg) {
+        const int n = n_wave + 16 * cg + j;
+        if (n >= g.N) continue;
+        // the whole vector is cast, then indexed: hipcc miscompiles the bit
+        // cast of one element of a vector (it yields element 0)
+        const i4_t bits = __builtin_bit_cast(i4_t, acc[cg]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int m = 4 * grp + t;
+            if (m >= g.M) break;
+            if (g.splits > 1)
+                __builtin_amdgcn_raw_buffer_store_b32(bits[t], rp, (unsigned)((blockIdx.y * mn + (int64_t)m * g.N + n) * 4),
+                                                      0, 0);
+            else
+                finish(g, m, n, acc[cg][t]);
+        }
+    }
+}
+
 template <int DT>
 int launch_dt(const GemvArgs& a, void* stream) {
-    const dim3 grid((unsigned)((a.N + kGemvCols - 1) / kGemvCols), (unsigned)a.splits);
     hipStream_t s = (hipStream_t)stream;
+    if (a.b_col) {
+        const dim3 grid_t((unsigned)((a.N + kGemvTCols - 1) / kGemvTCols), (unsigned)a.splits);
+        hipLaunchKernelGGL((gemv_t_kernel<DT>), grid_t, dim3(kThreads), 0, s, a);
+        int st = (int)hipGetLastError();
+        if (st != 0 || a.splits <= 1) return st;
+        const int64_t mn = (int64_t)a.M * a.N;
+        hipLaunchKernelGGL(gemv_reduce_kernel, dim3((unsigned)((mn + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, a);
+        return (int)hipGetLastError();
+    }
+    const dim3 grid((unsigned)((a.N + kGemvCols - 1) / kGemvCols), (unsigned)a.splits);
     switch (gemv_rows_bucket(a.M)) {
     case 1: hipLaunchKernelGGL((gemv_split_kernel<DT, 1>), grid, dim3(kThreads), 0, s, a); break;
     case 2: hipLaunchKernelGGL((gemv_split_kernel<DT, 2>), grid, dim3(kThreads), 0, s, a); break;
@@ -293,9 +387,12 @@ int launch_dt(const GemvArgs& a, void* stream) {
 }  // namespace gemv
 
 int launch_gemv(int dtype, const GemvArgs& a, void* stream) {
-    if (a.M < 1 || a.M > kGemvMaxRows || a.N < 1 || a.N % 4 || a.splits < 1 || a.kw < kGemvKAlign ||
-        a.kw % kGemvKAlign || a.kw > gemv::Gemv<F16, 1>::KW_MAX || (int64_t)a.splits * a.kw < a.K ||
+    if (a.M < 1 || a.M > kGemvMaxRows || a.N < 1 || a.splits < 1 || (int64_t)a.splits * a.kw < a.K ||
         (a.splits > 1 && !a.partial) || (int64_t)a.splits * a.M * a.N * 4 >= (int64_t)gemv::kOOB)
+        return (int)hipErrorInvalidValue;
+    if (a.b_col ? (a.kw < kGemvTKAlign || a.kw % kGemvTKAlign || a.K % 8 || a.a_bytes >= (int64_t)gemv::kOOB ||
+                   a.b_bytes >= (int64_t)gemv::kOOB)
+                : (a.N % 4 || a.kw < kGemvKAlign || a.kw % kGemvKAlign || a.kw > gemv::Gemv<F16, 1>::KW_MAX))
         return (int)hipErrorInvalidValue;
     if (dtype == F16) return gemv::launch_dt<F16>(a, stream);
     if (dtype == BF16) return gemv::launch_dt<BF16>(a, stream);

@@ -269,11 +269,14 @@ Estimate estimate(const Problem& p, int ci, int cus, int force_mode, int sk_grid
 }  // namespace
 
 bool gemv_eligible(const Problem& p) {
-    return (p.dtype == F16 || p.dtype == BF16) && !p.a_col && !p.b_col && !p.conv && !p.group && p.batch <= 1 &&
-           p.M >= 1 && p.M <= kGemvMaxRows && p.N >= 4 && p.N % 4 == 0 && p.K >= 1 && p.K <= (1LL << 22) &&
-           p.lda % 8 == 0 &&
-           p.ldb % 4 == 0 && p.aligned && p.ldc < (1LL << 31) && p.lda < (1LL << 31) &&
-           (p.K - 1) * p.ldb * 2 + p.N * 2 < (1LL << 31);
+    const bool common = (p.dtype == F16 || p.dtype == BF16) && !p.a_col && !p.conv && !p.group && p.batch <= 1 &&
+                        p.M >= 1 && p.M <= kGemvMaxRows && p.K >= 1 && p.K <= (1LL << 22) && p.lda % 8 == 0 &&
+                        p.aligned && p.ldc < (1LL << 31) && p.lda < (1LL << 31);
+    if (!common) return false;
+    if (p.b_col)  // 16-byte pieces of k along every row of A and column of B; both below 2 GiB
+        return p.K % 8 == 0 && p.ldb % 8 == 0 && p.N >= 1 && ((p.M - 1) * p.lda + p.K) * 2 < (1LL << 31) &&
+               ((p.N - 1) * p.ldb + p.K) * 2 < (1LL << 31);
+    return p.N >= 4 && p.N % 4 == 0 && p.ldb % 4 == 0 && (p.K - 1) * p.ldb * 2 + p.N * 2 < (1LL << 31);
 }
 
 // Up to 8 rows the GEMV beats the tiled kernel's Stream-K plans on N = K =
@@ -293,6 +296,28 @@ namespace {
 // kept within an eighth of B's bytes, and at most kGemvKMax rows a range.
 constexpr int64_t kGemvKMax = 1024;
 void gemv_plan(const Problem& p, const Options& o, int cus, Plan* pl) {
+    pl->kernel = 3;
+    pl->config = -1;
+    pl->mode = 1;
+    if (p.b_col) {
+        // column-major B: every wave keeps its whole k range in flight, so a
+        // range is one group of kGemvTSteps 32-k steps (256 rows) unless
+        // more are asked for; many workgroups hide each other's latency
+        const int64_t nb = cdiv(p.N, kGemvTCols);
+        int64_t kw = kGemvTKAlign;
+        if (o.gemv_splits > 0) kw = std::max<int64_t>(1, cdiv(cdiv(p.K, o.gemv_splits), kGemvTKAlign)) * kGemvTKAlign;
+        const int64_t splits = cdiv(p.K, kw);
+        pl->bm = 16;
+        pl->bn = kGemvTCols;
+        pl->bk = (int)kw;
+        pl->iters = splits;
+        pl->tiles = nb;
+        pl->grid = (int)(nb * splits);
+        pl->dp_tiles = nb;
+        pl->ws_partial_bytes = splits > 1 ? splits * p.M * p.N * 4 : 0;
+        pl->fixup_kernel = splits > 1;
+        return;
+    }
     const int64_t nb = cdiv(p.N, kGemvCols);
     int64_t splits = o.gemv_splits;
     if (splits <= 0) {
@@ -303,12 +328,9 @@ void gemv_plan(const Problem& p, const Options& o, int cus, Plan* pl) {
     int64_t kw = cdiv(cdiv(p.K, splits), kGemvKAlign) * kGemvKAlign;
     if (kw > kGemvKMax) kw = kGemvKMax;
     splits = cdiv(p.K, kw);
-    pl->kernel = 3;
-    pl->config = -1;
     pl->bm = gemv_rows_bucket(p.M);
     pl->bn = kGemvCols;
     pl->bk = (int)kw;
-    pl->mode = 1;
     pl->iters = splits;
     pl->tiles = nb;
     pl->grid = (int)(nb * splits);

@@ -429,9 +429,9 @@ std::string describe(const Plan& pl, const Problem& p) {
         snprintf(buf, sizeof buf, "empty problem M=%lld N=%lld", (long long)p.M, (long long)p.N);
     } else if (pl.kernel == 3) {
         snprintf(buf, sizeof buf,
-                 "kernel=gemv rows=%d cols_per_wg=%d k_per_wg=%d splits=%lld grid=%d M=%lld N=%lld K=%lld dtype=%d%s",
+                 "kernel=gemv rows=%d cols_per_wg=%d k_per_wg=%d splits=%lld grid=%d M=%lld N=%lld K=%lld dtype=%d b_col=%d%s",
                  pl.bm, pl.bn, pl.bk, (long long)pl.iters, pl.grid, (long long)p.M, (long long)p.N, (long long)p.K, p.dtype,
-                 pl.fixup_kernel ? " fixup=kernel" : "");
+                 (int)p.b_col, pl.fixup_kernel ? " fixup=kernel" : "");
     } else if (pl.kernel == 1) {
         snprintf(buf, sizeof buf, "kernel=generic tile=64x64 tiles=%lld iters=%lld M=%lld N=%lld K=%lld dtype=%d batch=%lld%s",
                  (long long)pl.tiles, (long long)pl.iters, (long long)p.M, (long long)p.N, (long long)p.K, p.dtype,
@@ -788,6 +788,8 @@ int gemm_impl(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int
         v.splits = (int)pl.iters;
         v.kw = pl.bk;
         v.b_bytes = b_one;
+        v.a_bytes = a_one;
+        v.b_col = p.b_col ? 1 : 0;
         if (pl.ws_partial_bytes > 0) {
             if (noalloc) {
                 char* base = nullptr;

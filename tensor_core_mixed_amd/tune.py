@@ -175,9 +175,9 @@ def _label(shape):
 
 
 def gemv_shape(shape):
-    """Shapes the split-k GEMV can serve (f16 / bf16, row-major B, at most 16 rows)."""
+    """Shapes the split-k GEMV can serve (f16 / bf16, at most 16 rows)."""
     dt, M, N, K, b_col, epi, c_type = shape
-    return dt in (F16, BF16) and not b_col and M <= 16 and N % 4 == 0 and K % 8 == 0
+    return dt in (F16, BF16) and M <= 16 and K % 8 == 0 and (b_col or N % 4 == 0)
 
 
 def tune(shapes, iters, out, merge=False):

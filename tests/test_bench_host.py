@@ -51,7 +51,13 @@ def test_gemv_counters_are_keyed_to_the_gemv_sources():
     assert bench.kernel_source_hash(bench.GEMV_SOURCES) != bench.kernel_source_hash()
     t = json.load(open(os.path.join(ROOT, "profiles", "traffic_skinny_m1.json")))
     if "gemv" in (t.get("dominant_kernel") or ""):
-        assert t["source_hash"] == bench.kernel_source_hash(bench.GEMV_SOURCES)
+        plan = ("kernel=gemv rows=1 cols_per_wg=256 k_per_wg=128 splits=32 grid=512 M=1 N=4096 K=4096 dtype=0 b_col=0 "
+                "fixup=kernel")
+        got = bench.load_traffic(S.workload("skinny_m1"), plan)
+        if t["source_hash"] == bench.kernel_source_hash(bench.GEMV_SOURCES):
+            assert got == t["hbm_bytes_per_launch"]
+        else:  # counters taken on other GEMV code are not reported
+            assert got is None
 
 
 def _with_traffic(tmp_path, monkeypatch, record):

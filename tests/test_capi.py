@@ -620,12 +620,13 @@ def test_planner_gemv_for_few_rows(M, tuned):
 
 
 def test_planner_gemv_not_taken_when_ineligible():
-    """More than 16 rows, column-major B, N not a multiple of 4, a padded A
-    row off 16 bytes, int8 or f32, a forced tile config or mode: tiles."""
+    """More than 16 rows, row-major B with N not a multiple of 4,
+    column-major B with K not a multiple of 8, a padded A row off 16 bytes,
+    int8 or f32, a forced tile config or mode: tiles."""
     code = T.TCM_F16_F32
     assert T.tcm_plan(8, 4096, 4096, 4096, 4096, 4096, code)["kernel"] == 2
     assert T.tcm_plan(17, 4096, 4096, 4096, 4096, 4096, code)["kernel"] == 1
-    assert T.tcm_plan(8, 4096, 4096, 4096, 4096, 4096, code | T.TCM_B_COLMAJOR)["kernel"] == 1
+    assert T.tcm_plan(8, 4096, 4100, 4104, 4104, 4096, code | T.TCM_B_COLMAJOR)["kernel"] != 2
     assert T.tcm_plan(8, 4094, 4096, 4096, 4094, 4094, code)["kernel"] != 2
     assert T.tcm_plan(8, 4096, 4096, 4100, 4096, 4096, code)["kernel"] != 2
     assert T.tcm_plan(8, 4096, 4096, 4096, 4096, 4096, T.TCM_F32_F32)["kernel"] != 2
@@ -670,3 +671,19 @@ def test_planner_gemv_k_ranges(K, splits):
         assert kw == min(1024, -(-(-(-K // splits)) // 64) * 64)
     assert p["fixup_kernel"] == (ranges > 1)
     assert p["workspace_bytes"] == (ranges * 2 * 1024 * 4 if ranges > 1 else 0)
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+def test_planner_gemv_column_major_b(M):
+    """Column-major B (k contiguous): 128 columns a workgroup, k ranges of
+    256 rows, 16 rows computed whatever M is; K must be a multiple of 8."""
+    T.tcm_set_option("tuned", 0)
+    try:
+        p = T.tcm_plan(M, 4096, 4096, 4096, 4096, 4096, T.TCM_F16_F32 | T.TCM_B_COLMAJOR)
+        q = T.tcm_plan(M, 4096, 4100, 4104, 4104, 4096, T.TCM_F16_F32 | T.TCM_B_COLMAJOR)
+    finally:
+        T.tcm_set_option("tuned", 1)
+    assert p["kernel"] == 2 and p["bn"] == 128 and p["bk"] == 256 and p["bm"] == 16
+    assert p["iters_per_tile"] == 16 and p["grid"] == 32 * 16
+    assert p["workspace_bytes"] == 16 * M * 4096 * 4
+    assert q["kernel"] != 2  # K = 4100 is not a multiple of 8

@@ -68,7 +68,7 @@ def test_planner_uses_every_shipped_entry(i):
     lda, ldb = (M if a_col else K), (K if b_col else N)
     q = T.tcm_plan(M, N, K, lda, ldb, N, code, epi, bool(aligned))
     if config == 100:  # the split-k GEMV (the planner picks its own k ranges)
-        assert q["kernel"] == 2 and q["config"] == -1 and M <= 16 and not b_col, (e, q)
+        assert q["kernel"] == 2 and q["config"] == -1 and M <= 16, (e, q)
         return
     assert q["kernel"] == 1 and (q["config"], q["mode"]) == (config, mode), (e, q)
     if e[12] == 2:  # equal shares of every tile
@@ -76,4 +76,5 @@ def test_planner_uses_every_shipped_entry(i):
     T.tcm_set_option("tuned", 0)
     q0 = T.tcm_plan(M, N, K, lda, ldb, N, code, epi, bool(aligned))
     T.tcm_set_option("tuned", 1)
-    assert q0["kernel"] == 1  # the model's plan is a tiled one as well
+    # the model's plan is a tiled one as well, or the GEMV for a few rows
+    assert q0["kernel"] == 1 or (q0["kernel"] == 2 and M <= 8)
