@@ -15,6 +15,7 @@ pytestmark = pytest.mark.gpu
 @pytest.fixture(autouse=True)
 def _reset_options():
     yield
+    T.tcm_set_option("gemv", 0)
     T.tcm_set_option("force_mode", 0)
     T.tcm_set_option("force_config", -1)
     T.tcm_set_option("sk_grid", 0)
@@ -142,3 +143,31 @@ def test_graph_replay_after_the_workspace_grew():
                                  s2.cuda_stream))
     say(f"       growth under capture: {T.tcm_status_string(status[0])}")
     assert status == [T.TCM_ERR_NOT_SUPPORTED]
+
+
+@pytest.mark.parametrize("b_col", [False, True])
+def test_graph_capture_replays_gemv(b_col):
+    """The split-k GEMV (two launches: the k ranges, then their sum) captured
+    into a graph after an eager call made the stream's workspace: every
+    replay gives the eager bits."""
+    T.tcm_set_option("gemv", 2)
+    c = Call(S.small_problem(S.F16, 5, 1024, 2048, seed=405, bias=True, relu=True, b_col=b_col))
+    s = torch.cuda.Stream()
+    c(s)
+    torch.cuda.synchronize()
+    eager = c.C.clone()
+    c.check()
+    say(f"[case] graph capture, gemv b_col={b_col}: {T.tcm_last_plan()}")
+    assert "kernel=gemv" in T.tcm_last_plan() and "fixup=kernel" in T.tcm_last_plan()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        c(s)
+    for i in range(3):
+        c.C.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(torch.nan_to_num(c.C, nan=1e9), torch.nan_to_num(eager, nan=1e9)), f"replay {i} differs"
+        x = torch.randn(1024, device="cuda")
+        (x @ x).item()
+    c.check()
