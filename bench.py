@@ -72,6 +72,8 @@ def plan_kernels(plan):
     if f.get("kernel") == "gemv":
         if f.get("b_col") == "1":
             names = {f"void tcm::gemv::gemv_t_kernel<{f['dtype']}>(tcm::GemvArgs)"}
+        elif f.get("mfma") == "16x16x32":
+            names = {f"void tcm::gemv::gemv_r_kernel<{f['dtype']}, {f['rows']}>(tcm::GemvArgs)"}
         else:
             names = {f"void tcm::gemv::gemv_split_kernel<{f['dtype']}, {f['rows']}>(tcm::GemvArgs)"}
         if f.get("fixup") == "kernel":

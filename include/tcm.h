@@ -118,18 +118,21 @@ enum { TCM_EPI_NONE = 0, TCM_EPI_BIAS = 1, TCM_EPI_RELU = 2, TCM_EPI_BIAS_RELU =
  * layouts take the tiled fast path; anything else runs on the generic
  * kernel, which reads and writes single bytes when a pointer is not a
  * multiple of its element size.
- * Products of at most 8 rows (at most 16 with option "gemv" = 2) in f16 or
- * bf16 with row-major A run on a split-k GEMV instead of the tiles when lda
- * is a multiple of 8, every pointer 16-byte aligned, and A and B lie below
- * 2 GiB; with row-major B also N a multiple of 4 and ldb of 4, with
- * column-major B (k contiguous) K and ldb multiples of 8.  B streams from
- * HBM once over an even split of the k range (the Stream-K reproduction
- * post on leiblog.wang): row-major B 256 columns per workgroup, each lane
- * multiplying the 4 x 4 blocks of B it loads on the matrix cores' 4x4x4
- * blocks; column-major B 128 columns per workgroup in 16x16x32 blocks fed
- * straight from memory.  The k ranges' partial sums (ranges x M x N floats
- * of workspace) are added in range order by a second kernel on the stream,
- * which runs the epilogue.
+ * Products of few rows in f16 or bf16 with row-major A run on a split-k
+ * GEMV instead of the tiles when lda is a multiple of 8, every pointer
+ * 16-byte aligned, and A and B lie below 2 GiB: at most 32 rows with
+ * row-major B and ldb a multiple of 8, else at most 8 rows, with row-major
+ * B N and ldb multiples of 4, with column-major B (k contiguous) K and ldb
+ * multiples of 8 (up to 64 / 16 rows with option "gemv" = 2).  B streams
+ * from HBM once over an even split of the k range (the Stream-K
+ * reproduction post on leiblog.wang).  Row-major B from 5 rows on: 128
+ * columns per workgroup, each lane transposing the 8 x 8 blocks of B it
+ * loads in registers into operands of the matrix cores' 16x16x32 blocks;
+ * below 5 rows (or ldb not a multiple of 8): 256 columns per workgroup in
+ * 4x4x4 blocks; column-major B: 128 columns per workgroup in 16x16x32
+ * blocks fed straight from memory.  The k ranges' partial sums (ranges x M
+ * x N floats of workspace) are added in range order by a second kernel on
+ * the stream, which runs the epilogue.
  * Returns TCM_OK once the work is enqueued; TCM_ERR_INVALID_VALUE for
  * negative sizes, too-small leading dimensions, a NULL operand with a
  * non-empty extent, unknown dtype/flags/epilogue, both output type flags or
@@ -318,15 +321,22 @@ const char* tcm_status_string(int status);
  *                  whose class it holds; 0 = ignore it.  force_config /
  *                  force_mode / sk_grid / gemv win.
  *   "gemv"         the split-k GEMV (tcm_gemm): 0 = planner decides (calls
- *                  it can serve with at most 8 rows, or the tuning table's
+ *                  it can serve with at most 32 rows on the 16x16x32
+ *                  row-major-B kernel, else 8, or the tuning table's
  *                  choice), 1 = never, 2 = every call it can serve (at most
- *                  16 rows) unless a tile config or mode is forced.
- *   "gemv_splits"  0 = planner decides (row-major B: about two workgroups
+ *                  64 / 16 rows) unless a tile config or mode is forced.
+ *   "gemv_wide"    which GEMV kernel serves row-major B: 0 = planner
+ *                  decides (16x16x32 from 5 rows on, where eligible), 1 =
+ *                  never the 16x16x32 kernel, 2 = always it where eligible.
+ *   "gemv_splits"  0 = planner decides (4x4x4 kernel: about two workgroups
  *                  per CU, the partial sums kept within an eighth of B's
- *                  bytes; column-major B: ranges of 256 rows), else the
- *                  number of k ranges, rounded to ranges of a multiple of
- *                  64 rows, at most 1024 each (row-major B), or of a
- *                  multiple of 256 rows (column-major B) (1..4096).
+ *                  bytes; 16x16x32 row-major kernel: one workgroup per CU,
+ *                  ranges of a multiple of 512 rows (256 above 16 rows)
+ *                  where K allows; column-major B: ranges of 256 rows), else
+ *                  the number of k ranges, rounded to ranges of a multiple
+ *                  of 64 rows, at most 1024 each (4x4x4 kernel), of 128
+ *                  rows (16x16x32 row-major kernel) or of 256 rows
+ *                  (column-major B) (1..4096).
  * Unknown keys or out-of-range values: TCM_ERR_INVALID_VALUE.
  * tcm_get_option returns the value, or -2 for an unknown key.
  */
@@ -338,10 +348,11 @@ typedef struct {
     int32_t kernel;        /* 0 = generic kernel, 1 = tiled MFMA kernel, 2 = split-k GEMV */
     int32_t config;        /* tile-table index (tiled kernel) or -1 */
     int32_t bm, bn, bk;    /* macro tile; bk in elements.  GEMV: the rows it
-                              computes (1, 2, 4, 8, 16), the columns per
-                              workgroup (256, or 128 with column-major B), k rows
-                              per range; iters_per_tile = the k ranges, tiles =
-                              the column blocks */
+                              computes (1, 2, 4, 8, 16; 16, 32, 64 on the
+                              16x16x32 row-major-B kernel), the columns per
+                              workgroup (256 on the 4x4x4 kernel, else 128), k
+                              rows per range; iters_per_tile = the k ranges,
+                              tiles = the column blocks */
     int32_t mode;          /* 1 = data-parallel, 2 = Stream-K (+ data-parallel tiles) */
     int32_t grid;          /* workgroups launched */
     int64_t tiles;         /* ceil(M/bm) * ceil(N/bn) */
@@ -414,7 +425,9 @@ int tcm_tile_order(int32_t t, int32_t tiles_m, int32_t tiles_n, int32_t* tm, int
  * epilogue flags, whether every pointer is 16-byte aligned, whether the call
  * is a batch, and the half octave of each of M, N and K (floor(2*log2(x)):
  * e.g. every M in [4096, 5792] shares class 24).  An entry gives the tile
- * config and mode (or the split-k GEMV, config 100 in the text), the split-k grid policy (the planner's; g/8 workgroups
+ * config and mode (or a split-k GEMV kernel: config 100 in the text for the
+ * 4x4x4 row-major-B or the column-major-B kernel, 101 for the 16x16x32
+ * row-major-B one), the split-k grid policy (the planner's; g/8 workgroups
  * per CU; or s workgroups per tile, every tile split into s equal shares),
  * the way split tiles are summed (the planner's, last arrival, fix-up
  * kernel) and the tile-order group rows (the planner's, or 1..16).
@@ -435,7 +448,7 @@ int tcm_tile_order(int32_t t, int32_t tiles_m, int32_t tiles_n, int32_t* tm, int
  * tcm_tune -- search the tuning space on this problem and record the
  * fastest point for its shape class.  Stage 1 times every tile config in
  * both modes (data-parallel, split-k) with the planner's other parameters,
- * and the split-k GEMV where it can serve the call;
+ * and the split-k GEMV kernels where they can serve the call;
  * stage 2 varies, around the three fastest tile plans, the tile-order group rows and,
  * for split-k, the grid (0.5 to 2 workgroups per CU, 1 to 4 equal shares per
  * tile) and the fix-up.  Each candidate is timed twice and keeps its better
@@ -460,8 +473,8 @@ int tcm_tune(int64_t M, int64_t N, int64_t K,
  *   "tcm-tune-2 dtype a_col b_col c_type epilogue aligned batched mclass
  *    nclass kclass config mode grid_kind grid_param fixup group_m
  *    microseconds M N K"
- * (c_type 0 = the accumulator type, 1 = f16, 2 = bf16; config 100 = the
- * split-k GEMV, with mode 1 and zeros after it; grid_kind 0 = the
+ * (c_type 0 = the accumulator type, 1 = f16, 2 = bf16; config 100 / 101 =
+ * the split-k GEMV kernels, with mode 1 and zeros after it; grid_kind 0 = the
  * planner's, 1 = grid_param/8 workgroups per CU, 2 = grid_param per tile;
  * fixup and group_m 0 = the planner's; M N K = the shape it was tuned on).
  * Writes it NUL-terminated into buf (truncated to len) and returns its full

@@ -357,9 +357,176 @@ __global__ __launch_bounds__(kThreads) void gemv_t_kernel(GemvArgs g) {
     }
 }
 
+// ------------------------------------------- row-major B, up to 64 rows
+// The layout of the first kernel (B n-contiguous) on the full-rate
+// v_mfma_f32_16x16x32, whose B operand wants 8 consecutive k of one column
+// per lane.  A lane loads 8 consecutive rows of B, 16 bytes (8 columns) of
+// each, and transposes that 8 x 8 block in registers: column j's 8 k values,
+// two per register, take 4 v_perm.  The 16 lanes of lane group g
+// (16g .. 16g+15) hold the same 8 rows, k = 8g .. 8g+7 of the step, so they
+// fill the instruction's 16 column slots and its k layout: issue j of a step
+// multiplies columns n0 + 8c + j (c = lane & 15), and A's operand is one
+// 16-byte load per 16-row block in its own layout (row c, k = 8g ..).  A
+// wave covers 128 columns x 32 k per step with 8 loads of B and one of A per
+// 16 rows; B never goes through LDS, and at 64 rows the matrix cores need
+// about a quarter of the time B's bytes take.
+//
+// Work split as in the first kernel: workgroup (x, y) owns 128 columns and
+// the k range [kw y, kw y + kw); wave w takes its 32-k steps w, w + 4, ...,
+// the loads of wide_steps<MB>() of them in flight together.  The four waves'
+// sums meet in LDS and are added in wave order, then stored as a partial
+// (several k ranges) or through the epilogue (one).
+//
+// Rows of B at or past K read as zeros (buffer range check); A's k past K
+// are zeroed in registers, so a padding value never reaches a sum.  Columns
+// at or past N come from whatever the row holds there and are never stored.
+
+// keep the first nv (1 .. 7) of the 8 halves of v
+__device__ __forceinline__ u4_t keep_low_halves(u4_t v, int nv) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) v[d] = 2 * d + 1 < nv ? v[d] : (2 * d < nv ? (v[d] & 0xffffu) : 0u);
+    return v;
+}
+
+// 32-k steps per wave whose loads are in flight together: at 16 rows four
+// (216 registers), at 32 two, so that the accumulators stay in the 256
+// registers of two waves per SIMD (with four, or at 64 rows, the compiler
+// moves them through the accumulation registers every step)
+template <int MB>
+constexpr int wide_steps() { return MB == 16 ? 4 : 2; }
+
+// NS 32-k steps of one wave, from step s (then s + 4, ...): every load of
+// the group issued before the first multiply waits for its data
+template <int DT, int RB, int NS>
+__device__ __forceinline__ void wide_group(f4_t (&acc)[RB][8], __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                           const unsigned (&a_row)[RB], unsigned b_lane, unsigned ldb_bytes, int kb, int K) {
+    u4_t bv[NS][8], av[NS][RB];
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        const int k = kb + 128 * i;  // this lane's 8 rows of B and 8 k of A
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const unsigned off = k + r < K && b_lane != kOOB ? (unsigned)(k + r) * ldb_bytes + b_lane : kOOB;
+            bv[i][r] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
+        }
+#pragma unroll
+        for (int q = 0; q < RB; ++q) {
+            const unsigned off = k < K && a_row[q] != kOOB ? a_row[q] + 2u * (unsigned)k : kOOB;
+            av[i][q] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0));
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        const int k = kb + 128 * i;
+        if (k < K && k + 8 > K) {  // A's piece ends past K: zero those k (B's rows there read as zeros)
+#pragma unroll
+            for (int q = 0; q < RB; ++q) av[i][q] = keep_low_halves(av[i][q], K - k);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            // column n0 + 8c + j at k .. k+7: (row 2p, row 2p+1) halves j of the lane's rows
+            const int d = j >> 1;
+            const unsigned sel = (j & 1) ? 0x07060302u : 0x05040100u;
+            const u4_t bt = u4_t{__builtin_amdgcn_perm(bv[i][1][d], bv[i][0][d], sel),
+                                 __builtin_amdgcn_perm(bv[i][3][d], bv[i][2][d], sel),
+                                 __builtin_amdgcn_perm(bv[i][5][d], bv[i][4][d], sel),
+                                 __builtin_amdgcn_perm(bv[i][7][d], bv[i][6][d], sel)};
+#pragma unroll
+            for (int q = 0; q < RB; ++q) {
+                if constexpr (DT == F16)
+                    acc[q][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, av[i][q]),
+                                                                       __builtin_bit_cast(h8_t, bt), acc[q][j], 0, 0, 0);
+                else
+                    acc[q][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8_t, av[i][q]),
+                                                                        __builtin_bit_cast(b8_t, bt), acc[q][j], 0, 0, 0);
+            }
+        }
+    }
+}
+
+template <int DT, int MB>
+__global__ __launch_bounds__(kThreads, MB <= 32 ? 2 : 1) void gemv_r_kernel(GemvArgs g) {
+    constexpr int RB = MB / 16;  // 16-row blocks
+    constexpr int S = wide_steps<MB>();
+    static_assert(S * (8 + RB) <= 63, "loads in flight within the vmcnt range");
+    __shared__ __attribute__((aligned(16))) float red[4][MB][kGemvWCols];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c = lane & 15, grp = lane >> 4;
+    const int n0 = blockIdx.x * kGemvWCols;
+    const int k0 = blockIdx.y * g.kw, K = g.K;
+    // The ranges end at the 16-byte boundary past each operand's last
+    // element: the range check zeroes a whole dword that crosses the end, and
+    // the last piece of A's last row (K odd) or of B's last row (N not a
+    // multiple of 8) holds elements that are used.  A, B and their rows are
+    // 16-byte aligned, so that boundary lies in the same page as the
+    // element; the bytes past it are masked (A) or feed only columns past N.
+    const int64_t a_lim = (g.a_bytes + 15) & ~(int64_t)15, b_lim = (g.b_bytes + 15) & ~(int64_t)15;
+    const __amdgpu_buffer_rsrc_t ra =
+        __builtin_amdgcn_make_buffer_rsrc((void*)g.A, (short)0, a_lim < (int64_t)kOOB ? (int)a_lim : (int)kOOB, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rb =
+        __builtin_amdgcn_make_buffer_rsrc((void*)g.B, (short)0, b_lim < (int64_t)kOOB ? (int)b_lim : (int)kOOB, kRsrcWord3);
+    const unsigned ldb_bytes = (unsigned)g.ldb * 2u;
+    const unsigned b_lane = n0 + 8 * c < g.N ? (unsigned)(n0 + 8 * c) * 2u : kOOB;  // bytes to this lane's columns
+    unsigned a_row[RB];                                                             // bytes to this lane's rows of A
+#pragma unroll
+    for (int q = 0; q < RB; ++q) a_row[q] = 16 * q + c < g.M ? (unsigned)((16 * q + c) * g.lda) * 2u : kOOB;
+    f4_t acc[RB][8];
+#pragma unroll
+    for (int q = 0; q < RB; ++q)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[q][j] = f4_t{0.f, 0.f, 0.f, 0.f};
+
+    // groups of S steps, then the range's last steps one at a time (the
+    // host makes kw a multiple of 4 S steps where K allows)
+    const int steps = g.kw / 32;
+    int s0 = wave;
+    for (; s0 + 4 * (S - 1) < steps; s0 += 4 * S)
+        wide_group<DT, RB, S>(acc, ra, rb, a_row, b_lane, ldb_bytes, k0 + 32 * s0 + 8 * grp, K);
+    for (; s0 < steps; s0 += 4) wide_group<DT, RB, 1>(acc, ra, rb, a_row, b_lane, ldb_bytes, k0 + 32 * s0 + 8 * grp, K);
+    // lane l holds rows 16q + 4g + t (t = 0 .. 3) of columns n0 + 8c + j
+#pragma unroll
+    for (int q = 0; q < RB; ++q)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int m = 16 * q + 4 * grp + t;
+            if (m < g.M) {
+                *(f4_t*)&red[wave][m][8 * c] = f4_t{acc[q][0][t], acc[q][1][t], acc[q][2][t], acc[q][3][t]};
+                *(f4_t*)&red[wave][m][8 * c + 4] = f4_t{acc[q][4][t], acc[q][5][t], acc[q][6][t], acc[q][7][t]};
+            }
+        }
+    __syncthreads();
+    // the four waves' sums, added in wave order: thread t takes column t mod 128 of every other row
+    const int col = tid & (kGemvWCols - 1), n = n0 + col;
+    if (n >= g.N) return;
+    const int64_t mn = (int64_t)g.M * g.N;
+    for (int m = tid / kGemvWCols; m < MB && m < g.M; m += kThreads / kGemvWCols) {
+        const float s = ((red[0][m][col] + red[1][m][col]) + red[2][m][col]) + red[3][m][col];
+        if (g.splits == 1)
+            finish(g, m, n, s);
+        else
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, s), partial_rsrc(g),
+                                                  (unsigned)((blockIdx.y * mn + (int64_t)m * g.N + n) * 4), 0, 0);
+    }
+}
+
 template <int DT>
 int launch_dt(const GemvArgs& a, void* stream) {
     hipStream_t s = (hipStream_t)stream;
+    if (a.wide) {
+        const dim3 grid_w((unsigned)((a.N + kGemvWCols - 1) / kGemvWCols), (unsigned)a.splits);
+        switch (gemv_wide_rows_bucket(a.M)) {
+        case 16: hipLaunchKernelGGL((gemv_r_kernel<DT, 16>), grid_w, dim3(kThreads), 0, s, a); break;
+        case 32: hipLaunchKernelGGL((gemv_r_kernel<DT, 32>), grid_w, dim3(kThreads), 0, s, a); break;
+        default: hipLaunchKernelGGL((gemv_r_kernel<DT, 64>), grid_w, dim3(kThreads), 0, s, a); break;
+        }
+        int st = (int)hipGetLastError();
+        if (st != 0 || a.splits <= 1) return st;
+        const int64_t mn = (int64_t)a.M * a.N;
+        hipLaunchKernelGGL(gemv_reduce_kernel, dim3((unsigned)((mn + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, a);
+        return (int)hipGetLastError();
+    }
     if (a.b_col) {
         const dim3 grid_t((unsigned)((a.N + kGemvTCols - 1) / kGemvTCols), (unsigned)a.splits);
         hipLaunchKernelGGL((gemv_t_kernel<DT>), grid_t, dim3(kThreads), 0, s, a);
@@ -387,13 +554,20 @@ int launch_dt(const GemvArgs& a, void* stream) {
 }  // namespace gemv
 
 int launch_gemv(int dtype, const GemvArgs& a, void* stream) {
-    if (a.M < 1 || a.M > kGemvMaxRows || a.N < 1 || a.splits < 1 || (int64_t)a.splits * a.kw < a.K ||
-        (a.splits > 1 && !a.partial) || (int64_t)a.splits * a.M * a.N * 4 >= (int64_t)gemv::kOOB)
+    if (a.M < 1 || a.M > (a.wide ? kGemvWideRows : kGemvMaxRows) || a.N < 1 || a.splits < 1 ||
+        (int64_t)a.splits * a.kw < a.K || (a.splits > 1 && !a.partial) ||
+        (int64_t)a.splits * a.M * a.N * 4 >= (int64_t)gemv::kOOB)
         return (int)hipErrorInvalidValue;
-    if (a.b_col ? (a.kw < kGemvTKAlign || a.kw % kGemvTKAlign || a.K % 8 || a.a_bytes >= (int64_t)gemv::kOOB ||
-                   a.b_bytes >= (int64_t)gemv::kOOB)
-                : (a.N % 4 || a.kw < kGemvKAlign || a.kw % kGemvKAlign || a.kw > gemv::Gemv<F16, 1>::KW_MAX))
+    if (a.wide) {  // 16-byte pieces of rows of A and B; every offset below 2 GiB
+        if (a.b_col || a.kw < kGemvWKAlign || a.kw % kGemvWKAlign || a.lda % 8 || a.ldb % 8 ||
+            a.a_bytes >= (int64_t)gemv::kOOB || (int64_t)a.K * a.ldb * 2 >= (int64_t)gemv::kOOB ||
+            (int64_t)a.M * a.lda * 2 >= (int64_t)gemv::kOOB)
+            return (int)hipErrorInvalidValue;
+    } else if (a.b_col ? (a.kw < kGemvTKAlign || a.kw % kGemvTKAlign || a.K % 8 || a.a_bytes >= (int64_t)gemv::kOOB ||
+                          a.b_bytes >= (int64_t)gemv::kOOB)
+                       : (a.N % 4 || a.kw < kGemvKAlign || a.kw % kGemvKAlign || a.kw > gemv::Gemv<F16, 1>::KW_MAX)) {
         return (int)hipErrorInvalidValue;
+    }
     if (dtype == F16) return gemv::launch_dt<F16>(a, stream);
     if (dtype == BF16) return gemv::launch_dt<BF16>(a, stream);
     return (int)hipErrorInvalidValue;

@@ -268,7 +268,14 @@ Estimate estimate(const Problem& p, int ci, int cus, int force_mode, int sk_grid
 
 }  // namespace
 
-bool gemv_eligible(const Problem& p) {
+bool gemv_wide_eligible(const Problem& p) {
+    return (p.dtype == F16 || p.dtype == BF16) && !p.a_col && !p.b_col && !p.conv && !p.group && p.batch <= 1 &&
+           p.M >= 1 && p.M <= kGemvWideRows && p.N >= 1 && p.K >= 1 && p.K <= (1LL << 22) && p.lda % 8 == 0 &&
+           p.ldb % 8 == 0 && p.aligned && p.ldc < (1LL << 31) && p.M * p.lda * 2 < (1LL << 31) &&
+           p.K * p.ldb * 2 < (1LL << 31);
+}
+
+bool gemv_narrow_eligible(const Problem& p) {
     const bool common = (p.dtype == F16 || p.dtype == BF16) && !p.a_col && !p.conv && !p.group && p.batch <= 1 &&
                         p.M >= 1 && p.M <= kGemvMaxRows && p.K >= 1 && p.K <= (1LL << 22) && p.lda % 8 == 0 &&
                         p.aligned && p.ldc < (1LL << 31) && p.lda < (1LL << 31);
@@ -279,14 +286,35 @@ bool gemv_eligible(const Problem& p) {
     return p.N >= 4 && p.N % 4 == 0 && p.ldb % 4 == 0 && (p.K - 1) * p.ldb * 2 + p.N * 2 < (1LL << 31);
 }
 
-// Up to 8 rows the GEMV beats the tiled kernel's Stream-K plans on N = K =
-// 4096 (f16: 7.3 / 8.1 / 8.7 / 10.5 us at M = 1 / 2 / 4 / 8 against
-// 10.9-11.1 us); at 16 rows it is slower (12.5 against 11.3 us).
-constexpr int64_t kGemvAutoRows = 8;
+namespace {
+// a GEMV kernel can serve p under options o (gemv_wide = 1 leaves out the 16x16x32 kernel)
+bool gemv_ok(const Problem& p, const Options& o) {
+    return gemv_narrow_eligible(p) || (o.gemv_wide != 1 && gemv_wide_eligible(p));
+}
+// Row-major B: the 16x16x32 kernel from 5 rows on and where the 4x4x4 one
+// cannot serve (17 to 64 rows, N not a multiple of 4), or as option
+// gemv_wide asks.  On N = K = 4096 (f16, block of calls) the 4x4x4 kernel
+// takes 7.4 / 8.7 / 10.4 / 13.7 us at M = 1 / 4 / 8 / 12, the 16x16x32 one
+// 7.4-8.4 / 8.8 / 8.4 / 8.5 us.
+constexpr int64_t kGemvWideFrom = 5;
+bool gemv_pick_wide(const Problem& p, const Options& o) {
+    if (!gemv_wide_eligible(p) || o.gemv_wide == 1) return false;
+    return o.gemv_wide == 2 || !gemv_narrow_eligible(p) || p.M >= kGemvWideFrom;
+}
+}  // namespace
+
+bool gemv_eligible(const Problem& p) { return gemv_wide_eligible(p) || gemv_narrow_eligible(p); }
+
+// The GEMV beats the tiled kernel's Stream-K plans on N = K = 4096 (f16,
+// row-major B) up to 32 rows: 7.4 / 8.4 / 8.8 / 10.7 / 11.5 us at M = 1 / 8 /
+// 16 / 24 / 32 against 10.9 / 11.0 / 11.4 / 11.8 / 12.3 us; at 48 rows it
+// is slower (14.7 against 13.3 us).  Without the 16x16x32 kernel (column-
+// major B, rows of B not 16-byte aligned) it stops at 8 rows.
+constexpr int64_t kGemvAutoRows = 8, kGemvWideAutoRows = 32;
 bool gemv_preferred(const Problem& p, const Options& o) {
     if (o.generic || o.gemv == 1 || o.force_config >= 0 || o.force_mode != 0 || o.sk_grid != 0) return false;
-    if (!gemv_eligible(p)) return false;
-    return o.gemv == 2 || p.M <= kGemvAutoRows;
+    if (!gemv_ok(p, o)) return false;
+    return o.gemv == 2 || p.M <= kGemvAutoRows || (p.M <= kGemvWideAutoRows && gemv_pick_wide(p, o));
 }
 
 namespace {
@@ -299,6 +327,34 @@ void gemv_plan(const Problem& p, const Options& o, int cus, Plan* pl) {
     pl->kernel = 3;
     pl->config = -1;
     pl->mode = 1;
+    if (gemv_pick_wide(p, o)) {
+        // 16x16x32 kernel: one workgroup per CU (at N = K = 4096 and 8 to 32
+        // rows 8 k ranges beat 16 by 1.1-2.5 us: fewer partial sums), each k
+        // range a multiple of a group of in-flight steps for all four waves
+        // (4 x 4 x 32 k at 16 rows, 4 x 2 x 32 above) where K allows; an
+        // asked-for count on the 128-row grid
+        const int bucket = gemv_wide_rows_bucket(p.M);
+        const int64_t nb = cdiv(p.N, kGemvWCols);
+        int64_t kw;
+        if (o.gemv_splits > 0) {
+            kw = cdiv(cdiv(p.K, o.gemv_splits), kGemvWKAlign) * kGemvWKAlign;
+        } else {
+            const int64_t align = kGemvWKAlign * (bucket == 16 ? 4 : 2);
+            kw = cdiv(cdiv(p.K, std::max<int64_t>(1, cus / nb)), align) * align;
+        }
+        const int64_t splits = cdiv(p.K, kw);
+        pl->gemv_wide = true;
+        pl->bm = bucket;
+        pl->bn = kGemvWCols;
+        pl->bk = (int)kw;
+        pl->iters = splits;
+        pl->tiles = nb;
+        pl->grid = (int)(nb * splits);
+        pl->dp_tiles = nb;
+        pl->ws_partial_bytes = splits > 1 ? splits * p.M * p.N * 4 : 0;
+        pl->fixup_kernel = splits > 1;
+        return;
+    }
     if (p.b_col) {
         // column-major B: every wave keeps its whole k range in flight, so a
         // range is one group of kGemvTSteps 32-k steps (256 rows) unless
@@ -350,7 +406,7 @@ bool make_plan(const Problem& p, const Options& o, int cus, Plan* out) {
         return true;
     }
     if (cus <= 0) cus = kDefaultCUs;
-    if (gemv_eligible(p) && (gemv_preferred(p, o) || (o.gemv == 2 && !o.generic && o.force_config < 0))) {
+    if (gemv_ok(p, o) && (gemv_preferred(p, o) || (o.gemv == 2 && !o.generic && o.force_config < 0))) {
         gemv_plan(p, o, cus, &pl);
         *out = pl;
         return true;

@@ -23,6 +23,7 @@ struct Options {
     int group_m = 0;        // tile-order group rows (0: the planner's 4)
     int gemv = 0;           // split-k GEMV for products of at most 16 rows: 0 planner decides, 1 never, 2 whenever eligible
     int gemv_splits = 0;    // its k ranges (0: the planner's)
+    int gemv_wide = 0;      // row-major B: the 16x16x32 GEMV kernel (up to 64 rows): 0 planner decides, 1 never, 2 whenever eligible
     int sk_occ[kNumConfigs] = {0};  // Stream-K workgroups per CU by config (0: static estimate)
 };
 
@@ -54,6 +55,7 @@ struct Problem {
 struct Plan {
     int kernel = 0;   // 0 none (empty problem), 1 generic, 2 tiled, 3 split-k GEMV (bm = rows bucket,
                       // bn = columns per workgroup, bk = k per workgroup, iters = k ranges)
+    bool gemv_wide = false;  // GEMV on row-major B: the 16x16x32 kernel (else the 4x4x4 one)
     int config = -1;
     int bm = 0, bn = 0, bk = 0;
     int mode = 1;     // 1 data-parallel, 2 Stream-K (+ data-parallel tiles)
@@ -74,10 +76,16 @@ bool tile_eligible(const Problem& p, const TileConfig& c);
 // estimate), for the data-parallel and the Stream-K kernel.
 int tile_wg_per_cu(const TileConfig& c);
 int tile_sk_wg_per_cu(const TileConfig& c);
-// Split-k GEMV eligibility: f16 / bf16, row-major A and B, 1 <= M <= 16,
-// a single product, N a multiple of 4, 16-byte aligned pointers and rows of
-// A, 8-byte aligned rows of B, B below 2 GiB.
+// Split-k GEMV eligibility: f16 / bf16, row-major A, a single product,
+// 16-byte aligned pointers and rows of A, offsets below 2 GiB, and either
+// (4x4x4 kernel) B row-major, 1 <= M <= 16, N a multiple of 4, 8-byte
+// aligned rows of B; or (16x16x32 kernel) B row-major, 1 <= M <= 64,
+// 16-byte aligned rows of B; or B column-major, 1 <= M <= 16, K and ldb
+// multiples of 8.
 bool gemv_eligible(const Problem& p);
+// The 16x16x32 row-major-B kernel's part of that, and the other kernels'.
+bool gemv_wide_eligible(const Problem& p);
+bool gemv_narrow_eligible(const Problem& p);
 // Whether the planner (no option forcing a tile config or mode) takes the
 // GEMV for an eligible p.
 bool gemv_preferred(const Problem& p, const Options& o);

@@ -133,12 +133,14 @@ TuneKey tune_key(const Problem& p) {
     return TuneKey{p.dtype, (int)p.a_col, (int)p.b_col, p.c_type, p.epilogue, (int)p.aligned, p.batch > 1 ? 1 : 0,
                    half_octave(p.M), half_octave(p.N), half_octave(p.K)};
 }
-// The split-k GEMV as a candidate: config kGemvCand (outside the tile
-// table's index range), mode 1, no other parameter (its k ranges are the
-// planner's).
-constexpr int kGemvCand = 100;
+// The split-k GEMV kernels as candidates: configs outside the tile table's
+// index range, mode 1, no other parameter (their k ranges are the
+// planner's).  kGemvCand: the 4x4x4 row-major-B kernel or the column-major-B
+// one; kGemvWideCand: the 16x16x32 row-major-B kernel.
+constexpr int kGemvCand = 100, kGemvWideCand = 101;
+bool gemv_cand(int config) { return config == kGemvCand || config == kGemvWideCand; }
 bool valid_cand(const Cand& c) {
-    if (c.config == kGemvCand)
+    if (gemv_cand(c.config))
         return c.mode == 1 && c.grid_kind == 0 && c.grid_param == 0 && c.fixup == 0 && c.group_m == 0;
     return c.config >= 0 && c.config < kNumConfigs && (c.mode == 1 || c.mode == 2) && c.grid_kind >= 0 &&
            c.grid_kind <= 2 && c.grid_param >= 0 && c.grid_param <= 64 && (c.grid_kind == 0 || c.grid_param > 0) &&
@@ -147,10 +149,11 @@ bool valid_cand(const Cand& c) {
 // Apply candidate c to options o.
 void apply_cand(const Cand& c, Options* o) {
     o->sk_grid = 0;
-    if (c.config == kGemvCand) {
+    if (gemv_cand(c.config)) {
         o->force_config = -1;
         o->force_mode = 0;
         o->gemv = 2;
+        o->gemv_wide = c.config == kGemvWideCand ? 2 : 1;
         return;
     }
     o->force_config = c.config;
@@ -307,11 +310,15 @@ Options plan_options(const Problem& p) {
             !(o.gemv == 2 && gemv_eligible(p))) {
             const TuneKey k = tune_key(p);
             auto it = entry_for(p, k, cus);
-            // a GEMV entry does not apply with option gemv = 1 (never)
-            if (it != g_tune.end() && !(it->second.c.config == kGemvCand && o.gemv == 1)) {
+            // a GEMV entry does not apply with option gemv = 1 (never), nor
+            // against option gemv_wide's choice of kernel
+            const bool skip = it != g_tune.end() && gemv_cand(it->second.c.config) &&
+                              (o.gemv == 1 || (it->second.c.config == kGemvWideCand ? o.gemv_wide == 1 : o.gemv_wide == 2));
+            if (it != g_tune.end() && !skip) {
                 const Cand& c = it->second.c;
-                if (c.config == kGemvCand) {
+                if (gemv_cand(c.config)) {
                     o.gemv = 2;  // (a problem it cannot serve is planned as if untuned)
+                    o.gemv_wide = c.config == kGemvWideCand ? 2 : 1;
                 } else {
                     o.force_config = c.config;
                     o.force_mode = c.mode;
@@ -429,9 +436,10 @@ std::string describe(const Plan& pl, const Problem& p) {
         snprintf(buf, sizeof buf, "empty problem M=%lld N=%lld", (long long)p.M, (long long)p.N);
     } else if (pl.kernel == 3) {
         snprintf(buf, sizeof buf,
-                 "kernel=gemv rows=%d cols_per_wg=%d k_per_wg=%d splits=%lld grid=%d M=%lld N=%lld K=%lld dtype=%d b_col=%d%s",
+                 "kernel=gemv rows=%d cols_per_wg=%d k_per_wg=%d splits=%lld grid=%d M=%lld N=%lld K=%lld dtype=%d b_col=%d "
+                 "mfma=%s%s",
                  pl.bm, pl.bn, pl.bk, (long long)pl.iters, pl.grid, (long long)p.M, (long long)p.N, (long long)p.K, p.dtype,
-                 (int)p.b_col, pl.fixup_kernel ? " fixup=kernel" : "");
+                 (int)p.b_col, p.b_col || pl.gemv_wide ? "16x16x32" : "4x4x4", pl.fixup_kernel ? " fixup=kernel" : "");
     } else if (pl.kernel == 1) {
         snprintf(buf, sizeof buf, "kernel=generic tile=64x64 tiles=%lld iters=%lld M=%lld N=%lld K=%lld dtype=%d batch=%lld%s",
                  (long long)pl.tiles, (long long)pl.iters, (long long)p.M, (long long)p.N, (long long)p.K, p.dtype,
@@ -534,6 +542,9 @@ int tcm_set_option(const char* key, int64_t value) {
     } else if (!strcmp(key, "gemv_splits")) {
         if (value < 0 || value > 4096) return TCM_ERR_INVALID_VALUE;
         g_opts.gemv_splits = (int)value;
+    } else if (!strcmp(key, "gemv_wide")) {
+        if (value < 0 || value > 2) return TCM_ERR_INVALID_VALUE;
+        g_opts.gemv_wide = (int)value;
     } else {
         return TCM_ERR_INVALID_VALUE;
     }
@@ -554,6 +565,7 @@ int64_t tcm_get_option(const char* key) {
     if (!strcmp(key, "tuned")) return g_use_tuned;
     if (!strcmp(key, "gemv")) return g_opts.gemv;
     if (!strcmp(key, "gemv_splits")) return g_opts.gemv_splits;
+    if (!strcmp(key, "gemv_wide")) return g_opts.gemv_wide;
     return -2;
 }
 
@@ -790,6 +802,7 @@ int gemm_impl(int64_t batch, int64_t M, int64_t N, int64_t K, const void* A, int
         v.b_bytes = b_one;
         v.a_bytes = a_one;
         v.b_col = p.b_col ? 1 : 0;
+        v.wide = pl.gemv_wide ? 1 : 0;
         if (pl.ws_partial_bytes > 0) {
             if (noalloc) {
                 char* base = nullptr;
@@ -1276,8 +1289,10 @@ int tcm_tune(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
         st = run();  // warm-up, and the plan this candidate really gets
         const std::string plan = t_last_plan;
         const int pm = strstr(plan.c_str(), "mode=streamk") ? 2 : 1;
-        const bool as_asked = c.config == kGemvCand ? strstr(plan.c_str(), "kernel=gemv") != nullptr
-                                                    : strstr(plan.c_str(), "kernel=tile") && field(plan, " config=") == c.config;
+        const bool wide = strstr(plan.c_str(), "kernel=gemv") && strstr(plan.c_str(), " b_col=0 mfma=16x16x32");
+        const bool as_asked = c.config == kGemvCand       ? strstr(plan.c_str(), "kernel=gemv") && !wide
+                              : c.config == kGemvWideCand ? wide
+                                                          : strstr(plan.c_str(), "kernel=tile") && field(plan, " config=") == c.config;
         if (st != TCM_OK || !as_asked || pm != c.mode) {
             t_cand = nullptr;
             return false;
@@ -1325,12 +1340,13 @@ int tcm_tune(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
             x.mode = mode;
             stage1.push_back({x, 1e300, 0});
         }
-    if (gemv_eligible(p)) {
-        Cand x;
-        x.config = kGemvCand;
-        x.mode = 1;
-        stage1.push_back({x, 1e300, 0});
-    }
+    for (int gc : {kGemvCand, kGemvWideCand})
+        if (gc == kGemvCand ? gemv_narrow_eligible(p) : gemv_wide_eligible(p)) {
+            Cand x;
+            x.config = gc;
+            x.mode = 1;
+            stage1.push_back({x, 1e300, 0});
+        }
     std::vector<char> valid(stage1.size(), 1);
     for (int sweep = 0; sweep < 2 && st == TCM_OK; ++sweep)
         for (size_t i = 0; i < stage1.size() && st == TCM_OK; ++i) {
@@ -1353,7 +1369,7 @@ int tcm_tune(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
     const int cus = current_cus();
     for (size_t r = 0; r < ranked.size() && r < 3; ++r) {
         const Cand b = ranked[r].c;
-        if (b.config == kGemvCand) continue;  // nothing of the tile schedule applies
+        if (gemv_cand(b.config)) continue;  // nothing of the tile schedule applies
         const int64_t T = ranked[r].tiles;
         for (int gm : {1, 2, 8}) {
             Cand x = b;

@@ -175,9 +175,12 @@ def _label(shape):
 
 
 def gemv_shape(shape):
-    """Shapes the split-k GEMV can serve (f16 / bf16, at most 16 rows)."""
+    """Shapes a split-k GEMV kernel can serve (f16 / bf16; at most 16 rows,
+    or at most 64 with row-major B and rows of A and B 16-byte aligned)."""
     dt, M, N, K, b_col, epi, c_type = shape
-    return dt in (F16, BF16) and M <= 16 and K % 8 == 0 and (b_col or N % 4 == 0)
+    if dt not in (F16, BF16) or K % 8:
+        return False
+    return (M <= 16 and (b_col or N % 4 == 0)) or (not b_col and M <= 64 and N % 8 == 0)
 
 
 def tune(shapes, iters, out, merge=False):
@@ -285,8 +288,8 @@ def _write_report(report, results, iters):
         f.write("For each shape (none of them in the tuning set), `auto` is the call's own plan (the shipped table "
                 "`tensor_core_mixed_amd/tuned/mi355x.txt` where it holds the shape's class, else the cost model); "
                 "`best` is the fastest point `tcm_tune` finds "
-                "for the shape (two stages: every tile config in both modes and, where it can serve the shape, the split-k GEMV "
-                "(config 100); then group rows, Stream-K grid and fix-up around the three fastest tile plans).  Both are then re-timed alternately, five blocks of back-to-back calls each, "
+                "for the shape (two stages: every tile config in both modes and, where they can serve the shape, the split-k GEMV "
+                "kernels (configs 100 and 101); then group rows, Stream-K grid and fix-up around the three fastest tile plans).  Both are then re-timed alternately, five blocks of back-to-back calls each, "
                 "and the medians compared: `ratio` = auto / best (the search's own minimum over many candidates reads "
                 "low, so it is not used).\n\n")
         for title, rows in results:

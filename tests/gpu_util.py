@@ -63,6 +63,7 @@ def value_range(store, dtype):
         v = torch.from_numpy(store.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
     else:
         v = store.astype(np.float64)
+    v = v[np.isfinite(v)]  # padding may hold non-finite values that no sum reads
     return float(np.max(np.abs(v))) if v.size else 0.0
 
 

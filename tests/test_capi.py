@@ -217,11 +217,16 @@ def test_deep_config_is_the_small_tile_with_more_stages():
         # the skinny unit: 32 x 64, two waves
         bm, bn, _, waves = T.tcm_config_info(6, dt)
         assert (bm, bn, waves) == (32, 64, 2)
-    # it serves single-row products only, and as Stream-K
-    p = T.tcm_plan(16, 4096, 4096, 4096, 4096, 4096, T.TCM_F16_F32)
-    assert p["config"] == 6 and p["mode"] == 2
-    assert T.tcm_plan(64, 4096, 4096, 4096, 4096, 4096, T.TCM_F16_F32)["config"] != 6
-    assert T.tcm_plan(512, 512, 512, 512, 512, 512, T.TCM_F16_F32)["config"] != 6
+    # it serves products of few rows only, and as Stream-K (the split-k GEMV
+    # left out, which takes such products where it can)
+    T.tcm_set_option("gemv", 1)
+    try:
+        p = T.tcm_plan(16, 4096, 4096, 4096, 4096, 4096, T.TCM_F16_F32)
+        assert p["config"] == 6 and p["mode"] == 2
+        assert T.tcm_plan(64, 4096, 4096, 4096, 4096, 4096, T.TCM_F16_F32)["config"] != 6
+        assert T.tcm_plan(512, 512, 512, 512, 512, 512, T.TCM_F16_F32)["config"] != 6
+    finally:
+        T.tcm_set_option("gemv", 0)
 
 
 def test_planner_keeps_split_128_tiles_for_phase_aligned_shapes():
@@ -603,29 +608,38 @@ def test_data_parallel_entries_carry_over_to_fewer_waves_only():
 @pytest.mark.parametrize("tuned", [0, 1])
 @pytest.mark.parametrize("M", [1, 2, 3, 4, 5, 8])
 def test_planner_gemv_for_few_rows(M, tuned):
-    """Row-major f16 products of at most 8 rows run on the split-k GEMV, with
-    or without the shipped table (whose entries for those classes name it):
-    256 columns a workgroup, k ranges of a multiple of 64 rows covering K,
-    their partial sums (ranges x M x N floats) added by a second kernel."""
+    """Row-major f16 products of at most 32 rows run on a split-k GEMV, with
+    or without the shipped table (whose entries for those classes name one):
+    below 5 rows the 4x4x4 kernel (256 columns a workgroup, k ranges of a
+    multiple of 64 rows), from 5 rows the 16x16x32 one (128 columns, ranges
+    of a multiple of 128 rows, one workgroup per CU without the table); k
+    ranges cover K, their partial sums (ranges x M x N floats) added by a
+    second kernel."""
     T.tcm_set_option("tuned", tuned)
     try:
         p = T.tcm_plan(M, 4096, 4096, 4096, 4096, 4096, T.TCM_F16_F32)
     finally:
         T.tcm_set_option("tuned", 1)
     assert p["kernel"] == 2 and p["config"] == -1
-    assert p["bn"] == 256 and p["bk"] % 64 == 0 and p["bk"] * p["iters_per_tile"] >= 4096
-    assert p["grid"] == 16 * p["iters_per_tile"]
+    if p["bn"] == 256:
+        assert p["bk"] % 64 == 0 and p["bm"] == {1: 1, 2: 2, 3: 4, 4: 4, 5: 8, 8: 8}[M]
+    else:
+        assert p["bn"] == 128 and p["bk"] % 128 == 0 and p["bm"] == (16 if M <= 16 else 32)
+    assert p["bk"] * p["iters_per_tile"] >= 4096 and p["grid"] == 4096 // p["bn"] * p["iters_per_tile"]
     assert p["workspace_bytes"] == p["iters_per_tile"] * M * 4096 * 4 and p["fixup_kernel"] == 1
-    assert p["bm"] == {1: 1, 2: 2, 3: 4, 4: 4, 5: 8, 8: 8}[M]
+    if not tuned:
+        assert p["bn"] == (256 if M <= 4 else 128)
+        if M >= 5:
+            assert p["iters_per_tile"] == 8 and p["bk"] == 512
 
 
 def test_planner_gemv_not_taken_when_ineligible():
-    """More than 16 rows, row-major B with N not a multiple of 4,
+    """More than 32 rows, row-major B with N not a multiple of 4,
     column-major B with K not a multiple of 8, a padded A row off 16 bytes,
     int8 or f32, a forced tile config or mode: tiles."""
     code = T.TCM_F16_F32
     assert T.tcm_plan(8, 4096, 4096, 4096, 4096, 4096, code)["kernel"] == 2
-    assert T.tcm_plan(17, 4096, 4096, 4096, 4096, 4096, code)["kernel"] == 1
+    assert T.tcm_plan(33, 4096, 4096, 4096, 4096, 4096, code)["kernel"] == 1
     assert T.tcm_plan(8, 4096, 4100, 4104, 4104, 4096, code | T.TCM_B_COLMAJOR)["kernel"] != 2
     assert T.tcm_plan(8, 4094, 4096, 4096, 4094, 4094, code)["kernel"] != 2
     assert T.tcm_plan(8, 4096, 4096, 4100, 4096, 4096, code)["kernel"] != 2
@@ -640,19 +654,60 @@ def test_planner_gemv_not_taken_when_ineligible():
             T.tcm_set_option(key, -1 if key == "force_config" else 0)
 
 
-def test_planner_gemv_forced_up_to_16_rows():
-    """Option gemv = 2 takes the GEMV for any eligible call (16 rows at most);
-    the planner alone stops at 8 rows."""
+def test_planner_gemv_rows_limits():
+    """Without the table the planner takes the GEMV up to 32 rows (row-major
+    B, 16-byte rows of B); option gemv = 2 takes it for any eligible call (64
+    rows on the 16x16x32 kernel; 16 with gemv_wide = 1, which leaves only the
+    4x4x4 kernel); column-major B stops at 8 rows, or 16 forced."""
     code = T.TCM_F16_F32
     T.tcm_set_option("tuned", 0)
     try:
-        assert T.tcm_plan(16, 4096, 4096, 4096, 4096, 4096, code)["kernel"] == 1
+        assert T.tcm_plan(32, 4096, 4096, 4096, 4096, 4096, code)["kernel"] == 2
+        assert T.tcm_plan(33, 4096, 4096, 4096, 4096, 4096, code)["kernel"] == 1
+        assert T.tcm_plan(9, 4096, 4096, 4096, 4096, 4096, code | T.TCM_B_COLMAJOR)["kernel"] == 1
         T.tcm_set_option("gemv", 2)
-        assert T.tcm_plan(16, 4096, 4096, 4096, 4096, 4096, code)["kernel"] == 2
+        p = T.tcm_plan(64, 4096, 4096, 4096, 4096, 4096, code)
+        assert p["kernel"] == 2 and p["bm"] == 64 and p["bn"] == 128
+        assert T.tcm_plan(65, 4096, 4096, 4096, 4096, 4096, code)["kernel"] == 1
+        assert T.tcm_plan(16, 4096, 4096, 4096, 4096, 4096, code | T.TCM_B_COLMAJOR)["kernel"] == 2
+        assert T.tcm_plan(17, 4096, 4096, 4096, 4096, 4096, code | T.TCM_B_COLMAJOR)["kernel"] == 1
+        T.tcm_set_option("gemv_wide", 1)
+        p = T.tcm_plan(16, 4096, 4096, 4096, 4096, 4096, code)
+        assert p["kernel"] == 2 and p["bn"] == 256
         assert T.tcm_plan(17, 4096, 4096, 4096, 4096, 4096, code)["kernel"] == 1
+        T.tcm_set_option("gemv_wide", 2)
+        p = T.tcm_plan(1, 4096, 4096, 4096, 4096, 4096, code)
+        assert p["kernel"] == 2 and p["bn"] == 128 and p["bm"] == 16
     finally:
         T.tcm_set_option("gemv", 0)
+        T.tcm_set_option("gemv_wide", 0)
         T.tcm_set_option("tuned", 1)
+
+
+@pytest.mark.parametrize("K,splits", [(8, 0), (1000, 0), (4096, 0), (4096, 3), (70000, 0), (70000, 7)])
+@pytest.mark.parametrize("M", [12, 24, 64])
+def test_planner_gemv_wide_k_ranges(M, K, splits):
+    """16x16x32 row-major kernel: one workgroup per CU (N = 1024: 8 column
+    blocks, 32 ranges), ranges of a multiple of 512 rows (16-row bucket) or
+    256 (32 and 64) where K allows, an asked-for count rounded to ranges of a
+    multiple of 128 rows; together they cover K."""
+    T.tcm_set_option("gemv", 2)
+    T.tcm_set_option("gemv_splits", splits)
+    try:
+        p = T.tcm_plan(M, 1024, K, -(-K // 8) * 8, 1024, 1024, T.TCM_F16_F32)
+    finally:
+        T.tcm_set_option("gemv", 0)
+        T.tcm_set_option("gemv_splits", 0)
+    kw, ranges = p["bk"], p["iters_per_tile"]
+    assert p["kernel"] == 2 and p["bn"] == 128 and p["tiles"] == 8 and p["grid"] == 8 * ranges
+    assert kw * ranges >= K and kw * (ranges - 1) < K
+    if splits:
+        assert kw == -(-(-(-K // splits)) // 128) * 128
+    else:
+        align = 512 if M <= 16 else 256
+        assert kw == -(-(-(-K // 32)) // align) * align
+    assert p["fixup_kernel"] == (ranges > 1)
+    assert p["workspace_bytes"] == (ranges * M * 1024 * 4 if ranges > 1 else 0)
 
 
 @pytest.mark.parametrize("K,splits", [(64, 1), (100, 1), (4096, 5), (70000, 0)])

@@ -16,6 +16,7 @@ pytestmark = pytest.mark.gpu
 def _reset_options():
     yield
     T.tcm_set_option("gemv", 0)
+    T.tcm_set_option("gemv_wide", 0)
     T.tcm_set_option("force_mode", 0)
     T.tcm_set_option("force_config", -1)
     T.tcm_set_option("sk_grid", 0)
@@ -145,20 +146,24 @@ def test_graph_replay_after_the_workspace_grew():
     assert status == [T.TCM_ERR_NOT_SUPPORTED]
 
 
-@pytest.mark.parametrize("b_col", [False, True])
-def test_graph_capture_replays_gemv(b_col):
-    """The split-k GEMV (two launches: the k ranges, then their sum) captured
-    into a graph after an eager call made the stream's workspace: every
-    replay gives the eager bits."""
+@pytest.mark.parametrize("form", ["b_row", "b_wide", "b_col"])
+def test_graph_capture_replays_gemv(form):
+    """The split-k GEMV kernels (two launches: the k ranges, then their sum)
+    captured into a graph after an eager call made the stream's workspace:
+    every replay gives the eager bits."""
+    b_col = form == "b_col"
     T.tcm_set_option("gemv", 2)
-    c = Call(S.small_problem(S.F16, 5, 1024, 2048, seed=405, bias=True, relu=True, b_col=b_col))
+    T.tcm_set_option("gemv_wide", 2 if form == "b_wide" else 1)
+    c = Call(S.small_problem(S.F16, 5 if form != "b_wide" else 40, 1024, 2048, seed=405, bias=True, relu=True,
+                             b_col=b_col))
     s = torch.cuda.Stream()
     c(s)
     torch.cuda.synchronize()
     eager = c.C.clone()
     c.check()
-    say(f"[case] graph capture, gemv b_col={b_col}: {T.tcm_last_plan()}")
+    say(f"[case] graph capture, gemv {form}: {T.tcm_last_plan()}")
     assert "kernel=gemv" in T.tcm_last_plan() and "fixup=kernel" in T.tcm_last_plan()
+    assert ("mfma=16x16x32" in T.tcm_last_plan()) == (form != "b_row")
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
         c(s)

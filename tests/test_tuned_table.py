@@ -67,8 +67,12 @@ def test_planner_uses_every_shipped_entry(i):
     code |= {0: 0, 1: T.TCM_C_F16, 2: T.TCM_C_BF16}[c_type]
     lda, ldb = (M if a_col else K), (K if b_col else N)
     q = T.tcm_plan(M, N, K, lda, ldb, N, code, epi, bool(aligned))
-    if config == 100:  # the split-k GEMV (the planner picks its own k ranges)
-        assert q["kernel"] == 2 and q["config"] == -1 and M <= 16, (e, q)
+    if config in (100, 101):  # a split-k GEMV kernel (the planner picks its own k ranges)
+        assert q["kernel"] == 2 and q["config"] == -1, (e, q)
+        if config == 100:  # the 4x4x4 row-major-B kernel (256 columns a workgroup) or the column-major-B one
+            assert M <= 16 and (b_col or q["bn"] == 256), (e, q)
+        else:  # the 16x16x32 row-major-B kernel
+            assert M <= 64 and not b_col and q["bn"] == 128, (e, q)
         return
     assert q["kernel"] == 1 and (q["config"], q["mode"]) == (config, mode), (e, q)
     if e[12] == 2:  # equal shares of every tile
@@ -77,4 +81,4 @@ def test_planner_uses_every_shipped_entry(i):
     q0 = T.tcm_plan(M, N, K, lda, ldb, N, code, epi, bool(aligned))
     T.tcm_set_option("tuned", 1)
     # the model's plan is a tiled one as well, or the GEMV for a few rows
-    assert q0["kernel"] == 1 or (q0["kernel"] == 2 and M <= 8)
+    assert q0["kernel"] == 1 or (q0["kernel"] == 2 and M <= 32)

@@ -81,12 +81,15 @@ def test_noalloc_matches_tcm_gemm_two_calls(dtype, case):
             check(p, g, ref)
 
 
+@pytest.mark.parametrize("shapes", [((8, 4096, 4096), (3, 1028, 1000)), ((40, 4096, 4096), (17, 2048, 1000))],
+                         ids=["both_kernels", "wide"])
 @pytest.mark.parametrize("dtype", [S.F16, S.BF16])
-def test_noalloc_gemv_two_calls(dtype):
-    """The split-k GEMV keeps its partial sums in the same array: two calls
-    in a row, the second smaller, bit-identical to tcm_gemm's."""
+def test_noalloc_gemv_two_calls(dtype, shapes):
+    """The split-k GEMV kernels keep their partial sums in the same array:
+    two calls in a row, the second smaller, bit-identical to tcm_gemm's (the
+    16x16x32 kernel then the 4x4x4 one; the 16x16x32 kernel twice)."""
     T.tcm_set_option("gemv", 2)
-    for i, (M, N, K) in enumerate(((8, 4096, 4096), (3, 1028, 1000))):
+    for i, (M, N, K) in enumerate(shapes):
         p = S.small_problem(dtype, M, N, K, seed=520 + i, bias=True, relu=(i == 1))
         say(f"[case] noalloc gemv call {i + 1}: {p.name} dtype={dtype}")
         g = S.generate(p)
