@@ -613,11 +613,13 @@ def run_all(args):
         C = make_c(p)
         s = torch.cuda.current_stream()
         modes = [0, 1, 2] if name.startswith(("skinny", "sk_")) else [0]
-        if name.startswith("skinny") and p.M <= 16:
-            modes += [3, 4]  # the split-k GEMV forced, and the tiled kernel's own plan
+        if name.startswith("skinny") and p.M <= 64:
+            # the split-k GEMV forced, the tiled kernel's own plan, and the 4x4x4 GEMV kernel
+            modes += [3, 4] + ([5] if p.M <= 16 else [])
         for mode in modes:
             T.tcm_set_option("force_mode", mode if mode <= 2 else 0)
-            T.tcm_set_option("gemv", {3: 2, 4: 1}.get(mode, 0))
+            T.tcm_set_option("gemv", {3: 2, 4: 1, 5: 2}.get(mode, 0))
+            T.tcm_set_option("gemv_wide", 1 if mode == 5 else 0)
             call = make_call(p, A, B, bias, C, s.cuda_stream)
             reset_c(p, g, C)
             call()
@@ -632,7 +634,7 @@ def run_all(args):
                 torch.cuda.synchronize()
                 par = _oracle_sampled_check(p, g, C)
             v = p.flops / (ms * 1e-3) / 1e12
-            row = {"workload": name, "mode": ["auto", "dp", "streamk", "gemv", "tiles"][mode], "ms": round(ms, 5),
+            row = {"workload": name, "mode": ["auto", "dp", "streamk", "gemv", "tiles", "gemv4x4x4"][mode], "ms": round(ms, 5),
                    "per_call_us": pc, "tflops": round(v, 2), "frac_peak": round(v / PEAK[p.dtype], 4),
                    "hbm_frac": round(p.alg_bytes / (ms * 1e-3) / (HBM_PEAK_GBS * 1e9), 4),
                    "parity_ok": par["ok"] if par else None, "plan": plan}
@@ -656,6 +658,7 @@ def run_all(args):
             rows.append(row)
         T.tcm_set_option("force_mode", 0)
         T.tcm_set_option("gemv", 0)
+        T.tcm_set_option("gemv_wide", 0)
         mine = [r for r in rows if r["workload"] == name]
         by_mode = {r["mode"]: r for r in mine}
         if "dp" in by_mode and "streamk" in by_mode:
@@ -739,7 +742,8 @@ def render_report(src, dst):
          "`block` is the average of back-to-back calls between two events, `per call` the median of calls timed one by "
          "one (it includes the launch gap).  For the split-k workloads every mode is timed: `auto` (the planner, with "
          "the shipped tuning table), `dp` (data-parallel tiles only) and `streamk`; `Stream-K lift` = dp / streamk.  "
-         "Products of at most 16 rows also run `gemv` (the split-k GEMV forced) and `tiles` (the tiled kernel's own plan); "
+         "Skinny products of at most 64 rows also run `gemv` (the split-k GEMV forced: the 16x16x32 kernel on row-major B) "
+         "and `tiles` (the tiled kernel's own plan), and up to 16 rows `gemv4x4x4` (the GEMV's 4x4x4 kernel); "
          "`GEMV lift` = tiles / gemv.  `cold` "
          "(skinny products): the median call after a 512 MiB write that evicts the MALL.  `tuned`: the same call after "
          "`tcm_tune` searched it (block time).", "",
@@ -749,7 +753,8 @@ def render_report(src, dst):
         pc = r.get("per_call_us", {}).get("median", "") if isinstance(r.get("per_call_us"), dict) else ""
         tuned = r.get("tuned", {}).get("ms")
         plan = " ".join(kv for kv in r["plan"].split() if kv.split("=")[0] in ("kernel", "config", "tile", "mode", "grid",
-                                                                                  "fixup", "group", "tuned", "splits"))
+                                                                                  "fixup", "group", "tuned", "splits",
+                                                                                  "mfma"))
         L.append(f"| {r['workload']} | {r['mode']} | {r['ms'] * 1e3:.1f} | {pc} | {r['tflops']:.1f} | "
                  f"{100 * r['frac_peak']:.1f}% | {100 * r['hbm_frac']:.1f}% | {r.get('cold_median_us', '')} | "
                  f"{r.get('streamk_lift_dp_over_sk', '')} | {r.get('gemv_lift_tiles_over_gemv', '')} | "

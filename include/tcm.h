@@ -125,12 +125,12 @@ enum { TCM_EPI_NONE = 0, TCM_EPI_BIAS = 1, TCM_EPI_RELU = 2, TCM_EPI_BIAS_RELU =
  * B N and ldb multiples of 4, with column-major B (k contiguous) K and ldb
  * multiples of 8 (up to 64 / 16 rows with option "gemv" = 2).  B streams
  * from HBM once over an even split of the k range (the Stream-K
- * reproduction post on leiblog.wang).  Row-major B from 5 rows on: 128
- * columns per workgroup, each lane transposing the 8 x 8 blocks of B it
- * loads in registers into operands of the matrix cores' 16x16x32 blocks;
- * below 5 rows (or ldb not a multiple of 8): 256 columns per workgroup in
- * 4x4x4 blocks; column-major B: 128 columns per workgroup in 16x16x32
- * blocks fed straight from memory.  The k ranges' partial sums (ranges x M
+ * reproduction post on leiblog.wang).  Row-major B: 128 columns per
+ * workgroup, each lane transposing the 8 x 8 blocks of B it loads in
+ * registers into operands of the matrix cores' 16x16x32 blocks (with ldb
+ * not a multiple of 8: 256 columns per workgroup in 4x4x4 blocks);
+ * column-major B: 128 columns per workgroup in 16x16x32 blocks fed straight
+ * from memory.  The k ranges' partial sums (ranges x M
  * x N floats of workspace) are added in range order by a second kernel on
  * the stream, which runs the epilogue.
  * Returns TCM_OK once the work is enqueued; TCM_ERR_INVALID_VALUE for
@@ -325,9 +325,9 @@ const char* tcm_status_string(int status);
  *                  row-major-B kernel, else 8, or the tuning table's
  *                  choice), 1 = never, 2 = every call it can serve (at most
  *                  64 / 16 rows) unless a tile config or mode is forced.
- *   "gemv_wide"    which GEMV kernel serves row-major B: 0 = planner
- *                  decides (16x16x32 from 5 rows on, where eligible), 1 =
- *                  never the 16x16x32 kernel, 2 = always it where eligible.
+ *   "gemv_wide"    which GEMV kernel serves row-major B: 0 or 2 = the
+ *                  16x16x32 kernel where eligible, 1 = never it (the 4x4x4
+ *                  kernel, at most 16 rows).
  *   "gemv_splits"  0 = planner decides (4x4x4 kernel: about two workgroups
  *                  per CU, the partial sums kept within an eighth of B's
  *                  bytes; 16x16x32 row-major kernel: one workgroup per CU,

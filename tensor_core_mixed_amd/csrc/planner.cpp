@@ -291,24 +291,22 @@ namespace {
 bool gemv_ok(const Problem& p, const Options& o) {
     return gemv_narrow_eligible(p) || (o.gemv_wide != 1 && gemv_wide_eligible(p));
 }
-// Row-major B: the 16x16x32 kernel from 5 rows on and where the 4x4x4 one
-// cannot serve (17 to 64 rows, N not a multiple of 4), or as option
-// gemv_wide asks.  On N = K = 4096 (f16, block of calls) the 4x4x4 kernel
-// takes 7.4 / 8.7 / 10.4 / 13.7 us at M = 1 / 4 / 8 / 12, the 16x16x32 one
-// 7.4-8.4 / 8.8 / 8.4 / 8.5 us.
-constexpr int64_t kGemvWideFrom = 5;
+// Row-major B: the 16x16x32 kernel wherever it can serve, unless option
+// gemv_wide says never; the 4x4x4 one is left for rows of B that are not
+// 16-byte aligned.  On N = K = 4096 (f16, block of calls) the 4x4x4 kernel
+// takes 7.4 / 10.3 / 14.5 us at M = 1 / 8 / 16, the 16x16x32 one 6.6 / 8.6 /
+// 8.6 us.
 bool gemv_pick_wide(const Problem& p, const Options& o) {
-    if (!gemv_wide_eligible(p) || o.gemv_wide == 1) return false;
-    return o.gemv_wide == 2 || !gemv_narrow_eligible(p) || p.M >= kGemvWideFrom;
+    return gemv_wide_eligible(p) && o.gemv_wide != 1;
 }
 }  // namespace
 
 bool gemv_eligible(const Problem& p) { return gemv_wide_eligible(p) || gemv_narrow_eligible(p); }
 
 // The GEMV beats the tiled kernel's Stream-K plans on N = K = 4096 (f16,
-// row-major B) up to 32 rows: 7.4 / 8.4 / 8.8 / 10.7 / 11.5 us at M = 1 / 8 /
-// 16 / 24 / 32 against 10.9 / 11.0 / 11.4 / 11.8 / 12.3 us; at 48 rows it
-// is slower (14.7 against 13.3 us).  Without the 16x16x32 kernel (column-
+// row-major B) up to 32 rows: 6.6 / 8.6 / 8.6 / 10.7 / 11.3 us at M = 1 / 8 /
+// 16 / 24 / 32 against 10.9 / 11.0 / 11.4 / 11.8 / 12.5 us; at 48 rows it
+// is slower (14.5 against 13.3 us).  Without the 16x16x32 kernel (column-
 // major B, rows of B not 16-byte aligned) it stops at 8 rows.
 constexpr int64_t kGemvAutoRows = 8, kGemvWideAutoRows = 32;
 bool gemv_preferred(const Problem& p, const Options& o) {

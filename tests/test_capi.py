@@ -610,10 +610,10 @@ def test_data_parallel_entries_carry_over_to_fewer_waves_only():
 def test_planner_gemv_for_few_rows(M, tuned):
     """Row-major f16 products of at most 32 rows run on a split-k GEMV, with
     or without the shipped table (whose entries for those classes name one):
-    below 5 rows the 4x4x4 kernel (256 columns a workgroup, k ranges of a
-    multiple of 64 rows), from 5 rows the 16x16x32 one (128 columns, ranges
-    of a multiple of 128 rows, one workgroup per CU without the table); k
-    ranges cover K, their partial sums (ranges x M x N floats) added by a
+    the 16x16x32 kernel (128 columns, ranges of a multiple of 128 rows, one
+    workgroup per CU without the table) or, as a table entry may say, the
+    4x4x4 one (256 columns a workgroup, k ranges of a multiple of 64 rows);
+    k ranges cover K, their partial sums (ranges x M x N floats) added by a
     second kernel."""
     T.tcm_set_option("tuned", tuned)
     try:
@@ -628,9 +628,7 @@ def test_planner_gemv_for_few_rows(M, tuned):
     assert p["bk"] * p["iters_per_tile"] >= 4096 and p["grid"] == 4096 // p["bn"] * p["iters_per_tile"]
     assert p["workspace_bytes"] == p["iters_per_tile"] * M * 4096 * 4 and p["fixup_kernel"] == 1
     if not tuned:
-        assert p["bn"] == (256 if M <= 4 else 128)
-        if M >= 5:
-            assert p["iters_per_tile"] == 8 and p["bk"] == 512
+        assert p["bn"] == 128 and p["iters_per_tile"] == 8 and p["bk"] == 512
 
 
 def test_planner_gemv_not_taken_when_ineligible():
@@ -712,13 +710,15 @@ def test_planner_gemv_wide_k_ranges(M, K, splits):
 
 @pytest.mark.parametrize("K,splits", [(64, 1), (100, 1), (4096, 5), (70000, 0)])
 def test_planner_gemv_k_ranges(K, splits):
-    """The k ranges: multiples of 64 rows, at most 1024 each, together
-    covering K; an asked-for count is rounded to that grid."""
+    """The 4x4x4 kernel's k ranges: multiples of 64 rows, at most 1024 each,
+    together covering K; an asked-for count is rounded to that grid."""
     T.tcm_set_option("gemv_splits", splits)
+    T.tcm_set_option("gemv_wide", 1)
     try:
         p = T.tcm_plan(2, 1024, K, -(-K // 8) * 8, 1024, 1024, T.TCM_BF16_F32)
     finally:
         T.tcm_set_option("gemv_splits", 0)
+        T.tcm_set_option("gemv_wide", 0)
     kw, ranges = p["bk"], p["iters_per_tile"]
     assert p["kernel"] == 2 and kw % 64 == 0 and kw <= 1024
     assert kw * ranges >= K and kw * (ranges - 1) < K
