@@ -39,7 +39,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_{name}.json")
 
 # the sources of the tiled GEMM, grouped and convolution kernels, whose launches the stored counters describe
 KERNEL_SOURCES = ("tcm_internal.h", "tile_kernel.h", "tile_instances.h", "tile_f16.hip", "tile_bf16.hip",
-                  "tile_f32.hip", "tile_i8.hip", "conv_f16.hip", "conv_bf16.hip", "conv_f32.hip", "conv_i8.hip",
+                  "tile_f32.hip", "tile_i8.hip", "tile_acol_f16.hip", "tile_acol_bf16.hip", "tile_acol_f32.hip",
+                  "tile_acol_i8.hip", "conv_f16.hip", "conv_bf16.hip", "conv_f32.hip", "conv_i8.hip",
                   "group_f16.hip", "group_bf16.hip", "group_f32.hip", "group_i8.hip")
 
 
@@ -86,6 +87,8 @@ def plan_kernels(plan):
         head = f"void tcm::tile_conv_kernel<{f['dtype']}, {f['config']}, "
     elif "group" in f:
         head = f"void tcm::tile_group_kernel<{f['dtype']}, {f['config']}, {b}, "
+    elif f.get("a_col") == "1":  # A column-major
+        head = f"void tcm::tile_gemm_acol_kernel<{f['dtype']}, {f['config']}, {b}, "
     else:
         head = f"void tcm::tile_gemm_kernel<{f['dtype']}, {f['config']}, {b}, "
     args = "(tcm::GroupArgs)" if "group" in f else "(tcm::TileArgs)"

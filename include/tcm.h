@@ -115,9 +115,11 @@ enum { TCM_EPI_NONE = 0, TCM_EPI_BIAS = 1, TCM_EPI_RELU = 2, TCM_EPI_BIAS_RELU =
  * Any alignment and any leading dimension is served (je-d.tistory.com, the
  * auto-tensorcore note: code off the matrix-core fast path is slower but
  * functionally equal): 16-byte aligned pointers with 16-byte multiple
- * layouts take the tiled fast path; anything else runs on the generic
- * kernel, which reads and writes single bytes when a pointer is not a
- * multiple of its element size.
+ * layouts take the tiled fast path, in either layout of A and of B (K, lda
+ * and ldb whole numbers of 16-byte pieces; N too with row-major B, M too
+ * with column-major A, which runs on tiles of at least 64 rows); anything
+ * else runs on the generic kernel, which reads and writes single bytes when
+ * a pointer is not a multiple of its element size.
  * Products of few rows in f16 or bf16 with row-major A run on a split-k
  * GEMV instead of the tiles when lda is a multiple of 8, every pointer
  * 16-byte aligned, and A and B lie below 2 GiB: at most 32 rows with

@@ -113,6 +113,8 @@ def _workloads():
     w["bf16_8192"] = Problem("bf16_8192", BF16, 8192, 8192, 8192, b_col=True, dist="normal", seed=2)
     # the same product with B stored row-major (k rows of n contiguous)
     w["f16_8192_brow"] = Problem("f16_8192_brow", F16, 8192, 8192, 8192, dist="normal", seed=2)
+    # A stored column-major (k columns of m contiguous: a transposed operand)
+    w["f16_4096_acol"] = Problem("f16_4096_acol", F16, 4096, 4096, 4096, a_col=True, b_col=True, dist="normal", seed=9)
     for m in (1, 16, 64, 256):
         w[f"skinny_m{m}"] = Problem(f"skinny_m{m}", F16, m, 4096, 4096, dist="uniform", seed=3)
     w["sk_1536x1536x16384"] = Problem("sk_1536x1536x16384", F16, 1536, 1536, 16384, dist="uniform", seed=3)

@@ -91,7 +91,11 @@ int tile_sk_wg_per_cu(const TileConfig& c) {
 bool tile_eligible(const Problem& p, const TileConfig& c) {
     const int es = elem_bytes(p.dtype);
     const int ce = kChunkBytes / es;
-    if (p.a_col || !p.aligned) return false;
+    if (!p.aligned) return false;
+    // column-major A (m contiguous): the GEMM kernels (not the grouped or
+    // convolution ones) of tiles of at least 64 rows, M a whole number of
+    // 16-byte pieces, as for the columns of a row-major B
+    if (p.a_col && (p.conv || p.group || c.bm < 64 || p.M % ce)) return false;
     if (p.K <= 0 || p.M <= 0 || p.N <= 0) return false;
     if (p.M >= (1LL << 31) || p.N >= (1LL << 31) || p.K >= (1LL << 31)) return false;
     if (p.lda >= (1LL << 31) || p.ldb >= (1LL << 31) || p.ldc >= (1LL << 31)) return false;
@@ -108,6 +112,8 @@ bool tile_eligible(const Problem& p, const TileConfig& c) {
         if (p.conv_c % bk_elems(p.dtype)) return false;
         if (p.conv_x_bytes >= kOffsetLimit) return false;
         if (p.M + c.bm >= (1LL << 31)) return false;
+    } else if (p.a_col) {
+        if ((int64_t)bk_elems(p.dtype) * p.lda * es + (int64_t)c.bm * es >= kOffsetLimit) return false;
     } else if ((int64_t)c.bm * p.lda * es + kStepBytes >= kOffsetLimit) {
         return false;
     }

@@ -26,6 +26,10 @@ TileLauncher tile_launcher_f16(int config, bool b_kmajor);
 TileLauncher tile_launcher_bf16(int config, bool b_kmajor);
 TileLauncher tile_launcher_f32(int config, bool b_kmajor);
 TileLauncher tile_launcher_i8(int config, bool b_kmajor);
+TileLauncher tile_acol_launcher_f16(int config, bool b_kmajor);
+TileLauncher tile_acol_launcher_bf16(int config, bool b_kmajor);
+TileLauncher tile_acol_launcher_f32(int config, bool b_kmajor);
+TileLauncher tile_acol_launcher_i8(int config, bool b_kmajor);
 int tile_sk_occupancy_f16(int config, bool b_kmajor);
 int tile_sk_occupancy_bf16(int config, bool b_kmajor);
 int tile_sk_occupancy_f32(int config, bool b_kmajor);
@@ -84,7 +88,16 @@ int tile_sk_occupancy(int config, int dtype, bool b_kmajor) {
     }
 }
 
-TileLauncher tile_launcher(int config, int dtype, bool b_kmajor) {
+TileLauncher tile_launcher(int config, int dtype, bool b_kmajor, bool a_mmajor) {
+    if (a_mmajor) {
+        switch (dtype) {
+        case F16: return tile_acol_launcher_f16(config, b_kmajor);
+        case BF16: return tile_acol_launcher_bf16(config, b_kmajor);
+        case F32: return tile_acol_launcher_f32(config, b_kmajor);
+        case I8: return tile_acol_launcher_i8(config, b_kmajor);
+        default: return nullptr;
+        }
+    }
     switch (dtype) {
     case F16: return tile_launcher_f16(config, b_kmajor);
     case BF16: return tile_launcher_bf16(config, b_kmajor);
@@ -447,11 +460,11 @@ std::string describe(const Plan& pl, const Problem& p) {
     } else {
         snprintf(buf, sizeof buf,
                  "kernel=%s config=%d tile=%dx%dx%d mode=%s grid=%d tiles=%lld iters=%lld dp_tiles=%lld sk_tiles=%lld "
-                 "M=%lld N=%lld K=%lld dtype=%d b_col=%d batch=%lld est_cycles=%.0f%s",
+                 "M=%lld N=%lld K=%lld dtype=%d b_col=%d batch=%lld est_cycles=%.0f%s%s",
                  p.conv ? "conv" : "tile", pl.config, pl.bm, pl.bn, pl.bk, pl.mode == 1 ? "dp" : "streamk", pl.grid, (long long)pl.tiles,
                  (long long)pl.iters, (long long)pl.dp_tiles, (long long)pl.sk_tiles, (long long)p.M, (long long)p.N,
                  (long long)p.K, p.dtype, (int)p.b_col, (long long)p.batch, pl.est_cycles,
-                 pl.fixup_kernel ? " fixup=kernel" : "");
+                 pl.fixup_kernel ? " fixup=kernel" : "", p.a_col ? " a_col=1" : "");
     }
     return buf;
 }
@@ -873,7 +886,7 @@ int launch_tiled(const Problem& p, const Plan& pl, TileArgs& a, int dev, void* s
         a.ws_partial = (float*)w.partial;
         a.ws_counter = w.counters;
     }
-    TileLauncher launch = p.conv ? conv_launcher(pl.config, p.dtype) : tile_launcher(pl.config, p.dtype, p.b_col);
+    TileLauncher launch = p.conv ? conv_launcher(pl.config, p.dtype) : tile_launcher(pl.config, p.dtype, p.b_col, p.a_col);
     if (!launch) return TCM_ERR_NOT_SUPPORTED;
     return launch(a, stream) == 0 ? TCM_OK : TCM_ERR_HIP;
 }
@@ -1066,7 +1079,7 @@ int grouped_impl(int64_t count, const tcm_group_entry* ent, int64_t K, int dtype
     }
     for (int c = 0; c < kNumConfigs; ++c) {
         int64_t tiles = 0;
-        bool ok = aligned;
+        bool ok = aligned && !p.a_col;  // the grouped kernels stage k-contiguous A only
         for (int64_t i = 0; i < count && ok; ++i) {
             if (ent[i].M == 0 || ent[i].N == 0) continue;
             Problem q = pe[i];

@@ -205,8 +205,8 @@ using TileLauncher = int (*)(const TileArgs&, void* stream);
 using GroupLauncher = int (*)(const GroupArgs&, void* stream);
 // the grouped kernels: config index, dtype, B column-major -> launcher
 GroupLauncher group_launcher(int config, int dtype, bool b_kmajor);
-// config index, dtype, B column-major (K-contiguous) -> launcher, or nullptr
-TileLauncher tile_launcher(int config, int dtype, bool b_kmajor);
+// config index, dtype, B column-major (K-contiguous), A column-major (M-contiguous) -> launcher, or nullptr
+TileLauncher tile_launcher(int config, int dtype, bool b_kmajor, bool a_mmajor);
 // the implicit-GEMM convolution kernels (B = the KRSC filter, k-contiguous)
 TileLauncher conv_launcher(int config, int dtype);
 // Stream-K workgroups of a config that fit on one CU, from the compiled

@@ -35,6 +35,20 @@ int pick_sk_occupancy(int config, bool b_kmajor) {
     }
 }
 
+// column-major A: the configs of at least 64 rows (the transposing reads of
+// an m-contiguous tile are laid out for 4 to 64 chunks a k row)
+template <int DT>
+TileLauncher pick_tile_acol(int config, bool b_kmajor) {
+    switch (config) {
+    case 0: return b_kmajor ? &launch_tile_acol<DT, 0, true> : &launch_tile_acol<DT, 0, false>;
+    case 1: return b_kmajor ? &launch_tile_acol<DT, 1, true> : &launch_tile_acol<DT, 1, false>;
+    case 3: return b_kmajor ? &launch_tile_acol<DT, 3, true> : &launch_tile_acol<DT, 3, false>;
+    case 4: return b_kmajor ? &launch_tile_acol<DT, 4, true> : &launch_tile_acol<DT, 4, false>;
+    case 5: return b_kmajor ? &launch_tile_acol<DT, 5, true> : &launch_tile_acol<DT, 5, false>;
+    default: return nullptr;
+    }
+}
+
 template <int DT>
 TileLauncher pick_conv(int config) {
     switch (config) {
@@ -83,6 +97,11 @@ GroupLauncher pick_group(int config, bool b_kmajor) {
     namespace tcm {                                                                                    \
     TileLauncher tile_launcher_##NAME(int config, bool b_kmajor) { return pick_tile<DT>(config, b_kmajor); } \
     int tile_sk_occupancy_##NAME(int config, bool b_kmajor) { return pick_sk_occupancy<DT>(config, b_kmajor); } \
+    }
+
+#define TCM_TILE_ACOL_TU(DT, NAME)                                                                          \
+    namespace tcm {                                                                                         \
+    TileLauncher tile_acol_launcher_##NAME(int config, bool b_kmajor) { return pick_tile_acol<DT>(config, b_kmajor); } \
     }
 
 #define TCM_CONV_TU(DT, NAME)                                                                     \

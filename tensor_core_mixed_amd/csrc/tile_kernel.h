@@ -111,7 +111,9 @@ __device__ __forceinline__ int swz_mn(int k) {
     return s & (CPR - 1);
 }
 
-template <int DT, int CFG, bool B_KMAJ, bool CONV = false, int NST = 2>
+// A_MMAJ: A stored column-major (m contiguous), staged as [k][m] tiles and
+// read with the transposing fragment reads of an n-contiguous B.
+template <int DT, int CFG, bool B_KMAJ, bool CONV = false, int NST = 2, bool A_MMAJ = false>
 struct TileKernel {
     static constexpr TileConfig cfg = kConfigs[CFG];
     static constexpr int BM = cfg.bm, BN = cfg.bn, WM = cfg.wm, WN = cfg.wn;
@@ -134,7 +136,10 @@ struct TileKernel {
     static constexpr int IA = BM / (8 * NWC);        // DMA instructions per copier wave per stage (A)
     static constexpr int IB = BN / (8 * NWC);        // (B)
     static constexpr int B_CPR = BN * ES / kChunkBytes;  // chunks per [k] row of an n-contiguous B tile
+    static constexpr int A_CPR = BM * ES / kChunkBytes;  // chunks per [k] row of an m-contiguous A tile
     static_assert((B_CPR & (B_CPR - 1)) == 0, "chunk count per row must be a power of two");
+    static_assert(!A_MMAJ || ((A_CPR & (A_CPR - 1)) == 0 && A_CPR >= 4 && A_CPR <= 64 && !CONV),
+                  "m-contiguous A: a power-of-two chunk count per row, 4 to 64");
     static_assert(BM % (8 * NWC) == 0 && BN % (8 * NWC) == 0, "tile rows must fill whole wave DMA instructions");
     static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32x32");
     static_assert(LDS <= 160 * 1024, "LDS budget of one CU");
@@ -150,12 +155,14 @@ struct TileKernel {
     // through j's parity and its row advances by ADV rows every two
     // instructions, so a lane keeps two offsets per operand and adds a
     // uniform stride.  Rows outside the matrix (m >= M, n >= N for
-    // k-contiguous operands; k >= K for n-contiguous B) lie past the end of
-    // the step's buffer range and read as zeros; columns n >= N of an
-    // n-contiguous B are folded into the offsets; the k tail of k-contiguous
-    // operands is one select per parity.
+    // k-contiguous operands; k >= K for m/n-contiguous ones) lie past the end
+    // of the step's buffer range and read as zeros; rows m >= M of an
+    // m-contiguous A and columns n >= N of an n-contiguous B are folded into
+    // the offsets; the k tail of k-contiguous operands is one select per
+    // parity.
+    static constexpr int A_RPI = A_MMAJ ? 64 / A_CPR : 8;  // rows per instruction of the A tile
     static constexpr int B_RPI = B_KMAJ ? 8 : 64 / B_CPR;  // rows per instruction of the B tile
-    static constexpr int A_ADV = 2 * NWC * 8;
+    static constexpr int A_ADV = 2 * NWC * A_RPI;
     static constexpr int B_ADV = 2 * NWC * B_RPI;
 
     struct Dma {
@@ -186,7 +193,11 @@ struct TileKernel {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const int p = (q * NWC + wave) * 64 + lane;
-            {
+            if constexpr (A_MMAJ) {
+                const int kr = p / A_CPR, c = (p % A_CPR) ^ swz_mn<DT, A_CPR>(kr);
+                d.a_off[q] = m0 + c * CE < a.M ? (unsigned)(kr * a.lda + c * CE) * ES : kOOB;
+                d.a_k[q] = 0;
+            } else {
                 const int r = p >> 3, c = (p & 7) ^ swz_k(r);
                 d.a_off[q] = (unsigned)(r * a.lda + c * CE) * ES;
                 d.a_k[q] = c * CE;
@@ -238,10 +249,21 @@ struct TileKernel {
                                                          16, off, 0, 0, 0);
             }
         } else {
-            const char* base = (const char*)a.A + ((int64_t)m0 * a.lda + k0) * ES;
-            const int nrec = clamp_range(((int64_t)(a.M - m0) * a.lda - k0) * ES);
+            const char* base;
+            int nrec;
+            unsigned o0, o1;
+            if constexpr (A_MMAJ) {
+                base = (const char*)a.A + ((int64_t)k0 * a.lda + m0) * ES;
+                nrec = clamp_range(((int64_t)krem * a.lda - m0) * ES);
+                o0 = d.a_off[0];
+                o1 = d.a_off[1];
+            } else {
+                base = (const char*)a.A + ((int64_t)m0 * a.lda + k0) * ES;
+                nrec = clamp_range(((int64_t)(a.M - m0) * a.lda - k0) * ES);
+                o0 = d.a_k[0] < krem ? d.a_off[0] : kOOB;
+                o1 = d.a_k[1] < krem ? d.a_off[1] : kOOB;
+            }
             const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, nrec, kRsrcWord3);
-            const unsigned o0 = d.a_k[0] < krem ? d.a_off[0] : kOOB, o1 = d.a_k[1] < krem ? d.a_off[1] : kOOB;
             const unsigned hop = (unsigned)(A_ADV * a.lda * ES);
             lds_char* la = smem + st * STAGE;
 #pragma unroll
@@ -289,10 +311,12 @@ struct TileKernel {
         int c = 2 * sub + h;
         return lds_read16<i4_t>(lb + row * kStepBytes + ((c ^ swz_k(row)) << 4));
     }
-    // B fragment from an n-contiguous [k][n] tile: the lane's column n and
-    // the 8 (f16/bf16) or 16 (int8) k-values of chunk c = 2*sub + h.
-    __device__ __forceinline__ static i4_t load_b_mn(const lds_char* lb, int ncol0, int sub, int lane) {
-        constexpr int RB = BN * ES;  // bytes per k row
+    // Fragment from an m- or n-contiguous [k][x] tile of RB bytes per k row
+    // and CPR chunks (A column-major, B row-major): the lane's row or
+    // column x (the MFMA's A and B operands share one lane layout) and the 8
+    // (f16/bf16) or 16 (int8) k-values of chunk c = 2*sub + h.
+    template <int RB, int CPR>
+    __device__ __forceinline__ static i4_t load_mn(const lds_char* lb, int ncol0, int sub, int lane) {
         const int g = lane >> 4, t = lane & 15, h = g >> 1;
         const int c = 2 * sub + h;
         i4_t out;
@@ -301,7 +325,7 @@ struct TileKernel {
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int k = 16 * c + 8 * q + (t >> 1);
-                const lds_char* p = lb + k * RB + (((n >> 4) ^ swz_mn<DT, B_CPR>(k)) << 4) + (n & 15);
+                const lds_char* p = lb + k * RB + (((n >> 4) ^ swz_mn<DT, CPR>(k)) << 4) + (n & 15);
                 i2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i2_t*)p);
                 out[2 * q] = v[0];
                 out[2 * q + 1] = v[1];
@@ -311,7 +335,7 @@ struct TileKernel {
 #pragma unroll
             for (int q = 0; q < 2; ++q) {
                 const int k = 8 * c + 4 * q + (t >> 2);
-                const lds_char* p = lb + k * RB + (((n >> 3) ^ swz_mn<DT, B_CPR>(k)) << 4) + ((n & 7) << 1);
+                const lds_char* p = lb + k * RB + (((n >> 3) ^ swz_mn<DT, CPR>(k)) << 4) + ((n & 7) << 1);
                 s4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4_t*)p);
                 i2_t w = __builtin_bit_cast(i2_t, v);
                 out[2 * q] = w[0];
@@ -320,11 +344,30 @@ struct TileKernel {
         }
         return out;
     }
-    // f32, n-contiguous B: single k-value e of chunk-substep sub.
-    __device__ __forceinline__ static float load_b_mn_f32(const lds_char* lb, int n, int sub, int h, int e) {
-        constexpr int RB = BN * ES;
+    __device__ __forceinline__ static i4_t load_b_mn(const lds_char* lb, int ncol0, int sub, int lane) {
+        return load_mn<BN * ES, B_CPR>(lb, ncol0, sub, lane);
+    }
+    // f32, m- or n-contiguous tile: single k-value e of chunk-substep sub.
+    template <int RB, int CPR>
+    __device__ __forceinline__ static float load_mn_f32(const lds_char* lb, int n, int sub, int h, int e) {
         const int k = 8 * sub + 4 * h + e;
-        return *(const __attribute__((address_space(3))) float*)(lb + k * RB + (((n >> 2) ^ swz_mn<DT, B_CPR>(k)) << 4) + ((n & 3) << 2));
+        return *(const __attribute__((address_space(3))) float*)(lb + k * RB + (((n >> 2) ^ swz_mn<DT, CPR>(k)) << 4) + ((n & 3) << 2));
+    }
+    __device__ __forceinline__ static float load_b_mn_f32(const lds_char* lb, int n, int sub, int h, int e) {
+        return load_mn_f32<BN * ES, B_CPR>(lb, n, sub, h, e);
+    }
+    // A fragment of 32 rows from row mrow0 of the wave's block, either layout
+    __device__ __forceinline__ static i4_t load_a_any(const lds_char* la, int mrow0, int sub, int lane) {
+        if constexpr (!A_MMAJ) {
+            return load_a(la, mrow0 + (lane & 31), sub, lane >> 5);
+        } else if constexpr (DT == F32) {
+            f4_t v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = load_mn_f32<BM * ES, A_CPR>(la, mrow0 + (lane & 31), sub, lane >> 5, e);
+            return __builtin_bit_cast(i4_t, v);
+        } else {
+            return load_mn<BM * ES, A_CPR>(la, mrow0, sub, lane);
+        }
     }
 
     // ------------------------------------------------------------- MFMA
@@ -353,7 +396,7 @@ struct TileKernel {
         const lds_char* lb = la + A_BYTES;
         const int h = lane >> 5, l32 = lane & 31;
         // issue order = first use by the MFMA sequence: a0, b0..b(FN-1), a1..a(FM-1)
-        f.a[0] = load_a(la, wm * TM + l32, sub, h);
+        f.a[0] = load_a_any(la, wm * TM, sub, lane);
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) {
             if constexpr (B_KMAJ) {
@@ -368,7 +411,7 @@ struct TileKernel {
             }
         }
 #pragma unroll
-        for (int fm = 1; fm < FM; ++fm) f.a[fm] = load_a(la, wm * TM + fm * 32 + l32, sub, h);
+        for (int fm = 1; fm < FM; ++fm) f.a[fm] = load_a_any(la, wm * TM + fm * 32, sub, lane);
     }
 
     __device__ __forceinline__ static void mma_frag(Acc (&acc)[FM][FN], const Frag& f) {
@@ -689,7 +732,8 @@ struct TileKernel {
     // Interleave the next sub-step's 8 fragment reads with this sub-step's
     // 16 MFMAs (one read between each pair).
     static constexpr int NMF = FM * FN * (DT == F32 ? 4 : 1);              // MFMAs per sub-step
-    static constexpr int NRD = FM + FN * ((DT == F32 && !B_KMAJ) ? 4 : (B_KMAJ ? 1 : 2));  // LDS reads per sub-step
+    static constexpr int NRD = FM * ((DT == F32 && A_MMAJ) ? 4 : (A_MMAJ ? 2 : 1)) +
+                               FN * ((DT == F32 && !B_KMAJ) ? 4 : (B_KMAJ ? 1 : 2));  // LDS reads per sub-step
     __device__ __forceinline__ static void sched_reads() {
 #pragma unroll
         for (int i = 0; i < NMF; ++i) {
@@ -1073,6 +1117,29 @@ int launch_tile(const TileArgs& a, void* stream) {
         hipLaunchKernelGGL((tile_gemm_kernel<DT, CFG, B_KMAJ, false>), dim3(a.dp_tiles), dim3(TileThreads<CFG>::value), 0, s, a);
     if (a.sk_tiles > 0)
         hipLaunchKernelGGL((tile_gemm_kernel<DT, CFG, B_KMAJ, true>), dim3(a.grid), dim3(TileThreads<CFG>::value), 0, s, a);
+    if (a.sk_tiles > 0 && a.sk_fixup_kernel)
+        hipLaunchKernelGGL((tile_fixup_kernel<DT, CFG, B_KMAJ>), dim3(a.sk_tiles), dim3(TileThreads<CFG>::value), 0, s, a);
+    return (int)hipGetLastError();
+}
+
+// Column-major A (m contiguous): the same kernels with A staged as [k][m]
+// tiles.  Split tiles are summed by tile_fixup_kernel, which reads only the
+// partials.
+template <int DT, int CFG, bool B_KMAJ, bool SK>
+__global__ __launch_bounds__(TileThreads<CFG>::value) __attribute__((amdgpu_waves_per_eu(TileWaves<CFG, SK>::value)))
+void tile_gemm_acol_kernel(TileArgs a) {
+    if constexpr (SK) TileKernel<DT, CFG, B_KMAJ, false, kConfigs[CFG].sk_stages, true>::run_sk(a);
+    else TileKernel<DT, CFG, B_KMAJ, false, 2, true>::run_dp(a);
+}
+
+template <int DT, int CFG, bool B_KMAJ>
+int launch_tile_acol(const TileArgs& a, void* stream) {
+    hipStream_t s = (hipStream_t)stream;
+    if (a.dp_tiles > 0)
+        hipLaunchKernelGGL((tile_gemm_acol_kernel<DT, CFG, B_KMAJ, false>), dim3(a.dp_tiles), dim3(TileThreads<CFG>::value), 0, s,
+                           a);
+    if (a.sk_tiles > 0)
+        hipLaunchKernelGGL((tile_gemm_acol_kernel<DT, CFG, B_KMAJ, true>), dim3(a.grid), dim3(TileThreads<CFG>::value), 0, s, a);
     if (a.sk_tiles > 0 && a.sk_fixup_kernel)
         hipLaunchKernelGGL((tile_fixup_kernel<DT, CFG, B_KMAJ>), dim3(a.sk_tiles), dim3(TileThreads<CFG>::value), 0, s, a);
     return (int)hipGetLastError();

@@ -35,6 +35,10 @@ def test_plan_kernels_names_the_launched_kernels():
     conv = HYBRID_PLAN.replace("kernel=tile", "kernel=conv").replace("b_col=0", "b_col=1")
     assert bench.plan_kernels(conv) == {"void tcm::tile_conv_kernel<0, 1, false>(tcm::TileArgs)",
                                         "void tcm::tile_conv_kernel<0, 1, true>(tcm::TileArgs)"}
+    acol = HYBRID_PLAN + " fixup=kernel a_col=1"
+    assert bench.plan_kernels(acol) == {"void tcm::tile_gemm_acol_kernel<0, 1, false, false>(tcm::TileArgs)",
+                                        "void tcm::tile_gemm_acol_kernel<0, 1, false, true>(tcm::TileArgs)",
+                                        "void tcm::tile_fixup_kernel<0, 1, false>(tcm::TileArgs)"}
     group = HYBRID_PLAN + " group=8"
     assert bench.plan_kernels(group) == {"void tcm::tile_group_kernel<0, 1, false, false>(tcm::GroupArgs)",
                                          "void tcm::tile_group_kernel<0, 1, false, true>(tcm::GroupArgs)"}
@@ -51,8 +55,12 @@ def test_gemv_counters_are_keyed_to_the_gemv_sources():
     assert bench.kernel_source_hash(bench.GEMV_SOURCES) != bench.kernel_source_hash()
     t = json.load(open(os.path.join(ROOT, "profiles", "traffic_skinny_m1.json")))
     if "gemv" in (t.get("dominant_kernel") or ""):
-        plan = ("kernel=gemv rows=1 cols_per_wg=256 k_per_wg=128 splits=32 grid=512 M=1 N=4096 K=4096 dtype=0 b_col=0 "
-                "fixup=kernel")
+        if "gemv_r_kernel" in t["dominant_kernel"]:  # the 16x16x32 kernel's plan
+            plan = ("kernel=gemv rows=16 cols_per_wg=128 k_per_wg=512 splits=8 grid=256 M=1 N=4096 K=4096 dtype=0 "
+                    "b_col=0 mfma=16x16x32 fixup=kernel")
+        else:
+            plan = ("kernel=gemv rows=1 cols_per_wg=256 k_per_wg=128 splits=32 grid=512 M=1 N=4096 K=4096 dtype=0 "
+                    "b_col=0 mfma=4x4x4 fixup=kernel")
         got = bench.load_traffic(S.workload("skinny_m1"), plan)
         if t["source_hash"] == bench.kernel_source_hash(bench.GEMV_SOURCES):
             assert got == t["hbm_bytes_per_launch"]

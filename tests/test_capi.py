@@ -504,6 +504,29 @@ def _conv(**kw):
                         a["bias"] or None, a["epilogue"], None)
 
 
+def test_planner_column_major_a():
+    """Column-major A (m contiguous) runs on the tiles of at least 64 rows when
+    M and lda are whole numbers of 16-byte pieces (the split-k GEMV and the
+    32-row configs take row-major A only); otherwise the generic kernel."""
+    code = T.TCM_F16_F32 | T.TCM_A_COLMAJOR
+    p = T.tcm_plan(4096, 4096, 4096, 4096, 4096, 4096, code | T.TCM_B_COLMAJOR)
+    assert p["kernel"] == 1 and (p["bm"], p["bn"]) == (256, 256)
+    p = T.tcm_plan(16, 4096, 4096, 16, 4096, 4096, code)
+    assert p["kernel"] == 1 and p["bm"] >= 64
+    assert T.tcm_plan(1000, 1000, 512, 1000, 1000, 1000, code)["kernel"] == 1
+    assert T.tcm_plan(1004, 1000, 512, 1004, 1000, 1000, code)["kernel"] == 0  # M % 8 != 0
+    assert T.tcm_plan(1000, 1000, 512, 1004, 1000, 1000, code)["kernel"] == 0  # lda % 8 != 0
+    assert T.tcm_plan(1024, 1024, 1024, 1024, 1024, 1024, T.TCM_I8_I32 | T.TCM_A_COLMAJOR)["kernel"] == 1
+    assert T.tcm_plan(1000, 1024, 1024, 1000, 1024, 1024, T.TCM_I8_I32 | T.TCM_A_COLMAJOR)["kernel"] == 0  # 1000 % 16
+    for cfg in (2, 6):  # 32-row tiles: not for column-major A
+        T.tcm_set_option("force_config", cfg)
+        try:
+            q = T.tcm_plan(64, 4096, 4096, 64, 4096, 4096, code)
+        finally:
+            T.tcm_set_option("force_config", -1)
+        assert q["kernel"] != 1 or q["config"] != cfg
+
+
 BAD_CONV = [
     dict(N=-1), dict(H=-1), dict(C=-1), dict(K=-1), dict(R=0), dict(S=0),  # negative / empty filter
     dict(pad_h=-1), dict(stride_w=0), dict(dil_h=0),

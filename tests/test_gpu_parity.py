@@ -84,6 +84,54 @@ def test_every_config_and_mode(dtype, config, mode):
     check(p, g, C)
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("config", [0, 1, 3, 4, 5])
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("b_col", [False, True])
+def test_column_major_a_every_config_and_mode(dtype, config, mode, b_col):
+    """A stored column-major (m contiguous) on the tiles: each config of at
+    least 64 rows, data-parallel and Stream-K, both B layouts, on a shape
+    with edges in M (208: a partial tile of every height), N and K, bias and
+    ReLU, and A's columns padded (lda past M)."""
+    ce = {S.F16: 8, S.BF16: 8, S.F32: 4, S.I8: 16}[dtype]
+    p = S.small_problem(dtype, 208, 304, 53 * ce, seed=config * 10 + mode + 3, a_col=True, b_col=b_col, bias=True,
+                        relu=(mode == 2), lda=208 + ce)
+    T.tcm_set_option("force_config", config)
+    T.tcm_set_option("force_mode", mode)
+    g, C, plan = _run(p)
+    assert "kernel=tile" in plan and f"config={config}" in plan
+    assert ("mode=dp" if mode == 1 else "mode=streamk") in plan
+    check(p, g, C)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shape", [(512, 512, 512), (64, 520, 136), (1024, 96, 392), (16, 4096, 1024)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("b_col", [False, True])
+def test_column_major_a_planned(dtype, shape, b_col):
+    """The planner's own plan for column-major A: the tiles (M is a whole
+    number of 16-byte pieces here), with ragged N and a K tail."""
+    M, N, K = shape
+    ce = {S.F16: 8, S.BF16: 8, S.F32: 4, S.I8: 16}[dtype]
+    K = max(ce, K // ce * ce)
+    if not b_col:
+        N = max(ce, N // ce * ce)
+    p = S.small_problem(dtype, M, N, K, seed=sum(shape) % 97, a_col=True, b_col=b_col, bias=True, relu=True)
+    g, C, plan = _run(p)
+    assert "kernel=tile" in plan, plan
+    check(p, g, C)
+
+
+@pytest.mark.parametrize("dtype", [S.F16, S.I8])
+def test_column_major_a_off_the_piece_grid_is_generic(dtype):
+    """M not a whole number of 16-byte pieces: the generic kernel, correct."""
+    ce = {S.F16: 8, S.I8: 16}[dtype]
+    p = S.small_problem(dtype, 4 * ce + 1, 256, 8 * ce, seed=41, a_col=True, b_col=True, bias=True)
+    g, C, plan = _run(p)
+    assert "kernel=generic" in plan
+    check(p, g, C)
+
+
 @pytest.mark.parametrize("dtype", [S.F16, S.BF16])
 @pytest.mark.parametrize("ksteps", [1, 2, 3, 33])
 @pytest.mark.parametrize("mode", [1, 2])
