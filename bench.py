@@ -847,7 +847,8 @@ def summarize_counters(d, name, calib=None):
     # per kernel (a Stream-K plan launches a data-parallel and a Stream-K kernel): medians per dispatch
     import synthetic as S
     kpat = ("tile_conv_kernel" if name in S.CONV_WORKLOADS else
-            "tile_group_kernel" if name in S.GROUP_WORKLOADS else "tile_gemm_kernel")
+            "tile_group_kernel" if name in S.GROUP_WORKLOADS else
+            "tile_gemm_acol_kernel" if S.workload(name).a_col else "tile_gemm_kernel")
     fetch = per_kernel(d, "fetch", "FETCH_SIZE", kpat)
     write = per_kernel(d, "write", "WRITE_SIZE", kpat)
     if not fetch:  # a product the split-k GEMV serves
