@@ -1,0 +1,102 @@
+"""Seeded random parity sweep through tcm_gemm: element type, both layouts of
+A and B, shapes on and off the 16-byte piece grid (so that the tiled kernel,
+the split-k GEMV and the generic kernel all take part), padded leading
+dimensions, every epilogue flag, 16-bit outputs, and now and then a forced
+tile config, mode or Stream-K grid.  Each case is drawn from its own seed,
+printed before it touches the GPU, and compared with the oracle on every
+entry (C's padding columns must keep their fill)."""
+import numpy as np
+import pytest
+
+import synthetic as S
+import tensor_core_mixed_amd as T
+from gpu_util import check, check_padding_untouched, run_tcm, say
+
+pytestmark = pytest.mark.gpu
+
+CE = {S.F16: 8, S.BF16: 8, S.F32: 4, S.I8: 16}  # elements per 16-byte piece
+N_CASES = 320
+
+
+@pytest.fixture(autouse=True)
+def _reset_options():
+    yield
+    for k, v in (("force_mode", 0), ("force_config", -1), ("sk_grid", 0), ("sk_fixup", 0), ("gemv", 0),
+                 ("gemv_wide", 0)):
+        T.tcm_set_option(k, v)
+
+
+def _dim(rng, lo, hi, ce, on_grid):
+    x = int(rng.integers(lo, hi + 1))
+    return max(ce, x // ce * ce) if on_grid else x
+
+
+def draw(seed):
+    """Case `seed`: the problem and the options it runs under."""
+    rng = np.random.default_rng(9000 + seed)
+    dtype = [S.F16, S.BF16, S.F32, S.I8][int(rng.integers(4))]
+    ce = CE[dtype]
+    on_grid = rng.random() < 0.75  # most cases can take the tiles
+    a_col, b_col = bool(rng.integers(2)), bool(rng.integers(2))
+    small_m = rng.random() < 0.3
+    M = _dim(rng, 1, 40, ce, on_grid and a_col) if small_m else _dim(rng, 1, 600, ce, on_grid and a_col)
+    N = _dim(rng, 1, 600, ce, on_grid and not b_col)
+    K = _dim(rng, 1, 1100, ce, on_grid)
+    pad = lambda: int(rng.integers(0, 3)) * ce if rng.random() < 0.5 else 0
+    lda = (M if a_col else K) + pad()
+    ldb = (K if b_col else N) + pad()
+    ldc = N + pad()
+    bias, relu = bool(rng.integers(2)), bool(rng.integers(2))
+    c_type = "acc" if dtype in (S.I8, S.F32) else ["acc", "f16", "bf16"][int(rng.integers(3))]
+    if c_type == "bf16" and dtype == S.F16:
+        c_type = "f16"
+    if c_type == "f16" and dtype == S.BF16:
+        c_type = "bf16"
+    accum = rng.random() < 0.25
+    p = S.small_problem(dtype, M, N, K, seed=300 + seed, a_col=a_col, b_col=b_col, bias=bias, relu=relu, lda=lda,
+                        ldb=ldb, ldc=ldc, c_type=c_type, accum=accum)
+    opts = {}
+    r = rng.random()
+    if r < 0.2:
+        opts["force_mode"] = int(rng.integers(1, 3))
+    elif r < 0.35:
+        opts["force_mode"] = 2
+        opts["sk_grid"] = int(rng.integers(1, 400))
+        opts["sk_fixup"] = int(rng.integers(0, 3))
+    elif r < 0.45:
+        opts["force_config"] = int(rng.integers(0, T.tcm_config_count()))
+    return p, opts
+
+
+@pytest.mark.parametrize("seed", range(N_CASES))
+def test_random_case(seed):
+    p, opts = draw(seed)
+    for k, v in opts.items():
+        assert T.tcm_set_option(k, v) == T.TCM_OK
+    say(f"[case] random {seed}: {p.name} dtype={p.dtype} M={p.M} N={p.N} K={p.K} a_col={p.a_col} b_col={p.b_col} "
+        f"lda={p.LDA} ldb={p.LDB} ldc={p.LDC} bias={p.bias} relu={p.relu} c={p.c_type} accum={p.accum} opts={opts}")
+    g = S.generate(p)
+    C, plan = run_tcm(p, g)
+    say(f"       plan: {plan}")
+    check(p, g, C)
+    if p.c_type == "acc" and not p.accum:
+        check_padding_untouched(p, C, -7 if p.dtype == S.I8 else float("nan"))
+
+
+def test_random_cases_reach_every_kernel():
+    """The drawn set plans the tiled kernel (both A layouts), the split-k
+    GEMV and the generic kernel (checked on the CPU with tcm_plan)."""
+    kinds = set()
+    for seed in range(N_CASES):
+        p, opts = draw(seed)
+        code = p.dtype | (T.TCM_A_COLMAJOR if p.a_col else 0) | (T.TCM_B_COLMAJOR if p.b_col else 0)
+        code |= {"acc": 0, "f16": T.TCM_C_F16, "bf16": T.TCM_C_BF16}[p.c_type]
+        for k, v in opts.items():
+            T.tcm_set_option(k, v)
+        try:
+            q = T.tcm_plan(p.M, p.N, p.K, p.LDA, p.LDB, p.LDC, code)
+        finally:
+            for k, v in (("force_mode", 0), ("force_config", -1), ("sk_grid", 0), ("sk_fixup", 0)):
+                T.tcm_set_option(k, v)
+        kinds.add((q["kernel"], p.a_col if q["kernel"] == 1 else None))
+    assert {(0, None), (1, False), (1, True), (2, None)} <= kinds, kinds
