@@ -118,6 +118,21 @@ def test_batched_every_config_and_mode(dtype, config, mode):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("config", [1, 4])
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("b_col", [False, True])
+def test_batched_column_major_a(dtype, config, mode, b_col):
+    """Column-major A on the tiles across a batch: each entry's A at its own
+    stride, Stream-K segments crossing entries."""
+    T.tcm_set_option("force_config", config)
+    T.tcm_set_option("force_mode", mode)
+    p = S.small_problem(dtype, 80, 144, 208, seed=99 + config, a_col=True, b_col=b_col, bias=True, relu=True, batch=3)
+    g, C, plan = _case(p)
+    assert "kernel=tile" in plan and f"config={config}" in plan and "a_col=1" in plan
+    check_batch(p, g, C)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_batched_shared_b_and_bias(dtype):
     """Stride 0 shares B (and the bias) across the batch."""
     p = S.small_problem(dtype, 33, 80, 96, seed=95, bias=True, batch=5, b_shared=True, b_col=True)
