@@ -1,10 +1,12 @@
-"""Seeded random parity sweep through tcm_gemm: element type, both layouts of
-A and B, shapes on and off the 16-byte piece grid (so that the tiled kernel,
-the split-k GEMV and the generic kernel all take part), padded leading
-dimensions, every epilogue flag, 16-bit outputs, and now and then a forced
-tile config, mode or Stream-K grid.  Each case is drawn from its own seed,
-printed before it touches the GPU, and compared with the oracle on every
-entry (C's padding columns must keep their fill)."""
+"""Seeded random parity sweep through tcm_gemm and tcm_gemm_batched: element
+type, both layouts of A and B, shapes on and off the 16-byte piece grid (so
+that the tiled kernel, the split-k GEMV and the generic kernel all take
+part), padded leading dimensions, every epilogue flag, 16-bit outputs, and
+now and then a forced tile config, mode or Stream-K grid; batches of 2 to 5
+entries (B shared or not) at padded strides.  Each case is drawn from its
+own seed, printed before it touches the GPU, and compared with the oracle
+on every entry (C's padding columns, and the gaps between batch entries,
+must keep their fill)."""
 import numpy as np
 import pytest
 
@@ -100,3 +102,40 @@ def test_random_cases_reach_every_kernel():
                 T.tcm_set_option(k, v)
         kinds.add((q["kernel"], p.a_col if q["kernel"] == 1 else None))
     assert {(0, None), (1, False), (1, True), (2, None)} <= kinds, kinds
+
+
+N_BATCHED = 64
+
+
+def draw_batched(seed):
+    """Batched case `seed`: a drawn problem of a few entries (own or shared B)
+    and the entries' padding (16-byte multiples keep the tiles eligible)."""
+    p, opts = draw(5000 + seed)
+    rng = np.random.default_rng(19000 + seed)
+    batch = int(rng.integers(2, 6))
+    b_shared = rng.random() < 0.25
+    from dataclasses import replace
+    p = replace(p, batch=batch, b_shared=b_shared, M=min(p.M, 300), K=min(p.K, 600))
+    if p.a_col:
+        p = replace(p, lda=max(p.LDA, p.M) if p.lda else 0)
+    else:
+        p = replace(p, lda=max(p.LDA, p.K) if p.lda else 0)
+    if p.b_col:
+        p = replace(p, ldb=max(p.LDB, p.K) if p.ldb else 0)
+    pads = tuple(int(x) for x in rng.integers(0, 4, 3) * 64)
+    return p, opts, pads
+
+
+@pytest.mark.parametrize("seed", range(N_BATCHED))
+def test_random_batched_case(seed):
+    from test_gpu_batched import check_batch, run_batched
+    p, opts, pads = draw_batched(seed)
+    for k, v in opts.items():
+        assert T.tcm_set_option(k, v) == T.TCM_OK
+    say(f"[case] random batched {seed}: {p.name} dtype={p.dtype} batch={p.batch} b_shared={p.b_shared} M={p.M} N={p.N} "
+        f"K={p.K} a_col={p.a_col} b_col={p.b_col} lda={p.LDA} ldb={p.LDB} ldc={p.LDC} bias={p.bias} relu={p.relu} "
+        f"c={p.c_type} accum={p.accum} pads={pads} opts={opts}")
+    g = S.generate(p)
+    C, plan = run_batched(p, g, pads=pads)
+    say(f"       plan: {plan}")
+    check_batch(p, g, C)
