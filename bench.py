@@ -83,6 +83,10 @@ def plan_kernels(plan):
     if f.get("kernel") not in ("tile", "conv"):
         return set()
     b = "true" if f.get("b_col") == "1" else "false"
+    if int(f.get("split", 0)) > 1:  # equal shares of every tile, then the wave-per-block sum
+        a = "true" if f.get("a_col") == "1" else "false"
+        return {f"void tcm::tile_split_kernel<{f['dtype']}, {f['config']}, {b}, {a}>(tcm::TileArgs)",
+                f"void tcm::tile_split_fixup_kernel<{f['dtype']}, {f['config']}>(tcm::TileArgs)"}
     if f["kernel"] == "conv":
         head = f"void tcm::tile_conv_kernel<{f['dtype']}, {f['config']}, "
     elif "group" in f:

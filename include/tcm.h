@@ -299,7 +299,11 @@ const char* tcm_status_string(int status);
  * tcm_set_option / tcm_get_option -- process-wide tuning switches, for
  * experiments and tests.  Keys:
  *   "force_mode"   0 = planner decides, 1 = data-parallel tiles only,
- *                  2 = split-k (Stream-K) over a persistent grid.
+ *                  2 = split-k (Stream-K) over a persistent grid; on the
+ *                  eight-wave 256x256 config (tile-table row 0), unless
+ *                  "sk_grid" or "grid_per_cu8" is given, as equal shares:
+ *                  every tile cut into at most 8 k ranges of equal length,
+ *                  one workgroup each, summed by a second kernel.
  *   "force_config" -1 = planner decides, else an index into the tile table
  *                  (tcm_config_count()); a config that cannot serve the call
  *                  is ignored.
@@ -311,14 +315,16 @@ const char* tcm_status_string(int status);
  *                  or more segments), 1 = its last-arriving workgroup sums
  *                  the partials, 2 = a second kernel launched on the same
  *                  stream sums them.  Both add the partials in the same
- *                  order: the results are bit-identical.
+ *                  order: the results are bit-identical.  Equal shares are
+ *                  always summed by the second kernel.
  *   "group_m"      0 = planner decides (4), else the rows of tiles per group
  *                  of the tile order (1..16).
  *   "grid_per_cu8" 0 = planner decides, else a split-k grid of value/8
  *                  workgroups per CU (1..64).
  *   "grid_shares"  0 = planner decides, else a split-k grid of value
  *                  workgroups per tile (1..64): every split tile in equal
- *                  shares that start at the same k.
+ *                  shares that start at the same k (the equal shares of the
+ *                  eight-wave config: at most 8, each at least one K-step).
  *   "tuned"        1 (default) = use the tuning table (tcm_tune) for problems
  *                  whose class it holds; 0 = ignore it.  force_config /
  *                  force_mode / sk_grid / gemv win.
@@ -363,7 +369,9 @@ typedef struct {
     int64_t sk_tiles;      /* tiles whose k range is split over workgroups */
     int64_t workspace_bytes; /* split-k workspace the call needs */
     int32_t fixup_kernel;  /* 1 = split tiles are summed by a second kernel on the stream */
-    int32_t reserved;      /* 0 */
+    int32_t split;         /* > 1: Stream-K as equal shares, every split tile cut
+                              into this many k ranges of equal length, one
+                              workgroup each (grid = sk_tiles * split); else 0 */
 } tcm_plan_info;
 
 /*

@@ -35,7 +35,7 @@ class _PlanInfo(ctypes.Structure):
                 ("bn", ctypes.c_int32), ("bk", ctypes.c_int32), ("mode", ctypes.c_int32), ("grid", ctypes.c_int32),
                 ("tiles", ctypes.c_int64), ("iters_per_tile", ctypes.c_int64), ("dp_tiles", ctypes.c_int64),
                 ("sk_tiles", ctypes.c_int64), ("workspace_bytes", ctypes.c_int64),
-                ("fixup_kernel", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("fixup_kernel", ctypes.c_int32), ("split", ctypes.c_int32)]
 
 
 class GroupEntry(ctypes.Structure):

@@ -54,6 +54,10 @@ constexpr double kStaggerBytesPerClk = 14.6;
 // short-K products such as 768^3 .. 1536^3, where split segments are a few
 // K-steps long).
 constexpr double kSplitFixed = 9600.0;
+// Equal shares of the eight-wave tile: the sum kernel's launch and its one
+// memory round trip.
+constexpr double kSplitSum = 6000.0;
+constexpr int kEpiAccumBit = 4;  // the epilogue flag that reads C_in (C read as well as written)
 constexpr double kMallBytesPerClk = 16.0e12 / 2.4e9;
 constexpr double kMallBytes = 128.0 * 1024 * 1024;
 
@@ -142,6 +146,7 @@ struct Estimate {
     int mode;
     int grid;
     int64_t dp_tiles, sk_tiles;
+    int split = 0;  // equal shares of every tile (the eight-wave config's Stream-K)
 };
 
 // Tiles of the work list for config ci.
@@ -261,11 +266,39 @@ Estimate estimate(const Problem& p, int ci, int cus, int force_mode, int sk_grid
         sk.dp_tiles = dp_tiles;
         sk.sk_tiles = sk_tiles;
     }
+    // Equal shares (the eight-wave config): its persistent Stream-K kernel
+    // runs out of registers (the partial-tile sum on top of 128 accumulators
+    // a wave) and spills inside the main loop, so its Stream-K is the split
+    // aligned to whole tiles: each of the T tiles in S equal k shares, one
+    // workgroup each, on the data-parallel loop, every share storing its
+    // partial tile and a second kernel summing them.  S fills the co-resident
+    // slots (at most kMaxSplit shares, each at least one K-step) unless the
+    // equal-shares option gives it; a forced grid keeps the persistent kernel.
+    // All shares store their partials at once at the end, and the sum reads
+    // them back: both at HBM rate.  Single products only, as for aligned
+    // Stream-K grids.
+    Estimate sp{1e300, 2, 0, 0, 0};
+    if (split_config(ci) && !p.group && !p.conv && p.batch <= 1 && sk_grid <= 0 && grid_per_cu8 <= 0) {
+        int64_t S = grid_shares > 0 ? grid_shares : slots / std::max<int64_t>(T, 1);
+        S = std::min<int64_t>(std::min<int64_t>(S, kMaxSplit), I);
+        if (S >= 2) {
+            const int64_t per = cdiv(I, S);
+            const int64_t busy = std::min<int64_t>(T * S, slots);
+            const double share = (double)std::min<int64_t>(occ, cdiv(busy, cus));
+            const double partials = (double)T * S * c.bm * c.bn * 4;
+            const double c_bytes = (double)p.M * p.N * c_elem_bytes(p.c_type) * ((p.epilogue & kEpiAccumBit) ? 2 : 1);
+            sp.cycles = std::max(cdiv(T * S, slots) * per * std::max(step * share, lone_step) +
+                                     (2 * partials + c_bytes) / kHbmBytesPerClk + kSplitSum,
+                                 hbm_floor);
+            sp.grid = (int)(T * S);
+            sp.dp_tiles = 0;
+            sp.sk_tiles = T;
+            sp.split = (int)S;
+        }
+    }
     if (force_mode == 1) return dp;
-    if (force_mode == 2) return sk;
-    // the 8-wave 256x256 config runs out of registers in its Stream-K variant
-    // (partial-tile fix-up on top of 128 accumulators per wave): data-parallel only
-    if (c.wm * c.wn > 4) return dp;
+    if (force_mode == 2) return sp.split ? sp : sk;
+    if (split_config(ci)) return sp.cycles < 0.97 * dp.cycles ? sp : dp;
     // the 32-row deep unit exists for its Stream-K pipeline (as data-parallel
     // tiles it is no faster than 64x64 ones on the products it may serve)
     if (c.bm < 64 && c.sk_stages > 2) return sk;
@@ -478,6 +511,15 @@ bool make_plan(const Problem& p, const Options& o, int cus, Plan* out) {
         pl.sk_tiles = best_e.sk_tiles;
         pl.ws_partial_bytes = 2LL * pl.grid * c.bm * c.bn * 4;
         pl.ws_counters = pl.sk_tiles;
+        if (best_e.split > 1) {  // equal shares: one partial a workgroup, summed by the second kernel
+            pl.split = best_e.split;
+            pl.ws_partial_bytes = (int64_t)pl.grid * c.bm * c.bn * 4;
+            pl.ws_counters = 0;
+            pl.fixup_kernel = true;
+            pl.group_m = o.group_m > 0 ? o.group_m : 4;
+            *out = pl;
+            return true;
+        }
         // Split tiles cut into many short segments are summed by a second
         // kernel: the segments then store their partials and end, instead
         // of waiting for the stores, counting their arrival and having the

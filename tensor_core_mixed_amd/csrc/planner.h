@@ -64,6 +64,7 @@ struct Plan {
     int64_t ws_partial_bytes = 0, ws_counters = 0;
     int group_m = 4;
     bool fixup_kernel = false;  // Stream-K split tiles summed by a second kernel
+    int split = 0;    // > 1: Stream-K as that many equal shares of every tile on the data-parallel loop
     double est_cycles = 0;  // the cost model's estimate (for logs)
 };
 

@@ -460,11 +460,12 @@ std::string describe(const Plan& pl, const Problem& p) {
     } else {
         snprintf(buf, sizeof buf,
                  "kernel=%s config=%d tile=%dx%dx%d mode=%s grid=%d tiles=%lld iters=%lld dp_tiles=%lld sk_tiles=%lld "
-                 "M=%lld N=%lld K=%lld dtype=%d b_col=%d batch=%lld est_cycles=%.0f%s%s",
+                 "M=%lld N=%lld K=%lld dtype=%d b_col=%d batch=%lld est_cycles=%.0f%s%s%s",
                  p.conv ? "conv" : "tile", pl.config, pl.bm, pl.bn, pl.bk, pl.mode == 1 ? "dp" : "streamk", pl.grid, (long long)pl.tiles,
                  (long long)pl.iters, (long long)pl.dp_tiles, (long long)pl.sk_tiles, (long long)p.M, (long long)p.N,
                  (long long)p.K, p.dtype, (int)p.b_col, (long long)p.batch, pl.est_cycles,
-                 pl.fixup_kernel ? " fixup=kernel" : "", p.a_col ? " a_col=1" : "");
+                 pl.fixup_kernel ? " fixup=kernel" : "", p.a_col ? " a_col=1" : "",
+                 pl.split > 1 ? (" split=" + std::to_string(pl.split)).c_str() : "");
     }
     return buf;
 }
@@ -625,7 +626,7 @@ int tcm_plan_batched(int64_t batch, int64_t M, int64_t N, int64_t K, int64_t lda
     out->sk_tiles = pl.sk_tiles;
     out->workspace_bytes = pl.ws_partial_bytes + pl.ws_counters * (int64_t)sizeof(int);
     out->fixup_kernel = pl.fixup_kernel ? 1 : 0;
-    out->reserved = 0;
+    out->split = pl.split > 1 ? pl.split : 0;
     return TCM_OK;
 }
 
@@ -869,6 +870,7 @@ int launch_tiled(const Problem& p, const Plan& pl, TileArgs& a, int dev, void* s
     a.ws_partial = nullptr;
     a.ws_counter = nullptr;
     a.sk_fixup_kernel = pl.fixup_kernel ? 1 : 0;
+    a.split = pl.split;
     if (pl.mode == 2 && pl.sk_tiles > 0 && noalloc) {
         char* base = nullptr;
         int st = scratch_of(dev, &base);

@@ -32,6 +32,8 @@ struct TileConfig {
     const char* name;
 };
 constexpr int kNumConfigs = 7;
+// Equal shares of a tile (TileArgs::split): at most this many per tile.
+constexpr int kMaxSplit = 8;
 constexpr TileConfig kConfigs[kNumConfigs] = {
     {256, 256, 4, 2, 2, "256x256 w4x2"},     // big square problems: 64x128 per wave, two waves per SIMD
     {128, 128, 2, 2, 2, "128x128 w2x2"},     // mid sizes, 2 workgroups per CU
@@ -43,6 +45,10 @@ constexpr TileConfig kConfigs[kNumConfigs] = {
     {32, 64, 1, 2, 6, "32x64 w1x2 deep"},    // skinny M (M <= 32): six Stream-K stages of 12 KiB, two workgroups
                                              // per CU, most of a short segment's copies in flight at once
 };
+// Configs whose Stream-K plans run as equal shares of every tile on the
+// data-parallel loop (TileArgs::split): the eight-wave tile, whose
+// persistent Stream-K kernel has no registers for the partial-tile sum.
+constexpr bool split_config(int ci) { return kConfigs[ci].wm * kConfigs[ci].wn > 4; }
 inline int lds_bytes(const TileConfig& c, bool sk = false) { return (sk ? c.sk_stages : 2) * (c.bm + c.bn) * kStepBytes; }
 
 // Arguments of the tiled MFMA kernel.  Sizes are in elements, strides of the
@@ -73,6 +79,11 @@ struct TileArgs {
     float* ws_partial;    // Stream-K partial tiles: 2 slots per workgroup, bm*bn 4-byte values each
     int* ws_counter;      // one arrival counter per split tile (zero between launches)
     int sk_fixup_kernel;  // 1: split tiles are summed by a second kernel, not by their last arrival
+    // Equal shares (eight-wave config): > 1 cuts every one of the sk_tiles
+    // tiles into `split` k ranges of equal length, one per workgroup of a
+    // grid of sk_tiles * split, each run on the data-parallel loop and stored
+    // as a partial tile (slot s * sk_tiles + t); a second kernel sums them.
+    int split;
     // Implicit-GEMM convolution (kernels built with CONV only): A is the
     // im2col view of an NHWC input x: row m = output pixel (n, p, q), column
     // k = (r*S + s)*C + c.  C is a multiple of the K-step, so every K-step

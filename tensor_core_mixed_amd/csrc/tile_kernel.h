@@ -1067,6 +1067,103 @@ struct TileKernel {
         }
         store_tile(acc, e, m0, n0, wm, wn, lane);
     }
+
+    // Equal shares (a.split = S > 1): the k-iterations of each of the T
+    // tiles are cut into S ranges [s*I/S, (s+1)*I/S), one per workgroup, and
+    // each range runs on the data-parallel loop (the Stream-K split of the
+    // whole work evenly over the grid, aligned to whole shares of tiles).
+    // Workgroup ids are renumbered by XCD over the T*S (share, tile) pairs,
+    // shares outermost: an XCD runs neighbouring tiles' same share, whose
+    // operand panels sit at the same k and stream through its L2 together.
+    // Share 0 carries the initial value (bias, C_in); every share stores its
+    // partial tile at slot s*T + t.
+    template <class Args>
+    __device__ __forceinline__ static void run_split(const Args& g) {
+        const TileArgs& a = base_args(g);
+        __shared__ __attribute__((aligned(1024))) char smem_raw[LDS];
+        lds_char* smem = (lds_char*)smem_raw;
+        const int tid = threadIdx.x, lane = tid & 63;
+        const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+        const int wm = wave / WN, wn = wave % WN;
+        const int T = a.sk_tiles, S = a.split;
+        const int n = xcd_order(blockIdx.x, T * S);
+        const int s = n / T, t = n - s * T;
+        Acc acc[FM][FN];
+        int tm, tn;
+        const TileArgs e = tile_of(g, t, tm, tn);
+        const int m0 = tm * BM, n0 = tn * BN;
+        const int k_lo = (int)((int64_t)s * e.iters / S), k_hi = (int)((int64_t)(s + 1) * e.iters / S);
+        init_acc<true>(acc, e, smem, s == 0, m0, n0, wm, wn, lane);
+        mainloop(acc, e, smem, m0, n0, k_lo, k_hi, wave, lane);
+        store_partial(acc, partial_rsrc(a, s * T + t), wave, wm, lane, e.M - m0);
+    }
+
+    // Sum of an equal-shares launch: one wave per 32x32 accumulator block of
+    // a tile (workgroup b: tile b / (NW*FM*FN), then wave slot, fm, fn).  It
+    // issues the loads of all S partials of its block at once (one memory
+    // round trip), adds them in share order and stores the block with the
+    // epilogue.  (One workgroup per tile, as the Stream-K fix-up has, waits
+    // on a round trip per share with a few hundred kilobytes in flight.)
+    __device__ __forceinline__ static void run_split_fixup(const TileArgs& a) {
+        const int lane = threadIdx.x;
+        const int T = a.sk_tiles, S = a.split;
+        int b = blockIdx.x;
+        const int fn = b % FN;
+        b /= FN;
+        const int fm = b % FM;
+        b /= FM;
+        const int wave = b % NW, t = b / NW;
+        const int wm = wave / WN, wn = wave % WN;
+        int tm, tn;
+        const TileArgs e = tile_of(a, t, tm, tn);
+        const int m0 = tm * BM, n0 = tn * BN, mrem = e.M - m0;
+        i4_t p[kMaxSplit][4];
+#pragma unroll
+        for (int s = 0; s < kMaxSplit; ++s)
+            if (s < S) {
+                const __amdgpu_buffer_rsrc_t r = partial_rsrc(a, s * T + t);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    p[s][q] = __builtin_amdgcn_raw_buffer_load_b128(r, partial_off(wave, fm, fn, q, lane, wm, mrem), 0, kCoherent);
+            }
+        Acc acc = {};
+#pragma unroll
+        for (int s = 0; s < kMaxSplit; ++s)
+            if (s < S) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if constexpr (DT == I8) {
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) acc[4 * q + x] = s == 0 ? p[s][q][x] : acc[4 * q + x] + p[s][q][x];
+                    } else {
+                        const f4_t fv = __builtin_bit_cast(f4_t, p[s][q]);
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) acc[4 * q + x] = s == 0 ? fv[x] : acc[4 * q + x] + fv[x];
+                    }
+                }
+            }
+        const CView cv = c_view(e, m0, n0, wm, wn, lane);
+        unsigned coff = kOOB;  // this lane's column offset in block column fn (a select, not an indexed register array)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+            if (j == fn) coff = cv.coff[j];
+        if constexpr (DT != I8) {
+            if (e.c_type == C_F16) return store_block<C_F16>(acc, e, cv, coff, fm);
+            if (e.c_type == C_BF16) return store_block<C_BF16>(acc, e, cv, coff, fm);
+        }
+        store_block<C_ACC>(acc, e, cv, coff, fm);
+    }
+    // one 32x32 accumulator block (rows of fragment fm, the lane's column at coff), with ReLU
+    template <int CT>
+    __device__ __forceinline__ static void store_block(const Acc& acc, const TileArgs& a, const CView& cv, unsigned coff, int fm) {
+        const bool relu = a.relu;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            AccS v = acc[r];
+            if (relu) v = v > (AccS)0 ? v : (AccS)0;
+            store_c<CT>(cv, coff + c_roff(a, cv, fm, r), v);
+        }
+    }
 };
 
 template <int CFG>
@@ -1110,9 +1207,39 @@ __global__ __launch_bounds__(TileThreads<CFG>::value) void tile_fixup_kernel(Til
     TileKernel<DT, CFG, B_KMAJ, false, kConfigs[CFG].sk_stages>::run_fixup(a);
 }
 
+// Equal shares (TileArgs::split > 1, the eight-wave config): the shares on
+// the data-parallel loop, then the wave-per-block sum.
+template <int DT, int CFG, bool B_KMAJ, bool A_MMAJ>
+__global__ __launch_bounds__(TileThreads<CFG>::value) __attribute__((amdgpu_waves_per_eu(TileWaves<CFG, false>::value)))
+void tile_split_kernel(TileArgs a) {
+    TileKernel<DT, CFG, B_KMAJ, false, 2, A_MMAJ>::run_split(a);
+}
+
+// (the sum reads partial tiles and writes C: B's layout plays no part)
+template <int DT, int CFG>
+__global__ __launch_bounds__(64) void tile_split_fixup_kernel(TileArgs a) {
+    TileKernel<DT, CFG, true>::run_split_fixup(a);
+}
+
+// Launches an equal-shares plan; returns -1 if this config has no such
+// kernels (the planner gives equal shares to the eight-wave config only).
+template <int DT, int CFG, bool B_KMAJ, bool A_MMAJ>
+int launch_split(const TileArgs& a, hipStream_t s) {
+    if constexpr (split_config(CFG)) {
+        using K = TileKernel<DT, CFG, true>;
+        hipLaunchKernelGGL((tile_split_kernel<DT, CFG, B_KMAJ, A_MMAJ>), dim3(a.sk_tiles * a.split), dim3(TileThreads<CFG>::value),
+                           0, s, a);
+        hipLaunchKernelGGL((tile_split_fixup_kernel<DT, CFG>), dim3(a.sk_tiles * K::NW * K::FM * K::FN), dim3(64), 0, s, a);
+        return (int)hipGetLastError();
+    } else {
+        return -1;
+    }
+}
+
 template <int DT, int CFG, bool B_KMAJ>
 int launch_tile(const TileArgs& a, void* stream) {
     hipStream_t s = (hipStream_t)stream;
+    if (a.split > 1) return launch_split<DT, CFG, B_KMAJ, false>(a, s);
     if (a.dp_tiles > 0)
         hipLaunchKernelGGL((tile_gemm_kernel<DT, CFG, B_KMAJ, false>), dim3(a.dp_tiles), dim3(TileThreads<CFG>::value), 0, s, a);
     if (a.sk_tiles > 0)
@@ -1135,6 +1262,7 @@ void tile_gemm_acol_kernel(TileArgs a) {
 template <int DT, int CFG, bool B_KMAJ>
 int launch_tile_acol(const TileArgs& a, void* stream) {
     hipStream_t s = (hipStream_t)stream;
+    if (a.split > 1) return launch_split<DT, CFG, B_KMAJ, true>(a, s);
     if (a.dp_tiles > 0)
         hipLaunchKernelGGL((tile_gemm_acol_kernel<DT, CFG, B_KMAJ, false>), dim3(a.dp_tiles), dim3(TileThreads<CFG>::value), 0, s,
                            a);

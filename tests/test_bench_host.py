@@ -39,6 +39,11 @@ def test_plan_kernels_names_the_launched_kernels():
     assert bench.plan_kernels(acol) == {"void tcm::tile_gemm_acol_kernel<0, 1, false, false>(tcm::TileArgs)",
                                         "void tcm::tile_gemm_acol_kernel<0, 1, false, true>(tcm::TileArgs)",
                                         "void tcm::tile_fixup_kernel<0, 1, false>(tcm::TileArgs)"}
+    split = SK_PLAN.replace("config=4", "config=0").replace("grid=768", "grid=252") + " fixup=kernel split=7"
+    assert bench.plan_kernels(split) == {"void tcm::tile_split_kernel<0, 0, false, false>(tcm::TileArgs)",
+                                         "void tcm::tile_split_fixup_kernel<0, 0>(tcm::TileArgs)"}
+    assert bench.plan_kernels(split + " a_col=1") == {"void tcm::tile_split_kernel<0, 0, false, true>(tcm::TileArgs)",
+                                                      "void tcm::tile_split_fixup_kernel<0, 0>(tcm::TileArgs)"}
     group = HYBRID_PLAN + " group=8"
     assert bench.plan_kernels(group) == {"void tcm::tile_group_kernel<0, 1, false, false>(tcm::GroupArgs)",
                                          "void tcm::tile_group_kernel<0, 1, false, true>(tcm::GroupArgs)"}

@@ -159,22 +159,25 @@ def test_planner_skinny_uses_streamk(M, tiles_only):
     assert p["config"] in (5, 6) and p["bm"] <= 64 and p["bn"] == 64
 
 
-@pytest.mark.parametrize("M,N,K,fixup", [(1, 4096, 4096, 1), (16, 4096, 4096, 1), (64, 4096, 4096, None),
-                                         (256, 4096, 4096, None), (1536, 1536, 16384, 0)])
-def test_planner_fixup_kernel_for_many_segments(M, N, K, fixup, tiles_only):
+@pytest.mark.parametrize("M,N,K,fixup,config", [(1, 4096, 4096, 1, -1), (16, 4096, 4096, 1, -1), (64, 4096, 4096, None, -1),
+                                                (256, 4096, 4096, None, -1), (1536, 1536, 16384, 0, 1)])
+def test_planner_fixup_kernel_for_many_segments(M, N, K, fixup, config, tiles_only):
     """Split tiles with five or more segments are summed by a second kernel;
-    with fewer, by their last arrival.  The option overrides either way."""
-    p = T.tcm_plan(M, N, K, K, N, N, T.TCM_F16_F32)
-    per_wg = -(-p["sk_tiles"] * p["iters_per_tile"] // p["grid"])
-    assert p["mode"] == 2 and p["fixup_kernel"] == int(p["iters_per_tile"] >= 5 * per_wg)
-    if fixup is not None:
-        assert p["fixup_kernel"] == fixup
+    with fewer, by their last arrival.  The option overrides either way.
+    (1536^2 x 16384 on 128x128 units: three aligned shares a tile.)"""
+    T.tcm_set_option("force_config", config)
     try:
+        p = T.tcm_plan(M, N, K, K, N, N, T.TCM_F16_F32)
+        per_wg = -(-p["sk_tiles"] * p["iters_per_tile"] // p["grid"])
+        assert p["mode"] == 2 and p["split"] == 0 and p["fixup_kernel"] == int(p["iters_per_tile"] >= 5 * per_wg)
+        if fixup is not None:
+            assert p["fixup_kernel"] == fixup
         for opt, want in ((1, 0), (2, 1)):
             assert T.tcm_set_option("sk_fixup", opt) == T.TCM_OK
             assert T.tcm_plan(M, N, K, K, N, N, T.TCM_F16_F32)["fixup_kernel"] == want
     finally:
         T.tcm_set_option("sk_fixup", 0)
+        T.tcm_set_option("force_config", -1)
     # data-parallel plans have nothing to sum
     assert T.tcm_plan(8192, 8192, 8192, 8192, 8192, 8192, T.TCM_F16_F32 | T.TCM_B_COLMAJOR)["fixup_kernel"] == 0
 
@@ -183,16 +186,65 @@ def test_streamk_grid_aligned_to_the_tiles():
     """When the tiles fit the co-resident grid two or more times over, the
     Stream-K grid is an exact multiple of the tile count (every tile's shares
     start at the same k); otherwise it is the co-resident grid."""
-    p = T.tcm_plan(1536, 1536, 16384, 16384, 1536, 1536, T.TCM_F16_F32)
-    assert p["mode"] == 2 and (p["bm"], p["bn"]) == (128, 128)
-    assert p["sk_tiles"] == 144 and p["grid"] == 432  # 144 x 3 of 512 slots
-    p = T.tcm_plan(2048, 2048, 8192, 8192, 2048, 2048, T.TCM_F16_F32)
-    assert p["mode"] == 2 and p["grid"] % p["sk_tiles"] == 0
     try:
+        T.tcm_set_option("force_config", 1)
+        p = T.tcm_plan(1536, 1536, 16384, 16384, 1536, 1536, T.TCM_F16_F32)
+        assert p["mode"] == 2 and (p["bm"], p["bn"]) == (128, 128) and p["split"] == 0
+        assert p["sk_tiles"] == 144 and p["grid"] == 432  # 144 x 3 of 512 slots
+        p = T.tcm_plan(2048, 2048, 8192, 8192, 2048, 2048, T.TCM_F16_F32)
+        assert p["mode"] == 2 and p["grid"] % p["sk_tiles"] == 0
+        T.tcm_set_option("force_config", -1)
         T.tcm_set_option("sk_grid", 500)  # an explicit grid is kept
-        assert T.tcm_plan(1536, 1536, 16384, 16384, 1536, 1536, T.TCM_F16_F32)["grid"] == 500
+        p = T.tcm_plan(1536, 1536, 16384, 16384, 1536, 1536, T.TCM_F16_F32)
+        assert p["grid"] == 500 and p["split"] == 0
     finally:
         T.tcm_set_option("sk_grid", 0)
+        T.tcm_set_option("force_config", -1)
+
+
+@pytest.fixture
+def model_only():
+    """Plans from the cost model alone (the shipped tuning table ignored)."""
+    T.tcm_set_option("tuned", 0)
+    yield
+    T.tcm_set_option("tuned", 1)
+    for k, v in (("force_config", -1), ("force_mode", 0), ("grid_shares", 0), ("sk_grid", 0), ("grid_per_cu8", 0)):
+        T.tcm_set_option(k, v)
+
+
+def test_equal_shares_of_the_eight_wave_tile(model_only):
+    """The eight-wave 256x256 config's Stream-K is equal shares: every tile cut
+    into S k ranges (S fills the 256 CUs, at most 8, each share at least one
+    K-step), grid T x S, one partial tile a workgroup (no arrival counters),
+    always summed by the second kernel."""
+    p = T.tcm_plan(1536, 1536, 16384, 16384, 1536, 1536, T.TCM_F16_F32)  # 36 tiles: 7 shares fill 252 CUs
+    assert (p["config"], p["mode"], p["sk_tiles"], p["split"], p["grid"]) == (0, 2, 36, 7, 252)
+    assert p["dp_tiles"] == 0 and p["fixup_kernel"] == 1
+    assert p["workspace_bytes"] == 252 * 256 * 256 * 4
+    T.tcm_set_option("force_config", 0)
+    T.tcm_set_option("force_mode", 2)
+    for M, N, K, dt, want in ((256, 256, 16384, T.TCM_F16_F32, 8),      # one tile: at most 8 shares
+                              (256, 256, 192, T.TCM_F16_F32, 3),        # three K-steps: three shares
+                              (512, 1024, 4096, T.TCM_I8_I32, 8),       # int8: 128-element K-steps
+                              (2048, 2048, 8192, T.TCM_BF16_F32, 4),    # 64 tiles x 4
+                              (1024, 8192, 8192, T.TCM_F16_F32, 2)):    # 128 tiles x 2
+        p = T.tcm_plan(M, N, K, K, N, N, dt)
+        assert p["split"] == want and p["grid"] == p["sk_tiles"] * want, (M, N, K, p)
+    T.tcm_set_option("grid_shares", 3)  # the equal-shares option gives S
+    p = T.tcm_plan(1536, 1536, 16384, 16384, 1536, 1536, T.TCM_F16_F32)
+    assert (p["split"], p["grid"], p["workspace_bytes"]) == (3, 108, 108 * 256 * 256 * 4)
+    T.tcm_set_option("grid_shares", 0)
+    # a given grid keeps the persistent Stream-K kernel
+    T.tcm_set_option("sk_grid", 200)
+    p = T.tcm_plan(1536, 1536, 16384, 16384, 1536, 1536, T.TCM_F16_F32)
+    assert p["config"] == 0 and p["mode"] == 2 and p["split"] == 0 and p["grid"] == 200
+    T.tcm_set_option("sk_grid", 0)
+    # tiles that fill half the CUs or more: no second share, the persistent kernel
+    p = T.tcm_plan(3840, 3840, 4096, 4096, 3840, 3840, T.TCM_F16_F32)
+    assert p["config"] == 0 and p["mode"] == 2 and p["split"] == 0
+    # batches keep the persistent grid (entries share no operand panel)
+    p = T.tcm_plan_batched(2, 1536, 1536, 16384, 16384, 1536, 1536, T.TCM_F16_F32)
+    assert p["split"] == 0
 
 
 def test_forced_streamk_skips_the_eight_wave_config():

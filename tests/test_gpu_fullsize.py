@@ -60,6 +60,17 @@ def test_splitk_sweep_both_modes(name, mode):
     assert ("mode=dp" if mode == 1 else "mode=streamk") in plan
 
 
+def test_equal_shares_full_size():
+    """1536^2 x 16384 as equal shares of the eight-wave 256x256 tile: 36 tiles
+    in 7 shares of 36-37 K-steps on 252 workgroups, sampled entries."""
+    T.tcm_set_option("force_config", 0)
+    try:
+        C, plan = _check_workload("sk_1536x1536x16384", 2)
+    finally:
+        T.tcm_set_option("force_config", -1)
+    assert "config=0" in plan and "split=7" in plan and "grid=252" in plan
+
+
 def test_int8_full_rows_bit_exact():
     """int8 4096^3 with bias + ReLU: 64 complete rows bit-exact (plus the sampled entries above)."""
     p = S.workload("i8_4096")

@@ -26,6 +26,7 @@ def _reset_options():
     T.tcm_set_option("sk_grid", 0)
     T.tcm_set_option("generic", 0)
     T.tcm_set_option("sk_fixup", 0)
+    T.tcm_set_option("grid_shares", 0)
 
 
 def _run(p, **kw):
@@ -211,6 +212,79 @@ def test_int8_and_float_dp_vs_streamk_agree(dtype):
     assert np.array_equal(C_sk1, C_sk2), "Stream-K result differs between runs"
     if dtype == S.I8:
         assert np.array_equal(C_dp, C_sk1), "int8 data-parallel and Stream-K differ"
+
+
+# ------------------------------------------- equal shares (the eight-wave tile's Stream-K)
+
+BK = {S.F16: 64, S.BF16: 64, S.F32: 32, S.I8: 128}  # elements of one K-step
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("shares", [2, 3, 5, 8])
+@pytest.mark.parametrize("b_col", [False, True])
+def test_equal_shares_every_count(dtype, shares, b_col):
+    """Every tile of the eight-wave 256x256 config cut into 2 to 8 equal k
+    shares, each on the data-parallel loop, summed by the wave-per-block
+    kernel: partial tiles at the M and N edges (520 x 272: 3 x 2 tiles), 42
+    K-steps with a partial last one (shares of 5 to 21 steps, the last share
+    holding the tail), bias + ReLU (the bias in share 0 only)."""
+    ce = {S.F16: 8, S.BF16: 8, S.F32: 4, S.I8: 16}[dtype]
+    p = S.small_problem(dtype, 520, 272, 41 * BK[dtype] + ce, seed=60 + shares, b_col=b_col, bias=True, relu=True)
+    T.tcm_set_option("force_config", 0)
+    T.tcm_set_option("force_mode", 2)
+    T.tcm_set_option("grid_shares", shares)
+    g, C, plan = _run(p)
+    assert "config=0" in plan and f"split={shares}" in plan and f"grid={6 * shares}" in plan
+    check(p, g, C)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("b_col", [False, True])
+def test_equal_shares_column_major_a(dtype, b_col):
+    """The equal shares with A stored column-major (the [k][m] staging), the
+    planner's share count (two tiles: eight shares), padded lda."""
+    ce = {S.F16: 8, S.BF16: 8, S.F32: 4, S.I8: 16}[dtype]
+    p = S.small_problem(dtype, 208, 304, 29 * BK[dtype] + ce, seed=70, a_col=True, b_col=b_col, bias=True,
+                        lda=208 + ce)
+    T.tcm_set_option("force_config", 0)
+    T.tcm_set_option("force_mode", 2)
+    g, C, plan = _run(p)
+    assert "config=0" in plan and "split=8" in plan and "a_col=1" in plan
+    check(p, g, C)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_equal_shares_fixed_sum_order(dtype):
+    """The shares are added in share order: the float result is the same bits
+    on every call, and int8 (exact integer sums) equals the data-parallel
+    result bit for bit."""
+    ce = {S.F16: 8, S.BF16: 8, S.F32: 4, S.I8: 16}[dtype]
+    p = S.small_problem(dtype, 512, 512, 48 * BK[dtype], seed=6, bias=True, relu=True)
+    T.tcm_set_option("force_config", 0)
+    T.tcm_set_option("force_mode", 1)
+    g, C_dp, _ = _run(p)
+    T.tcm_set_option("force_mode", 2)
+    _, C_s1, plan = _run(p)
+    _, C_s2, _ = _run(p)
+    assert "split=8" in plan
+    check(p, g, C_s1)
+    assert np.array_equal(C_s1, C_s2), "equal-shares result differs between calls"
+    if dtype == S.I8:
+        assert np.array_equal(C_dp, C_s1), "int8 data-parallel and equal shares differ"
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_eight_wave_persistent_streamk_when_grid_given(dtype):
+    """A given Stream-K grid keeps the eight-wave config's persistent kernel
+    (segments cross tile boundaries; last arrival or fix-up kernel)."""
+    ce = {S.F16: 8, S.BF16: 8, S.F32: 4, S.I8: 16}[dtype]
+    p = S.small_problem(dtype, 300, 528, 20 * BK[dtype] + ce, seed=8, bias=True, relu=True)
+    T.tcm_set_option("force_config", 0)
+    T.tcm_set_option("force_mode", 2)
+    T.tcm_set_option("sk_grid", 7)
+    g, C, plan = _run(p)
+    assert "config=0" in plan and "mode=streamk" in plan and "split=" not in plan
+    check(p, g, C)
 
 
 # ------------------------------------------------------------ generic kernel

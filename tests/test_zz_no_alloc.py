@@ -51,6 +51,7 @@ CASES = [
     (6, 2, 2, (16, 4096, 4096), (1, 1024, 2048)),      # skinny Stream-K units
     (-1, 0, 0, (1536, 1536, 4096), (520, 264, 640)),   # the planner's choice
     (0, 1, 0, (600, 520, 512), (260, 136, 256)),       # data-parallel: no scratch used
+    (0, 2, 0, (1024, 768, 2048), (520, 264, 640)),     # equal shares of the eight-wave tile: one partial a workgroup
 ]
 
 
