@@ -1391,7 +1391,18 @@ int tcm_tune(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
             x.group_m = gm;
             stage2.push_back({x, 1e300, 0});
         }
-        if (b.mode == 2) {
+        if (b.mode == 2 && split_config(b.config)) {
+            // the eight-wave config's Stream-K is equal shares: their count
+            // (per-CU grids would run its persistent kernel, and the shares
+            // are always summed by the second kernel)
+            for (int sh = 2; sh <= kMaxSplit; ++sh)
+                if (T > 0 && T * sh <= 2LL * cus) {
+                    Cand x = b;
+                    x.grid_kind = 2;
+                    x.grid_param = sh;
+                    stage2.push_back({x, 1e300, 0});
+                }
+        } else if (b.mode == 2) {
             for (int g8 : {4, 8, 12, 16}) {
                 Cand x = b;
                 x.grid_kind = 1;

@@ -3,6 +3,7 @@
     python -m tensor_core_mixed_amd.tune                 # tune the shape set, write tuned/mi355x.txt
     python -m tensor_core_mixed_amd.tune --heldout R.md  # check held-out shapes against the table
     python -m tensor_core_mixed_amd.tune --only gemv     # re-tune the shapes the split-k GEMV can serve
+    python -m tensor_core_mixed_amd.tune --only split    # re-tune the shapes equal shares of the 256x256 tile can serve
 
 Tuning: for every shape of TUNE_SHAPES, tcm_tune searches the tile configs in
 both modes (and the split-k GEMV where it can serve the shape), then the
@@ -183,11 +184,22 @@ def gemv_shape(shape):
     return (M <= 16 and (b_col or N % 4 == 0)) or (not b_col and M <= 64 and N % 8 == 0)
 
 
-def tune(shapes, iters, out, merge=False):
+def split_shape(shape):
+    """Shapes the eight-wave config's equal shares may serve: 256x256 tiles
+    that fill at most half the 256 CUs (two or more shares a tile), at least
+    16 K-steps to share out, and at least 128 rows and columns (a product of
+    fewer rows wastes most of a 256-row tile's matrix-core work)."""
+    dt, M, N, K, b_col, epi, c_type = shape
+    tiles = -(-M // 256) * -(-N // 256)
+    steps = -(-K // {F16: 64, BF16: 64, F32: 32, I8: 128}[dt])
+    return tiles <= 128 and steps >= 16 and M >= 128 and N >= 128
+
+
+def tune(shapes, iters, out, merge=None):
     import torch
     import tensor_core_mixed_amd as T
     T.tcm_plan(64, 64, 64, 64, 64, 64, F16)  # the first plan loads the shipped table ...
-    if not merge:
+    if merge is None:
         T.tcm_tune_clear()                    # ... which is dropped: tune from the cost model
     s = torch.cuda.current_stream().cuda_stream
     for shape in shapes:
@@ -202,7 +214,8 @@ def tune(shapes, iters, out, merge=False):
     os.makedirs(os.path.dirname(out), exist_ok=True)
     props = torch.cuda.get_device_properties(0)
     with open(out, "w") as f:
-        what = (f"{len(TUNE_SHAPES)} shapes ({len(shapes)} re-tuned with `--only gemv`)" if merge else f"{len(shapes)} shapes")
+        what = (f"{len(TUNE_SHAPES)} shapes ({len(shapes)} re-tuned with `--only {merge}`)" if merge else
+                f"{len(shapes)} shapes")
         f.write(f"# tuning table of libtcm for {props.name} ({props.multi_processor_count} CUs), "
                 f"written by tensor_core_mixed_amd/tune.py from {what}, {iters} timed calls per candidate\n")
         f.write("# tcm-tune-2 dtype a_col b_col c_type epilogue aligned batched mclass nclass kclass "
@@ -309,8 +322,9 @@ def main():
     ap.add_argument("--out", default=TABLE)
     ap.add_argument("--iters", type=int, default=20)
     ap.add_argument("--heldout", default=None, help="write the held-out report here instead of tuning")
-    ap.add_argument("--only", choices=["gemv"], default=None,
-                    help="re-tune only the shapes the split-k GEMV can serve, keeping the shipped entries of the others")
+    ap.add_argument("--only", choices=["gemv", "split"], default=None,
+                    help="re-tune only the shapes the split-k GEMV (gemv) or the equal shares of the 256x256 tile "
+                         "(split) can serve, keeping the shipped entries of the others")
     a = ap.parse_args()
     sys.path.insert(0, os.path.dirname(HERE))
     import torch
@@ -321,8 +335,9 @@ def main():
                   HELDOUT2_SHAPES),
                  ("Held-out set 3 (drawn after set 2 shaped the wave-regime rule)", HELDOUT3_SHAPES)],
                 a.iters, a.heldout)
-    elif a.only == "gemv":
-        tune([x for x in TUNE_SHAPES if gemv_shape(x)], a.iters, a.out, merge=True)
+    elif a.only:
+        pick = gemv_shape if a.only == "gemv" else split_shape
+        tune([x for x in TUNE_SHAPES if pick(x)], a.iters, a.out, merge=a.only)
     else:
         tune(TUNE_SHAPES, a.iters, a.out)
 
