@@ -837,11 +837,12 @@ def summarize_counters(d, name, calib=None):
 
     calib = calib or d
 
-    def per_kernel(root, sub, counter, kernel_pat):
+    def per_kernel(root, sub, counter, kernel_pats):
+        pats = (kernel_pats,) if isinstance(kernel_pats, str) else kernel_pats
         out = {}
         for f in glob.glob(os.path.join(root, sub, "**", "*counter_collection.csv"), recursive=True):
             for r in csv.DictReader(open(f)):
-                if r["Counter_Name"] == counter and kernel_pat in r["Kernel_Name"]:
+                if r["Counter_Name"] == counter and any(k in r["Kernel_Name"] for k in pats):
                     out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         return out
 
@@ -854,11 +855,13 @@ def summarize_counters(d, name, calib=None):
                     vals.append(float(r["Counter_Value"]))
         return vals
 
-    # per kernel (a Stream-K plan launches a data-parallel and a Stream-K kernel): medians per dispatch
+    # per kernel (a Stream-K plan launches a data-parallel and a Stream-K kernel, and may sum its split
+    # tiles in a second kernel; equal shares launch the shares' kernel and their sum): medians per dispatch
     import synthetic as S
-    kpat = ("tile_conv_kernel" if name in S.CONV_WORKLOADS else
-            "tile_group_kernel" if name in S.GROUP_WORKLOADS else
-            "tile_gemm_acol_kernel" if S.workload(name).a_col else "tile_gemm_kernel")
+    kpat = (("tile_conv_kernel", "conv_fixup_kernel") if name in S.CONV_WORKLOADS else
+            ("tile_group_kernel", "group_fixup_kernel") if name in S.GROUP_WORKLOADS else
+            ("tile_gemm_acol_kernel" if S.workload(name).a_col else "tile_gemm_kernel", "tile_fixup_kernel",
+             "tile_split_kernel", "tile_split_fixup_kernel"))
     fetch = per_kernel(d, "fetch", "FETCH_SIZE", kpat)
     write = per_kernel(d, "write", "WRITE_SIZE", kpat)
     if not fetch:  # a product the split-k GEMV serves

@@ -453,15 +453,17 @@ bool make_plan(const Problem& p, const Options& o, int cus, Plan* out) {
     if (!o.generic) {
         for (int c = 0; c < kNumConfigs; ++c) {
             if (o.force_config >= 0 && c != o.force_config) continue;
-            // the eight-wave config is data-parallel only (its Stream-K kernel
-            // spills registers): a forced Stream-K picks among the others
-            // unless that config is forced too
-            if (o.force_mode == 2 && o.force_config < 0 && kConfigs[c].wm * kConfigs[c].wn > 4) continue;
             // the 32-row deep unit is planned for products of one tile row
             // (M <= 32; a group counts all its rows) unless it is forced
             if (o.force_config < 0 && kConfigs[c].bm < 64 && kConfigs[c].sk_stages > 2 && p.M > kConfigs[c].bm) continue;
             if (p.group ? !p.group_ok[c] : !tile_eligible(p, kConfigs[c])) continue;
             Estimate e = estimate(p, c, cus, o.force_mode, o.sk_grid, o.sk_occ[c], o.grid_per_cu8, o.grid_shares);
+            // the eight-wave config's Stream-K is its equal shares; where they
+            // cannot serve (tiles filling more than half the CUs, a batch, a
+            // given grid) it would run the persistent kernel, which spills
+            // registers: a forced Stream-K then picks among the other configs
+            // unless that config is forced too
+            if (o.force_mode == 2 && o.force_config < 0 && split_config(c) && e.split == 0) continue;
             // configs run from large tiles to small: a smaller tile must be
             // clearly cheaper, since the model underrates its extra operand
             // traffic (2560 x 4096 x 4096: 64x64 tiles estimated 0.7% below

@@ -234,6 +234,11 @@ def test_equal_shares_of_the_eight_wave_tile(model_only):
     p = T.tcm_plan(1536, 1536, 16384, 16384, 1536, 1536, T.TCM_F16_F32)
     assert (p["split"], p["grid"], p["workspace_bytes"]) == (3, 108, 108 * 256 * 256 * 4)
     T.tcm_set_option("grid_shares", 0)
+    # a forced Stream-K without a forced config may take the equal shares
+    T.tcm_set_option("force_config", -1)
+    p = T.tcm_plan(1536, 1536, 16384, 16384, 1536, 1536, T.TCM_F16_F32)
+    assert (p["config"], p["mode"], p["split"]) == (0, 2, 7)
+    T.tcm_set_option("force_config", 0)
     # a given grid keeps the persistent Stream-K kernel
     T.tcm_set_option("sk_grid", 200)
     p = T.tcm_plan(1536, 1536, 16384, 16384, 1536, 1536, T.TCM_F16_F32)
@@ -248,8 +253,9 @@ def test_equal_shares_of_the_eight_wave_tile(model_only):
 
 
 def test_forced_streamk_skips_the_eight_wave_config():
-    """The eight-wave config is data-parallel only: a forced Stream-K plan
-    uses another config unless that one is forced too."""
+    """Where the eight-wave config's equal shares cannot serve (225 tiles fill
+    more than half the CUs), its Stream-K would be the persistent kernel: a
+    forced Stream-K plan uses another config unless that one is forced too."""
     try:
         T.tcm_set_option("force_mode", 2)
         p = T.tcm_plan(3840, 3840, 4096, 4096, 3840, 3840, T.TCM_F16_F32)
