@@ -766,7 +766,7 @@ def render_report(src, dst):
         pc = r.get("per_call_us", {}).get("median", "") if isinstance(r.get("per_call_us"), dict) else ""
         tuned = r.get("tuned", {}).get("ms")
         plan = " ".join(kv for kv in r["plan"].split() if kv.split("=")[0] in ("kernel", "config", "tile", "mode", "grid",
-                                                                                  "fixup", "group", "tuned", "splits",
+                                                                                  "fixup", "group", "tuned", "splits", "split",
                                                                                   "mfma"))
         L.append(f"| {r['workload']} | {r['mode']} | {r['ms'] * 1e3:.1f} | {pc} | {r['tflops']:.1f} | "
                  f"{100 * r['frac_peak']:.1f}% | {100 * r['hbm_frac']:.1f}% | {r.get('cold_median_us', '')} | "
