@@ -804,7 +804,8 @@ struct TileKernel {
     }
 
     // ------------------------------------------------- ping-pong main loop
-    // Eight-wave data-parallel kernel, n-contiguous B (f16 / bf16): waves
+    // Eight-wave data-parallel kernel, n-contiguous B or m-contiguous A
+    // (f16 / bf16): waves
     // 0-3 (group A) and 4-7 (group B) sit one of each per SIMD and run the
     // same loop one phase apart, phases separated by workgroup barriers.  In
     // a memory phase a wave reads all fragments of one K-step from LDS; in a
@@ -812,9 +813,11 @@ struct TileKernel {
     // waits on LDS, its partner keeps the matrix core fed.  This pays where
     // fragment reads are many: the transpose reads of an n-contiguous B tile
     // return 8 bytes per lane, twice the LDS instructions of a k-contiguous
-    // one (8192^3 f16: 915 against 1023 us).  With k-contiguous B the
-    // interleaved loop below is faster (880 against 925 us), and on int8
-    // the two are even.
+    // one (8192^3 f16: 915 against 1023 us), and so do those of an
+    // m-contiguous A tile (A column-major, B column-major, 8192^3 f16: 938
+    // against 1019 us).  With both operands k-contiguous the interleaved
+    // loop below is faster (880 against 925 us), and on int8 the two are
+    // even.
     //
     // Copies, two LDS stages.  Group A issues the A-operand copies of step
     // kt+1 in its memory phase of step kt.  Group B (copier slot wave-4)
@@ -826,7 +829,7 @@ struct TileKernel {
     // its compute phase, B at the end of its memory phase.  One loop serves
     // both groups: two loops in the branches of a group test spill
     // registers.
-    static constexpr bool PINGPONG = NW == 8 && !CONV && NST == 2 && !B_KMAJ && (DT == F16 || DT == BF16);
+    static constexpr bool PINGPONG = NW == 8 && !CONV && NST == 2 && (!B_KMAJ || A_MMAJ) && (DT == F16 || DT == BF16);
 
     // a workgroup barrier that nothing is scheduled across
     __device__ __forceinline__ static void phase_barrier() {

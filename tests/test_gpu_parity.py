@@ -135,22 +135,29 @@ def test_column_major_a_off_the_piece_grid_is_generic(dtype):
 
 @pytest.mark.parametrize("dtype", [S.F16, S.BF16])
 @pytest.mark.parametrize("ksteps", [1, 2, 3, 33])
-@pytest.mark.parametrize("mode", [1, 2])
-def test_pingpong_loop_step_counts(dtype, ksteps, mode):
-    """The eight-wave kernel with row-major B runs its wave groups one phase
+@pytest.mark.parametrize("mode", [1, 2, 3])
+@pytest.mark.parametrize("layout", ["b_row", "a_col_b_col", "a_col_b_row"])
+def test_pingpong_loop_step_counts(dtype, ksteps, mode, layout):
+    """The eight-wave kernel with row-major B or column-major A (operands
+    read back with transposing LDS reads) runs its wave groups one phase
     apart, each group copying one operand, group B two K-steps ahead: one,
     two and three K-steps exercise the prologue and the steps that issue no
     copies, 33 the steady state (with a ragged k tail), on ragged M and N.
-    Stream-K runs the same loop on segments that start mid-tile."""
+    Stream-K runs the same loop on segments that start mid-tile (mode 2, a
+    given grid) and on equal shares (mode 3 here: Stream-K without a grid)."""
     K = 64 * ksteps - (24 if ksteps == 33 else 0)
-    p = S.small_problem(dtype, 520, 264, K, seed=70 + ksteps, bias=True, relu=(mode == 1))
+    a_col, b_col = layout.startswith("a_col"), layout.endswith("b_col")
+    p = S.small_problem(dtype, 520, 264, K, seed=70 + ksteps, bias=True, relu=(mode == 1), a_col=a_col, b_col=b_col,
+                        lda=520 + 8 if a_col else 0)
     T.tcm_set_option("force_config", 0)
-    T.tcm_set_option("force_mode", mode)
+    T.tcm_set_option("force_mode", min(mode, 2))
     if mode == 2:
         T.tcm_set_option("sk_grid", 5)
     g, C, plan = _run(p)
-    assert "config=0" in plan and "b_col=0" in plan
+    assert "config=0" in plan and f"b_col={int(b_col)}" in plan and (("a_col=1" in plan) == a_col)
     assert ("mode=dp" if mode == 1 else "mode=streamk") in plan
+    if mode == 3 and ksteps > 1:
+        assert f"split={min(8, ksteps)}" in plan
     check(p, g, C)
 
 
