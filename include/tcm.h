@@ -324,7 +324,8 @@ const char* tcm_status_string(int status);
  *   "grid_shares"  0 = planner decides, else a split-k grid of value
  *                  workgroups per tile (1..64): every split tile in equal
  *                  shares that start at the same k (the equal shares of the
- *                  eight-wave config: at most 8, each at least one K-step).
+ *                  eight-wave config: at most 8, at most as many as fill the
+ *                  CUs once, each at least one K-step).
  *   "tuned"        1 (default) = use the tuning table (tcm_tune) for problems
  *                  whose class it holds; 0 = ignore it.  force_config /
  *                  force_mode / sk_grid / gemv win.

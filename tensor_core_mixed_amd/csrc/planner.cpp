@@ -273,13 +273,19 @@ Estimate estimate(const Problem& p, int ci, int cus, int force_mode, int sk_grid
     // workgroup each, on the data-parallel loop, every share storing its
     // partial tile and a second kernel summing them.  S fills the co-resident
     // slots (at most kMaxSplit shares, each at least one K-step) unless the
-    // equal-shares option gives it; a forced grid keeps the persistent kernel.
+    // equal-shares option gives a smaller S; a forced grid keeps the
+    // persistent kernel.
     // All shares store their partials at once at the end, and the sum reads
     // them back: both at HBM rate.  Single products only, as for aligned
     // Stream-K grids.
     Estimate sp{1e300, 2, 0, 0, 0};
     if (split_config(ci) && !p.group && !p.conv && p.batch <= 1 && sk_grid <= 0 && grid_per_cu8 <= 0) {
-        int64_t S = grid_shares > 0 ? grid_shares : slots / std::max<int64_t>(T, 1);
+        // (a second wave of shares costs a whole second round of K-steps:
+        // 1536^2 x 16384 at 8 shares, 288 workgroups, ran 1.45x slower than
+        // at 7; a tuned share count carried to a shape with more tiles is
+        // capped the same way)
+        const int64_t fit = slots / std::max<int64_t>(T, 1);
+        int64_t S = grid_shares > 0 ? std::min<int64_t>(grid_shares, fit) : fit;
         S = std::min<int64_t>(std::min<int64_t>(S, kMaxSplit), I);
         if (S >= 2) {
             const int64_t per = cdiv(I, S);

@@ -1377,6 +1377,16 @@ int tcm_tune(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
     for (size_t i = 0; i < stage1.size(); ++i)
         if (valid[i]) ranked.push_back(stage1[i]);
     std::sort(ranked.begin(), ranked.end(), [](const Timed& x, const Timed& y) { return x.us < y.us; });
+    // A data-parallel point within 2% of a faster Stream-K one ranks first:
+    // within timing noise the plan without split tiles carries better to the
+    // other shapes of its class (f32 768^3: Stream-K 17.42 against 17.50 us
+    // data-parallel; on 1024^3, which uses that entry, 26.1 against 22.8 us).
+    if (!ranked.empty() && ranked[0].c.mode == 2 && !gemv_cand(ranked[0].c.config))
+        for (size_t i = 1; i < ranked.size(); ++i)
+            if (ranked[i].c.mode == 1 && !gemv_cand(ranked[i].c.config) && ranked[i].us <= 1.02 * ranked[0].us) {
+                std::rotate(ranked.begin(), ranked.begin() + i, ranked.begin() + i + 1);
+                break;
+            }
     // Stage 2: around the three fastest, the parameters the table leaves to
     // the planner: tile-order group rows; for Stream-K also the grid (per-CU
     // sizes, equal shares of every tile) and the way split tiles are summed.
@@ -1396,7 +1406,7 @@ int tcm_tune(int64_t M, int64_t N, int64_t K, const void* A, int64_t lda, const 
             // (per-CU grids would run its persistent kernel, and the shares
             // are always summed by the second kernel)
             for (int sh = 2; sh <= kMaxSplit; ++sh)
-                if (T > 0 && T * sh <= 2LL * cus) {
+                if (T > 0 && T * sh <= cus) {  // (the planner caps the shares at one wave)
                     Cand x = b;
                     x.grid_kind = 2;
                     x.grid_param = sh;

@@ -233,6 +233,10 @@ def test_equal_shares_of_the_eight_wave_tile(model_only):
     T.tcm_set_option("grid_shares", 3)  # the equal-shares option gives S
     p = T.tcm_plan(1536, 1536, 16384, 16384, 1536, 1536, T.TCM_F16_F32)
     assert (p["split"], p["grid"], p["workspace_bytes"]) == (3, 108, 108 * 256 * 256 * 4)
+    # more shares than fill the CUs once are capped (64 tiles: at most 4)
+    T.tcm_set_option("grid_shares", 5)
+    p = T.tcm_plan(2048, 2048, 4096, 4096, 2048, 2048, T.TCM_F16_F32)
+    assert (p["config"], p["split"], p["grid"]) == (0, 4, 256)
     T.tcm_set_option("grid_shares", 0)
     # a forced Stream-K without a forced config may take the equal shares
     T.tcm_set_option("force_config", -1)
