@@ -276,10 +276,11 @@ Estimate estimate(const Problem& p, int ci, int cus, int force_mode, int sk_grid
     // equal-shares option gives a smaller S; a forced grid keeps the
     // persistent kernel.
     // All shares store their partials at once at the end, and the sum reads
-    // them back: both at HBM rate.  Single products only, as for aligned
-    // Stream-K grids.
+    // them back: both at HBM rate.  A batch's tiles form one list (shares of
+    // neighbouring tiles of one entry share operand panels, as in a single
+    // product); groups and convolutions keep their own kernels.
     Estimate sp{1e300, 2, 0, 0, 0};
-    if (split_config(ci) && !p.group && !p.conv && p.batch <= 1 && sk_grid <= 0 && grid_per_cu8 <= 0) {
+    if (split_config(ci) && !p.group && !p.conv && sk_grid <= 0 && grid_per_cu8 <= 0) {
         // (a second wave of shares costs a whole second round of K-steps:
         // 1536^2 x 16384 at 8 shares, 288 workgroups, ran 1.45x slower than
         // at 7; a tuned share count carried to a shape with more tiles is

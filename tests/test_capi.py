@@ -251,9 +251,9 @@ def test_equal_shares_of_the_eight_wave_tile(model_only):
     # tiles that fill half the CUs or more: no second share, the persistent kernel
     p = T.tcm_plan(3840, 3840, 4096, 4096, 3840, 3840, T.TCM_F16_F32)
     assert p["config"] == 0 and p["mode"] == 2 and p["split"] == 0
-    # batches keep the persistent grid (entries share no operand panel)
+    # a batch's tiles form one list: two entries of 36 tiles, 3 shares each
     p = T.tcm_plan_batched(2, 1536, 1536, 16384, 16384, 1536, 1536, T.TCM_F16_F32)
-    assert p["split"] == 0
+    assert (p["sk_tiles"], p["split"], p["grid"]) == (72, 3, 216)
 
 
 def test_forced_streamk_skips_the_eight_wave_config():

@@ -25,6 +25,7 @@ def _reset_options():
     T.tcm_set_option("sk_grid", 0)
     T.tcm_set_option("generic", 0)
     T.tcm_set_option("sk_fixup", 0)
+    T.tcm_set_option("grid_shares", 0)
 
 
 def _pack(arr, n_entries, pad, fill):
@@ -114,6 +115,26 @@ def test_batched_every_config_and_mode(dtype, config, mode):
     p = S.small_problem(dtype, 40, 144, 208, seed=90 + config, bias=True, relu=True, batch=3)
     g, C, plan = _case(p)
     assert f"config={config}" in plan and "batch=3" in plan
+    check_batch(p, g, C)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("a_col", [False, True])
+@pytest.mark.parametrize("b_shared", [False, True])
+def test_batched_equal_shares(dtype, a_col, b_shared):
+    """Equal shares of the eight-wave tile across a batch: the entries' tiles
+    form one list (3 entries x 2 x 2 tiles), every tile cut into 5 k shares
+    (the last holding the K tail), each share and the sum on its entry's
+    operands, B shared or not, both layouts of A."""
+    ce = {S.F16: 8, S.BF16: 8, S.F32: 4, S.I8: 16}[dtype]
+    bk = {S.F16: 64, S.BF16: 64, S.F32: 32, S.I8: 128}[dtype]
+    T.tcm_set_option("force_config", 0)
+    T.tcm_set_option("force_mode", 2)
+    T.tcm_set_option("grid_shares", 5)
+    p = S.small_problem(dtype, 272, 272, 25 * bk + ce, seed=120, a_col=a_col, bias=True, relu=True, batch=3,
+                        b_shared=b_shared, lda=272 + ce if a_col else 0)
+    g, C, plan = _case(p)
+    assert "config=0" in plan and "split=5" in plan and "grid=60" in plan and "batch=3" in plan
     check_batch(p, g, C)
 
 

@@ -66,23 +66,27 @@ def test_two_streams_at_once(mode):
     b.check()
 
 
-@pytest.mark.parametrize("mode,fixup", [(1, 0), (2, 1), (2, 2)])
-def test_graph_capture_replays(mode, fixup):
+@pytest.mark.parametrize("mode,fixup,config", [(1, 0, 4), (2, 1, 4), (2, 2, 4), (2, 0, 0)])
+def test_graph_capture_replays(mode, fixup, config):
     """A call captured into a HIP graph (the split-k workspace already exists
     for the stream, so capture allocates nothing) gives the eager result on
     every replay; eager work and synchronisations run between the replays.
-    With fixup 2 the call is two launches: Stream-K and its fix-up kernel."""
+    With fixup 2 the call is two launches: Stream-K and its fix-up kernel;
+    on the eight-wave config (config 0) the equal shares and their sum."""
     T.tcm_set_option("force_mode", mode)
-    T.tcm_set_option("force_config", 4)
+    T.tcm_set_option("force_config", config)
     T.tcm_set_option("sk_fixup", fixup)
-    c = Call(S.small_problem(S.F16, 128, 256, 1024, seed=402, bias=True, relu=True))
+    c = Call(S.small_problem(S.F16, 128 if config else 520, 256 if config else 272, 1024, seed=402, bias=True,
+                             relu=True))
     s = torch.cuda.Stream()
     c(s)  # warm-up: plans, and creates this stream's workspace
     torch.cuda.synchronize()
     eager = c.C.clone()
     c.check()
-    say(f"[case] graph capture, mode {mode}, fixup {fixup}: {T.tcm_last_plan()}")
-    if mode == 2:
+    say(f"[case] graph capture, mode {mode}, fixup {fixup}, config {config}: {T.tcm_last_plan()}")
+    if mode == 2 and config == 0:
+        assert "split=8" in T.tcm_last_plan()
+    elif mode == 2:
         assert ("fixup=kernel" in T.tcm_last_plan()) == (fixup == 2)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
