@@ -466,7 +466,7 @@ bool make_plan(const Problem& p, const Options& o, int cus, Plan* out) {
             if (p.group ? !p.group_ok[c] : !tile_eligible(p, kConfigs[c])) continue;
             Estimate e = estimate(p, c, cus, o.force_mode, o.sk_grid, o.sk_occ[c], o.grid_per_cu8, o.grid_shares);
             // the eight-wave config's Stream-K is its equal shares; where they
-            // cannot serve (tiles filling more than half the CUs, a batch, a
+            // cannot serve (tiles filling more than half the CUs, a group, a
             // given grid) it would run the persistent kernel, which spills
             // registers: a forced Stream-K then picks among the other configs
             // unless that config is forced too
