@@ -2,7 +2,9 @@
 type, both layouts of A and B, shapes on and off the 16-byte piece grid (so
 that the tiled kernel, the split-k GEMV and the generic kernel all take
 part), padded leading dimensions, every epilogue flag, 16-bit outputs, and
-now and then a forced tile config, mode or Stream-K grid; batches of 2 to 5
+now and then a forced tile config, mode or Stream-K grid (forced Stream-K
+without a grid plans the eight-wave tile's equal shares in 40 of the 320
+single cases); batches of 2 to 5
 entries (B shared or not) at padded strides.  Each case is drawn from its
 own seed, printed before it touches the GPU, and compared with the oracle
 on every entry (C's padding columns, and the gaps between batch entries,
@@ -87,8 +89,11 @@ def test_random_case(seed):
 
 def test_random_cases_reach_every_kernel():
     """The drawn set plans the tiled kernel (both A layouts), the split-k
-    GEMV and the generic kernel (checked on the CPU with tcm_plan)."""
+    GEMV and the generic kernel (checked on the CPU with tcm_plan), and among
+    the tiled plans at least ten equal-shares ones (forced Stream-K without a
+    grid on the eight-wave tile)."""
     kinds = set()
+    shares = 0
     for seed in range(N_CASES):
         p, opts = draw(seed)
         code = p.dtype | (T.TCM_A_COLMAJOR if p.a_col else 0) | (T.TCM_B_COLMAJOR if p.b_col else 0)
@@ -101,7 +106,9 @@ def test_random_cases_reach_every_kernel():
             for k, v in (("force_mode", 0), ("force_config", -1), ("sk_grid", 0), ("sk_fixup", 0)):
                 T.tcm_set_option(k, v)
         kinds.add((q["kernel"], p.a_col if q["kernel"] == 1 else None))
+        shares += q["split"] > 1
     assert {(0, None), (1, False), (1, True), (2, None)} <= kinds, kinds
+    assert shares >= 10, shares
 
 
 N_BATCHED = 64
