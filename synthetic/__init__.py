@@ -130,6 +130,9 @@ def _workloads():
                                         c_type="f16", accum=True)
     # a strided batch of skinny products, each with its own B (experts of a mixture, a few rows each)
     w["batch8_m16_4096"] = Problem("batch8_m16_4096", F16, 16, 4096, 4096, dist="uniform", seed=8, batch=8)
+    # a strided batch of two long-K products whose 72 tiles of 256x256 fill under a third of the CUs
+    w["sk_batch2_1536x1536x16384"] = Problem("sk_batch2_1536x1536x16384", F16, 1536, 1536, 16384, dist="uniform",
+                                             seed=10, batch=2)
     return w
 
 

@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 FULL = {"f16_512", "f32_2048", "skinny_m1", "skinny_m16", "skinny_m64", "skinny_m256"}
 SPLITK = ["skinny_m1", "skinny_m16", "skinny_m64", "skinny_m256", "sk_1536x1536x16384", "sk_3840x3840x4096",
-          "batch8_m16_4096"]
+          "batch8_m16_4096", "sk_batch2_1536x1536x16384"]
 
 
 @pytest.fixture(autouse=True)
