@@ -871,6 +871,7 @@ int launch_tiled(const Problem& p, const Plan& pl, TileArgs& a, int dev, void* s
     a.ws_counter = nullptr;
     a.sk_fixup_kernel = pl.fixup_kernel ? 1 : 0;
     a.split = pl.split;
+    if (pl.split > kMaxSplit) return TCM_ERR_INVALID_VALUE;  // the sum kernel holds at most kMaxSplit partials a block
     if (pl.mode == 2 && pl.sk_tiles > 0 && noalloc) {
         char* base = nullptr;
         int st = scratch_of(dev, &base);
