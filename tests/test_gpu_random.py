@@ -4,11 +4,12 @@ that the tiled kernel, the split-k GEMV and the generic kernel all take
 part), padded leading dimensions, every epilogue flag, 16-bit outputs, and
 now and then a forced tile config, mode or Stream-K grid (forced Stream-K
 without a grid plans the eight-wave tile's equal shares in 40 of the 320
-single cases); batches of 2 to 5
-entries (B shared or not) at padded strides.  Each case is drawn from its
+single cases); batches of 2 to 5 entries (B shared or not) at padded
+strides.  Each case is drawn from its
 own seed, printed before it touches the GPU, and compared with the oracle
 on every entry (C's padding columns, and the gaps between batch entries,
-must keep their fill)."""
+must keep their fill).  A third set draws larger products (up to 2048 x
+2048, K up to 8192), half of them on the eight-wave tile's equal shares."""
 import numpy as np
 import pytest
 
@@ -26,7 +27,7 @@ N_CASES = 320
 def _reset_options():
     yield
     for k, v in (("force_mode", 0), ("force_config", -1), ("sk_grid", 0), ("sk_fixup", 0), ("gemv", 0),
-                 ("gemv_wide", 0)):
+                 ("gemv_wide", 0), ("grid_shares", 0)):
         T.tcm_set_option(k, v)
 
 
@@ -146,3 +147,68 @@ def test_random_batched_case(seed):
     C, plan = run_batched(p, g, pads=pads)
     say(f"       plan: {plan}")
     check_batch(p, g, C)
+
+
+N_LARGE = 40
+
+
+def draw_large(seed):
+    """Larger case `seed`: 64 to 2048 rows and columns (whole 16-byte pieces),
+    K from 256 to 8192, either layout of A and B, padded leading dimensions,
+    a batch of 2-3 now and then (smaller entries), any epilogue; half of the
+    cases forced onto the eight-wave tile's Stream-K (its equal shares,
+    sometimes with a given share count)."""
+    rng = np.random.default_rng(77000 + seed)
+    dtype = [S.F16, S.BF16, S.F32, S.I8][int(rng.integers(4))]
+    ce = CE[dtype]
+    a_col, b_col = bool(rng.integers(2)), bool(rng.integers(2))
+    M = int(rng.integers(64, 2049)) // ce * ce
+    N = int(rng.integers(64, 2049)) // ce * ce
+    K = int(rng.integers(256, 8193)) // ce * ce
+    batch = 1 if rng.random() < 0.7 else int(rng.integers(2, 4))
+    if batch > 1:
+        M, N, K = min(M, 768), min(N, 768), min(K, 4096)
+    bias, relu = bool(rng.integers(2)), bool(rng.integers(2))
+    c_type = "acc" if dtype in (S.I8, S.F32) else ["acc", "f16", "bf16"][int(rng.integers(3))]
+    if c_type == "bf16" and dtype == S.F16:
+        c_type = "f16"
+    if c_type == "f16" and dtype == S.BF16:
+        c_type = "bf16"
+    accum = rng.random() < 0.25
+    pad = lambda: int(rng.integers(0, 3)) * ce
+    p = S.small_problem(dtype, M, N, K, seed=900 + seed, a_col=a_col, b_col=b_col, bias=bias, relu=relu,
+                        lda=(M if a_col else K) + pad(), ldb=(K if b_col else N) + pad(), ldc=N + pad(), c_type=c_type,
+                        accum=accum)
+    if batch > 1:
+        from dataclasses import replace
+        p = replace(p, batch=batch)
+    opts = {}
+    if rng.random() < 0.5:
+        opts = {"force_config": 0, "force_mode": 2}
+        if rng.random() < 0.5:
+            opts["grid_shares"] = int(rng.integers(2, 9))
+    return p, opts
+
+
+@pytest.mark.parametrize("seed", range(N_LARGE))
+def test_random_large_case(seed):
+    from test_gpu_batched import check_batch, run_batched
+    p, opts = draw_large(seed)
+    for k, v in opts.items():
+        assert T.tcm_set_option(k, v) == T.TCM_OK
+    say(f"[case] random large {seed}: {p.name} dtype={p.dtype} batch={p.batch} M={p.M} N={p.N} K={p.K} a_col={p.a_col} "
+        f"b_col={p.b_col} lda={p.LDA} ldb={p.LDB} ldc={p.LDC} bias={p.bias} relu={p.relu} c={p.c_type} accum={p.accum} "
+        f"opts={opts}")
+    g = S.generate(p)
+    if p.batch > 1:
+        C, plan = run_batched(p, g)
+        say(f"       plan: {plan}")
+        check_batch(p, g, C)
+    else:
+        C, plan = run_tcm(p, g)
+        say(f"       plan: {plan}")
+        if p.M * p.N * p.K > 2e9:  # sampled entries, computed one by one by the oracle
+            ii, jj = S.sample_entries(p)
+            check(p, g, C, ii, jj)
+        else:
+            check(p, g, C)
