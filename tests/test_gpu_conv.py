@@ -267,3 +267,44 @@ def test_conv_full_size_sampled(name):
     mm, kk = S.sample_conv_entries(p)
     check_conv(p, g, y, mm, kk)
     assert p.dtype == S.I8 or np.all(np.isfinite(y)), "unwritten outputs"
+
+
+N_RANDOM = 100
+
+
+def draw_conv(seed):
+    """Random convolution `seed`: element type, channels on the K-step grid
+    (the tiled gather) or off it (the generic kernel), 1x1 to 3x3 filters,
+    padding, stride and dilation up to 2, 1 to 159 output channels, bias,
+    ReLU, C's type, and now and then a forced tile config and mode."""
+    rng = np.random.default_rng(55000 + seed)
+    dt = [S.F16, S.BF16, S.F32, S.I8][int(rng.integers(4))]
+    C = BKE[dt] * int(rng.integers(1, 4)) if rng.random() < 0.8 else int(rng.integers(1, 40))
+    R, Sd = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+    pad = (int(rng.integers(0, R)), int(rng.integers(0, Sd)))
+    stride = (int(rng.integers(1, 3)), int(rng.integers(1, 3)))
+    dil = (int(rng.integers(1, 3)), int(rng.integers(1, 3)))
+    H, W = int(rng.integers(R * dil[0], 16)), int(rng.integers(Sd * dil[1], 16))
+    N, K = int(rng.integers(1, 5)), int(rng.integers(1, 160))
+    c_type = "acc" if dt in (S.I8, S.F32) else ["acc", "f16", "bf16"][int(rng.integers(3))]
+    if c_type == "bf16" and dt == S.F16:
+        c_type = "f16"
+    if c_type == "f16" and dt == S.BF16:
+        c_type = "bf16"
+    p = S.small_conv(dt, N, H, W, C, K, R, Sd, pad=pad, stride=stride, dil=dil, seed=700 + seed,
+                     bias=bool(rng.integers(2)), relu=bool(rng.integers(2)), c_type=c_type)
+    opts = {}
+    r = rng.random()
+    if r < 0.3:
+        opts = {"force_config": int(rng.integers(0, T.tcm_config_count())), "force_mode": int(rng.integers(1, 3))}
+    elif r < 0.4:
+        opts = {"force_mode": 2}
+    return p, opts
+
+
+@pytest.mark.parametrize("seed", range(N_RANDOM))
+def test_random_conv_case(seed):
+    p, opts = draw_conv(seed)
+    for k, v in opts.items():
+        assert T.tcm_set_option(k, v) == T.TCM_OK
+    _run_check(p)

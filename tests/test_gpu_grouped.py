@@ -170,3 +170,52 @@ def test_torch_convenience_grouped():
     for A, B, b, C in zip(As, Bs, bs, Cs):
         ref = (A.float() @ B.float() + b).relu()
         assert torch.allclose(C, ref, atol=1e-2, rtol=1e-3)
+
+
+N_RANDOM = 60
+
+
+def draw_group(seed):
+    """Random group `seed`: 1 to 12 entries sharing K and the type, each with
+    its own M (0 to 300) and N (on the 16-byte grid, or not: such groups run
+    entry by entry), either layout of B, padded leading dimensions, any
+    epilogue, and now and then a forced tile config, mode or Stream-K grid."""
+    rng = np.random.default_rng(66000 + seed)
+    dtype = DTYPES[int(rng.integers(len(DTYPES)))]
+    ce = {S.F16: 8, S.BF16: 8, S.F32: 4, S.I8: 16}[dtype]
+    on_grid = rng.random() < 0.8
+    count = int(rng.integers(1, 13))
+    shapes = []
+    for _ in range(count):
+        M = int(rng.integers(0, 301)) if rng.random() < 0.9 else 0
+        N = int(rng.integers(1, 300))
+        shapes.append((M, max(ce, N // ce * ce) if on_grid else N))
+    K = int(rng.integers(1, 1200))
+    K = max(ce, K // ce * ce) if on_grid else K
+    c_type = "acc" if dtype in (S.I8, S.F32) else ["acc", "f16", "bf16"][int(rng.integers(3))]
+    if c_type == "bf16" and dtype == S.F16:
+        c_type = "f16"
+    if c_type == "f16" and dtype == S.BF16:
+        c_type = "bf16"
+    ps = make_group(dtype, shapes, K, seed=3000 + 20 * seed, b_col=bool(rng.integers(2)), bias=bool(rng.integers(2)),
+                    relu=bool(rng.integers(2)), c_type=c_type, accum=rng.random() < 0.25,
+                    ld_pad=int(rng.integers(0, 3)) * ce)
+    opts = {}
+    r = rng.random()
+    if r < 0.25:
+        opts = {"force_config": int(rng.integers(0, T.tcm_config_count())), "force_mode": int(rng.integers(1, 3))}
+    elif r < 0.4:
+        opts = {"force_mode": 2, "sk_grid": int(rng.integers(1, 400))}
+    return ps, opts
+
+
+@pytest.mark.parametrize("seed", range(N_RANDOM))
+def test_random_group_case(seed):
+    ps, opts = draw_group(seed)
+    for k, v in opts.items():
+        assert T.tcm_set_option(k, v) == T.TCM_OK
+    if all(p.M == 0 for p in ps):
+        ps[0] = S.small_problem(ps[0].dtype, 7, ps[0].N, ps[0].K, seed=ps[0].seed, b_col=ps[0].b_col, bias=ps[0].bias,
+                                relu=ps[0].relu, c_type=ps[0].c_type, accum=ps[0].accum)
+    gs, outs, plan = run_group(ps)
+    check_group(ps, gs, outs)
